@@ -1,0 +1,147 @@
+"""ctypes binding of libdbs.so (C ABI in include/dbs.h).
+
+Argument marshalling only: every step of a pass runs in the HIP kernels of
+libdbs.so.  Tensors must be float32, contiguous, on a CUDA (HIP) device, of
+shape [n,n] or [batch,n,n]; calls enqueue on the tensor device's current
+torch stream and return without synchronising.  There is no CPU fallback:
+without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SO_PATH = os.path.join(HERE, "libdbs.so")
+
+ALGO_AUTO, ALGO_PERK, ALGO_LDS, ALGO_BLOCKED = 0, 1, 2, 3
+_ALGOS = {"auto": ALGO_AUTO, "perk": ALGO_PERK, "lds": ALGO_LDS, "blocked": ALGO_BLOCKED}
+
+CHECK_FLAGS = {
+    "asym": 1, "diag": 2, "nonfinite": 4, "l_gt_u": 8, "l_neg": 16,
+    "unquant": 32, "range": 64, "negzero": 128,
+}
+
+DBS_OK, DBS_EINVAL, DBS_EDEVICE, DBS_ELAUNCH, DBS_EUNSUPPORTED = 0, -1, -2, -3, -4
+
+EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_rounds", "dbs_check", "dbs_lds_max_n",
+           "dbs_auto_algo", "dbs_strerror", "dbs_version")
+
+
+class DbsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libdbs.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(SO_PATH):
+            raise ImportError(f"{SO_PATH} is missing: build it first "
+                              "(python -m distance_geometry_bound_amd.build)")
+        L = ctypes.CDLL(SO_PATH)
+        vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.dbs_smooth.argtypes = [vp, vp, i64, i64, vp]
+        L.dbs_smooth_algo.argtypes = [vp, vp, i64, i64, vp, c_int]
+        L.dbs_rounds.argtypes = [vp, vp, i64, i64, i64, i64, vp]
+        L.dbs_check.argtypes = [vp, vp, i64, i64, vp, vp]
+        L.dbs_auto_algo.argtypes = [i64, i64]
+        L.dbs_strerror.argtypes = [c_int]
+        L.dbs_strerror.restype = ctypes.c_char_p
+        for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_rounds", "dbs_check",
+                  "dbs_lds_max_n", "dbs_auto_algo", "dbs_version"):
+            getattr(L, f).restype = c_int
+        _lib = L
+    return _lib
+
+
+def _raise(status: int):
+    if status == DBS_OK:
+        return
+    msg = lib().dbs_strerror(status).decode()
+    if status in (DBS_EINVAL, DBS_EUNSUPPORTED):
+        raise ValueError(f"{msg} (status {status})")
+    raise DbsError(status, msg)
+
+
+def _shape(U, L):
+    import torch
+
+    for name, T in (("U", U), ("L", L)):
+        if not isinstance(T, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if T.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+        if T.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU")
+        if not T.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if U.shape != L.shape or U.dim() not in (2, 3) or U.shape[-1] != U.shape[-2]:
+        raise ValueError(f"U and L must be [n,n] or [batch,n,n] and equal; got "
+                         f"{tuple(U.shape)} and {tuple(L.shape)}")
+    if U.device != L.device:
+        raise ValueError("U and L must be on the same device")
+    n = U.shape[-1]
+    batch = 1 if U.dim() == 2 else U.shape[0]
+    return n, batch
+
+
+def _stream(T):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(T.device).cuda_stream)
+
+
+def _call(T, fn, *args):
+    import torch
+
+    with torch.cuda.device(T.device):
+        _raise(fn(*args))
+
+
+def smooth(U, L, algo: str = "auto") -> None:
+    """One full smoothing pass on U, L in place (enqueued on the current stream)."""
+    n, batch = _shape(U, L)
+    if algo not in _ALGOS:
+        raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
+    if n == 0 or batch == 0:
+        return
+    _call(U, lib().dbs_smooth_algo, U.data_ptr(), L.data_ptr(), n, batch, _stream(U),
+          _ALGOS[algo])
+
+
+def smooth_rounds(U, L, k_begin: int, k_end: int) -> None:
+    """Rounds k_begin..k_end-1 of a pass, one launch per round, in place."""
+    n, batch = _shape(U, L)
+    if n == 0 or batch == 0:
+        return
+    _call(U, lib().dbs_rounds, U.data_ptr(), L.data_ptr(), n, batch, int(k_begin),
+          int(k_end), _stream(U))
+
+
+def smooth_round(U, L, k: int) -> None:
+    """Round k only."""
+    smooth_rounds(U, L, k, k + 1)
+
+
+def check(U, L) -> int:
+    """Precondition flags (CHECK_FLAGS bits) of U, L; synchronises the stream."""
+    import torch
+
+    n, batch = _shape(U, L)
+    flags = torch.zeros(1, dtype=torch.int32, device=U.device)
+    if n == 0 or batch == 0:
+        return 0
+    _call(U, lib().dbs_check, U.data_ptr(), L.data_ptr(), n, batch, flags.data_ptr(),
+          _stream(U))
+    return int(flags.item()) & 0xFFFFFFFF
+
+
+def auto_algo(n: int, batch: int = 1) -> str:
+    code = lib().dbs_auto_algo(n, batch)
+    return {v: k for k, v in _ALGOS.items()}[code]

@@ -1,0 +1,75 @@
+// dbs_internal.h -- private declarations shared by the libdbs translation units.
+//
+// Every kernel here updates the bound matrices of GPU Gems 2, Ch. 43 "GPU
+// Computing for Protein Structure Prediction" (study notes), §2:
+//     U[i,j] <- min(U[i,j], U[i,k] + U[k,j])
+//     L[i,j] <- max(L[i,j], L[i,k] - U[k,j], L[k,j] - U[i,k])
+// for intermediate atoms k in Floyd-Warshall order (§3).
+//
+// Facts the kernels rely on (all under the preconditions stated in dbs.h):
+//  * Row k and column k do not change in round k (U[k,k] = L[k,k] = 0 and
+//    L >= 0 make every candidate for them equal to the old value), so a
+//    round can run in place instead of on the notes' §4 front/back buffers,
+//    cells of a round can run in any order, and the lower update may read U
+//    before or after the round's upper update.
+//  * Symmetry is preserved exactly (fp add and max are commutative), so
+//    U[i,k] = U[k,i]: row k alone supplies both operands of a round.
+//  * On the 2^-6 grid every candidate is exact, so blocked schedules and
+//    merged rounds give the same bits as the plain round order.
+//  * Padding: an out-of-range atom p is given U = +inf and L = 0.  Then
+//    every candidate through p is +inf (upper) or -inf (lower), so padded
+//    rows, columns and intermediates never change a real cell.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dbs {
+
+constexpr float kInf = __builtin_inff();
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// One intermediate atom applied to one cell:
+//   (u, l) <- (min(u, cu + ru), max(l, cl - ru, rl - cu))
+// where cu/cl = U/L[i,k] and ru/rl = U/L[k,j].
+__device__ __forceinline__ void relax1(float &u, float &l, float cu, float cl, float ru,
+                                       float rl) {
+  u = fminf(u, cu + ru);
+  l = fmaxf(fmaxf(l, cl - ru), rl - cu);
+}
+
+// Two intermediate atoms k0, k1 applied to one cell (folds into 3-input
+// min/max instructions).  Same result as relax1(k0) then relax1(k1).
+__device__ __forceinline__ void relax2(float &u, float &l, float cu0, float cl0, float ru0,
+                                       float rl0, float cu1, float cl1, float ru1, float rl1) {
+  u = fminf(fminf(u, cu0 + ru0), cu1 + ru1);
+  l = fmaxf(fmaxf(l, cl0 - ru0), rl0 - cu0);
+  l = fmaxf(fmaxf(l, cl1 - ru1), rl1 - cu1);
+}
+
+// Largest molecule the single-workgroup path holds (4x4 cells per thread,
+// upper-triangle tiles only, at most 1024 threads).
+constexpr int kSmallMaxN = 176;
+
+// Launchers (host side).  They enqueue on `s` and return the first launch
+// error, if any.
+hipError_t launch_round(float *U, float *L, int64_t n, int64_t batch, int64_t k, hipStream_t s);
+hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, hipStream_t s);
+hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStream_t s);
+hipError_t launch_check(const float *U, const float *L, int64_t n, int64_t batch,
+                        uint32_t *flags, hipStream_t s);
+
+// Single-workgroup Floyd-Warshall over an m x m symmetric block (m <= kSmallMaxN)
+// at element offset `off` of each molecule (row stride `ld`, molecule stride
+// `mstride`); grid = molecules.  Used for whole small molecules and for the
+// diagonal tile of the blocked pass.
+hipError_t launch_small_block(float *U, float *L, int64_t ld, int64_t mstride, int64_t off,
+                              int m, int64_t batch, hipStream_t s);
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Grid dimensions above this are folded into in-kernel loops.
+constexpr int64_t kMaxGridYZ = 65535;
+
+}  // namespace dbs

@@ -1,0 +1,89 @@
+// round.hip -- one Floyd-Warshall round k over every pair (i,j), in place.
+//
+// This is the round structure of GPU Gems 2, Ch. 43 notes, §3-§4: one
+// launch per intermediate atom k covering the whole matrix, each cell written
+// by exactly one thread.  The notes' ping-pong buffers are not needed: row k
+// and column k are unchanged by round k, so the in-place result is identical.
+// Each thread owns four consecutive columns of one row (the notes' RGBA
+// packing of four neighbouring entries, §4) and reads the broadcast value of
+// column k of its row once.
+//
+// Bound by HBM: per cell and round it reads U[i,j], L[i,j] and writes them
+// back (16 bytes); row k (8n bytes) stays in cache.
+#include "dbs_internal.h"
+
+namespace dbs {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Vector path: n % 4 == 0 and both base pointers 16-byte aligned.
+__global__ __launch_bounds__(kThreads) void k_round_vec(float *__restrict__ U,
+                                                        float *__restrict__ L, int64_t n,
+                                                        int64_t batch, int64_t k) {
+  const int64_t n4 = n >> 2;
+  const int64_t j4 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j4 >= n4) return;
+  const int64_t nn = n * n;
+  for (int64_t b = blockIdx.z; b < batch; b += gridDim.z) {
+    float *Ub = U + b * nn;
+    float *Lb = L + b * nn;
+    const float4 ru = reinterpret_cast<const float4 *>(Ub + k * n)[j4];
+    const float4 rl = reinterpret_cast<const float4 *>(Lb + k * n)[j4];
+    for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+      if (i == k) continue;  // row k is unchanged by round k
+      const float cu = Ub[i * n + k];
+      const float cl = Lb[i * n + k];
+      float4 *pu = reinterpret_cast<float4 *>(Ub + i * n) + j4;
+      float4 *pl = reinterpret_cast<float4 *>(Lb + i * n) + j4;
+      float4 u = *pu, l = *pl;
+      relax1(u.x, l.x, cu, cl, ru.x, rl.x);
+      relax1(u.y, l.y, cu, cl, ru.y, rl.y);
+      relax1(u.z, l.z, cu, cl, ru.z, rl.z);
+      relax1(u.w, l.w, cu, cl, ru.w, rl.w);
+      *pu = u;
+      *pl = l;
+    }
+  }
+}
+
+// Scalar path: any n, any 4-byte alignment.
+__global__ __launch_bounds__(kThreads) void k_round_scalar(float *__restrict__ U,
+                                                           float *__restrict__ L, int64_t n,
+                                                           int64_t batch, int64_t k) {
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= n) return;
+  const int64_t nn = n * n;
+  for (int64_t b = blockIdx.z; b < batch; b += gridDim.z) {
+    float *Ub = U + b * nn;
+    float *Lb = L + b * nn;
+    const float ru = Ub[k * n + j];
+    const float rl = Lb[k * n + j];
+    for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+      if (i == k) continue;
+      const float cu = Ub[i * n + k];
+      const float cl = Lb[i * n + k];
+      float u = Ub[i * n + j], l = Lb[i * n + j];
+      relax1(u, l, cu, cl, ru, rl);
+      Ub[i * n + j] = u;
+      Lb[i * n + j] = l;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_round(float *U, float *L, int64_t n, int64_t batch, int64_t k,
+                        hipStream_t s) {
+  const bool vec = (n % 4 == 0) && aligned16(U) && aligned16(L);
+  const int64_t cols = vec ? n / 4 : n;
+  dim3 grid((unsigned)ceil_div(cols, kThreads), (unsigned)(n < kMaxGridYZ ? n : kMaxGridYZ),
+            (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ));
+  if (vec)
+    k_round_vec<<<grid, kThreads, 0, s>>>(U, L, n, batch, k);
+  else
+    k_round_scalar<<<grid, kThreads, 0, s>>>(U, L, n, batch, k);
+  return hipGetLastError();
+}
+
+}  // namespace dbs

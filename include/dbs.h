@@ -1,0 +1,139 @@
+/*
+ * dbs.h -- C ABI of libdbs: distance-bound triangle smoothing on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (GPU Gems 2, Ch. 43 "GPU Computing for Protein Structure
+ * Prediction", study notes):
+ *   - §1: a molecule of n atoms is the complete graph K_n.  Pair (i,j) has
+ *     an upper bound U[i,j] and a lower bound L[i,j] on its distance; the
+ *     two bounds live in two dense n x n matrices.
+ *   - §2: through an intermediate atom k the bounds tighten as
+ *         U[i,j] <- min(U[i,j], U[i,k] + U[k,j])
+ *         L[i,j] <- max(L[i,j], L[i,k] - U[k,j], L[k,j] - U[i,k])
+ *     with the upper bounds tightened before the lower bounds read them.
+ *   - §3: Floyd-Warshall order: rounds k = 0..n-1 in sequence, all pairs of
+ *     a round independent, each round seeing the whole previous round.
+ * One "pass" is all n rounds.  The library runs a pass on a batch of
+ * independent molecules, in place.
+ *
+ * Data layout (all entry points): U and L are device pointers to
+ * [batch][n][n] float32, row-major, contiguous, batch stride n*n.  The
+ * caller allocates and owns them (e.g. torch tensors); the library keeps no
+ * reference after a call returns and allocates no device memory.  U and L
+ * must not overlap.  4-byte alignment is enough; 16-byte aligned rows take
+ * vector loads.
+ *
+ * Preconditions for exact results (dbs_check tests the per-entry ones on
+ * the device; none is tested by the smoothing calls):
+ *   - U and L bit-for-bit symmetric, both diagonals +0.0;
+ *   - every value finite, 0 <= L, a multiple of 2^-6 with |x| < 2^17, and
+ *     no -0.0.  On that grid every sum and difference of two bounds is
+ *     exact in fp32 (32-bit IEEE float, as in the notes' §6), so every
+ *     schedule reaches the same bits;
+ *   - the bounds are consistent: no L[i,j] exceeds the shortest-path upper
+ *     bound between i and j.  Sound bounds (ones that contain the distances
+ *     of some real coordinates) are always consistent.  A pass over
+ *     inconsistent bounds still returns the exact shortest-path upper
+ *     bounds, leaves L > U somewhere (which dbs_check on the result
+ *     reports), and leaves the lower bounds unspecified.
+ * Violating a precondition never causes an out-of-bounds access.
+ *
+ * Execution: every call validates its arguments on the host, then enqueues
+ * kernels on `stream` (a hipStream_t; NULL means the null stream) and
+ * returns without synchronising.  Faults of enqueued kernels surface at the
+ * caller's next synchronisation, as usual in HIP.  Calls on different
+ * streams are independent; calls that touch the same matrices must be
+ * ordered by the caller.  The library is thread-safe.
+ *
+ * Status codes (every int-returning entry point):
+ */
+#ifndef DBS_H
+#define DBS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DBS_OK 0           /* success                                         */
+#define DBS_EINVAL (-1)    /* bad argument; nothing was enqueued              */
+#define DBS_EDEVICE (-2)   /* no HIP device, or the current device is not gfx950 */
+#define DBS_ELAUNCH (-3)   /* the HIP runtime rejected a launch               */
+#define DBS_EUNSUPPORTED (-4) /* the requested algorithm cannot run this shape */
+
+/* Algorithms for dbs_smooth_algo.  All of them produce the same bits. */
+#define DBS_ALGO_AUTO 0    /* LDS when it fits, else BLOCKED                  */
+#define DBS_ALGO_PERK 1    /* one launch per round k (the notes' §3-§4 round
+                              structure, in place instead of front/back buffers) */
+#define DBS_ALGO_LDS 2     /* one workgroup per molecule runs the whole pass;
+                              n <= dbs_lds_max_n()                            */
+#define DBS_ALGO_BLOCKED 3 /* three-phase blocked pass (diagonal tile, panel,
+                              remaining tiles), symmetric tile schedule       */
+
+/*
+ * dbs_smooth -- one full smoothing pass (rounds k = 0..n-1) on every molecule,
+ * in place.  Same as dbs_smooth_algo(..., DBS_ALGO_AUTO).
+ *   U, L   device pointers, [batch][n][n] float32, read and written.
+ *   n      atoms per molecule, >= 1 (n = 1 is a no-op).
+ *   batch  number of molecules, >= 1.
+ *   stream hipStream_t to enqueue on (NULL = null stream).
+ * Returns DBS_OK, DBS_EINVAL (null pointer, n < 1, batch < 1, a size that
+ * overflows 64-bit byte counts, n >= 2^31, or overlapping U/L),
+ * DBS_EDEVICE or DBS_ELAUNCH.
+ */
+int dbs_smooth(float *U, float *L, int64_t n, int64_t batch, void *stream);
+
+/*
+ * dbs_smooth_algo -- dbs_smooth with an explicit algorithm (DBS_ALGO_*).
+ * DBS_EUNSUPPORTED if `algo` is DBS_ALGO_LDS and n > dbs_lds_max_n();
+ * DBS_EINVAL for an unknown `algo`.
+ */
+int dbs_smooth_algo(float *U, float *L, int64_t n, int64_t batch, void *stream,
+                    int algo);
+
+/*
+ * dbs_rounds -- rounds k_begin..k_end-1 of a pass on every molecule, one
+ * launch per round (the per-round state after round k_end-1 equals that of
+ * the notes' §4 front/back-buffer scheme).  0 <= k_begin <= k_end <= n,
+ * else DBS_EINVAL.  k_begin == k_end enqueues nothing.
+ */
+int dbs_rounds(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
+               int64_t k_end, void *stream);
+
+/*
+ * dbs_check -- test the per-entry preconditions on the device in O(n^2).
+ * ORs DBS_CHECK_* bits into *d_flags (a device pointer to one uint32 that
+ * the caller zeroes beforehand and reads after synchronising).  Run it on
+ * the output of a pass to detect inconsistent bounds (DBS_CHECK_L_GT_U).
+ * Same argument errors as dbs_smooth (d_flags must be non-null).
+ */
+int dbs_check(const float *U, const float *L, int64_t n, int64_t batch,
+              uint32_t *d_flags, void *stream);
+
+#define DBS_CHECK_ASYM 1u        /* U or L not bit-for-bit symmetric          */
+#define DBS_CHECK_DIAG 2u        /* a diagonal entry is not +0.0              */
+#define DBS_CHECK_NONFINITE 4u   /* NaN or infinity                           */
+#define DBS_CHECK_L_GT_U 8u      /* L[i,j] > U[i,j]                           */
+#define DBS_CHECK_L_NEG 16u      /* L[i,j] < 0                                */
+#define DBS_CHECK_UNQUANT 32u    /* not a multiple of 2^-6                    */
+#define DBS_CHECK_RANGE 64u      /* |x| >= 2^17                               */
+#define DBS_CHECK_NEGZERO 128u   /* -0.0                                      */
+
+/* Largest n the LDS algorithm accepts. */
+int dbs_lds_max_n(void);
+
+/* The algorithm DBS_ALGO_AUTO picks for this shape (n, batch >= 1). */
+int dbs_auto_algo(int64_t n, int64_t batch);
+
+/* Static description of a status code (never NULL). */
+const char *dbs_strerror(int status);
+
+/* Library version, 0xMMmmpp. */
+int dbs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBS_H */

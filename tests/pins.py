@@ -194,3 +194,35 @@ def variant_blocked(Ui: np.ndarray, Li: np.ndarray, B: int):
                     (cl[:, :, None] - ru[None, :, :]).max(1),
                     (rl[None, :, :] - cu[:, :, None]).max(1)))
     return U, L
+
+
+def sssp_dense(U, sources) -> np.ndarray:
+    """Textbook O(n^2) Dijkstra from each source over the dense weights U.
+
+    float64 (exact on the grid); returns [len(sources), n] shortest-path
+    lengths.  All sources advance together, one settled vertex per step.
+    """
+    W = np.asarray(U)
+    n = W.shape[0]
+    S = len(sources)
+    dist = np.full((S, n), np.inf)
+    done = np.zeros((S, n), dtype=bool)
+    rows = np.arange(S)
+    dist[rows, list(sources)] = 0.0
+    for _ in range(n):
+        cand = np.where(done, np.inf, dist)
+        u = cand.argmin(axis=1)
+        done[rows, u] = True
+        np.minimum(dist, dist[rows, u][:, None] + W[u].astype(np.float64), out=dist)
+    return dist
+
+
+def lower_pair(L, Us_i, Us_j) -> float:
+    """L*[i,j] = max_{k,l} L[k,l] - U*[i,k] - U*[l,j] for one pair, from the
+    shortest-path rows of i and j (U* symmetric).  float64, exact on the grid."""
+    best = -np.inf
+    n = L.shape[0]
+    for s in range(0, n, 2048):
+        blk = L[s:s + 2048].astype(np.float64) - Us_i[s:s + 2048, None] - Us_j[None, :]
+        best = max(best, float(blk.max()))
+    return best

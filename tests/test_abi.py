@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import distance_geometry_bound_amd as dgb
+from distance_geometry_bound_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dbs.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dbs_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = dgb.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (DBS_[A-Z_]+) \(?(-?\d+)u?\)?", text))
+    assert int(consts["DBS_OK"]) == _lib.DBS_OK
+    assert int(consts["DBS_EINVAL"]) == _lib.DBS_EINVAL
+    assert int(consts["DBS_EDEVICE"]) == _lib.DBS_EDEVICE
+    assert int(consts["DBS_ELAUNCH"]) == _lib.DBS_ELAUNCH
+    assert int(consts["DBS_EUNSUPPORTED"]) == _lib.DBS_EUNSUPPORTED
+    assert int(consts["DBS_ALGO_PERK"]) == _lib.ALGO_PERK
+    assert int(consts["DBS_ALGO_LDS"]) == _lib.ALGO_LDS
+    assert int(consts["DBS_ALGO_BLOCKED"]) == _lib.ALGO_BLOCKED
+    for k, v in _lib.CHECK_FLAGS.items():
+        assert int(consts["DBS_CHECK_" + k.upper().replace("NONFINITE", "NONFINITE")]) == v
+
+
+def test_static_queries():
+    L = dgb.lib()
+    assert L.dbs_version() == 0x000100
+    assert L.dbs_lds_max_n() >= 128
+    assert L.dbs_auto_algo(128, 1) == _lib.ALGO_LDS
+    assert L.dbs_auto_algo(12288, 1) == _lib.ALGO_BLOCKED
+    assert L.dbs_strerror(-1) == b"invalid argument"
+    assert L.dbs_strerror(12345) == b"unknown status"
+
+
+# host-side argument validation: fake, never dereferenced addresses
+A, B = 0x10000000, 0x20000000
+
+
+@pytest.mark.parametrize("args", [
+    (0, B, 4, 1), (A, 0, 4, 1), (A, B, 0, 1), (A, B, -3, 1), (A, B, 4, 0),
+    (A, B, 1 << 31, 1), (A, B, 1 << 20, 1 << 40), (A, A + 32, 4, 1), (A + 2, B, 4, 1),
+])
+def test_smooth_rejects_bad_arguments(args):
+    L = dgb.lib()
+    assert L.dbs_smooth(*args, None) == _lib.DBS_EINVAL
+    assert L.dbs_smooth_algo(*args, None, 0) == _lib.DBS_EINVAL
+
+
+def test_rounds_and_algo_range_checks():
+    L = dgb.lib()
+    assert L.dbs_rounds(A, B, 8, 1, 5, 4, None) == _lib.DBS_EINVAL
+    assert L.dbs_rounds(A, B, 8, 1, -1, 4, None) == _lib.DBS_EINVAL
+    assert L.dbs_rounds(A, B, 8, 1, 0, 9, None) == _lib.DBS_EINVAL
+    assert L.dbs_smooth_algo(A, B, 8, 1, None, 7) == _lib.DBS_EINVAL
+    assert L.dbs_smooth_algo(A, B, 1000, 1, None, _lib.ALGO_LDS) == _lib.DBS_EUNSUPPORTED
+    assert L.dbs_check(A, B, 8, 1, None, None) == _lib.DBS_EINVAL
+
+
+def test_no_device_is_reported():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = dgb.lib()
+    assert L.dbs_smooth(A, B, 8, 1, None) == _lib.DBS_EDEVICE
+    assert L.dbs_rounds(A, B, 8, 1, 0, 1, None) == _lib.DBS_EDEVICE
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+
+    U = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        dgb.smooth(U, U.clone())
+    with pytest.raises(TypeError):
+        dgb.smooth(U.double(), U.double())

@@ -264,3 +264,21 @@ def test_rejects_bad_arguments():
         oracle.rounds(U0, L0, 3, 2)
     with pytest.raises(ValueError):
         oracle.rounds(U0, L0, 0, 6)
+
+
+# ------------------------------------------------- pins used at full size
+def test_sssp_dense_matches_scipy():
+    U0, L0, _ = gen.random_sound_bounds(150, seed=21, box=30.0)
+    src = [0, 7, 149]
+    assert np.array_equal(pins.sssp_dense(U0, src), pins.apsp_scipy(U0)[src])
+
+
+def test_lower_pair_matches_oracle():
+    m = gen.make_molecule(300, seed=22, cutoff=6.0, p=0.5)
+    U, L = oracle.smooth(m.U, m.L)
+    src = [3, 100, 299]
+    D = pins.sssp_dense(m.U, src)
+    assert np.array_equal(D, U[src].astype(np.float64))
+    for a in range(3):
+        for b in range(3):
+            assert pins.lower_pair(m.L, D[a], D[b]) == float(L[src[a], src[b]])
