@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark: one full distance-bound smoothing pass per step on one MI355X.
+
+A step restores the synthetic input (device-to-device copy, kept inside the
+timed region) and runs one pass (all rounds k = 0..n-1) through the C ABI,
+dbs_smooth.  The default workload is n = 12288: 48 self-avoiding chains of
+256 atoms packed in a 90 A sphere (dense fp32 U and L, 1.2 GB together).
+
+Printed: one JSON line with
+  value        bound-updates/s = 2 n^3 batch / (seconds per step)
+  pct_fp32_valu_peak  = 6 n^3 batch / t / 157.3e12 (3 ops per bound-update)
+  roofline     the phase-3 tile kernel (k_tiles): executed algorithmic ops per
+               launch / mean launch time from HIP events (dbs_smooth_profiled)
+  perk         the per-round kernel: HBM bytes of the round formulation
+               (16 B per cell per round) / mean round time
+  cpu_baseline the CPU reference (oracle) on a bounded prefix of rounds of
+               the same workload, on this host's cores
+Run with --gpus N > 1 and it exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bound-updates/s (2·n³ per pass) + % fp32 VALU peak; HBM GB/s per-k kernel"
+FP32_VALU_PEAK = 157.3e12       # MI355X fp32 vector, ops/s
+HBM_PEAK = 8.0e12               # MI355X HBM3E, bytes/s
+OPS_PER_TRIPLE = 6              # 1 add + 1 min (upper), 2 sub + 2 max (lower)
+TILE, BK = 128, 64              # blocked-path geometry (csrc/blocked.hip)
+COUNTERS = os.path.join(ROOT, "profiles", "k_tiles_n12288_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "distance_geometry_bound_amd", "csrc", "blocked.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="n12288",
+                    choices=["n128", "n1024", "b64n500", "n4096", "n12288"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "blocked", "lds", "perk"])
+    ap.add_argument("--perk-rounds", type=int, default=64,
+                    help="rounds of the per-round kernel to time (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample (0 = skip)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy 5 times (counter scale)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+
+    dev = torch.device("cuda:0")
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_calibration_bytes": nbytes, "dispatches": 5}), flush=True)
+
+
+def tiles_ops_per_launch(n, batch):
+    """Executed (i,j,k) triples of one phase-3 launch x 6 ops (full k-block)."""
+    T = -(-n // TILE)
+    return OPS_PER_TRIPLE * batch * (T * (T + 1) // 2) * TILE * TILE * BK
+
+
+def counters_traffic(n, batch):
+    """HBM bytes per phase-3 launch from the committed counter run, if the
+    kernel source is unchanged since it was taken; else None."""
+    try:
+        rec = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha or rec.get("n") != n or rec.get("batch") != batch:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(W, target_s):
+    """Time the oracle on a prefix of rounds of the same workload."""
+    import ctypes
+
+    import numpy as np
+
+    import oracle
+
+    lib = oracle.load()
+    threads = oracle.max_threads()
+    f32p = ctypes.POINTER(ctypes.c_float)
+    U = np.array(W.U[:1], copy=True)
+    L = np.array(W.L[:1], copy=True)
+
+    def run(rounds):
+        t0 = time.perf_counter()
+        rc = lib.dbs_oracle_rounds(U.ctypes.data_as(f32p), L.ctypes.data_as(f32p), W.n, 1, 0,
+                                   rounds, threads)
+        dt = time.perf_counter() - t0
+        assert rc == 0
+        return dt
+
+    # grow the prefix until it costs a quarter of the target, then scale
+    rounds = 4
+    t = run(rounds)
+    while t < 0.25 * target_s and rounds < W.n:
+        rounds = min(W.n, rounds * 4)
+        t = run(rounds)
+    rounds = int(max(1, min(W.n, round(rounds * target_s / max(t, 1e-6)))))
+    t = run(rounds)
+    bu = 2.0 * W.n * W.n * rounds
+    return {"value": bu / t, "unit": "bound-updates/s", "cores": threads, "kind": "oracle",
+            "sample": f"rounds 0..{rounds - 1} of the {W.name} pass on molecule 0 "
+                      f"({rounds} of {W.n} rounds, {t:.1f} s)",
+            "seconds": t}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import distance_geometry_bound_amd as dgb
+    from distance_geometry_bound_amd import gen
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    W = gen.make_workload(args.workload)
+    n, batch = W.n, W.batch
+    print(f"[bench] workload {W.name}: n={n} batch={batch} generated in "
+          f"{time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    U0 = torch.from_numpy(W.U).to(dev)
+    L0 = torch.from_numpy(W.L).to(dev)
+    U = torch.empty_like(U0)
+    L = torch.empty_like(L0)
+    algo = args.algo if args.algo != "auto" else dgb.auto_algo(n, batch)
+
+    def step():
+        U.copy_(U0)
+        L.copy_(L0)
+        dgb.smooth(U, L, algo=algo)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    dt = (time.perf_counter() - t0) / max(args.steps, 1)
+    print(f"[bench] timed {args.steps} steps: {dt * 1e3:.2f} ms/step", file=sys.stderr, flush=True)
+    triples = float(n) ** 3 * batch
+    out = {
+        "metric": METRIC,
+        "value": 2.0 * triples / dt,
+        "unit": "bound-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": W.name, "n": n, "batch": batch, "algo": algo,
+                   "step": "restore U,L (device copy) + one full pass"},
+        "pct_fp32_valu_peak": OPS_PER_TRIPLE * triples / dt / FP32_VALU_PEAK,
+    }
+
+    # per-kernel device times from HIP events around every launch of a pass
+    prof_steps = max(1, min(args.steps, 3))
+    tot = {k: [0, 0.0] for k in dgb.PROF_KINDS}
+    for _ in range(prof_steps):
+        U.copy_(U0)
+        L.copy_(L0)
+        p = dgb.smooth_profiled(U, L, algo=algo)
+        for k, (c, ms) in p.items():
+            tot[k][0] += c
+            tot[k][1] += ms
+    out["phases_ms_per_pass"] = {k: v[1] / prof_steps for k, v in tot.items() if v[0]}
+    out["launches_per_pass"] = {k: v[0] // prof_steps for k, v in tot.items() if v[0]}
+    if tot["tiles"][0]:
+        launch_ms = tot["tiles"][1] / tot["tiles"][0]
+        ops = tiles_ops_per_launch(n, batch)
+        achieved = ops / (launch_ms * 1e-3)
+        # the same launch produces results for the full square of cells
+        # outside the k-block (the lower half by symmetry)
+        dense_ops = OPS_PER_TRIPLE * batch * (n - BK) ** 2 * BK
+        traffic = counters_traffic(n, batch)
+        out["roofline"] = {
+            "bound": "alu", "kernel": "k_tiles",
+            "achieved": achieved / 1e12, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
+            "frac": achieved / FP32_VALU_PEAK,
+            "traffic": traffic,
+            "launch_ms": launch_ms, "launches": tot["tiles"][0],
+            "ops_per_launch": ops,
+            "frac_effective": dense_ops / (launch_ms * 1e-3) / FP32_VALU_PEAK,
+        }
+
+    if args.perk_rounds > 0:
+        R = min(args.perk_rounds, n)
+        U.copy_(U0)
+        L.copy_(L0)
+        s = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dgb.smooth_rounds(U, L, 0, 1)            # warm
+        e0.record(s)
+        dgb.smooth_rounds(U, L, 1, 1 + R if 1 + R <= n else n)
+        e1.record(s)
+        torch.cuda.synchronize(dev)
+        R = min(R, n - 1)
+        if R > 0:
+            ms = e0.elapsed_time(e1) / R
+            gbps = 16.0 * n * n * batch / (ms * 1e-3) / 1e9
+            out["perk"] = {"kernel": "k_round_vec" if n % 4 == 0 else "k_round_scalar",
+                           "rounds": R, "ms_per_round": ms, "GBps": gbps,
+                           "frac_hbm": gbps * 1e9 / HBM_PEAK,
+                           "bytes_per_round": 16 * n * n * batch}
+
+    if not args.no_cpu and args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,7 +7,7 @@ imported on machines without a GPU.
 """
 __version__ = "0.1.0"
 
-_API = ("smooth", "smooth_round", "smooth_rounds", "check", "lib", "DbsError", "auto_algo",
+_API = ("smooth", "smooth_round", "smooth_rounds", "check", "lib", "DbsError", "auto_algo", "smooth_profiled", "PROF_KINDS",
         "ALGO_AUTO", "ALGO_PERK", "ALGO_LDS", "ALGO_BLOCKED", "CHECK_FLAGS")
 
 

@@ -24,8 +24,10 @@ CHECK_FLAGS = {
 
 DBS_OK, DBS_EINVAL, DBS_EDEVICE, DBS_ELAUNCH, DBS_EUNSUPPORTED = 0, -1, -2, -3, -4
 
-EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_rounds", "dbs_check", "dbs_lds_max_n",
-           "dbs_auto_algo", "dbs_strerror", "dbs_version")
+EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
+           "dbs_lds_max_n", "dbs_auto_algo", "dbs_strerror", "dbs_version")
+
+PROF_KINDS = ("round", "small", "panel", "tiles", "mirror")
 
 
 class DbsError(RuntimeError):
@@ -48,12 +50,14 @@ def lib():
         vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.dbs_smooth.argtypes = [vp, vp, i64, i64, vp]
         L.dbs_smooth_algo.argtypes = [vp, vp, i64, i64, vp, c_int]
+        L.dbs_smooth_profiled.argtypes = [vp, vp, i64, i64, vp, c_int,
+                                          ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
         L.dbs_rounds.argtypes = [vp, vp, i64, i64, i64, i64, vp]
         L.dbs_check.argtypes = [vp, vp, i64, i64, vp, vp]
         L.dbs_auto_algo.argtypes = [i64, i64]
         L.dbs_strerror.argtypes = [c_int]
         L.dbs_strerror.restype = ctypes.c_char_p
-        for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_rounds", "dbs_check",
+        for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
                   "dbs_lds_max_n", "dbs_auto_algo", "dbs_version"):
             getattr(L, f).restype = c_int
         _lib = L
@@ -113,6 +117,20 @@ def smooth(U, L, algo: str = "auto") -> None:
         return
     _call(U, lib().dbs_smooth_algo, U.data_ptr(), L.data_ptr(), n, batch, _stream(U),
           _ALGOS[algo])
+
+
+def smooth_profiled(U, L, algo: str = "auto") -> dict:
+    """smooth() with HIP events around every kernel launch; synchronises and
+    returns {kind: (launches, total_ms)} for the kernel kinds in PROF_KINDS."""
+    n, batch = _shape(U, L)
+    if algo not in _ALGOS:
+        raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
+    counts = (ctypes.c_int64 * len(PROF_KINDS))()
+    ms = (ctypes.c_double * len(PROF_KINDS))()
+    if n > 0 and batch > 0:
+        _call(U, lib().dbs_smooth_profiled, U.data_ptr(), L.data_ptr(), n, batch, _stream(U),
+              _ALGOS[algo], counts, ms)
+    return {k: (int(counts[i]), float(ms[i])) for i, k in enumerate(PROF_KINDS)}
 
 
 def smooth_rounds(U, L, k_begin: int, k_end: int) -> None:

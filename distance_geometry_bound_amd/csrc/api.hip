@@ -43,7 +43,8 @@ int validate(const void *U, const void *L, int64_t n, int64_t batch) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? DBS_OK : DBS_ELAUNCH; }
 
-int run(float *U, float *L, int64_t n, int64_t batch, void *stream, int algo) {
+int run(float *U, float *L, int64_t n, int64_t batch, void *stream, int algo,
+        dbs::Prof *prof = nullptr) {
   int st = validate(U, L, n, batch);
   if (st != DBS_OK) return st;
   if (algo < DBS_ALGO_AUTO || algo > DBS_ALGO_BLOCKED) return DBS_EINVAL;
@@ -56,13 +57,14 @@ int run(float *U, float *L, int64_t n, int64_t batch, void *stream, int algo) {
   switch (algo) {
     case DBS_ALGO_PERK: {
       hipError_t e = hipSuccess;
-      for (int64_t k = 0; k < n && e == hipSuccess; ++k) e = dbs::launch_round(U, L, n, batch, k, s);
+      for (int64_t k = 0; k < n && e == hipSuccess; ++k)
+        e = dbs::launch_round(U, L, n, batch, k, s, prof);
       return status_of(e);
     }
     case DBS_ALGO_LDS:
-      return status_of(dbs::launch_small(U, L, n, batch, s));
+      return status_of(dbs::launch_small(U, L, n, batch, s, prof));
     default:
-      return status_of(dbs::launch_blocked(U, L, n, batch, s));
+      return status_of(dbs::launch_blocked(U, L, n, batch, s, prof));
   }
 }
 
@@ -76,6 +78,26 @@ int dbs_smooth(float *U, float *L, int64_t n, int64_t batch, void *stream) {
 
 int dbs_smooth_algo(float *U, float *L, int64_t n, int64_t batch, void *stream, int algo) {
   return run(U, L, n, batch, stream, algo);
+}
+
+int dbs_smooth_profiled(float *U, float *L, int64_t n, int64_t batch, void *stream, int algo,
+                        int64_t *counts, double *ms) {
+  if (!counts || !ms) return DBS_EINVAL;
+  for (int i = 0; i < DBS_PROF_KINDS; ++i) {
+    counts[i] = 0;
+    ms[i] = 0.0;
+  }
+  dbs::Prof prof;
+  int st = run(U, L, n, batch, stream, algo, &prof);
+  if (st != DBS_OK) return st;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return DBS_ELAUNCH;
+  for (const auto &m : prof.marks) {
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, m.start, m.stop) != hipSuccess) return DBS_ELAUNCH;
+    counts[m.kind] += 1;
+    ms[m.kind] += t;
+  }
+  return DBS_OK;
 }
 
 int dbs_rounds(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,

@@ -349,21 +349,10 @@ __global__ __launch_bounds__(kThreads) void k_mirror(float *__restrict__ U, floa
   }
 }
 
-template <typename T>
-struct ident {
-  using type = T;
-};
-
-template <typename... KArgs>
-hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
-                  typename ident<KArgs>::type... args) {
-  void *ptrs[] = {(void *)&args...};
-  return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, s);
-}
-
 }  // namespace
 
-hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStream_t s) {
+hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStream_t s,
+                          Prof *prof) {
   if (n <= 1) return hipSuccess;
   const int64_t TB = ceil_div(n, BK);    // k-blocks
   const int64_t T = ceil_div(n, TILE);   // phase-3 tiles per side
@@ -374,18 +363,19 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStrea
   for (int64_t K = 0; K < TB && e == hipSuccess; ++K) {
     const int64_t k0 = K * BK;
     const int bK = (int)(n - k0 < BK ? n - k0 : BK);
-    e = launch_small_block(U, L, n, nn, k0 * n + k0, bK, batch, s);
+    e = launch_small_block(U, L, n, nn, k0 * n + k0, bK, batch, s, prof);
     if (e != hipSuccess || TB == 1) break;
     const dim3 g2((unsigned)(TB - 1), gy);
-    e = vec ? launch(k_panel<true>, g2, dim3(kThreads), s, U, L, n, batch, K)
-            : launch(k_panel<false>, g2, dim3(kThreads), s, U, L, n, batch, K);
+    e = launch(prof, kProfPanel, vec ? k_panel<true> : k_panel<false>, g2, dim3(kThreads), s, U,
+               L, n, batch, K);
     if (e != hipSuccess) break;
     const dim3 g3((unsigned)(T * (T + 1) / 2), gy);
-    e = vec ? launch(k_tiles<true>, g3, dim3(kThreads), s, U, L, n, batch, K)
-            : launch(k_tiles<false>, g3, dim3(kThreads), s, U, L, n, batch, K);
+    e = launch(prof, kProfTiles, vec ? k_tiles<true> : k_tiles<false>, g3, dim3(kThreads), s, U,
+               L, n, batch, K);
   }
   if (e == hipSuccess && T > 1)
-    e = launch(k_mirror, dim3((unsigned)(TB * TB), gy), dim3(kThreads), s, U, L, n, batch, TB);
+    e = launch(prof, kProfMirror, k_mirror, dim3((unsigned)(TB * TB), gy), dim3(kThreads), s, U,
+               L, n, batch, TB);
   return e;
 }
 

@@ -53,9 +53,8 @@ hipError_t launch_check(const float *U, const float *L, int64_t n, int64_t batch
   const int64_t total = n * n * batch;
   int64_t blocks = ceil_div(total, kThreads);
   if (blocks > 65536) blocks = 65536;
-  void *args[] = {(void *)&U, (void *)&L, (void *)&n, (void *)&batch, (void *)&flags};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&k_check), dim3((unsigned)blocks),
-                         dim3(kThreads), args, 0, s);
+  return launch(nullptr, 0, k_check, dim3((unsigned)blocks), dim3(kThreads), s, U, L, n, batch,
+                flags);
 }
 
 }  // namespace dbs

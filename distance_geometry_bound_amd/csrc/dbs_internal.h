@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace dbs {
 
 constexpr float kInf = __builtin_inff();
@@ -52,11 +54,64 @@ __device__ __forceinline__ void relax2(float &u, float &l, float cu0, float cl0,
 // upper-triangle tiles only, at most 1024 threads).
 constexpr int kSmallMaxN = 176;
 
+// Optional launch timing.  When a launcher is given a Prof, every kernel it
+// enqueues is bracketed by a pair of HIP events on the launch stream, tagged
+// with the kernel kind (the DBS_PROF_* numbering of dbs.h).
+struct Prof {
+  struct Mark {
+    int kind;
+    hipEvent_t start, stop;
+  };
+  std::vector<Mark> marks;
+  Prof() = default;
+  Prof(const Prof &) = delete;
+  Prof &operator=(const Prof &) = delete;
+  ~Prof() {
+    for (auto &m : marks) {
+      (void)hipEventDestroy(m.start);
+      (void)hipEventDestroy(m.stop);
+    }
+  }
+};
+
+enum ProfKind { kProfRound = 0, kProfSmall = 1, kProfPanel = 2, kProfTiles = 3, kProfMirror = 4 };
+
+template <typename T>
+struct ident {
+  using type = T;
+};
+
+// Launch `kernel` with by-value arguments (hipLaunchKernel returns the launch
+// status directly), optionally timed.
+template <typename... KArgs>
+hipError_t launch(Prof *prof, int kind, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                  hipStream_t s, typename ident<KArgs>::type... args) {
+  void *ptrs[] = {(void *)&args...};
+  if (!prof) return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, s);
+  Prof::Mark m{kind, nullptr, nullptr};
+  hipError_t e = hipEventCreate(&m.start);
+  if (e != hipSuccess) return e;
+  e = hipEventCreate(&m.stop);
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(m.start);
+    return e;
+  }
+  prof->marks.push_back(m);
+  if ((e = hipEventRecord(m.start, s)) != hipSuccess) return e;
+  if ((e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, s)) !=
+      hipSuccess)
+    return e;
+  return hipEventRecord(m.stop, s);
+}
+
 // Launchers (host side).  They enqueue on `s` and return the first launch
 // error, if any.
-hipError_t launch_round(float *U, float *L, int64_t n, int64_t batch, int64_t k, hipStream_t s);
-hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, hipStream_t s);
-hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStream_t s);
+hipError_t launch_round(float *U, float *L, int64_t n, int64_t batch, int64_t k, hipStream_t s,
+                        Prof *prof = nullptr);
+hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, hipStream_t s,
+                        Prof *prof = nullptr);
+hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStream_t s,
+                          Prof *prof = nullptr);
 hipError_t launch_check(const float *U, const float *L, int64_t n, int64_t batch,
                         uint32_t *flags, hipStream_t s);
 
@@ -65,7 +120,7 @@ hipError_t launch_check(const float *U, const float *L, int64_t n, int64_t batch
 // `mstride`); grid = molecules.  Used for whole small molecules and for the
 // diagonal tile of the blocked pass.
 hipError_t launch_small_block(float *U, float *L, int64_t ld, int64_t mstride, int64_t off,
-                              int m, int64_t batch, hipStream_t s);
+                              int m, int64_t batch, hipStream_t s, Prof *prof = nullptr);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -74,16 +74,13 @@ __global__ __launch_bounds__(kThreads) void k_round_scalar(float *__restrict__ U
 }  // namespace
 
 hipError_t launch_round(float *U, float *L, int64_t n, int64_t batch, int64_t k,
-                        hipStream_t s) {
+                        hipStream_t s, Prof *prof) {
   const bool vec = (n % 4 == 0) && aligned16(U) && aligned16(L);
   const int64_t cols = vec ? n / 4 : n;
   dim3 grid((unsigned)ceil_div(cols, kThreads), (unsigned)(n < kMaxGridYZ ? n : kMaxGridYZ),
             (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ));
-  if (vec)
-    k_round_vec<<<grid, kThreads, 0, s>>>(U, L, n, batch, k);
-  else
-    k_round_scalar<<<grid, kThreads, 0, s>>>(U, L, n, batch, k);
-  return hipGetLastError();
+  return launch(prof, kProfRound, vec ? k_round_vec : k_round_scalar, grid, dim3(kThreads), s,
+                U, L, n, batch, k);
 }
 
 }  // namespace dbs

@@ -125,18 +125,19 @@ __global__ __launch_bounds__(1024) void k_small(float *__restrict__ U, float *__
 }  // namespace
 
 hipError_t launch_small_block(float *U, float *L, int64_t ld, int64_t mstride, int64_t off,
-                              int m, int64_t batch, hipStream_t s) {
+                              int m, int64_t batch, hipStream_t s, Prof *prof) {
   if (m <= 1) return hipSuccess;
   const int G = (m + 3) / 4;
   const int tiles = G * (G + 1) / 2;
   const int threads = (tiles + 63) / 64 * 64;
   const unsigned grid = (unsigned)(batch < 1048576 ? batch : 1048576);
-  k_small<<<grid, threads, 0, s>>>(U, L, ld, mstride, off, m, batch);
-  return hipGetLastError();
+  return launch(prof, kProfSmall, k_small, dim3(grid), dim3(threads), s, U, L, ld, mstride, off,
+                m, batch);
 }
 
-hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, hipStream_t s) {
-  return launch_small_block(U, L, n, n * n, 0, (int)n, batch, s);
+hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, hipStream_t s,
+                        Prof *prof) {
+  return launch_small_block(U, L, n, n * n, 0, (int)n, batch, s, prof);
 }
 
 }  // namespace dbs

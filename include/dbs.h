@@ -120,6 +120,25 @@ int dbs_check(const float *U, const float *L, int64_t n, int64_t batch,
 #define DBS_CHECK_RANGE 64u      /* |x| >= 2^17                               */
 #define DBS_CHECK_NEGZERO 128u   /* -0.0                                      */
 
+/*
+ * dbs_smooth_profiled -- dbs_smooth_algo with every kernel launch bracketed by
+ * a HIP event pair on `stream`; waits for the pass to finish (synchronises
+ * `stream`) and fills, per kernel kind DBS_PROF_*, the number of launches
+ * (counts[kind]) and their summed device time in milliseconds (ms[kind]).
+ *   counts, ms  host arrays of DBS_PROF_KINDS elements, written by the call.
+ * Same argument errors as dbs_smooth_algo; DBS_EINVAL if counts or ms is
+ * null.  The events add a few microseconds per launch; for measurement only.
+ */
+int dbs_smooth_profiled(float *U, float *L, int64_t n, int64_t batch, void *stream,
+                        int algo, int64_t *counts, double *ms);
+
+#define DBS_PROF_ROUND 0   /* per-round kernel                                 */
+#define DBS_PROF_SMALL 1   /* single-workgroup pass (whole molecule or diagonal tile) */
+#define DBS_PROF_PANEL 2   /* blocked phase 2: panel tiles                     */
+#define DBS_PROF_TILES 3   /* blocked phase 3: remaining tiles                 */
+#define DBS_PROF_MIRROR 4  /* blocked: final transposed copy                   */
+#define DBS_PROF_KINDS 5
+
 /* Largest n the LDS algorithm accepts. */
 int dbs_lds_max_n(void);
 

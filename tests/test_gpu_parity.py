@@ -207,7 +207,7 @@ def test_deterministic_and_side_stream():
 
 def test_unaligned_rows_take_the_scalar_path():
     n = 260                                   # n % 4 == 0, base misaligned by 4 bytes
-    U0, L0 = sound_input(n, 1, seed=9)
+    U0, L0, _ = gen.random_sound_bounds(n, seed=9, box=40.0)
     Ue, Le = oracle.smooth(U0, L0)
     for algo in ("blocked", "perk"):
         bu = torch.zeros(n * n + 1, device=DEV)
