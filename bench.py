@@ -9,8 +9,9 @@ dbs_smooth.  The default workload is n = 12288: 48 self-avoiding chains of
 Printed: one JSON line with
   value        bound-updates/s = 2 n^3 batch / (seconds per step)
   pct_fp32_valu_peak  = 6 n^3 batch / t / 157.3e12 (3 ops per bound-update)
-  roofline     the phase-3 tile kernel (k_tiles): executed algorithmic ops per
-               launch / mean launch time from HIP events (dbs_smooth_profiled)
+  roofline     the bulk phase-3 kernel (k_tiles): algorithmic ops of the cells a
+               launch stores / mean launch time from HIP events
+               (dbs_smooth_profiled on the launch stream)
   perk         the per-round kernel: HBM bytes of the round formulation
                (16 B per cell per round) / mean round time
   cpu_baseline the CPU reference (oracle) on a bounded prefix of rounds of
@@ -69,10 +70,30 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": nbytes, "dispatches": 5}), flush=True)
 
 
-def tiles_ops_per_launch(n, batch):
-    """Executed (i,j,k) triples of one phase-3 launch x 6 ops (full k-block)."""
+def tiles_units_per_pass(n, batch):
+    """(stored, dense) (i,j,k) triples of the bulk phase-3 kernel over one pass.
+
+    Launch K runs over every TILE x TILE tile with I <= J and stores every
+    cell outside band K (final after phase 2) and band K+1 (updated ahead by
+    the strip kernel; none for the last k-block).  `stored` counts those
+    cells x the launch's atoms; `dense` counts the full square of live rows
+    x live columns (the cells below the diagonal follow by symmetry)."""
     T = -(-n // TILE)
-    return OPS_PER_TRIPLE * batch * (T * (T + 1) // 2) * TILE * TILE * BK
+    TB = -(-n // BK)
+    stored = dense = 0
+    for K in range(TB):
+        bands = [(K * BK, min(n, K * BK + BK))]
+        if K + 1 < TB:
+            bands.append(((K + 1) * BK, min(n, K * BK + 2 * BK)))
+        r = []
+        for I in range(T):
+            lo, hi = I * TILE, min(n, I * TILE + TILE)
+            r.append(hi - lo - sum(max(0, min(hi, b1) - max(lo, b0)) for b0, b1 in bands))
+        S, Q = sum(r), sum(x * x for x in r)
+        bK = min(BK, n - K * BK)
+        stored += (S * S + Q) // 2 * bK
+        dense += S * S * bK
+    return stored * batch, dense * batch
 
 
 def counters_traffic(n, batch):
@@ -199,12 +220,11 @@ def main():
     out["phases_ms_per_pass"] = {k: v[1] / prof_steps for k, v in tot.items() if v[0]}
     out["launches_per_pass"] = {k: v[0] // prof_steps for k, v in tot.items() if v[0]}
     if tot["tiles"][0]:
+        launches = tot["tiles"][0] // prof_steps
         launch_ms = tot["tiles"][1] / tot["tiles"][0]
-        ops = tiles_ops_per_launch(n, batch)
+        stored, dense = tiles_units_per_pass(n, batch)
+        ops = OPS_PER_TRIPLE * stored / launches          # per launch, averaged over the pass
         achieved = ops / (launch_ms * 1e-3)
-        # the same launch produces results for the full square of cells
-        # outside the k-block (the lower half by symmetry)
-        dense_ops = OPS_PER_TRIPLE * batch * (n - BK) ** 2 * BK
         traffic = counters_traffic(n, batch)
         out["roofline"] = {
             "bound": "alu", "kernel": "k_tiles",
@@ -213,7 +233,8 @@ def main():
             "traffic": traffic,
             "launch_ms": launch_ms, "launches": tot["tiles"][0],
             "ops_per_launch": ops,
-            "frac_effective": dense_ops / (launch_ms * 1e-3) / FP32_VALU_PEAK,
+            "frac_effective": OPS_PER_TRIPLE * dense / launches / (launch_ms * 1e-3)
+                              / FP32_VALU_PEAK,
         }
 
     if args.perk_rounds > 0:

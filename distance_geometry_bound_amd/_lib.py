@@ -27,7 +27,7 @@ DBS_OK, DBS_EINVAL, DBS_EDEVICE, DBS_ELAUNCH, DBS_EUNSUPPORTED = 0, -1, -2, -3, 
 EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
            "dbs_lds_max_n", "dbs_auto_algo", "dbs_strerror", "dbs_version")
 
-PROF_KINDS = ("round", "small", "panel", "tiles", "mirror")
+PROF_KINDS = ("round", "small", "panel", "tiles", "mirror", "strip")
 
 
 class DbsError(RuntimeError):

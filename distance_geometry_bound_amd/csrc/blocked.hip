@@ -7,13 +7,14 @@
 // graph with no negative cycle, every candidate is exact on the 2^-6 grid, so
 // any partition of the rounds into blocks yields the same shortest paths.
 //
-// For k-block K (atoms k0..k0+bK-1):
+// For k-block K (atoms k0..k0+bK-1, "band K"):
 //   phase 1  the diagonal tile (K,K): a full pass over it, rounds in order
 //            (k_small, one workgroup per molecule);
-//   phase 2  every other tile on row K ("panel"): rounds in order, reading
+//   phase 2  every other tile of band K ("panel"): rounds in order, reading
 //            the final diagonal tile (k_panel, one workgroup per tile);
-//   phase 3  every remaining tile: all bK rounds at once from the finished
-//            panel (k_tiles).  This is where 1 - O(BK/n) of the work is.
+//   phase 3  every remaining cell: all bK rounds at once from the finished
+//            panel (k_tiles, plus k_strip for band K+1 when running ahead).
+//            This is where 1 - O(BK/n) of the work is.
 //
 // Symmetric schedule.  U and L stay exactly symmetric, so only the cells of
 // TILE x TILE tiles (I,J) with I <= J are kept current ("fresh"); tiles below
@@ -23,13 +24,15 @@
 // so phase 2 must leave all of row band K fresh: it updates each panel tile
 // from whichever orientation is fresh and writes both orientations.
 //
-// Phase 3 kernel: a 256-thread workgroup owns a 128x128 tile; each thread an
+// Phase 3 bulk kernel: a 256-thread workgroup owns a 128x128 tile; each thread an
 // 8x8 register tile (rows ty*4+{0..3} and 64+ty*4+{0..3}, same for columns,
 // so the LDS reads of a wave are contiguous).  The panel rows of the k-block
 // are staged through LDS in chunks of KC atoms.  Per atom and cell the VALU
 // does one add and one min for U, two subtracts and two max for L; pairs of
 // atoms fold into 3-input min/max.  No matrix cores: min-plus is not a
 // multiply-add contraction.
+#include <mutex>
+
 #include "dbs_internal.h"
 
 namespace dbs {
@@ -44,17 +47,40 @@ constexpr int kThreads = 256;
 // (k-block tile a, k-block tile b) is fresh under the symmetric schedule
 __device__ __forceinline__ bool fresh(int64_t a, int64_t b) { return a / RATIO <= b / RATIO; }
 
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ float4 inf4() { return make_float4(kInf, kInf, kInf, kInf); }
+__device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+
+// Four consecutive entries p[0..3]; entry q is used only if q < cnt, else the
+// neutral value `fill`.  VEC: p is 16-byte aligned and cnt is 0 or >= 4.
+// Branch-free: an entry that is not used is read from `safe` (any valid,
+// 16-byte aligned address) and replaced afterwards, so that the compiler can
+// issue a run of these loads back to back instead of one at a time.
+template <bool VEC>
+__device__ __forceinline__ float4 load4(const float *p, int cnt, float fill, const float *safe) {
+  if (VEC) {
+    const float4 v = *reinterpret_cast<const float4 *>(cnt >= 4 ? p : safe);
+    return cnt >= 4 ? v : make_float4(fill, fill, fill, fill);
+  }
+  const float x0 = *(cnt > 0 ? p : safe), x1 = *(cnt > 1 ? p + 1 : safe);
+  const float x2 = *(cnt > 2 ? p + 2 : safe), x3 = *(cnt > 3 ? p + 3 : safe);
+  return make_float4(cnt > 0 ? x0 : fill, cnt > 1 ? x1 : fill, cnt > 2 ? x2 : fill,
+                     cnt > 3 ? x3 : fill);
+}
+
+__device__ __forceinline__ int clamp4(int64_t left) { return left < 0 ? 0 : (left > 4 ? 4 : (int)left); }
+
 // ---------------------------------------------------------------- phase 2
-// grid.x = k-block tiles on row K other than K itself, grid.y = molecules.
-// Thread (ty, tx) owns rows a = ty*4+{0..3}, columns c = tx*4+{0..3} of the
-// panel tile R = (K, J) seen in row orientation.
+// Panel tile R = (K, J) in row orientation, BK x BK, one workgroup each.
+// grid.x = k-block tiles other than K, grid.y = molecules.  Thread (ty, tx)
+// owns rows a = 4ty..4ty+3 and columns c = 4tx..4tx+3.
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float *__restrict__ L,
                                                     int64_t n, int64_t batch, int64_t K) {
-  __shared__ float du[BK][BK];
-  __shared__ float dl[BK][BK];
-  __shared__ float vu[2][BK];
-  __shared__ float vl[2][BK];
+  __shared__ float4 du[BK][BK / 4];
+  __shared__ float4 dl[BK][BK / 4];
+  __shared__ float4 vu[2][BK / 4];
+  __shared__ float4 vl[2][BK / 4];
 
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   int64_t J = blockIdx.x;
@@ -69,13 +95,25 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
     float *Ub = U + b * nn;
     float *Lb = L + b * nn;
 
-    // the finished diagonal tile (both halves current after phase 1)
-    for (int e = tid; e < BK * BK; e += kThreads) {
-      const int m = e / BK, a = e % BK;
-      const bool in = m < bK && a < bK;
-      const int64_t g = (k0 + m) * n + k0 + a;
-      du[m][a] = in ? Ub[g] : kInf;
-      dl[m][a] = in ? Lb[g] : 0.0f;
+    // the finished diagonal tile (both halves current after phase 1): all
+    // loads issued before the LDS stores
+    {
+      float4 xu[BK * BK / 4 / kThreads], xl[BK * BK / 4 / kThreads];
+#pragma unroll
+      for (int t = 0; t < BK * BK / 4 / kThreads; ++t) {
+        const int e = tid + t * kThreads;
+        const int m = e / (BK / 4), a4 = (e % (BK / 4)) * 4;
+        const int cnt = m < bK ? clamp4(bK - a4) : 0;
+        const int64_t g = (k0 + m) * n + k0 + a4;
+        xu[t] = load4<VEC>(Ub + g, cnt, kInf, Ub);
+        xl[t] = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+      }
+#pragma unroll
+      for (int t = 0; t < BK * BK / 4 / kThreads; ++t) {
+        const int e = tid + t * kThreads;
+        du[e / (BK / 4)][e % (BK / 4)] = xu[t];
+        dl[e / (BK / 4)][e % (BK / 4)] = xl[t];
+      }
     }
 
     float u[4][4], l[4][4];
@@ -84,42 +122,22 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int a = ty * 4 + r;
+        const int cnt = a < bK ? clamp4(bJ - tx * 4) : 0;
         const int64_t g = (k0 + a) * n + j0 + tx * 4;
-        if (VEC) {
-          const bool in = a < bK && tx * 4 < bJ;
-          const float4 x = in ? *reinterpret_cast<const float4 *>(Ub + g) : make_float4(kInf, kInf, kInf, kInf);
-          const float4 y = in ? *reinterpret_cast<const float4 *>(Lb + g) : make_float4(0.f, 0.f, 0.f, 0.f);
-          u[r][0] = x.x; u[r][1] = x.y; u[r][2] = x.z; u[r][3] = x.w;
-          l[r][0] = y.x; l[r][1] = y.y; l[r][2] = y.z; l[r][3] = y.w;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bool in = a < bK && tx * 4 + q < bJ;
-            u[r][q] = in ? Ub[g + q] : kInf;
-            l[r][q] = in ? Lb[g + q] : 0.0f;
-          }
-        }
+        const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+        u[r][0] = x.x; u[r][1] = x.y; u[r][2] = x.z; u[r][3] = x.w;
+        l[r][0] = y.x; l[r][1] = y.y; l[r][2] = y.z; l[r][3] = y.w;
       }
     } else {
       // R[a][c] = M[j0+c][k0+a]
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = tx * 4 + q;
+        const int cnt = c < bJ ? clamp4(bK - ty * 4) : 0;
         const int64_t g = (j0 + c) * n + k0 + ty * 4;
-        if (VEC) {
-          const bool in = c < bJ && ty * 4 < bK;
-          const float4 x = in ? *reinterpret_cast<const float4 *>(Ub + g) : make_float4(kInf, kInf, kInf, kInf);
-          const float4 y = in ? *reinterpret_cast<const float4 *>(Lb + g) : make_float4(0.f, 0.f, 0.f, 0.f);
-          u[0][q] = x.x; u[1][q] = x.y; u[2][q] = x.z; u[3][q] = x.w;
-          l[0][q] = y.x; l[1][q] = y.y; l[2][q] = y.z; l[3][q] = y.w;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool in = c < bJ && ty * 4 + r < bK;
-            u[r][q] = in ? Ub[g + r] : kInf;
-            l[r][q] = in ? Lb[g + r] : 0.0f;
-          }
-        }
+        const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+        u[0][q] = x.x; u[1][q] = x.y; u[2][q] = x.z; u[3][q] = x.w;
+        l[0][q] = y.x; l[1][q] = y.y; l[2][q] = y.z; l[3][q] = y.w;
       }
     }
     __syncthreads();
@@ -131,25 +149,18 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
         if (m >= bK) break;  // uniform
         const int buf = m & 1;
         if (ty == mb) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            vu[buf][tx * 4 + q] = u[r][q];
-            vl[buf][tx * 4 + q] = l[r][q];
-          }
+          vu[buf][tx] = make_float4(u[r][0], u[r][1], u[r][2], u[r][3]);
+          vl[buf][tx] = make_float4(l[r][0], l[r][1], l[r][2], l[r][3]);
         }
         __syncthreads();
-        float ru[4], rl[4], cu[4], cl[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          ru[q] = vu[buf][tx * 4 + q];
-          rl[q] = vl[buf][tx * 4 + q];
-          cu[q] = du[m][ty * 4 + q];  // U[i,k] = D[a][m] = D[m][a]
-          cl[q] = dl[m][ty * 4 + q];
-        }
+        const float4 ru = vu[buf][tx], rl = vl[buf][tx];
+        const float4 cu = du[m][ty], cl = dl[m][ty];  // U[i,k] = D[a][m] = D[m][a]
+        const float cuv[4] = {cu.x, cu.y, cu.z, cu.w}, clv[4] = {cl.x, cl.y, cl.z, cl.w};
+        const float ruv[4] = {ru.x, ru.y, ru.z, ru.w}, rlv[4] = {rl.x, rl.y, rl.z, rl.w};
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) relax1(u[a][q], l[a][q], cu[a], cl[a], ru[q], rl[q]);
+          for (int q = 0; q < 4; ++q) relax1(u[a][q], l[a][q], cuv[a], clv[a], ruv[q], rlv[q]);
       }
     }
 
@@ -179,12 +190,21 @@ __device__ __forceinline__ int64_t tri_col(int64_t p) {
   return J;
 }
 
-// grid.x = T(T+1)/2 tiles (I <= J, column-major over the upper triangle),
-// grid.y = molecules.
+// Tiles are numbered column-major over the upper triangle.  The hardware
+// deals consecutive workgroups to the 8 XCDs in turn, so at any moment an
+// XCD works on a few tile columns and on every 8th tile row of them: the
+// panel slices it needs fit its L2.  (Giving each XCD a contiguous run of
+// tiles instead makes it sweep every row slice of the panel, and is slower.)
+
+// Bulk of phase 3.  grid.x = T(T+1)/2 tiles (I <= J), grid.y = molecules.
+// Cells in band K (final after phase 2) and in band s1 (the next k-block's
+// band, updated ahead by k_strip; s1 < 0 for none) are neither read nor
+// written, and band s1's panel columns are not read: while this kernel runs,
+// another stream may be updating exactly those cells.
 template <bool VEC>
 __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
                                                        float *__restrict__ L, int64_t n,
-                                                       int64_t batch, int64_t K) {
+                                                       int64_t batch, int64_t K, int64_t s1) {
   __shared__ float4 scu[KC][TILE / 4];
   __shared__ float4 scl[KC][TILE / 4];
   __shared__ float4 sru[KC][TILE / 4];
@@ -197,10 +217,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
   const int64_t i0 = I * TILE, j0 = J * TILE;
   const int64_t k0 = K * BK;
   const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int64_t e1 = s1 < 0 ? -1 : (s1 + BK < n ? s1 + BK : n);
   const int64_t nn = n * n;
+  // x is live: in range and outside both bands (band edges are multiples of 4)
+  auto live = [&](int64_t x) { return x < n && (x < k0 || x >= k0 + bK) && (x < s1 || x >= e1); };
+  auto in_s1 = [&](int64_t x) { return x >= s1 && x < e1; };
 
   // rows of this thread: i0 + rofs(r), r < 8; columns likewise with tx
   auto rofs = [](int t, int r) { return (r < 4 ? 0 : TILE / 2 - 4) + t * 4 + r; };
+  // liveness of the thread's 8 rows and 8 columns, one bit each
+  unsigned rmask = 0, cmask = 0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    rmask |= (unsigned)live(i0 + rofs(ty, r)) << r;
+    cmask |= (unsigned)live(j0 + rofs(tx, r)) << r;
+  }
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
     float *Ub = U + b * nn;
@@ -213,57 +244,42 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int64_t j = j0 + rofs(tx, h * 4);
-        const int64_t g = i * n + j;
-        if (VEC) {
-          const bool in = i < n && j < n;
-          const float4 x = in ? *reinterpret_cast<const float4 *>(Ub + g) : make_float4(kInf, kInf, kInf, kInf);
-          const float4 y = in ? *reinterpret_cast<const float4 *>(Lb + g) : make_float4(0.f, 0.f, 0.f, 0.f);
-          u[r][h * 4 + 0] = x.x; u[r][h * 4 + 1] = x.y; u[r][h * 4 + 2] = x.z; u[r][h * 4 + 3] = x.w;
-          l[r][h * 4 + 0] = y.x; l[r][h * 4 + 1] = y.y; l[r][h * 4 + 2] = y.z; l[r][h * 4 + 3] = y.w;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bool in = i < n && j + q < n;
-            u[r][h * 4 + q] = in ? Ub[g + q] : kInf;
-            l[r][h * 4 + q] = in ? Lb[g + q] : 0.0f;
-          }
-        }
+        const bool on = ((rmask >> r) & (cmask >> (h * 4)) & 1u) != 0;
+        const int cnt = on ? (VEC ? 4 : clamp4(n - j)) : 0;
+        const float4 x = load4<VEC>(Ub + i * n + j, cnt, kInf, Ub);
+        const float4 y = load4<VEC>(Lb + i * n + j, cnt, 0.0f, Lb);
+        u[r][h * 4 + 0] = x.x; u[r][h * 4 + 1] = x.y; u[r][h * 4 + 2] = x.z; u[r][h * 4 + 3] = x.w;
+        l[r][h * 4 + 0] = y.x; l[r][h * 4 + 1] = y.y; l[r][h * 4 + 2] = y.z; l[r][h * 4 + 3] = y.w;
       }
     }
 
     for (int kc = 0; kc < bK; kc += KC) {
-      // stage panel rows k0+kc .. k0+kc+KC-1, columns of I and of J
-      for (int e = tid; e < KC * (TILE / 4); e += kThreads) {
+      // stage panel rows k0+kc .. k0+kc+KC-1, columns of I and of J: every
+      // global load of the chunk is issued before the first LDS store
+      constexpr int kIter = KC * (TILE / 4) / kThreads;
+      float4 st[kIter][4];
+#pragma unroll
+      for (int it = 0; it < kIter; ++it) {
+        const int e = tid + it * kThreads;
         const int kk = e / (TILE / 4), x4 = e % (TILE / 4);
         const int64_t k = k0 + kc + kk;
         const bool kin = kc + kk < bK;
         const int64_t ci = i0 + x4 * 4, cj = j0 + x4 * 4;
-        float4 a, c, d, f;
-        if (VEC) {
-          const bool ini = kin && ci < n, inj = kin && cj < n;
-          a = ini ? *reinterpret_cast<const float4 *>(Ub + k * n + ci) : make_float4(kInf, kInf, kInf, kInf);
-          c = ini ? *reinterpret_cast<const float4 *>(Lb + k * n + ci) : make_float4(0.f, 0.f, 0.f, 0.f);
-          d = inj ? *reinterpret_cast<const float4 *>(Ub + k * n + cj) : make_float4(kInf, kInf, kInf, kInf);
-          f = inj ? *reinterpret_cast<const float4 *>(Lb + k * n + cj) : make_float4(0.f, 0.f, 0.f, 0.f);
-        } else {
-          float ta[4], tc[4], td[4], tf[4];
+        const int ni = (kin && !in_s1(ci)) ? clamp4(n - ci) : 0;
+        const int nj = (kin && !in_s1(cj)) ? clamp4(n - cj) : 0;
+        st[it][0] = load4<VEC>(Ub + k * n + ci, ni, kInf, Ub);
+        st[it][1] = load4<VEC>(Lb + k * n + ci, ni, 0.0f, Lb);
+        st[it][2] = load4<VEC>(Ub + k * n + cj, nj, kInf, Ub);
+        st[it][3] = load4<VEC>(Lb + k * n + cj, nj, 0.0f, Lb);
+      }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bool ini = kin && ci + q < n, inj = kin && cj + q < n;
-            ta[q] = ini ? Ub[k * n + ci + q] : kInf;
-            tc[q] = ini ? Lb[k * n + ci + q] : 0.0f;
-            td[q] = inj ? Ub[k * n + cj + q] : kInf;
-            tf[q] = inj ? Lb[k * n + cj + q] : 0.0f;
-          }
-          a = make_float4(ta[0], ta[1], ta[2], ta[3]);
-          c = make_float4(tc[0], tc[1], tc[2], tc[3]);
-          d = make_float4(td[0], td[1], td[2], td[3]);
-          f = make_float4(tf[0], tf[1], tf[2], tf[3]);
-        }
-        scu[kk][x4] = a;
-        scl[kk][x4] = c;
-        sru[kk][x4] = d;
-        srl[kk][x4] = f;
+      for (int it = 0; it < kIter; ++it) {
+        const int e = tid + it * kThreads;
+        const int kk = e / (TILE / 4), x4 = e % (TILE / 4);
+        scu[kk][x4] = st[it][0];
+        scl[kk][x4] = st[it][1];
+        sru[kk][x4] = st[it][2];
+        srl[kk][x4] = st[it][3];
       }
       __syncthreads();
 
@@ -294,20 +310,116 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
       __syncthreads();
     }
 
-    // store, except the k-block's own rows and columns (final after phase 2)
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int64_t i = i0 + rofs(ty, r);
-      const bool row_ok = i < n && (i < k0 || i >= k0 + bK);
+      if (!((rmask >> r) & 1u)) continue;
+      float *pu = Ub + (i0 + rofs(ty, r)) * n + j0;
+      float *pl = Lb + (i0 + rofs(ty, r)) * n + j0;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const int64_t j = j0 + rofs(tx, c);
-        if (row_ok && j < n && (j < k0 || j >= k0 + bK)) {
-          Ub[i * n + j] = u[r][c];
-          Lb[i * n + j] = l[r][c];
+        if ((cmask >> c) & 1u) {
+          pu[rofs(tx, c)] = u[r][c];
+          pl[rofs(tx, c)] = l[r][c];
         }
       }
     }
+    __syncthreads();
+  }
+}
+
+// Phase 3 on band K+1 only, run ahead of the bulk: the cells (i, j) with i in
+// band K+1 and j outside band K, each kept in its fresh orientation.
+// grid.x = k-block tiles J other than K (one BK x BK tile each),
+// grid.y = molecules.  Thread (ty, tx) owns a 4x4 cell tile.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float *__restrict__ L,
+                                                    int64_t n, int64_t batch, int64_t K) {
+  __shared__ float4 scu[KC][BK / 4];
+  __shared__ float4 scl[KC][BK / 4];
+  __shared__ float4 sru[KC][BK / 4];
+  __shared__ float4 srl[KC][BK / 4];
+
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  int64_t J = blockIdx.x;
+  if (J >= K) ++J;
+  const int64_t k0 = K * BK, s1 = (K + 1) * BK, j0 = J * BK;
+  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int b1 = (int)(n - s1 < BK ? n - s1 : BK);
+  const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
+  const bool rowor = fresh(K + 1, J);
+  const int64_t nn = n * n;
+
+  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    float *Ub = U + b * nn;
+    float *Lb = L + b * nn;
+
+    // logical cell (a, c) = (s1 + a, j0 + c); stored at (s1+a, j0+c) or (j0+c, s1+a)
+    float u[4][4], l[4][4];
+    if (rowor) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int a = ty * 4 + r;
+        const int cnt = a < b1 ? clamp4(bJ - tx * 4) : 0;
+        const int64_t g = (s1 + a) * n + j0 + tx * 4;
+        const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+        u[r][0] = x.x; u[r][1] = x.y; u[r][2] = x.z; u[r][3] = x.w;
+        l[r][0] = y.x; l[r][1] = y.y; l[r][2] = y.z; l[r][3] = y.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = tx * 4 + q;
+        const int cnt = c < bJ ? clamp4(b1 - ty * 4) : 0;
+        const int64_t g = (j0 + c) * n + s1 + ty * 4;
+        const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+        u[0][q] = x.x; u[1][q] = x.y; u[2][q] = x.z; u[3][q] = x.w;
+        l[0][q] = y.x; l[1][q] = y.y; l[2][q] = y.z; l[3][q] = y.w;
+      }
+    }
+
+    for (int kc = 0; kc < bK; kc += KC) {
+      {
+        // KC x BK/4 float4 per array: one of each per thread
+        const int kk = tid / (BK / 4), x4 = tid % (BK / 4);
+        const int64_t k = k0 + kc + kk;
+        const bool kin = kc + kk < bK;
+        const int ni = kin ? clamp4(b1 - x4 * 4) : 0;
+        const int nj = kin ? clamp4(bJ - x4 * 4) : 0;
+        scu[kk][x4] = load4<VEC>(Ub + k * n + s1 + x4 * 4, ni, kInf, Ub);
+        scl[kk][x4] = load4<VEC>(Lb + k * n + s1 + x4 * 4, ni, 0.0f, Lb);
+        sru[kk][x4] = load4<VEC>(Ub + k * n + j0 + x4 * 4, nj, kInf, Ub);
+        srl[kk][x4] = load4<VEC>(Lb + k * n + j0 + x4 * 4, nj, 0.0f, Lb);
+      }
+      __syncthreads();
+#pragma unroll 2
+      for (int kk = 0; kk < KC; kk += 2) {
+        const float4 a0 = scu[kk][ty], b0 = scl[kk][ty], c0 = sru[kk][tx], d0 = srl[kk][tx];
+        const float4 a1 = scu[kk + 1][ty], b1v = scl[kk + 1][ty], c1 = sru[kk + 1][tx], d1 = srl[kk + 1][tx];
+        const float cu0[4] = {a0.x, a0.y, a0.z, a0.w}, cl0[4] = {b0.x, b0.y, b0.z, b0.w};
+        const float ru0[4] = {c0.x, c0.y, c0.z, c0.w}, rl0[4] = {d0.x, d0.y, d0.z, d0.w};
+        const float cu1[4] = {a1.x, a1.y, a1.z, a1.w}, cl1[4] = {b1v.x, b1v.y, b1v.z, b1v.w};
+        const float ru1[4] = {c1.x, c1.y, c1.z, c1.w}, rl1[4] = {d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            relax2(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
+                   rl1[q]);
+      }
+      __syncthreads();
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int a = ty * 4 + r, c = tx * 4 + q;
+        if (a < b1 && c < bJ) {
+          const int64_t g = rowor ? (s1 + a) * n + j0 + c : (j0 + c) * n + s1 + a;
+          Ub[g] = u[r][q];
+          Lb[g] = l[r][q];
+        }
+      }
     __syncthreads();
   }
 }
@@ -349,8 +461,57 @@ __global__ __launch_bounds__(kThreads) void k_mirror(float *__restrict__ U, floa
   }
 }
 
+// Side stream for the lookahead (one per device, default priority, created
+// on first use and kept for the life of the process).
+hipStream_t side_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev]) {
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess) streams[dev] = st;
+  }
+  return streams[dev];
+}
+
+// Ordering events of the lookahead: one set per host thread and device,
+// created on first use and re-recorded by every pass (a stream wait captures
+// the event's state when it is enqueued, so re-recording is safe).
+struct Events {
+  hipEvent_t e[3] = {nullptr, nullptr, nullptr};  // e[0] unused
+  bool ready = false;
+  bool init() {
+    if (ready) return true;
+    for (auto &x : e)
+      if (!x && hipEventCreateWithFlags(&x, hipEventDisableTiming) != hipSuccess) return false;
+    ready = true;
+    return true;
+  }
+  ~Events() {
+    for (auto &x : e)
+      if (x) (void)hipEventDestroy(x);
+  }
+};
+
+Events *thread_events() {
+  thread_local Events per_device[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  return per_device[dev].init() ? &per_device[dev] : nullptr;
+}
+
 }  // namespace
 
+// Enqueue one pass.  With more than one k-block the pass runs ahead: phase 3
+// of block K is split into band K+1 (k_strip) and everything else (k_tiles).
+// The side stream runs strip(K), then phases 1 and 2 of block K+1, while the
+// caller's stream runs tiles(K); so the short, latency-bound phases hide
+// under the long one.  Everything on the side stream reads and writes only
+// band K+1 cells and band K's panel rows, which tiles(K) neither writes nor
+// (for band K+1) reads.  Events order strip(K) after tiles(K-1), and
+// tiles(K+1) after phase 2 of K+1.
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStream_t s,
                           Prof *prof) {
   if (n <= 1) return hipSuccess;
@@ -359,19 +520,47 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStrea
   const bool vec = (n % 4 == 0) && aligned16(U) && aligned16(L);
   const unsigned gy = (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ);
   const int64_t nn = n * n;
-  hipError_t e = hipSuccess;
-  for (int64_t K = 0; K < TB && e == hipSuccess; ++K) {
+  auto panel = vec ? k_panel<true> : k_panel<false>;
+  auto tiles = vec ? k_tiles<true> : k_tiles<false>;
+  auto strip = vec ? k_strip<true> : k_strip<false>;
+
+  auto phase12 = [&](int64_t K, hipStream_t st) -> hipError_t {
     const int64_t k0 = K * BK;
     const int bK = (int)(n - k0 < BK ? n - k0 : BK);
-    e = launch_small_block(U, L, n, nn, k0 * n + k0, bK, batch, s, prof);
-    if (e != hipSuccess || TB == 1) break;
-    const dim3 g2((unsigned)(TB - 1), gy);
-    e = launch(prof, kProfPanel, vec ? k_panel<true> : k_panel<false>, g2, dim3(kThreads), s, U,
-               L, n, batch, K);
-    if (e != hipSuccess) break;
-    const dim3 g3((unsigned)(T * (T + 1) / 2), gy);
-    e = launch(prof, kProfTiles, vec ? k_tiles<true> : k_tiles<false>, g3, dim3(kThreads), s, U,
-               L, n, batch, K);
+    hipError_t e = launch_small_block(U, L, n, nn, k0 * n + k0, bK, batch, st, prof);
+    if (e != hipSuccess || TB == 1) return e;
+    return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(kThreads), st, U,
+                  L, n, batch, K);
+  };
+  // s1: first atom of the band the bulk launch must leave alone (-1: none)
+  auto phase3 = [&](int64_t K, int64_t s1, hipStream_t st) -> hipError_t {
+    return launch(prof, kProfTiles, tiles, dim3((unsigned)(T * (T + 1) / 2), gy), dim3(kThreads),
+                  st, U, L, n, batch, K, s1);
+  };
+
+  hipError_t e = phase12(0, s);
+  if (e != hipSuccess || TB == 1) return e;
+
+  hipStream_t side = T > 1 ? side_stream() : nullptr;
+  Events *ev = side ? thread_events() : nullptr;
+  const bool ahead = side != nullptr && ev != nullptr;
+  for (int64_t K = 0; K < TB && e == hipSuccess; ++K) {
+    if (K + 1 == TB) {
+      e = phase3(K, -1, s);
+    } else if (!ahead) {
+      e = phase3(K, -1, s);
+      if (e == hipSuccess) e = phase12(K + 1, s);
+    } else {
+      if ((e = hipEventRecord(ev->e[1], s)) != hipSuccess) break;
+      if ((e = hipStreamWaitEvent(side, ev->e[1], 0)) != hipSuccess) break;
+      if ((e = launch(prof, kProfStrip, strip, dim3((unsigned)(TB - 1), gy), dim3(kThreads), side,
+                      U, L, n, batch, K)) != hipSuccess)
+        break;
+      if ((e = phase12(K + 1, side)) != hipSuccess) break;
+      if ((e = hipEventRecord(ev->e[2], side)) != hipSuccess) break;
+      if ((e = phase3(K, (K + 1) * BK, s)) != hipSuccess) break;
+      e = hipStreamWaitEvent(s, ev->e[2], 0);
+    }
   }
   if (e == hipSuccess && T > 1)
     e = launch(prof, kProfMirror, k_mirror, dim3((unsigned)(TB * TB), gy), dim3(kThreads), s, U,

@@ -74,7 +74,14 @@ struct Prof {
   }
 };
 
-enum ProfKind { kProfRound = 0, kProfSmall = 1, kProfPanel = 2, kProfTiles = 3, kProfMirror = 4 };
+enum ProfKind {
+  kProfRound = 0,
+  kProfSmall = 1,
+  kProfPanel = 2,
+  kProfTiles = 3,
+  kProfMirror = 4,
+  kProfStrip = 5
+};
 
 template <typename T>
 struct ident {

@@ -135,9 +135,12 @@ int dbs_smooth_profiled(float *U, float *L, int64_t n, int64_t batch, void *stre
 #define DBS_PROF_ROUND 0   /* per-round kernel                                 */
 #define DBS_PROF_SMALL 1   /* single-workgroup pass (whole molecule or diagonal tile) */
 #define DBS_PROF_PANEL 2   /* blocked phase 2: panel tiles                     */
-#define DBS_PROF_TILES 3   /* blocked phase 3: remaining tiles                 */
+#define DBS_PROF_TILES 3   /* blocked phase 3: the bulk (every upper tile, less
+                              the current and the next k-block's bands)       */
 #define DBS_PROF_MIRROR 4  /* blocked: final transposed copy                   */
-#define DBS_PROF_KINDS 5
+#define DBS_PROF_STRIP 5   /* blocked phase 3 on the next k-block's band, run
+                              ahead on a second stream                        */
+#define DBS_PROF_KINDS 6
 
 /* Largest n the LDS algorithm accepts. */
 int dbs_lds_max_n(void);
