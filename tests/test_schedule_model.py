@@ -1,0 +1,170 @@
+"""CPU model of the blocked pass's schedule (test code only).
+
+The GPU pass (csrc/blocked.hip) runs, per k-block K of BK = 64 atoms,
+  phase 1  FW on the diagonal tile (K,K);
+  phase 2  the panel tiles of band K, each read from its fresh orientation
+           (upper TILE x TILE region) and written in both orientations;
+  phase 3  band K+1 first (the strip, on a second stream, followed there by
+           phases 1-2 of K+1), and every other live cell of the upper
+           TILE x TILE tiles (the bulk, on the caller's stream);
+and mirrors the upper tiles into the lower ones at the end.
+
+This model re-implements that data flow in plain Python on exact int64 units
+(one cell at a time, no shared code with the kernels or the oracle) and checks
+  * that it reaches the oracle's result bit for bit, and
+  * that the two streams of one k-block touch disjoint cells: nothing the
+    side stream writes is read or written by the bulk, and nothing the bulk
+    writes is read by the side stream.
+The GPU parity tests then check the kernels themselves against the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pins
+from distance_geometry_bound_amd import gen
+
+BK, TILE = 64, 128
+RATIO = TILE // BK
+
+
+def fresh(a, b):
+    return a // RATIO <= b // RATIO
+
+
+class Model:
+    def __init__(self, U0, L0):
+        self.n = U0.shape[0]
+        self.U = pins.units(U0).copy()
+        self.L = pins.units(L0).copy()
+        self.TB = -(-self.n // BK)
+        self.T = -(-self.n // TILE)
+
+    def band(self, K):
+        return list(range(K * BK, min(self.n, K * BK + BK)))
+
+    def relax(self, i, j, k, U, L):
+        """One round k on cell (i, j), reading row k for both operands
+        (U[i,k] = U[k,i] by symmetry)."""
+        u = min(U[i, j], U[k, i] + U[k, j])
+        l = max(L[i, j], L[k, i] - U[k, j], L[k, j] - U[k, i])
+        return u, l
+
+    def phase1(self, K):
+        b = self.band(K)
+        U, L = self.U, self.L
+        for k in b:
+            new = {(i, j): self.relax(i, j, k, U, L) for i in b for j in b}
+            for (i, j), (u, l) in new.items():
+                U[i, j], L[i, j] = u, l
+        cells = {(i, j) for i in b for j in b}
+        return cells, cells
+
+    def phase2(self, K):
+        reads, writes = set(), set()
+        kb = self.band(K)
+        reads |= {(i, j) for i in kb for j in kb}
+        for J in range(self.TB):
+            if J == K:
+                continue
+            jb = self.band(J)
+            # R[a][c] = cell (k0+a, j0+c), read from the fresh orientation
+            R = {}
+            for a in kb:
+                for c in jb:
+                    src = (a, c) if fresh(K, J) else (c, a)
+                    R[(a, c)] = (self.U[src], self.L[src])
+                    reads.add(src)
+            D = lambda x, y: (self.U[x, y], self.L[x, y])
+            for m in kb:
+                new = {}
+                for a in kb:
+                    cu, cl = D(m, a)               # U[a,m] = D[m][a]
+                    for c in jb:
+                        ru, rl = R[(m, c)]
+                        u, l = R[(a, c)]
+                        new[(a, c)] = (min(u, cu + ru), max(l, cl - ru, rl - cu))
+                R = new
+            for (a, c), (u, l) in R.items():
+                self.U[a, c] = self.U[c, a] = u
+                self.L[a, c] = self.L[c, a] = l
+                writes |= {(a, c), (c, a)}
+        return reads, writes
+
+    def strip(self, K):
+        reads, writes = set(), set()
+        kb, s1 = self.band(K), self.band(K + 1)
+        for J in range(self.TB):
+            if J == K:
+                continue
+            jb = self.band(J)
+            reads |= {(k, x) for k in kb for x in s1 + jb}
+            for a in s1:
+                for c in jb:
+                    dst = (a, c) if fresh(K + 1, J) else (c, a)
+                    u, l = self.U[dst], self.L[dst]
+                    reads.add(dst)
+                    for k in kb:
+                        u = min(u, self.U[k, a] + self.U[k, c])
+                        l = max(l, self.L[k, a] - self.U[k, c], self.L[k, c] - self.U[k, a])
+                    self.U[dst], self.L[dst] = u, l
+                    writes.add(dst)
+        return reads, writes
+
+    def tiles(self, K, ahead):
+        n = self.n
+        reads, writes = set(), set()
+        dead = set(self.band(K)) | (set(self.band(K + 1)) if ahead else set())
+        s1 = set(self.band(K + 1)) if ahead else set()
+        kb = self.band(K)
+        new = {}
+        for J in range(self.T):
+            for I in range(J + 1):
+                rows = range(I * TILE, min(n, I * TILE + TILE))
+                cols = range(J * TILE, min(n, J * TILE + TILE))
+                reads |= {(k, x) for k in kb for x in list(rows) + list(cols) if x not in s1}
+                for i in rows:
+                    for j in cols:
+                        if i in dead or j in dead:
+                            continue
+                        u, l = self.U[i, j], self.L[i, j]
+                        reads.add((i, j))
+                        for k in kb:
+                            u = min(u, self.U[k, i] + self.U[k, j])
+                            l = max(l, self.L[k, i] - self.U[k, j], self.L[k, j] - self.U[k, i])
+                        new[(i, j)] = (u, l)
+                        writes.add((i, j))
+        for (i, j), (u, l) in new.items():
+            self.U[i, j], self.L[i, j] = u, l
+        return reads, writes
+
+    def run(self):
+        self.phase1(0)
+        if self.TB > 1:
+            self.phase2(0)
+        for K in range(self.TB):
+            if K + 1 == self.TB:
+                self.tiles(K, ahead=False)
+                continue
+            sr, sw = self.strip(K)
+            r1, w1 = self.phase1(K + 1)
+            r2, w2 = self.phase2(K + 1)
+            side_r, side_w = sr | r1 | r2, sw | w1 | w2
+            tr, tw = self.tiles(K, ahead=True)
+            assert not (side_w & (tr | tw)), f"k-block {K}: side stream writes what the bulk touches"
+            assert not (tw & side_r), f"k-block {K}: bulk writes what the side stream reads"
+        n = self.n
+        for i in range(n):
+            for j in range(n):
+                if (i // BK) // RATIO > (j // BK) // RATIO:
+                    self.U[i, j], self.L[i, j] = self.U[j, i], self.L[j, i]
+        return self.U, self.L
+
+
+@pytest.mark.parametrize("n", [65, 130, 200, 257])
+def test_schedule_model_matches_oracle_and_streams_are_disjoint(n):
+    U0, L0, _ = gen.random_sound_bounds(n, seed=n, box=6.0 + n / 8)
+    Ue, Le = oracle.smooth(U0, L0)
+    Um, Lm = Model(U0, L0).run()
+    assert np.array_equal(Um, pins.units(Ue))
+    assert np.array_equal(Lm, pins.units(Le))
