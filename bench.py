@@ -14,6 +14,8 @@ Printed: one JSON line with
                (dbs_smooth_profiled on the launch stream)
   perk         the per-round kernel: HBM bytes of the round formulation
                (16 B per cell per round) / mean round time
+  restraints   the workload's restraint list to dense bounds (fill + scatter)
+  tightened    the mask of cells a pass changed
   cpu_baseline the CPU reference (oracle) on a bounded prefix of rounds of
                the same workload, on this host's cores
 Run with --gpus N > 1 and it exits: this build runs on one GPU.
@@ -52,6 +54,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 = skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-steps-extra", dest="steps_extra", action="store_false",
+                    help="skip timing the restraint-to-bounds and tightened-mask steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy 5 times (counter scale)")
     return ap.parse_args()
@@ -107,6 +111,53 @@ def counters_traffic(n, batch):
     if rec.get("source_sha256") != sha or rec.get("n") != n or rec.get("batch") != batch:
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def extra_steps(W, U, L, U0, L0, dev, reps=3):
+    """Time the steps around a pass on the same workload: the restraint list
+    to dense bounds (placeholder fill + interval scatter; the fill writes 8
+    bytes per cell) and the tightened-cell mask of a finished pass (reads 16,
+    writes 1 byte per cell).  Both are HBM-bound."""
+    import torch
+
+    import distance_geometry_bound_amd as dgb
+    from distance_geometry_bound_amd import gen
+
+    res = {}
+    mol, ia, ja, lo, hi, ul, uu, n, nb = gen.workload_restraints(W.name)
+    t = [torch.from_numpy(x).to(dev) for x in (mol, ia, ja, lo, hi)]
+    s = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dgb.bounds_from_restraints(n, t[1], t[2], t[3], t[4], ul, uu, mol=t[0], batch=nb,
+                               out=(U, L))
+    ms = 0.0
+    for _ in range(reps):
+        e0.record(s)
+        _, _, st = dgb.bounds_from_restraints(n, t[1], t[2], t[3], t[4], ul, uu, mol=t[0],
+                                              batch=nb, out=(U, L))
+        e1.record(s)
+        torch.cuda.synchronize(dev)
+        ms += e0.elapsed_time(e1) / reps
+    cells = n * n * nb
+    res["restraints"] = {"count": int(len(ia)), "status": st, "ms": ms,
+                         "GBps_fill": 8.0 * cells / (ms * 1e-3) / 1e9,
+                         "frac_hbm": 8.0 * cells / (ms * 1e-3) / HBM_PEAK,
+                         "bytes": 8 * cells}
+    U.copy_(U0)
+    L.copy_(L0)
+    dgb.smooth(U, L)
+    dgb.tightened(U0, L0, U, L)
+    ms = 0.0
+    for _ in range(reps):
+        e0.record(s)
+        m = dgb.tightened(U0, L0, U, L)
+        e1.record(s)
+        torch.cuda.synchronize(dev)
+        ms += e0.elapsed_time(e1) / reps
+    res["tightened"] = {"ms": ms, "cells_changed": int(m.sum().item()),
+                        "GBps": 17.0 * cells / (ms * 1e-3) / 1e9,
+                        "frac_hbm": 17.0 * cells / (ms * 1e-3) / HBM_PEAK}
+    return res
 
 
 def cpu_baseline(W, target_s):
@@ -256,6 +307,9 @@ def main():
                            "rounds": R, "ms_per_round": ms, "GBps": gbps,
                            "frac_hbm": gbps * 1e9 / HBM_PEAK,
                            "bytes_per_round": 16 * n * n * batch}
+
+    if args.steps_extra:
+        out.update(extra_steps(W, U, L, U0, L0, dev))
 
     if not args.no_cpu and args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

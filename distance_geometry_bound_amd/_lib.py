@@ -25,9 +25,12 @@ CHECK_FLAGS = {
 DBS_OK, DBS_EINVAL, DBS_EDEVICE, DBS_ELAUNCH, DBS_EUNSUPPORTED = 0, -1, -2, -3, -4
 
 EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
+           "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened", "dbs_bounds_from_restraints",
            "dbs_lds_max_n", "dbs_auto_algo", "dbs_strerror", "dbs_version")
 
-PROF_KINDS = ("round", "small", "panel", "tiles", "mirror", "strip")
+RESTRAINT_FLAGS = {"index": 1, "value": 2}
+
+PROF_KINDS = ("round", "small", "panel", "tiles", "mirror", "strip", "fill", "scatter")
 
 
 class DbsError(RuntimeError):
@@ -53,12 +56,17 @@ def lib():
         L.dbs_smooth_profiled.argtypes = [vp, vp, i64, i64, vp, c_int,
                                           ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
         L.dbs_rounds.argtypes = [vp, vp, i64, i64, i64, i64, vp]
+        L.dbs_smooth_range.argtypes = [vp, vp, i64, i64, i64, i64, vp, c_int]
+        L.dbs_tightened.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp]
+        L.dbs_bounds_from_restraints.argtypes = [vp, vp, i64, i64, ctypes.c_float,
+                                                 ctypes.c_float, vp, vp, vp, vp, vp, i64, vp, vp]
         L.dbs_check.argtypes = [vp, vp, i64, i64, vp, vp]
         L.dbs_auto_algo.argtypes = [i64, i64]
         L.dbs_strerror.argtypes = [c_int]
         L.dbs_strerror.restype = ctypes.c_char_p
         for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
-                  "dbs_lds_max_n", "dbs_auto_algo", "dbs_version"):
+                  "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened",
+                  "dbs_bounds_from_restraints", "dbs_lds_max_n", "dbs_auto_algo", "dbs_version"):
             getattr(L, f).restype = c_int
         _lib = L
     return _lib
@@ -145,6 +153,68 @@ def smooth_rounds(U, L, k_begin: int, k_end: int) -> None:
 def smooth_round(U, L, k: int) -> None:
     """Round k only."""
     smooth_rounds(U, L, k, k + 1)
+
+
+def smooth_range(U, L, k_begin: int, k_end: int, algo: str = "auto") -> None:
+    """Rounds k_begin..k_end-1 of a pass, in place (see dbs_smooth_range)."""
+    n, batch = _shape(U, L)
+    if algo not in _ALGOS:
+        raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
+    if n == 0 or batch == 0:
+        return
+    _call(U, lib().dbs_smooth_range, U.data_ptr(), L.data_ptr(), n, batch, int(k_begin),
+          int(k_end), _stream(U), _ALGOS[algo])
+
+
+def tightened(U0, L0, U1, L1):
+    """uint8 mask of the cells whose U or L differs between two states."""
+    import torch
+
+    n, batch = _shape(U0, L0)
+    if _shape(U1, L1) != (n, batch) or U1.device != U0.device:
+        raise ValueError("the two states must have the same shape and device")
+    mask = torch.empty(U0.shape, dtype=torch.uint8, device=U0.device)
+    if n and batch:
+        _call(U0, lib().dbs_tightened, U0.data_ptr(), L0.data_ptr(), U1.data_ptr(),
+              L1.data_ptr(), n, batch, mask.data_ptr(), _stream(U0))
+    return mask
+
+
+def bounds_from_restraints(n: int, ia, ja, lo, hi, unknown_L: float, unknown_U: float,
+                           mol=None, batch: int = 1, out=None):
+    """Dense [batch,n,n] (U, L) from a restraint list (see dbs_bounds_from_restraints).
+
+    ia, ja, mol: int32 tensors, lo, hi: float32 tensors, all on one GPU.
+    out: optional (U, L) to write into; else new tensors on that GPU.
+    Returns (U, L, status) with status the DBS_RESTRAINT_* bits (synchronises).
+    """
+    import torch
+
+    dev = ia.device
+    for name, t, dt in (("ia", ia, torch.int32), ("ja", ja, torch.int32),
+                        ("lo", lo, torch.float32), ("hi", hi, torch.float32)):
+        if t.dtype != dt or t.device != dev or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError(f"{name} must be a contiguous 1-D {dt} tensor on {dev}")
+    count = ia.numel()
+    if not (ja.numel() == lo.numel() == hi.numel() == count):
+        raise ValueError("restraint arrays differ in length")
+    if mol is not None and (mol.dtype != torch.int32 or mol.device != dev or
+                            not mol.is_contiguous() or mol.numel() != count):
+        raise ValueError("mol must be a contiguous int32 tensor like ia")
+    if out is None:
+        U = torch.empty((batch, n, n), dtype=torch.float32, device=dev)
+        L = torch.empty_like(U)
+    else:
+        U, L = out
+    n_, b_ = _shape(U, L)
+    if (n_, b_) != (n, batch):
+        raise ValueError("out has the wrong shape")
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _call(U, lib().dbs_bounds_from_restraints, U.data_ptr(), L.data_ptr(), n, batch,
+          float(unknown_L), float(unknown_U), mol.data_ptr() if mol is not None else None,
+          ia.data_ptr(), ja.data_ptr(), lo.data_ptr(), hi.data_ptr(), count, status.data_ptr(),
+          _stream(U))
+    return U, L, int(status.item()) & 0xFFFFFFFF
 
 
 def check(U, L) -> int:

@@ -1,5 +1,6 @@
 // api.hip -- the extern "C" entry points declared in include/dbs.h:
 // argument validation, device check, algorithm choice, launch sequencing.
+#include <math.h>
 #include <string.h>
 
 #include <mutex>
@@ -62,9 +63,10 @@ int run(float *U, float *L, int64_t n, int64_t batch, void *stream, int algo,
       return status_of(e);
     }
     case DBS_ALGO_LDS:
-      return status_of(dbs::launch_small(U, L, n, batch, s, prof));
+      return status_of(dbs::launch_small(U, L, n, batch, 0, (int)n, s, prof));
     default:
-      return status_of(dbs::launch_blocked(U, L, n, batch, s, prof));
+      return status_of(dbs::launch_blocked(U, L, n, batch, 0, dbs::ceil_div(n, dbs::kBlockRounds),
+                                           s, prof));
   }
 }
 
@@ -122,6 +124,75 @@ int dbs_check(const float *U, const float *L, int64_t n, int64_t batch, uint32_t
   st = device_status();
   if (st != DBS_OK) return st;
   return status_of(dbs::launch_check(U, L, n, batch, d_flags, static_cast<hipStream_t>(stream)));
+}
+
+int dbs_smooth_range(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
+                     int64_t k_end, void *stream, int algo) {
+  int st = validate(U, L, n, batch);
+  if (st != DBS_OK) return st;
+  if (k_begin < 0 || k_end > n || k_begin > k_end) return DBS_EINVAL;
+  if (algo < DBS_ALGO_AUTO || algo > DBS_ALGO_BLOCKED) return DBS_EINVAL;
+  const int64_t B = dbs::kBlockRounds;
+  const bool aligned = k_begin % B == 0 && (k_end % B == 0 || k_end == n);
+  if (algo == DBS_ALGO_AUTO)
+    algo = n <= dbs::kSmallMaxN ? DBS_ALGO_LDS : aligned ? DBS_ALGO_BLOCKED : DBS_ALGO_PERK;
+  if (algo == DBS_ALGO_LDS && n > dbs::kSmallMaxN) return DBS_EUNSUPPORTED;
+  if (algo == DBS_ALGO_BLOCKED && !aligned) return DBS_EUNSUPPORTED;
+  st = device_status();
+  if (st != DBS_OK) return st;
+  if (k_begin == k_end || n == 1) return DBS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (algo) {
+    case DBS_ALGO_PERK: {
+      hipError_t e = hipSuccess;
+      for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
+        e = dbs::launch_round(U, L, n, batch, k, s);
+      return status_of(e);
+    }
+    case DBS_ALGO_LDS:
+      return status_of(dbs::launch_small(U, L, n, batch, (int)k_begin, (int)k_end, s));
+    default:
+      return status_of(
+          dbs::launch_blocked(U, L, n, batch, k_begin / B, dbs::ceil_div(k_end, B), s));
+  }
+}
+
+int dbs_block_rounds(void) { return dbs::kBlockRounds; }
+
+int dbs_tightened(const float *U0, const float *L0, const float *U1, const float *L1,
+                  int64_t n, int64_t batch, uint8_t *mask, void *stream) {
+  // the four inputs may alias one another; none may overlap the mask
+  if (!U0 || !L0 || !U1 || !L1 || !mask || n < 1 || batch < 1 || n >= ((int64_t)1 << 31))
+    return DBS_EINVAL;
+  if (batch > INT64_MAX / 4 / (n * n)) return DBS_EINVAL;
+  const uint64_t fbytes = (uint64_t)(n * n * batch) * 4u, mbytes = fbytes / 4u;
+  const uintptr_t m = reinterpret_cast<uintptr_t>(mask);
+  for (const float *p : {U0, L0, U1, L1}) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if ((a & 3u) || (a < m + mbytes && m < a + fbytes)) return DBS_EINVAL;
+  }
+  const int st = device_status();
+  if (st != DBS_OK) return st;
+  return status_of(
+      dbs::launch_tightened(U0, L0, U1, L1, n, batch, mask, static_cast<hipStream_t>(stream)));
+}
+
+int dbs_bounds_from_restraints(float *U, float *L, int64_t n, int64_t batch, float unknown_L,
+                               float unknown_U, const int32_t *mol, const int32_t *ia,
+                               const int32_t *ja, const float *lo, const float *hi,
+                               int64_t count, uint32_t *d_status, void *stream) {
+  int st = validate(U, L, n, batch);
+  if (st != DBS_OK) return st;
+  if (count < 0) return DBS_EINVAL;
+  if (count > 0 && (!ia || !ja || !lo || !hi || (batch > 1 && !mol))) return DBS_EINVAL;
+  if (!(unknown_L >= 0.0f && unknown_L <= unknown_U && unknown_U < 131072.0f)) return DBS_EINVAL;
+  st = device_status();
+  if (st != DBS_OK) return st;
+  // placeholders, rounded outward on the host (exact in float: see the kernel)
+  const float uL = floorf(unknown_L * 64.0f) / 64.0f, uU = ceilf(unknown_U * 64.0f) / 64.0f;
+  if (uU >= 131072.0f) return DBS_EINVAL;
+  return status_of(dbs::launch_restraints(U, L, n, batch, uL, uU, mol, ia, ja, lo, hi, count,
+                                          d_status, static_cast<hipStream_t>(stream)));
 }
 
 int dbs_lds_max_n(void) { return dbs::kSmallMaxN; }

@@ -512,10 +512,12 @@ Events *thread_events() {
 // band K+1 cells and band K's panel rows, which tiles(K) neither writes nor
 // (for band K+1) reads.  Events order strip(K) after tiles(K-1), and
 // tiles(K+1) after phase 2 of K+1.
-hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStream_t s,
-                          Prof *prof) {
-  if (n <= 1) return hipSuccess;
+hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
+                          hipStream_t s, Prof *prof) {
+  static_assert(BK == kBlockRounds, "k-block size");
   const int64_t TB = ceil_div(n, BK);    // k-blocks
+  if (K1 > TB) K1 = TB;
+  if (n <= 1 || K0 >= K1) return hipSuccess;
   const int64_t T = ceil_div(n, TILE);   // phase-3 tiles per side
   const bool vec = (n % 4 == 0) && aligned16(U) && aligned16(L);
   const unsigned gy = (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ);
@@ -527,7 +529,7 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStrea
   auto phase12 = [&](int64_t K, hipStream_t st) -> hipError_t {
     const int64_t k0 = K * BK;
     const int bK = (int)(n - k0 < BK ? n - k0 : BK);
-    hipError_t e = launch_small_block(U, L, n, nn, k0 * n + k0, bK, batch, st, prof);
+    hipError_t e = launch_small_block(U, L, n, nn, k0 * n + k0, bK, 0, bK, batch, st, prof);
     if (e != hipSuccess || TB == 1) return e;
     return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(kThreads), st, U,
                   L, n, batch, K);
@@ -538,14 +540,14 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStrea
                   st, U, L, n, batch, K, s1);
   };
 
-  hipError_t e = phase12(0, s);
+  hipError_t e = phase12(K0, s);
   if (e != hipSuccess || TB == 1) return e;
 
   hipStream_t side = T > 1 ? side_stream() : nullptr;
   Events *ev = side ? thread_events() : nullptr;
   const bool ahead = side != nullptr && ev != nullptr;
-  for (int64_t K = 0; K < TB && e == hipSuccess; ++K) {
-    if (K + 1 == TB) {
+  for (int64_t K = K0; K < K1 && e == hipSuccess; ++K) {
+    if (K + 1 == K1) {
       e = phase3(K, -1, s);
     } else if (!ahead) {
       e = phase3(K, -1, s);

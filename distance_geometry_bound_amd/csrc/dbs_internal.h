@@ -80,7 +80,9 @@ enum ProfKind {
   kProfPanel = 2,
   kProfTiles = 3,
   kProfMirror = 4,
-  kProfStrip = 5
+  kProfStrip = 5,
+  kProfFill = 6,
+  kProfScatter = 7
 };
 
 template <typename T>
@@ -115,10 +117,19 @@ hipError_t launch(Prof *prof, int kind, void (*kernel)(KArgs...), dim3 grid, dim
 // error, if any.
 hipError_t launch_round(float *U, float *L, int64_t n, int64_t batch, int64_t k, hipStream_t s,
                         Prof *prof = nullptr);
-hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, hipStream_t s,
-                        Prof *prof = nullptr);
-hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, hipStream_t s,
-                          Prof *prof = nullptr);
+// rounds k_lo..k_hi-1 of a whole small molecule in one workgroup
+hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, int k_lo, int k_hi,
+                        hipStream_t s, Prof *prof = nullptr);
+// k-blocks K0..K1-1 of the blocked pass (rounds 64*K0 .. min(64*K1, n)-1)
+hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
+                          hipStream_t s, Prof *prof = nullptr);
+constexpr int kBlockRounds = 64;
+hipError_t launch_restraints(float *U, float *L, int64_t n, int64_t batch, float unknown_L,
+                             float unknown_U, const int32_t *mol, const int32_t *ia,
+                             const int32_t *ja, const float *lo, const float *hi, int64_t count,
+                             uint32_t *status, hipStream_t s, Prof *prof = nullptr);
+hipError_t launch_tightened(const float *U0, const float *L0, const float *U1, const float *L1,
+                            int64_t n, int64_t batch, uint8_t *mask, hipStream_t s);
 hipError_t launch_check(const float *U, const float *L, int64_t n, int64_t batch,
                         uint32_t *flags, hipStream_t s);
 
@@ -127,7 +138,8 @@ hipError_t launch_check(const float *U, const float *L, int64_t n, int64_t batch
 // `mstride`); grid = molecules.  Used for whole small molecules and for the
 // diagonal tile of the blocked pass.
 hipError_t launch_small_block(float *U, float *L, int64_t ld, int64_t mstride, int64_t off,
-                              int m, int64_t batch, hipStream_t s, Prof *prof = nullptr);
+                              int m, int k_lo, int k_hi, int64_t batch, hipStream_t s,
+                              Prof *prof = nullptr);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -35,7 +35,7 @@ __device__ __forceinline__ void publish(float (&u)[4][4], float (&l)[4][4], int 
 
 __global__ __launch_bounds__(1024) void k_small(float *__restrict__ U, float *__restrict__ L,
                                                 int64_t ld, int64_t mstride, int64_t off, int m,
-                                                int64_t batch) {
+                                                int k_lo, int k_hi, int64_t batch) {
   __shared__ float vu[2][4 * kMaxG];
   __shared__ float vl[2][4 * kMaxG];
 
@@ -70,11 +70,12 @@ __global__ __launch_bounds__(1024) void k_small(float *__restrict__ U, float *__
         }
     }
 
-    for (int kb = 0; kb < G; ++kb) {
+    for (int kb = k_lo / 4; kb < G; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int k = kb * 4 + r;
-        if (k >= m) break;  // uniform across the workgroup
+        if (k >= k_hi) break;  // uniform across the workgroup
+        if (k < k_lo) continue;
         const int buf = k & 1;
         if (active) {
           if (ty == kb)
@@ -125,19 +126,20 @@ __global__ __launch_bounds__(1024) void k_small(float *__restrict__ U, float *__
 }  // namespace
 
 hipError_t launch_small_block(float *U, float *L, int64_t ld, int64_t mstride, int64_t off,
-                              int m, int64_t batch, hipStream_t s, Prof *prof) {
-  if (m <= 1) return hipSuccess;
+                              int m, int k_lo, int k_hi, int64_t batch, hipStream_t s,
+                              Prof *prof) {
+  if (m <= 1 || k_lo >= k_hi) return hipSuccess;
   const int G = (m + 3) / 4;
   const int tiles = G * (G + 1) / 2;
   const int threads = (tiles + 63) / 64 * 64;
   const unsigned grid = (unsigned)(batch < 1048576 ? batch : 1048576);
   return launch(prof, kProfSmall, k_small, dim3(grid), dim3(threads), s, U, L, ld, mstride, off,
-                m, batch);
+                m, k_lo, k_hi, batch);
 }
 
-hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, hipStream_t s,
-                        Prof *prof) {
-  return launch_small_block(U, L, n, n * n, 0, (int)n, batch, s, prof);
+hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, int k_lo, int k_hi,
+                        hipStream_t s, Prof *prof) {
+  return launch_small_block(U, L, n, n * n, 0, (int)n, k_lo, k_hi, batch, s, prof);
 }
 
 }  // namespace dbs

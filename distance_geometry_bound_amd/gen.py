@@ -37,8 +37,8 @@ MAX_TRIES = 1000       # failed placements before a chain restarts
 
 __all__ = [
     "Molecule", "Workload", "WORKLOADS", "round_down", "round_up",
-    "walk_chain", "sphere_chains", "bounds_from_coords", "make_molecule",
-    "make_workload", "random_bounds", "random_sound_bounds",
+    "walk_chain", "sphere_chains", "restraints_from_coords", "bounds_from_coords",
+    "make_molecule", "molecule_restraints", "make_workload", "workload_restraints", "random_bounds", "random_sound_bounds",
     "random_directed_bounds", "true_distances",
 ]
 
@@ -197,26 +197,19 @@ def _diameter(X: np.ndarray) -> float:
     return best
 
 
-def bounds_from_coords(X: np.ndarray, chain_len: int, rng, *, cutoff: float,
-                       p: float, halfwidth, unknown_L: float,
-                       unknown_U: float | None) -> tuple[np.ndarray, np.ndarray]:
-    """Dense symmetric [n,n] float32 (U, L) from coordinates.
+def restraints_from_coords(X: np.ndarray, chain_len: int, rng, *, cutoff: float, p: float,
+                           halfwidth):
+    """The measured pairs of a molecule, before rounding.
 
-    * bonded neighbours (i, i+1) of one chain: the true distance, rounded out;
+    * bonded neighbours (i, i+1) of one chain: the true distance d as [d, d];
     * other pairs with d < cutoff, each kept with probability p: [d-w, d+w]
-      (w a number, or w ~ U(lo, hi) per pair when `halfwidth` is a pair);
-    * every other pair: [unknown_L, unknown_U]; unknown_U None means the
-      molecular diameter (largest true distance), rounded up;
-    * diagonal 0.
+      (w a number, or w ~ U(lo, hi) per pair when `halfwidth` is a pair).
     Random draws: one uniform per candidate pair for the keep decision, then
     one half-width per candidate when it is drawn, both in sorted pair order.
+    Returns (ia, ja, lo, hi): int64 atom indices (i < j) and float64 bounds,
+    kept pairs first, then the bonded neighbours.
     """
     n = X.shape[0]
-    if unknown_U is None:
-        unknown_U = float(round_up(_diameter(X))) if n > 1 else 0.0
-    U = np.full((n, n), unknown_U, dtype=np.float32)
-    L = np.full((n, n), unknown_L, dtype=np.float32)
-
     pr, d = _pairs_within(X, cutoff)
     bonded = (pr[:, 1] == pr[:, 0] + 1) & (pr[:, 0] // chain_len == pr[:, 1] // chain_len)
     cand, dc = pr[~bonded], d[~bonded]
@@ -226,25 +219,49 @@ def bounds_from_coords(X: np.ndarray, chain_len: int, rng, *, cutoff: float,
     else:
         w = np.full(len(cand), float(halfwidth))
     kept = u < p
-    ki, kj = cand[kept, 0], cand[kept, 1]
-    lo = round_down(np.maximum(dc[kept] - w[kept], 0.0)).astype(np.float32)
-    hi = round_up(dc[kept] + w[kept]).astype(np.float32)
-    U[ki, kj] = hi; U[kj, ki] = hi
-    L[ki, kj] = lo; L[kj, ki] = lo
-
-    # bonded neighbours are always known (the distance itself, rounded out)
     bi = np.arange(n - 1)
     bi = bi[(bi // chain_len) == ((bi + 1) // chain_len)]
     bd = np.sqrt(((X[bi] - X[bi + 1]) ** 2).sum(-1))
-    blo = round_down(bd).astype(np.float32)
-    bhi = round_up(bd).astype(np.float32)
-    U[bi, bi + 1] = bhi; U[bi + 1, bi] = bhi
-    L[bi, bi + 1] = blo; L[bi + 1, bi] = blo
+    ia = np.concatenate([cand[kept, 0], bi])
+    ja = np.concatenate([cand[kept, 1], bi + 1])
+    lo = np.concatenate([dc[kept] - w[kept], bd])
+    hi = np.concatenate([dc[kept] + w[kept], bd])
+    return ia, ja, lo, hi
 
+
+def bounds_from_coords(X: np.ndarray, chain_len: int, rng, *, cutoff: float,
+                       p: float, halfwidth, unknown_L: float,
+                       unknown_U: float | None) -> tuple[np.ndarray, np.ndarray]:
+    """Dense symmetric [n,n] float32 (U, L) from coordinates.
+
+    Every measured pair of restraints_from_coords gets its interval rounded
+    outward (the lower end clipped at 0); every other pair gets
+    [unknown_L, unknown_U], where unknown_U None means the molecular diameter
+    (largest true distance) rounded up; the diagonal is 0.
+    """
+    n = X.shape[0]
+    if unknown_U is None:
+        unknown_U = float(round_up(_diameter(X))) if n > 1 else 0.0
+    U = np.full((n, n), unknown_U, dtype=np.float32)
+    L = np.full((n, n), unknown_L, dtype=np.float32)
+    ia, ja, lo, hi = restraints_from_coords(X, chain_len, rng, cutoff=cutoff, p=p,
+                                            halfwidth=halfwidth)
+    lo = round_down(np.maximum(lo, 0.0)).astype(np.float32)
+    hi = round_up(hi).astype(np.float32)
+    U[ia, ja] = hi; U[ja, ia] = hi
+    L[ia, ja] = lo; L[ja, ia] = lo
     idx = np.arange(n)
     U[idx, idx] = 0.0
     L[idx, idx] = 0.0
     return U, L
+
+
+def _molecule_setup(n: int, seed: int, chains: int, radius):
+    if chains == 1:
+        return walk_chain(n, seed), max(n, 1)
+    if n % chains:
+        raise ValueError("n must be a multiple of chains")
+    return sphere_chains(chains, n // chains, radius, seed), n // chains
 
 
 def make_molecule(n: int, seed: int, *, cutoff: float = 5.0, p: float = 0.5,
@@ -252,19 +269,30 @@ def make_molecule(n: int, seed: int, *, cutoff: float = 5.0, p: float = 0.5,
                   unknown_U: float | None = None, chains: int = 1,
                   radius: float | None = None) -> Molecule:
     """One molecule of n atoms (a single walk, or `chains` walks in a sphere)."""
-    if chains == 1:
-        X = walk_chain(n, seed)
-        chain_len = max(n, 1)
-    else:
-        if n % chains:
-            raise ValueError("n must be a multiple of chains")
-        chain_len = n // chains
-        X = sphere_chains(chains, chain_len, radius, seed)
+    X, chain_len = _molecule_setup(n, seed, chains, radius)
     rng = np.random.default_rng([seed, 0xB0])
     U, L = bounds_from_coords(X, chain_len, rng, cutoff=cutoff, p=p,
                               halfwidth=halfwidth, unknown_L=unknown_L,
                               unknown_U=unknown_U)
     return Molecule(U=U, L=L, X=X, chain_len=chain_len)
+
+
+def molecule_restraints(n: int, seed: int, *, cutoff: float = 5.0, p: float = 0.5,
+                        halfwidth=0.5, unknown_L: float = 0.0,
+                        unknown_U: float | None = None, chains: int = 1,
+                        radius: float | None = None):
+    """The restraint list behind make_molecule (same arguments, same draws).
+
+    Returns (ia, ja, lo, hi, unknown_L, unknown_U): the measured pairs with
+    their unrounded float64 intervals, and the placeholders (unknown_U None
+    becomes the molecular diameter, rounded up)."""
+    X, chain_len = _molecule_setup(n, seed, chains, radius)
+    rng = np.random.default_rng([seed, 0xB0])
+    if unknown_U is None:
+        unknown_U = float(round_up(_diameter(X))) if n > 1 else 0.0
+    ia, ja, lo, hi = restraints_from_coords(X, chain_len, rng, cutoff=cutoff, p=p,
+                                            halfwidth=halfwidth)
+    return ia, ja, lo, hi, unknown_L, unknown_U
 
 
 @dataclass
@@ -313,6 +341,29 @@ def make_workload(name: str, batch: int | None = None) -> Workload:
         U[b], L[b] = m.U, m.L
         Xs.append(m.X)
     return Workload(name=name, n=n, batch=len(seeds), U=U, L=L, X=Xs)
+
+
+def workload_restraints(name: str, batch: int | None = None):
+    """Restraint lists of a named workload (molecule b's list has mol == b).
+
+    Returns (mol, ia, ja, lo, hi, unknown_L, unknown_U, n, nbatch) with int32
+    indices and float32 intervals (the unrounded values cast to float32), the
+    form the GPU library takes.  The placeholders must agree across the
+    batch; for the diameter-placeholder workloads the largest diameter is
+    used.
+    """
+    spec = _workload_spec(name)
+    seeds = spec["seeds"] if batch is None else spec["seeds"][:batch]
+    parts, uL, uU = [], None, 0.0
+    for b, s in enumerate(seeds):
+        ia, ja, lo, hi, ul, uu = molecule_restraints(spec["n"], s, **spec["kw"])
+        parts.append((np.full(len(ia), b), ia, ja, lo, hi))
+        uL = ul
+        uU = max(uU, uu)
+    cat = [np.concatenate([p_[k] for p_ in parts]) for k in range(5)]
+    return (cat[0].astype(np.int32), cat[1].astype(np.int32), cat[2].astype(np.int32),
+            cat[3].astype(np.float32), cat[4].astype(np.float32), float(uL), float(uU),
+            spec["n"], len(seeds))
 
 
 def random_bounds(n: int, seed: int, *, umax_units: int = 256, batch: int | None = None):

@@ -140,7 +140,77 @@ int dbs_smooth_profiled(float *U, float *L, int64_t n, int64_t batch, void *stre
 #define DBS_PROF_MIRROR 4  /* blocked: final transposed copy                   */
 #define DBS_PROF_STRIP 5   /* blocked phase 3 on the next k-block's band, run
                               ahead on a second stream                        */
-#define DBS_PROF_KINDS 6
+#define DBS_PROF_FILL 6    /* restraints: placeholder fill                     */
+#define DBS_PROF_SCATTER 7 /* restraints: interval scatter                     */
+#define DBS_PROF_KINDS 8
+
+/*
+ * dbs_smooth_range -- rounds k_begin..k_end-1 of a pass, in place: the state
+ * after the first rounds of a pass, or the rest of a pass resumed from it
+ * (the notes' §5 experiment steps the number of finished rounds).
+ * 0 <= k_begin <= k_end <= n, else DBS_EINVAL; k_begin == k_end is a no-op.
+ * `algo`: DBS_ALGO_PERK runs one launch per round; DBS_ALGO_LDS (n <=
+ * dbs_lds_max_n()) runs the range in one workgroup per molecule;
+ * DBS_ALGO_BLOCKED needs both ends on k-block boundaries (multiples of
+ * dbs_block_rounds(), or k_end == n; else DBS_EUNSUPPORTED); DBS_ALGO_AUTO
+ * takes LDS when it fits, else BLOCKED when the ends allow it, else PERK.
+ * Every algorithm gives the same bits.  The input must meet the
+ * preconditions above (it does when it is the output of earlier ranges).
+ */
+int dbs_smooth_range(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
+                     int64_t k_end, void *stream, int algo);
+
+/* Rounds per k-block of the blocked algorithm (64). */
+int dbs_block_rounds(void);
+
+/*
+ * dbs_tightened -- which cells a smoothing step changed (the notes' §5 marks
+ * the entries tightened relative to the initial bounds).  mask[b][i][j] = 1
+ * if U1 or L1 differs bit for bit from U0 or L0 at (b,i,j), else 0.
+ *   U0, L0, U1, L1  device [batch][n][n] float32, read only.
+ *   mask            device [batch][n][n] uint8, written.
+ * Same argument errors as dbs_smooth (mask must be non-null; the four inputs
+ * may alias each other but not mask).
+ */
+int dbs_tightened(const float *U0, const float *L0, const float *U1, const float *L1,
+                  int64_t n, int64_t batch, uint8_t *mask, void *stream);
+
+/*
+ * dbs_bounds_from_restraints -- dense bound matrices from a list of distance
+ * restraints, the input the notes describe in §1: the experiment gives an
+ * interval for some pairs; every other pair starts at a placeholder (the
+ * molecular diameter above, about zero below).  For every molecule b:
+ *   off the diagonal  L = unknown_L rounded down, U = unknown_U rounded up;
+ *   on the diagonal   L = U = +0;
+ *   then each restraint r of molecule b on the pair (i,j), i != j, tightens
+ *   both (i,j) and (j,i):  L = max(L, round_down(max(lo[r], 0))),
+ *                          U = min(U, round_up(hi[r])).
+ * Rounding is outward to multiples of 2^-6 (down for lower bounds, up for
+ * upper bounds), so the bounds stay sound and exactly representable.
+ * Duplicate restraints of a pair combine to the tightest interval, in any
+ * order.  Restraints with i == j are ignored.
+ *   U, L        device [batch][n][n] float32, written (every entry).
+ *   unknown_L, unknown_U  host values, finite, 0 <= unknown_L <= unknown_U
+ *               < 2^17, else DBS_EINVAL.
+ *   mol         device int32[count]: molecule of each restraint; may be NULL
+ *               when batch == 1.
+ *   ia, ja      device int32[count]: the two atoms of each restraint.
+ *   lo, hi      device float32[count]: the interval of each restraint.
+ *   count       number of restraints, >= 0 (0: placeholders only).
+ *   d_status    device uint32 into which the kernel ORs DBS_RESTRAINT_* bits
+ *               (caller zeroes; may be NULL).  A flagged restraint is skipped.
+ * DBS_EINVAL for a null U, L, ia, ja, lo or hi (with count > 0), for a null
+ * mol with batch > 1 and count > 0, or for the size checks of dbs_smooth.
+ */
+int dbs_bounds_from_restraints(float *U, float *L, int64_t n, int64_t batch,
+                               float unknown_L, float unknown_U, const int32_t *mol,
+                               const int32_t *ia, const int32_t *ja, const float *lo,
+                               const float *hi, int64_t count, uint32_t *d_status,
+                               void *stream);
+
+#define DBS_RESTRAINT_INDEX 1u  /* molecule or atom index out of range        */
+#define DBS_RESTRAINT_VALUE 2u  /* NaN or infinite value, lo > hi, hi < 0, or
+                                   |value| >= 2^17                            */
 
 /* Largest n the LDS algorithm accepts. */
 int dbs_lds_max_n(void);

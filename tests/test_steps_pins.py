@@ -1,0 +1,82 @@
+"""Pins of the oracle's restraint-to-bounds and tightened-mask definitions."""
+import numpy as np
+import pytest
+
+from distance_geometry_bound_amd import gen
+from oracle import steps
+
+
+def test_hand_case_rounding_duplicates_and_skips():
+    ia = [0, 1, 2, 3, 0, 5, 1, 2, 2]
+    ja = [1, 0, 2, 0, 2, 1, 3, 3, 3]
+    lo = [1.001, 1.5, 7.0, -1.0, 2.0, 1.0, np.nan, 4.0, 2.0]
+    hi = [2.999, 2.5, 9.0, 0.5, 1.0, 2.0, 3.0, 4.0, 6.0]
+    U, L, st = steps.bounds_from_restraints(4, 1, 0.0, 20.0, ia, ja, lo, hi)
+    U, L = U[0], L[0]
+    # (0,1): [1.001, 2.999] -> [64/64, 192/64] = [1.0, 3.0]; duplicate (1,0)
+    # [1.5, 2.5] tightens to [1.5, 2.5]
+    assert (L[0, 1], U[0, 1]) == (1.5, 2.5) and (L[1, 0], U[1, 0]) == (1.5, 2.5)
+    # (2,2) ignored; (3,0): lo < 0 clips to 0, hi 0.5 -> [0, 0.5]
+    assert U[2, 2] == 0 and L[2, 2] == 0
+    assert (L[3, 0], U[3, 0]) == (0.0, 0.5) and (L[0, 3], U[0, 3]) == (0.0, 0.5)
+    # (0,2) has lo > hi, (5,1) an index out of range, (1,3) a NaN: all skipped
+    assert (L[0, 2], U[0, 2]) == (0.0, 20.0) and (L[1, 3], U[1, 3]) == (0.0, 20.0)
+    assert st == steps.INDEX | steps.VALUE
+    # (2,3) twice: [4, 4] and [2, 6] -> [4, 4]
+    assert (L[2, 3], U[2, 3]) == (4.0, 4.0)
+    # placeholders elsewhere, zero diagonal
+    assert (L[1, 2], U[1, 2]) == (0.0, 20.0)
+    assert np.all(np.diag(U) == 0) and np.all(np.diag(L) == 0)
+
+
+def test_placeholders_are_rounded_outward():
+    U, L, _ = steps.bounds_from_restraints(3, 2, 0.3, 7.001, [], [], [], [], mol=[])
+    assert L[1, 0, 1] == np.floor(0.3 * 64) / 64 and U[0, 2, 1] == np.ceil(7.001 * 64) / 64
+
+
+def test_range_limit_flags():
+    big = 2.0 ** 17
+    U, L, st = steps.bounds_from_restraints(3, 1, 0.0, 10.0, [0, 0], [1, 2], [1.0, 1.0],
+                                            [big - 1e-3, big - 1.0])
+    assert st == steps.VALUE          # the first rounds up to 2^17 and is skipped
+    assert L[0, 0, 1] == 0.0 and L[0, 0, 2] == 1.0 and U[0, 0, 2] == 10.0
+
+
+@pytest.mark.parametrize("name,batch", [("n128", None), ("b64n500", 3), ("n1024", None),
+                                        ("n4096", None)])
+def test_matches_generator_dense_bounds(name, batch):
+    # the generator builds its dense bounds with its own code; the oracle
+    # rebuilt from the generator's (float64) restraint list must agree
+    W = gen.make_workload(name, batch=batch)
+    spec = gen._workload_spec(name)
+    for b in range(W.batch):
+        ia, ja, lo, hi, ul, uu = gen.molecule_restraints(W.n, spec["seeds"][b], **spec["kw"])
+        U, L, st = steps.bounds_from_restraints(W.n, 1, ul, uu, ia, ja, lo, hi)
+        assert st == 0
+        assert np.array_equal(U[0], W.U[b]) and np.array_equal(L[0], W.L[b])
+
+
+def test_restraint_order_does_not_matter():
+    rng = np.random.default_rng(3)
+    n, m = 20, 300
+    ia, ja = rng.integers(0, n, m), rng.integers(0, n, m)
+    lo = rng.uniform(0, 10, m)
+    hi = lo + rng.uniform(0, 10, m)
+    a = steps.bounds_from_restraints(n, 1, 0.5, 30.0, ia, ja, lo, hi)
+    p = rng.permutation(m)
+    b = steps.bounds_from_restraints(n, 1, 0.5, 30.0, ia[p], ja[p], lo[p], hi[p])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_tightened_definition():
+    U0 = np.array([[0, 2], [2, 0]], np.float32)
+    L0 = np.array([[0, 1], [1, 0]], np.float32)
+    U1, L1 = U0.copy(), L0.copy()
+    U1[0, 1] = 1.5
+    L1[1, 0] = 1.25
+    m = steps.tightened(U0, L0, U1, L1)
+    assert m.tolist() == [[0, 1], [1, 0]]
+    # -0.0 and +0.0 differ bit for bit
+    U2 = U0.copy()
+    U2[0, 0] = -0.0
+    assert steps.tightened(U0, L0, U2, L0)[0, 0] == 1
