@@ -16,6 +16,8 @@ Printed: one JSON line with
                (16 B per cell per round) / mean round time
   restraints   the workload's restraint list to dense bounds (fill + scatter)
   tightened    the mask of cells a pass changed
+  packed       the same pass on the one-buffer layout (U above the diagonal,
+               L below), with the pack and unpack steps timed apart
   cpu_baseline the CPU reference (oracle) on a bounded prefix of rounds of
                the same workload, on this host's cores
 Run with --gpus N > 1 and it exits: this build runs on one GPU.
@@ -158,6 +160,43 @@ def extra_steps(W, U, L, U0, L0, dev, reps=3):
                         "GBps": 17.0 * cells / (ms * 1e-3) / 1e9,
                         "frac_hbm": 17.0 * cells / (ms * 1e-3) / HBM_PEAK}
     return res
+
+
+def packed_pass(U0, L0, dev, reps=2):
+    """Time the one-buffer layout on the same workload: pack (reads 8, writes
+    4 bytes per cell), one full pass in place on the packed buffer, unpack
+    (reads 8, writes 8 bytes per cell)."""
+    import torch
+
+    import distance_geometry_bound_amd as dgb
+
+    s = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    P0 = dgb.pack(U0, L0)
+    P = torch.empty_like(P0)
+    P.copy_(P0)
+    dgb.smooth_packed(P)                     # warm
+    ms = [0.0, 0.0, 0.0]
+    for _ in range(reps):
+        P.copy_(P0)
+        ev[0].record(s)
+        dgb.pack(U0, L0, out=P)
+        ev[1].record(s)
+        dgb.smooth_packed(P)
+        ev[2].record(s)
+        dgb.unpack(P)
+        ev[3].record(s)
+        torch.cuda.synchronize(dev)
+        for i in range(3):
+            ms[i] += ev[i].elapsed_time(ev[i + 1]) / reps
+    n, batch = U0.shape[-1], U0.numel() // (U0.shape[-1] ** 2)
+    triples = float(n) ** 3 * batch
+    cells = n * n * batch
+    return {"pass_ms": ms[1], "value": 2.0 * triples / (ms[1] * 1e-3),
+            "pct_fp32_valu_peak": OPS_PER_TRIPLE * triples / (ms[1] * 1e-3) / FP32_VALU_PEAK,
+            "pack_ms": ms[0], "pack_GBps": 12.0 * cells / (ms[0] * 1e-3) / 1e9,
+            "unpack_ms": ms[2], "unpack_GBps": 16.0 * cells / (ms[2] * 1e-3) / 1e9,
+            "bytes": 4 * cells}
 
 
 def cpu_baseline(W, target_s):
@@ -310,6 +349,7 @@ def main():
 
     if args.steps_extra:
         out.update(extra_steps(W, U, L, U0, L0, dev))
+        out["packed"] = packed_pass(U0, L0, dev)
 
     if not args.no_cpu and args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

@@ -26,6 +26,8 @@ DBS_OK, DBS_EINVAL, DBS_EDEVICE, DBS_ELAUNCH, DBS_EUNSUPPORTED = 0, -1, -2, -3, 
 
 EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
            "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened", "dbs_bounds_from_restraints",
+           "dbs_pack", "dbs_unpack", "dbs_smooth_packed", "dbs_smooth_packed_range",
+           "dbs_check_packed",
            "dbs_lds_max_n", "dbs_auto_algo", "dbs_strerror", "dbs_version")
 
 RESTRAINT_FLAGS = {"index": 1, "value": 2}
@@ -58,15 +60,22 @@ def lib():
         L.dbs_rounds.argtypes = [vp, vp, i64, i64, i64, i64, vp]
         L.dbs_smooth_range.argtypes = [vp, vp, i64, i64, i64, i64, vp, c_int]
         L.dbs_tightened.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp]
+        L.dbs_pack.argtypes = [vp, vp, vp, i64, i64, vp]
+        L.dbs_unpack.argtypes = [vp, vp, vp, i64, i64, vp]
+        L.dbs_smooth_packed.argtypes = [vp, i64, i64, vp]
+        L.dbs_smooth_packed_range.argtypes = [vp, i64, i64, i64, i64, vp]
         L.dbs_bounds_from_restraints.argtypes = [vp, vp, i64, i64, ctypes.c_float,
                                                  ctypes.c_float, vp, vp, vp, vp, vp, i64, vp, vp]
         L.dbs_check.argtypes = [vp, vp, i64, i64, vp, vp]
+        L.dbs_check_packed.argtypes = [vp, i64, i64, vp, vp]
         L.dbs_auto_algo.argtypes = [i64, i64]
         L.dbs_strerror.argtypes = [c_int]
         L.dbs_strerror.restype = ctypes.c_char_p
         for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
                   "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened",
-                  "dbs_bounds_from_restraints", "dbs_lds_max_n", "dbs_auto_algo", "dbs_version"):
+                  "dbs_bounds_from_restraints", "dbs_pack", "dbs_unpack", "dbs_smooth_packed",
+                  "dbs_smooth_packed_range", "dbs_check_packed", "dbs_lds_max_n", "dbs_auto_algo",
+                  "dbs_version"):
             getattr(L, f).restype = c_int
         _lib = L
     return _lib
@@ -217,6 +226,52 @@ def bounds_from_restraints(n: int, ia, ja, lo, hi, unknown_L: float, unknown_U: 
     return U, L, int(status.item()) & 0xFFFFFFFF
 
 
+def _shape1(P):
+    import torch
+
+    if not isinstance(P, torch.Tensor) or P.dtype != torch.float32:
+        raise TypeError("P must be a float32 torch.Tensor")
+    if P.device.type != "cuda" or not P.is_contiguous():
+        raise ValueError("P must be a contiguous GPU tensor")
+    if P.dim() not in (2, 3) or P.shape[-1] != P.shape[-2]:
+        raise ValueError(f"P must be [n,n] or [batch,n,n], got {tuple(P.shape)}")
+    return P.shape[-1], 1 if P.dim() == 2 else P.shape[0]
+
+
+def pack(U, L, out=None):
+    """Packed one-buffer form of symmetric U, L (see dbs_pack)."""
+    import torch
+
+    n, batch = _shape(U, L)
+    P = torch.empty_like(U) if out is None else out
+    if _shape1(P) != (n, batch):
+        raise ValueError("out has the wrong shape")
+    if n and batch:
+        _call(U, lib().dbs_pack, U.data_ptr(), L.data_ptr(), P.data_ptr(), n, batch, _stream(U))
+    return P
+
+
+def unpack(P):
+    """(U, L) from the packed form (see dbs_unpack)."""
+    import torch
+
+    n, batch = _shape1(P)
+    U, L = torch.empty_like(P), torch.empty_like(P)
+    if n and batch:
+        _call(P, lib().dbs_unpack, P.data_ptr(), U.data_ptr(), L.data_ptr(), n, batch, _stream(P))
+    return U, L
+
+
+def smooth_packed(P, k_begin: int = 0, k_end=None) -> None:
+    """Rounds k_begin..k_end-1 (default: a full pass) on the packed form, in place."""
+    n, batch = _shape1(P)
+    if n == 0 or batch == 0:
+        return
+    k_end = n if k_end is None else int(k_end)
+    _call(P, lib().dbs_smooth_packed_range, P.data_ptr(), n, batch, int(k_begin), k_end,
+          _stream(P))
+
+
 def check(U, L) -> int:
     """Precondition flags (CHECK_FLAGS bits) of U, L; synchronises the stream."""
     import torch
@@ -227,6 +282,18 @@ def check(U, L) -> int:
         return 0
     _call(U, lib().dbs_check, U.data_ptr(), L.data_ptr(), n, batch, flags.data_ptr(),
           _stream(U))
+    return int(flags.item()) & 0xFFFFFFFF
+
+
+def check_packed(P) -> int:
+    """Precondition flags of the pair a packed buffer stands for; synchronises."""
+    import torch
+
+    n, batch = _shape1(P)
+    flags = torch.zeros(1, dtype=torch.int32, device=P.device)
+    if n == 0 or batch == 0:
+        return 0
+    _call(P, lib().dbs_check_packed, P.data_ptr(), n, batch, flags.data_ptr(), _stream(P))
     return int(flags.item()) & 0xFFFFFFFF
 
 

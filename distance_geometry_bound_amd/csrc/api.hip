@@ -28,6 +28,22 @@ int device_status() {
   return g_dev_ok[dev] == 1 ? DBS_OK : DBS_EDEVICE;
 }
 
+// Size checks of one [batch][n][n] float buffer; 0 when fine.
+int check_buffer(const void *p, int64_t n, int64_t batch, uint64_t *bytes) {
+  if (!p || n < 1 || batch < 1 || n >= ((int64_t)1 << 31)) return DBS_EINVAL;
+  const int64_t nn = n * n;
+  if (batch > INT64_MAX / 4 / nn) return DBS_EINVAL;
+  *bytes = (uint64_t)(nn * batch) * 4u;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  if (a + *bytes < a || (a & 3u)) return DBS_EINVAL;
+  return DBS_OK;
+}
+
+bool overlap(const void *a, const void *b, uint64_t bytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bytes && y < x + bytes;
+}
+
 // Host-side argument checks shared by every entry point.
 int validate(const void *U, const void *L, int64_t n, int64_t batch) {
   if (!U || !L || n < 1 || batch < 1) return DBS_EINVAL;
@@ -193,6 +209,62 @@ int dbs_bounds_from_restraints(float *U, float *L, int64_t n, int64_t batch, flo
   if (uU >= 131072.0f) return DBS_EINVAL;
   return status_of(dbs::launch_restraints(U, L, n, batch, uL, uU, mol, ia, ja, lo, hi, count,
                                           d_status, static_cast<hipStream_t>(stream)));
+}
+
+int dbs_pack(const float *U, const float *L, float *P, int64_t n, int64_t batch, void *stream) {
+  int st = validate(U, L, n, batch);
+  if (st != DBS_OK) return st;
+  uint64_t bytes = 0;
+  if (check_buffer(P, n, batch, &bytes) != DBS_OK || overlap(P, U, bytes) || overlap(P, L, bytes))
+    return DBS_EINVAL;
+  st = device_status();
+  if (st != DBS_OK) return st;
+  return status_of(dbs::launch_pack(U, L, P, n, batch, static_cast<hipStream_t>(stream)));
+}
+
+int dbs_unpack(const float *P, float *U, float *L, int64_t n, int64_t batch, void *stream) {
+  int st = validate(U, L, n, batch);
+  if (st != DBS_OK) return st;
+  uint64_t bytes = 0;
+  if (check_buffer(P, n, batch, &bytes) != DBS_OK || overlap(P, U, bytes) || overlap(P, L, bytes))
+    return DBS_EINVAL;
+  st = device_status();
+  if (st != DBS_OK) return st;
+  return status_of(dbs::launch_unpack(P, U, L, n, batch, static_cast<hipStream_t>(stream)));
+}
+
+int dbs_smooth_packed_range(float *P, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,
+                            void *stream) {
+  uint64_t bytes = 0;
+  if (check_buffer(P, n, batch, &bytes) != DBS_OK) return DBS_EINVAL;
+  if (k_begin < 0 || k_end > n || k_begin > k_end) return DBS_EINVAL;
+  const int st = device_status();
+  if (st != DBS_OK) return st;
+  if (k_begin == k_end || n == 1) return DBS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t B = dbs::kBlockRounds;
+  // same algorithm choice as dbs_smooth_range with DBS_ALGO_AUTO
+  if (n <= dbs::kSmallMaxN)
+    return status_of(dbs::launch_small(P, P, n, batch, (int)k_begin, (int)k_end, s, nullptr, true));
+  if (k_begin % B == 0 && (k_end % B == 0 || k_end == n))
+    return status_of(dbs::launch_blocked(P, P, n, batch, k_begin / B, dbs::ceil_div(k_end, B), s,
+                                         nullptr, true));
+  hipError_t e = hipSuccess;
+  for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
+    e = dbs::launch_round_packed(P, n, batch, k, s);
+  return status_of(e);
+}
+
+int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags, void *stream) {
+  uint64_t bytes = 0;
+  if (check_buffer(P, n, batch, &bytes) != DBS_OK || !d_flags) return DBS_EINVAL;
+  const int st = device_status();
+  if (st != DBS_OK) return st;
+  return status_of(dbs::launch_check_packed(P, n, batch, d_flags, static_cast<hipStream_t>(stream)));
+}
+
+int dbs_smooth_packed(float *P, int64_t n, int64_t batch, void *stream) {
+  return dbs_smooth_packed_range(P, n, batch, 0, n, stream);
 }
 
 int dbs_lds_max_n(void) { return dbs::kSmallMaxN; }

@@ -70,11 +70,71 @@ __device__ __forceinline__ float4 load4(const float *p, int cnt, float fill, con
 
 __device__ __forceinline__ int clamp4(int64_t left) { return left < 0 ? 0 : (left > 4 ? 4 : (int)left); }
 
+// ---------------------------------------------------------------- packed blocks
+// Packed layout: logical cell (i, j) has U at P[min][max] and L at P[max][min].
+// A BK x BK block of logical cells (r0 + a, c0 + c), a < rows, c < cols, is
+// read into u/l[4][4] of thread (ty, tx) (rows 4ty.., columns 4tx..) from
+// the row segments P[r0+a][c0..] and the column segments P[c0+c][r0..], both
+// as float4.  Right of the diagonal (r0 < c0) the row segments hold U; left
+// of it L; on a diagonal block (r0 == c0) it is decided per cell, and the
+// diagonal itself reads P[i][i] for both.  Cells outside get the neutral
+// values.
+template <bool VEC>
+__device__ __forceinline__ void packed_block_load(const float *P, int64_t n, int64_t r0,
+                                                  int64_t c0, int rows, int cols, int ty, int tx,
+                                                  float (&u)[4][4], float (&l)[4][4]) {
+  float d[4][4], t[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int a = ty * 4 + r;
+    const int cnt = a < rows ? clamp4(cols - tx * 4) : 0;
+    const float4 x = load4<VEC>(P + (r0 + a) * n + c0 + tx * 4, cnt, 0.0f, P);
+    d[r][0] = x.x; d[r][1] = x.y; d[r][2] = x.z; d[r][3] = x.w;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = tx * 4 + q;
+    const int cnt = c < cols ? clamp4(rows - ty * 4) : 0;
+    const float4 y = load4<VEC>(P + (c0 + c) * n + r0 + ty * 4, cnt, 0.0f, P);
+    t[0][q] = y.x; t[1][q] = y.y; t[2][q] = y.z; t[3][q] = y.w;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int a = ty * 4 + r, c = tx * 4 + q;
+      const bool in = a < rows && c < cols;
+      const bool upper = r0 < c0 || (r0 == c0 && a < c);
+      const bool lower = r0 > c0 || (r0 == c0 && a > c);
+      u[r][q] = in ? (lower ? t[r][q] : d[r][q]) : kInf;
+      l[r][q] = in ? (upper ? t[r][q] : d[r][q]) : 0.0f;
+    }
+}
+
+// The inverse of packed_block_load (the diagonal of a diagonal block is not
+// written: its single slot holds U[i][i]).  On a diagonal block cells (a, c)
+// and (c, a) write the same two slots with equal values.
+__device__ __forceinline__ void packed_block_store(float *P, int64_t n, int64_t r0, int64_t c0,
+                                                   int rows, int cols, int ty, int tx,
+                                                   const float (&u)[4][4],
+                                                   const float (&l)[4][4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int a = ty * 4 + r, c = tx * 4 + q;
+      if (a >= rows || c >= cols || (r0 == c0 && a == c)) continue;
+      const bool upper = r0 < c0 || (r0 == c0 && a < c);
+      P[(r0 + a) * n + c0 + c] = upper ? u[r][q] : l[r][q];
+      P[(c0 + c) * n + r0 + a] = upper ? l[r][q] : u[r][q];
+    }
+}
+
 // ---------------------------------------------------------------- phase 2
 // Panel tile R = (K, J) in row orientation, BK x BK, one workgroup each.
 // grid.x = k-block tiles other than K, grid.y = molecules.  Thread (ty, tx)
 // owns rows a = 4ty..4ty+3 and columns c = 4tx..4tx+3.
-template <bool VEC>
+template <bool VEC, bool PK>
 __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float *__restrict__ L,
                                                     int64_t n, int64_t batch, int64_t K) {
   __shared__ float4 du[BK][BK / 4];
@@ -93,11 +153,45 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
     float *Ub = U + b * nn;
-    float *Lb = L + b * nn;
+    float *Lb = PK ? Ub : L + b * nn;
 
     // the finished diagonal tile (both halves current after phase 1): all
     // loads issued before the LDS stores
-    {
+    if (PK) {
+      // the raw P tile (K, K) goes to dl; then U = P[min][max] and
+      // L = P[max][min] are read back out of it
+      float4 xp[BK * BK / 4 / kThreads];
+#pragma unroll
+      for (int t = 0; t < BK * BK / 4 / kThreads; ++t) {
+        const int e = tid + t * kThreads;
+        const int m = e / (BK / 4), a4 = (e % (BK / 4)) * 4;
+        const int cnt = m < bK ? clamp4(bK - a4) : 0;
+        xp[t] = load4<VEC>(Ub + (k0 + m) * n + k0 + a4, cnt, 0.0f, Ub);
+      }
+#pragma unroll
+      for (int t = 0; t < BK * BK / 4 / kThreads; ++t) {
+        const int e = tid + t * kThreads;
+        dl[e / (BK / 4)][e % (BK / 4)] = xp[t];
+      }
+      __syncthreads();
+      const float *raw = reinterpret_cast<const float *>(dl);
+      float xu[BK * BK / kThreads], xl[BK * BK / kThreads];
+#pragma unroll
+      for (int t = 0; t < BK * BK / kThreads; ++t) {
+        const int e = tid + t * kThreads, m = e / BK, a = e % BK;
+        const int lo = m < a ? m : a, hi = m < a ? a : m;
+        const bool in = m < bK && a < bK;
+        xu[t] = in ? raw[lo * BK + hi] : kInf;
+        xl[t] = in ? raw[hi * BK + lo] : 0.0f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < BK * BK / kThreads; ++t) {
+        const int e = tid + t * kThreads;
+        reinterpret_cast<float *>(du)[e] = xu[t];
+        reinterpret_cast<float *>(dl)[e] = xl[t];
+      }
+    } else {
       float4 xu[BK * BK / 4 / kThreads], xl[BK * BK / 4 / kThreads];
 #pragma unroll
       for (int t = 0; t < BK * BK / 4 / kThreads; ++t) {
@@ -117,7 +211,9 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
     }
 
     float u[4][4], l[4][4];
-    if (rowor) {
+    if (PK) {
+      packed_block_load<VEC>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
+    } else if (rowor) {
       // R[a][c] = M[k0+a][j0+c]
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -164,13 +260,14 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
       }
     }
 
-    // write both orientations
+    // write both orientations (packed: the one slot of U and of L)
+    if (PK) packed_block_store(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int a = ty * 4 + r, c = tx * 4 + q;
-        if (a < bK && c < bJ) {
+        if (!PK && a < bK && c < bJ) {
           Ub[(k0 + a) * n + j0 + c] = u[r][q];
           Lb[(k0 + a) * n + j0 + c] = l[r][q];
           Ub[(j0 + c) * n + k0 + a] = u[r][q];
@@ -181,14 +278,57 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
   }
 }
 
-// ---------------------------------------------------------------- phase 3
-__device__ __forceinline__ int64_t tri_col(int64_t p) {
-  // p -> J with J(J+1)/2 <= p < (J+1)(J+2)/2
-  int64_t J = (int64_t)((sqrt(8.0 * (double)p + 1.0) - 1.0) * 0.5);
-  while (J * (J + 1) / 2 > p) --J;
-  while ((J + 1) * (J + 2) / 2 <= p) ++J;
-  return J;
+
+// ---------------------------------------------------------------- packed panel staging
+// Packed layout: the panel values of band K at the 64 columns xh..xh+63 and
+// rows k0+kc..k0+kc+KC-1 are U[k][x] = P[min(k,x)][max(k,x)] and
+// L[k][x] = P[max(k,x)][min(k,x)].  Right of the band (x > k) U is a row
+// segment of P and L a column segment; left of it the other way round.  A
+// column segment is read as rows of P, four consecutive k per float4.  Each
+// of the 256 threads loads one float4 of each kind.  `dead` (band K, band
+// K+1 or beyond n: values no live cell uses) gives the neutral values.
+struct HalfLoad {
+  float4 direct, across;
+};
+
+template <bool VEC>
+__device__ __forceinline__ HalfLoad packed_half_load(const float *P, int64_t n, int64_t k0,
+                                                     int kc, int bK, int64_t xh, bool right,
+                                                     bool dead, int tid) {
+  HalfLoad h;
+  {
+    const int kk = tid / (BK / 4), x4 = tid % (BK / 4);
+    const int64_t x = xh + 4 * x4;
+    const int cnt = (!dead && kc + kk < bK) ? clamp4(n - x) : 0;
+    h.direct = load4<VEC>(P + (k0 + kc + kk) * n + x, cnt, right ? kInf : 0.0f, P);
+  }
+  {
+    const int xt = tid / (KC / 4), kq = tid % (KC / 4);
+    const int64_t x = xh + xt;
+    const int cnt = (!dead && x < n) ? clamp4(bK - (kc + 4 * kq)) : 0;
+    h.across = load4<VEC>(P + x * n + k0 + kc + 4 * kq, cnt, right ? 0.0f : kInf, P);
+  }
+  return h;
 }
+
+// Store a HalfLoad into LDS arrays su, sl ([KC][stride] floats) at column col.
+__device__ __forceinline__ void packed_half_store(const HalfLoad &h, bool right, float *su,
+                                                  float *sl, int stride, int col, int tid) {
+  float *dst_direct = right ? su : sl, *dst_across = right ? sl : su;
+  {
+    const int kk = tid / (BK / 4), x4 = tid % (BK / 4);
+    *reinterpret_cast<float4 *>(dst_direct + kk * stride + col + 4 * x4) = h.direct;
+  }
+  {
+    const int xt = tid / (KC / 4), kq = tid % (KC / 4);
+    dst_across[(4 * kq + 0) * stride + col + xt] = h.across.x;
+    dst_across[(4 * kq + 1) * stride + col + xt] = h.across.y;
+    dst_across[(4 * kq + 2) * stride + col + xt] = h.across.z;
+    dst_across[(4 * kq + 3) * stride + col + xt] = h.across.w;
+  }
+}
+
+// ---------------------------------------------------------------- phase 3
 
 // Tiles are numbered column-major over the upper triangle.  The hardware
 // deals consecutive workgroups to the 8 XCDs in turn, so at any moment an
@@ -201,7 +341,7 @@ __device__ __forceinline__ int64_t tri_col(int64_t p) {
 // band, updated ahead by k_strip; s1 < 0 for none) are neither read nor
 // written, and band s1's panel columns are not read: while this kernel runs,
 // another stream may be updating exactly those cells.
-template <bool VEC>
+template <bool VEC, bool PK>
 __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
                                                        float *__restrict__ L, int64_t n,
                                                        int64_t batch, int64_t K, int64_t s1) {
@@ -235,8 +375,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
     float *Ub = U + b * nn;
-    float *Lb = L + b * nn;
+    float *Lb = PK ? Ub : L + b * nn;
 
+    // U (and dense L) at (i, j); packed U is P tile (I, J) itself
     float u[8][8], l[8][8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -247,15 +388,69 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
         const bool on = ((rmask >> r) & (cmask >> (h * 4)) & 1u) != 0;
         const int cnt = on ? (VEC ? 4 : clamp4(n - j)) : 0;
         const float4 x = load4<VEC>(Ub + i * n + j, cnt, kInf, Ub);
-        const float4 y = load4<VEC>(Lb + i * n + j, cnt, 0.0f, Lb);
         u[r][h * 4 + 0] = x.x; u[r][h * 4 + 1] = x.y; u[r][h * 4 + 2] = x.z; u[r][h * 4 + 3] = x.w;
-        l[r][h * 4 + 0] = y.x; l[r][h * 4 + 1] = y.y; l[r][h * 4 + 2] = y.z; l[r][h * 4 + 3] = y.w;
+        if (!PK) {
+          const float4 y = load4<VEC>(Lb + i * n + j, cnt, 0.0f, Lb);
+          l[r][h * 4 + 0] = y.x; l[r][h * 4 + 1] = y.y; l[r][h * 4 + 2] = y.z; l[r][h * 4 + 3] = y.w;
+        }
+      }
+    }
+    if (PK) {
+      // packed L(i,j) = P[j][i] (tile (J, I) read across): for each column j
+      // two float4 along i
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int64_t j = j0 + rofs(tx, c);
+#pragma unroll
+        for (int hr = 0; hr < 2; ++hr) {
+          const int64_t i = i0 + rofs(ty, hr * 4);
+          const bool on = ((cmask >> c) & (rmask >> (hr * 4)) & 1u) != 0;
+          const int cnt = on ? (VEC ? 4 : clamp4(n - i)) : 0;
+          const float4 t = load4<VEC>(Ub + j * n + i, cnt, 0.0f, Ub);
+          l[hr * 4 + 0][c] = t.x; l[hr * 4 + 1][c] = t.y; l[hr * 4 + 2][c] = t.z; l[hr * 4 + 3][c] = t.w;
+        }
+      }
+      if (I == J) {
+        // a diagonal tile: below the diagonal P[i][j] is L(i,j) and P[j][i] is U(i,j)
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const int64_t i = i0 + rofs(ty, r), j = j0 + rofs(tx, c);
+            if (i > j) {
+              const float t = u[r][c];
+              u[r][c] = l[r][c];
+              l[r][c] = t;
+            } else if (i == j) {
+              l[r][c] = u[r][c];
+            }
+          }
       }
     }
 
     for (int kc = 0; kc < bK; kc += KC) {
       // stage panel rows k0+kc .. k0+kc+KC-1, columns of I and of J: every
       // global load of the chunk is issued before the first LDS store
+      if (PK) {
+        // addresses recomputed per chunk (not hoisted out of the k loop)
+        int tl = tid;
+        asm volatile("" : "+v"(tl));
+        HalfLoad hl[4];
+        bool right[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t xh = (q < 2 ? i0 : j0) + (q & 1) * (TILE / 2);
+          right[q] = xh > k0;
+          const bool dead = xh == k0 || xh == s1 || xh >= n;
+          hl[q] = packed_half_load<VEC>(Ub, n, k0, kc, bK, xh, right[q], dead, tl);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          packed_half_store(hl[q], right[q],
+                            reinterpret_cast<float *>(q < 2 ? &scu[0][0] : &sru[0][0]),
+                            reinterpret_cast<float *>(q < 2 ? &scl[0][0] : &srl[0][0]), TILE,
+                            (q & 1) * (TILE / 2), tl);
+      } else {
       constexpr int kIter = KC * (TILE / 4) / kThreads;
       float4 st[kIter][4];
 #pragma unroll
@@ -280,6 +475,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
         scl[kk][x4] = st[it][1];
         sru[kk][x4] = st[it][2];
         srl[kk][x4] = st[it][3];
+      }
       }
       __syncthreads();
 
@@ -310,16 +506,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
       __syncthreads();
     }
 
+    // the store addresses are recomputed here rather than kept live across
+    // the k loop from the loads
+    int ts = tid;
+    asm volatile("" : "+v"(ts));
+    const int sy = ts >> 4, sx = ts & 15;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       if (!((rmask >> r) & 1u)) continue;
-      float *pu = Ub + (i0 + rofs(ty, r)) * n + j0;
-      float *pl = Lb + (i0 + rofs(ty, r)) * n + j0;
+      const int64_t i = i0 + rofs(sy, r);
+      float *pu = Ub + i * n + j0;
+      float *pl = Lb + i * n + j0;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        if ((cmask >> c) & 1u) {
-          pu[rofs(tx, c)] = u[r][c];
-          pl[rofs(tx, c)] = l[r][c];
+        if (!((cmask >> c) & 1u)) continue;
+        const int64_t j = j0 + rofs(sx, c);
+        if (!PK) {
+          pu[rofs(sx, c)] = u[r][c];
+          pl[rofs(sx, c)] = l[r][c];
+        } else if (I != J) {
+          Ub[i * n + j] = u[r][c];
+          Ub[j * n + i] = l[r][c];
+        } else if (i != j) {
+          Ub[i * n + j] = i < j ? u[r][c] : l[r][c];
         }
       }
     }
@@ -331,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
 // band K+1 and j outside band K, each kept in its fresh orientation.
 // grid.x = k-block tiles J other than K (one BK x BK tile each),
 // grid.y = molecules.  Thread (ty, tx) owns a 4x4 cell tile.
-template <bool VEC>
+template <bool VEC, bool PK>
 __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float *__restrict__ L,
                                                     int64_t n, int64_t batch, int64_t K) {
   __shared__ float4 scu[KC][BK / 4];
@@ -351,11 +560,13 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
     float *Ub = U + b * nn;
-    float *Lb = L + b * nn;
+    float *Lb = PK ? Ub : L + b * nn;
 
     // logical cell (a, c) = (s1 + a, j0 + c); stored at (s1+a, j0+c) or (j0+c, s1+a)
     float u[4][4], l[4][4];
-    if (rowor) {
+    if (PK) {
+      packed_block_load<VEC>(Ub, n, s1, j0, b1, bJ, ty, tx, u, l);
+    } else if (rowor) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int a = ty * 4 + r;
@@ -378,7 +589,15 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
     }
 
     for (int kc = 0; kc < bK; kc += KC) {
-      {
+      if (PK) {
+        // band K+1 lies right of band K; band J right or left of it
+        const HalfLoad hc = packed_half_load<VEC>(Ub, n, k0, kc, bK, s1, true, false, tid);
+        const HalfLoad hr = packed_half_load<VEC>(Ub, n, k0, kc, bK, j0, J > K, false, tid);
+        packed_half_store(hc, true, reinterpret_cast<float *>(&scu[0][0]),
+                          reinterpret_cast<float *>(&scl[0][0]), BK, 0, tid);
+        packed_half_store(hr, J > K, reinterpret_cast<float *>(&sru[0][0]),
+                          reinterpret_cast<float *>(&srl[0][0]), BK, 0, tid);
+      } else {
         // KC x BK/4 float4 per array: one of each per thread
         const int kk = tid / (BK / 4), x4 = tid % (BK / 4);
         const int64_t k = k0 + kc + kk;
@@ -409,12 +628,13 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
       __syncthreads();
     }
 
+    if (PK) packed_block_store(Ub, n, s1, j0, b1, bJ, ty, tx, u, l);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int a = ty * 4 + r, c = tx * 4 + q;
-        if (a < b1 && c < bJ) {
+        if (!PK && a < b1 && c < bJ) {
           const int64_t g = rowor ? (s1 + a) * n + j0 + c : (j0 + c) * n + s1 + a;
           Ub[g] = u[r][q];
           Lb[g] = l[r][q];
@@ -513,7 +733,7 @@ Events *thread_events() {
 // (for band K+1) reads.  Events order strip(K) after tiles(K-1), and
 // tiles(K+1) after phase 2 of K+1.
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
-                          hipStream_t s, Prof *prof) {
+                          hipStream_t s, Prof *prof, bool packed) {
   static_assert(BK == kBlockRounds, "k-block size");
   const int64_t TB = ceil_div(n, BK);    // k-blocks
   if (K1 > TB) K1 = TB;
@@ -522,14 +742,19 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   const bool vec = (n % 4 == 0) && aligned16(U) && aligned16(L);
   const unsigned gy = (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ);
   const int64_t nn = n * n;
-  auto panel = vec ? k_panel<true> : k_panel<false>;
-  auto tiles = vec ? k_tiles<true> : k_tiles<false>;
-  auto strip = vec ? k_strip<true> : k_strip<false>;
+  if (packed) L = U;
+  auto panel = packed ? (vec ? k_panel<true, true> : k_panel<false, true>)
+                      : (vec ? k_panel<true, false> : k_panel<false, false>);
+  auto tiles = packed ? (vec ? k_tiles<true, true> : k_tiles<false, true>)
+                      : (vec ? k_tiles<true, false> : k_tiles<false, false>);
+  auto strip = packed ? (vec ? k_strip<true, true> : k_strip<false, true>)
+                      : (vec ? k_strip<true, false> : k_strip<false, false>);
 
   auto phase12 = [&](int64_t K, hipStream_t st) -> hipError_t {
     const int64_t k0 = K * BK;
     const int bK = (int)(n - k0 < BK ? n - k0 : BK);
-    hipError_t e = launch_small_block(U, L, n, nn, k0 * n + k0, bK, 0, bK, batch, st, prof);
+    hipError_t e =
+        launch_small_block(U, L, n, nn, k0 * n + k0, bK, 0, bK, batch, st, prof, packed);
     if (e != hipSuccess || TB == 1) return e;
     return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(kThreads), st, U,
                   L, n, batch, K);
@@ -564,7 +789,8 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
       e = hipStreamWaitEvent(s, ev->e[2], 0);
     }
   }
-  if (e == hipSuccess && T > 1)
+  // packed storage keeps one slot per value: nothing goes stale
+  if (e == hipSuccess && T > 1 && !packed)
     e = launch(prof, kProfMirror, k_mirror, dim3((unsigned)(TB * TB), gy), dim3(kThreads), s, U,
                L, n, batch, TB);
   return e;

@@ -46,7 +46,62 @@ __global__ __launch_bounds__(kThreads) void k_check(const float *__restrict__ U,
   if (f) atomicOr(flags, f);
 }
 
+// Packed buffer: U[i,j] = P[min,max], L[i,j] = P[max,min].  The tile pairs
+// (I <= J) of PT x PT tiles are dealt to the workgroups of grid.x; for each,
+// a workgroup tests the entries of tile (I, J) and of its mirror (J, I)
+// (read transposed through LDS so that both reads are row-contiguous), and
+// the pair conditions L <= U and 0 <= L on the cells of tile (I, J) above the
+// diagonal.
+constexpr int PT = 64;
+
+__global__ __launch_bounds__(kThreads) void k_check_packed(const float *__restrict__ P, int64_t n,
+                                                           int64_t batch,
+                                                           uint32_t *__restrict__ flags) {
+  __shared__ float t[PT][PT + 1];
+  const int tid = threadIdx.x;
+  const int64_t T = ceil_div(n, PT), pairs = T * (T + 1) / 2, nn = n * n;
+  uint32_t f = 0;
+  for (int64_t p = blockIdx.x; p < pairs; p += gridDim.x) {
+    const int64_t J = tri_col(p), I = p - J * (J + 1) / 2;
+    const int64_t i0 = I * PT, j0 = J * PT;
+    for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+      const float *Pb = P + b * nn;
+      for (int e = tid; e < PT * PT; e += kThreads) {
+        const int r = e / PT, c = e % PT;
+        const int64_t gi = j0 + r, gj = i0 + c;  // P[j0 + r][i0 + c]
+        if (gi < n && gj < n) t[r][c] = Pb[gi * n + gj];
+      }
+      __syncthreads();
+      for (int e = tid; e < PT * PT; e += kThreads) {
+        const int r = e / PT, c = e % PT;
+        const int64_t i = i0 + r, j = j0 + c;
+        if (i >= n || j >= n) continue;
+        const float d = Pb[i * n + j];  // P[i][j]
+        const float m = t[c][r];        // P[j][i]
+        f |= entry_flags(d);
+        if (I != J) f |= entry_flags(m);
+        if (i < j) {
+          if (m > d) f |= DBS_CHECK_L_GT_U;
+          if (m < 0.0f) f |= DBS_CHECK_L_NEG;
+        } else if (i == j && __float_as_uint(d) != 0u) {
+          f |= DBS_CHECK_DIAG;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (f) atomicOr(flags, f);
+}
+
 }  // namespace
+
+hipError_t launch_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *flags,
+                               hipStream_t s) {
+  const int64_t T = ceil_div(n, PT), pairs = T * (T + 1) / 2;
+  const dim3 g((unsigned)(pairs < (1 << 20) ? pairs : (1 << 20)),
+               (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ));
+  return launch(nullptr, 0, k_check_packed, g, dim3(kThreads), s, P, n, batch, flags);
+}
 
 hipError_t launch_check(const float *U, const float *L, int64_t n, int64_t batch,
                         uint32_t *flags, hipStream_t s) {

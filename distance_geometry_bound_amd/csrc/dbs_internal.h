@@ -54,6 +54,20 @@ __device__ __forceinline__ void relax2(float &u, float &l, float cu0, float cl0,
 // upper-triangle tiles only, at most 1024 threads).
 constexpr int kSmallMaxN = 176;
 
+// Where the bounds of cell (i, j) live, as element offsets from the block's
+// base (row stride ld).  Dense: U and L are two arrays with (i, j) at the
+// same offset.  Packed (one array P, the notes' §6 triangle storage):
+// U(i,j) = P[min(i,j)][max(i,j)], L(i,j) = P[max(i,j)][min(i,j)].
+template <bool PK>
+struct Cell {
+  __device__ static __forceinline__ int64_t u(int64_t i, int64_t j, int64_t ld) {
+    return PK ? (i < j ? i * ld + j : j * ld + i) : i * ld + j;
+  }
+  __device__ static __forceinline__ int64_t l(int64_t i, int64_t j, int64_t ld) {
+    return PK ? (i > j ? i * ld + j : j * ld + i) : i * ld + j;
+  }
+};
+
 // Optional launch timing.  When a launcher is given a Prof, every kernel it
 // enqueues is bracketed by a pair of HIP events on the launch stream, tagged
 // with the kernel kind (the DBS_PROF_* numbering of dbs.h).
@@ -119,19 +133,28 @@ hipError_t launch_round(float *U, float *L, int64_t n, int64_t batch, int64_t k,
                         Prof *prof = nullptr);
 // rounds k_lo..k_hi-1 of a whole small molecule in one workgroup
 hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, int k_lo, int k_hi,
-                        hipStream_t s, Prof *prof = nullptr);
-// k-blocks K0..K1-1 of the blocked pass (rounds 64*K0 .. min(64*K1, n)-1)
+                        hipStream_t s, Prof *prof = nullptr, bool packed = false);
+// k-blocks K0..K1-1 of the blocked pass (rounds 64*K0 .. min(64*K1, n)-1);
+// packed: U == L == P in the one-buffer layout
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
-                          hipStream_t s, Prof *prof = nullptr);
+                          hipStream_t s, Prof *prof = nullptr, bool packed = false);
 constexpr int kBlockRounds = 64;
 hipError_t launch_restraints(float *U, float *L, int64_t n, int64_t batch, float unknown_L,
                              float unknown_U, const int32_t *mol, const int32_t *ia,
                              const int32_t *ja, const float *lo, const float *hi, int64_t count,
                              uint32_t *status, hipStream_t s, Prof *prof = nullptr);
+hipError_t launch_round_packed(float *P, int64_t n, int64_t batch, int64_t k, hipStream_t s,
+                               Prof *prof = nullptr);
+hipError_t launch_pack(const float *U, const float *L, float *P, int64_t n, int64_t batch,
+                       hipStream_t s);
+hipError_t launch_unpack(const float *P, float *U, float *L, int64_t n, int64_t batch,
+                         hipStream_t s);
 hipError_t launch_tightened(const float *U0, const float *L0, const float *U1, const float *L1,
                             int64_t n, int64_t batch, uint8_t *mask, hipStream_t s);
 hipError_t launch_check(const float *U, const float *L, int64_t n, int64_t batch,
                         uint32_t *flags, hipStream_t s);
+hipError_t launch_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *flags,
+                               hipStream_t s);
 
 // Single-workgroup Floyd-Warshall over an m x m symmetric block (m <= kSmallMaxN)
 // at element offset `off` of each molecule (row stride `ld`, molecule stride
@@ -139,7 +162,16 @@ hipError_t launch_check(const float *U, const float *L, int64_t n, int64_t batch
 // diagonal tile of the blocked pass.
 hipError_t launch_small_block(float *U, float *L, int64_t ld, int64_t mstride, int64_t off,
                               int m, int k_lo, int k_hi, int64_t batch, hipStream_t s,
-                              Prof *prof = nullptr);
+                              Prof *prof = nullptr, bool packed = false);
+
+// Tile pair p of the upper triangle, numbered column-major (p = J(J+1)/2 + I,
+// I <= J): returns J.
+__device__ __forceinline__ int64_t tri_col(int64_t p) {
+  int64_t J = (int64_t)((sqrt(8.0 * (double)p + 1.0) - 1.0) * 0.5);
+  while (J * (J + 1) / 2 > p) --J;
+  while ((J + 1) * (J + 2) / 2 <= p) ++J;
+  return J;
+}
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -1,6 +1,7 @@
 // small.hip -- a whole Floyd-Warshall pass over a small symmetric block in
 // one workgroup.
 //
+// Works on dense U, L or on the packed one-buffer layout (PK; U == L == P).
 // Used (a) for whole molecules with n <= kSmallMaxN, one workgroup per
 // molecule (the batched path for many small molecules), and (b) for the
 // diagonal tile of the blocked pass.  Rounds k run in order (GPU Gems 2,
@@ -33,9 +34,10 @@ __device__ __forceinline__ void publish(float (&u)[4][4], float (&l)[4][4], int 
   }
 }
 
-__global__ __launch_bounds__(1024) void k_small(float *__restrict__ U, float *__restrict__ L,
-                                                int64_t ld, int64_t mstride, int64_t off, int m,
-                                                int k_lo, int k_hi, int64_t batch) {
+template <bool PK>
+__global__ __launch_bounds__(1024) void k_small(float *U, float *L, int64_t ld, int64_t mstride,
+                                                int64_t off, int m, int k_lo, int k_hi,
+                                                int64_t batch) {
   __shared__ float vu[2][4 * kMaxG];
   __shared__ float vl[2][4 * kMaxG];
 
@@ -65,8 +67,8 @@ __global__ __launch_bounds__(1024) void k_small(float *__restrict__ U, float *__
         for (int c = 0; c < 4; ++c) {
           const int i = i0 + r, j = j0 + c;
           const bool in = i < m && j < m;
-          u[r][c] = in ? Ub[(int64_t)i * ld + j] : kInf;
-          l[r][c] = in ? Lb[(int64_t)i * ld + j] : 0.0f;
+          u[r][c] = in ? Ub[Cell<PK>::u(i, j, ld)] : kInf;
+          l[r][c] = in ? Lb[Cell<PK>::l(i, j, ld)] : 0.0f;
         }
     }
 
@@ -107,7 +109,14 @@ __global__ __launch_bounds__(1024) void k_small(float *__restrict__ U, float *__
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int i = i0 + r, j = j0 + c;
-          if (i < m && j < m) {
+          if (PK) {
+            // one slot each for U(i,j) and L(i,j); a diagonal tile holds both
+            // (i,j) and (j,i) with the same values, the diagonal stays 0
+            if (i < m && j < m && i != j) {
+              Ub[Cell<PK>::u(i, j, ld)] = u[r][c];
+              Lb[Cell<PK>::l(i, j, ld)] = l[r][c];
+            }
+          } else if (i < m && j < m) {
             Ub[(int64_t)i * ld + j] = u[r][c];
             Lb[(int64_t)i * ld + j] = l[r][c];
             if (ty != tx) {
@@ -127,19 +136,19 @@ __global__ __launch_bounds__(1024) void k_small(float *__restrict__ U, float *__
 
 hipError_t launch_small_block(float *U, float *L, int64_t ld, int64_t mstride, int64_t off,
                               int m, int k_lo, int k_hi, int64_t batch, hipStream_t s,
-                              Prof *prof) {
+                              Prof *prof, bool packed) {
   if (m <= 1 || k_lo >= k_hi) return hipSuccess;
   const int G = (m + 3) / 4;
   const int tiles = G * (G + 1) / 2;
   const int threads = (tiles + 63) / 64 * 64;
   const unsigned grid = (unsigned)(batch < 1048576 ? batch : 1048576);
-  return launch(prof, kProfSmall, k_small, dim3(grid), dim3(threads), s, U, L, ld, mstride, off,
-                m, k_lo, k_hi, batch);
+  return launch(prof, kProfSmall, packed ? k_small<true> : k_small<false>, dim3(grid),
+                dim3(threads), s, U, L, ld, mstride, off, m, k_lo, k_hi, batch);
 }
 
 hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, int k_lo, int k_hi,
-                        hipStream_t s, Prof *prof) {
-  return launch_small_block(U, L, n, n * n, 0, (int)n, k_lo, k_hi, batch, s, prof);
+                        hipStream_t s, Prof *prof, bool packed) {
+  return launch_small_block(U, L, n, n * n, 0, (int)n, k_lo, k_hi, batch, s, prof, packed);
 }
 
 }  // namespace dbs

@@ -212,6 +212,36 @@ int dbs_bounds_from_restraints(float *U, float *L, int64_t n, int64_t batch,
 #define DBS_RESTRAINT_VALUE 2u  /* NaN or infinite value, lo > hi, hi < 0, or
                                    |value| >= 2^17                            */
 
+/*
+ * Packed storage (the notes' §6 keeps the two symmetric matrices as two
+ * triangles): one [batch][n][n] float32 buffer P with P[i,j] = U[i,j] for
+ * i < j, L[i,j] for i > j, and U[i,i] (= L[i,i] = 0) on the diagonal.  It
+ * needs half the memory of the U, L pair.
+ *
+ * dbs_pack    -- P from symmetric U, L (reads U above and L below the diagonal).
+ * dbs_unpack  -- U, L from P (U[i,j] = P[min,max], L[i,j] = P[max,min]).
+ *   U, L, P device pointers, caller-owned; P may overlap neither U nor L.
+ * dbs_smooth_packed_range -- rounds k_begin..k_end-1 of a pass on P in place;
+ *   the result equals pack(smoothed U, L) bit for bit.  Algorithm as
+ *   dbs_smooth_range with DBS_ALGO_AUTO: one workgroup per molecule for
+ *   n <= dbs_lds_max_n(), else the blocked pass when both ends are on
+ *   k-block boundaries (or k_end == n), else one launch per round.
+ *   0 <= k_begin <= k_end <= n, else DBS_EINVAL.
+ * dbs_smooth_packed -- a full pass (k = 0..n-1) on P.
+ * dbs_check_packed -- dbs_check of the U, L pair that P stands for, without
+ *   unpacking it: ORs DBS_CHECK_* bits into *d_flags (device pointer, zeroed
+ *   by the caller).  DBS_CHECK_ASYM never appears (the pair is symmetric by
+ *   construction); DBS_CHECK_DIAG means P[i][i] is not +0.0.
+ * Same argument errors and preconditions as dbs_smooth (on the unpacked
+ * U, L: the packed form is symmetric by construction).
+ */
+int dbs_pack(const float *U, const float *L, float *P, int64_t n, int64_t batch, void *stream);
+int dbs_unpack(const float *P, float *U, float *L, int64_t n, int64_t batch, void *stream);
+int dbs_smooth_packed(float *P, int64_t n, int64_t batch, void *stream);
+int dbs_smooth_packed_range(float *P, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,
+                            void *stream);
+int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags, void *stream);
+
 /* Largest n the LDS algorithm accepts. */
 int dbs_lds_max_n(void);
 

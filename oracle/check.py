@@ -52,3 +52,21 @@ def flags(U, L) -> int:
     if np.any(ub == 0x80000000) or np.any(lb == 0x80000000):
         f |= NEGZERO
     return f
+
+
+def flags_packed(P) -> int:
+    """The checks of a packed buffer (U strictly above the diagonal, L strictly
+    below, the shared zero diagonal on it; GPU Gems 2, Ch. 43 notes, §6 on
+    keeping one triangle of each symmetric matrix): by definition those of the
+    dense pair it stands for, U[i,j] = P[min,max] and L[i,j] = P[max,min].
+    That pair is symmetric by construction, so ASYM never appears."""
+    P = np.asarray(P, dtype=np.float32)
+    if P.ndim == 2:
+        P = P[None]
+    n = P.shape[-1]
+    upper = np.triu(np.ones((n, n), dtype=bool), 1)
+    lower = upper.T
+    Pt = P.transpose(0, 2, 1)
+    U = np.where(lower, Pt, P)           # P[min, max]
+    L = np.where(upper, Pt, P)           # P[max, min]
+    return flags(U, L)

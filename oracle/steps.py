@@ -67,3 +67,31 @@ def tightened(U0, L0, U1, L1):
     """uint8 mask: 1 where U or L differs bit for bit between the two states."""
     a = [np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) for x in (U0, L0, U1, L1)]
     return ((a[0] != a[2]) | (a[1] != a[3])).astype(np.uint8)
+
+
+def pack(U, L):
+    """One-buffer storage of a molecule's bounds (GPU Gems 2, Ch. 43 notes, §6
+    keeps the two symmetric matrices as two triangles): P[i,j] = U[i,j] above
+    the diagonal, L[i,j] below it, and U[i,i] on it.  [..., n, n] float32."""
+    U = np.asarray(U, dtype=np.float32)
+    L = np.asarray(L, dtype=np.float32)
+    n = U.shape[-1]
+    iu = np.triu(np.ones((n, n), dtype=bool), 1)
+    il = np.tril(np.ones((n, n), dtype=bool), -1)
+    P = np.where(iu, U, np.where(il, L, U))
+    return P.astype(np.float32)
+
+
+def unpack(P):
+    """Inverse of pack for symmetric bounds: U[i,j] = P[min,max],
+    L[i,j] = P[max,min], U[i,i] = L[i,i] = P[i,i]."""
+    P = np.asarray(P, dtype=np.float32)
+    n = P.shape[-1]
+    iu = np.triu(np.ones((n, n), dtype=bool), 1)
+    Pt = np.swapaxes(P, -1, -2)
+    U = np.where(iu, P, Pt)                       # upper part, mirrored
+    L = np.where(iu, Pt, P)                       # lower part, mirrored
+    d = np.arange(n)
+    U[..., d, d] = P[..., d, d]
+    L[..., d, d] = P[..., d, d]
+    return U.astype(np.float32), L.astype(np.float32)

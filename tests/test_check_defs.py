@@ -45,3 +45,93 @@ def test_single_violation(case, flag):
     assert f & flag
     # no other flag may fire
     assert f == flag, (case, f)
+
+
+# ---------------------------------------------------------------- packed buffer
+def _packed(n=9):
+    from oracle import steps
+    U, L = _base(n)
+    return steps.pack(U, L)
+
+
+def test_packed_clean_and_never_asym():
+    P = _packed()
+    assert check.flags_packed(P) == 0
+    # any buffer stands for a symmetric pair: make the upper triangle unlike
+    # the lower one and only the pair conditions may fire
+    P[1, 2], P[2, 1] = 5.0, 1.0
+    assert check.flags_packed(P) == 0
+
+
+@pytest.mark.parametrize("slot,value,flag", [
+    ((3, 3), 1.0, check.DIAG),              # the shared diagonal
+    ((3, 3), -0.0, check.DIAG | check.NEGZERO),
+    ((1, 6), np.nan, check.NONFINITE),      # U slot
+    ((6, 1), np.inf, check.NONFINITE | check.L_GT_U),   # L slot, above its U
+    ((6, 1), 99.0, check.L_GT_U),           # L above its U at (1, 6)
+    ((6, 1), -1.0, check.L_NEG),
+    ((2, 7), "+2^-8", check.UNQUANT),
+    ((2, 7), 2.0 ** 17, check.RANGE),
+    ((7, 2), -0.0, check.NEGZERO),
+])
+def test_packed_single_violation(slot, value, flag):
+    P = _packed()
+    P[slot] = P[slot] + 2.0 ** -8 if value == "+2^-8" else value
+    assert check.flags_packed(P) == flag, (slot, value)
+
+
+def test_packed_lower_slot_is_l_of_both_orientations():
+    # P[6][1] is L[1,6] and L[6,1]: raising it above P[1][6] breaks L <= U
+    # once (one pair), and a batch reports the union over its molecules
+    P = np.stack([_packed(), _packed()])
+    P[1, 6, 1] = P[1, 1, 6] + 1.0
+    P[0, 4, 4] = 2.0
+    assert check.flags_packed(P) == check.L_GT_U | check.DIAG
+
+
+def _packed_battery(flags_packed):
+    """True if a flags_packed implementation passes every packed pin above."""
+    try:
+        P = _packed()
+        if flags_packed(P) != 0:
+            return False
+        for slot, value, flag in PACKED_CASES:
+            P = _packed()
+            P[slot] = P[slot] + 2.0 ** -8 if value == "+2^-8" else value
+            if flags_packed(P) != flag:
+                return False
+        P = np.stack([_packed(), _packed()])
+        P[1, 6, 1] = P[1, 1, 6] + 1.0
+        P[0, 4, 4] = 2.0
+        return flags_packed(P) == check.L_GT_U | check.DIAG
+    except Exception:
+        return False
+
+
+PACKED_CASES = [
+    ((3, 3), 1.0, check.DIAG), ((3, 3), -0.0, check.DIAG | check.NEGZERO),
+    ((1, 6), np.nan, check.NONFINITE), ((6, 1), np.inf, check.NONFINITE | check.L_GT_U),
+    ((6, 1), 99.0, check.L_GT_U), ((6, 1), -1.0, check.L_NEG),
+    ((2, 7), "+2^-8", check.UNQUANT), ((2, 7), 2.0 ** 17, check.RANGE),
+    ((7, 2), -0.0, check.NEGZERO), ((1, 6), 0.0, check.L_GT_U),
+]
+
+PACKED_MUTANTS = {
+    "roles_swapped": ("U = np.where(lower, Pt, P)", "U = np.where(upper, Pt, P)"),
+    "lower_not_mirrored": ("L = np.where(upper, Pt, P)", "L = P"),
+    "no_transpose": ("Pt = P.transpose(0, 2, 1)", "Pt = P"),
+    "molecule_axis_swapped": ("Pt = P.transpose(0, 2, 1)", "Pt = P.transpose(1, 0, 2)"),
+}
+
+
+@pytest.mark.parametrize("name", [None] + sorted(PACKED_MUTANTS))
+def test_packed_pins_reject_mutants(name):
+    import oracle.check as mod
+    src = open(mod.__file__).read()
+    if name:
+        old, new = PACKED_MUTANTS[name]
+        assert src.count(old) == 1
+        src = src.replace(old, new)
+    ns = {"__name__": "mutant_check"}
+    exec(compile(src, "mutant_check", "exec"), ns)
+    assert _packed_battery(ns["flags_packed"]) == (name is None), name

@@ -135,3 +135,88 @@ def test_tightened_matches_oracle(n, batch):
     U1, L1 = oracle.rounds(U0, L0, 0, min(n, 3))
     m = dgb.tightened(dev(U0), dev(L0), dev(U1), dev(L1))
     assert np.array_equal(host(m), steps.tightened(U0, L0, U1, L1))
+
+
+# ---------------------------------------------------------------- packed storage
+@pytest.mark.parametrize("n,batch", [(1, 1), (2, 2), (5, 1), (63, 1), (64, 2), (65, 1),
+                                     (130, 3), (257, 1), (260, 1)])
+def test_pack_unpack_match_oracle(n, batch):
+    U0, L0 = sound(n, batch, seed=3 * n)
+    P = dgb.pack(dev(U0), dev(L0))
+    assert bits_equal(host(P), steps.pack(U0, L0))
+    U, L = dgb.unpack(P)
+    assert bits_equal(host(U), U0) and bits_equal(host(L), L0)
+
+
+@pytest.mark.parametrize("n,batch", [(3, 1), (7, 2), (64, 1), (65, 2), (129, 1), (130, 3)])
+def test_packed_each_round_matches_oracle(n, batch):
+    U0, L0 = sound(n, batch, seed=5 * n)
+    P = dgb.pack(dev(U0), dev(L0))
+    Ue, Le = U0, L0
+    for k in range(n):
+        dgb.smooth_packed(P, k, k + 1)
+        Ue, Le = oracle.rounds(Ue, Le, k, k + 1)
+        assert bits_equal(host(P), steps.pack(Ue, Le)), (n, batch, k)
+
+
+@pytest.mark.parametrize("name,batch", [("n128", None), ("n1024", None), ("b64n500", 4)])
+def test_packed_full_pass_workloads(name, batch):
+    W = gen.make_workload(name, batch=batch)
+    Ue, Le = oracle.smooth(W.U, W.L)
+    P = dgb.pack(dev(W.U), dev(W.L))
+    dgb.smooth_packed(P)
+    assert bits_equal(host(P), steps.pack(Ue, Le))
+    U, L = dgb.unpack(P)
+    assert bits_equal(host(U), Ue) and bits_equal(host(L), Le)
+
+
+def test_packed_misaligned_and_ragged():
+    n = 260
+    U0, L0, _ = gen.random_sound_bounds(n, seed=8, box=40.0)
+    Ue, Le = oracle.smooth(U0, L0)
+    buf = torch.zeros(n * n + 1, device=DEV)
+    P = buf[1:].view(n, n)
+    dgb.pack(dev(U0), dev(L0), out=P)
+    assert P.data_ptr() % 16 != 0
+    dgb.smooth_packed(P)
+    assert bits_equal(host(P), steps.pack(Ue, Le))
+
+
+@pytest.mark.parametrize("n,batch", [(177, 1), (191, 2), (192, 1), (193, 1), (255, 1),
+                                     (257, 2), (320, 1), (383, 1), (385, 1), (700, 1)])
+def test_packed_blocked_full_pass(n, batch):
+    U0, L0 = sound(n, batch, seed=7 * n)
+    Ue, Le = oracle.smooth(U0, L0)
+    P = dgb.pack(dev(U0), dev(L0))
+    dgb.smooth_packed(P)
+    assert bits_equal(host(P), steps.pack(Ue, Le))
+
+
+def test_packed_ranges_mix_per_round_and_blocked():
+    n = 257
+    U0, L0 = sound(n, 2, seed=11)
+    P = dgb.pack(dev(U0), dev(L0))
+    Ue, Le = U0, L0
+    for a, b in ((0, 1), (1, 64), (64, 128), (128, 200), (200, 257)):
+        dgb.smooth_packed(P, a, b)
+        Ue, Le = oracle.rounds(Ue, Le, a, b)
+        assert bits_equal(host(P), steps.pack(Ue, Le)), (a, b)
+
+
+@pytest.mark.parametrize("n,batch,slots", [
+    (1, 1, [((0, 0), 1.0)]),
+    (5, 2, []),
+    (5, 2, [((1, 3, 1), -1.0)]),
+    (63, 1, [((62, 0), 99.0)]),
+    (64, 1, [((0, 63), np.nan)]),
+    (65, 3, [((2, 64, 64), 1.0), ((1, 10, 64), 0.001)]),
+    (130, 2, [((1, 129, 3), 2.0 ** 17), ((0, 3, 129), -0.0)]),
+    (200, 1, [((150, 140), 1e9), ((140, 150), np.inf)]),
+])
+def test_check_packed_matches_definitions(n, batch, slots):
+    from oracle import check as check_defs
+    U0, L0 = sound(n, batch, seed=n)
+    P = steps.pack(U0, L0)
+    for s, v in slots:
+        P[s if batch > 1 or len(s) == 3 else (0,) + s] = v
+    assert dgb.check_packed(dev(P)) == check_defs.flags_packed(P)

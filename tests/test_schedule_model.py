@@ -14,7 +14,8 @@ This model re-implements that data flow in plain Python on exact int64 units
   * that it reaches the oracle's result bit for bit, and
   * that the two streams of one k-block touch disjoint cells: nothing the
     side stream writes is read or written by the bulk, and nothing the bulk
-    writes is read by the side stream.
+    writes is read by the side stream -- in the dense layout, and in the
+    packed one-buffer layout (where cell (i,j) occupies P[i][j] and P[j][i]).
 The GPU parity tests then check the kernels themselves against the oracle.
 """
 import numpy as np
@@ -153,6 +154,11 @@ class Model:
             tr, tw = self.tiles(K, ahead=True)
             assert not (side_w & (tr | tw)), f"k-block {K}: side stream writes what the bulk touches"
             assert not (tw & side_r), f"k-block {K}: bulk writes what the side stream reads"
+            # packed storage: logical cell (i,j) lives in P[min][max] (U) and
+            # P[max][min] (L), so a footprint becomes its symmetric closure
+            sym = lambda cells: cells | {(j, i) for (i, j) in cells}
+            assert not (sym(side_w) & sym(tr | tw)), f"k-block {K}: packed overlap (writes)"
+            assert not (sym(tw) & sym(side_r)), f"k-block {K}: packed overlap (reads)"
         n = self.n
         for i in range(n):
             for j in range(n):

@@ -80,3 +80,15 @@ def test_tightened_definition():
     U2 = U0.copy()
     U2[0, 0] = -0.0
     assert steps.tightened(U0, L0, U2, L0)[0, 0] == 1
+
+
+def test_pack_unpack_hand_case_and_round_trip():
+    U = np.array([[0, 3, 5], [3, 0, 4], [5, 4, 0]], np.float32)
+    L = np.array([[0, 1, 2], [1, 0, 1.5], [2, 1.5, 0]], np.float32)
+    P = steps.pack(U, L)
+    assert P.tolist() == [[0, 3, 5], [1, 0, 4], [2, 1.5, 0]]
+    U2, L2 = steps.unpack(P)
+    assert np.array_equal(U2, U) and np.array_equal(L2, L)
+    Ub, Lb, _ = gen.random_sound_bounds(17, seed=4, batch=3)
+    U3, L3 = steps.unpack(steps.pack(Ub, Lb))
+    assert np.array_equal(U3, Ub) and np.array_equal(L3, Lb)
