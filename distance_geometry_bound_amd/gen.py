@@ -425,6 +425,74 @@ def random_sound_bounds(n: int, seed: int, *, box: float = 20.0, known: float = 
     return U, L, Xs
 
 
+def f32_down(x):
+    """The largest float32 <= x (x float64), elementwise."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    return np.where(f.astype(np.float64) > x, np.nextafter(f, np.float32(-np.inf)), f)
+
+
+def f32_up(x):
+    """The smallest float32 >= x (x float64), elementwise."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    return np.where(f.astype(np.float64) < x, np.nextafter(f, np.float32(np.inf)), f)
+
+
+def random_unquantised_bounds(n: int, seed: int, *, box: float = 20.0, known: float = 0.4,
+                              slack: float = 2.0, batch: int | None = None):
+    """random_sound_bounds without the 2^-6 grid: each known pair gets
+    [d - a, d + b] (a, b ~ U(0, slack); slack 0 gives [d, d]) rounded outward
+    to the neighbouring float32 values, so sums and differences of bounds
+    are generally not exact in float32.  Unknown pairs get [0, 2*box]."""
+    rng = np.random.default_rng([seed, 0xF32])
+    nb = 1 if batch is None else batch
+    U = np.empty((nb, n, n), dtype=np.float32)
+    L = np.empty((nb, n, n), dtype=np.float32)
+    Xs = []
+    for b in range(nb):
+        X = rng.uniform(0.0, box, size=(n, 3))
+        d = true_distances(X)
+        a = rng.uniform(0.0, slack, size=(n, n)) if slack > 0 else np.zeros((n, n))
+        c = rng.uniform(0.0, slack, size=(n, n)) if slack > 0 else np.zeros((n, n))
+        k = rng.random((n, n)) < known
+        a, c, k = np.triu(a, 1), np.triu(c, 1), np.triu(k, 1)
+        a, c, k = a + a.T, c + c.T, k | k.T
+        lo = np.where(k, f32_down(np.maximum(d - a, 0.0)), 0.0)
+        hi = np.where(k, f32_up(d + c), f32_up(2.0 * box))
+        np.fill_diagonal(lo, 0.0)
+        np.fill_diagonal(hi, 0.0)
+        U[b], L[b] = hi, lo
+        Xs.append(X)
+    if batch is None:
+        return U[0], L[0], Xs[0]
+    return U, L, Xs
+
+
+def unquantised_line(n: int, seed: int, *, spacing: tuple = (1.0, 4.0)):
+    """Atoms on a line at random float64 positions (gaps ~ U(spacing)): each
+    neighbour pair and the two end atoms known exactly, [d, d] rounded
+    outward to float32, every other pair [0, total length + 1 rounded up].
+    Along a line distances add, so the smoothed upper bounds are sums of many
+    rounded terms, and the lower bounds (end-to-end length minus the rest)
+    differences of them: a stringent case for the soundness of rounding.
+    Returns (U, L, positions)."""
+    rng = np.random.default_rng([seed, 0x11E])
+    x = np.concatenate([[0.0], np.cumsum(rng.uniform(spacing[0], spacing[1], n - 1))])
+    X = np.stack([x, np.zeros(n), np.zeros(n)], axis=1)
+    U = np.full((n, n), f32_up(x[-1] - x[0] + 1.0), dtype=np.float32)
+    L = np.zeros((n, n), dtype=np.float32)
+    i = np.arange(n - 1)
+    gap = x[1:] - x[:-1]
+    U[i, i + 1] = U[i + 1, i] = f32_up(gap)
+    L[i, i + 1] = L[i + 1, i] = f32_down(gap)
+    if n > 2:
+        U[0, n - 1] = U[n - 1, 0] = f32_up(x[-1] - x[0])
+        L[0, n - 1] = L[n - 1, 0] = f32_down(x[-1] - x[0])
+    np.fill_diagonal(U, 0.0)
+    return U, L, X
+
+
 def random_directed_bounds(n: int, seed: int, *, box: float = 12.0,
                            known: float = 0.5, slack: float = 3.0):
     """Asymmetric bounds around a symmetric metric (random points in a cube).

@@ -6,7 +6,8 @@ binding never import this package, and this package imports nothing of
 theirs; the two share only the seeded input generator.
 
 `oracle.c` holds the arithmetic (one Floyd-Warshall round per intermediate
-atom, upper bounds before lower bounds, front/back buffers, fp32), following
+atom, upper bounds before lower bounds, front/back buffers, fp32, with
+round-to-nearest or with sums rounded up and differences rounded down), following
 GPU Gems 2, Ch. 43 "GPU Computing for Protein Structure Prediction" (study
 notes), §2-§4 and §6.  `check.py` holds the plain definitions of the input
 checks the library's validator reports.
@@ -27,10 +28,11 @@ _lib = None
 
 
 def build(verbose: bool = False) -> str:
-    """Compile oracle.c with gcc (plain -O2, OpenMP, no fast-math)."""
+    """Compile oracle.c with gcc (plain -O2, OpenMP, no fast-math; the
+    rounding mode is honoured, -frounding-math)."""
     tmp = SO + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-           "-fno-fast-math", "-ffp-contract=off", SRC, "-o", tmp]
+           "-fno-fast-math", "-ffp-contract=off", "-frounding-math", SRC, "-lm", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -48,6 +50,9 @@ def load():
         i64 = ctypes.c_int64
         lib.dbs_oracle_rounds.argtypes = [f32p, f32p, i64, i64, i64, i64, ctypes.c_int]
         lib.dbs_oracle_rounds.restype = ctypes.c_int
+        lib.dbs_oracle_rounds_directed.argtypes = [f32p, f32p, i64, i64, i64, i64,
+                                                   ctypes.c_int]
+        lib.dbs_oracle_rounds_directed.restype = ctypes.c_int
         lib.dbs_oracle_smooth.argtypes = [f32p, f32p, i64, i64, ctypes.c_int]
         lib.dbs_oracle_smooth.restype = ctypes.c_int
         lib.dbs_oracle_max_threads.restype = ctypes.c_int
@@ -81,6 +86,24 @@ def smooth(U, L, threads: int = 0):
     """One full pass (every intermediate atom); returns new (U, L)."""
     U, L, n, batch = _prep(U, L)
     return rounds(U, L, 0, n, threads)
+
+
+def rounds_directed(U, L, k_begin: int, k_end: int, threads: int = 0):
+    """rounds() with upper-bound sums rounded toward +inf and lower-bound
+    differences toward -inf; returns new (U, L) float32 arrays."""
+    U, L, n, batch = _prep(U, L)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    rc = load().dbs_oracle_rounds_directed(U.ctypes.data_as(f32p), L.ctypes.data_as(f32p),
+                                           n, batch, k_begin, k_end, threads)
+    if rc != 0:
+        raise ValueError(f"dbs_oracle_rounds_directed failed ({rc})")
+    return U, L
+
+
+def smooth_directed(U, L, threads: int = 0):
+    """A full pass with directed rounding; returns new (U, L)."""
+    U, L, n, batch = _prep(U, L)
+    return rounds_directed(U, L, 0, n, threads)
 
 
 def max_threads() -> int:

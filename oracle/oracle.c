@@ -21,7 +21,8 @@
  *     complete result of the previous one.
  *   - §4: a round reads the previous round's matrices and writes fresh ones
  *     (front/back buffers swapped after the round).
- *   - §6: arithmetic is 32-bit IEEE float.
+ *   - §6: arithmetic is 32-bit IEEE float, and the result is sensitive to
+ *     its precision.
  *
  * So one round k is written out literally: first the upper sweep over every
  * pair, reading the front U; then the lower sweep over every pair, reading
@@ -29,9 +30,17 @@
  * reordered or fused.  OpenMP splits the rows of a sweep over threads, which
  * changes no arithmetic (every pair is computed by the same expression).
  *
+ * Directed rounding (dbs_oracle_rounds_directed): the same rounds with every
+ * upper-bound sum rounded toward +infinity and every lower-bound difference
+ * toward -infinity (the C rounding mode of each sweep, set in every OpenMP
+ * thread), so that, on inputs that are not on an exact grid, the results
+ * stay sound bounds: an upper bound is never rounded below the sum it
+ * stands for, a lower bound never above its difference.
+ *
  * Layout: U and L are [batch][n][n] float32, row-major, batch stride n*n.
  * Return codes: 0 ok, -1 bad argument, -2 out of host memory.
  */
+#include <fenv.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -51,38 +60,50 @@ static int nthreads(int threads)
 #endif
 }
 
-/* One Floyd-Warshall round with intermediate atom k (§2, §3, §4). */
+/* One Floyd-Warshall round with intermediate atom k (§2, §3, §4).
+   directed: round the upper sweep's sums up and the lower sweep's
+   differences down (each thread sets, then restores, its own mode). */
 static void one_round(const float *Uf, const float *Lf, float *Ub, float *Lb,
-                      int64_t n, int64_t k, int threads)
+                      int64_t n, int64_t k, int threads, int directed)
 {
-    int64_t i, j;
-    /* upper bounds first: U[i,j] <- min(U[i,j], U[i,k] + U[k,j]) */
-#pragma omp parallel for num_threads(threads) schedule(static) private(j)
-    for (i = 0; i < n; ++i) {
-        for (j = 0; j < n; ++j) {
-            float keep = Uf[i * n + j];
-            float path = Uf[i * n + k] + Uf[k * n + j];
-            Ub[i * n + j] = path < keep ? path : keep;
+#pragma omp parallel num_threads(threads)
+    {
+        int64_t i, j;
+        if (directed)
+            fesetround(FE_UPWARD);
+        /* upper bounds first: U[i,j] <- min(U[i,j], U[i,k] + U[k,j]) */
+#pragma omp for schedule(static)
+        for (i = 0; i < n; ++i) {
+            for (j = 0; j < n; ++j) {
+                float keep = Uf[i * n + j];
+                float path = Uf[i * n + k] + Uf[k * n + j];
+                Ub[i * n + j] = path < keep ? path : keep;
+            }
         }
-    }
-    /* then lower bounds, from this round's upper bounds:
-       L[i,j] <- max(L[i,j], L[i,k] - U[k,j], L[k,j] - U[i,k]) */
-#pragma omp parallel for num_threads(threads) schedule(static) private(j)
-    for (i = 0; i < n; ++i) {
-        for (j = 0; j < n; ++j) {
-            float best = Lf[i * n + j];
-            float a = Lf[i * n + k] - Ub[k * n + j];
-            float b = Lf[k * n + j] - Ub[i * n + k];
-            if (a > best) best = a;
-            if (b > best) best = b;
-            Lb[i * n + j] = best;
+        /* (the loop's barrier: every upper bound of the round is written) */
+        if (directed)
+            fesetround(FE_DOWNWARD);
+        /* then lower bounds, from this round's upper bounds:
+           L[i,j] <- max(L[i,j], L[i,k] - U[k,j], L[k,j] - U[i,k]) */
+#pragma omp for schedule(static)
+        for (i = 0; i < n; ++i) {
+            for (j = 0; j < n; ++j) {
+                float best = Lf[i * n + j];
+                float a = Lf[i * n + k] - Ub[k * n + j];
+                float b = Lf[k * n + j] - Ub[i * n + k];
+                if (a > best) best = a;
+                if (b > best) best = b;
+                Lb[i * n + j] = best;
+            }
         }
+        if (directed)
+            fesetround(FE_TONEAREST);
     }
 }
 
 /* Rounds k_begin..k_end-1 of one pass, in place on every molecule. */
-int dbs_oracle_rounds(float *U, float *L, int64_t n, int64_t batch,
-                      int64_t k_begin, int64_t k_end, int threads)
+static int run_rounds(float *U, float *L, int64_t n, int64_t batch,
+                      int64_t k_begin, int64_t k_end, int threads, int directed)
 {
     if (!U || !L || n < 1 || batch < 1 || k_begin < 0 || k_end > n || k_begin > k_end)
         return -1;
@@ -102,7 +123,7 @@ int dbs_oracle_rounds(float *U, float *L, int64_t n, int64_t batch,
         float *fu = Umol, *fl = Lmol;           /* front: last finished round */
         float *bu = spare_u, *bl = spare_l;     /* back: the round being written */
         for (int64_t k = k_begin; k < k_end; ++k) {
-            one_round(fu, fl, bu, bl, n, k, t);
+            one_round(fu, fl, bu, bl, n, k, t, directed);
             float *tu = fu, *tl = fl;
             fu = bu; fl = bl;
             bu = tu; bl = tl;
@@ -115,6 +136,19 @@ int dbs_oracle_rounds(float *U, float *L, int64_t n, int64_t batch,
     free(spare_u);
     free(spare_l);
     return 0;
+}
+
+int dbs_oracle_rounds(float *U, float *L, int64_t n, int64_t batch,
+                      int64_t k_begin, int64_t k_end, int threads)
+{
+    return run_rounds(U, L, n, batch, k_begin, k_end, threads, 0);
+}
+
+/* The same rounds with directed rounding (sums up, differences down). */
+int dbs_oracle_rounds_directed(float *U, float *L, int64_t n, int64_t batch,
+                               int64_t k_begin, int64_t k_end, int threads)
+{
+    return run_rounds(U, L, n, batch, k_begin, k_end, threads, 1);
 }
 
 /* One full pass (rounds 0..n-1) on every molecule. */

@@ -41,7 +41,7 @@ def _build(src_text, tmp_path, name):
     so = tmp_path / f"lib{name}.so"
     c.write_text(src_text)
     subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-                    str(c), "-o", str(so)], check=True)
+                    "-frounding-math", str(c), "-lm", "-o", str(so)], check=True)
     lib = ctypes.CDLL(str(so))
     f32p = ctypes.POINTER(ctypes.c_float)
     lib.dbs_oracle_smooth.argtypes = [f32p, f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
