@@ -16,6 +16,8 @@ Printed: one JSON line with
                (16 B per cell per round) / mean round time
   restraints   the workload's restraint list to dense bounds (fill + scatter)
   tightened    the mask of cells a pass changed
+  directed     the same pass with sums rounded up and differences rounded
+               down (sound bounds on inputs off the 2^-6 grid)
   packed       the same pass on the one-buffer layout (U above the diagonal,
                L below), with the pack and unpack steps timed apart
   cpu_baseline the CPU reference (oracle) on a bounded prefix of rounds of
@@ -199,6 +201,33 @@ def packed_pass(U0, L0, dev, reps=2):
             "bytes": 4 * cells}
 
 
+def directed_pass(U, L, U0, L0, dev, reps=2):
+    """Time the directed-rounding pass on the same workload (the same kernels
+    with the fp32 rounding mode set toward +inf)."""
+    import torch
+
+    import distance_geometry_bound_amd as dgb
+
+    s = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    U.copy_(U0)
+    L.copy_(L0)
+    dgb.smooth_directed(U, L)                # warm
+    ms = 0.0
+    for _ in range(reps):
+        U.copy_(U0)
+        L.copy_(L0)
+        e0.record(s)
+        dgb.smooth_directed(U, L)
+        e1.record(s)
+        torch.cuda.synchronize(dev)
+        ms += e0.elapsed_time(e1) / reps
+    n, batch = U0.shape[-1], U0.numel() // (U0.shape[-1] ** 2)
+    triples = float(n) ** 3 * batch
+    return {"pass_ms": ms, "value": 2.0 * triples / (ms * 1e-3),
+            "pct_fp32_valu_peak": OPS_PER_TRIPLE * triples / (ms * 1e-3) / FP32_VALU_PEAK}
+
+
 def cpu_baseline(W, target_s):
     """Time the oracle on a prefix of rounds of the same workload."""
     import ctypes
@@ -349,6 +378,7 @@ def main():
 
     if args.steps_extra:
         out.update(extra_steps(W, U, L, U0, L0, dev))
+        out["directed"] = directed_pass(U, L, U0, L0, dev)
         out["packed"] = packed_pass(U0, L0, dev)
 
     if not args.no_cpu and args.cpu_seconds > 0:

@@ -27,7 +27,8 @@ DBS_OK, DBS_EINVAL, DBS_EDEVICE, DBS_ELAUNCH, DBS_EUNSUPPORTED = 0, -1, -2, -3, 
 EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
            "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened", "dbs_bounds_from_restraints",
            "dbs_pack", "dbs_unpack", "dbs_smooth_packed", "dbs_smooth_packed_range",
-           "dbs_check_packed",
+           "dbs_check_packed", "dbs_smooth_directed", "dbs_smooth_directed_range",
+           "dbs_smooth_packed_directed_range",
            "dbs_lds_max_n", "dbs_auto_algo", "dbs_strerror", "dbs_version")
 
 RESTRAINT_FLAGS = {"index": 1, "value": 2}
@@ -68,14 +69,18 @@ def lib():
                                                  ctypes.c_float, vp, vp, vp, vp, vp, i64, vp, vp]
         L.dbs_check.argtypes = [vp, vp, i64, i64, vp, vp]
         L.dbs_check_packed.argtypes = [vp, i64, i64, vp, vp]
+        L.dbs_smooth_directed.argtypes = [vp, vp, i64, i64, vp]
+        L.dbs_smooth_directed_range.argtypes = [vp, vp, i64, i64, i64, i64, vp, c_int]
+        L.dbs_smooth_packed_directed_range.argtypes = [vp, i64, i64, i64, i64, vp]
         L.dbs_auto_algo.argtypes = [i64, i64]
         L.dbs_strerror.argtypes = [c_int]
         L.dbs_strerror.restype = ctypes.c_char_p
         for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
                   "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened",
                   "dbs_bounds_from_restraints", "dbs_pack", "dbs_unpack", "dbs_smooth_packed",
-                  "dbs_smooth_packed_range", "dbs_check_packed", "dbs_lds_max_n", "dbs_auto_algo",
-                  "dbs_version"):
+                  "dbs_smooth_packed_range", "dbs_check_packed", "dbs_smooth_directed",
+                  "dbs_smooth_directed_range", "dbs_smooth_packed_directed_range",
+                  "dbs_lds_max_n", "dbs_auto_algo", "dbs_version"):
             getattr(L, f).restype = c_int
         _lib = L
     return _lib
@@ -175,6 +180,24 @@ def smooth_range(U, L, k_begin: int, k_end: int, algo: str = "auto") -> None:
           int(k_end), _stream(U), _ALGOS[algo])
 
 
+def smooth_directed_range(U, L, k_begin: int, k_end: int, algo: str = "auto") -> None:
+    """smooth_range with directed rounding: sums of upper bounds rounded up,
+    differences of lower bounds rounded down (see dbs_smooth_directed_range)."""
+    n, batch = _shape(U, L)
+    if algo not in _ALGOS:
+        raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
+    if n == 0 or batch == 0:
+        return
+    _call(U, lib().dbs_smooth_directed_range, U.data_ptr(), L.data_ptr(), n, batch,
+          int(k_begin), int(k_end), _stream(U), _ALGOS[algo])
+
+
+def smooth_directed(U, L, algo: str = "auto") -> None:
+    """A full pass with directed rounding, in place."""
+    n, _ = _shape(U, L)
+    smooth_directed_range(U, L, 0, n, algo)
+
+
 def tightened(U0, L0, U1, L1):
     """uint8 mask of the cells whose U or L differs between two states."""
     import torch
@@ -269,6 +292,16 @@ def smooth_packed(P, k_begin: int = 0, k_end=None) -> None:
         return
     k_end = n if k_end is None else int(k_end)
     _call(P, lib().dbs_smooth_packed_range, P.data_ptr(), n, batch, int(k_begin), k_end,
+          _stream(P))
+
+
+def smooth_packed_directed(P, k_begin: int = 0, k_end=None) -> None:
+    """smooth_packed with directed rounding, in place."""
+    n, batch = _shape1(P)
+    if n == 0 or batch == 0:
+        return
+    k_end = n if k_end is None else int(k_end)
+    _call(P, lib().dbs_smooth_packed_directed_range, P.data_ptr(), n, batch, int(k_begin), k_end,
           _stream(P))
 
 

@@ -86,6 +86,65 @@ int run(float *U, float *L, int64_t n, int64_t batch, void *stream, int algo,
   }
 }
 
+// Rounds k_begin..k_end-1 with algorithm `algo` (AUTO: the single workgroup
+// for small n, blocked when both ends are on k-block boundaries, else one
+// launch per round); flags: dbs::kDirected or 0.
+int range_impl(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,
+               void *stream, int algo, unsigned flags) {
+  int st = validate(U, L, n, batch);
+  if (st != DBS_OK) return st;
+  if (k_begin < 0 || k_end > n || k_begin > k_end) return DBS_EINVAL;
+  if (algo < DBS_ALGO_AUTO || algo > DBS_ALGO_BLOCKED) return DBS_EINVAL;
+  const int64_t B = dbs::kBlockRounds;
+  const bool aligned = k_begin % B == 0 && (k_end % B == 0 || k_end == n);
+  if (algo == DBS_ALGO_AUTO)
+    algo = n <= dbs::kSmallMaxN ? DBS_ALGO_LDS : aligned ? DBS_ALGO_BLOCKED : DBS_ALGO_PERK;
+  if (algo == DBS_ALGO_LDS && n > dbs::kSmallMaxN) return DBS_EUNSUPPORTED;
+  if (algo == DBS_ALGO_BLOCKED && !aligned) return DBS_EUNSUPPORTED;
+  st = device_status();
+  if (st != DBS_OK) return st;
+  if (k_begin == k_end || n == 1) return DBS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (algo) {
+    case DBS_ALGO_PERK: {
+      hipError_t e = hipSuccess;
+      for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
+        e = dbs::launch_round(U, L, n, batch, k, s, nullptr, flags);
+      return status_of(e);
+    }
+    case DBS_ALGO_LDS:
+      return status_of(
+          dbs::launch_small(U, L, n, batch, (int)k_begin, (int)k_end, s, nullptr, flags));
+    default:
+      return status_of(dbs::launch_blocked(U, L, n, batch, k_begin / B, dbs::ceil_div(k_end, B),
+                                           s, nullptr, flags));
+  }
+}
+
+// The packed counterpart (P in the one-buffer layout), same algorithm choice.
+int packed_range_impl(float *P, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,
+                      void *stream, unsigned flags) {
+  uint64_t bytes = 0;
+  if (check_buffer(P, n, batch, &bytes) != DBS_OK) return DBS_EINVAL;
+  if (k_begin < 0 || k_end > n || k_begin > k_end) return DBS_EINVAL;
+  const int st = device_status();
+  if (st != DBS_OK) return st;
+  if (k_begin == k_end || n == 1) return DBS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t B = dbs::kBlockRounds;
+  flags |= dbs::kPacked;
+  if (n <= dbs::kSmallMaxN)
+    return status_of(
+        dbs::launch_small(P, P, n, batch, (int)k_begin, (int)k_end, s, nullptr, flags));
+  if (k_begin % B == 0 && (k_end % B == 0 || k_end == n))
+    return status_of(dbs::launch_blocked(P, P, n, batch, k_begin / B, dbs::ceil_div(k_end, B), s,
+                                         nullptr, flags));
+  hipError_t e = hipSuccess;
+  for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
+    e = dbs::launch_round_packed(P, n, batch, k, s, nullptr, flags);
+  return status_of(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,33 +203,16 @@ int dbs_check(const float *U, const float *L, int64_t n, int64_t batch, uint32_t
 
 int dbs_smooth_range(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
                      int64_t k_end, void *stream, int algo) {
-  int st = validate(U, L, n, batch);
-  if (st != DBS_OK) return st;
-  if (k_begin < 0 || k_end > n || k_begin > k_end) return DBS_EINVAL;
-  if (algo < DBS_ALGO_AUTO || algo > DBS_ALGO_BLOCKED) return DBS_EINVAL;
-  const int64_t B = dbs::kBlockRounds;
-  const bool aligned = k_begin % B == 0 && (k_end % B == 0 || k_end == n);
-  if (algo == DBS_ALGO_AUTO)
-    algo = n <= dbs::kSmallMaxN ? DBS_ALGO_LDS : aligned ? DBS_ALGO_BLOCKED : DBS_ALGO_PERK;
-  if (algo == DBS_ALGO_LDS && n > dbs::kSmallMaxN) return DBS_EUNSUPPORTED;
-  if (algo == DBS_ALGO_BLOCKED && !aligned) return DBS_EUNSUPPORTED;
-  st = device_status();
-  if (st != DBS_OK) return st;
-  if (k_begin == k_end || n == 1) return DBS_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (algo) {
-    case DBS_ALGO_PERK: {
-      hipError_t e = hipSuccess;
-      for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
-        e = dbs::launch_round(U, L, n, batch, k, s);
-      return status_of(e);
-    }
-    case DBS_ALGO_LDS:
-      return status_of(dbs::launch_small(U, L, n, batch, (int)k_begin, (int)k_end, s));
-    default:
-      return status_of(
-          dbs::launch_blocked(U, L, n, batch, k_begin / B, dbs::ceil_div(k_end, B), s));
-  }
+  return range_impl(U, L, n, batch, k_begin, k_end, stream, algo, 0);
+}
+
+int dbs_smooth_directed_range(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
+                              int64_t k_end, void *stream, int algo) {
+  return range_impl(U, L, n, batch, k_begin, k_end, stream, algo, dbs::kDirected);
+}
+
+int dbs_smooth_directed(float *U, float *L, int64_t n, int64_t batch, void *stream) {
+  return range_impl(U, L, n, batch, 0, n, stream, DBS_ALGO_AUTO, dbs::kDirected);
 }
 
 int dbs_block_rounds(void) { return dbs::kBlockRounds; }
@@ -235,24 +277,12 @@ int dbs_unpack(const float *P, float *U, float *L, int64_t n, int64_t batch, voi
 
 int dbs_smooth_packed_range(float *P, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,
                             void *stream) {
-  uint64_t bytes = 0;
-  if (check_buffer(P, n, batch, &bytes) != DBS_OK) return DBS_EINVAL;
-  if (k_begin < 0 || k_end > n || k_begin > k_end) return DBS_EINVAL;
-  const int st = device_status();
-  if (st != DBS_OK) return st;
-  if (k_begin == k_end || n == 1) return DBS_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t B = dbs::kBlockRounds;
-  // same algorithm choice as dbs_smooth_range with DBS_ALGO_AUTO
-  if (n <= dbs::kSmallMaxN)
-    return status_of(dbs::launch_small(P, P, n, batch, (int)k_begin, (int)k_end, s, nullptr, true));
-  if (k_begin % B == 0 && (k_end % B == 0 || k_end == n))
-    return status_of(dbs::launch_blocked(P, P, n, batch, k_begin / B, dbs::ceil_div(k_end, B), s,
-                                         nullptr, true));
-  hipError_t e = hipSuccess;
-  for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
-    e = dbs::launch_round_packed(P, n, batch, k, s);
-  return status_of(e);
+  return packed_range_impl(P, n, batch, k_begin, k_end, stream, 0);
+}
+
+int dbs_smooth_packed_directed_range(float *P, int64_t n, int64_t batch, int64_t k_begin,
+                                     int64_t k_end, void *stream) {
+  return packed_range_impl(P, n, batch, k_begin, k_end, stream, dbs::kDirected);
 }
 
 int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags, void *stream) {

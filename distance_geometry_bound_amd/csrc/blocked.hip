@@ -134,7 +134,7 @@ __device__ __forceinline__ void packed_block_store(float *P, int64_t n, int64_t 
 // Panel tile R = (K, J) in row orientation, BK x BK, one workgroup each.
 // grid.x = k-block tiles other than K, grid.y = molecules.  Thread (ty, tx)
 // owns rows a = 4ty..4ty+3 and columns c = 4tx..4tx+3.
-template <bool VEC, bool PK>
+template <bool VEC, bool PK, bool RU>
 __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float *__restrict__ L,
                                                     int64_t n, int64_t batch, int64_t K) {
   __shared__ float4 du[BK][BK / 4];
@@ -142,6 +142,7 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
   __shared__ float4 vu[2][BK / 4];
   __shared__ float4 vl[2][BK / 4];
 
+  rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   int64_t J = blockIdx.x;
   if (J >= K) ++J;
@@ -256,10 +257,14 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) relax1(u[a][q], l[a][q], cuv[a], clv[a], ruv[q], rlv[q]);
+          for (int q = 0; q < 4; ++q) relax1<RU>(u[a][q], l[a][q], cuv[a], clv[a], ruv[q], rlv[q]);
       }
     }
 
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) l[r][q] = lower_out<RU>(l[r][q]);
     // write both orientations (packed: the one slot of U and of L)
     if (PK) packed_block_store(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
 #pragma unroll
@@ -341,7 +346,7 @@ __device__ __forceinline__ void packed_half_store(const HalfLoad &h, bool right,
 // band, updated ahead by k_strip; s1 < 0 for none) are neither read nor
 // written, and band s1's panel columns are not read: while this kernel runs,
 // another stream may be updating exactly those cells.
-template <bool VEC, bool PK>
+template <bool VEC, bool PK, bool RU>
 __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
                                                        float *__restrict__ L, int64_t n,
                                                        int64_t batch, int64_t K, int64_t s1) {
@@ -350,6 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
   __shared__ float4 sru[KC][TILE / 4];
   __shared__ float4 srl[KC][TILE / 4];
 
+  rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int64_t p = blockIdx.x;
   const int64_t J = tri_col(p);
@@ -500,12 +506,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
         for (int r = 0; r < 8; ++r)
 #pragma unroll
           for (int c = 0; c < 8; ++c)
-            relax2(u[r][c], l[r][c], cu0[r], cl0[r], ru0[c], rl0[c], cu1[r], cl1[r], ru1[c],
+            relax2<RU>(u[r][c], l[r][c], cu0[r], cl0[r], ru0[c], rl0[c], cu1[r], cl1[r], ru1[c],
                    rl1[c]);
       }
       __syncthreads();
     }
 
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) l[r][c] = lower_out<RU>(l[r][c]);
     // the store addresses are recomputed here rather than kept live across
     // the k loop from the loads
     int ts = tid;
@@ -540,7 +550,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
 // band K+1 and j outside band K, each kept in its fresh orientation.
 // grid.x = k-block tiles J other than K (one BK x BK tile each),
 // grid.y = molecules.  Thread (ty, tx) owns a 4x4 cell tile.
-template <bool VEC, bool PK>
+template <bool VEC, bool PK, bool RU>
 __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float *__restrict__ L,
                                                     int64_t n, int64_t batch, int64_t K) {
   __shared__ float4 scu[KC][BK / 4];
@@ -548,6 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
   __shared__ float4 sru[KC][BK / 4];
   __shared__ float4 srl[KC][BK / 4];
 
+  rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   int64_t J = blockIdx.x;
   if (J >= K) ++J;
@@ -622,12 +633,16 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            relax2(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
+            relax2<RU>(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
                    rl1[q]);
       }
       __syncthreads();
     }
 
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) l[r][q] = lower_out<RU>(l[r][q]);
     if (PK) packed_block_store(Ub, n, s1, j0, b1, bJ, ty, tx, u, l);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -733,28 +748,32 @@ Events *thread_events() {
 // (for band K+1) reads.  Events order strip(K) after tiles(K-1), and
 // tiles(K+1) after phase 2 of K+1.
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
-                          hipStream_t s, Prof *prof, bool packed) {
+                          hipStream_t s, Prof *prof, unsigned flags) {
   static_assert(BK == kBlockRounds, "k-block size");
   const int64_t TB = ceil_div(n, BK);    // k-blocks
   if (K1 > TB) K1 = TB;
   if (n <= 1 || K0 >= K1) return hipSuccess;
   const int64_t T = ceil_div(n, TILE);   // phase-3 tiles per side
+  const bool packed = flags & kPacked, ru = flags & kDirected;
   const bool vec = (n % 4 == 0) && aligned16(U) && aligned16(L);
   const unsigned gy = (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ);
   const int64_t nn = n * n;
   if (packed) L = U;
-  auto panel = packed ? (vec ? k_panel<true, true> : k_panel<false, true>)
-                      : (vec ? k_panel<true, false> : k_panel<false, false>);
-  auto tiles = packed ? (vec ? k_tiles<true, true> : k_tiles<false, true>)
-                      : (vec ? k_tiles<true, false> : k_tiles<false, false>);
-  auto strip = packed ? (vec ? k_strip<true, true> : k_strip<false, true>)
-                      : (vec ? k_strip<true, false> : k_strip<false, false>);
+#define DBS_PICK(K)                                                                   \
+  (packed ? (ru ? (vec ? K<true, true, true> : K<false, true, true>)                  \
+                : (vec ? K<true, true, false> : K<false, true, false>))               \
+          : (ru ? (vec ? K<true, false, true> : K<false, false, true>)                \
+                : (vec ? K<true, false, false> : K<false, false, false>)))
+  auto panel = DBS_PICK(k_panel);
+  auto tiles = DBS_PICK(k_tiles);
+  auto strip = DBS_PICK(k_strip);
+#undef DBS_PICK
 
   auto phase12 = [&](int64_t K, hipStream_t st) -> hipError_t {
     const int64_t k0 = K * BK;
     const int bK = (int)(n - k0 < BK ? n - k0 : BK);
     hipError_t e =
-        launch_small_block(U, L, n, nn, k0 * n + k0, bK, 0, bK, batch, st, prof, packed);
+        launch_small_block(U, L, n, nn, k0 * n + k0, bK, 0, bK, batch, st, prof, flags);
     if (e != hipSuccess || TB == 1) return e;
     return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(kThreads), st, U,
                   L, n, batch, K);

@@ -15,7 +15,10 @@
 //  * Symmetry is preserved exactly (fp add and max are commutative), so
 //    U[i,k] = U[k,i]: row k alone supplies both operands of a round.
 //  * On the 2^-6 grid every candidate is exact, so blocked schedules and
-//    merged rounds give the same bits as the plain round order.
+//    merged rounds give the same bits as the plain round order.  Off the
+//    grid (directed rounding below) the per-round and single-workgroup
+//    kernels still give the bits of the plain round order; the blocked pass
+//    groups the roundings differently and agrees within a rounding bound.
 //  * Padding: an out-of-range atom p is given U = +inf and L = 0.  Then
 //    every candidate through p is +inf (upper) or -inf (lower), so padded
 //    rows, columns and intermediates never change a real cell.
@@ -32,23 +35,70 @@ constexpr float kInf = __builtin_inff();
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Directed rounding (a pass over bounds that are not on an exact grid): the
+// upper-bound sums are rounded toward +inf and the lower-bound differences
+// toward -inf, so that no bound is rounded past the value it stands for.
+// Both come from one rounding mode, toward +inf, set for the whole kernel:
+// a lower candidate L[i,k] - U[k,j] rounded down equals -(U[k,j] - L[i,k])
+// rounded up, and the negation is exact (it folds into the source modifiers
+// of the max instruction, so the instruction count does not change).
+//
+// The MODE register's FP_ROUND field holds the rounding of f32 operations in
+// bits [1:0] (0 nearest even, 1 toward +inf, 2 toward -inf, 3 toward zero);
+// the f64/f16 bits and the other fields are left alone.  Every wave starts
+// with the mode of its kernel descriptor (nearest even), so the change ends
+// with the kernel.
+__device__ __forceinline__ void round_f32_toward_pos_inf() {
+  constexpr int kHwRegMode = 1, kOffset = 0, kSize = 2;
+  __builtin_amdgcn_s_setreg(kHwRegMode | (kOffset << 6) | ((kSize - 1) << 11), 1);
+}
+
+template <bool RU>
+__device__ __forceinline__ void rounding_prologue() {
+  if (RU) round_f32_toward_pos_inf();
+}
+
+// A lower bound as stored.  With directed rounding a zero candidate comes out
+// as -(x - x) = -0; adding +0 (exact, and +0 for -0 when rounding up) keeps
+// the stored bits those of the plain definition.
+template <bool RU>
+__device__ __forceinline__ float lower_out(float l) {
+  return RU ? l + 0.0f : l;
+}
+
 // One intermediate atom applied to one cell:
 //   (u, l) <- (min(u, cu + ru), max(l, cl - ru, rl - cu))
 // where cu/cl = U/L[i,k] and ru/rl = U/L[k,j].
+template <bool RU = false>
 __device__ __forceinline__ void relax1(float &u, float &l, float cu, float cl, float ru,
                                        float rl) {
   u = fminf(u, cu + ru);
-  l = fmaxf(fmaxf(l, cl - ru), rl - cu);
+  if (RU)
+    l = fmaxf(fmaxf(l, -(ru - cl)), -(cu - rl));
+  else
+    l = fmaxf(fmaxf(l, cl - ru), rl - cu);
 }
 
 // Two intermediate atoms k0, k1 applied to one cell (folds into 3-input
 // min/max instructions).  Same result as relax1(k0) then relax1(k1).
+template <bool RU = false>
 __device__ __forceinline__ void relax2(float &u, float &l, float cu0, float cl0, float ru0,
                                        float rl0, float cu1, float cl1, float ru1, float rl1) {
   u = fminf(fminf(u, cu0 + ru0), cu1 + ru1);
-  l = fmaxf(fmaxf(l, cl0 - ru0), rl0 - cu0);
-  l = fmaxf(fmaxf(l, cl1 - ru1), rl1 - cu1);
+  if (RU) {
+    l = fmaxf(fmaxf(l, -(ru0 - cl0)), -(cu0 - rl0));
+    l = fmaxf(fmaxf(l, -(ru1 - cl1)), -(cu1 - rl1));
+  } else {
+    l = fmaxf(fmaxf(l, cl0 - ru0), rl0 - cu0);
+    l = fmaxf(fmaxf(l, cl1 - ru1), rl1 - cu1);
+  }
 }
+
+// Variants of a pass: storage layout and rounding.
+enum : unsigned {
+  kPacked = 1u,    // one buffer P: U above the diagonal, L below
+  kDirected = 2u,  // sums rounded up, differences rounded down
+};
 
 // Largest molecule the single-workgroup path holds (4x4 cells per thread,
 // upper-triangle tiles only, at most 1024 threads).
@@ -128,23 +178,23 @@ hipError_t launch(Prof *prof, int kind, void (*kernel)(KArgs...), dim3 grid, dim
 }
 
 // Launchers (host side).  They enqueue on `s` and return the first launch
-// error, if any.
+// error, if any.  `flags` (kPacked, kDirected) selects the variant; with
+// kPacked, U == L == P in the one-buffer layout.
 hipError_t launch_round(float *U, float *L, int64_t n, int64_t batch, int64_t k, hipStream_t s,
-                        Prof *prof = nullptr);
+                        Prof *prof = nullptr, unsigned flags = 0);
 // rounds k_lo..k_hi-1 of a whole small molecule in one workgroup
 hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, int k_lo, int k_hi,
-                        hipStream_t s, Prof *prof = nullptr, bool packed = false);
-// k-blocks K0..K1-1 of the blocked pass (rounds 64*K0 .. min(64*K1, n)-1);
-// packed: U == L == P in the one-buffer layout
+                        hipStream_t s, Prof *prof = nullptr, unsigned flags = 0);
+// k-blocks K0..K1-1 of the blocked pass (rounds 64*K0 .. min(64*K1, n)-1)
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
-                          hipStream_t s, Prof *prof = nullptr, bool packed = false);
+                          hipStream_t s, Prof *prof = nullptr, unsigned flags = 0);
 constexpr int kBlockRounds = 64;
 hipError_t launch_restraints(float *U, float *L, int64_t n, int64_t batch, float unknown_L,
                              float unknown_U, const int32_t *mol, const int32_t *ia,
                              const int32_t *ja, const float *lo, const float *hi, int64_t count,
                              uint32_t *status, hipStream_t s, Prof *prof = nullptr);
 hipError_t launch_round_packed(float *P, int64_t n, int64_t batch, int64_t k, hipStream_t s,
-                               Prof *prof = nullptr);
+                               Prof *prof = nullptr, unsigned flags = kPacked);
 hipError_t launch_pack(const float *U, const float *L, float *P, int64_t n, int64_t batch,
                        hipStream_t s);
 hipError_t launch_unpack(const float *P, float *U, float *L, int64_t n, int64_t batch,
@@ -162,7 +212,7 @@ hipError_t launch_check_packed(const float *P, int64_t n, int64_t batch, uint32_
 // diagonal tile of the blocked pass.
 hipError_t launch_small_block(float *U, float *L, int64_t ld, int64_t mstride, int64_t off,
                               int m, int k_lo, int k_hi, int64_t batch, hipStream_t s,
-                              Prof *prof = nullptr, bool packed = false);
+                              Prof *prof = nullptr, unsigned flags = 0);
 
 // Tile pair p of the upper triangle, numbered column-major (p = J(J+1)/2 + I,
 // I <= J): returns J.

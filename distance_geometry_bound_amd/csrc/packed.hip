@@ -27,10 +27,11 @@ constexpr int PT = 64;  // tile side
 
 // grid = (tiles per side, tiles per side, molecules); thread (ty, tx) owns
 // rows 4ty..4ty+3 and columns 4tx..4tx+3 of the tile.
-template <bool VEC>
+template <bool VEC, bool RU>
 __global__ __launch_bounds__(kThreads) void k_round_packed(float *__restrict__ P, int64_t n,
                                                            int64_t batch, int64_t k) {
   __shared__ float su[2][PT], sl[2][PT];  // [0]: rows of the tile, [1]: columns
+  rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int64_t i0 = (int64_t)blockIdx.y * PT, j0 = (int64_t)blockIdx.x * PT;
   const int64_t nn = n * n;
@@ -72,7 +73,8 @@ __global__ __launch_bounds__(kThreads) void k_round_packed(float *__restrict__ P
         if (i < j)
           v[q] = fminf(v[q], ui + uj);
         else if (i > j)
-          v[q] = fmaxf(fmaxf(v[q], li - uj), lj - ui);
+          v[q] = RU ? lower_out<RU>(fmaxf(fmaxf(v[q], -(uj - li)), -(ui - lj)))
+                    : fmaxf(fmaxf(v[q], li - uj), lj - ui);
       }
       // column k is unchanged by round k; rewriting it with the same value
       // would race with other workgroups' reads of it, so it is skipped
@@ -139,12 +141,13 @@ __global__ __launch_bounds__(kThreads) void k_unpack(const float *__restrict__ P
 }  // namespace
 
 hipError_t launch_round_packed(float *P, int64_t n, int64_t batch, int64_t k, hipStream_t s,
-                               Prof *prof) {
-  const bool vec = n % 4 == 0 && aligned16(P);
+                               Prof *prof, unsigned flags) {
+  const bool vec = n % 4 == 0 && aligned16(P), ru = flags & kDirected;
   const unsigned tiles = (unsigned)ceil_div(n, PT);
   const dim3 g(tiles, tiles, (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ));
-  return launch(prof, kProfRound, vec ? k_round_packed<true> : k_round_packed<false>, g,
-                dim3(kThreads), s, P, n, batch, k);
+  auto kern = vec ? (ru ? k_round_packed<true, true> : k_round_packed<true, false>)
+                  : (ru ? k_round_packed<false, true> : k_round_packed<false, false>);
+  return launch(prof, kProfRound, kern, g, dim3(kThreads), s, P, n, batch, k);
 }
 
 hipError_t launch_pack(const float *U, const float *L, float *P, int64_t n, int64_t batch,

@@ -18,9 +18,12 @@ namespace {
 constexpr int kThreads = 256;
 
 // Vector path: n % 4 == 0 and both base pointers 16-byte aligned.
+// RU: directed rounding (dbs_internal.h).
+template <bool RU>
 __global__ __launch_bounds__(kThreads) void k_round_vec(float *__restrict__ U,
                                                         float *__restrict__ L, int64_t n,
                                                         int64_t batch, int64_t k) {
+  rounding_prologue<RU>();
   const int64_t n4 = n >> 2;
   const int64_t j4 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (j4 >= n4) return;
@@ -37,20 +40,23 @@ __global__ __launch_bounds__(kThreads) void k_round_vec(float *__restrict__ U,
       float4 *pu = reinterpret_cast<float4 *>(Ub + i * n) + j4;
       float4 *pl = reinterpret_cast<float4 *>(Lb + i * n) + j4;
       float4 u = *pu, l = *pl;
-      relax1(u.x, l.x, cu, cl, ru.x, rl.x);
-      relax1(u.y, l.y, cu, cl, ru.y, rl.y);
-      relax1(u.z, l.z, cu, cl, ru.z, rl.z);
-      relax1(u.w, l.w, cu, cl, ru.w, rl.w);
+      relax1<RU>(u.x, l.x, cu, cl, ru.x, rl.x);
+      relax1<RU>(u.y, l.y, cu, cl, ru.y, rl.y);
+      relax1<RU>(u.z, l.z, cu, cl, ru.z, rl.z);
+      relax1<RU>(u.w, l.w, cu, cl, ru.w, rl.w);
       *pu = u;
-      *pl = l;
+      *pl = make_float4(lower_out<RU>(l.x), lower_out<RU>(l.y), lower_out<RU>(l.z),
+                        lower_out<RU>(l.w));
     }
   }
 }
 
 // Scalar path: any n, any 4-byte alignment.
+template <bool RU>
 __global__ __launch_bounds__(kThreads) void k_round_scalar(float *__restrict__ U,
                                                            float *__restrict__ L, int64_t n,
                                                            int64_t batch, int64_t k) {
+  rounding_prologue<RU>();
   const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (j >= n) return;
   const int64_t nn = n * n;
@@ -64,9 +70,9 @@ __global__ __launch_bounds__(kThreads) void k_round_scalar(float *__restrict__ U
       const float cu = Ub[i * n + k];
       const float cl = Lb[i * n + k];
       float u = Ub[i * n + j], l = Lb[i * n + j];
-      relax1(u, l, cu, cl, ru, rl);
+      relax1<RU>(u, l, cu, cl, ru, rl);
       Ub[i * n + j] = u;
-      Lb[i * n + j] = l;
+      Lb[i * n + j] = lower_out<RU>(l);
     }
   }
 }
@@ -74,13 +80,15 @@ __global__ __launch_bounds__(kThreads) void k_round_scalar(float *__restrict__ U
 }  // namespace
 
 hipError_t launch_round(float *U, float *L, int64_t n, int64_t batch, int64_t k,
-                        hipStream_t s, Prof *prof) {
+                        hipStream_t s, Prof *prof, unsigned flags) {
   const bool vec = (n % 4 == 0) && aligned16(U) && aligned16(L);
   const int64_t cols = vec ? n / 4 : n;
   dim3 grid((unsigned)ceil_div(cols, kThreads), (unsigned)(n < kMaxGridYZ ? n : kMaxGridYZ),
             (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ));
-  return launch(prof, kProfRound, vec ? k_round_vec : k_round_scalar, grid, dim3(kThreads), s,
-                U, L, n, batch, k);
+  const bool ru = flags & kDirected;
+  auto kern = vec ? (ru ? k_round_vec<true> : k_round_vec<false>)
+                  : (ru ? k_round_scalar<true> : k_round_scalar<false>);
+  return launch(prof, kProfRound, kern, grid, dim3(kThreads), s, U, L, n, batch, k);
 }
 
 }  // namespace dbs

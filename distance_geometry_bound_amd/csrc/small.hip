@@ -34,13 +34,14 @@ __device__ __forceinline__ void publish(float (&u)[4][4], float (&l)[4][4], int 
   }
 }
 
-template <bool PK>
+template <bool PK, bool RU>
 __global__ __launch_bounds__(1024) void k_small(float *U, float *L, int64_t ld, int64_t mstride,
                                                 int64_t off, int m, int k_lo, int k_hi,
                                                 int64_t batch) {
   __shared__ float vu[2][4 * kMaxG];
   __shared__ float vl[2][4 * kMaxG];
 
+  rounding_prologue<RU>();
   const int G = (m + 3) >> 2;
   const int tiles = G * (G + 1) / 2;
   const int t = threadIdx.x;
@@ -98,7 +99,8 @@ __global__ __launch_bounds__(1024) void k_small(float *U, float *L, int64_t ld, 
 #pragma unroll
           for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) relax1(u[a][c], l[a][c], cu[a], cl[a], ru[c], rl[c]);
+            for (int c = 0; c < 4; ++c)
+              relax1<RU>(u[a][c], l[a][c], cu[a], cl[a], ru[c], rl[c]);
         }
       }
     }
@@ -109,6 +111,7 @@ __global__ __launch_bounds__(1024) void k_small(float *U, float *L, int64_t ld, 
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int i = i0 + r, j = j0 + c;
+          l[r][c] = lower_out<RU>(l[r][c]);
           if (PK) {
             // one slot each for U(i,j) and L(i,j); a diagonal tile holds both
             // (i,j) and (j,i) with the same values, the diagonal stays 0
@@ -136,19 +139,22 @@ __global__ __launch_bounds__(1024) void k_small(float *U, float *L, int64_t ld, 
 
 hipError_t launch_small_block(float *U, float *L, int64_t ld, int64_t mstride, int64_t off,
                               int m, int k_lo, int k_hi, int64_t batch, hipStream_t s,
-                              Prof *prof, bool packed) {
+                              Prof *prof, unsigned flags) {
   if (m <= 1 || k_lo >= k_hi) return hipSuccess;
   const int G = (m + 3) / 4;
   const int tiles = G * (G + 1) / 2;
   const int threads = (tiles + 63) / 64 * 64;
   const unsigned grid = (unsigned)(batch < 1048576 ? batch : 1048576);
-  return launch(prof, kProfSmall, packed ? k_small<true> : k_small<false>, dim3(grid),
-                dim3(threads), s, U, L, ld, mstride, off, m, k_lo, k_hi, batch);
+  const bool pk = flags & kPacked, ru = flags & kDirected;
+  auto kern = pk ? (ru ? k_small<true, true> : k_small<true, false>)
+                 : (ru ? k_small<false, true> : k_small<false, false>);
+  return launch(prof, kProfSmall, kern, dim3(grid), dim3(threads), s, U, L, ld, mstride, off, m,
+                k_lo, k_hi, batch);
 }
 
 hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, int k_lo, int k_hi,
-                        hipStream_t s, Prof *prof, bool packed) {
-  return launch_small_block(U, L, n, n * n, 0, (int)n, k_lo, k_hi, batch, s, prof, packed);
+                        hipStream_t s, Prof *prof, unsigned flags) {
+  return launch_small_block(U, L, n, n * n, 0, (int)n, k_lo, k_hi, batch, s, prof, flags);
 }
 
 }  // namespace dbs

@@ -213,6 +213,37 @@ int dbs_bounds_from_restraints(float *U, float *L, int64_t n, int64_t batch,
                                    |value| >= 2^17                            */
 
 /*
+ * Directed rounding (the notes' §6: the smoothing is sensitive to the
+ * precision of its float arithmetic).  On bounds that are not on the 2^-6
+ * grid a sum or difference of two bounds is generally not representable in
+ * float32, and round-to-nearest can move a bound past the value it stands
+ * for (a shortened upper bound, a raised lower bound: an unsound result,
+ * and even L > U on consistent input).  These entry points round every
+ * upper-bound sum toward +inf and every lower-bound difference toward
+ * -inf, so that each result is an upper (lower) bound on the exact value of
+ * the path it comes from, and sound bounds stay sound.
+ *
+ * dbs_smooth_directed_range -- as dbs_smooth_range, with directed rounding.
+ *   With DBS_ALGO_PERK and DBS_ALGO_LDS the result is bit for bit that of
+ *   the rounds k_begin..k_end-1 in plain order with sums rounded up and
+ *   differences rounded down.  DBS_ALGO_BLOCKED groups the same candidates
+ *   differently, so its bits may differ from the plain order within the
+ *   rounding error (relative 2^-23 per addition along a path); it is sound
+ *   in the same sense.  On grid inputs (every operation exact) all
+ *   algorithms give the bits of dbs_smooth_range.
+ * dbs_smooth_directed -- a full pass, algorithm as dbs_smooth.
+ * dbs_smooth_packed_directed_range -- dbs_smooth_packed_range with directed
+ *   rounding (same algorithm choice, same remarks).
+ * Preconditions and argument errors as dbs_smooth, except that values need
+ * not lie on the 2^-6 grid (finite, 0 <= L, symmetric, zero diagonal).
+ */
+int dbs_smooth_directed(float *U, float *L, int64_t n, int64_t batch, void *stream);
+int dbs_smooth_directed_range(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
+                              int64_t k_end, void *stream, int algo);
+int dbs_smooth_packed_directed_range(float *P, int64_t n, int64_t batch, int64_t k_begin,
+                                     int64_t k_end, void *stream);
+
+/*
  * Packed storage (the notes' §6 keeps the two symmetric matrices as two
  * triangles): one [batch][n][n] float32 buffer P with P[i,j] = U[i,j] for
  * i < j, L[i,j] for i > j, and U[i,i] (= L[i,i] = 0) on the diagonal.  It
