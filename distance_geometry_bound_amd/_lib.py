@@ -24,8 +24,8 @@ CHECK_FLAGS = {
 
 DBS_OK, DBS_EINVAL, DBS_EDEVICE, DBS_ELAUNCH, DBS_EUNSUPPORTED = 0, -1, -2, -3, -4
 
-EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
-           "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened", "dbs_bounds_from_restraints",
+EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_round",
+           "dbs_check", "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened", "dbs_bounds_from_restraints",
            "dbs_pack", "dbs_unpack", "dbs_smooth_packed", "dbs_smooth_packed_range",
            "dbs_check_packed", "dbs_smooth_directed", "dbs_smooth_directed_range",
            "dbs_smooth_packed_directed_range",
@@ -59,6 +59,7 @@ def lib():
         L.dbs_smooth_profiled.argtypes = [vp, vp, i64, i64, vp, c_int,
                                           ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
         L.dbs_rounds.argtypes = [vp, vp, i64, i64, i64, i64, vp]
+        L.dbs_round.argtypes = [vp, vp, i64, i64, i64, vp]
         L.dbs_smooth_range.argtypes = [vp, vp, i64, i64, i64, i64, vp, c_int]
         L.dbs_tightened.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp]
         L.dbs_pack.argtypes = [vp, vp, vp, i64, i64, vp]
@@ -75,7 +76,8 @@ def lib():
         L.dbs_auto_algo.argtypes = [i64, i64]
         L.dbs_strerror.argtypes = [c_int]
         L.dbs_strerror.restype = ctypes.c_char_p
-        for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_check",
+        for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_round",
+                  "dbs_check",
                   "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened",
                   "dbs_bounds_from_restraints", "dbs_pack", "dbs_unpack", "dbs_smooth_packed",
                   "dbs_smooth_packed_range", "dbs_check_packed", "dbs_smooth_directed",
@@ -130,13 +132,21 @@ def _call(T, fn, *args):
         _raise(fn(*args))
 
 
-def smooth(U, L, algo: str = "auto") -> None:
-    """One full smoothing pass on U, L in place (enqueued on the current stream)."""
+def smooth(U, L, algo: str = "auto", check: bool = False) -> None:
+    """One full smoothing pass on U, L in place (enqueued on the current stream).
+
+    check=True first tests the preconditions on the device (dbs_check; this
+    synchronises) and raises ValueError naming the violated ones."""
     n, batch = _shape(U, L)
     if algo not in _ALGOS:
         raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
     if n == 0 or batch == 0:
         return
+    if check:
+        bad = _check_flags(U, L)
+        if bad:
+            names = [k for k, v in CHECK_FLAGS.items() if bad & v]
+            raise ValueError(f"bounds violate the preconditions: {', '.join(names)}")
     _call(U, lib().dbs_smooth_algo, U.data_ptr(), L.data_ptr(), n, batch, _stream(U),
           _ALGOS[algo])
 
@@ -165,8 +175,11 @@ def smooth_rounds(U, L, k_begin: int, k_end: int) -> None:
 
 
 def smooth_round(U, L, k: int) -> None:
-    """Round k only."""
-    smooth_rounds(U, L, k, k + 1)
+    """Round k only (dbs_round)."""
+    n, batch = _shape(U, L)
+    if n == 0 or batch == 0:
+        return
+    _call(U, lib().dbs_round, U.data_ptr(), L.data_ptr(), n, batch, int(k), _stream(U))
 
 
 def smooth_range(U, L, k_begin: int, k_end: int, algo: str = "auto") -> None:
@@ -305,7 +318,7 @@ def smooth_packed_directed(P, k_begin: int = 0, k_end=None) -> None:
           _stream(P))
 
 
-def check(U, L) -> int:
+def _check_flags(U, L) -> int:
     """Precondition flags (CHECK_FLAGS bits) of U, L; synchronises the stream."""
     import torch
 
@@ -316,6 +329,11 @@ def check(U, L) -> int:
     _call(U, lib().dbs_check, U.data_ptr(), L.data_ptr(), n, batch, flags.data_ptr(),
           _stream(U))
     return int(flags.item()) & 0xFFFFFFFF
+
+
+def check(U, L) -> int:
+    """Precondition flags (CHECK_FLAGS bits) of U, L; synchronises the stream."""
+    return _check_flags(U, L)
 
 
 def check_packed(P) -> int:

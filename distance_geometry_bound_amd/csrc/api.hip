@@ -191,6 +191,11 @@ int dbs_rounds(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin, in
   return status_of(e);
 }
 
+int dbs_round(float *U, float *L, int64_t n, int64_t batch, int64_t k, void *stream) {
+  if (k < 0 || k >= n) return DBS_EINVAL;
+  return dbs_rounds(U, L, n, batch, k, k + 1, stream);
+}
+
 int dbs_check(const float *U, const float *L, int64_t n, int64_t batch, uint32_t *d_flags,
               void *stream) {
   int st = validate(U, L, n, batch);

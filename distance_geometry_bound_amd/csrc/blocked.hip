@@ -8,10 +8,10 @@
 // any partition of the rounds into blocks yields the same shortest paths.
 //
 // For k-block K (atoms k0..k0+bK-1, "band K"):
-//   phase 1  the diagonal tile (K,K): a full pass over it, rounds in order
-//            (k_small, one workgroup per molecule);
-//   phase 2  every other tile of band K ("panel"): rounds in order, reading
-//            the final diagonal tile (k_panel, one workgroup per tile);
+//   phase 1  the diagonal tile (K,K): a full pass over it, rounds in order;
+//   phase 2  every other tile of band K ("panel"): rounds in order, over
+//            the diagonal tile's rows (phases 1 and 2 run together in
+//            k_diag_panel, one workgroup per panel tile);
 //   phase 3  every remaining cell: all bK rounds at once from the finished
 //            panel (k_tiles, plus k_strip for band K+1 when running ahead).
 //            This is where 1 - O(BK/n) of the work is.
@@ -130,17 +130,28 @@ __device__ __forceinline__ void packed_block_store(float *P, int64_t n, int64_t 
     }
 }
 
-// ---------------------------------------------------------------- phase 2
-// Panel tile R = (K, J) in row orientation, BK x BK, one workgroup each.
-// grid.x = k-block tiles other than K, grid.y = molecules.  Thread (ty, tx)
-// owns rows a = 4ty..4ty+3 and columns c = 4tx..4tx+3.
+// ---------------------------------------------------------------- phases 1 and 2
+// Phases 1 and 2 of k-block K in one launch.  Workgroup J (one per k-block
+// tile other than K; grid.y = molecules) holds the diagonal tile D = (K, K)
+// and its panel tile R = (K, J) in registers, thread (ty, tx) owning rows
+// 4ty..4ty+3 and columns 4tx..4tx+3 of each, and runs the rounds m of band K
+// in order over both.  Row m of D and of R is published through LDS
+// (double-buffered, one barrier per round); column m of D equals its row m
+// by symmetry:
+//   D[a][b] <- relax(D[a][b], D[a][m], D[m][b])
+//   R[a][c] <- relax(R[a][c], D[a][m], R[m][c]).
+// These are the plain rounds of the notes' §3 restricted to the rows of band
+// K, so they reach the values of finishing D first and the panel from it
+// (exactly, on the 2^-6 grid).  Every workgroup repeats D's rounds: that
+// costs less than a launch of its own on the critical path of the pass.
+// Workgroup 0 writes D back.  Cells outside the matrix start neutral and stay
+// neutral (every candidate through them is +inf for U and <= 0 for L).
 template <bool VEC, bool PK, bool RU>
-__global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float *__restrict__ L,
-                                                    int64_t n, int64_t batch, int64_t K) {
-  __shared__ float4 du[BK][BK / 4];
-  __shared__ float4 dl[BK][BK / 4];
-  __shared__ float4 vu[2][BK / 4];
-  __shared__ float4 vl[2][BK / 4];
+__global__ __launch_bounds__(kThreads) void k_diag_panel(float *__restrict__ U,
+                                                         float *__restrict__ L, int64_t n,
+                                                         int64_t batch, int64_t K) {
+  __shared__ float4 dvu[2][BK / 4], dvl[2][BK / 4];  // row m of D
+  __shared__ float4 rvu[2][BK / 4], rvl[2][BK / 4];  // row m of R
 
   rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
@@ -150,94 +161,52 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
   const int bK = (int)(n - k0 < BK ? n - k0 : BK);
   const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
   const bool rowor = fresh(K, J);
+  const bool writes_d = blockIdx.x == 0;
   const int64_t nn = n * n;
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
     float *Ub = U + b * nn;
     float *Lb = PK ? Ub : L + b * nn;
 
-    // the finished diagonal tile (both halves current after phase 1): all
-    // loads issued before the LDS stores
+    float du[4][4], dl[4][4];  // D[4ty + r][4tx + q]
+    float u[4][4], l[4][4];    // R[4ty + r][4tx + q] = cell (k0 + 4ty + r, j0 + 4tx + q)
     if (PK) {
-      // the raw P tile (K, K) goes to dl; then U = P[min][max] and
-      // L = P[max][min] are read back out of it
-      float4 xp[BK * BK / 4 / kThreads];
-#pragma unroll
-      for (int t = 0; t < BK * BK / 4 / kThreads; ++t) {
-        const int e = tid + t * kThreads;
-        const int m = e / (BK / 4), a4 = (e % (BK / 4)) * 4;
-        const int cnt = m < bK ? clamp4(bK - a4) : 0;
-        xp[t] = load4<VEC>(Ub + (k0 + m) * n + k0 + a4, cnt, 0.0f, Ub);
-      }
-#pragma unroll
-      for (int t = 0; t < BK * BK / 4 / kThreads; ++t) {
-        const int e = tid + t * kThreads;
-        dl[e / (BK / 4)][e % (BK / 4)] = xp[t];
-      }
-      __syncthreads();
-      const float *raw = reinterpret_cast<const float *>(dl);
-      float xu[BK * BK / kThreads], xl[BK * BK / kThreads];
-#pragma unroll
-      for (int t = 0; t < BK * BK / kThreads; ++t) {
-        const int e = tid + t * kThreads, m = e / BK, a = e % BK;
-        const int lo = m < a ? m : a, hi = m < a ? a : m;
-        const bool in = m < bK && a < bK;
-        xu[t] = in ? raw[lo * BK + hi] : kInf;
-        xl[t] = in ? raw[hi * BK + lo] : 0.0f;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int t = 0; t < BK * BK / kThreads; ++t) {
-        const int e = tid + t * kThreads;
-        reinterpret_cast<float *>(du)[e] = xu[t];
-        reinterpret_cast<float *>(dl)[e] = xl[t];
-      }
-    } else {
-      float4 xu[BK * BK / 4 / kThreads], xl[BK * BK / 4 / kThreads];
-#pragma unroll
-      for (int t = 0; t < BK * BK / 4 / kThreads; ++t) {
-        const int e = tid + t * kThreads;
-        const int m = e / (BK / 4), a4 = (e % (BK / 4)) * 4;
-        const int cnt = m < bK ? clamp4(bK - a4) : 0;
-        const int64_t g = (k0 + m) * n + k0 + a4;
-        xu[t] = load4<VEC>(Ub + g, cnt, kInf, Ub);
-        xl[t] = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
-      }
-#pragma unroll
-      for (int t = 0; t < BK * BK / 4 / kThreads; ++t) {
-        const int e = tid + t * kThreads;
-        du[e / (BK / 4)][e % (BK / 4)] = xu[t];
-        dl[e / (BK / 4)][e % (BK / 4)] = xl[t];
-      }
-    }
-
-    float u[4][4], l[4][4];
-    if (PK) {
+      packed_block_load<VEC>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
       packed_block_load<VEC>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
-    } else if (rowor) {
-      // R[a][c] = M[k0+a][j0+c]
+    } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int a = ty * 4 + r;
-        const int cnt = a < bK ? clamp4(bJ - tx * 4) : 0;
-        const int64_t g = (k0 + a) * n + j0 + tx * 4;
+        const int cnt = a < bK ? clamp4(bK - tx * 4) : 0;
+        const int64_t g = (k0 + a) * n + k0 + tx * 4;
         const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
-        u[r][0] = x.x; u[r][1] = x.y; u[r][2] = x.z; u[r][3] = x.w;
-        l[r][0] = y.x; l[r][1] = y.y; l[r][2] = y.z; l[r][3] = y.w;
+        du[r][0] = x.x; du[r][1] = x.y; du[r][2] = x.z; du[r][3] = x.w;
+        dl[r][0] = y.x; dl[r][1] = y.y; dl[r][2] = y.z; dl[r][3] = y.w;
       }
-    } else {
-      // R[a][c] = M[j0+c][k0+a]
+      if (rowor) {
+        // R[a][c] = M[k0+a][j0+c]
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = tx * 4 + q;
-        const int cnt = c < bJ ? clamp4(bK - ty * 4) : 0;
-        const int64_t g = (j0 + c) * n + k0 + ty * 4;
-        const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
-        u[0][q] = x.x; u[1][q] = x.y; u[2][q] = x.z; u[3][q] = x.w;
-        l[0][q] = y.x; l[1][q] = y.y; l[2][q] = y.z; l[3][q] = y.w;
+        for (int r = 0; r < 4; ++r) {
+          const int a = ty * 4 + r;
+          const int cnt = a < bK ? clamp4(bJ - tx * 4) : 0;
+          const int64_t g = (k0 + a) * n + j0 + tx * 4;
+          const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+          u[r][0] = x.x; u[r][1] = x.y; u[r][2] = x.z; u[r][3] = x.w;
+          l[r][0] = y.x; l[r][1] = y.y; l[r][2] = y.z; l[r][3] = y.w;
+        }
+      } else {
+        // R[a][c] = M[j0+c][k0+a]
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = tx * 4 + q;
+          const int cnt = c < bJ ? clamp4(bK - ty * 4) : 0;
+          const int64_t g = (j0 + c) * n + k0 + ty * 4;
+          const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+          u[0][q] = x.x; u[1][q] = x.y; u[2][q] = x.z; u[3][q] = x.w;
+          l[0][q] = y.x; l[1][q] = y.y; l[2][q] = y.z; l[3][q] = y.w;
+        }
       }
     }
-    __syncthreads();
 
     for (int mb = 0; mb < BK / 4; ++mb) {
 #pragma unroll
@@ -246,27 +215,41 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
         if (m >= bK) break;  // uniform
         const int buf = m & 1;
         if (ty == mb) {
-          vu[buf][tx] = make_float4(u[r][0], u[r][1], u[r][2], u[r][3]);
-          vl[buf][tx] = make_float4(l[r][0], l[r][1], l[r][2], l[r][3]);
+          dvu[buf][tx] = make_float4(du[r][0], du[r][1], du[r][2], du[r][3]);
+          dvl[buf][tx] = make_float4(dl[r][0], dl[r][1], dl[r][2], dl[r][3]);
+          rvu[buf][tx] = make_float4(u[r][0], u[r][1], u[r][2], u[r][3]);
+          rvl[buf][tx] = make_float4(l[r][0], l[r][1], l[r][2], l[r][3]);
         }
         __syncthreads();
-        const float4 ru = vu[buf][tx], rl = vl[buf][tx];
-        const float4 cu = du[m][ty], cl = dl[m][ty];  // U[i,k] = D[a][m] = D[m][a]
+        const float4 cu = dvu[buf][ty], cl = dvl[buf][ty];  // D[a][m] = D[m][a]
+        const float4 eu = dvu[buf][tx], el = dvl[buf][tx];  // D[m][b]
+        const float4 ru = rvu[buf][tx], rl = rvl[buf][tx];  // R[m][c]
         const float cuv[4] = {cu.x, cu.y, cu.z, cu.w}, clv[4] = {cl.x, cl.y, cl.z, cl.w};
+        const float euv[4] = {eu.x, eu.y, eu.z, eu.w}, elv[4] = {el.x, el.y, el.z, el.w};
         const float ruv[4] = {ru.x, ru.y, ru.z, ru.w}, rlv[4] = {rl.x, rl.y, rl.z, rl.w};
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) relax1<RU>(u[a][q], l[a][q], cuv[a], clv[a], ruv[q], rlv[q]);
+          for (int q = 0; q < 4; ++q) {
+            relax1<RU>(du[a][q], dl[a][q], cuv[a], clv[a], euv[q], elv[q]);
+            relax1<RU>(u[a][q], l[a][q], cuv[a], clv[a], ruv[q], rlv[q]);
+          }
       }
     }
 
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) l[r][q] = lower_out<RU>(l[r][q]);
-    // write both orientations (packed: the one slot of U and of L)
-    if (PK) packed_block_store(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
+      for (int q = 0; q < 4; ++q) {
+        l[r][q] = lower_out<RU>(l[r][q]);
+        dl[r][q] = lower_out<RU>(dl[r][q]);
+      }
+    // R in both orientations (packed: the one slot of U and of L); D, which
+    // lies in a fresh tile, as a full square
+    if (PK) {
+      packed_block_store(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
+      if (writes_d) packed_block_store(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -278,11 +261,14 @@ __global__ __launch_bounds__(kThreads) void k_panel(float *__restrict__ U, float
           Ub[(j0 + c) * n + k0 + a] = u[r][q];
           Lb[(j0 + c) * n + k0 + a] = l[r][q];
         }
+        if (!PK && writes_d && a < bK && c < bK) {
+          Ub[(k0 + a) * n + k0 + c] = du[r][q];
+          Lb[(k0 + a) * n + k0 + c] = dl[r][q];
+        }
       }
     __syncthreads();  // LDS reuse by the next molecule
   }
 }
-
 
 // ---------------------------------------------------------------- packed panel staging
 // Packed layout: the panel values of band K at the 64 columns xh..xh+63 and
@@ -764,17 +750,16 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
                 : (vec ? K<true, true, false> : K<false, true, false>))               \
           : (ru ? (vec ? K<true, false, true> : K<false, false, true>)                \
                 : (vec ? K<true, false, false> : K<false, false, false>)))
-  auto panel = DBS_PICK(k_panel);
+  auto panel = DBS_PICK(k_diag_panel);
   auto tiles = DBS_PICK(k_tiles);
   auto strip = DBS_PICK(k_strip);
 #undef DBS_PICK
 
+  // phases 1 and 2 of block K: one launch (the diagonal tile alone when it is
+  // the only block)
   auto phase12 = [&](int64_t K, hipStream_t st) -> hipError_t {
-    const int64_t k0 = K * BK;
-    const int bK = (int)(n - k0 < BK ? n - k0 : BK);
-    hipError_t e =
-        launch_small_block(U, L, n, nn, k0 * n + k0, bK, 0, bK, batch, st, prof, flags);
-    if (e != hipSuccess || TB == 1) return e;
+    if (TB == 1)
+      return launch_small_block(U, L, n, nn, 0, (int)n, 0, (int)n, batch, st, prof, flags);
     return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(kThreads), st, U,
                   L, n, batch, K);
   };

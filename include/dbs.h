@@ -102,6 +102,13 @@ int dbs_rounds(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
                int64_t k_end, void *stream);
 
 /*
+ * dbs_round -- the single round k (the notes' §3-§4: one render pass per
+ * intermediate atom), in place on every molecule.  0 <= k < n, else
+ * DBS_EINVAL.  Equivalent to dbs_rounds(U, L, n, batch, k, k + 1, stream).
+ */
+int dbs_round(float *U, float *L, int64_t n, int64_t batch, int64_t k, void *stream);
+
+/*
  * dbs_check -- test the per-entry preconditions on the device in O(n^2).
  * ORs DBS_CHECK_* bits into *d_flags (a device pointer to one uint32 that
  * the caller zeroes beforehand and reads after synchronising).  Run it on

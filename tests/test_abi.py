@@ -96,3 +96,13 @@ def test_python_wrapper_rejects_cpu_tensors():
         dgb.smooth(U, U.clone())
     with pytest.raises(TypeError):
         dgb.smooth(U.double(), U.double())
+
+
+def test_round_rejects_k_out_of_range_on_the_host():
+    # argument errors are found before anything is enqueued (no device needed)
+    import ctypes
+    lib = dgb.lib()
+    buf = (ctypes.c_float * 16)()
+    p = ctypes.cast(buf, ctypes.c_void_p).value
+    assert lib.dbs_round(p, p, 4, 1, -1, None) == -1
+    assert lib.dbs_round(p, p, 4, 1, 4, None) == -1

@@ -269,3 +269,22 @@ def test_empty_and_trivial_shapes():
     U = torch.zeros(8, 8, device=DEV)
     with pytest.raises(ValueError):
         dgb.smooth(U, U)                       # U and L overlap
+
+
+def test_single_round_entry_and_smooth_check_option():
+    U0, L0, _ = gen.random_sound_bounds(70, seed=70, batch=2)
+    U, L = dev(U0), dev(L0)
+    Ue, Le = U0, L0
+    for k in (0, 1, 69):
+        dgb.smooth_round(U, L, k)
+        Ue, Le = oracle.rounds(Ue, Le, k, k + 1)
+        assert_bits(host(U), host(L), Ue, Le, f"round {k}")
+    with pytest.raises(ValueError):
+        dgb.smooth_round(U, L, 70)
+    U, L = dev(U0), dev(L0)
+    dgb.smooth(U, L, check=True)
+    assert_bits(host(U), host(L), *oracle.smooth(U0, L0), "checked pass")
+    Ub = U0.copy()
+    Ub[0, 1, 2] = Ub[0, 2, 1] = Ub[0, 1, 2] + 0.001   # off the grid
+    with pytest.raises(ValueError, match="unquant"):
+        dgb.smooth(dev(Ub), dev(L0), check=True)

@@ -1,9 +1,10 @@
 """CPU model of the blocked pass's schedule (test code only).
 
 The GPU pass (csrc/blocked.hip) runs, per k-block K of BK = 64 atoms,
-  phase 1  FW on the diagonal tile (K,K);
-  phase 2  the panel tiles of band K, each read from its fresh orientation
-           (upper TILE x TILE region) and written in both orientations;
+  phases 1+2  the rounds of band K over the diagonal tile (K,K) and, in the
+           same loop, over each panel tile of band K (one workgroup per
+           panel tile), panel tiles read from their fresh orientation (upper
+           TILE x TILE region) and written in both orientations;
   phase 3  band K+1 first (the strip, on a second stream, followed there by
            phases 1-2 of K+1), and every other live cell of the upper
            TILE x TILE tiles (the bulk, on the caller's stream);
@@ -51,45 +52,41 @@ class Model:
         l = max(L[i, j], L[k, i] - U[k, j], L[k, j] - U[k, i])
         return u, l
 
-    def phase1(self, K):
-        b = self.band(K)
-        U, L = self.U, self.L
-        for k in b:
-            new = {(i, j): self.relax(i, j, k, U, L) for i in b for j in b}
-            for (i, j), (u, l) in new.items():
-                U[i, j], L[i, j] = u, l
-        cells = {(i, j) for i in b for j in b}
-        return cells, cells
-
-    def phase2(self, K):
+    def phase12(self, K):
+        """Phases 1 and 2 in one launch (k_diag_panel): every panel workgroup
+        runs the rounds m of band K in order over the diagonal tile D and its
+        panel tile R, each round reading row m of both as they stand before
+        the round (D's column m is its row m by symmetry).  Panel tiles are
+        read from their fresh orientation and written in both; D is written
+        as a full square."""
         reads, writes = set(), set()
         kb = self.band(K)
-        reads |= {(i, j) for i in kb for j in kb}
+        U, L = self.U, self.L
+        D = {(a, b): (U[a, b], L[a, b]) for a in kb for b in kb}
+        reads |= set(D)
+        R = {}
         for J in range(self.TB):
             if J == K:
                 continue
-            jb = self.band(J)
-            # R[a][c] = cell (k0+a, j0+c), read from the fresh orientation
-            R = {}
             for a in kb:
-                for c in jb:
+                for c in self.band(J):
                     src = (a, c) if fresh(K, J) else (c, a)
-                    R[(a, c)] = (self.U[src], self.L[src])
+                    R[(a, c)] = (U[src], L[src])
                     reads.add(src)
-            D = lambda x, y: (self.U[x, y], self.L[x, y])
-            for m in kb:
-                new = {}
-                for a in kb:
-                    cu, cl = D(m, a)               # U[a,m] = D[m][a]
-                    for c in jb:
-                        ru, rl = R[(m, c)]
-                        u, l = R[(a, c)]
-                        new[(a, c)] = (min(u, cu + ru), max(l, cl - ru, rl - cu))
-                R = new
-            for (a, c), (u, l) in R.items():
-                self.U[a, c] = self.U[c, a] = u
-                self.L[a, c] = self.L[c, a] = l
-                writes |= {(a, c), (c, a)}
+        for m in kb:
+            def rel(cell, row):
+                (u, l), (cu, cl), (ru, rl) = cell, D[(m, row[0])], row[1]
+                return min(u, cu + ru), max(l, cl - ru, rl - cu)
+            newD = {(a, b): rel(D[(a, b)], (a, D[(m, b)])) for (a, b) in D}
+            newR = {(a, c): rel(R[(a, c)], (a, R[(m, c)])) for (a, c) in R}
+            D, R = newD, newR
+        for (a, b), (u, l) in D.items():
+            U[a, b], L[a, b] = u, l
+            writes.add((a, b))
+        for (a, c), (u, l) in R.items():
+            U[a, c] = U[c, a] = u
+            L[a, c] = L[c, a] = l
+            writes |= {(a, c), (c, a)}
         return reads, writes
 
     def strip(self, K):
@@ -140,17 +137,14 @@ class Model:
         return reads, writes
 
     def run(self):
-        self.phase1(0)
-        if self.TB > 1:
-            self.phase2(0)
+        self.phase12(0)
         for K in range(self.TB):
             if K + 1 == self.TB:
                 self.tiles(K, ahead=False)
                 continue
             sr, sw = self.strip(K)
-            r1, w1 = self.phase1(K + 1)
-            r2, w2 = self.phase2(K + 1)
-            side_r, side_w = sr | r1 | r2, sw | w1 | w2
+            r2, w2 = self.phase12(K + 1)
+            side_r, side_w = sr | r2, sw | w2
             tr, tw = self.tiles(K, ahead=True)
             assert not (side_w & (tr | tw)), f"k-block {K}: side stream writes what the bulk touches"
             assert not (tw & side_r), f"k-block {K}: bulk writes what the side stream reads"
