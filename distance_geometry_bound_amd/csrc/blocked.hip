@@ -44,6 +44,12 @@ constexpr int RATIO = TILE / BK;
 constexpr int KC = 16;          // atoms per LDS chunk in phase 3
 constexpr int kThreads = 256;
 
+// The side-stream kernels (band K+1 strip, then phases 1-2 of block K+1) are
+// the critical path of a k-block whenever they share compute units with the
+// bulk kernel: their waves take instruction-issue priority over its waves on
+// the same SIMD (wave priority only; the streams keep the default priority).
+__device__ __forceinline__ void critical_path_priority() { __builtin_amdgcn_s_setprio(2); }
+
 // (k-block tile a, k-block tile b) is fresh under the symmetric schedule
 __device__ __forceinline__ bool fresh(int64_t a, int64_t b) { return a / RATIO <= b / RATIO; }
 
@@ -70,59 +76,94 @@ __device__ __forceinline__ float4 load4(const float *p, int cnt, float fill, con
 
 __device__ __forceinline__ int clamp4(int64_t left) { return left < 0 ? 0 : (left > 4 ? 4 : (int)left); }
 
+// Two consecutive entries, as load4.  VEC: p is 8-byte aligned and cnt is 0
+// or >= 2.
+template <bool VEC>
+__device__ __forceinline__ float2 load2(const float *p, int cnt, float fill, const float *safe) {
+  if (VEC) {
+    const float2 v = *reinterpret_cast<const float2 *>(cnt >= 2 ? p : safe);
+    return cnt >= 2 ? v : make_float2(fill, fill);
+  }
+  const float x0 = *(cnt > 0 ? p : safe), x1 = *(cnt > 1 ? p + 1 : safe);
+  return make_float2(cnt > 0 ? x0 : fill, cnt > 1 ? x1 : fill);
+}
+
+// S consecutive entries (S = 2 or 4) as an array.
+template <int S>
+struct Seg {
+  float v[S];
+};
+
+template <bool VEC, int S>
+__device__ __forceinline__ Seg<S> load_seg(const float *p, int64_t left, float fill,
+                                           const float *safe) {
+  Seg<S> r;
+  const int cnt = left < 0 ? 0 : (left > S ? S : (int)left);
+  if constexpr (S == 4) {
+    const float4 x = load4<VEC>(p, cnt, fill, safe);
+    r.v[0] = x.x; r.v[1] = x.y; r.v[2] = x.z; r.v[3] = x.w;
+  } else {
+    static_assert(S == 2, "segments of 2 or 4 entries");
+    const float2 x = load2<VEC>(p, cnt, fill, safe);
+    r.v[0] = x.x; r.v[1] = x.y;
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------- packed blocks
 // Packed layout: logical cell (i, j) has U at P[min][max] and L at P[max][min].
 // A BK x BK block of logical cells (r0 + a, c0 + c), a < rows, c < cols, is
-// read into u/l[4][4] of thread (ty, tx) (rows 4ty.., columns 4tx..) from
+// read into u/l[S][S] of thread (ty, tx) (rows S*ty.., columns S*tx..) from
 // the row segments P[r0+a][c0..] and the column segments P[c0+c][r0..], both
-// as float4.  Right of the diagonal (r0 < c0) the row segments hold U; left
+// as S-wide vectors.  Right of the diagonal (r0 < c0) the row segments hold U; left
 // of it L; on a diagonal block (r0 == c0) it is decided per cell, and the
 // diagonal itself reads P[i][i] for both.  Cells outside get the neutral
 // values.
-template <bool VEC>
+template <bool VEC, int S = 4>
 __device__ __forceinline__ void packed_block_load(const float *P, int64_t n, int64_t r0,
                                                   int64_t c0, int rows, int cols, int ty, int tx,
-                                                  float (&u)[4][4], float (&l)[4][4]) {
-  float d[4][4], t[4][4];
+                                                  float (&u)[S][S], float (&l)[S][S]) {
+  // all 2S loads are issued before any value is unpacked
+  Seg<S> x[S], y[S];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int a = ty * 4 + r;
-    const int cnt = a < rows ? clamp4(cols - tx * 4) : 0;
-    const float4 x = load4<VEC>(P + (r0 + a) * n + c0 + tx * 4, cnt, 0.0f, P);
-    d[r][0] = x.x; d[r][1] = x.y; d[r][2] = x.z; d[r][3] = x.w;
+  for (int r = 0; r < S; ++r) {
+    const int a = ty * S + r;
+    x[r] = load_seg<VEC, S>(P + (r0 + a) * n + c0 + tx * S, a < rows ? cols - tx * S : 0, 0.0f,
+                            P);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = tx * 4 + q;
-    const int cnt = c < cols ? clamp4(rows - ty * 4) : 0;
-    const float4 y = load4<VEC>(P + (c0 + c) * n + r0 + ty * 4, cnt, 0.0f, P);
-    t[0][q] = y.x; t[1][q] = y.y; t[2][q] = y.z; t[3][q] = y.w;
+  for (int q = 0; q < S; ++q) {
+    const int c = tx * S + q;
+    y[q] = load_seg<VEC, S>(P + (c0 + c) * n + r0 + ty * S, c < cols ? rows - ty * S : 0, 0.0f,
+                            P);
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < S; ++r)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int a = ty * 4 + r, c = tx * 4 + q;
+    for (int q = 0; q < S; ++q) {
+      const int a = ty * S + r, c = tx * S + q;
+      const float d = x[r].v[q], t = y[q].v[r];  // P[r0+a][c0+c], P[c0+c][r0+a]
       const bool in = a < rows && c < cols;
       const bool upper = r0 < c0 || (r0 == c0 && a < c);
       const bool lower = r0 > c0 || (r0 == c0 && a > c);
-      u[r][q] = in ? (lower ? t[r][q] : d[r][q]) : kInf;
-      l[r][q] = in ? (upper ? t[r][q] : d[r][q]) : 0.0f;
+      u[r][q] = in ? (lower ? t : d) : kInf;
+      l[r][q] = in ? (upper ? t : d) : 0.0f;
     }
 }
 
 // The inverse of packed_block_load (the diagonal of a diagonal block is not
 // written: its single slot holds U[i][i]).  On a diagonal block cells (a, c)
 // and (c, a) write the same two slots with equal values.
+template <int S = 4>
 __device__ __forceinline__ void packed_block_store(float *P, int64_t n, int64_t r0, int64_t c0,
                                                    int rows, int cols, int ty, int tx,
-                                                   const float (&u)[4][4],
-                                                   const float (&l)[4][4]) {
+                                                   const float (&u)[S][S],
+                                                   const float (&l)[S][S]) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < S; ++r)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int a = ty * 4 + r, c = tx * 4 + q;
+    for (int q = 0; q < S; ++q) {
+      const int a = ty * S + r, c = tx * S + q;
       if (a >= rows || c >= cols || (r0 == c0 && a == c)) continue;
       const bool upper = r0 < c0 || (r0 == c0 && a < c);
       P[(r0 + a) * n + c0 + c] = upper ? u[r][q] : l[r][q];
@@ -133,8 +174,7 @@ __device__ __forceinline__ void packed_block_store(float *P, int64_t n, int64_t 
 // ---------------------------------------------------------------- phases 1 and 2
 // Phases 1 and 2 of k-block K in one launch.  Workgroup J (one per k-block
 // tile other than K; grid.y = molecules) holds the diagonal tile D = (K, K)
-// and its panel tile R = (K, J) in registers, thread (ty, tx) owning rows
-// 4ty..4ty+3 and columns 4tx..4tx+3 of each, and runs the rounds m of band K
+// and its panel tile R = (K, J) in registers and runs the rounds m of band K
 // in order over both.  Row m of D and of R is published through LDS
 // (double-buffered, one barrier per round); column m of D equals its row m
 // by symmetry:
@@ -146,15 +186,24 @@ __device__ __forceinline__ void packed_block_store(float *P, int64_t n, int64_t 
 // costs less than a launch of its own on the critical path of the pass.
 // Workgroup 0 writes D back.  Cells outside the matrix start neutral and stay
 // neutral (every candidate through them is +inf for U and <= 0 for L).
+//
+// The rounds are latency-bound (a barrier and LDS round trip each), so the
+// workgroup is 1024 threads, four waves per SIMD to cover each other's
+// stalls, and thread (ty, tx) owns a 2x2 cell block of D and of R: rows
+// 2ty, 2ty+1 and columns 2tx, 2tx+1.
+constexpr int kPanelThreads = 1024;
+constexpr int PS = 2;  // cells per side and thread in k_diag_panel
+
 template <bool VEC, bool PK, bool RU>
-__global__ __launch_bounds__(kThreads) void k_diag_panel(float *__restrict__ U,
-                                                         float *__restrict__ L, int64_t n,
-                                                         int64_t batch, int64_t K) {
-  __shared__ float4 dvu[2][BK / 4], dvl[2][BK / 4];  // row m of D
-  __shared__ float4 rvu[2][BK / 4], rvl[2][BK / 4];  // row m of R
+__global__ __launch_bounds__(kPanelThreads) void k_diag_panel(float *__restrict__ U,
+                                                              float *__restrict__ L, int64_t n,
+                                                              int64_t batch, int64_t K) {
+  __shared__ float2 dvu[2][BK / PS], dvl[2][BK / PS];  // row m of D
+  __shared__ float2 rvu[2][BK / PS], rvl[2][BK / PS];  // row m of R
 
   rounding_prologue<RU>();
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  critical_path_priority();
+  const int tid = threadIdx.x, ty = tid / (BK / PS), tx = tid % (BK / PS);
   int64_t J = blockIdx.x;
   if (J >= K) ++J;
   const int64_t k0 = K * BK, j0 = J * BK;
@@ -168,69 +217,67 @@ __global__ __launch_bounds__(kThreads) void k_diag_panel(float *__restrict__ U,
     float *Ub = U + b * nn;
     float *Lb = PK ? Ub : L + b * nn;
 
-    float du[4][4], dl[4][4];  // D[4ty + r][4tx + q]
-    float u[4][4], l[4][4];    // R[4ty + r][4tx + q] = cell (k0 + 4ty + r, j0 + 4tx + q)
+    float du[PS][PS], dl[PS][PS];  // D[2ty + r][2tx + q]
+    float u[PS][PS], l[PS][PS];    // R[2ty + r][2tx + q] = cell (k0 + 2ty + r, j0 + 2tx + q)
     if (PK) {
-      packed_block_load<VEC>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
-      packed_block_load<VEC>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
+      packed_block_load<VEC, PS>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
+      packed_block_load<VEC, PS>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
     } else {
+      // all loads are issued before any value is unpacked
+      Seg<PS> xu[PS], xl[PS], yu[PS], yl[PS];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int a = ty * 4 + r;
-        const int cnt = a < bK ? clamp4(bK - tx * 4) : 0;
-        const int64_t g = (k0 + a) * n + k0 + tx * 4;
-        const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
-        du[r][0] = x.x; du[r][1] = x.y; du[r][2] = x.z; du[r][3] = x.w;
-        dl[r][0] = y.x; dl[r][1] = y.y; dl[r][2] = y.z; dl[r][3] = y.w;
+      for (int r = 0; r < PS; ++r) {
+        const int a = ty * PS + r;
+        const int64_t g = (k0 + a) * n + k0 + tx * PS;
+        const int64_t left = a < bK ? bK - tx * PS : 0;
+        xu[r] = load_seg<VEC, PS>(Ub + g, left, kInf, Ub);
+        xl[r] = load_seg<VEC, PS>(Lb + g, left, 0.0f, Lb);
       }
-      if (rowor) {
-        // R[a][c] = M[k0+a][j0+c]
+      // the panel tile from its fresh orientation: R[a][c] = M[k0+a][j0+c]
+      // (row segments), else M[j0+c][k0+a] (column segments)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int a = ty * 4 + r;
-          const int cnt = a < bK ? clamp4(bJ - tx * 4) : 0;
-          const int64_t g = (k0 + a) * n + j0 + tx * 4;
-          const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
-          u[r][0] = x.x; u[r][1] = x.y; u[r][2] = x.z; u[r][3] = x.w;
-          l[r][0] = y.x; l[r][1] = y.y; l[r][2] = y.z; l[r][3] = y.w;
-        }
-      } else {
-        // R[a][c] = M[j0+c][k0+a]
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = tx * 4 + q;
-          const int cnt = c < bJ ? clamp4(bK - ty * 4) : 0;
-          const int64_t g = (j0 + c) * n + k0 + ty * 4;
-          const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
-          u[0][q] = x.x; u[1][q] = x.y; u[2][q] = x.z; u[3][q] = x.w;
-          l[0][q] = y.x; l[1][q] = y.y; l[2][q] = y.z; l[3][q] = y.w;
-        }
+      for (int r = 0; r < PS; ++r) {
+        const int64_t left = rowor ? (ty * PS + r < bK ? bJ - tx * PS : 0)
+                                   : (tx * PS + r < bJ ? bK - ty * PS : 0);
+        const int64_t g = rowor ? (k0 + ty * PS + r) * n + j0 + tx * PS
+                                : (j0 + tx * PS + r) * n + k0 + ty * PS;
+        yu[r] = load_seg<VEC, PS>(Ub + g, left, kInf, Ub);
+        yl[r] = load_seg<VEC, PS>(Lb + g, left, 0.0f, Lb);
       }
+#pragma unroll
+      for (int r = 0; r < PS; ++r)
+#pragma unroll
+        for (int q = 0; q < PS; ++q) {
+          du[r][q] = xu[r].v[q];
+          dl[r][q] = xl[r].v[q];
+          u[r][q] = rowor ? yu[r].v[q] : yu[q].v[r];
+          l[r][q] = rowor ? yl[r].v[q] : yl[q].v[r];
+        }
     }
 
-    for (int mb = 0; mb < BK / 4; ++mb) {
+    for (int mb = 0; mb < BK / PS; ++mb) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = mb * 4 + r;
+      for (int r = 0; r < PS; ++r) {
+        const int m = mb * PS + r;
         if (m >= bK) break;  // uniform
         const int buf = m & 1;
         if (ty == mb) {
-          dvu[buf][tx] = make_float4(du[r][0], du[r][1], du[r][2], du[r][3]);
-          dvl[buf][tx] = make_float4(dl[r][0], dl[r][1], dl[r][2], dl[r][3]);
-          rvu[buf][tx] = make_float4(u[r][0], u[r][1], u[r][2], u[r][3]);
-          rvl[buf][tx] = make_float4(l[r][0], l[r][1], l[r][2], l[r][3]);
+          dvu[buf][tx] = make_float2(du[r][0], du[r][1]);
+          dvl[buf][tx] = make_float2(dl[r][0], dl[r][1]);
+          rvu[buf][tx] = make_float2(u[r][0], u[r][1]);
+          rvl[buf][tx] = make_float2(l[r][0], l[r][1]);
         }
         __syncthreads();
-        const float4 cu = dvu[buf][ty], cl = dvl[buf][ty];  // D[a][m] = D[m][a]
-        const float4 eu = dvu[buf][tx], el = dvl[buf][tx];  // D[m][b]
-        const float4 ru = rvu[buf][tx], rl = rvl[buf][tx];  // R[m][c]
-        const float cuv[4] = {cu.x, cu.y, cu.z, cu.w}, clv[4] = {cl.x, cl.y, cl.z, cl.w};
-        const float euv[4] = {eu.x, eu.y, eu.z, eu.w}, elv[4] = {el.x, el.y, el.z, el.w};
-        const float ruv[4] = {ru.x, ru.y, ru.z, ru.w}, rlv[4] = {rl.x, rl.y, rl.z, rl.w};
+        const float2 cu = dvu[buf][ty], cl = dvl[buf][ty];  // D[a][m] = D[m][a]
+        const float2 eu = dvu[buf][tx], el = dvl[buf][tx];  // D[m][b]
+        const float2 ru = rvu[buf][tx], rl = rvl[buf][tx];  // R[m][c]
+        const float cuv[2] = {cu.x, cu.y}, clv[2] = {cl.x, cl.y};
+        const float euv[2] = {eu.x, eu.y}, elv[2] = {el.x, el.y};
+        const float ruv[2] = {ru.x, ru.y}, rlv[2] = {rl.x, rl.y};
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < PS; ++a)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < PS; ++q) {
             relax1<RU>(du[a][q], dl[a][q], cuv[a], clv[a], euv[q], elv[q]);
             relax1<RU>(u[a][q], l[a][q], cuv[a], clv[a], ruv[q], rlv[q]);
           }
@@ -238,23 +285,23 @@ __global__ __launch_bounds__(kThreads) void k_diag_panel(float *__restrict__ U,
     }
 
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < PS; ++r)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < PS; ++q) {
         l[r][q] = lower_out<RU>(l[r][q]);
         dl[r][q] = lower_out<RU>(dl[r][q]);
       }
     // R in both orientations (packed: the one slot of U and of L); D, which
     // lies in a fresh tile, as a full square
     if (PK) {
-      packed_block_store(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
-      if (writes_d) packed_block_store(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
+      packed_block_store<PS>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
+      if (writes_d) packed_block_store<PS>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < PS; ++r)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int a = ty * 4 + r, c = tx * 4 + q;
+      for (int q = 0; q < PS; ++q) {
+        const int a = ty * PS + r, c = tx * PS + q;
         if (!PK && a < bK && c < bJ) {
           Ub[(k0 + a) * n + j0 + c] = u[r][q];
           Lb[(k0 + a) * n + j0 + c] = l[r][q];
@@ -545,6 +592,7 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
   __shared__ float4 srl[KC][BK / 4];
 
   rounding_prologue<RU>();
+  critical_path_priority();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   int64_t J = blockIdx.x;
   if (J >= K) ++J;
@@ -760,8 +808,8 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   auto phase12 = [&](int64_t K, hipStream_t st) -> hipError_t {
     if (TB == 1)
       return launch_small_block(U, L, n, nn, 0, (int)n, 0, (int)n, batch, st, prof, flags);
-    return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(kThreads), st, U,
-                  L, n, batch, K);
+    return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(kPanelThreads), st,
+                  U, L, n, batch, K);
   };
   // s1: first atom of the band the bulk launch must leave alone (-1: none)
   auto phase3 = [&](int64_t K, int64_t s1, hipStream_t st) -> hipError_t {
