@@ -13,8 +13,9 @@
 //            the diagonal tile's rows (phases 1 and 2 run together in
 //            k_diag_panel, one workgroup per panel tile);
 //   phase 3  every remaining cell: all bK rounds at once from the finished
-//            panel (k_tiles, plus k_strip for band K+1 when running ahead).
-//            This is where 1 - O(BK/n) of the work is.
+//            panel (k_blocks: the bulk on 64x64 quadrants, and band K+1
+//            alone when running ahead).  This is where 1 - O(BK/n) of the
+//            work is.
 //
 // Symmetric schedule.  U and L stay exactly symmetric, so only the cells of
 // TILE x TILE tiles (I,J) with I <= J are kept current ("fresh"); tiles below
@@ -24,13 +25,9 @@
 // so phase 2 must leave all of row band K fresh: it updates each panel tile
 // from whichever orientation is fresh and writes both orientations.
 //
-// Phase 3 bulk kernel: a 256-thread workgroup owns a 128x128 tile; each thread an
-// 8x8 register tile (rows ty*4+{0..3} and 64+ty*4+{0..3}, same for columns,
-// so the LDS reads of a wave are contiguous).  The panel rows of the k-block
-// are staged through LDS in chunks of KC atoms.  Per atom and cell the VALU
-// does one add and one min for U, two subtracts and two max for L; pairs of
-// atoms fold into 3-input min/max.  No matrix cores: min-plus is not a
-// multiply-add contraction.
+// Phase 3: a 256-thread workgroup owns a 64x64 block, each thread a 4x4
+// register tile; the panel rows of the k-block are staged through LDS.  No
+// matrix cores: min-plus is not a multiply-add contraction.
 #include <mutex>
 
 #include "dbs_internal.h"
@@ -39,9 +36,11 @@ namespace dbs {
 namespace {
 
 constexpr int BK = 64;          // atoms per k-block (phases 1 and 2 tile size)
-constexpr int TILE = 128;       // phase-3 tile size; fresh region is I <= J in these tiles
+constexpr int TILE = 128;       // freshness granularity: tiles I <= J are kept current
 constexpr int RATIO = TILE / BK;
 constexpr int KC = 16;          // atoms per LDS chunk in phase 3
+// phase-3 tiles (times molecules) from which the pass runs two bands ahead
+constexpr int64_t kDeepTiles = 256;
 constexpr int kThreads = 256;
 
 // The side-stream kernels (band K+1 strip, then phases 1-2 of block K+1) are
@@ -187,23 +186,26 @@ __device__ __forceinline__ void packed_block_store(float *P, int64_t n, int64_t 
 // Workgroup 0 writes D back.  Cells outside the matrix start neutral and stay
 // neutral (every candidate through them is +inf for U and <= 0 for L).
 //
-// The rounds are latency-bound (a barrier and LDS round trip each), so the
-// workgroup is 1024 threads, four waves per SIMD to cover each other's
-// stalls, and thread (ty, tx) owns a 2x2 cell block of D and of R: rows
-// 2ty, 2ty+1 and columns 2tx, 2tx+1.
-constexpr int kPanelThreads = 1024;
-constexpr int PS = 2;  // cells per side and thread in k_diag_panel
+// Thread (ty, tx) owns an S x S cell block of D and of R (rows S*ty.., columns
+// S*tx..), so the workgroup has (BK/S)^2 threads.  S = 2 (1024 threads, four
+// waves per SIMD) hides the latency of the rounds best when the kernel has
+// the chip to itself; S = 4 (256 threads, a footprint like a phase-3
+// workgroup) gets compute units while the bulk of phase 3 runs.
+template <int S>
+constexpr int panel_threads() { return (BK / S) * (BK / S); }
 
-template <bool VEC, bool PK, bool RU>
-__global__ __launch_bounds__(kPanelThreads) void k_diag_panel(float *__restrict__ U,
-                                                              float *__restrict__ L, int64_t n,
-                                                              int64_t batch, int64_t K) {
-  __shared__ float2 dvu[2][BK / PS], dvl[2][BK / PS];  // row m of D
-  __shared__ float2 rvu[2][BK / PS], rvl[2][BK / PS];  // row m of R
+template <bool VEC, bool PK, bool RU, int S>
+__global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__restrict__ U,
+                                                                   float *__restrict__ L,
+                                                                   int64_t n, int64_t batch,
+                                                                   int64_t K) {
+  constexpr int NT = BK / S;  // threads per side
+  __shared__ __align__(16) float dvu[2][BK], dvl[2][BK];  // row m of D
+  __shared__ __align__(16) float rvu[2][BK], rvl[2][BK];  // row m of R
 
   rounding_prologue<RU>();
   critical_path_priority();
-  const int tid = threadIdx.x, ty = tid / (BK / PS), tx = tid % (BK / PS);
+  const int tid = threadIdx.x, ty = tid / NT, tx = tid % NT;
   int64_t J = blockIdx.x;
   if (J >= K) ++J;
   const int64_t k0 = K * BK, j0 = J * BK;
@@ -217,37 +219,37 @@ __global__ __launch_bounds__(kPanelThreads) void k_diag_panel(float *__restrict_
     float *Ub = U + b * nn;
     float *Lb = PK ? Ub : L + b * nn;
 
-    float du[PS][PS], dl[PS][PS];  // D[2ty + r][2tx + q]
-    float u[PS][PS], l[PS][PS];    // R[2ty + r][2tx + q] = cell (k0 + 2ty + r, j0 + 2tx + q)
+    float du[S][S], dl[S][S];  // D[S*ty + r][S*tx + q]
+    float u[S][S], l[S][S];    // R[S*ty + r][S*tx + q] = cell (k0 + S*ty + r, j0 + S*tx + q)
     if (PK) {
-      packed_block_load<VEC, PS>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
-      packed_block_load<VEC, PS>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
+      packed_block_load<VEC, S>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
+      packed_block_load<VEC, S>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
     } else {
       // all loads are issued before any value is unpacked
-      Seg<PS> xu[PS], xl[PS], yu[PS], yl[PS];
+      Seg<S> xu[S], xl[S], yu[S], yl[S];
 #pragma unroll
-      for (int r = 0; r < PS; ++r) {
-        const int a = ty * PS + r;
-        const int64_t g = (k0 + a) * n + k0 + tx * PS;
-        const int64_t left = a < bK ? bK - tx * PS : 0;
-        xu[r] = load_seg<VEC, PS>(Ub + g, left, kInf, Ub);
-        xl[r] = load_seg<VEC, PS>(Lb + g, left, 0.0f, Lb);
+      for (int r = 0; r < S; ++r) {
+        const int a = ty * S + r;
+        const int64_t g = (k0 + a) * n + k0 + tx * S;
+        const int64_t left = a < bK ? bK - tx * S : 0;
+        xu[r] = load_seg<VEC, S>(Ub + g, left, kInf, Ub);
+        xl[r] = load_seg<VEC, S>(Lb + g, left, 0.0f, Lb);
       }
       // the panel tile from its fresh orientation: R[a][c] = M[k0+a][j0+c]
       // (row segments), else M[j0+c][k0+a] (column segments)
 #pragma unroll
-      for (int r = 0; r < PS; ++r) {
-        const int64_t left = rowor ? (ty * PS + r < bK ? bJ - tx * PS : 0)
-                                   : (tx * PS + r < bJ ? bK - ty * PS : 0);
-        const int64_t g = rowor ? (k0 + ty * PS + r) * n + j0 + tx * PS
-                                : (j0 + tx * PS + r) * n + k0 + ty * PS;
-        yu[r] = load_seg<VEC, PS>(Ub + g, left, kInf, Ub);
-        yl[r] = load_seg<VEC, PS>(Lb + g, left, 0.0f, Lb);
+      for (int r = 0; r < S; ++r) {
+        const int64_t left = rowor ? (ty * S + r < bK ? bJ - tx * S : 0)
+                                   : (tx * S + r < bJ ? bK - ty * S : 0);
+        const int64_t g = rowor ? (k0 + ty * S + r) * n + j0 + tx * S
+                                : (j0 + tx * S + r) * n + k0 + ty * S;
+        yu[r] = load_seg<VEC, S>(Ub + g, left, kInf, Ub);
+        yl[r] = load_seg<VEC, S>(Lb + g, left, 0.0f, Lb);
       }
 #pragma unroll
-      for (int r = 0; r < PS; ++r)
+      for (int r = 0; r < S; ++r)
 #pragma unroll
-        for (int q = 0; q < PS; ++q) {
+        for (int q = 0; q < S; ++q) {
           du[r][q] = xu[r].v[q];
           dl[r][q] = xl[r].v[q];
           u[r][q] = rowor ? yu[r].v[q] : yu[q].v[r];
@@ -255,53 +257,60 @@ __global__ __launch_bounds__(kPanelThreads) void k_diag_panel(float *__restrict_
         }
     }
 
-    for (int mb = 0; mb < BK / PS; ++mb) {
+    for (int mb = 0; mb < NT; ++mb) {
 #pragma unroll
-      for (int r = 0; r < PS; ++r) {
-        const int m = mb * PS + r;
+      for (int r = 0; r < S; ++r) {
+        const int m = mb * S + r;
         if (m >= bK) break;  // uniform
         const int buf = m & 1;
         if (ty == mb) {
-          dvu[buf][tx] = make_float2(du[r][0], du[r][1]);
-          dvl[buf][tx] = make_float2(dl[r][0], dl[r][1]);
-          rvu[buf][tx] = make_float2(u[r][0], u[r][1]);
-          rvl[buf][tx] = make_float2(l[r][0], l[r][1]);
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            dvu[buf][tx * S + q] = du[r][q];
+            dvl[buf][tx * S + q] = dl[r][q];
+            rvu[buf][tx * S + q] = u[r][q];
+            rvl[buf][tx * S + q] = l[r][q];
+          }
         }
         __syncthreads();
-        const float2 cu = dvu[buf][ty], cl = dvl[buf][ty];  // D[a][m] = D[m][a]
-        const float2 eu = dvu[buf][tx], el = dvl[buf][tx];  // D[m][b]
-        const float2 ru = rvu[buf][tx], rl = rvl[buf][tx];  // R[m][c]
-        const float cuv[2] = {cu.x, cu.y}, clv[2] = {cl.x, cl.y};
-        const float euv[2] = {eu.x, eu.y}, elv[2] = {el.x, el.y};
-        const float ruv[2] = {ru.x, ru.y}, rlv[2] = {rl.x, rl.y};
+        float cu[S], cl[S], eu[S], el[S], ru[S], rl[S];
 #pragma unroll
-        for (int a = 0; a < PS; ++a)
+        for (int q = 0; q < S; ++q) {
+          cu[q] = dvu[buf][ty * S + q];  // D[a][m] = D[m][a]
+          cl[q] = dvl[buf][ty * S + q];
+          eu[q] = dvu[buf][tx * S + q];  // D[m][b]
+          el[q] = dvl[buf][tx * S + q];
+          ru[q] = rvu[buf][tx * S + q];  // R[m][c]
+          rl[q] = rvl[buf][tx * S + q];
+        }
 #pragma unroll
-          for (int q = 0; q < PS; ++q) {
-            relax1<RU>(du[a][q], dl[a][q], cuv[a], clv[a], euv[q], elv[q]);
-            relax1<RU>(u[a][q], l[a][q], cuv[a], clv[a], ruv[q], rlv[q]);
+        for (int a = 0; a < S; ++a)
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            relax1<RU>(du[a][q], dl[a][q], cu[a], cl[a], eu[q], el[q]);
+            relax1<RU>(u[a][q], l[a][q], cu[a], cl[a], ru[q], rl[q]);
           }
       }
     }
 
 #pragma unroll
-    for (int r = 0; r < PS; ++r)
+    for (int r = 0; r < S; ++r)
 #pragma unroll
-      for (int q = 0; q < PS; ++q) {
+      for (int q = 0; q < S; ++q) {
         l[r][q] = lower_out<RU>(l[r][q]);
         dl[r][q] = lower_out<RU>(dl[r][q]);
       }
     // R in both orientations (packed: the one slot of U and of L); D, which
     // lies in a fresh tile, as a full square
     if (PK) {
-      packed_block_store<PS>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
-      if (writes_d) packed_block_store<PS>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
+      packed_block_store<S>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
+      if (writes_d) packed_block_store<S>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
     }
 #pragma unroll
-    for (int r = 0; r < PS; ++r)
+    for (int r = 0; r < S; ++r)
 #pragma unroll
-      for (int q = 0; q < PS; ++q) {
-        const int a = ty * PS + r, c = tx * PS + q;
+      for (int q = 0; q < S; ++q) {
+        const int a = ty * S + r, c = tx * S + q;
         if (!PK && a < bK && c < bJ) {
           Ub[(k0 + a) * n + j0 + c] = u[r][q];
           Lb[(k0 + a) * n + j0 + c] = l[r][q];
@@ -368,298 +377,155 @@ __device__ __forceinline__ void packed_half_store(const HalfLoad &h, bool right,
 
 // ---------------------------------------------------------------- phase 3
 
-// Tiles are numbered column-major over the upper triangle.  The hardware
-// deals consecutive workgroups to the 8 XCDs in turn, so at any moment an
-// XCD works on a few tile columns and on every 8th tile row of them: the
-// panel slices it needs fit its L2.  (Giving each XCD a contiguous run of
-// tiles instead makes it sweep every row slice of the panel, and is slower.)
+// TILE x TILE tiles are numbered column-major over the upper triangle, and
+// each is split into its four BK x BK quadrants (consecutive workgroups).
+// The hardware deals consecutive workgroups to the 8 XCDs in turn, so at any
+// moment an XCD works on a few tile columns and on every 8th tile row of
+// them: the panel slices it needs fit its L2.  (Giving each XCD a contiguous
+// run of tiles instead makes it sweep every row slice of the panel, and is
+// slower.)
 
-// Bulk of phase 3.  grid.x = T(T+1)/2 tiles (I <= J), grid.y = molecules.
-// Cells in band K (final after phase 2) and in band s1 (the next k-block's
-// band, updated ahead by k_strip; s1 < 0 for none) are neither read nor
-// written, and band s1's panel columns are not read: while this kernel runs,
-// another stream may be updating exactly those cells.
+// Phase 3 on BK x BK blocks, thread (ty, tx) owning a 4x4 cell tile;
+// grid.y = molecules.  Two uses:
+//  * bulk (bulk != 0): every fresh cell outside band K and the bands
+//    starting at s1 and s2, as the four BK x BK quadrants of each upper
+//    TILE x TILE tile (grid.x = 4 T(T+1)/2).  Band K is final after phase 2;
+//    bands s1 and s2 (the next two k-blocks' bands; < 0 for none) are
+//    updated ahead on the other stream.  A quadrant in any of them is
+//    skipped whole (quadrants and bands are both BK wide): it is neither
+//    read nor written, and the panel columns of bands s1 and s2 are not
+//    read, since the other stream may be updating exactly those cells while
+//    this launch runs.
+//  * strip (bulk == 0): the row band starting at s1 only, run ahead of the
+//    bulk on the second stream.  grid.x = the k-block tiles J other than K
+//    and the band starting at s2 (< 0 for none); block (s1 / BK, J) is kept
+//    in its fresh orientation.
+// The panel rows of band K are staged through LDS in chunks of KC atoms; the
+// global loads of chunk c+1 are issued before chunk c is computed.  Per atom
+// and cell the VALU does one add and one min for U, two subtracts and two max
+// for L; pairs of atoms fold into 3-input min/max (4.5 instructions per cell
+// and atom).  12 waves per CU (3 workgroups) keep the VALU busy through the
+// LDS and global latencies.
 template <bool VEC, bool PK, bool RU>
-__global__ __launch_bounds__(kThreads, 2) void k_tiles(float *__restrict__ U,
-                                                       float *__restrict__ L, int64_t n,
-                                                       int64_t batch, int64_t K, int64_t s1) {
-  __shared__ float4 scu[KC][TILE / 4];
-  __shared__ float4 scl[KC][TILE / 4];
-  __shared__ float4 sru[KC][TILE / 4];
-  __shared__ float4 srl[KC][TILE / 4];
-
-  rounding_prologue<RU>();
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int64_t p = blockIdx.x;
-  const int64_t J = tri_col(p);
-  const int64_t I = p - J * (J + 1) / 2;
-  const int64_t i0 = I * TILE, j0 = J * TILE;
-  const int64_t k0 = K * BK;
-  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
-  const int64_t e1 = s1 < 0 ? -1 : (s1 + BK < n ? s1 + BK : n);
-  const int64_t nn = n * n;
-  // x is live: in range and outside both bands (band edges are multiples of 4)
-  auto live = [&](int64_t x) { return x < n && (x < k0 || x >= k0 + bK) && (x < s1 || x >= e1); };
-  auto in_s1 = [&](int64_t x) { return x >= s1 && x < e1; };
-
-  // rows of this thread: i0 + rofs(r), r < 8; columns likewise with tx
-  auto rofs = [](int t, int r) { return (r < 4 ? 0 : TILE / 2 - 4) + t * 4 + r; };
-  // liveness of the thread's 8 rows and 8 columns, one bit each
-  unsigned rmask = 0, cmask = 0;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    rmask |= (unsigned)live(i0 + rofs(ty, r)) << r;
-    cmask |= (unsigned)live(j0 + rofs(tx, r)) << r;
-  }
-
-  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
-    float *Ub = U + b * nn;
-    float *Lb = PK ? Ub : L + b * nn;
-
-    // U (and dense L) at (i, j); packed U is P tile (I, J) itself
-    float u[8][8], l[8][8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int64_t i = i0 + rofs(ty, r);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t j = j0 + rofs(tx, h * 4);
-        const bool on = ((rmask >> r) & (cmask >> (h * 4)) & 1u) != 0;
-        const int cnt = on ? (VEC ? 4 : clamp4(n - j)) : 0;
-        const float4 x = load4<VEC>(Ub + i * n + j, cnt, kInf, Ub);
-        u[r][h * 4 + 0] = x.x; u[r][h * 4 + 1] = x.y; u[r][h * 4 + 2] = x.z; u[r][h * 4 + 3] = x.w;
-        if (!PK) {
-          const float4 y = load4<VEC>(Lb + i * n + j, cnt, 0.0f, Lb);
-          l[r][h * 4 + 0] = y.x; l[r][h * 4 + 1] = y.y; l[r][h * 4 + 2] = y.z; l[r][h * 4 + 3] = y.w;
-        }
-      }
-    }
-    if (PK) {
-      // packed L(i,j) = P[j][i] (tile (J, I) read across): for each column j
-      // two float4 along i
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int64_t j = j0 + rofs(tx, c);
-#pragma unroll
-        for (int hr = 0; hr < 2; ++hr) {
-          const int64_t i = i0 + rofs(ty, hr * 4);
-          const bool on = ((cmask >> c) & (rmask >> (hr * 4)) & 1u) != 0;
-          const int cnt = on ? (VEC ? 4 : clamp4(n - i)) : 0;
-          const float4 t = load4<VEC>(Ub + j * n + i, cnt, 0.0f, Ub);
-          l[hr * 4 + 0][c] = t.x; l[hr * 4 + 1][c] = t.y; l[hr * 4 + 2][c] = t.z; l[hr * 4 + 3][c] = t.w;
-        }
-      }
-      if (I == J) {
-        // a diagonal tile: below the diagonal P[i][j] is L(i,j) and P[j][i] is U(i,j)
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const int64_t i = i0 + rofs(ty, r), j = j0 + rofs(tx, c);
-            if (i > j) {
-              const float t = u[r][c];
-              u[r][c] = l[r][c];
-              l[r][c] = t;
-            } else if (i == j) {
-              l[r][c] = u[r][c];
-            }
-          }
-      }
-    }
-
-    for (int kc = 0; kc < bK; kc += KC) {
-      // stage panel rows k0+kc .. k0+kc+KC-1, columns of I and of J: every
-      // global load of the chunk is issued before the first LDS store
-      if (PK) {
-        // addresses recomputed per chunk (not hoisted out of the k loop)
-        int tl = tid;
-        asm volatile("" : "+v"(tl));
-        HalfLoad hl[4];
-        bool right[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t xh = (q < 2 ? i0 : j0) + (q & 1) * (TILE / 2);
-          right[q] = xh > k0;
-          const bool dead = xh == k0 || xh == s1 || xh >= n;
-          hl[q] = packed_half_load<VEC>(Ub, n, k0, kc, bK, xh, right[q], dead, tl);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          packed_half_store(hl[q], right[q],
-                            reinterpret_cast<float *>(q < 2 ? &scu[0][0] : &sru[0][0]),
-                            reinterpret_cast<float *>(q < 2 ? &scl[0][0] : &srl[0][0]), TILE,
-                            (q & 1) * (TILE / 2), tl);
-      } else {
-      constexpr int kIter = KC * (TILE / 4) / kThreads;
-      float4 st[kIter][4];
-#pragma unroll
-      for (int it = 0; it < kIter; ++it) {
-        const int e = tid + it * kThreads;
-        const int kk = e / (TILE / 4), x4 = e % (TILE / 4);
-        const int64_t k = k0 + kc + kk;
-        const bool kin = kc + kk < bK;
-        const int64_t ci = i0 + x4 * 4, cj = j0 + x4 * 4;
-        const int ni = (kin && !in_s1(ci)) ? clamp4(n - ci) : 0;
-        const int nj = (kin && !in_s1(cj)) ? clamp4(n - cj) : 0;
-        st[it][0] = load4<VEC>(Ub + k * n + ci, ni, kInf, Ub);
-        st[it][1] = load4<VEC>(Lb + k * n + ci, ni, 0.0f, Lb);
-        st[it][2] = load4<VEC>(Ub + k * n + cj, nj, kInf, Ub);
-        st[it][3] = load4<VEC>(Lb + k * n + cj, nj, 0.0f, Lb);
-      }
-#pragma unroll
-      for (int it = 0; it < kIter; ++it) {
-        const int e = tid + it * kThreads;
-        const int kk = e / (TILE / 4), x4 = e % (TILE / 4);
-        scu[kk][x4] = st[it][0];
-        scl[kk][x4] = st[it][1];
-        sru[kk][x4] = st[it][2];
-        srl[kk][x4] = st[it][3];
-      }
-      }
-      __syncthreads();
-
-#pragma unroll 2
-      for (int kk = 0; kk < KC; kk += 2) {
-        float cu0[8], cl0[8], ru0[8], rl0[8], cu1[8], cl1[8], ru1[8], rl1[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int xi = h * (TILE / 8) + ty, xj = h * (TILE / 8) + tx;
-          const float4 a0 = scu[kk][xi], b0 = scl[kk][xi], c0 = sru[kk][xj], d0 = srl[kk][xj];
-          const float4 a1 = scu[kk + 1][xi], b1 = scl[kk + 1][xi], c1 = sru[kk + 1][xj], d1 = srl[kk + 1][xj];
-          cu0[h * 4 + 0] = a0.x; cu0[h * 4 + 1] = a0.y; cu0[h * 4 + 2] = a0.z; cu0[h * 4 + 3] = a0.w;
-          cl0[h * 4 + 0] = b0.x; cl0[h * 4 + 1] = b0.y; cl0[h * 4 + 2] = b0.z; cl0[h * 4 + 3] = b0.w;
-          ru0[h * 4 + 0] = c0.x; ru0[h * 4 + 1] = c0.y; ru0[h * 4 + 2] = c0.z; ru0[h * 4 + 3] = c0.w;
-          rl0[h * 4 + 0] = d0.x; rl0[h * 4 + 1] = d0.y; rl0[h * 4 + 2] = d0.z; rl0[h * 4 + 3] = d0.w;
-          cu1[h * 4 + 0] = a1.x; cu1[h * 4 + 1] = a1.y; cu1[h * 4 + 2] = a1.z; cu1[h * 4 + 3] = a1.w;
-          cl1[h * 4 + 0] = b1.x; cl1[h * 4 + 1] = b1.y; cl1[h * 4 + 2] = b1.z; cl1[h * 4 + 3] = b1.w;
-          ru1[h * 4 + 0] = c1.x; ru1[h * 4 + 1] = c1.y; ru1[h * 4 + 2] = c1.z; ru1[h * 4 + 3] = c1.w;
-          rl1[h * 4 + 0] = d1.x; rl1[h * 4 + 1] = d1.y; rl1[h * 4 + 2] = d1.z; rl1[h * 4 + 3] = d1.w;
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c)
-            relax2<RU>(u[r][c], l[r][c], cu0[r], cl0[r], ru0[c], rl0[c], cu1[r], cl1[r], ru1[c],
-                   rl1[c]);
-      }
-      __syncthreads();
-    }
-
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) l[r][c] = lower_out<RU>(l[r][c]);
-    // the store addresses are recomputed here rather than kept live across
-    // the k loop from the loads
-    int ts = tid;
-    asm volatile("" : "+v"(ts));
-    const int sy = ts >> 4, sx = ts & 15;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if (!((rmask >> r) & 1u)) continue;
-      const int64_t i = i0 + rofs(sy, r);
-      float *pu = Ub + i * n + j0;
-      float *pl = Lb + i * n + j0;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        if (!((cmask >> c) & 1u)) continue;
-        const int64_t j = j0 + rofs(sx, c);
-        if (!PK) {
-          pu[rofs(sx, c)] = u[r][c];
-          pl[rofs(sx, c)] = l[r][c];
-        } else if (I != J) {
-          Ub[i * n + j] = u[r][c];
-          Ub[j * n + i] = l[r][c];
-        } else if (i != j) {
-          Ub[i * n + j] = i < j ? u[r][c] : l[r][c];
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// Phase 3 on band K+1 only, run ahead of the bulk: the cells (i, j) with i in
-// band K+1 and j outside band K, each kept in its fresh orientation.
-// grid.x = k-block tiles J other than K (one BK x BK tile each),
-// grid.y = molecules.  Thread (ty, tx) owns a 4x4 cell tile.
-template <bool VEC, bool PK, bool RU>
-__global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float *__restrict__ L,
-                                                    int64_t n, int64_t batch, int64_t K) {
+__global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, float *__restrict__ L,
+                                                     int64_t n, int64_t batch, int64_t K,
+                                                     int64_t s1, int64_t s2, int bulk) {
   __shared__ float4 scu[KC][BK / 4];
   __shared__ float4 scl[KC][BK / 4];
   __shared__ float4 sru[KC][BK / 4];
   __shared__ float4 srl[KC][BK / 4];
 
   rounding_prologue<RU>();
-  critical_path_priority();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  int64_t J = blockIdx.x;
-  if (J >= K) ++J;
-  const int64_t k0 = K * BK, s1 = (K + 1) * BK, j0 = J * BK;
+  int64_t A, B;  // row band, column band of the block
+  bool rowor;    // stored as (A, B) (else as its transpose (B, A))
+  if (!bulk) {
+    // row band s1 / BK; every column band but K and s2 / BK (s2 < 0: none)
+    critical_path_priority();
+    A = s1 / BK;
+    const int64_t x = s2 < 0 ? -1 : s2 / BK;
+    const int64_t lo = x < 0 ? K : (x < K ? x : K), hi = x < 0 ? -1 : (x < K ? K : x);
+    B = blockIdx.x;
+    if (B >= lo) ++B;
+    if (hi >= 0 && B >= hi) ++B;
+    rowor = fresh(A, B);
+  } else {
+    const int64_t p = blockIdx.x >> 2, q = blockIdx.x & 3;
+    const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
+    A = RATIO * I2 + (q >> 1);
+    B = RATIO * J2 + (q & 1);
+    rowor = true;  // every quadrant of an upper tile is fresh
+    if (A * BK >= n || B * BK >= n || A == K || B == K || A * BK == s1 || B * BK == s1 ||
+        A * BK == s2 || B * BK == s2)
+      return;  // uniform over the workgroup, before any barrier
+    // packed: the lower-left quadrant of a diagonal tile holds the same
+    // slots as its upper-right one (transposed cells), which covers them
+    if (PK && I2 == J2 && q == 2) return;
+  }
+  const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
   const int bK = (int)(n - k0 < BK ? n - k0 : BK);
-  const int b1 = (int)(n - s1 < BK ? n - s1 : BK);
+  const int bA = (int)(n - a0 < BK ? n - a0 : BK);
   const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
-  const bool rowor = fresh(K + 1, J);
   const int64_t nn = n * n;
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
     float *Ub = U + b * nn;
     float *Lb = PK ? Ub : L + b * nn;
 
-    // logical cell (a, c) = (s1 + a, j0 + c); stored at (s1+a, j0+c) or (j0+c, s1+a)
+    // logical cell (a, c) = (a0 + a, j0 + c); stored at (a0+a, j0+c) or (j0+c, a0+a)
     float u[4][4], l[4][4];
     if (PK) {
-      packed_block_load<VEC>(Ub, n, s1, j0, b1, bJ, ty, tx, u, l);
-    } else if (rowor) {
+      packed_block_load<VEC>(Ub, n, a0, j0, bA, bJ, ty, tx, u, l);
+    } else {
+      float4 x[4], y[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int a = ty * 4 + r;
-        const int cnt = a < b1 ? clamp4(bJ - tx * 4) : 0;
-        const int64_t g = (s1 + a) * n + j0 + tx * 4;
-        const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
-        u[r][0] = x.x; u[r][1] = x.y; u[r][2] = x.z; u[r][3] = x.w;
-        l[r][0] = y.x; l[r][1] = y.y; l[r][2] = y.z; l[r][3] = y.w;
+        const int cnt = rowor ? (ty * 4 + r < bA ? clamp4(bJ - tx * 4) : 0)
+                              : (tx * 4 + r < bJ ? clamp4(bA - ty * 4) : 0);
+        const int64_t g = rowor ? (a0 + ty * 4 + r) * n + j0 + tx * 4
+                                : (j0 + tx * 4 + r) * n + a0 + ty * 4;
+        x[r] = load4<VEC>(Ub + g, cnt, kInf, Ub);
+        y[r] = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
       }
-    } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = tx * 4 + q;
-        const int cnt = c < bJ ? clamp4(b1 - ty * 4) : 0;
-        const int64_t g = (j0 + c) * n + s1 + ty * 4;
-        const float4 x = load4<VEC>(Ub + g, cnt, kInf, Ub), y = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
-        u[0][q] = x.x; u[1][q] = x.y; u[2][q] = x.z; u[3][q] = x.w;
-        l[0][q] = y.x; l[1][q] = y.y; l[2][q] = y.z; l[3][q] = y.w;
+      for (int r = 0; r < 4; ++r) {
+        const float xr[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
+        const float yr[4] = {y[r].x, y[r].y, y[r].z, y[r].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          (rowor ? u[r][q] : u[q][r]) = xr[q];
+          (rowor ? l[r][q] : l[q][r]) = yr[q];
+        }
       }
     }
 
-    for (int kc = 0; kc < bK; kc += KC) {
+    // staged operands of one chunk: panel rows k0+kc.., columns of band A
+    // (U/L[i,k] = U/L[k,i]) and of band B
+    auto fetch = [&](int kc, float4 (&st)[4], HalfLoad (&hl)[2]) {
       if (PK) {
-        // band K+1 lies right of band K; band J right or left of it
-        const HalfLoad hc = packed_half_load<VEC>(Ub, n, k0, kc, bK, s1, true, false, tid);
-        const HalfLoad hr = packed_half_load<VEC>(Ub, n, k0, kc, bK, j0, J > K, false, tid);
-        packed_half_store(hc, true, reinterpret_cast<float *>(&scu[0][0]),
-                          reinterpret_cast<float *>(&scl[0][0]), BK, 0, tid);
-        packed_half_store(hr, J > K, reinterpret_cast<float *>(&sru[0][0]),
-                          reinterpret_cast<float *>(&srl[0][0]), BK, 0, tid);
+        // band A and band B each lie right or left of band K
+        hl[0] = packed_half_load<VEC>(Ub, n, k0, kc, bK, a0, A > K, false, tid);
+        hl[1] = packed_half_load<VEC>(Ub, n, k0, kc, bK, j0, B > K, false, tid);
       } else {
         // KC x BK/4 float4 per array: one of each per thread
         const int kk = tid / (BK / 4), x4 = tid % (BK / 4);
         const int64_t k = k0 + kc + kk;
         const bool kin = kc + kk < bK;
-        const int ni = kin ? clamp4(b1 - x4 * 4) : 0;
+        const int ni = kin ? clamp4(bA - x4 * 4) : 0;
         const int nj = kin ? clamp4(bJ - x4 * 4) : 0;
-        scu[kk][x4] = load4<VEC>(Ub + k * n + s1 + x4 * 4, ni, kInf, Ub);
-        scl[kk][x4] = load4<VEC>(Lb + k * n + s1 + x4 * 4, ni, 0.0f, Lb);
-        sru[kk][x4] = load4<VEC>(Ub + k * n + j0 + x4 * 4, nj, kInf, Ub);
-        srl[kk][x4] = load4<VEC>(Lb + k * n + j0 + x4 * 4, nj, 0.0f, Lb);
+        st[0] = load4<VEC>(Ub + k * n + a0 + x4 * 4, ni, kInf, Ub);
+        st[1] = load4<VEC>(Lb + k * n + a0 + x4 * 4, ni, 0.0f, Lb);
+        st[2] = load4<VEC>(Ub + k * n + j0 + x4 * 4, nj, kInf, Ub);
+        st[3] = load4<VEC>(Lb + k * n + j0 + x4 * 4, nj, 0.0f, Lb);
       }
+    };
+    auto stage = [&](const float4 (&st)[4], const HalfLoad (&hl)[2]) {
+      if (PK) {
+        packed_half_store(hl[0], A > K, reinterpret_cast<float *>(&scu[0][0]),
+                          reinterpret_cast<float *>(&scl[0][0]), BK, 0, tid);
+        packed_half_store(hl[1], B > K, reinterpret_cast<float *>(&sru[0][0]),
+                          reinterpret_cast<float *>(&srl[0][0]), BK, 0, tid);
+      } else {
+        const int kk = tid / (BK / 4), x4 = tid % (BK / 4);
+        scu[kk][x4] = st[0];
+        scl[kk][x4] = st[1];
+        sru[kk][x4] = st[2];
+        srl[kk][x4] = st[3];
+      }
+    };
+
+    float4 st[4];
+    HalfLoad hl[2];
+    fetch(0, st, hl);
+    for (int kc = 0; kc < bK; kc += KC) {
+      stage(st, hl);
       __syncthreads();
+      if (kc + KC < bK) fetch(kc + KC, st, hl);  // in flight during this chunk
 #pragma unroll 2
       for (int kk = 0; kk < KC; kk += 2) {
-        const float4 a0 = scu[kk][ty], b0 = scl[kk][ty], c0 = sru[kk][tx], d0 = srl[kk][tx];
+        const float4 a0v = scu[kk][ty], b0 = scl[kk][ty], c0 = sru[kk][tx], d0 = srl[kk][tx];
         const float4 a1 = scu[kk + 1][ty], b1v = scl[kk + 1][ty], c1 = sru[kk + 1][tx], d1 = srl[kk + 1][tx];
-        const float cu0[4] = {a0.x, a0.y, a0.z, a0.w}, cl0[4] = {b0.x, b0.y, b0.z, b0.w};
+        const float cu0[4] = {a0v.x, a0v.y, a0v.z, a0v.w}, cl0[4] = {b0.x, b0.y, b0.z, b0.w};
         const float ru0[4] = {c0.x, c0.y, c0.z, c0.w}, rl0[4] = {d0.x, d0.y, d0.z, d0.w};
         const float cu1[4] = {a1.x, a1.y, a1.z, a1.w}, cl1[4] = {b1v.x, b1v.y, b1v.z, b1v.w};
         const float ru1[4] = {c1.x, c1.y, c1.z, c1.w}, rl1[4] = {d1.x, d1.y, d1.z, d1.w};
@@ -677,14 +543,14 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int q = 0; q < 4; ++q) l[r][q] = lower_out<RU>(l[r][q]);
-    if (PK) packed_block_store(Ub, n, s1, j0, b1, bJ, ty, tx, u, l);
+    if (PK) packed_block_store(Ub, n, a0, j0, bA, bJ, ty, tx, u, l);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int a = ty * 4 + r, c = tx * 4 + q;
-        if (!PK && a < b1 && c < bJ) {
-          const int64_t g = rowor ? (s1 + a) * n + j0 + c : (j0 + c) * n + s1 + a;
+        if (!PK && a < bA && c < bJ) {
+          const int64_t g = rowor ? (a0 + a) * n + j0 + c : (j0 + c) * n + a0 + a;
           Ub[g] = u[r][q];
           Lb[g] = l[r][q];
         }
@@ -749,13 +615,18 @@ hipStream_t side_stream() {
 // created on first use and re-recorded by every pass (a stream wait captures
 // the event's state when it is enqueued, so re-recording is safe).
 struct Events {
-  hipEvent_t e[3] = {nullptr, nullptr, nullptr};  // e[0] unused
-  bool ready = false;
+  // start: phases 1-2 of the first block; bulk[K & 1]: bulk(K) done;
+  // ready[K & 1]: the side stream's work that bulk(K) needs is done
+  hipEvent_t e[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  hipEvent_t &start() { return e[0]; }
+  hipEvent_t &bulk(int64_t K) { return e[1 + (K & 1)]; }
+  hipEvent_t &ready(int64_t K) { return e[3 + (K & 1)]; }
+  bool created = false;
   bool init() {
-    if (ready) return true;
+    if (created) return true;
     for (auto &x : e)
       if (!x && hipEventCreateWithFlags(&x, hipEventDisableTiming) != hipSuccess) return false;
-    ready = true;
+    created = true;
     return true;
   }
   ~Events() {
@@ -773,14 +644,19 @@ Events *thread_events() {
 
 }  // namespace
 
-// Enqueue one pass.  With more than one k-block the pass runs ahead: phase 3
-// of block K is split into band K+1 (k_strip) and everything else (k_tiles).
-// The side stream runs strip(K), then phases 1 and 2 of block K+1, while the
-// caller's stream runs tiles(K); so the short, latency-bound phases hide
-// under the long one.  Everything on the side stream reads and writes only
-// band K+1 cells and band K's panel rows, which tiles(K) neither writes nor
-// (for band K+1) reads.  Events order strip(K) after tiles(K-1), and
-// tiles(K+1) after phase 2 of K+1.
+// Enqueue one pass.  With more than one k-block the pass runs ahead on a
+// second stream, by two bands when there are many phase-3 tiles.  Per k-block
+// K the caller's stream runs bulk(K): phase 3 of block K on everything but
+// band K and the bands run ahead.  Two bands ahead, the side stream runs
+// phase 3 of block K on band K+1 (strip), phases 1-2 of block K+1, then
+// (once bulk(K-1) is done) phase 3 of block K on band K+2; bulk(K+1) waits
+// only for the side stream's work before that, so phases 1-2 of block K+1
+// have all of bulk(K) to finish in.  One band ahead, the side stream waits
+// for bulk(K-1), then runs the band K+1 strip and phases 1-2 of block K+1
+// while bulk(K) runs.  The side work a bulk launch may overlap touches only
+// bands it leaves alone and reads only panel rows it does not write; the
+// CPU model of this schedule in the tests checks that cell by cell, for both
+// depths.
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
                           hipStream_t s, Prof *prof, unsigned flags) {
   static_assert(BK == kBlockRounds, "k-block size");
@@ -798,47 +674,73 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
                 : (vec ? K<true, true, false> : K<false, true, false>))               \
           : (ru ? (vec ? K<true, false, true> : K<false, false, true>)                \
                 : (vec ? K<true, false, false> : K<false, false, false>)))
-  auto panel = DBS_PICK(k_diag_panel);
-  auto tiles = DBS_PICK(k_tiles);
-  auto strip = DBS_PICK(k_strip);
+  auto blocks = DBS_PICK(k_blocks);
 #undef DBS_PICK
+  // With many phase-3 tiles the bulk runs long enough to hide phases 1-2 of
+  // the next blocks: they run two bands ahead, on 256-thread workgroups that
+  // fit where phase-3 workgroups finish.  With few tiles they are the
+  // critical path: one band ahead, on 1024-thread workgroups that hide the
+  // latency of their rounds best.
+  const int64_t pairs = T * (T + 1) / 2;
+  const bool deep = pairs * batch >= kDeepTiles;
+#define DBS_PICK_PANEL(S)                                                                   \
+  (packed ? (ru ? (vec ? k_diag_panel<true, true, true, S> : k_diag_panel<false, true, true, S>)   \
+                : (vec ? k_diag_panel<true, true, false, S> : k_diag_panel<false, true, false, S>)) \
+          : (ru ? (vec ? k_diag_panel<true, false, true, S> : k_diag_panel<false, false, true, S>)  \
+                : (vec ? k_diag_panel<true, false, false, S> : k_diag_panel<false, false, false, S>)))
+  auto panel = deep ? DBS_PICK_PANEL(4) : DBS_PICK_PANEL(2);
+  const unsigned panel_block = deep ? panel_threads<4>() : panel_threads<2>();
+#undef DBS_PICK_PANEL
 
   // phases 1 and 2 of block K: one launch (the diagonal tile alone when it is
   // the only block)
   auto phase12 = [&](int64_t K, hipStream_t st) -> hipError_t {
     if (TB == 1)
       return launch_small_block(U, L, n, nn, 0, (int)n, 0, (int)n, batch, st, prof, flags);
-    return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(kPanelThreads), st,
-                  U, L, n, batch, K);
+    return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(panel_block), st, U,
+                  L, n, batch, K);
   };
-  // s1: first atom of the band the bulk launch must leave alone (-1: none)
-  auto phase3 = [&](int64_t K, int64_t s1, hipStream_t st) -> hipError_t {
-    return launch(prof, kProfTiles, tiles, dim3((unsigned)(T * (T + 1) / 2), gy), dim3(kThreads),
-                  st, U, L, n, batch, K, s1);
+  // s1, s2: first atoms of the bands the bulk launch must leave alone (-1: none)
+  auto phase3 = [&](int64_t K, int64_t s1, int64_t s2, hipStream_t st) -> hipError_t {
+    return launch(prof, kProfTiles, blocks, dim3((unsigned)(4 * pairs), gy), dim3(kThreads), st,
+                  U, L, n, batch, K, s1, s2, 1);
   };
 
   hipError_t e = phase12(K0, s);
   if (e != hipSuccess || TB == 1) return e;
 
+  // phase 3 of block K on row band A, every column band but K and `skip`
+  auto strip = [&](int64_t K, int64_t A, int64_t skip, hipStream_t st) -> hipError_t {
+    return launch(prof, kProfStrip, blocks, dim3((unsigned)(TB - 1 - (skip >= 0)), gy),
+                  dim3(kThreads), st, U, L, n, batch, K, A * BK, skip < 0 ? -1 : skip * BK, 0);
+  };
   hipStream_t side = T > 1 ? side_stream() : nullptr;
   Events *ev = side ? thread_events() : nullptr;
-  const bool ahead = side != nullptr && ev != nullptr;
-  for (int64_t K = K0; K < K1 && e == hipSuccess; ++K) {
-    if (K + 1 == K1) {
-      e = phase3(K, -1, s);
-    } else if (!ahead) {
-      e = phase3(K, -1, s);
-      if (e == hipSuccess) e = phase12(K + 1, s);
-    } else {
-      if ((e = hipEventRecord(ev->e[1], s)) != hipSuccess) break;
-      if ((e = hipStreamWaitEvent(side, ev->e[1], 0)) != hipSuccess) break;
-      if ((e = launch(prof, kProfStrip, strip, dim3((unsigned)(TB - 1), gy), dim3(kThreads), side,
-                      U, L, n, batch, K)) != hipSuccess)
-        break;
-      if ((e = phase12(K + 1, side)) != hipSuccess) break;
-      if ((e = hipEventRecord(ev->e[2], side)) != hipSuccess) break;
-      if ((e = phase3(K, (K + 1) * BK, s)) != hipSuccess) break;
-      e = hipStreamWaitEvent(s, ev->e[2], 0);
+  if (side == nullptr || ev == nullptr) {
+    for (int64_t K = K0; K < K1 && e == hipSuccess; ++K) {
+      e = phase3(K, -1, -1, s);
+      if (e == hipSuccess && K + 1 < K1) e = phase12(K + 1, s);
+    }
+  } else {
+    if ((e = hipEventRecord(ev->start(), s)) == hipSuccess)
+      e = hipStreamWaitEvent(side, ev->start(), 0);
+    for (int64_t K = K0; K < K1 && e == hipSuccess; ++K) {
+      const bool n1 = K + 1 < K1, n2 = deep && K + 2 < K1;
+      if (K > K0 && (e = hipStreamWaitEvent(s, ev->ready(K), 0)) != hipSuccess) break;
+      if ((e = phase3(K, n1 ? (K + 1) * BK : -1, n2 ? (K + 2) * BK : -1, s)) != hipSuccess) break;
+      if ((e = hipEventRecord(ev->bulk(K), s)) != hipSuccess) break;
+      if (n1) {
+        // one band ahead, band K+1 after block K-1 comes from bulk(K-1)
+        if (!deep && K > K0 && (e = hipStreamWaitEvent(side, ev->bulk(K - 1), 0)) != hipSuccess)
+          break;
+        if ((e = strip(K, K + 1, -1, side)) != hipSuccess) break;
+        if ((e = phase12(K + 1, side)) != hipSuccess) break;
+      }
+      if (n2) {
+        if (K > K0 && (e = hipStreamWaitEvent(side, ev->bulk(K - 1), 0)) != hipSuccess) break;
+        if ((e = strip(K, K + 2, K + 1, side)) != hipSuccess) break;
+      }
+      if (n1 && (e = hipEventRecord(ev->ready(K + 1), side)) != hipSuccess) break;
     }
   }
   // packed storage keeps one slot per value: nothing goes stale

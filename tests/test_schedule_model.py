@@ -7,7 +7,9 @@ The GPU pass (csrc/blocked.hip) runs, per k-block K of BK = 64 atoms,
            TILE x TILE region) and written in both orientations;
   phase 3  band K+1 first (the strip, on a second stream, followed there by
            phases 1-2 of K+1), and every other live cell of the upper
-           TILE x TILE tiles (the bulk, on the caller's stream);
+           TILE x TILE tiles (the bulk, on the caller's stream, as BK x BK
+           quadrants: a quadrant in band K or K+1 is skipped whole, which
+           leaves exactly the live cells modelled here);
 and mirrors the upper tiles into the lower ones at the end.
 
 This model re-implements that data flow in plain Python on exact int64 units
@@ -35,7 +37,9 @@ def fresh(a, b):
 
 
 class Model:
-    def __init__(self, U0, L0):
+    def __init__(self, U0, L0, depth=2, skip_second=True):
+        self.depth = depth                # bands run ahead on the side stream
+        self.skip_second = skip_second    # False plants an overlap (self-test)
         self.n = U0.shape[0]
         self.U = pins.units(U0).copy()
         self.L = pins.units(L0).copy()
@@ -89,17 +93,19 @@ class Model:
             writes |= {(a, c), (c, a)}
         return reads, writes
 
-    def strip(self, K):
+    def strip(self, K, A, skip):
+        """Phase 3 of block K on row band A only: blocks (A, J) for every
+        column band J other than K and `skip`, each in its fresh orientation."""
         reads, writes = set(), set()
-        kb, s1 = self.band(K), self.band(K + 1)
+        kb, ab = self.band(K), self.band(A)
         for J in range(self.TB):
-            if J == K:
+            if J == K or J == skip:
                 continue
             jb = self.band(J)
-            reads |= {(k, x) for k in kb for x in s1 + jb}
-            for a in s1:
+            reads |= {(k, x) for k in kb for x in ab + jb}
+            for a in ab:
                 for c in jb:
-                    dst = (a, c) if fresh(K + 1, J) else (c, a)
+                    dst = (a, c) if fresh(A, J) else (c, a)
                     u, l = self.U[dst], self.L[dst]
                     reads.add(dst)
                     for k in kb:
@@ -109,22 +115,23 @@ class Model:
                     writes.add(dst)
         return reads, writes
 
-    def tiles(self, K, ahead):
+    def bulk(self, K, skip_bands):
+        """Phase 3 of block K on the BK x BK quadrants of the upper TILE x TILE
+        tiles, a quadrant in band K or in a skipped band left whole."""
         n = self.n
         reads, writes = set(), set()
-        dead = set(self.band(K)) | (set(self.band(K + 1)) if ahead else set())
-        s1 = set(self.band(K + 1)) if ahead else set()
+        dead = set(self.band(K))
+        for b in skip_bands:
+            dead |= set(self.band(b))
         kb = self.band(K)
         new = {}
         for J in range(self.T):
             for I in range(J + 1):
-                rows = range(I * TILE, min(n, I * TILE + TILE))
-                cols = range(J * TILE, min(n, J * TILE + TILE))
-                reads |= {(k, x) for k in kb for x in list(rows) + list(cols) if x not in s1}
+                rows = [i for i in range(I * TILE, min(n, I * TILE + TILE)) if i not in dead]
+                cols = [j for j in range(J * TILE, min(n, J * TILE + TILE)) if j not in dead]
+                reads |= {(k, x) for k in kb for x in rows + cols}
                 for i in rows:
                     for j in cols:
-                        if i in dead or j in dead:
-                            continue
                         u, l = self.U[i, j], self.L[i, j]
                         reads.add((i, j))
                         for k in kb:
@@ -137,22 +144,51 @@ class Model:
         return reads, writes
 
     def run(self):
+        """The pass as the two streams issue it.  Two bands ahead:
+          main  per K: [wait ready(K)] bulk(K) skipping bands K, K+1, K+2
+          side  per K: strip(K, band K+1), phases 1-2 of K+1,
+                       [wait bulk(K-1)] strip(K, band K+2 without band K+1),
+                       record ready(K+1)
+        One band ahead:
+          main  per K: [wait ready(K)] bulk(K) skipping bands K, K+1
+          side  per K: [wait bulk(K-1)] strip(K, band K+1), phases 1-2 of K+1,
+                       record ready(K+1)
+        Side work that bulk(K) may overlap is everything after ready(K) and
+        before the side's wait for bulk(K); each such footprint must be
+        disjoint from bulk(K)'s."""
+        TB, deep = self.TB, self.depth == 2
         self.phase12(0)
-        for K in range(self.TB):
-            if K + 1 == self.TB:
-                self.tiles(K, ahead=False)
-                continue
-            sr, sw = self.strip(K)
-            r2, w2 = self.phase12(K + 1)
-            side_r, side_w = sr | r2, sw | w2
-            tr, tw = self.tiles(K, ahead=True)
-            assert not (side_w & (tr | tw)), f"k-block {K}: side stream writes what the bulk touches"
-            assert not (tw & side_r), f"k-block {K}: bulk writes what the side stream reads"
-            # packed storage: logical cell (i,j) lives in P[min][max] (U) and
-            # P[max][min] (L), so a footprint becomes its symmetric closure
-            sym = lambda cells: cells | {(j, i) for (i, j) in cells}
-            assert not (sym(side_w) & sym(tr | tw)), f"k-block {K}: packed overlap (writes)"
-            assert not (sym(tw) & sym(side_r)), f"k-block {K}: packed overlap (reads)"
+        side = []          # (iteration, kind, reads, writes) in side-stream order
+        bulks = {}
+        ready_at = {}      # K -> index into `side` after which ready(K) is recorded
+        wait_at = {}       # K -> index into `side` at which the side waits for bulk(K)
+        for K in range(TB):
+            # the model executes in an order consistent with both streams: the
+            # side work of iteration K (it only reads state bulk(K) leaves alone)
+            if K + 1 < TB:
+                if not deep:
+                    wait_at[K - 1] = len(side)
+                side.append((K, "strip1", *self.strip(K, K + 1, None)))
+                side.append((K, "phase12", *self.phase12(K + 1)))
+            if deep and K + 2 < TB:
+                wait_at[K - 1] = len(side)
+                side.append((K, "strip2", *self.strip(K, K + 2, K + 1)))
+            if K + 1 < TB:
+                ready_at[K + 1] = len(side)
+            ahead = (K + 1, K + 2) if deep and self.skip_second else (K + 1,)
+            bulks[K] = self.bulk(K, [b for b in ahead if b < TB])
+        sym = lambda cells: cells | {(j, i) for (i, j) in cells}
+        for K, (br, bw) in bulks.items():
+            lo = ready_at.get(K, 0)
+            hi = wait_at.get(K, len(side))
+            for it, kind, sr, sw in side[lo:hi]:
+                tag = f"bulk({K}) vs {kind}({it})"
+                assert not (sw & (br | bw)), tag + ": side writes what the bulk touches"
+                assert not (bw & sr), tag + ": bulk writes what the side reads"
+                # packed storage: a logical cell (i,j) lives in P[min][max] (U)
+                # and P[max][min] (L), so a footprint becomes its symmetric closure
+                assert not (sym(sw) & sym(br | bw)), tag + ": packed overlap (writes)"
+                assert not (sym(bw) & sym(sr)), tag + ": packed overlap (reads)"
         n = self.n
         for i in range(n):
             for j in range(n):
@@ -161,10 +197,19 @@ class Model:
         return self.U, self.L
 
 
-@pytest.mark.parametrize("n", [65, 130, 200, 257])
-def test_schedule_model_matches_oracle_and_streams_are_disjoint(n):
+@pytest.mark.parametrize("n,depth", [(65, 2), (130, 2), (200, 2), (257, 2), (330, 2),
+                                     (130, 1), (257, 1)])
+def test_schedule_model_matches_oracle_and_streams_are_disjoint(n, depth):
     U0, L0, _ = gen.random_sound_bounds(n, seed=n, box=6.0 + n / 8)
     Ue, Le = oracle.smooth(U0, L0)
-    Um, Lm = Model(U0, L0).run()
+    Um, Lm = Model(U0, L0, depth=depth).run()
     assert np.array_equal(Um, pins.units(Ue))
     assert np.array_equal(Lm, pins.units(Le))
+
+
+def test_schedule_model_detects_a_planted_overlap():
+    # a bulk that forgets to leave band K+2 alone overlaps the side stream's
+    # second strip: the footprint check must say so
+    U0, L0, _ = gen.random_sound_bounds(200, seed=1, box=30.0)
+    with pytest.raises(AssertionError, match="side writes what the bulk touches"):
+        Model(U0, L0, skip_second=False).run()
