@@ -78,21 +78,20 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": nbytes, "dispatches": 5}), flush=True)
 
 
-def tiles_units_per_pass(n, batch):
-    """(stored, dense) (i,j,k) triples of the bulk phase-3 kernel over one pass.
+def tiles_units_per_pass(n, batch, ahead):
+    """(stored, dense) (i,j,k) triples of the bulk phase-3 launches over one pass.
 
-    Launch K runs over every TILE x TILE tile with I <= J and stores every
-    cell outside band K (final after phase 2) and band K+1 (updated ahead by
-    the strip kernel; none for the last k-block).  `stored` counts those
-    cells x the launch's atoms; `dense` counts the full square of live rows
-    x live columns (the cells below the diagonal follow by symmetry)."""
+    Launch K runs over the 64x64 quadrants of every TILE x TILE tile with
+    I <= J and stores every cell outside band K (final after phase 2) and
+    the `ahead` bands after it (updated ahead on the second stream; fewer
+    near the end).  `stored` counts those cells x the launch's atoms;
+    `dense` counts the full square of live rows x live columns (the cells
+    below the diagonal follow by symmetry)."""
     T = -(-n // TILE)
     TB = -(-n // BK)
     stored = dense = 0
     for K in range(TB):
-        bands = [(K * BK, min(n, K * BK + BK))]
-        if K + 1 < TB:
-            bands.append(((K + 1) * BK, min(n, K * BK + 2 * BK)))
+        bands = [(B * BK, min(n, B * BK + BK)) for B in range(K, min(TB, K + 1 + ahead))]
         r = []
         for I in range(T):
             lo, hi = I * TILE, min(n, I * TILE + TILE)
@@ -341,7 +340,8 @@ def main():
     if tot["tiles"][0]:
         launches = tot["tiles"][0] // prof_steps
         launch_ms = tot["tiles"][1] / tot["tiles"][0]
-        stored, dense = tiles_units_per_pass(n, batch)
+        ahead = dgb.lookahead_bands(n, batch)
+        stored, dense = tiles_units_per_pass(n, batch, ahead)
         ops = OPS_PER_TRIPLE * stored / launches          # per launch, averaged over the pass
         achieved = ops / (launch_ms * 1e-3)
         traffic = counters_traffic(n, batch)
@@ -350,7 +350,7 @@ def main():
             "achieved": achieved / 1e12, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
             "frac": achieved / FP32_VALU_PEAK,
             "traffic": traffic,
-            "launch_ms": launch_ms, "launches": tot["tiles"][0],
+            "launch_ms": launch_ms, "launches": tot["tiles"][0], "lookahead_bands": ahead,
             "ops_per_launch": ops,
             "frac_effective": OPS_PER_TRIPLE * dense / launches / (launch_ms * 1e-3)
                               / FP32_VALU_PEAK,

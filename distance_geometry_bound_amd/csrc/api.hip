@@ -304,6 +304,11 @@ int dbs_smooth_packed(float *P, int64_t n, int64_t batch, void *stream) {
 
 int dbs_lds_max_n(void) { return dbs::kSmallMaxN; }
 
+int dbs_lookahead_bands(int64_t n, int64_t batch) {
+  if (n < 1 || batch < 1) return DBS_EINVAL;
+  return dbs::lookahead_bands(n, batch);
+}
+
 int dbs_auto_algo(int64_t n, int64_t batch) {
   (void)batch;
   return n <= dbs::kSmallMaxN ? DBS_ALGO_LDS : DBS_ALGO_BLOCKED;

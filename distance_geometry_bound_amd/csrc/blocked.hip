@@ -40,7 +40,7 @@ constexpr int TILE = 128;       // freshness granularity: tiles I <= J are kept 
 constexpr int RATIO = TILE / BK;
 constexpr int KC = 16;          // atoms per LDS chunk in phase 3
 // phase-3 tiles (times molecules) from which the pass runs two bands ahead
-constexpr int64_t kDeepTiles = 256;
+constexpr int64_t kDeepTiles = 2048;
 constexpr int kThreads = 256;
 
 // The side-stream kernels (band K+1 strip, then phases 1-2 of block K+1) are
@@ -387,7 +387,7 @@ __device__ __forceinline__ void packed_half_store(const HalfLoad &h, bool right,
 
 // Phase 3 on BK x BK blocks, thread (ty, tx) owning a 4x4 cell tile;
 // grid.y = molecules.  Two uses:
-//  * bulk (bulk != 0): every fresh cell outside band K and the bands
+//  * bulk (BULK): every fresh cell outside band K and the bands
 //    starting at s1 and s2, as the four BK x BK quadrants of each upper
 //    TILE x TILE tile (grid.x = 4 T(T+1)/2).  Band K is final after phase 2;
 //    bands s1 and s2 (the next two k-blocks' bands; < 0 for none) are
@@ -396,7 +396,7 @@ __device__ __forceinline__ void packed_half_store(const HalfLoad &h, bool right,
 //    read nor written, and the panel columns of bands s1 and s2 are not
 //    read, since the other stream may be updating exactly those cells while
 //    this launch runs.
-//  * strip (bulk == 0): the row band starting at s1 only, run ahead of the
+//  * strip (!BULK): the row band starting at s1 only, run ahead of the
 //    bulk on the second stream.  grid.x = the k-block tiles J other than K
 //    and the band starting at s2 (< 0 for none); block (s1 / BK, J) is kept
 //    in its fresh orientation.
@@ -406,10 +406,10 @@ __device__ __forceinline__ void packed_half_store(const HalfLoad &h, bool right,
 // for L; pairs of atoms fold into 3-input min/max (4.5 instructions per cell
 // and atom).  12 waves per CU (3 workgroups) keep the VALU busy through the
 // LDS and global latencies.
-template <bool VEC, bool PK, bool RU>
+template <bool VEC, bool PK, bool RU, bool BULK>
 __global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, float *__restrict__ L,
                                                      int64_t n, int64_t batch, int64_t K,
-                                                     int64_t s1, int64_t s2, int bulk) {
+                                                     int64_t s1, int64_t s2) {
   __shared__ float4 scu[KC][BK / 4];
   __shared__ float4 scl[KC][BK / 4];
   __shared__ float4 sru[KC][BK / 4];
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, floa
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   int64_t A, B;  // row band, column band of the block
   bool rowor;    // stored as (A, B) (else as its transpose (B, A))
-  if (!bulk) {
+  if (!BULK) {
     // row band s1 / BK; every column band but K and s2 / BK (s2 < 0: none)
     critical_path_priority();
     A = s1 / BK;
@@ -644,6 +644,12 @@ Events *thread_events() {
 
 }  // namespace
 
+int lookahead_bands(int64_t n, int64_t batch) {
+  const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
+  if (TB <= 1 || T <= 1) return 0;
+  return T * (T + 1) / 2 * batch >= kDeepTiles ? 2 : 1;
+}
+
 // Enqueue one pass.  With more than one k-block the pass runs ahead on a
 // second stream, by two bands when there are many phase-3 tiles.  Per k-block
 // K the caller's stream runs bulk(K): phase 3 of block K on everything but
@@ -669,12 +675,13 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   const unsigned gy = (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ);
   const int64_t nn = n * n;
   if (packed) L = U;
-#define DBS_PICK(K)                                                                   \
-  (packed ? (ru ? (vec ? K<true, true, true> : K<false, true, true>)                  \
-                : (vec ? K<true, true, false> : K<false, true, false>))               \
-          : (ru ? (vec ? K<true, false, true> : K<false, false, true>)                \
-                : (vec ? K<true, false, false> : K<false, false, false>)))
-  auto blocks = DBS_PICK(k_blocks);
+#define DBS_PICK(K, X)                                                                     \
+  (packed ? (ru ? (vec ? K<true, true, true, X> : K<false, true, true, X>)                 \
+                : (vec ? K<true, true, false, X> : K<false, true, false, X>))              \
+          : (ru ? (vec ? K<true, false, true, X> : K<false, false, true, X>)               \
+                : (vec ? K<true, false, false, X> : K<false, false, false, X>)))
+  auto bulk_kernel = DBS_PICK(k_blocks, true);
+  auto strip_kernel = DBS_PICK(k_blocks, false);
 #undef DBS_PICK
   // With many phase-3 tiles the bulk runs long enough to hide phases 1-2 of
   // the next blocks: they run two bands ahead, on 256-thread workgroups that
@@ -682,7 +689,7 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   // critical path: one band ahead, on 1024-thread workgroups that hide the
   // latency of their rounds best.
   const int64_t pairs = T * (T + 1) / 2;
-  const bool deep = pairs * batch >= kDeepTiles;
+  const bool deep = lookahead_bands(n, batch) == 2;
 #define DBS_PICK_PANEL(S)                                                                   \
   (packed ? (ru ? (vec ? k_diag_panel<true, true, true, S> : k_diag_panel<false, true, true, S>)   \
                 : (vec ? k_diag_panel<true, true, false, S> : k_diag_panel<false, true, false, S>)) \
@@ -702,8 +709,8 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   };
   // s1, s2: first atoms of the bands the bulk launch must leave alone (-1: none)
   auto phase3 = [&](int64_t K, int64_t s1, int64_t s2, hipStream_t st) -> hipError_t {
-    return launch(prof, kProfTiles, blocks, dim3((unsigned)(4 * pairs), gy), dim3(kThreads), st,
-                  U, L, n, batch, K, s1, s2, 1);
+    return launch(prof, kProfTiles, bulk_kernel, dim3((unsigned)(4 * pairs), gy), dim3(kThreads),
+                  st, U, L, n, batch, K, s1, s2);
   };
 
   hipError_t e = phase12(K0, s);
@@ -711,8 +718,8 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
 
   // phase 3 of block K on row band A, every column band but K and `skip`
   auto strip = [&](int64_t K, int64_t A, int64_t skip, hipStream_t st) -> hipError_t {
-    return launch(prof, kProfStrip, blocks, dim3((unsigned)(TB - 1 - (skip >= 0)), gy),
-                  dim3(kThreads), st, U, L, n, batch, K, A * BK, skip < 0 ? -1 : skip * BK, 0);
+    return launch(prof, kProfStrip, strip_kernel, dim3((unsigned)(TB - 1 - (skip >= 0)), gy),
+                  dim3(kThreads), st, U, L, n, batch, K, A * BK, skip < 0 ? -1 : skip * BK);
   };
   hipStream_t side = T > 1 ? side_stream() : nullptr;
   Events *ev = side ? thread_events() : nullptr;

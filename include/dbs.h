@@ -280,6 +280,16 @@ int dbs_smooth_packed_range(float *P, int64_t n, int64_t batch, int64_t k_begin,
                             void *stream);
 int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags, void *stream);
 
+/*
+ * dbs_lookahead_bands -- how many k-block bands the blocked pass (DBS_ALGO_
+ * BLOCKED) updates ahead on its second stream for this shape: 0 (a single
+ * k-block or phase-3 tile: no second stream), 1, or 2 (many phase-3 tiles:
+ * phases 1-2 of the next block then have a whole phase-3 launch to hide
+ * under).  Phase 3's bulk launches leave those bands to the second stream.
+ * For measurement and tests; DBS_EINVAL for n < 1 or batch < 1.
+ */
+int dbs_lookahead_bands(int64_t n, int64_t batch);
+
 /* Largest n the LDS algorithm accepts. */
 int dbs_lds_max_n(void);
 

@@ -106,3 +106,17 @@ def test_round_rejects_k_out_of_range_on_the_host():
     p = ctypes.cast(buf, ctypes.c_void_p).value
     assert lib.dbs_round(p, p, 4, 1, -1, None) == -1
     assert lib.dbs_round(p, p, 4, 1, 4, None) == -1
+
+
+def test_lookahead_bands_query():
+    # host-side shape logic only (no device call)
+    lib = dgb.lib()
+    assert lib.dbs_lookahead_bands(1, 1) == 0        # nothing to run ahead
+    assert lib.dbs_lookahead_bands(64, 1) == 0       # one k-block
+    assert lib.dbs_lookahead_bands(128, 3) == 0      # one phase-3 tile
+    assert lib.dbs_lookahead_bands(200, 1) == 1
+    assert lib.dbs_lookahead_bands(500, 64) == 1
+    assert lib.dbs_lookahead_bands(4096, 1) == 1
+    assert lib.dbs_lookahead_bands(12288, 1) == 2
+    assert lib.dbs_lookahead_bands(0, 1) == -1 and lib.dbs_lookahead_bands(5, 0) == -1
+    assert dgb.lookahead_bands(12288) == 2
