@@ -375,6 +375,61 @@ __device__ __forceinline__ void packed_half_store(const HalfLoad &h, bool right,
   }
 }
 
+// ---------------------------------------------------------------- block write-back
+// v[r][q] of thread (ty, tx) (a 4x4 cell tile of a BK x BK block) to
+// P[r0 + 4ty + r][c0 + 4tx + q], rows < rows and columns < cols: one float4
+// per row where the row segment is whole (VEC: 16-byte aligned).
+template <bool VEC>
+__device__ __forceinline__ void store_rows(float *P, int64_t n, int64_t r0, int64_t c0, int rows,
+                                           int cols, int ty, int tx, const float (&v)[4][4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int a = ty * 4 + r, c = tx * 4;
+    if (a >= rows) continue;
+    float *p = P + (r0 + a) * n + c0 + c;
+    if (VEC && c + 3 < cols) {
+      *reinterpret_cast<float4 *>(p) = make_float4(v[r][0], v[r][1], v[r][2], v[r][3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (c + q < cols) p[q] = v[r][q];
+    }
+  }
+}
+
+// The same cells to their transposed position P[c0 + 4tx + q][r0 + 4ty + r].
+// The block is turned around in the LDS tile `tr` first (stride BK + 1: the
+// writes meet at most 8 threads on a bank, the reads 2), so that the global
+// writes are row segments, 16 threads to a 256-byte row.  Contains barriers:
+// every thread of the workgroup must call it.
+template <bool VEC>
+__device__ __forceinline__ void store_transposed(float *P, int64_t n, int64_t r0, int64_t c0,
+                                                 int rows, int cols, int ty, int tx,
+                                                 const float (&v)[4][4],
+                                                 float (*tr)[BK + 1]) {
+  __syncthreads();  // tr free (a previous call may still be reading it)
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tr[tx * 4 + q][ty * 4 + r] = v[r][q];
+  __syncthreads();
+  const int tid = ty * (BK / 4) + tx;
+#pragma unroll
+  for (int it = 0; it < BK * BK / 4 / kThreads; ++it) {
+    const int e = tid + it * kThreads, c = e / (BK / 4), a = (e % (BK / 4)) * 4;
+    if (c >= cols) continue;
+    float *p = P + (c0 + c) * n + r0 + a;
+    if (VEC && a + 3 < rows) {
+      *reinterpret_cast<float4 *>(p) = make_float4(tr[c][a], tr[c][a + 1], tr[c][a + 2],
+                                                    tr[c][a + 3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (a + i < rows) p[i] = tr[c][a + i];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- phase 3
 
 // TILE x TILE tiles are numbered column-major over the upper triangle, and
@@ -414,6 +469,7 @@ __global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, floa
   __shared__ float4 scl[KC][BK / 4];
   __shared__ float4 sru[KC][BK / 4];
   __shared__ float4 srl[KC][BK / 4];
+  __shared__ float tr[BK][BK + 1];  // write-back of transposed values
 
   rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
@@ -543,18 +599,32 @@ __global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, floa
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int q = 0; q < 4; ++q) l[r][q] = lower_out<RU>(l[r][q]);
-    if (PK) packed_block_store(Ub, n, a0, j0, bA, bJ, ty, tx, u, l);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int a = ty * 4 + r, c = tx * 4 + q;
-        if (!PK && a < bA && c < bJ) {
-          const int64_t g = rowor ? (a0 + a) * n + j0 + c : (j0 + c) * n + a0 + a;
-          Ub[g] = u[r][q];
-          Lb[g] = l[r][q];
-        }
+    // write-back as row segments: scattered single-float writes across rows
+    // cost more than the LDS round trip of the transposed half.  The thread
+    // index is re-derived here so that the write addresses are computed
+    // after the k loop instead of being kept live through it.
+    int tw = tid;
+    asm volatile("" : "+v"(tw));
+    const int wy = tw >> 4, wx = tw & 15;
+    if (PK && a0 == j0) {
+      // diagonal block: per cell, the diagonal slot untouched
+      packed_block_store(Ub, n, a0, j0, bA, bJ, wy, wx, u, l);
+    } else if (PK) {
+      // one side of the diagonal: the row slots hold U right of it, L left
+      if (a0 < j0) {
+        store_rows<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, u);
+        store_transposed<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, l, tr);
+      } else {
+        store_rows<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, l);
+        store_transposed<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, u, tr);
       }
+    } else if (rowor) {
+      store_rows<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, u);
+      store_rows<VEC>(Lb, n, a0, j0, bA, bJ, wy, wx, l);
+    } else {
+      store_transposed<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, u, tr);
+      store_transposed<VEC>(Lb, n, a0, j0, bA, bJ, wy, wx, l, tr);
+    }
     __syncthreads();
   }
 }
