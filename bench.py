@@ -103,14 +103,22 @@ def tiles_units_per_pass(n, batch, ahead):
     return stored * batch, dense * batch
 
 
+def source_digest(path):
+    """sha256 of a C++ source with its // comments and all whitespace removed,
+    so that the counter record stays valid across edits of comments only."""
+    import re
+    text = re.sub(r"//[^\n]*", "", open(path).read())
+    return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()
+
+
 def counters_traffic(n, batch):
     """HBM bytes per phase-3 launch from the committed counter run, if the
-    kernel source is unchanged since it was taken; else None."""
+    kernel source (comments aside) is unchanged since it was taken; else None."""
     try:
         rec = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    sha = source_digest(KERNEL_SRC)
     if rec.get("source_sha256") != sha or rec.get("n") != n or rec.get("batch") != batch:
         return None
     return rec.get("traffic_bytes_per_launch")

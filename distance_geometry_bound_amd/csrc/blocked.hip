@@ -459,7 +459,7 @@ __device__ __forceinline__ void store_transposed(float *P, int64_t n, int64_t r0
 // global loads of chunk c+1 are issued before chunk c is computed.  Per atom
 // and cell the VALU does one add and one min for U, two subtracts and two max
 // for L; pairs of atoms fold into 3-input min/max (4.5 instructions per cell
-// and atom).  12 waves per CU (3 workgroups) keep the VALU busy through the
+// and atom).  16 waves per CU (4 workgroups, dense bulk) keep the VALU busy through the
 // LDS and global latencies.
 template <bool VEC, bool PK, bool RU, bool BULK>
 __global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, float *__restrict__ L,
