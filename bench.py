@@ -9,7 +9,7 @@ dbs_smooth.  The default workload is n = 12288: 48 self-avoiding chains of
 Printed: one JSON line with
   value        bound-updates/s = 2 n^3 batch / (seconds per step)
   pct_fp32_valu_peak  = 6 n^3 batch / t / 157.3e12 (3 ops per bound-update)
-  roofline     the bulk phase-3 kernel (k_blocks on 64x64 quadrants):
+  roofline     the bulk phase-3 kernel (k_quads on 64x64 quadrants):
                algorithmic ops of the cells a launch stores / mean launch
                time from HIP events (dbs_smooth_profiled on the launch stream)
   perk         the per-round kernel: HBM bytes of the round formulation
@@ -41,7 +41,7 @@ FP32_VALU_PEAK = 157.3e12       # MI355X fp32 vector, ops/s
 HBM_PEAK = 8.0e12               # MI355X HBM3E, bytes/s
 OPS_PER_TRIPLE = 6              # 1 add + 1 min (upper), 2 sub + 2 max (lower)
 TILE, BK = 128, 64              # blocked-path geometry (csrc/blocked.hip)
-COUNTERS = os.path.join(ROOT, "profiles", "k_blocks_n12288_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "k_quads_n12288_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "distance_geometry_bound_amd", "csrc", "blocked.hip")
 
 
@@ -354,7 +354,7 @@ def main():
         achieved = ops / (launch_ms * 1e-3)
         traffic = counters_traffic(n, batch)
         out["roofline"] = {
-            "bound": "alu", "kernel": "k_blocks (bulk)",
+            "bound": "alu", "kernel": "k_quads (dense bulk of phase 3)",
             "achieved": achieved / 1e12, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
             "frac": achieved / FP32_VALU_PEAK,
             "traffic": traffic,

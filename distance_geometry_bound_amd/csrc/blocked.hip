@@ -629,6 +629,166 @@ __global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, floa
   }
 }
 
+// Bulk of phase 3 for the dense layout: thread (ty, tx) owns RT x CT cells of
+// a BK x BK quadrant (rows a0 + RT*ty + r, columns j0 + CT*tx + q).  Same
+// quadrants, skips, staging (KCH atoms per chunk, next chunk prefetched) and
+// row-segment write-back as the bulk mode of k_blocks, without its layout
+// and mode switches.  Larger tiles read fewer staged operand floats per cell
+// (the LDS return traffic limits the 4x4 tile) but lose occupancy; 4x4 is
+// the fastest measured (kBulkRT below).
+template <bool VEC, bool RU, int RT, int CT, int KCH>
+__global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restrict__ U,
+                                                                 float *__restrict__ L,
+                                                                 int64_t n, int64_t batch,
+                                                                 int64_t K, int64_t s1,
+                                                                 int64_t s2) {
+  constexpr int NTX = BK / CT, NT = (BK / RT) * NTX;
+  constexpr int RQ = RT / 4, CQ = CT / 4;            // float4 per row / column group
+  constexpr int ITER = KCH * (BK / 4) / NT;          // staged float4 per thread and array
+  static_assert(ITER >= 1 && KCH * (BK / 4) % NT == 0, "staging split");
+  __shared__ float4 scu[KCH][BK / 4];
+  __shared__ float4 scl[KCH][BK / 4];
+  __shared__ float4 sru[KCH][BK / 4];
+  __shared__ float4 srl[KCH][BK / 4];
+
+  rounding_prologue<RU>();
+  const int tid = threadIdx.x, ty = tid / NTX, tx = tid % NTX;
+  const int64_t p = blockIdx.x >> 2, qd = blockIdx.x & 3;
+  const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
+  const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
+  if (A * BK >= n || B * BK >= n || A == K || B == K || A * BK == s1 || B * BK == s1 ||
+      A * BK == s2 || B * BK == s2)
+    return;  // uniform over the workgroup, before any barrier
+  const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
+  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int bA = (int)(n - a0 < BK ? n - a0 : BK);
+  const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
+  const int64_t nn = n * n;
+
+  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    float *Ub = U + b * nn;
+    float *Lb = L + b * nn;
+
+    float u[RT][CT], l[RT][CT];
+    {
+      float4 x[RT][CQ], y[RT][CQ];
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int h = 0; h < CQ; ++h) {
+          const int a = ty * RT + r, c = tx * CT + 4 * h;
+          const int cnt = a < bA ? clamp4(bJ - c) : 0;
+          const int64_t g = (a0 + a) * n + j0 + c;
+          x[r][h] = load4<VEC>(Ub + g, cnt, kInf, Ub);
+          y[r][h] = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+        }
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int h = 0; h < CQ; ++h) {
+          u[r][4 * h + 0] = x[r][h].x; u[r][4 * h + 1] = x[r][h].y;
+          u[r][4 * h + 2] = x[r][h].z; u[r][4 * h + 3] = x[r][h].w;
+          l[r][4 * h + 0] = y[r][h].x; l[r][4 * h + 1] = y[r][h].y;
+          l[r][4 * h + 2] = y[r][h].z; l[r][4 * h + 3] = y[r][h].w;
+        }
+    }
+
+    float4 st[ITER][4];
+    auto fetch = [&](int kc) {
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const int e = tid + it * NT, kk = e / (BK / 4), x4 = e % (BK / 4);
+        const int64_t k = k0 + kc + kk;
+        const bool kin = kc + kk < bK;
+        const int ni = kin ? clamp4(bA - x4 * 4) : 0;
+        const int nj = kin ? clamp4(bJ - x4 * 4) : 0;
+        st[it][0] = load4<VEC>(Ub + k * n + a0 + x4 * 4, ni, kInf, Ub);
+        st[it][1] = load4<VEC>(Lb + k * n + a0 + x4 * 4, ni, 0.0f, Lb);
+        st[it][2] = load4<VEC>(Ub + k * n + j0 + x4 * 4, nj, kInf, Ub);
+        st[it][3] = load4<VEC>(Lb + k * n + j0 + x4 * 4, nj, 0.0f, Lb);
+      }
+    };
+    fetch(0);
+    for (int kc = 0; kc < bK; kc += KCH) {
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const int e = tid + it * NT, kk = e / (BK / 4), x4 = e % (BK / 4);
+        scu[kk][x4] = st[it][0];
+        scl[kk][x4] = st[it][1];
+        sru[kk][x4] = st[it][2];
+        srl[kk][x4] = st[it][3];
+      }
+      __syncthreads();
+      if (kc + KCH < bK) fetch(kc + KCH);  // in flight during this chunk
+#pragma unroll 2
+      for (int kk = 0; kk < KCH; kk += 2) {
+        float cu0[RT], cl0[RT], cu1[RT], cl1[RT], ru0[CT], rl0[CT], ru1[CT], rl1[CT];
+#pragma unroll
+        for (int h = 0; h < RQ; ++h) {
+          const float4 a = scu[kk][RQ * ty + h], bb = scl[kk][RQ * ty + h];
+          const float4 c = scu[kk + 1][RQ * ty + h], d = scl[kk + 1][RQ * ty + h];
+          cu0[4 * h] = a.x; cu0[4 * h + 1] = a.y; cu0[4 * h + 2] = a.z; cu0[4 * h + 3] = a.w;
+          cl0[4 * h] = bb.x; cl0[4 * h + 1] = bb.y; cl0[4 * h + 2] = bb.z; cl0[4 * h + 3] = bb.w;
+          cu1[4 * h] = c.x; cu1[4 * h + 1] = c.y; cu1[4 * h + 2] = c.z; cu1[4 * h + 3] = c.w;
+          cl1[4 * h] = d.x; cl1[4 * h + 1] = d.y; cl1[4 * h + 2] = d.z; cl1[4 * h + 3] = d.w;
+        }
+#pragma unroll
+        for (int h = 0; h < CQ; ++h) {
+          const float4 a = sru[kk][CQ * tx + h], bb = srl[kk][CQ * tx + h];
+          const float4 c = sru[kk + 1][CQ * tx + h], d = srl[kk + 1][CQ * tx + h];
+          ru0[4 * h] = a.x; ru0[4 * h + 1] = a.y; ru0[4 * h + 2] = a.z; ru0[4 * h + 3] = a.w;
+          rl0[4 * h] = bb.x; rl0[4 * h + 1] = bb.y; rl0[4 * h + 2] = bb.z; rl0[4 * h + 3] = bb.w;
+          ru1[4 * h] = c.x; ru1[4 * h + 1] = c.y; ru1[4 * h + 2] = c.z; ru1[4 * h + 3] = c.w;
+          rl1[4 * h] = d.x; rl1[4 * h + 1] = d.y; rl1[4 * h + 2] = d.z; rl1[4 * h + 3] = d.w;
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+          for (int q = 0; q < CT; ++q)
+            relax2<RU>(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
+                       rl1[q]);
+      }
+      __syncthreads();
+    }
+
+    // write-back, one float4 per row group
+    int tw = tid;
+    asm volatile("" : "+v"(tw));
+    const int wy = tw / NTX, wx = tw % NTX;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int a = wy * RT + r;
+      if (a >= bA) continue;
+#pragma unroll
+      for (int h = 0; h < CQ; ++h) {
+        const int c = wx * CT + 4 * h;
+        float *pu = Ub + (a0 + a) * n + j0 + c, *pl = Lb + (a0 + a) * n + j0 + c;
+        const float lv[4] = {lower_out<RU>(l[r][4 * h]), lower_out<RU>(l[r][4 * h + 1]),
+                             lower_out<RU>(l[r][4 * h + 2]), lower_out<RU>(l[r][4 * h + 3])};
+        if (VEC && c + 3 < bJ) {
+          *reinterpret_cast<float4 *>(pu) =
+              make_float4(u[r][4 * h], u[r][4 * h + 1], u[r][4 * h + 2], u[r][4 * h + 3]);
+          *reinterpret_cast<float4 *>(pl) = make_float4(lv[0], lv[1], lv[2], lv[3]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (c + i < bJ) {
+              pu[i] = u[r][4 * h + i];
+              pl[i] = lv[i];
+            }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// The dense bulk's register tile.
+// (measured at n12288, bulk launch: 4x4 419 us at 4 workgroups per CU; 4x8
+// and 8x4 with 8-atom chunks 422-428 us at 3; 4x8, 8x4 with 16-atom chunks
+// 484-494 us at 2; 8x8 needs more than 256 VGPRs)
+constexpr int kBulkRT = 4, kBulkCT = 4, kBulkKC = 16;
+
 // ---------------------------------------------------------------- mirror
 // grid.x = TB*TB k-block tiles (a = x / TB, b = x % TB), grid.y = molecules.
 // Stale tiles (a,b) (a/RATIO > b/RATIO) are overwritten with the transpose
@@ -751,6 +911,12 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
           : (ru ? (vec ? K<true, false, true, X> : K<false, false, true, X>)               \
                 : (vec ? K<true, false, false, X> : K<false, false, false, X>)))
   auto bulk_kernel = DBS_PICK(k_blocks, true);
+  // the dense bulk runs with larger register tiles
+  auto quads_kernel = ru ? (vec ? k_quads<true, true, kBulkRT, kBulkCT, kBulkKC>
+                                : k_quads<false, true, kBulkRT, kBulkCT, kBulkKC>)
+                         : (vec ? k_quads<true, false, kBulkRT, kBulkCT, kBulkKC>
+                                : k_quads<false, false, kBulkRT, kBulkCT, kBulkKC>);
+  constexpr unsigned quads_block = (BK / kBulkRT) * (BK / kBulkCT);
   auto strip_kernel = DBS_PICK(k_blocks, false);
 #undef DBS_PICK
   // With many phase-3 tiles the bulk runs long enough to hide phases 1-2 of
@@ -779,6 +945,9 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   };
   // s1, s2: first atoms of the bands the bulk launch must leave alone (-1: none)
   auto phase3 = [&](int64_t K, int64_t s1, int64_t s2, hipStream_t st) -> hipError_t {
+    if (!packed)
+      return launch(prof, kProfTiles, quads_kernel, dim3((unsigned)(4 * pairs), gy),
+                    dim3(quads_block), st, U, L, n, batch, K, s1, s2);
     return launch(prof, kProfTiles, bulk_kernel, dim3((unsigned)(4 * pairs), gy), dim3(kThreads),
                   st, U, L, n, batch, K, s1, s2);
   };
