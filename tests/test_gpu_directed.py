@@ -170,3 +170,39 @@ def test_directed_blocked_sound_on_line(n):
     Un, Ln = dev(U0), dev(L0)
     dgb.smooth(Un, Ln, algo="blocked")
     assert np.any(host(Un).astype(np.float64) < d) or np.any(host(Ln).astype(np.float64) > d)
+
+
+# ---------------------------------------------------------------- full size
+def _n12288_sampled_checks(W, Ug, Lg, tag):
+    """Four shortest-path rows against a textbook Dijkstra, L at every pair of
+    those atoms against the closed form, symmetry, L <= U and soundness."""
+    import pins
+    rng = np.random.default_rng(12288)
+    src = sorted(rng.choice(W.n, size=4, replace=False).tolist())
+    D = pins.sssp_dense(W.U[0], src)
+    for a, s in enumerate(src):
+        assert np.array_equal(Ug[s].astype(np.float64), D[a]), f"{tag}: U row {s}"
+    for a in range(len(src)):
+        for b in range(a, len(src)):
+            want = pins.lower_pair(W.L[0], D[a], D[b])
+            assert float(Lg[src[a], src[b]]) == want, (tag, src[a], src[b])
+    assert np.array_equal(Ug.view(np.uint32), Ug.T.view(np.uint32))
+    assert np.array_equal(Lg.view(np.uint32), Lg.T.view(np.uint32))
+    assert np.all(Lg <= Ug) and pins.sound(Ug, Lg, W.X[0])
+
+
+def test_directed_n12288_on_grid_sampled():
+    # the n12288 workload is on the 2^-6 grid, so the directed pass must reach
+    # the exact result, checked at sampled rows and pairs
+    W = gen.make_workload("n12288")
+    U, L = dev(W.U[0]), dev(W.L[0])
+    dgb.smooth_directed(U, L)
+    _n12288_sampled_checks(W, host(U), host(L), "directed n12288")
+
+
+def test_packed_n12288_sampled():
+    W = gen.make_workload("n12288")
+    P = dgb.pack(dev(W.U[0]), dev(W.L[0]))
+    dgb.smooth_packed(P)
+    U, L = dgb.unpack(P)
+    _n12288_sampled_checks(W, host(U), host(L), "packed n12288")
