@@ -11,7 +11,10 @@ Printed: one JSON line with
   pct_fp32_valu_peak  = 6 n^3 batch / t / 157.3e12 (3 ops per bound-update)
   roofline     the bulk phase-3 kernel (k_quads on 64x64 quadrants):
                algorithmic ops of the cells a launch stores / mean launch
-               time from HIP events (dbs_smooth_profiled on the launch stream)
+               time from HIP events (dbs_smooth_profiled on the launch stream),
+               against the issue ceiling of its fp32 add/sub/min/max mix
+               (92 T op/s on gfx950; the 157.3 T fp32 vector peak counts
+               FMAs, which this path has none of)
   perk         the per-round kernel: HBM bytes of the round formulation
                (16 B per cell per round) / mean round time
   restraints   the workload's restraint list to dense bounds (fill + scatter)
@@ -37,7 +40,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "bound-updates/s (2·n³ per pass) + % fp32 VALU peak; HBM GB/s per-k kernel"
-FP32_VALU_PEAK = 157.3e12       # MI355X fp32 vector, ops/s
+FP32_VALU_PEAK = 157.3e12       # MI355X fp32 vector, ops/s (an FMA counted as 2)
+# Issue ceiling of phase 3's own instruction mix (add/sub at 32 lanes/clk per
+# SIMD, min/max at 16, partly overlapped): 256 CUs x 4 SIMDs x 37.4 op-lanes/clk
+# x 2.4 GHz, measured register-only by probe/valu_rates
+# (profiles/valu_issue_rates_gfx950.md).
+MIX_PEAK = 92.0e12
 HBM_PEAK = 8.0e12               # MI355X HBM3E, bytes/s
 OPS_PER_TRIPLE = 6              # 1 add + 1 min (upper), 2 sub + 2 max (lower)
 TILE, BK = 128, 64              # blocked-path geometry (csrc/blocked.hip)
@@ -355,8 +363,11 @@ def main():
         traffic = counters_traffic(n, batch)
         out["roofline"] = {
             "bound": "alu", "kernel": "k_quads (dense bulk of phase 3)",
-            "achieved": achieved / 1e12, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
-            "frac": achieved / FP32_VALU_PEAK,
+            "achieved": achieved / 1e12, "peak": MIX_PEAK / 1e12, "unit": "TFLOP/s",
+            "frac": achieved / MIX_PEAK,
+            "peak_basis": "issue ceiling of the kernel's fp32 add/sub/min/max mix on gfx950 "
+                          "(256 CUs x 4 SIMDs x 37.4 op-lanes/clk x 2.4 GHz)",
+            "frac_of_fp32_vector_peak": achieved / FP32_VALU_PEAK,
             "traffic": traffic,
             "launch_ms": launch_ms, "launches": tot["tiles"][0], "lookahead_bands": ahead,
             "ops_per_launch": ops,
