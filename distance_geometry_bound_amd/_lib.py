@@ -28,7 +28,7 @@ EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds",
            "dbs_check", "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened", "dbs_bounds_from_restraints",
            "dbs_pack", "dbs_unpack", "dbs_smooth_packed", "dbs_smooth_packed_range",
            "dbs_check_packed", "dbs_smooth_directed", "dbs_smooth_directed_range",
-           "dbs_smooth_packed_directed_range", "dbs_lookahead_bands",
+           "dbs_smooth_packed_directed_range", "dbs_lookahead_bands", "dbs_set_lookahead",
            "dbs_lds_max_n", "dbs_auto_algo", "dbs_strerror", "dbs_version")
 
 RESTRAINT_FLAGS = {"index": 1, "value": 2}
@@ -75,6 +75,7 @@ def lib():
         L.dbs_smooth_packed_directed_range.argtypes = [vp, i64, i64, i64, i64, vp]
         L.dbs_auto_algo.argtypes = [i64, i64]
         L.dbs_lookahead_bands.argtypes = [i64, i64]
+        L.dbs_set_lookahead.argtypes = [ctypes.c_int]
         L.dbs_strerror.argtypes = [c_int]
         L.dbs_strerror.restype = ctypes.c_char_p
         for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_round",
@@ -83,7 +84,8 @@ def lib():
                   "dbs_bounds_from_restraints", "dbs_pack", "dbs_unpack", "dbs_smooth_packed",
                   "dbs_smooth_packed_range", "dbs_check_packed", "dbs_smooth_directed",
                   "dbs_smooth_directed_range", "dbs_smooth_packed_directed_range",
-                  "dbs_lds_max_n", "dbs_auto_algo", "dbs_lookahead_bands", "dbs_version"):
+                  "dbs_lds_max_n", "dbs_auto_algo", "dbs_lookahead_bands", "dbs_set_lookahead",
+                  "dbs_version"):
             getattr(L, f).restype = c_int
         _lib = L
     return _lib
@@ -352,6 +354,12 @@ def check_packed(P) -> int:
 def lookahead_bands(n: int, batch: int = 1) -> int:
     """Bands the blocked pass updates ahead on its second stream (0, 1, 2)."""
     return int(lib().dbs_lookahead_bands(int(n), int(batch)))
+
+
+def set_lookahead(bands: int) -> None:
+    """Force the look-ahead depth of later blocked passes (0, 1, 2), or -1
+    for the automatic choice (process-wide)."""
+    _raise(lib().dbs_set_lookahead(int(bands)))
 
 
 def auto_algo(n: int, batch: int = 1) -> str:

@@ -309,6 +309,10 @@ int dbs_lookahead_bands(int64_t n, int64_t batch) {
   return dbs::lookahead_bands(n, batch);
 }
 
+int dbs_set_lookahead(int bands) {
+  return dbs::set_lookahead(bands) ? DBS_OK : DBS_EINVAL;
+}
+
 int dbs_auto_algo(int64_t n, int64_t batch) {
   (void)batch;
   return n <= dbs::kSmallMaxN ? DBS_ALGO_LDS : DBS_ALGO_BLOCKED;

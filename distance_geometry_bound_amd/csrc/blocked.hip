@@ -28,6 +28,7 @@
 // Phase 3: a 256-thread workgroup owns a 64x64 block, each thread a 4x4
 // register tile; the panel rows of the k-block are staged through LDS.  No
 // matrix cores: min-plus is not a multiply-add contraction.
+#include <atomic>
 #include <mutex>
 
 #include "dbs_internal.h"
@@ -41,6 +42,12 @@ constexpr int RATIO = TILE / BK;
 constexpr int KC = 16;          // atoms per LDS chunk in phase 3
 // phase-3 tiles (times molecules) from which the pass runs two bands ahead
 constexpr int64_t kDeepTiles = 2048;
+// Below this many phase-3 tiles (times molecules) a bulk launch is too short
+// to hide the band strip that running ahead puts on the critical path.
+constexpr int64_t kAheadTiles = 256;
+// Above this many phase 1-2 workgroups the panel launch fills the chip by
+// itself, and running it beside the bulk gains nothing (one per CU).
+constexpr int64_t kPanelFill = 256;
 constexpr int kThreads = 256;
 
 // The side-stream kernels (band K+1 strip, then phases 1-2 of block K+1) are
@@ -874,10 +881,27 @@ Events *thread_events() {
 
 }  // namespace
 
-int lookahead_bands(int64_t n, int64_t batch) {
+namespace {
+std::atomic<int> forced_lookahead{-1};  // -1: automatic
+}  // namespace
+
+bool set_lookahead(int bands) {
+  if (bands < -1 || bands > 2) return false;
+  forced_lookahead.store(bands);
+  return true;
+}
+
+int lookahead_bands(int64_t n, int64_t batch, bool packed) {
   const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
   if (TB <= 1 || T <= 1) return 0;
-  return T * (T + 1) / 2 * batch >= kDeepTiles ? 2 : 1;
+  const int forced = forced_lookahead.load();
+  if (forced >= 0) return forced;
+  const int64_t tiles = T * (T + 1) / 2 * batch;
+  if (tiles >= kDeepTiles) return 2;
+  // the packed bulk runs at 3 workgroups per CU and is slow enough to hide
+  // even a panel launch that fills the chip
+  if (tiles < kAheadTiles || (!packed && (TB - 1) * batch > kPanelFill)) return 0;
+  return 1;
 }
 
 // Enqueue one pass.  With more than one k-block the pass runs ahead on a
@@ -925,7 +949,8 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   // critical path: one band ahead, on 1024-thread workgroups that hide the
   // latency of their rounds best.
   const int64_t pairs = T * (T + 1) / 2;
-  const bool deep = lookahead_bands(n, batch) == 2;
+  const int ahead = lookahead_bands(n, batch, packed);
+  const bool deep = ahead == 2;
 #define DBS_PICK_PANEL(S)                                                                   \
   (packed ? (ru ? (vec ? k_diag_panel<true, true, true, S> : k_diag_panel<false, true, true, S>)   \
                 : (vec ? k_diag_panel<true, true, false, S> : k_diag_panel<false, true, false, S>)) \
@@ -960,7 +985,7 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
     return launch(prof, kProfStrip, strip_kernel, dim3((unsigned)(TB - 1 - (skip >= 0)), gy),
                   dim3(kThreads), st, U, L, n, batch, K, A * BK, skip < 0 ? -1 : skip * BK);
   };
-  hipStream_t side = T > 1 ? side_stream() : nullptr;
+  hipStream_t side = ahead > 0 ? side_stream() : nullptr;
   Events *ev = side ? thread_events() : nullptr;
   if (side == nullptr || ev == nullptr) {
     for (int64_t K = K0; K < K1 && e == hipSuccess; ++K) {

@@ -190,7 +190,10 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
                           hipStream_t s, Prof *prof = nullptr, unsigned flags = 0);
 constexpr int kBlockRounds = 64;
 // Bands the blocked pass updates ahead on its second stream (0, 1 or 2).
-int lookahead_bands(int64_t n, int64_t batch);
+int lookahead_bands(int64_t n, int64_t batch, bool packed = false);
+// Force the look-ahead depth (0..2) or restore the automatic choice (-1);
+// false (and no change) for any other value.
+bool set_lookahead(int bands);
 hipError_t launch_restraints(float *U, float *L, int64_t n, int64_t batch, float unknown_L,
                              float unknown_U, const int32_t *mol, const int32_t *ia,
                              const int32_t *ja, const float *lo, const float *hi, int64_t count,

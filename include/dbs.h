@@ -282,13 +282,32 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags
 
 /*
  * dbs_lookahead_bands -- how many k-block bands the blocked pass (DBS_ALGO_
- * BLOCKED) updates ahead on its second stream for this shape: 0 (a single
- * k-block or phase-3 tile: no second stream), 1, or 2 (many phase-3 tiles:
- * phases 1-2 of the next block then have a whole phase-3 launch to hide
- * under).  Phase 3's bulk launches leave those bands to the second stream.
- * For measurement and tests; DBS_EINVAL for n < 1 or batch < 1.
+ * BLOCKED) on the dense layout updates ahead on its second stream for this
+ * shape (the packed passes use the same rule without the panel-fill test):
+ *   0  no second stream: a single k-block or phase-3 tile; fewer than 256
+ *      phase-3 tiles x molecules (the bulk launch is shorter than the band
+ *      strip it would hide); or more than 256 phase 1-2 workgroups (the
+ *      panel launch fills the chip by itself; this criterion is for the
+ *      dense layout, whose bulk is faster than the packed one's);
+ *   1  otherwise, below 2048 tiles x molecules;
+ *   2  from 2048 tiles x molecules: phases 1-2 of the next block then have a
+ *      whole phase-3 launch to hide under.
+ * A depth set by dbs_set_lookahead replaces the automatic choice (still 0
+ * for a single k-block or tile).  Phase 3's bulk launches leave those bands
+ * to the second stream.  For measurement and tests; DBS_EINVAL for n < 1 or
+ * batch < 1.
  */
 int dbs_lookahead_bands(int64_t n, int64_t batch);
+
+/*
+ * dbs_set_lookahead -- process-wide override of the look-ahead depth of the
+ * blocked passes enqueued after the call: bands = 0, 1 or 2 forces that
+ * depth, -1 restores the automatic choice.  Every depth gives the same
+ * results (the schedule only reorders independent cell updates); this is
+ * for tests and tuning.  Returns DBS_OK, or DBS_EINVAL for any other value
+ * (the setting is then unchanged).
+ */
+int dbs_set_lookahead(int bands);
 
 /* Largest n the LDS algorithm accepts. */
 int dbs_lds_max_n(void);

@@ -114,9 +114,29 @@ def test_lookahead_bands_query():
     assert lib.dbs_lookahead_bands(1, 1) == 0        # nothing to run ahead
     assert lib.dbs_lookahead_bands(64, 1) == 0       # one k-block
     assert lib.dbs_lookahead_bands(128, 3) == 0      # one phase-3 tile
-    assert lib.dbs_lookahead_bands(200, 1) == 1
-    assert lib.dbs_lookahead_bands(500, 64) == 1
+    assert lib.dbs_lookahead_bands(200, 1) == 0       # 3 tiles: bulk shorter than a strip
+    assert lib.dbs_lookahead_bands(1024, 1) == 0      # 36 tiles
+    assert lib.dbs_lookahead_bands(500, 64) == 0      # 448 panel workgroups fill the chip
+    assert lib.dbs_lookahead_bands(2944, 1) == 1      # 276 tiles, 45 panel workgroups
     assert lib.dbs_lookahead_bands(4096, 1) == 1
+    assert lib.dbs_lookahead_bands(4096, 4) == 2      # 2112 tiles x molecules
     assert lib.dbs_lookahead_bands(12288, 1) == 2
     assert lib.dbs_lookahead_bands(0, 1) == -1 and lib.dbs_lookahead_bands(5, 0) == -1
     assert dgb.lookahead_bands(12288) == 2
+
+
+def test_set_lookahead_overrides_the_choice():
+    lib = dgb.lib()
+    dgb.set_lookahead(2)
+    try:
+        assert dgb.lookahead_bands(200) == 2 and dgb.lookahead_bands(4096) == 2
+        assert dgb.lookahead_bands(64) == 0 and dgb.lookahead_bands(128, 3) == 0  # nothing to run ahead
+        dgb.set_lookahead(0)
+        assert dgb.lookahead_bands(12288) == 0
+        assert lib.dbs_set_lookahead(3) == -1 and lib.dbs_set_lookahead(-2) == -1  # DBS_EINVAL
+        assert dgb.lookahead_bands(12288) == 0                                     # unchanged
+        with pytest.raises(ValueError):
+            dgb.set_lookahead(7)
+    finally:
+        dgb.set_lookahead(-1)
+    assert dgb.lookahead_bands(12288) == 2 and dgb.lookahead_bands(200) == 0

@@ -107,6 +107,39 @@ def test_full_pass_multi_tile(n):
         assert_bits(Ug, Lg, Ue, Le, f"{algo} n={n}")
 
 
+@pytest.fixture
+def restore_lookahead():
+    yield
+    dgb.set_lookahead(-1)
+
+
+@pytest.mark.parametrize("bands", [0, 1, 2])
+@pytest.mark.parametrize("n,batch", [(129, 2), (300, 1), (385, 2), (700, 1)])
+def test_every_lookahead_depth(n, batch, bands, restore_lookahead):
+    # the automatic choice runs these sizes without a second stream; forcing
+    # each depth covers the one- and two-band schedules at small sizes, on the
+    # dense, directed and packed passes and on ranges of whole k-blocks
+    from oracle import steps
+    U0, L0 = sound_input(n, batch, seed=31 * n + bands)
+    Ue, Le = oracle.smooth(U0, L0)
+    dgb.set_lookahead(bands)
+    assert dgb.lookahead_bands(n, batch) == bands
+    Ug, Lg = gpu_pass(U0, L0, "blocked")
+    assert_bits(Ug, Lg, Ue, Le, f"blocked n={n} batch={batch} bands={bands}")
+    U, L = dev(U0), dev(L0)
+    dgb.smooth_directed(U, L, algo="blocked")
+    assert_bits(host(U), host(L), Ue, Le, f"directed n={n} bands={bands}")
+    P = dgb.pack(dev(U0), dev(L0))
+    dgb.smooth_packed(P)
+    assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32))
+    U, L = dev(U0), dev(L0)
+    Ur, Lr = oracle.rounds(U0, L0, 0, 128)
+    dgb.smooth_range(U, L, 0, 128, algo="blocked")
+    assert_bits(host(U), host(L), Ur, Lr, f"range 0..128 n={n} bands={bands}")
+    dgb.smooth_range(U, L, 128, n, algo="blocked")
+    assert_bits(host(U), host(L), Ue, Le, f"range 128..n n={n} bands={bands}")
+
+
 def test_walk_molecules_batched():
     W = gen.make_workload("b64n500", batch=5)
     Ue, Le = oracle.smooth(W.U, W.L)
