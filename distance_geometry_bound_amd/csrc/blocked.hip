@@ -13,9 +13,9 @@
 //            the diagonal tile's rows (phases 1 and 2 run together in
 //            k_diag_panel, one workgroup per panel tile);
 //   phase 3  every remaining cell: all bK rounds at once from the finished
-//            panel (k_blocks: the bulk on 64x64 quadrants, and band K+1
-//            alone when running ahead).  This is where 1 - O(BK/n) of the
-//            work is.
+//            panel (k_quads / k_quads_packed: the bulk on 64x64 quadrants;
+//            k_strip: one band alone when running ahead).  This is where
+//            1 - O(BK/n) of the work is.
 //
 // Symmetric schedule.  U and L stay exactly symmetric, so only the cells of
 // TILE x TILE tiles (I,J) with I <= J are kept current ("fresh"); tiles below
@@ -447,31 +447,21 @@ __device__ __forceinline__ void store_transposed(float *P, int64_t n, int64_t r0
 // run of tiles instead makes it sweep every row slice of the panel, and is
 // slower.)
 
-// Phase 3 on BK x BK blocks, thread (ty, tx) owning a 4x4 cell tile;
-// grid.y = molecules.  Two uses:
-//  * bulk (BULK): every fresh cell outside band K and the bands
-//    starting at s1 and s2, as the four BK x BK quadrants of each upper
-//    TILE x TILE tile (grid.x = 4 T(T+1)/2).  Band K is final after phase 2;
-//    bands s1 and s2 (the next two k-blocks' bands; < 0 for none) are
-//    updated ahead on the other stream.  A quadrant in any of them is
-//    skipped whole (quadrants and bands are both BK wide): it is neither
-//    read nor written, and the panel columns of bands s1 and s2 are not
-//    read, since the other stream may be updating exactly those cells while
-//    this launch runs.
-//  * strip (!BULK): the row band starting at s1 only, run ahead of the
-//    bulk on the second stream.  grid.x = the k-block tiles J other than K
-//    and the band starting at s2 (< 0 for none); block (s1 / BK, J) is kept
-//    in its fresh orientation.
-// The panel rows of band K are staged through LDS in chunks of KC atoms; the
-// global loads of chunk c+1 are issued before chunk c is computed.  Per atom
-// and cell the VALU does one add and one min for U, two subtracts and two max
-// for L; pairs of atoms fold into 3-input min/max (4.5 instructions per cell
-// and atom).  16 waves per CU (4 workgroups, dense bulk) keep the VALU busy through the
-// LDS and global latencies.
-template <bool VEC, bool PK, bool RU, bool BULK>
-__global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, float *__restrict__ L,
-                                                     int64_t n, int64_t batch, int64_t K,
-                                                     int64_t s1, int64_t s2) {
+// Phase 3 of block K on one row band, run ahead of the bulk on the second
+// stream: the row band starting at s1, every column band J other than K and
+// the band starting at s2 (< 0 for none); grid.x = those J, grid.y =
+// molecules.  Block (s1 / BK, J) is read and written in its fresh
+// orientation (dense) or as its U and L slots (packed).  Thread (ty, tx)
+// owns a 4x4 cell tile.  The panel rows of band K are staged through LDS in
+// chunks of KC atoms; the global loads of chunk c+1 are issued before chunk
+// c is computed.  Per atom and cell the VALU does one add and one min for U,
+// two subtracts and two max for L; pairs of atoms fold into 3-input min/max
+// (4.5 instructions per cell and atom).  The strip is on the critical path
+// of the look-ahead and raises its waves' issue priority.
+template <bool VEC, bool PK, bool RU>
+__global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float *__restrict__ L,
+                                                    int64_t n, int64_t batch, int64_t K,
+                                                    int64_t s1, int64_t s2) {
   __shared__ float4 scu[KC][BK / 4];
   __shared__ float4 scl[KC][BK / 4];
   __shared__ float4 sru[KC][BK / 4];
@@ -480,31 +470,15 @@ __global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, floa
 
   rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  int64_t A, B;  // row band, column band of the block
-  bool rowor;    // stored as (A, B) (else as its transpose (B, A))
-  if (!BULK) {
-    // row band s1 / BK; every column band but K and s2 / BK (s2 < 0: none)
-    critical_path_priority();
-    A = s1 / BK;
-    const int64_t x = s2 < 0 ? -1 : s2 / BK;
-    const int64_t lo = x < 0 ? K : (x < K ? x : K), hi = x < 0 ? -1 : (x < K ? K : x);
-    B = blockIdx.x;
-    if (B >= lo) ++B;
-    if (hi >= 0 && B >= hi) ++B;
-    rowor = fresh(A, B);
-  } else {
-    const int64_t p = blockIdx.x >> 2, q = blockIdx.x & 3;
-    const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
-    A = RATIO * I2 + (q >> 1);
-    B = RATIO * J2 + (q & 1);
-    rowor = true;  // every quadrant of an upper tile is fresh
-    if (A * BK >= n || B * BK >= n || A == K || B == K || A * BK == s1 || B * BK == s1 ||
-        A * BK == s2 || B * BK == s2)
-      return;  // uniform over the workgroup, before any barrier
-    // packed: the lower-left quadrant of a diagonal tile holds the same
-    // slots as its upper-right one (transposed cells), which covers them
-    if (PK && I2 == J2 && q == 2) return;
-  }
+  critical_path_priority();
+  // row band A = s1 / BK; column band B: every band but K and s2 / BK
+  const int64_t A = s1 / BK;
+  const int64_t x = s2 < 0 ? -1 : s2 / BK;
+  const int64_t lo = x < 0 ? K : (x < K ? x : K), hi = x < 0 ? -1 : (x < K ? K : x);
+  int64_t B = blockIdx.x;
+  if (B >= lo) ++B;
+  if (hi >= 0 && B >= hi) ++B;
+  const bool rowor = fresh(A, B);  // stored as (A, B), else as its transpose (B, A)
   const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
   const int bK = (int)(n - k0 < BK ? n - k0 : BK);
   const int bA = (int)(n - a0 < BK ? n - a0 : BK);
@@ -546,9 +520,12 @@ __global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, floa
     // (U/L[i,k] = U/L[k,i]) and of band B
     auto fetch = [&](int kc, float4 (&st)[4], HalfLoad (&hl)[2]) {
       if (PK) {
-        // band A and band B each lie right or left of band K
-        hl[0] = packed_half_load<VEC>(Ub, n, k0, kc, bK, a0, A > K, false, tid);
-        hl[1] = packed_half_load<VEC>(Ub, n, k0, kc, bK, j0, B > K, false, tid);
+        // band A and band B each lie right or left of band K; the addresses
+        // are re-derived per chunk (laundered thread index), not kept live
+        int tf = tid;
+        asm volatile("" : "+v"(tf));
+        hl[0] = packed_half_load<VEC>(Ub, n, k0, kc, bK, a0, A > K, false, tf);
+        hl[1] = packed_half_load<VEC>(Ub, n, k0, kc, bK, j0, B > K, false, tf);
       } else {
         // KC x BK/4 float4 per array: one of each per thread
         const int kk = tid / (BK / 4), x4 = tid % (BK / 4);
@@ -564,10 +541,12 @@ __global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, floa
     };
     auto stage = [&](const float4 (&st)[4], const HalfLoad (&hl)[2]) {
       if (PK) {
+        int ts = tid;
+        asm volatile("" : "+v"(ts));
         packed_half_store(hl[0], A > K, reinterpret_cast<float *>(&scu[0][0]),
-                          reinterpret_cast<float *>(&scl[0][0]), BK, 0, tid);
+                          reinterpret_cast<float *>(&scl[0][0]), BK, 0, ts);
         packed_half_store(hl[1], B > K, reinterpret_cast<float *>(&sru[0][0]),
-                          reinterpret_cast<float *>(&srl[0][0]), BK, 0, tid);
+                          reinterpret_cast<float *>(&srl[0][0]), BK, 0, ts);
       } else {
         const int kk = tid / (BK / 4), x4 = tid % (BK / 4);
         scu[kk][x4] = st[0];
@@ -636,13 +615,20 @@ __global__ __launch_bounds__(kThreads) void k_blocks(float *__restrict__ U, floa
   }
 }
 
-// Bulk of phase 3 for the dense layout: thread (ty, tx) owns RT x CT cells of
-// a BK x BK quadrant (rows a0 + RT*ty + r, columns j0 + CT*tx + q).  Same
-// quadrants, skips, staging (KCH atoms per chunk, next chunk prefetched) and
-// row-segment write-back as the bulk mode of k_blocks, without its layout
-// and mode switches.  Larger tiles read fewer staged operand floats per cell
-// (the LDS return traffic limits the 4x4 tile) but lose occupancy; 4x4 is
-// the fastest measured (kBulkRT below).
+// Bulk of phase 3 for the dense layout: every fresh cell outside band K and
+// the bands starting at s1 and s2, as the four BK x BK quadrants of each
+// upper TILE x TILE tile (grid.x = 4 T(T+1)/2, grid.y = molecules).  Band K
+// is final after phase 2; bands s1 and s2 (the next two k-blocks' bands; < 0
+// for none) are updated ahead on the other stream.  A quadrant in any of them
+// is skipped whole (quadrants and bands are both BK wide): it is neither read
+// nor written, and the panel columns of bands s1 and s2 are not read, since
+// the other stream may be updating exactly those cells while this launch
+// runs.  Thread (ty, tx) owns RT x CT cells (rows a0 + RT*ty + r, columns
+// j0 + CT*tx + q).  The panel rows of band K are staged through LDS, KCH
+// atoms per chunk with the next chunk's loads in flight; the quadrant is
+// written back as row segments.  Larger tiles read fewer staged operand
+// floats per cell but lose occupancy; 4x4 is the fastest measured (kBulkRT
+// below).
 template <bool VEC, bool RU, int RT, int CT, int KCH>
 __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restrict__ U,
                                                                  float *__restrict__ L,
@@ -790,6 +776,131 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
   }
 }
 
+// Bulk of phase 3 for the packed layout (one buffer P: U above the diagonal,
+// L below), 4x4 cells per thread on the same quadrants as k_quads; the
+// lower-left quadrant of a diagonal tile is left out, since its slots are the
+// upper-right one's.  An off-diagonal quadrant (a0 < j0) reads its U as row
+// segments P[a0+a][j0..] and its L as column segments P[j0+c][a0..] (float4
+// along a, turned around in registers), and writes them back the same way,
+// the L half through an LDS tile so that the global writes are row segments.
+// A diagonal quadrant decides per cell.  The panel rows of band K lie right
+// or left of the diagonal, so each staged half is a row segment of P and a
+// column segment read four atoms per float4 (packed_half_load).
+template <bool VEC, bool RU>
+__global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P, int64_t n,
+                                                           int64_t batch, int64_t K, int64_t s1,
+                                                           int64_t s2) {
+  __shared__ float4 scu[KC][BK / 4];
+  __shared__ float4 scl[KC][BK / 4];
+  __shared__ float4 sru[KC][BK / 4];
+  __shared__ float4 srl[KC][BK / 4];
+  __shared__ float tr[BK][BK + 1];  // write-back of the L half
+
+  rounding_prologue<RU>();
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int64_t p = blockIdx.x >> 2, qd = blockIdx.x & 3;
+  const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
+  const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
+  if (A * BK >= n || B * BK >= n || A == K || B == K || A * BK == s1 || B * BK == s1 ||
+      A * BK == s2 || B * BK == s2 || (I2 == J2 && qd == 2))
+    return;  // uniform over the workgroup, before any barrier
+  const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
+  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int bA = (int)(n - a0 < BK ? n - a0 : BK);
+  const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
+  const bool diag = A == B;  // else A < B: every cell lies above the diagonal
+  const int64_t nn = n * n;
+
+  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    float *Pb = P + b * nn;
+
+    float u[4][4], l[4][4];
+    if (diag) {
+      packed_block_load<VEC>(Pb, n, a0, j0, bA, bJ, ty, tx, u, l);
+    } else {
+      float4 x[4], y[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int a = ty * 4 + r;
+        x[r] = load4<VEC>(Pb + (a0 + a) * n + j0 + tx * 4, a < bA ? clamp4(bJ - tx * 4) : 0,
+                          kInf, Pb);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = tx * 4 + q;
+        y[q] = load4<VEC>(Pb + (j0 + c) * n + a0 + ty * 4, c < bJ ? clamp4(bA - ty * 4) : 0,
+                          0.0f, Pb);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float xr[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) u[r][q] = xr[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float yq[4] = {y[q].x, y[q].y, y[q].z, y[q].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) l[r][q] = yq[r];
+      }
+    }
+
+    // the staging addresses are re-derived per chunk (laundered thread
+    // index) rather than kept live through the k loop
+    HalfLoad hl[2];
+    auto fetch = [&](int kc) {
+      int tf = tid;
+      asm volatile("" : "+v"(tf));
+      hl[0] = packed_half_load<VEC>(Pb, n, k0, kc, bK, a0, A > K, false, tf);
+      hl[1] = packed_half_load<VEC>(Pb, n, k0, kc, bK, j0, B > K, false, tf);
+    };
+    fetch(0);
+    for (int kc = 0; kc < bK; kc += KC) {
+      int ts = tid;
+      asm volatile("" : "+v"(ts));
+      packed_half_store(hl[0], A > K, reinterpret_cast<float *>(&scu[0][0]),
+                        reinterpret_cast<float *>(&scl[0][0]), BK, 0, ts);
+      packed_half_store(hl[1], B > K, reinterpret_cast<float *>(&sru[0][0]),
+                        reinterpret_cast<float *>(&srl[0][0]), BK, 0, ts);
+      __syncthreads();
+      if (kc + KC < bK) fetch(kc + KC);  // in flight during this chunk
+#pragma unroll 2
+      for (int kk = 0; kk < KC; kk += 2) {
+        const float4 a0v = scu[kk][ty], b0 = scl[kk][ty], c0 = sru[kk][tx], d0 = srl[kk][tx];
+        const float4 a1 = scu[kk + 1][ty], b1 = scl[kk + 1][ty], c1 = sru[kk + 1][tx],
+                     d1 = srl[kk + 1][tx];
+        const float cu0[4] = {a0v.x, a0v.y, a0v.z, a0v.w}, cl0[4] = {b0.x, b0.y, b0.z, b0.w};
+        const float ru0[4] = {c0.x, c0.y, c0.z, c0.w}, rl0[4] = {d0.x, d0.y, d0.z, d0.w};
+        const float cu1[4] = {a1.x, a1.y, a1.z, a1.w}, cl1[4] = {b1.x, b1.y, b1.z, b1.w};
+        const float ru1[4] = {c1.x, c1.y, c1.z, c1.w}, rl1[4] = {d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            relax2<RU>(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
+                       rl1[q]);
+      }
+      __syncthreads();
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) l[r][q] = lower_out<RU>(l[r][q]);
+    // the write addresses are computed after the k loop, not kept live in it
+    int tw = tid;
+    asm volatile("" : "+v"(tw));
+    const int wy = tw >> 4, wx = tw & 15;
+    if (diag) {
+      packed_block_store(Pb, n, a0, j0, bA, bJ, wy, wx, u, l);
+    } else {
+      store_rows<VEC>(Pb, n, a0, j0, bA, bJ, wy, wx, u);
+      store_transposed<VEC>(Pb, n, a0, j0, bA, bJ, wy, wx, l, tr);
+    }
+    __syncthreads();  // tr and the staging arrays are reused by the next molecule
+  }
+}
+
 // The dense bulk's register tile.
 // (measured at n12288, bulk launch: 4x4 419 us at 4 workgroups per CU; 4x8
 // and 8x4 with 8-atom chunks 422-428 us at 3; 4x8, 8x4 with 16-atom chunks
@@ -898,8 +1009,9 @@ int lookahead_bands(int64_t n, int64_t batch, bool packed) {
   if (forced >= 0) return forced;
   const int64_t tiles = T * (T + 1) / 2 * batch;
   if (tiles >= kDeepTiles) return 2;
-  // the packed bulk runs at 3 workgroups per CU and is slow enough to hide
-  // even a panel launch that fills the chip
+  // the packed layout's phase 1-2 kernel is slower (packed loads and
+  // stores), and gains from running beside the bulk even where its launch
+  // fills the chip
   if (tiles < kAheadTiles || (!packed && (TB - 1) * batch > kPanelFill)) return 0;
   return 1;
 }
@@ -929,20 +1041,19 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   const unsigned gy = (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ);
   const int64_t nn = n * n;
   if (packed) L = U;
-#define DBS_PICK(K, X)                                                                     \
-  (packed ? (ru ? (vec ? K<true, true, true, X> : K<false, true, true, X>)                 \
-                : (vec ? K<true, true, false, X> : K<false, true, false, X>))              \
-          : (ru ? (vec ? K<true, false, true, X> : K<false, false, true, X>)               \
-                : (vec ? K<true, false, false, X> : K<false, false, false, X>)))
-  auto bulk_kernel = DBS_PICK(k_blocks, true);
+  auto packed_kernel = ru ? (vec ? k_quads_packed<true, true> : k_quads_packed<false, true>)
+                          : (vec ? k_quads_packed<true, false> : k_quads_packed<false, false>);
   // the dense bulk runs with larger register tiles
   auto quads_kernel = ru ? (vec ? k_quads<true, true, kBulkRT, kBulkCT, kBulkKC>
                                 : k_quads<false, true, kBulkRT, kBulkCT, kBulkKC>)
                          : (vec ? k_quads<true, false, kBulkRT, kBulkCT, kBulkKC>
                                 : k_quads<false, false, kBulkRT, kBulkCT, kBulkKC>);
   constexpr unsigned quads_block = (BK / kBulkRT) * (BK / kBulkCT);
-  auto strip_kernel = DBS_PICK(k_blocks, false);
-#undef DBS_PICK
+  auto strip_kernel =
+      packed ? (ru ? (vec ? k_strip<true, true, true> : k_strip<false, true, true>)
+                   : (vec ? k_strip<true, true, false> : k_strip<false, true, false>))
+             : (ru ? (vec ? k_strip<true, false, true> : k_strip<false, false, true>)
+                   : (vec ? k_strip<true, false, false> : k_strip<false, false, false>));
   // With many phase-3 tiles the bulk runs long enough to hide phases 1-2 of
   // the next blocks: they run two bands ahead, on 256-thread workgroups that
   // fit where phase-3 workgroups finish.  With few tiles they are the
@@ -973,8 +1084,8 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
     if (!packed)
       return launch(prof, kProfTiles, quads_kernel, dim3((unsigned)(4 * pairs), gy),
                     dim3(quads_block), st, U, L, n, batch, K, s1, s2);
-    return launch(prof, kProfTiles, bulk_kernel, dim3((unsigned)(4 * pairs), gy), dim3(kThreads),
-                  st, U, L, n, batch, K, s1, s2);
+    return launch(prof, kProfTiles, packed_kernel, dim3((unsigned)(4 * pairs), gy),
+                  dim3(kThreads), st, U, n, batch, K, s1, s2);
   };
 
   hipError_t e = phase12(K0, s);
