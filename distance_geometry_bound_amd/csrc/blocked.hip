@@ -1016,8 +1016,10 @@ int lookahead_bands(int64_t n, int64_t batch, bool packed) {
   return 1;
 }
 
-// Enqueue one pass.  With more than one k-block the pass runs ahead on a
-// second stream, by two bands when there are many phase-3 tiles.  Per k-block
+// Enqueue one pass.  With more than one k-block the pass may run ahead on a
+// second stream (lookahead_bands: by two bands when there are many phase-3
+// tiles, one band for a mid-sized bulk, none when the bulk is too short to
+// hide a band strip or the phase 1-2 launch fills the chip).  Per k-block
 // K the caller's stream runs bulk(K): phase 3 of block K on everything but
 // band K and the bands run ahead.  Two bands ahead, the side stream runs
 // phase 3 of block K on band K+1 (strip), phases 1-2 of block K+1, then
@@ -1056,9 +1058,9 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
                    : (vec ? k_strip<true, false, false> : k_strip<false, false, false>));
   // With many phase-3 tiles the bulk runs long enough to hide phases 1-2 of
   // the next blocks: they run two bands ahead, on 256-thread workgroups that
-  // fit where phase-3 workgroups finish.  With few tiles they are the
-  // critical path: one band ahead, on 1024-thread workgroups that hide the
-  // latency of their rounds best.
+  // fit where phase-3 workgroups finish.  With fewer tiles they are the
+  // critical path: one band ahead or none, on 1024-thread workgroups that
+  // hide the latency of their rounds best.
   const int64_t pairs = T * (T + 1) / 2;
   const int ahead = lookahead_bands(n, batch, packed);
   const bool deep = ahead == 2;
