@@ -636,7 +636,11 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
                                                                  int64_t K, int64_t s1,
                                                                  int64_t s2) {
   constexpr int NTX = BK / CT, NT = (BK / RT) * NTX;
-  constexpr int RQ = RT / 4, CQ = CT / 4;            // float4 per row / column group
+  // operands and cells move as vectors of RW rows / CW columns (4, or 2 for
+  // 2-wide tiles)
+  constexpr int RW = RT < 4 ? RT : 4, CW = CT < 4 ? CT : 4;
+  constexpr int RQ = RT / RW, CQ = CT / CW;
+  static_assert(RW % 2 == 0 && CW % 2 == 0 && RT % RW == 0 && CT % CW == 0, "tile shape");
   constexpr int ITER = KCH * (BK / 4) / NT;          // staged float4 per thread and array
   static_assert(ITER >= 1 && KCH * (BK / 4) % NT == 0, "staging split");
   __shared__ float4 scu[KCH][BK / 4];
@@ -664,26 +668,26 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
 
     float u[RT][CT], l[RT][CT];
     {
-      float4 x[RT][CQ], y[RT][CQ];
+      Seg<CW> x[RT][CQ], y[RT][CQ];
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int h = 0; h < CQ; ++h) {
-          const int a = ty * RT + r, c = tx * CT + 4 * h;
-          const int cnt = a < bA ? clamp4(bJ - c) : 0;
+          const int a = ty * RT + r, c = tx * CT + CW * h;
+          const int64_t left = a < bA ? bJ - c : 0;
           const int64_t g = (a0 + a) * n + j0 + c;
-          x[r][h] = load4<VEC>(Ub + g, cnt, kInf, Ub);
-          y[r][h] = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+          x[r][h] = load_seg<VEC, CW>(Ub + g, left, kInf, Ub);
+          y[r][h] = load_seg<VEC, CW>(Lb + g, left, 0.0f, Lb);
         }
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int h = 0; h < CQ; ++h) {
-          u[r][4 * h + 0] = x[r][h].x; u[r][4 * h + 1] = x[r][h].y;
-          u[r][4 * h + 2] = x[r][h].z; u[r][4 * h + 3] = x[r][h].w;
-          l[r][4 * h + 0] = y[r][h].x; l[r][4 * h + 1] = y[r][h].y;
-          l[r][4 * h + 2] = y[r][h].z; l[r][4 * h + 3] = y[r][h].w;
-        }
+        for (int h = 0; h < CQ; ++h)
+#pragma unroll
+          for (int i = 0; i < CW; ++i) {
+            u[r][CW * h + i] = x[r][h].v[i];
+            l[r][CW * h + i] = y[r][h].v[i];
+          }
     }
 
     float4 st[ITER][4];
@@ -716,23 +720,31 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
 #pragma unroll 2
       for (int kk = 0; kk < KCH; kk += 2) {
         float cu0[RT], cl0[RT], cu1[RT], cl1[RT], ru0[CT], rl0[CT], ru1[CT], rl1[CT];
+        // W consecutive staged floats of atom row kk starting at float index i0
+        auto vec = [&](float4 (*arr)[BK / 4], int kr, int i0, int W, float *out) {
+          if (W == 4) {
+            const float4 v = arr[kr][i0 / 4];
+            out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+          } else {
+            const float2 v = reinterpret_cast<const float2 *>(&arr[kr][0])[i0 / 2];
+            out[0] = v.x; out[1] = v.y;
+          }
+        };
 #pragma unroll
         for (int h = 0; h < RQ; ++h) {
-          const float4 a = scu[kk][RQ * ty + h], bb = scl[kk][RQ * ty + h];
-          const float4 c = scu[kk + 1][RQ * ty + h], d = scl[kk + 1][RQ * ty + h];
-          cu0[4 * h] = a.x; cu0[4 * h + 1] = a.y; cu0[4 * h + 2] = a.z; cu0[4 * h + 3] = a.w;
-          cl0[4 * h] = bb.x; cl0[4 * h + 1] = bb.y; cl0[4 * h + 2] = bb.z; cl0[4 * h + 3] = bb.w;
-          cu1[4 * h] = c.x; cu1[4 * h + 1] = c.y; cu1[4 * h + 2] = c.z; cu1[4 * h + 3] = c.w;
-          cl1[4 * h] = d.x; cl1[4 * h + 1] = d.y; cl1[4 * h + 2] = d.z; cl1[4 * h + 3] = d.w;
+          const int i0 = RT * ty + RW * h;
+          vec(scu, kk, i0, RW, cu0 + RW * h);
+          vec(scl, kk, i0, RW, cl0 + RW * h);
+          vec(scu, kk + 1, i0, RW, cu1 + RW * h);
+          vec(scl, kk + 1, i0, RW, cl1 + RW * h);
         }
 #pragma unroll
         for (int h = 0; h < CQ; ++h) {
-          const float4 a = sru[kk][CQ * tx + h], bb = srl[kk][CQ * tx + h];
-          const float4 c = sru[kk + 1][CQ * tx + h], d = srl[kk + 1][CQ * tx + h];
-          ru0[4 * h] = a.x; ru0[4 * h + 1] = a.y; ru0[4 * h + 2] = a.z; ru0[4 * h + 3] = a.w;
-          rl0[4 * h] = bb.x; rl0[4 * h + 1] = bb.y; rl0[4 * h + 2] = bb.z; rl0[4 * h + 3] = bb.w;
-          ru1[4 * h] = c.x; ru1[4 * h + 1] = c.y; ru1[4 * h + 2] = c.z; ru1[4 * h + 3] = c.w;
-          rl1[4 * h] = d.x; rl1[4 * h + 1] = d.y; rl1[4 * h + 2] = d.z; rl1[4 * h + 3] = d.w;
+          const int i0 = CT * tx + CW * h;
+          vec(sru, kk, i0, CW, ru0 + CW * h);
+          vec(srl, kk, i0, CW, rl0 + CW * h);
+          vec(sru, kk + 1, i0, CW, ru1 + CW * h);
+          vec(srl, kk + 1, i0, CW, rl1 + CW * h);
         }
 #pragma unroll
         for (int r = 0; r < RT; ++r)
@@ -744,7 +756,7 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
       __syncthreads();
     }
 
-    // write-back, one float4 per row group
+    // write-back, one CW-float vector per row group
     int tw = tid;
     asm volatile("" : "+v"(tw));
     const int wy = tw / NTX, wx = tw % NTX;
@@ -754,19 +766,27 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
       if (a >= bA) continue;
 #pragma unroll
       for (int h = 0; h < CQ; ++h) {
-        const int c = wx * CT + 4 * h;
+        const int c = wx * CT + CW * h;
         float *pu = Ub + (a0 + a) * n + j0 + c, *pl = Lb + (a0 + a) * n + j0 + c;
-        const float lv[4] = {lower_out<RU>(l[r][4 * h]), lower_out<RU>(l[r][4 * h + 1]),
-                             lower_out<RU>(l[r][4 * h + 2]), lower_out<RU>(l[r][4 * h + 3])};
-        if (VEC && c + 3 < bJ) {
-          *reinterpret_cast<float4 *>(pu) =
-              make_float4(u[r][4 * h], u[r][4 * h + 1], u[r][4 * h + 2], u[r][4 * h + 3]);
-          *reinterpret_cast<float4 *>(pl) = make_float4(lv[0], lv[1], lv[2], lv[3]);
+        float uv[CW], lv[CW];
+#pragma unroll
+        for (int i = 0; i < CW; ++i) {
+          uv[i] = u[r][CW * h + i];
+          lv[i] = lower_out<RU>(l[r][CW * h + i]);
+        }
+        if (VEC && c + CW - 1 < bJ) {
+          if constexpr (CW == 4) {
+            *reinterpret_cast<float4 *>(pu) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+            *reinterpret_cast<float4 *>(pl) = make_float4(lv[0], lv[1], lv[2], lv[3]);
+          } else {
+            *reinterpret_cast<float2 *>(pu) = make_float2(uv[0], uv[1]);
+            *reinterpret_cast<float2 *>(pl) = make_float2(lv[0], lv[1]);
+          }
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < CW; ++i)
             if (c + i < bJ) {
-              pu[i] = u[r][4 * h + i];
+              pu[i] = uv[i];
               pl[i] = lv[i];
             }
         }
@@ -906,6 +926,12 @@ __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P
 // and 8x4 with 8-atom chunks 422-428 us at 3; 4x8, 8x4 with 16-atom chunks
 // 484-494 us at 2; 8x8 needs more than 256 VGPRs)
 constexpr int kBulkRT = 4, kBulkCT = 4, kBulkKC = 16;
+// A bulk launch with fewer quadrant workgroups than CUs (small n, one
+// stream) is latency-bound: there each quadrant takes 512 threads with 4x2
+// cells (measured at n1024, bulk launch: 4x4 17.3 us, 2x2 15.6 us with the
+// whole k-block staged at once, 2x4 13.3 us, 4x2 13.2 us).
+constexpr int kSmallRT = 4, kSmallCT = 2, kSmallKC = 32;
+constexpr int64_t kSmallGrid = 256;
 
 // ---------------------------------------------------------------- mirror
 // grid.x = TB*TB k-block tiles (a = x / TB, b = x % TB), grid.y = molecules.
@@ -1046,11 +1072,11 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   auto packed_kernel = ru ? (vec ? k_quads_packed<true, true> : k_quads_packed<false, true>)
                           : (vec ? k_quads_packed<true, false> : k_quads_packed<false, false>);
   // the dense bulk runs with larger register tiles
-  auto quads_kernel = ru ? (vec ? k_quads<true, true, kBulkRT, kBulkCT, kBulkKC>
-                                : k_quads<false, true, kBulkRT, kBulkCT, kBulkKC>)
-                         : (vec ? k_quads<true, false, kBulkRT, kBulkCT, kBulkKC>
-                                : k_quads<false, false, kBulkRT, kBulkCT, kBulkKC>);
-  constexpr unsigned quads_block = (BK / kBulkRT) * (BK / kBulkCT);
+#define DBS_QUADS(R, C, KC)                                                                  \
+  (ru ? (vec ? k_quads<true, true, R, C, KC> : k_quads<false, true, R, C, KC>)                \
+      : (vec ? k_quads<true, false, R, C, KC> : k_quads<false, false, R, C, KC>))
+  auto quads_kernel = DBS_QUADS(kBulkRT, kBulkCT, kBulkKC);
+  unsigned quads_block = (BK / kBulkRT) * (BK / kBulkCT);
   auto strip_kernel =
       packed ? (ru ? (vec ? k_strip<true, true, true> : k_strip<false, true, true>)
                    : (vec ? k_strip<true, true, false> : k_strip<false, true, false>))
@@ -1064,6 +1090,11 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   const int64_t pairs = T * (T + 1) / 2;
   const int ahead = lookahead_bands(n, batch, packed);
   const bool deep = ahead == 2;
+  if (ahead == 0 && 4 * pairs * batch <= kSmallGrid) {
+    quads_kernel = DBS_QUADS(kSmallRT, kSmallCT, kSmallKC);
+    quads_block = (BK / kSmallRT) * (BK / kSmallCT);
+  }
+#undef DBS_QUADS
 #define DBS_PICK_PANEL(S)                                                                   \
   (packed ? (ru ? (vec ? k_diag_panel<true, true, true, S> : k_diag_panel<false, true, true, S>)   \
                 : (vec ? k_diag_panel<true, true, false, S> : k_diag_panel<false, true, false, S>)) \
