@@ -988,6 +988,13 @@ hipStream_t side_stream() {
 // Ordering events of the lookahead: one set per host thread and device,
 // created on first use and re-recorded by every pass (a stream wait captures
 // the event's state when it is enqueued, so re-recording is safe).
+// The events only order the two streams of one device: the kernels they
+// follow end with a device-scope release and the kernels that wait on them
+// start with an acquire, so the event needs no timing and no system-scope
+// fence of its own (which writes back the caches and costs about 11 us per
+// hop between the streams).
+constexpr unsigned kOrderingEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
+
 struct Events {
   // start: phases 1-2 of the first block; bulk[K & 1]: bulk(K) done;
   // ready[K & 1]: the side stream's work that bulk(K) needs is done
@@ -999,7 +1006,7 @@ struct Events {
   bool init() {
     if (created) return true;
     for (auto &x : e)
-      if (!x && hipEventCreateWithFlags(&x, hipEventDisableTiming) != hipSuccess) return false;
+      if (!x && hipEventCreateWithFlags(&x, kOrderingEventFlags) != hipSuccess) return false;
     created = true;
     return true;
   }
