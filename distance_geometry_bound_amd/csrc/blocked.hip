@@ -26,7 +26,8 @@
 // from whichever orientation is fresh and writes both orientations.
 //
 // Phase 3: a 256-thread workgroup owns a 64x64 block, each thread a 4x4
-// register tile; the panel rows of the k-block are staged through LDS.  No
+// register tile (512 threads with 4x2 tiles when a launch has fewer blocks
+// than CUs); the panel rows of the k-block are staged through LDS.  No
 // matrix cores: min-plus is not a multiply-add contraction.
 #include <atomic>
 #include <mutex>
