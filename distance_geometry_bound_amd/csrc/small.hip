@@ -62,14 +62,29 @@ __global__ __launch_bounds__(1024) void k_small(float *U, float *L, int64_t ld, 
     float *Lb = L + b * mstride + off;
     float u[4][4], l[4][4];
     if (active) {
+      // element offsets from the row starts of the tile's rows and columns
+      // (packed: U of (i,j) at row min(i,j), L at row max(i,j)); they fit
+      // 32 bits (the launcher checks m * ld).  The tile corner is laundered
+      // so that the offsets are formed per molecule, not hoisted out of the
+      // molecule loop and kept live.
+      int li0 = i0, lj0 = j0;
+      asm volatile("" : "+v"(li0), "+v"(lj0));
+      int ib[4], jb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ib[q] = (li0 + q) * (int)ld;
+        jb[q] = (lj0 + q) * (int)ld;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int i = i0 + r, j = j0 + c;
+          const int i = li0 + r, j = lj0 + c;
           const bool in = i < m && j < m;
-          u[r][c] = in ? Ub[Cell<PK>::u(i, j, ld)] : kInf;
-          l[r][c] = in ? Lb[Cell<PK>::l(i, j, ld)] : 0.0f;
+          const int gu = !PK || i < j ? ib[r] + j : jb[c] + i;
+          const int gl = !PK || i > j ? ib[r] + j : jb[c] + i;
+          u[r][c] = in ? Ub[gu] : kInf;
+          l[r][c] = in ? Lb[gl] : 0.0f;
         }
     }
 
@@ -106,25 +121,35 @@ __global__ __launch_bounds__(1024) void k_small(float *U, float *L, int64_t ld, 
     }
 
     if (active) {
+      // the store offsets are re-derived here (laundered tile corner), not
+      // kept live through the rounds
+      int wi0 = i0, wj0 = j0;
+      asm volatile("" : "+v"(wi0), "+v"(wj0));
+      int ib[4], jb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ib[q] = (wi0 + q) * (int)ld;
+        jb[q] = (wj0 + q) * (int)ld;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int i = i0 + r, j = j0 + c;
+          const int i = wi0 + r, j = wj0 + c;
           l[r][c] = lower_out<RU>(l[r][c]);
           if (PK) {
             // one slot each for U(i,j) and L(i,j); a diagonal tile holds both
             // (i,j) and (j,i) with the same values, the diagonal stays 0
             if (i < m && j < m && i != j) {
-              Ub[Cell<PK>::u(i, j, ld)] = u[r][c];
-              Lb[Cell<PK>::l(i, j, ld)] = l[r][c];
+              Ub[i < j ? ib[r] + j : jb[c] + i] = u[r][c];
+              Lb[i > j ? ib[r] + j : jb[c] + i] = l[r][c];
             }
           } else if (i < m && j < m) {
-            Ub[(int64_t)i * ld + j] = u[r][c];
-            Lb[(int64_t)i * ld + j] = l[r][c];
-            if (ty != tx) {
-              Ub[(int64_t)j * ld + i] = u[r][c];
-              Lb[(int64_t)j * ld + i] = l[r][c];
+            Ub[ib[r] + j] = u[r][c];
+            Lb[ib[r] + j] = l[r][c];
+            if (wi0 != wj0) {
+              Ub[jb[c] + i] = u[r][c];
+              Lb[jb[c] + i] = l[r][c];
             }
           }
         }
@@ -141,6 +166,8 @@ hipError_t launch_small_block(float *U, float *L, int64_t ld, int64_t mstride, i
                               int m, int k_lo, int k_hi, int64_t batch, hipStream_t s,
                               Prof *prof, unsigned flags) {
   if (m <= 1 || k_lo >= k_hi) return hipSuccess;
+  // the kernel's element offsets within a molecule are 32-bit
+  if ((int64_t)m * (ld + 1) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int G = (m + 3) / 4;
   const int tiles = G * (G + 1) / 2;
   const int threads = (tiles + 63) / 64 * 64;
