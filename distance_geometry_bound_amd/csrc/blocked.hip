@@ -405,6 +405,22 @@ __device__ __forceinline__ void store_rows(float *P, int64_t n, int64_t r0, int6
   }
 }
 
+// A diagonal block of the packed layout (r0 == c0) holds both (a, c) and
+// (c, a), so its row segments alone cover every slot once: U of the cells
+// right of the diagonal, L of those left of it and U on it (the relaxed value
+// that the dense layout stores there).
+template <bool VEC>
+__device__ __forceinline__ void store_packed_diagonal(float *P, int64_t n, int64_t r0, int rows,
+                                                      int ty, int tx, const float (&u)[4][4],
+                                                      const float (&l)[4][4]) {
+  float v[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[r][q] = ty * 4 + r > tx * 4 + q ? l[r][q] : u[r][q];
+  store_rows<VEC>(P, n, r0, r0, rows, rows, ty, tx, v);
+}
+
 // The same cells to their transposed position P[c0 + 4tx + q][r0 + 4ty + r].
 // The block is turned around in the LDS tile `tr` first (stride BK + 1: the
 // writes meet at most 8 threads on a bank, the reads 2), so that the global
@@ -594,8 +610,7 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
     asm volatile("" : "+v"(tw));
     const int wy = tw >> 4, wx = tw & 15;
     if (PK && a0 == j0) {
-      // diagonal block: per cell, the diagonal slot untouched
-      packed_block_store(Ub, n, a0, j0, bA, bJ, wy, wx, u, l);
+      store_packed_diagonal<VEC>(Ub, n, a0, bA, wy, wx, u, l);
     } else if (PK) {
       // one side of the diagonal: the row slots hold U right of it, L left
       if (a0 < j0) {
@@ -804,9 +819,11 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
 // segments P[a0+a][j0..] and its L as column segments P[j0+c][a0..] (float4
 // along a, turned around in registers), and writes them back the same way,
 // the L half through an LDS tile so that the global writes are row segments.
-// A diagonal quadrant decides per cell.  The panel rows of band K lie right
-// or left of the diagonal, so each staged half is a row segment of P and a
-// column segment read four atoms per float4 (packed_half_load).
+// A diagonal quadrant loads the same segments, swaps U and L of its cells
+// left of the diagonal, and writes its rows only (they cover both halves).
+// The panel rows of band K lie right or left of the diagonal, so each staged
+// half is a row segment of P and a column segment read four atoms per float4
+// (packed_half_load).
 template <bool VEC, bool RU>
 __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P, int64_t n,
                                                            int64_t batch, int64_t K, int64_t s1,
@@ -836,9 +853,7 @@ __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P
     float *Pb = P + b * nn;
 
     float u[4][4], l[4][4];
-    if (diag) {
-      packed_block_load<VEC>(Pb, n, a0, j0, bA, bJ, ty, tx, u, l);
-    } else {
+    {
       float4 x[4], y[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -864,6 +879,18 @@ __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P
 #pragma unroll
         for (int r = 0; r < 4; ++r) l[r][q] = yq[r];
       }
+    }
+    if (diag) {
+      // left of the diagonal the row segment holds L and the column one U
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (ty * 4 + r > tx * 4 + q) {
+            const float t = u[r][q];
+            u[r][q] = l[r][q];
+            l[r][q] = t;
+          }
     }
 
     // the staging addresses are re-derived per chunk (laundered thread
@@ -913,7 +940,7 @@ __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P
     asm volatile("" : "+v"(tw));
     const int wy = tw >> 4, wx = tw & 15;
     if (diag) {
-      packed_block_store(Pb, n, a0, j0, bA, bJ, wy, wx, u, l);
+      store_packed_diagonal<VEC>(Pb, n, a0, bA, wy, wx, u, l);
     } else {
       store_rows<VEC>(Pb, n, a0, j0, bA, bJ, wy, wx, u);
       store_transposed<VEC>(Pb, n, a0, j0, bA, bJ, wy, wx, l, tr);
