@@ -89,25 +89,29 @@ def copy_calibration():
 def tiles_units_per_pass(n, batch, ahead):
     """(stored, dense) (i,j,k) triples of the bulk phase-3 launches over one pass.
 
-    Launch K runs over the 64x64 quadrants of every TILE x TILE tile with
-    I <= J and stores every cell outside band K (final after phase 2) and
-    the `ahead` bands after it (updated ahead on the second stream; fewer
-    near the end).  `stored` counts those cells x the launch's atoms;
-    `dense` counts the full square of live rows x live columns (the cells
-    below the diagonal follow by symmetry)."""
+    The pass steps over W k-blocks at a time (W = 2 when it runs two steps
+    ahead, else 1).  The launch of the step starting at block K runs the
+    step's atoms over the 64x64 quadrants of every TILE x TILE tile with
+    I <= J and stores every cell outside the step's bands (final after its
+    panel) and the bands of the `ahead` steps after it (updated ahead on the
+    second stream; fewer near the end).  `stored` counts those cells x the
+    launch's atoms; `dense` counts the full square of live rows x live
+    columns (the cells below the diagonal follow by symmetry)."""
     T = -(-n // TILE)
     TB = -(-n // BK)
+    W = 2 if ahead == 2 else 1
     stored = dense = 0
-    for K in range(TB):
-        bands = [(B * BK, min(n, B * BK + BK)) for B in range(K, min(TB, K + 1 + ahead))]
+    for K in range(0, TB, W):
+        end = min(TB, K + W * (1 + ahead))
+        bands = [(B * BK, min(n, B * BK + BK)) for B in range(K, end)]
         r = []
         for I in range(T):
             lo, hi = I * TILE, min(n, I * TILE + TILE)
             r.append(hi - lo - sum(max(0, min(hi, b1) - max(lo, b0)) for b0, b1 in bands))
         S, Q = sum(r), sum(x * x for x in r)
-        bK = min(BK, n - K * BK)
-        stored += (S * S + Q) // 2 * bK
-        dense += S * S * bK
+        atoms = min(n, (K + W) * BK) - K * BK
+        stored += (S * S + Q) // 2 * atoms
+        dense += S * S * atoms
     return stored * batch, dense * batch
 
 

@@ -41,8 +41,10 @@ constexpr int BK = 64;          // atoms per k-block (phases 1 and 2 tile size)
 constexpr int TILE = 128;       // freshness granularity: tiles I <= J are kept current
 constexpr int RATIO = TILE / BK;
 constexpr int KC = 16;          // atoms per LDS chunk in phase 3
-// phase-3 tiles (times molecules) from which the pass runs two bands ahead
-constexpr int64_t kDeepTiles = 2048;
+// Phase-3 tiles (times molecules) from which the pass runs two steps ahead,
+// in steps of two k-blocks (measured crossover: n5120, 820 tiles, one step
+// ahead 8.40 ms, two 8.76 ms; n5632, 990 tiles, 10.56 against 10.41 ms).
+constexpr int64_t kDeepTiles = 960;
 // Below this many phase-3 tiles (times molecules) a bulk launch is too short
 // to hide the band strip that running ahead puts on the critical path.
 constexpr int64_t kAheadTiles = 256;
@@ -464,12 +466,17 @@ __device__ __forceinline__ void store_transposed(float *P, int64_t n, int64_t r0
 // run of tiles instead makes it sweep every row slice of the panel, and is
 // slower.)
 
-// Phase 3 of block K on one row band, run ahead of the bulk on the second
-// stream: the row band starting at s1, every column band J other than K and
-// the band starting at s2 (< 0 for none); grid.x = those J, grid.y =
-// molecules.  Block (s1 / BK, J) is read and written in its fresh
-// orientation (dense) or as its U and L slots (packed).  Thread (ty, tx)
-// owns a 4x4 cell tile.  The panel rows of band K are staged through LDS in
+// Phase 3 of the k-blocks K .. K+nk-1 (their atoms in order) on one or two
+// row bands, run ahead of the bulk on the second stream.  Row band A0 takes
+// every column band outside [X0, X1); a second row band A0+1 (grid.z = 2)
+// also leaves out band X1, which is A0 where a second row band is asked for
+// (block (A0+1, A0) is block (A0, A0+1) of the first row band).  [X0, X1)
+// holds the atoms' own bands, whose rows are final.  grid.x = the first row
+// band's column bands, grid.y = molecules.  Block (A, J) is read and
+// written in its fresh orientation (dense) or as its U and L slots (packed);
+// with `both` (dense) its other orientation is written too, so that the
+// rows of band A can serve as a panel afterwards.  Thread (ty, tx) owns a
+// 4x4 cell tile.  The panel rows of the atoms are staged through LDS in
 // chunks of KC atoms; the global loads of chunk c+1 are issued before chunk
 // c is computed.  Per atom and cell the VALU does one add and one min for U,
 // two subtracts and two max for L; pairs of atoms fold into 3-input min/max
@@ -478,7 +485,8 @@ __device__ __forceinline__ void store_transposed(float *P, int64_t n, int64_t r0
 template <bool VEC, bool PK, bool RU>
 __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float *__restrict__ L,
                                                     int64_t n, int64_t batch, int64_t K,
-                                                    int64_t s1, int64_t s2) {
+                                                    int64_t nk, int64_t A0, int64_t X0,
+                                                    int64_t X1, int both) {
   __shared__ float4 scu[KC][BK / 4];
   __shared__ float4 scl[KC][BK / 4];
   __shared__ float4 sru[KC][BK / 4];
@@ -488,16 +496,16 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
   rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   critical_path_priority();
-  // row band A = s1 / BK; column band B: every band but K and s2 / BK
-  const int64_t A = s1 / BK;
-  const int64_t x = s2 < 0 ? -1 : s2 / BK;
-  const int64_t lo = x < 0 ? K : (x < K ? x : K), hi = x < 0 ? -1 : (x < K ? K : x);
+  // row band A = A0 + blockIdx.z; column band B: the blockIdx.x-th band
+  // outside [X0, X1 + blockIdx.z)
+  const int64_t TB = (n + BK - 1) / BK, A = A0 + blockIdx.z;
+  const int64_t xe = X1 + blockIdx.z < TB ? X1 + blockIdx.z : TB;
   int64_t B = blockIdx.x;
-  if (B >= lo) ++B;
-  if (hi >= 0 && B >= hi) ++B;
+  if (B >= TB - (xe - X0)) return;  // uniform, before any barrier
+  if (B >= X0) B += xe - X0;
   const bool rowor = fresh(A, B);  // stored as (A, B), else as its transpose (B, A)
   const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
-  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int bK = (int)(n - k0 < nk * BK ? n - k0 : nk * BK);
   const int bA = (int)(n - a0 < BK ? n - a0 : BK);
   const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
   const int64_t nn = n * n;
@@ -627,19 +635,29 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
       store_transposed<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, u, tr);
       store_transposed<VEC>(Lb, n, a0, j0, bA, bJ, wy, wx, l, tr);
     }
+    if (!PK && both && A != B) {
+      // the other orientation too (uniform over the workgroup)
+      if (rowor) {
+        store_transposed<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, u, tr);
+        store_transposed<VEC>(Lb, n, a0, j0, bA, bJ, wy, wx, l, tr);
+      } else {
+        store_rows<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, u);
+        store_rows<VEC>(Lb, n, a0, j0, bA, bJ, wy, wx, l);
+      }
+    }
     __syncthreads();
   }
 }
 
-// Bulk of phase 3 for the dense layout: every fresh cell outside band K and
-// the bands starting at s1 and s2, as the four BK x BK quadrants of each
-// upper TILE x TILE tile (grid.x = 4 T(T+1)/2, grid.y = molecules).  Band K
-// is final after phase 2; bands s1 and s2 (the next two k-blocks' bands; < 0
-// for none) are updated ahead on the other stream.  A quadrant in any of them
-// is skipped whole (quadrants and bands are both BK wide): it is neither read
-// nor written, and the panel columns of bands s1 and s2 are not read, since
-// the other stream may be updating exactly those cells while this launch
-// runs.  Thread (ty, tx) owns RT x CT cells (rows a0 + RT*ty + r, columns
+// Bulk of phase 3 for the dense layout: the atoms of k-blocks K .. K+nk-1 in
+// order on every fresh cell outside the bands [X0, X1), as the four BK x BK
+// quadrants of each upper TILE x TILE tile (grid.x = 4 T(T+1)/2, grid.y =
+// molecules).  [X0, X1) starts with the atoms' own bands, whose rows are
+// final, and goes on over the bands updated ahead on the other stream.  A
+// quadrant in any of them is skipped whole (quadrants and bands are both BK
+// wide): it is neither read nor written, and the panel columns of the bands
+// run ahead are not read, since the other stream may be updating exactly
+// those cells while this launch runs.  Thread (ty, tx) owns RT x CT cells (rows a0 + RT*ty + r, columns
 // j0 + CT*tx + q).  The panel rows of band K are staged through LDS, KCH
 // atoms per chunk with the next chunk's loads in flight; the quadrant is
 // written back as row segments.  Larger tiles read fewer staged operand
@@ -649,8 +667,8 @@ template <bool VEC, bool RU, int RT, int CT, int KCH>
 __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restrict__ U,
                                                                  float *__restrict__ L,
                                                                  int64_t n, int64_t batch,
-                                                                 int64_t K, int64_t s1,
-                                                                 int64_t s2) {
+                                                                 int64_t K, int64_t nk,
+                                                                 int64_t X0, int64_t X1) {
   constexpr int NTX = BK / CT, NT = (BK / RT) * NTX;
   // operands and cells move as vectors of RW rows / CW columns (4, or 2 for
   // 2-wide tiles)
@@ -669,11 +687,10 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
   const int64_t p = blockIdx.x >> 2, qd = blockIdx.x & 3;
   const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
   const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
-  if (A * BK >= n || B * BK >= n || A == K || B == K || A * BK == s1 || B * BK == s1 ||
-      A * BK == s2 || B * BK == s2)
+  if (A * BK >= n || B * BK >= n || (A >= X0 && A < X1) || (B >= X0 && B < X1))
     return;  // uniform over the workgroup, before any barrier
   const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
-  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int bK = (int)(n - k0 < nk * BK ? n - k0 : nk * BK);
   const int bA = (int)(n - a0 < BK ? n - a0 : BK);
   const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
   const int64_t nn = n * n;
@@ -826,8 +843,8 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
 // (packed_half_load).
 template <bool VEC, bool RU>
 __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P, int64_t n,
-                                                           int64_t batch, int64_t K, int64_t s1,
-                                                           int64_t s2) {
+                                                           int64_t batch, int64_t K, int64_t nk,
+                                                           int64_t X0, int64_t X1) {
   __shared__ float4 scu[KC][BK / 4];
   __shared__ float4 scl[KC][BK / 4];
   __shared__ float4 sru[KC][BK / 4];
@@ -839,11 +856,11 @@ __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P
   const int64_t p = blockIdx.x >> 2, qd = blockIdx.x & 3;
   const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
   const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
-  if (A * BK >= n || B * BK >= n || A == K || B == K || A * BK == s1 || B * BK == s1 ||
-      A * BK == s2 || B * BK == s2 || (I2 == J2 && qd == 2))
+  if (A * BK >= n || B * BK >= n || (A >= X0 && A < X1) || (B >= X0 && B < X1) ||
+      (I2 == J2 && qd == 2))
     return;  // uniform over the workgroup, before any barrier
   const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
-  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int bK = (int)(n - k0 < nk * BK ? n - k0 : nk * BK);
   const int bA = (int)(n - a0 < BK ? n - a0 : BK);
   const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
   const bool diag = A == B;  // else A < B: every cell lies above the diagonal
@@ -1024,12 +1041,12 @@ hipStream_t side_stream() {
 constexpr unsigned kOrderingEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
 
 struct Events {
-  // start: phases 1-2 of the first block; bulk[K & 1]: bulk(K) done;
-  // ready[K & 1]: the side stream's work that bulk(K) needs is done
+  // start: the first step's panel; bulk[t & 1]: bulk(t) done;
+  // ready[t & 1]: the side stream's work that bulk(t) needs is done
   hipEvent_t e[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
   hipEvent_t &start() { return e[0]; }
-  hipEvent_t &bulk(int64_t K) { return e[1 + (K & 1)]; }
-  hipEvent_t &ready(int64_t K) { return e[3 + (K & 1)]; }
+  hipEvent_t &bulk(int64_t t) { return e[1 + (t & 1)]; }
+  hipEvent_t &ready(int64_t t) { return e[3 + (t & 1)]; }
   bool created = false;
   bool init() {
     if (created) return true;
@@ -1078,20 +1095,23 @@ int lookahead_bands(int64_t n, int64_t batch, bool packed) {
 }
 
 // Enqueue one pass.  With more than one k-block the pass may run ahead on a
-// second stream (lookahead_bands: by two bands when there are many phase-3
-// tiles, one band for a mid-sized bulk, none when the bulk is too short to
-// hide a band strip or the phase 1-2 launch fills the chip).  Per k-block
-// K the caller's stream runs bulk(K): phase 3 of block K on everything but
-// band K and the bands run ahead.  Two bands ahead, the side stream runs
-// phase 3 of block K on band K+1 (strip), phases 1-2 of block K+1, then
-// (once bulk(K-1) is done) phase 3 of block K on band K+2; bulk(K+1) waits
-// only for the side stream's work before that, so phases 1-2 of block K+1
-// have all of bulk(K) to finish in.  One band ahead, the side stream waits
-// for bulk(K-1), then runs the band K+1 strip and phases 1-2 of block K+1
-// while bulk(K) runs.  The side work a bulk launch may overlap touches only
-// bands it leaves alone and reads only panel rows it does not write; the
-// CPU model of this schedule in the tests checks that cell by cell, for both
-// depths.
+// second stream (lookahead_bands: by two steps when there are many phase-3
+// tiles, one for a mid-sized bulk, none when the bulk is too short to hide a
+// band strip or the phase 1-2 launch fills the chip).  A step is one
+// k-block, or two when running two steps ahead: blocked Floyd-Warshall with
+// 128 atoms per phase 3, whose panel (the rows of both bands, final for all
+// 128 rounds) is built from the 64-wide phase 1-2 kernel and strips.  Per
+// step t the caller's stream runs bulk(t): phase 3 of step t's blocks on
+// everything but their bands and the bands run ahead.  Two steps ahead, the
+// side stream runs phase 3 of step t on the bands of step t+1 (strip),
+// step t+1's panel, then (once bulk(t-1) is done) phase 3 of step t on the
+// bands of step t+2; bulk(t+1) waits only for the side stream's work before
+// that, so step t+1's panel has all of bulk(t) to finish in.  One step
+// ahead, the side stream waits for bulk(t-1), then runs the strip and the
+// panel of step t+1 while bulk(t) runs.  The side work a bulk launch may
+// overlap touches only bands it leaves alone and reads only panel rows it
+// does not write; the CPU model of this schedule in the tests checks that
+// cell by cell, for both depths.
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
                           hipStream_t s, Prof *prof, unsigned flags) {
   static_assert(BK == kBlockRounds, "k-block size");
@@ -1147,50 +1167,77 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
     return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(panel_block), st, U,
                   L, n, batch, K);
   };
-  // s1, s2: first atoms of the bands the bulk launch must leave alone (-1: none)
-  auto phase3 = [&](int64_t K, int64_t s1, int64_t s2, hipStream_t st) -> hipError_t {
+  // The pass advances by steps of W k-blocks: step t holds the blocks
+  // [lo(t), hi(t)).  Two steps ahead the bulk takes two blocks per launch,
+  // which halves its loads and stores of the matrix per atom.
+  const int64_t W = deep ? 2 : 1, NS = ceil_div(K1 - K0, W);
+  auto lo = [&](int64_t t) { return K0 + t * W; };
+  auto hi = [&](int64_t t) { return K0 + (t + 1) * W < K1 ? K0 + (t + 1) * W : K1; };
+
+  // phase 3 of the blocks [K, K + nk) on the cells outside the bands [K, X1)
+  auto phase3 = [&](int64_t K, int64_t nk, int64_t X1, hipStream_t st) -> hipError_t {
     if (!packed)
       return launch(prof, kProfTiles, quads_kernel, dim3((unsigned)(4 * pairs), gy),
-                    dim3(quads_block), st, U, L, n, batch, K, s1, s2);
+                    dim3(quads_block), st, U, L, n, batch, K, nk, K, X1);
     return launch(prof, kProfTiles, packed_kernel, dim3((unsigned)(4 * pairs), gy),
-                  dim3(kThreads), st, U, n, batch, K, s1, s2);
+                  dim3(kThreads), st, U, n, batch, K, nk, K, X1);
+  };
+  // phase 3 of the blocks [K, K + nk) on the nr (1 or 2) row bands from A0,
+  // every column band outside [X0, X1) (and outside A0 for the second row
+  // band, where X1 == A0)
+  auto strip = [&](int64_t K, int64_t nk, int64_t A0, int64_t nr, int64_t X0, int64_t X1,
+                   bool both, hipStream_t st) -> hipError_t {
+    const int64_t cols = TB - ((X1 < TB ? X1 : TB) - X0);
+    return launch(prof, kProfStrip, strip_kernel, dim3((unsigned)cols, gy, (unsigned)nr),
+                  dim3(kThreads), st, U, L, n, batch, K, nk, A0, X0, X1, (int)both);
+  };
+  // the rows of step t's bands final for all of its rounds, in both
+  // orientations: phases 1-2 of its first block, that block on the second
+  // band, phases 1-2 of the second block, and that block on the first band
+  auto step_panel = [&](int64_t t, hipStream_t st) -> hipError_t {
+    const int64_t b = lo(t);
+    hipError_t r = phase12(b, st);
+    if (r != hipSuccess || hi(t) - b < 2) return r;
+    if ((r = strip(b, 1, b + 1, 1, b, b + 1, false, st)) != hipSuccess) return r;
+    if ((r = phase12(b + 1, st)) != hipSuccess) return r;
+    return strip(b + 1, 1, b, 1, b + 1, b + 2, true, st);
   };
 
-  hipError_t e = phase12(K0, s);
+  hipError_t e = step_panel(0, s);
   if (e != hipSuccess || TB == 1) return e;
 
-  // phase 3 of block K on row band A, every column band but K and `skip`
-  auto strip = [&](int64_t K, int64_t A, int64_t skip, hipStream_t st) -> hipError_t {
-    return launch(prof, kProfStrip, strip_kernel, dim3((unsigned)(TB - 1 - (skip >= 0)), gy),
-                  dim3(kThreads), st, U, L, n, batch, K, A * BK, skip < 0 ? -1 : skip * BK);
-  };
   hipStream_t side = ahead > 0 ? side_stream() : nullptr;
   Events *ev = side ? thread_events() : nullptr;
   if (side == nullptr || ev == nullptr) {
-    for (int64_t K = K0; K < K1 && e == hipSuccess; ++K) {
-      e = phase3(K, -1, -1, s);
-      if (e == hipSuccess && K + 1 < K1) e = phase12(K + 1, s);
+    for (int64_t t = 0; t < NS && e == hipSuccess; ++t) {
+      e = phase3(lo(t), hi(t) - lo(t), hi(t), s);
+      if (e == hipSuccess && t + 1 < NS) e = step_panel(t + 1, s);
     }
   } else {
     if ((e = hipEventRecord(ev->start(), s)) == hipSuccess)
       e = hipStreamWaitEvent(side, ev->start(), 0);
-    for (int64_t K = K0; K < K1 && e == hipSuccess; ++K) {
-      const bool n1 = K + 1 < K1, n2 = deep && K + 2 < K1;
-      if (K > K0 && (e = hipStreamWaitEvent(s, ev->ready(K), 0)) != hipSuccess) break;
-      if ((e = phase3(K, n1 ? (K + 1) * BK : -1, n2 ? (K + 2) * BK : -1, s)) != hipSuccess) break;
-      if ((e = hipEventRecord(ev->bulk(K), s)) != hipSuccess) break;
+    for (int64_t t = 0; t < NS && e == hipSuccess; ++t) {
+      const bool n1 = t + 1 < NS, n2 = deep && t + 2 < NS;
+      const int64_t b = lo(t), w = hi(t) - b;
+      if (t > 0 && (e = hipStreamWaitEvent(s, ev->ready(t), 0)) != hipSuccess) break;
+      if ((e = phase3(b, w, n2 ? hi(t + 2) : n1 ? hi(t + 1) : hi(t), s)) != hipSuccess) break;
+      if ((e = hipEventRecord(ev->bulk(t), s)) != hipSuccess) break;
       if (n1) {
-        // one band ahead, band K+1 after block K-1 comes from bulk(K-1)
-        if (!deep && K > K0 && (e = hipStreamWaitEvent(side, ev->bulk(K - 1), 0)) != hipSuccess)
+        // one step ahead, step t+1's bands after step t-1 come from bulk(t-1)
+        if (!deep && t > 0 && (e = hipStreamWaitEvent(side, ev->bulk(t - 1), 0)) != hipSuccess)
           break;
-        if ((e = strip(K, K + 1, -1, side)) != hipSuccess) break;
-        if ((e = phase12(K + 1, side)) != hipSuccess) break;
+        if ((e = strip(b, w, lo(t + 1), hi(t + 1) - lo(t + 1), b, hi(t), false, side)) !=
+            hipSuccess)
+          break;
+        if ((e = step_panel(t + 1, side)) != hipSuccess) break;
       }
       if (n2) {
-        if (K > K0 && (e = hipStreamWaitEvent(side, ev->bulk(K - 1), 0)) != hipSuccess) break;
-        if ((e = strip(K, K + 2, K + 1, side)) != hipSuccess) break;
+        if (t > 0 && (e = hipStreamWaitEvent(side, ev->bulk(t - 1), 0)) != hipSuccess) break;
+        if ((e = strip(b, w, lo(t + 2), hi(t + 2) - lo(t + 2), b, hi(t + 1), false, side)) !=
+            hipSuccess)
+          break;
       }
-      if (n1 && (e = hipEventRecord(ev->ready(K + 1), side)) != hipSuccess) break;
+      if (n1 && (e = hipEventRecord(ev->ready(t + 1), side)) != hipSuccess) break;
     }
   }
   // packed storage keeps one slot per value: nothing goes stale

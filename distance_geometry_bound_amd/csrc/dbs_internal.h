@@ -189,7 +189,8 @@ hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, int k_lo, 
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
                           hipStream_t s, Prof *prof = nullptr, unsigned flags = 0);
 constexpr int kBlockRounds = 64;
-// Bands the blocked pass updates ahead on its second stream (0, 1 or 2).
+// Look-ahead depth of the blocked pass: steps it updates ahead on its second
+// stream (0, 1 or 2; at 2 a step is two k-blocks).
 int lookahead_bands(int64_t n, int64_t batch, bool packed = false);
 // Force the look-ahead depth (0..2) or restore the automatic choice (-1);
 // false (and no change) for any other value.

@@ -281,22 +281,24 @@ int dbs_smooth_packed_range(float *P, int64_t n, int64_t batch, int64_t k_begin,
 int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags, void *stream);
 
 /*
- * dbs_lookahead_bands -- how many k-block bands the blocked pass (DBS_ALGO_
- * BLOCKED) on the dense layout updates ahead on its second stream for this
- * shape:
+ * dbs_lookahead_bands -- the look-ahead depth of the blocked pass (DBS_ALGO_
+ * BLOCKED) on the dense layout for this shape: how many steps it updates
+ * ahead on its second stream.
  *   0  no second stream: a single k-block or phase-3 tile; fewer than 256
  *      phase-3 tiles x molecules (the bulk launch is shorter than the band
  *      strip it would hide); or more than 256 phase 1-2 workgroups (the
  *      panel launch fills the chip by itself);
- *   1  otherwise, below 2048 tiles x molecules;
- *   2  from 2048 tiles x molecules: phases 1-2 of the next block then have a
- *      whole phase-3 launch to hide under.
+ *   1  otherwise, below 960 tiles x molecules: steps of one k-block;
+ *   2  from 960 tiles x molecules: steps of two k-blocks, so that each
+ *      phase-3 launch runs 128 atoms (half the loads and stores of the
+ *      matrix per atom), and the panel of the next step has a whole phase-3
+ *      launch to hide under.
  * The packed passes (dbs_smooth_packed*) leave out the panel-fill test:
  * their slower phase 1-2 kernel still gains from running beside the bulk.
  * A depth set by dbs_set_lookahead replaces the automatic choice (still 0
- * for a single k-block or tile).  Phase 3's bulk launches leave those bands
- * to the second stream.  For measurement and tests; DBS_EINVAL for n < 1 or
- * batch < 1.
+ * for a single k-block or tile).  Phase 3's bulk launches leave the bands of
+ * the steps run ahead to the second stream.  For measurement and tests;
+ * DBS_EINVAL for n < 1 or batch < 1.
  */
 int dbs_lookahead_bands(int64_t n, int64_t batch);
 

@@ -119,7 +119,9 @@ def test_lookahead_bands_query():
     assert lib.dbs_lookahead_bands(500, 64) == 0      # 448 panel workgroups fill the chip
     assert lib.dbs_lookahead_bands(2944, 1) == 1      # 276 tiles, 45 panel workgroups
     assert lib.dbs_lookahead_bands(4096, 1) == 1
-    assert lib.dbs_lookahead_bands(4096, 4) == 2      # 2112 tiles x molecules
+    assert lib.dbs_lookahead_bands(5120, 1) == 1      # 820 tiles
+    assert lib.dbs_lookahead_bands(5632, 1) == 2      # 990 tiles
+    assert lib.dbs_lookahead_bands(4096, 2) == 2      # 1056 tiles x molecules
     assert lib.dbs_lookahead_bands(12288, 1) == 2
     assert lib.dbs_lookahead_bands(0, 1) == -1 and lib.dbs_lookahead_bands(5, 0) == -1
     assert dgb.lookahead_bands(12288) == 2

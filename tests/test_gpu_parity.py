@@ -117,8 +117,9 @@ def restore_lookahead():
 @pytest.mark.parametrize("n,batch", [(129, 2), (300, 1), (385, 2), (700, 1)])
 def test_every_lookahead_depth(n, batch, bands, restore_lookahead):
     # the automatic choice runs these sizes without a second stream; forcing
-    # each depth covers the one- and two-band schedules at small sizes, on the
-    # dense, directed and packed passes and on ranges of whole k-blocks
+    # each depth covers the one- and two-step schedules (steps of one and of
+    # two k-blocks) at small sizes, on the dense, directed and packed passes
+    # and on ranges of whole k-blocks
     from oracle import steps
     U0, L0 = sound_input(n, batch, seed=31 * n + bands)
     Ue, Le = oracle.smooth(U0, L0)
@@ -138,6 +139,13 @@ def test_every_lookahead_depth(n, batch, bands, restore_lookahead):
     assert_bits(host(U), host(L), Ur, Lr, f"range 0..128 n={n} bands={bands}")
     dgb.smooth_range(U, L, 128, n, algo="blocked")
     assert_bits(host(U), host(L), Ue, Le, f"range 128..n n={n} bands={bands}")
+    # ranges that start at an odd k-block (two steps ahead pairs the blocks
+    # from the range's first one, so the pairs fall differently)
+    U, L = dev(U0), dev(L0)
+    cuts = sorted({0, 64, min(n, 320), n})
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        dgb.smooth_range(U, L, a, b, algo="blocked")
+    assert_bits(host(U), host(L), Ue, Le, f"ranges 0,64,320,n n={n} bands={bands}")
 
 
 def test_walk_molecules_batched():

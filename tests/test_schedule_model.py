@@ -1,15 +1,21 @@
 """CPU model of the blocked pass's schedule (test code only).
 
-The GPU pass (csrc/blocked.hip) runs, per k-block K of BK = 64 atoms,
-  phases 1+2  the rounds of band K over the diagonal tile (K,K) and, in the
-           same loop, over each panel tile of band K (one workgroup per
-           panel tile), panel tiles read from their fresh orientation (upper
-           TILE x TILE region) and written in both orientations;
-  phase 3  band K+1 first (the strip, on a second stream, followed there by
-           phases 1-2 of K+1), and every other live cell of the upper
-           TILE x TILE tiles (the bulk, on the caller's stream, as BK x BK
-           quadrants: a quadrant in band K or K+1 is skipped whole, which
-           leaves exactly the live cells modelled here);
+The GPU pass (csrc/blocked.hip) runs in steps of one k-block of BK = 64
+atoms (one step ahead) or two (two steps ahead), per step
+  panel    the rows of the step's bands made final for all of its rounds:
+           phases 1+2 of its first block (the rounds of band K over the
+           diagonal tile (K,K) and, in the same loop, over each panel tile
+           of band K, one workgroup per panel tile, panel tiles read from
+           their fresh orientation (upper TILE x TILE region) and written in
+           both orientations); with two blocks, block K on band K+1 (a
+           strip), phases 1+2 of K+1, and block K+1 on band K (a strip that
+           writes both orientations);
+  phase 3  the bands of the next steps first (strips, on a second stream,
+           followed there by the next step's panel), and every other live
+           cell of the upper TILE x TILE tiles (the bulk, on the caller's
+           stream, as BK x BK quadrants: a quadrant in a band of the step or
+           of a step run ahead is skipped whole, which leaves exactly the
+           live cells modelled here);
 and mirrors the upper tiles into the lower ones at the end.
 
 This model re-implements that data flow in plain Python on exact int64 units
@@ -93,13 +99,15 @@ class Model:
             writes |= {(a, c), (c, a)}
         return reads, writes
 
-    def strip(self, K, A, skip):
-        """Phase 3 of block K on row band A only: blocks (A, J) for every
-        column band J other than K and `skip`, each in its fresh orientation."""
+    def strip(self, Ks, A, excl, both=False):
+        """Phase 3 of the blocks Ks (their atoms in order) on row band A only:
+        blocks (A, J) for every column band J outside `excl`, each in its
+        fresh orientation, and with `both` in the other one too."""
         reads, writes = set(), set()
-        kb, ab = self.band(K), self.band(A)
+        kb = [k for K in Ks for k in self.band(K)]
+        ab = self.band(A)
         for J in range(self.TB):
-            if J == K or J == skip:
+            if J in excl:
                 continue
             jb = self.band(J)
             reads |= {(k, x) for k in kb for x in ab + jb}
@@ -113,17 +121,21 @@ class Model:
                         l = max(l, self.L[k, a] - self.U[k, c], self.L[k, c] - self.U[k, a])
                     self.U[dst], self.L[dst] = u, l
                     writes.add(dst)
+                    if both:
+                        self.U[dst[::-1]], self.L[dst[::-1]] = u, l
+                        writes.add(dst[::-1])
         return reads, writes
 
-    def bulk(self, K, skip_bands):
-        """Phase 3 of block K on the BK x BK quadrants of the upper TILE x TILE
-        tiles, a quadrant in band K or in a skipped band left whole."""
+    def bulk(self, Ks, skip_bands):
+        """Phase 3 of the blocks Ks on the BK x BK quadrants of the upper
+        TILE x TILE tiles, a quadrant in a band of Ks or in a skipped band
+        left whole."""
         n = self.n
         reads, writes = set(), set()
-        dead = set(self.band(K))
-        for b in skip_bands:
+        dead = set()
+        for b in list(Ks) + list(skip_bands):
             dead |= set(self.band(b))
-        kb = self.band(K)
+        kb = [k for K in Ks for k in self.band(K)]
         new = {}
         for J in range(self.T):
             for I in range(J + 1):
@@ -143,46 +155,69 @@ class Model:
             self.U[i, j], self.L[i, j] = u, l
         return reads, writes
 
+    def step_panel(self, Ks):
+        """The rows of the step's bands Ks final for all of its rounds, as
+        (kind, reads, writes) launches."""
+        b = Ks[0]
+        out = [("phase12", *self.phase12(b))]
+        if len(Ks) == 2:
+            out.append(("panel-strip", *self.strip([b], b + 1, {b})))
+            out.append(("phase12", *self.phase12(b + 1)))
+            out.append(("panel-strip", *self.strip([b + 1], b, {b + 1}, both=True)))
+        return out
+
     def run(self):
-        """The pass as the two streams issue it.  Two bands ahead:
-          main  per K: [wait ready(K)] bulk(K) skipping bands K, K+1, K+2
-          side  per K: strip(K, band K+1), phases 1-2 of K+1,
-                       [wait bulk(K-1)] strip(K, band K+2 without band K+1),
-                       record ready(K+1)
-        One band ahead:
-          main  per K: [wait ready(K)] bulk(K) skipping bands K, K+1
-          side  per K: [wait bulk(K-1)] strip(K, band K+1), phases 1-2 of K+1,
-                       record ready(K+1)
-        Side work that bulk(K) may overlap is everything after ready(K) and
-        before the side's wait for bulk(K); each such footprint must be
-        disjoint from bulk(K)'s."""
+        """The pass as the two streams issue it, in steps of W k-blocks (W = 2
+        two steps ahead, else 1); S(t) = the bands of step t.  Two steps ahead:
+          main  per t: [wait ready(t)] bulk(t) skipping S(t), S(t+1), S(t+2)
+          side  per t: strip(t, rows S(t+1)), panel of step t+1,
+                       [wait bulk(t-1)] strip(t, rows S(t+2) without
+                       columns S(t+1)), record ready(t+1)
+        One step ahead:
+          main  per t: [wait ready(t)] bulk(t) skipping S(t), S(t+1)
+          side  per t: [wait bulk(t-1)] strip(t, rows S(t+1)), panel of
+                       step t+1, record ready(t+1)
+        A strip over the two row bands of a step leaves the first band out of
+        the second's columns (those cells are the first band's).  Side work
+        that bulk(t) may overlap is everything after ready(t) and before the
+        side's wait for bulk(t); each such footprint must be disjoint from
+        bulk(t)'s."""
         TB, deep = self.TB, self.depth == 2
-        self.phase12(0)
+        W = 2 if deep else 1
+        steps = [list(range(b, min(b + W, TB))) for b in range(0, TB, W)]
+        NS = len(steps)
+        self.step_panel(steps[0])
         side = []          # (iteration, kind, reads, writes) in side-stream order
         bulks = {}
-        ready_at = {}      # K -> index into `side` after which ready(K) is recorded
-        wait_at = {}       # K -> index into `side` at which the side waits for bulk(K)
-        for K in range(TB):
+        ready_at = {}      # t -> index into `side` after which ready(t) is recorded
+        wait_at = {}       # t -> index into `side` at which the side waits for bulk(t)
+
+        def strip_rows(t, rows, excl_to):
+            for r, A in enumerate(rows):
+                excl = set(range(steps[t][0], excl_to + r))
+                side.append((t, "strip", *self.strip(steps[t], A, excl)))
+
+        for t in range(NS):
             # the model executes in an order consistent with both streams: the
-            # side work of iteration K (it only reads state bulk(K) leaves alone)
-            if K + 1 < TB:
+            # side work of iteration t (it only reads state bulk(t) leaves alone)
+            if t + 1 < NS:
                 if not deep:
-                    wait_at[K - 1] = len(side)
-                side.append((K, "strip1", *self.strip(K, K + 1, None)))
-                side.append((K, "phase12", *self.phase12(K + 1)))
-            if deep and K + 2 < TB:
-                wait_at[K - 1] = len(side)
-                side.append((K, "strip2", *self.strip(K, K + 2, K + 1)))
-            if K + 1 < TB:
-                ready_at[K + 1] = len(side)
-            ahead = (K + 1, K + 2) if deep and self.skip_second else (K + 1,)
-            bulks[K] = self.bulk(K, [b for b in ahead if b < TB])
+                    wait_at[t - 1] = len(side)
+                strip_rows(t, steps[t + 1], steps[t][-1] + 1)
+                side.extend((t, kind, r, w) for kind, r, w in self.step_panel(steps[t + 1]))
+            if deep and t + 2 < NS:
+                wait_at[t - 1] = len(side)
+                strip_rows(t, steps[t + 2], steps[t + 1][-1] + 1)
+            if t + 1 < NS:
+                ready_at[t + 1] = len(side)
+            ahead = steps[t + 1:t + 3] if deep and self.skip_second else steps[t + 1:t + 2]
+            bulks[t] = self.bulk(steps[t], [b for s_ in ahead for b in s_])
         sym = lambda cells: cells | {(j, i) for (i, j) in cells}
-        for K, (br, bw) in bulks.items():
-            lo = ready_at.get(K, 0)
-            hi = wait_at.get(K, len(side))
+        for t, (br, bw) in bulks.items():
+            lo = ready_at.get(t, 0)
+            hi = wait_at.get(t, len(side))
             for it, kind, sr, sw in side[lo:hi]:
-                tag = f"bulk({K}) vs {kind}({it})"
+                tag = f"bulk({t}) vs {kind}({it})"
                 assert not (sw & (br | bw)), tag + ": side writes what the bulk touches"
                 assert not (bw & sr), tag + ": bulk writes what the side reads"
                 # packed storage: a logical cell (i,j) lives in P[min][max] (U)
@@ -208,8 +243,9 @@ def test_schedule_model_matches_oracle_and_streams_are_disjoint(n, depth):
 
 
 def test_schedule_model_detects_a_planted_overlap():
-    # a bulk that forgets to leave band K+2 alone overlaps the side stream's
-    # second strip: the footprint check must say so
-    U0, L0, _ = gen.random_sound_bounds(200, seed=1, box=30.0)
+    # a bulk that forgets to leave the bands of step t+2 alone overlaps the
+    # side stream's second strip: the footprint check must say so
+    # (n = 260: five k-blocks, so step 0 has a step two ahead)
+    U0, L0, _ = gen.random_sound_bounds(260, seed=1, box=36.0)
     with pytest.raises(AssertionError, match="side writes what the bulk touches"):
         Model(U0, L0, skip_second=False).run()
