@@ -86,11 +86,10 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": nbytes, "dispatches": 5}), flush=True)
 
 
-def tiles_units_per_pass(n, batch, ahead):
+def tiles_units_per_pass(n, batch, ahead, W):
     """(stored, dense) (i,j,k) triples of the bulk phase-3 launches over one pass.
 
-    The pass steps over W k-blocks at a time (W = 2 when it runs two steps
-    ahead, else 1).  The launch of the step starting at block K runs the
+    The pass steps over W k-blocks at a time (dbs_step_blocks).  The launch of the step starting at block K runs the
     step's atoms over the 64x64 quadrants of every TILE x TILE tile with
     I <= J and stores every cell outside the step's bands (final after its
     panel) and the bands of the `ahead` steps after it (updated ahead on the
@@ -99,7 +98,6 @@ def tiles_units_per_pass(n, batch, ahead):
     columns (the cells below the diagonal follow by symmetry)."""
     T = -(-n // TILE)
     TB = -(-n // BK)
-    W = 2 if ahead == 2 else 1
     stored = dense = 0
     for K in range(0, TB, W):
         end = min(TB, K + W * (1 + ahead))
@@ -361,7 +359,8 @@ def main():
         launches = tot["tiles"][0] // prof_steps
         launch_ms = tot["tiles"][1] / tot["tiles"][0]
         ahead = dgb.lookahead_bands(n, batch)
-        stored, dense = tiles_units_per_pass(n, batch, ahead)
+        width = dgb.step_blocks(n, batch)
+        stored, dense = tiles_units_per_pass(n, batch, ahead, width)
         ops = OPS_PER_TRIPLE * stored / launches          # per launch, averaged over the pass
         achieved = ops / (launch_ms * 1e-3)
         traffic = counters_traffic(n, batch)
@@ -374,6 +373,7 @@ def main():
             "frac_of_fp32_vector_peak": achieved / FP32_VALU_PEAK,
             "traffic": traffic,
             "launch_ms": launch_ms, "launches": tot["tiles"][0], "lookahead_bands": ahead,
+            "step_blocks": width,
             "ops_per_launch": ops,
             "frac_effective": OPS_PER_TRIPLE * dense / launches / (launch_ms * 1e-3)
                               / FP32_VALU_PEAK,

@@ -29,7 +29,7 @@ EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds",
            "dbs_pack", "dbs_unpack", "dbs_smooth_packed", "dbs_smooth_packed_range",
            "dbs_check_packed", "dbs_smooth_directed", "dbs_smooth_directed_range",
            "dbs_smooth_packed_directed_range", "dbs_lookahead_bands", "dbs_set_lookahead",
-           "dbs_lds_max_n", "dbs_auto_algo", "dbs_strerror", "dbs_version")
+           "dbs_step_blocks", "dbs_set_step_blocks", "dbs_lds_max_n", "dbs_auto_algo", "dbs_strerror", "dbs_version")
 
 RESTRAINT_FLAGS = {"index": 1, "value": 2}
 
@@ -76,6 +76,8 @@ def lib():
         L.dbs_auto_algo.argtypes = [i64, i64]
         L.dbs_lookahead_bands.argtypes = [i64, i64]
         L.dbs_set_lookahead.argtypes = [ctypes.c_int]
+        L.dbs_step_blocks.argtypes = [i64, i64]
+        L.dbs_set_step_blocks.argtypes = [ctypes.c_int]
         L.dbs_strerror.argtypes = [c_int]
         L.dbs_strerror.restype = ctypes.c_char_p
         for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_round",
@@ -85,7 +87,7 @@ def lib():
                   "dbs_smooth_packed_range", "dbs_check_packed", "dbs_smooth_directed",
                   "dbs_smooth_directed_range", "dbs_smooth_packed_directed_range",
                   "dbs_lds_max_n", "dbs_auto_algo", "dbs_lookahead_bands", "dbs_set_lookahead",
-                  "dbs_version"):
+                  "dbs_step_blocks", "dbs_set_step_blocks", "dbs_version"):
             getattr(L, f).restype = c_int
         _lib = L
     return _lib
@@ -352,8 +354,19 @@ def check_packed(P) -> int:
 
 
 def lookahead_bands(n: int, batch: int = 1) -> int:
-    """Bands the blocked pass updates ahead on its second stream (0, 1, 2)."""
+    """Steps the blocked pass updates ahead on its second stream (0, 1, 2)."""
     return int(lib().dbs_lookahead_bands(int(n), int(batch)))
+
+
+def step_blocks(n: int, batch: int = 1) -> int:
+    """k-blocks per step of the blocked pass (1 .. 4)."""
+    return int(lib().dbs_step_blocks(int(n), int(batch)))
+
+
+def set_step_blocks(blocks: int) -> None:
+    """Force the k-blocks per step of later blocked passes (1 .. 4), or -1
+    for the automatic choice (process-wide)."""
+    _raise(lib().dbs_set_step_blocks(int(blocks)))
 
 
 def set_lookahead(bands: int) -> None:

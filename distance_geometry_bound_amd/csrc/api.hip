@@ -313,6 +313,15 @@ int dbs_set_lookahead(int bands) {
   return dbs::set_lookahead(bands) ? DBS_OK : DBS_EINVAL;
 }
 
+int dbs_step_blocks(int64_t n, int64_t batch) {
+  if (n < 1 || batch < 1) return DBS_EINVAL;
+  return dbs::step_blocks(n, batch);
+}
+
+int dbs_set_step_blocks(int blocks) {
+  return dbs::set_step_blocks(blocks) ? DBS_OK : DBS_EINVAL;
+}
+
 int dbs_auto_algo(int64_t n, int64_t batch) {
   (void)batch;
   return n <= dbs::kSmallMaxN ? DBS_ALGO_LDS : DBS_ALGO_BLOCKED;

@@ -45,6 +45,13 @@ constexpr int KC = 16;          // atoms per LDS chunk in phase 3
 // in steps of two k-blocks (measured crossover: n5120, 820 tiles, one step
 // ahead 8.40 ms, two 8.76 ms; n5632, 990 tiles, 10.56 against 10.41 ms).
 constexpr int64_t kDeepTiles = 960;
+// k-blocks per step when running two steps ahead: 4 from kStep4Tiles phase-3
+// tiles (times molecules), 3 from kStep3Tiles, else 2.  Wider steps spread a
+// bulk launch's fixed costs over more atoms but leave more bands to the
+// strips and lengthen the side stream's chain (measured, dense ms, widths
+// 2/3/4: n6144 11.8/13.2/14.0; n8192 25.5/24.9/25.8; n10240 49.5/47.8/47.0;
+// n12288 73.9/72.6/71.1).
+constexpr int64_t kStep4Tiles = 3000, kStep3Tiles = 1800;
 // Below this many phase-3 tiles (times molecules) a bulk launch is too short
 // to hide the band strip that running ahead puts on the critical path.
 constexpr int64_t kAheadTiles = 256;
@@ -466,13 +473,14 @@ __device__ __forceinline__ void store_transposed(float *P, int64_t n, int64_t r0
 // run of tiles instead makes it sweep every row slice of the panel, and is
 // slower.)
 
-// Phase 3 of the k-blocks K .. K+nk-1 (their atoms in order) on one or two
-// row bands, run ahead of the bulk on the second stream.  Row band A0 takes
-// every column band outside [X0, X1); a second row band A0+1 (grid.z = 2)
-// also leaves out band X1, which is A0 where a second row band is asked for
-// (block (A0+1, A0) is block (A0, A0+1) of the first row band).  [X0, X1)
-// holds the atoms' own bands, whose rows are final.  grid.x = the first row
-// band's column bands, grid.y = molecules.  Block (A, J) is read and
+// Phase 3 of the k-blocks K .. K+nk-1 (their atoms in order) on the row
+// bands A0 + r, r < grid.z, run ahead of the bulk on the second stream or
+// inside a step's panel.  Row band A0 + r takes every column band outside
+// [X0, X1 + r) and other than Y (< 0: none; Y >= X1 + r).  The callers put
+// the atoms' own bands (whose rows are final) in that set, and X1 = A0
+// where grid.z > 1: then row band A0 + r leaves out the row bands before it
+// (block (A0+r, A0+r') is block (A0+r', A0+r) of an earlier row band).
+// grid.x = the first row band's column bands, grid.y = molecules.  Block (A, J) is read and
 // written in its fresh orientation (dense) or as its U and L slots (packed);
 // with `both` (dense) its other orientation is written too, so that the
 // rows of band A can serve as a panel afterwards.  Thread (ty, tx) owns a
@@ -486,7 +494,7 @@ template <bool VEC, bool PK, bool RU>
 __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float *__restrict__ L,
                                                     int64_t n, int64_t batch, int64_t K,
                                                     int64_t nk, int64_t A0, int64_t X0,
-                                                    int64_t X1, int both) {
+                                                    int64_t X1, int64_t Y, int both) {
   __shared__ float4 scu[KC][BK / 4];
   __shared__ float4 scl[KC][BK / 4];
   __shared__ float4 sru[KC][BK / 4];
@@ -497,12 +505,14 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   critical_path_priority();
   // row band A = A0 + blockIdx.z; column band B: the blockIdx.x-th band
-  // outside [X0, X1 + blockIdx.z)
+  // outside [X0, X1 + blockIdx.z) and other than Y
   const int64_t TB = (n + BK - 1) / BK, A = A0 + blockIdx.z;
   const int64_t xe = X1 + blockIdx.z < TB ? X1 + blockIdx.z : TB;
+  const int64_t y = Y >= xe && Y < TB ? Y : -1;
   int64_t B = blockIdx.x;
-  if (B >= TB - (xe - X0)) return;  // uniform, before any barrier
+  if (B >= TB - (xe - X0) - (y >= 0)) return;  // uniform, before any barrier
   if (B >= X0) B += xe - X0;
+  if (y >= 0 && B >= y) ++B;
   const bool rowor = fresh(A, B);  // stored as (A, B), else as its transpose (B, A)
   const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
   const int bK = (int)(n - k0 < nk * BK ? n - k0 : nk * BK);
@@ -1072,12 +1082,27 @@ Events *thread_events() {
 
 namespace {
 std::atomic<int> forced_lookahead{-1};  // -1: automatic
+std::atomic<int> forced_step{-1};       // -1: automatic
 }  // namespace
 
 bool set_lookahead(int bands) {
   if (bands < -1 || bands > 2) return false;
   forced_lookahead.store(bands);
   return true;
+}
+
+bool set_step_blocks(int blocks) {
+  if (blocks != -1 && (blocks < 1 || blocks > kMaxStepBlocks)) return false;
+  forced_step.store(blocks);
+  return true;
+}
+
+int step_blocks(int64_t n, int64_t batch, bool packed) {
+  const int forced = forced_step.load();
+  if (forced > 0) return forced;
+  if (lookahead_bands(n, batch, packed) != 2) return 1;
+  const int64_t T = ceil_div(n, TILE), tiles = T * (T + 1) / 2 * batch;
+  return tiles >= kStep4Tiles ? 4 : tiles >= kStep3Tiles ? 3 : 2;
 }
 
 int lookahead_bands(int64_t n, int64_t batch, bool packed) {
@@ -1168,9 +1193,10 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
                   L, n, batch, K);
   };
   // The pass advances by steps of W k-blocks: step t holds the blocks
-  // [lo(t), hi(t)).  Two steps ahead the bulk takes two blocks per launch,
-  // which halves its loads and stores of the matrix per atom.
-  const int64_t W = deep ? 2 : 1, NS = ceil_div(K1 - K0, W);
+  // [lo(t), hi(t)).  Two steps ahead the bulk takes several blocks per
+  // launch, which spreads its fixed costs (the loads and stores of the
+  // matrix, the launch's ramp and tail) over more atoms.
+  const int64_t W = step_blocks(n, batch, packed), NS = ceil_div(K1 - K0, W);
   auto lo = [&](int64_t t) { return K0 + t * W; };
   auto hi = [&](int64_t t) { return K0 + (t + 1) * W < K1 ? K0 + (t + 1) * W : K1; };
 
@@ -1182,25 +1208,28 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
     return launch(prof, kProfTiles, packed_kernel, dim3((unsigned)(4 * pairs), gy),
                   dim3(kThreads), st, U, n, batch, K, nk, K, X1);
   };
-  // phase 3 of the blocks [K, K + nk) on the nr (1 or 2) row bands from A0,
-  // every column band outside [X0, X1) (and outside A0 for the second row
-  // band, where X1 == A0)
+  // phase 3 of the blocks [K, K + nk) on the nr row bands from A0: row band
+  // A0 + r on every column band outside [X0, X1 + r) and other than Y
   auto strip = [&](int64_t K, int64_t nk, int64_t A0, int64_t nr, int64_t X0, int64_t X1,
-                   bool both, hipStream_t st) -> hipError_t {
-    const int64_t cols = TB - ((X1 < TB ? X1 : TB) - X0);
+                   int64_t Y, bool both, hipStream_t st) -> hipError_t {
+    const int64_t xe = X1 < TB ? X1 : TB;
+    const int64_t cols = TB - (xe - X0) - (Y >= xe && Y < TB ? 1 : 0);
     return launch(prof, kProfStrip, strip_kernel, dim3((unsigned)cols, gy, (unsigned)nr),
-                  dim3(kThreads), st, U, L, n, batch, K, nk, A0, X0, X1, (int)both);
+                  dim3(kThreads), st, U, L, n, batch, K, nk, A0, X0, X1, Y, (int)both);
   };
-  // the rows of step t's bands final for all of its rounds, in both
-  // orientations: phases 1-2 of its first block, that block on the second
-  // band, phases 1-2 of the second block, and that block on the first band
+  // The rows of step t's bands final for all of its rounds, in both
+  // orientations.  Band b+j in turn takes the step's earlier blocks (one
+  // strip), runs phases 1-2 of its own block, and that block then goes over
+  // the earlier bands (one strip, both orientations).
   auto step_panel = [&](int64_t t, hipStream_t st) -> hipError_t {
-    const int64_t b = lo(t);
-    hipError_t r = phase12(b, st);
-    if (r != hipSuccess || hi(t) - b < 2) return r;
-    if ((r = strip(b, 1, b + 1, 1, b, b + 1, false, st)) != hipSuccess) return r;
-    if ((r = phase12(b + 1, st)) != hipSuccess) return r;
-    return strip(b + 1, 1, b, 1, b + 1, b + 2, true, st);
+    const int64_t b = lo(t), w = hi(t) - b;
+    hipError_t r = hipSuccess;
+    for (int64_t j = 0; j < w && r == hipSuccess; ++j) {
+      if (j > 0 && (r = strip(b, j, b + j, 1, b, b + j, -1, false, st)) != hipSuccess) break;
+      if ((r = phase12(b + j, st)) != hipSuccess) break;
+      if (j > 0) r = strip(b + j, 1, b, j, b, b, b + j, true, st);
+    }
+    return r;
   };
 
   hipError_t e = step_panel(0, s);
@@ -1226,15 +1255,15 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
         // one step ahead, step t+1's bands after step t-1 come from bulk(t-1)
         if (!deep && t > 0 && (e = hipStreamWaitEvent(side, ev->bulk(t - 1), 0)) != hipSuccess)
           break;
-        if ((e = strip(b, w, lo(t + 1), hi(t + 1) - lo(t + 1), b, hi(t), false, side)) !=
+        if ((e = strip(b, w, lo(t + 1), hi(t + 1) - lo(t + 1), b, hi(t), -1, false, side)) !=
             hipSuccess)
           break;
         if ((e = step_panel(t + 1, side)) != hipSuccess) break;
       }
       if (n2) {
         if (t > 0 && (e = hipStreamWaitEvent(side, ev->bulk(t - 1), 0)) != hipSuccess) break;
-        if ((e = strip(b, w, lo(t + 2), hi(t + 2) - lo(t + 2), b, hi(t + 1), false, side)) !=
-            hipSuccess)
+        if ((e = strip(b, w, lo(t + 2), hi(t + 2) - lo(t + 2), b, hi(t + 1), -1, false,
+                       side)) != hipSuccess)
           break;
       }
       if (n1 && (e = hipEventRecord(ev->ready(t + 1), side)) != hipSuccess) break;

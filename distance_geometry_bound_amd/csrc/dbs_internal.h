@@ -195,6 +195,11 @@ int lookahead_bands(int64_t n, int64_t batch, bool packed = false);
 // Force the look-ahead depth (0..2) or restore the automatic choice (-1);
 // false (and no change) for any other value.
 bool set_lookahead(int bands);
+// k-blocks per step of the blocked pass (1 .. kMaxStepBlocks), and the
+// override of that choice (-1: automatic).
+constexpr int kMaxStepBlocks = 4;
+int step_blocks(int64_t n, int64_t batch, bool packed = false);
+bool set_step_blocks(int blocks);
 hipError_t launch_restraints(float *U, float *L, int64_t n, int64_t batch, float unknown_L,
                              float unknown_U, const int32_t *mol, const int32_t *ia,
                              const int32_t *ja, const float *lo, const float *hi, int64_t count,

@@ -289,10 +289,10 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags
  *      strip it would hide); or more than 256 phase 1-2 workgroups (the
  *      panel launch fills the chip by itself);
  *   1  otherwise, below 960 tiles x molecules: steps of one k-block;
- *   2  from 960 tiles x molecules: steps of two k-blocks, so that each
- *      phase-3 launch runs 128 atoms (half the loads and stores of the
- *      matrix per atom), and the panel of the next step has a whole phase-3
- *      launch to hide under.
+ *   2  from 960 tiles x molecules: steps of two to four k-blocks
+ *      (dbs_step_blocks), so that each phase-3 launch runs 128 to 256 atoms
+ *      (fewer loads and stores of the matrix per atom), and the panel of
+ *      the next step has a whole phase-3 launch to hide under.
  * The packed passes (dbs_smooth_packed*) leave out the panel-fill test:
  * their slower phase 1-2 kernel still gains from running beside the bulk.
  * A depth set by dbs_set_lookahead replaces the automatic choice (still 0
@@ -311,6 +311,24 @@ int dbs_lookahead_bands(int64_t n, int64_t batch);
  * (the setting is then unchanged).
  */
 int dbs_set_lookahead(int bands);
+
+/*
+ * dbs_step_blocks -- k-blocks per step of the blocked pass on the dense
+ * layout for this shape, unless dbs_set_step_blocks set a width: where it
+ * runs two steps ahead (dbs_lookahead_bands), 4 from 3000 phase-3 tiles x
+ * molecules, 3 from 1800, else 2; 1 where it runs one step ahead or none.
+ * A step of w blocks is blocked Floyd-Warshall with 64w atoms per phase-3
+ * launch; its panel (the rows of the step's bands, final for all of its
+ * rounds) is built from the 64-wide phase 1-2 kernel and strips of phase 3.
+ * For measurement and tests; DBS_EINVAL for n < 1 or batch < 1.
+ *
+ * dbs_set_step_blocks -- process-wide override for the blocked passes
+ * enqueued after the call: blocks = 1 .. 4 forces that width, -1 restores
+ * the automatic choice.  Every width gives the same results.  Returns
+ * DBS_OK, or DBS_EINVAL for any other value (the setting is then unchanged).
+ */
+int dbs_step_blocks(int64_t n, int64_t batch);
+int dbs_set_step_blocks(int blocks);
 
 /* Largest n the LDS algorithm accepts. */
 int dbs_lds_max_n(void);

@@ -142,3 +142,25 @@ def test_set_lookahead_overrides_the_choice():
     finally:
         dgb.set_lookahead(-1)
     assert dgb.lookahead_bands(12288) == 2 and dgb.lookahead_bands(200) == 0
+
+
+def test_step_blocks_query_and_override():
+    # steps of two k-blocks where the pass runs two steps ahead, else one;
+    # the override forces a width for every shape, -1 restores the choice
+    lib = dgb.lib()
+    assert dgb.step_blocks(12288) == 4 and dgb.step_blocks(10240) == 4   # 4656, 3240 tiles
+    assert dgb.step_blocks(8192) == 3 and dgb.step_blocks(6144, 2) == 3  # 2080, 2352
+    assert dgb.step_blocks(5632) == 2 and dgb.step_blocks(6144) == 2     # 990, 1176
+    assert dgb.step_blocks(4096) == 1 and dgb.step_blocks(200) == 1
+    assert lib.dbs_step_blocks(0, 1) == -1 and lib.dbs_step_blocks(5, 0) == -1
+    try:
+        dgb.set_step_blocks(4)
+        assert dgb.step_blocks(200) == 4 and dgb.step_blocks(12288) == 4
+        assert lib.dbs_set_step_blocks(0) == -1 and lib.dbs_set_step_blocks(5) == -1
+        assert lib.dbs_set_step_blocks(-2) == -1
+        assert dgb.step_blocks(12288) == 4                                         # unchanged
+        with pytest.raises(ValueError):
+            dgb.set_step_blocks(9)
+    finally:
+        dgb.set_step_blocks(-1)
+    assert dgb.step_blocks(12288) == 4 and dgb.step_blocks(4096) == 1

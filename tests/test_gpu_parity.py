@@ -111,6 +111,7 @@ def test_full_pass_multi_tile(n):
 def restore_lookahead():
     yield
     dgb.set_lookahead(-1)
+    dgb.set_step_blocks(-1)
 
 
 @pytest.mark.parametrize("bands", [0, 1, 2])
@@ -146,6 +147,34 @@ def test_every_lookahead_depth(n, batch, bands, restore_lookahead):
     for a, b in zip(cuts[:-1], cuts[1:]):
         dgb.smooth_range(U, L, a, b, algo="blocked")
     assert_bits(host(U), host(L), Ue, Le, f"ranges 0,64,320,n n={n} bands={bands}")
+
+
+@pytest.mark.parametrize("blocks", [1, 2, 3, 4])
+@pytest.mark.parametrize("bands", [0, 1, 2])
+@pytest.mark.parametrize("n,batch", [(385, 2), (700, 1)])
+def test_every_step_width(n, batch, bands, blocks, restore_lookahead):
+    # steps of 1..4 k-blocks (the pass picks 1 or 2) at every look-ahead
+    # depth, on the dense, directed and packed passes and on ranges that
+    # start inside a step
+    from oracle import steps
+    U0, L0 = sound_input(n, batch, seed=97 * n + 7 * bands + blocks)
+    Ue, Le = oracle.smooth(U0, L0)
+    dgb.set_lookahead(bands)
+    dgb.set_step_blocks(blocks)
+    assert dgb.step_blocks(n, batch) == blocks
+    tag = f"n={n} batch={batch} bands={bands} blocks={blocks}"
+    Ug, Lg = gpu_pass(U0, L0, "blocked")
+    assert_bits(Ug, Lg, Ue, Le, "blocked " + tag)
+    U, L = dev(U0), dev(L0)
+    dgb.smooth_directed(U, L, algo="blocked")
+    assert_bits(host(U), host(L), Ue, Le, "directed " + tag)
+    P = dgb.pack(dev(U0), dev(L0))
+    dgb.smooth_packed(P)
+    assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
+    U, L = dev(U0), dev(L0)
+    for a, b in ((0, 192), (192, n)):
+        dgb.smooth_range(U, L, a, b, algo="blocked")
+    assert_bits(host(U), host(L), Ue, Le, "ranges 0,192,n " + tag)
 
 
 def test_walk_molecules_batched():

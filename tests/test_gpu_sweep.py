@@ -2,7 +2,8 @@
 
 Each case draws n (including k-block and tile tails), a batch, an algorithm, the layout (dense
 or packed), the rounding entry point (plain or directed; on grid inputs both must give the plain
-pass's bits) and a look-ahead depth (automatic or forced 0, 1, 2). It runs one full pass, or a
+pass's bits), a look-ahead depth (automatic or forced 0, 1, 2) and a step width (automatic or
+forced 1..4 k-blocks). It runs one full pass, or a
 pass split at a k-block boundary, and compares every entry with the oracle bit for bit. The draws
 are fixed by the seed, so a failure names a reproducible case.
 """
@@ -29,11 +30,13 @@ def _case(seed):
     directed = bool(rng.integers(0, 2))
     depth = int(rng.choice([-1, 0, 1, 2]))
     split = bool(rng.integers(0, 2)) and n > 128
-    return n, batch, algo, packed, directed, depth, split
+    blocks = int(rng.choice([-1, 1, 2, 3, 4]))
+    return n, batch, algo, packed, directed, depth, split, blocks
 
 
-def _run(U0, L0, n, algo, packed, directed, depth, split):
+def _run(U0, L0, n, algo, packed, directed, depth, split, blocks):
     dgb.set_lookahead(depth)
+    dgb.set_step_blocks(blocks)
     try:
         cuts = [0, 128, n] if split else [0, n]
         if packed:
@@ -53,16 +56,17 @@ def _run(U0, L0, n, algo, packed, directed, depth, split):
         return U.cpu().numpy(), L.cpu().numpy()
     finally:
         dgb.set_lookahead(-1)
+        dgb.set_step_blocks(-1)
 
 
 @pytest.mark.parametrize("seed", range(64))
 def test_random_case_matches_oracle(seed):
-    n, batch, algo, packed, directed, depth, split = _case(seed)
+    n, batch, algo, packed, directed, depth, split, blocks = _case(seed)
     tag = (f"seed={seed} n={n} batch={batch} algo={algo} packed={packed} "
-           f"directed={directed} depth={depth} split={split}")
+           f"directed={directed} depth={depth} split={split} blocks={blocks}")
     U0, L0, _ = gen.random_sound_bounds(n, seed=seed, batch=batch, box=6.0 + n / 8)
     Ue, Le = oracle.smooth(U0, L0)
-    A, B = _run(U0, L0, n, algo, packed, directed, depth, split)
+    A, B = _run(U0, L0, n, algo, packed, directed, depth, split, blocks)
     if packed:
         assert np.array_equal(A.view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
     else:

@@ -1,15 +1,16 @@
 """CPU model of the blocked pass's schedule (test code only).
 
-The GPU pass (csrc/blocked.hip) runs in steps of one k-block of BK = 64
-atoms (one step ahead) or two (two steps ahead), per step
+The GPU pass (csrc/blocked.hip) runs in steps of W k-blocks of BK = 64
+atoms (W = 1 one step ahead, 2 to 4 two steps ahead, any of 1..4 when forced),
+per step
   panel    the rows of the step's bands made final for all of its rounds:
-           phases 1+2 of its first block (the rounds of band K over the
-           diagonal tile (K,K) and, in the same loop, over each panel tile
-           of band K, one workgroup per panel tile, panel tiles read from
-           their fresh orientation (upper TILE x TILE region) and written in
-           both orientations); with two blocks, block K on band K+1 (a
-           strip), phases 1+2 of K+1, and block K+1 on band K (a strip that
-           writes both orientations);
+           for each band b+j of the step in turn, the step's earlier blocks
+           on it (a strip), phases 1+2 of block b+j (the rounds of band b+j
+           over the diagonal tile and, in the same loop, over each panel
+           tile of the band, one workgroup per panel tile, panel tiles read
+           from their fresh orientation (upper TILE x TILE region) and
+           written in both orientations), and block b+j on the step's
+           earlier bands (a strip that writes both orientations);
   phase 3  the bands of the next steps first (strips, on a second stream,
            followed there by the next step's panel), and every other live
            cell of the upper TILE x TILE tiles (the bulk, on the caller's
@@ -43,8 +44,9 @@ def fresh(a, b):
 
 
 class Model:
-    def __init__(self, U0, L0, depth=2, skip_second=True):
-        self.depth = depth                # bands run ahead on the side stream
+    def __init__(self, U0, L0, depth=2, skip_second=True, W=None):
+        self.depth = depth                # steps run ahead on the side stream
+        self.W = W if W else (2 if depth == 2 else 1)   # k-blocks per step
         self.skip_second = skip_second    # False plants an overlap (self-test)
         self.n = U0.shape[0]
         self.U = pins.units(U0).copy()
@@ -157,13 +159,16 @@ class Model:
 
     def step_panel(self, Ks):
         """The rows of the step's bands Ks final for all of its rounds, as
-        (kind, reads, writes) launches."""
-        b = Ks[0]
-        out = [("phase12", *self.phase12(b))]
-        if len(Ks) == 2:
-            out.append(("panel-strip", *self.strip([b], b + 1, {b})))
-            out.append(("phase12", *self.phase12(b + 1)))
-            out.append(("panel-strip", *self.strip([b + 1], b, {b + 1}, both=True)))
+        (kind, reads, writes) launches.  On the GPU the rows of the last
+        strip of each band are one launch (row band Ks[r] leaves out the
+        columns of the bands before it, whose blocks those rows hold)."""
+        out = []
+        for j, K in enumerate(Ks):
+            if j > 0:
+                out.append(("panel-strip", *self.strip(Ks[:j], K, set(Ks[:j]))))
+            out.append(("phase12", *self.phase12(K)))
+            for r, A in enumerate(Ks[:j]):
+                out.append(("panel-strip", *self.strip([K], A, set(Ks[:r]) | {K}, both=True)))
         return out
 
     def run(self):
@@ -182,8 +187,7 @@ class Model:
         that bulk(t) may overlap is everything after ready(t) and before the
         side's wait for bulk(t); each such footprint must be disjoint from
         bulk(t)'s."""
-        TB, deep = self.TB, self.depth == 2
-        W = 2 if deep else 1
+        TB, deep, W = self.TB, self.depth == 2, self.W
         steps = [list(range(b, min(b + W, TB))) for b in range(0, TB, W)]
         NS = len(steps)
         self.step_panel(steps[0])
@@ -232,12 +236,14 @@ class Model:
         return self.U, self.L
 
 
-@pytest.mark.parametrize("n,depth", [(65, 2), (130, 2), (200, 2), (257, 2), (330, 2),
-                                     (130, 1), (257, 1)])
-def test_schedule_model_matches_oracle_and_streams_are_disjoint(n, depth):
+@pytest.mark.parametrize("n,depth,W", [(65, 2, None), (130, 2, None), (200, 2, None),
+                                       (257, 2, None), (330, 2, None), (130, 1, None),
+                                       (257, 1, None), (330, 2, 3), (330, 2, 4), (257, 1, 3),
+                                       (200, 1, 2)])
+def test_schedule_model_matches_oracle_and_streams_are_disjoint(n, depth, W):
     U0, L0, _ = gen.random_sound_bounds(n, seed=n, box=6.0 + n / 8)
     Ue, Le = oracle.smooth(U0, L0)
-    Um, Lm = Model(U0, L0, depth=depth).run()
+    Um, Lm = Model(U0, L0, depth=depth, W=W).run()
     assert np.array_equal(Um, pins.units(Ue))
     assert np.array_equal(Lm, pins.units(Le))
 
