@@ -474,16 +474,17 @@ __device__ __forceinline__ void store_transposed(float *P, int64_t n, int64_t r0
 // slower.)
 
 // Phase 3 of the k-blocks K .. K+nk-1 (their atoms in order) on the row
-// bands A0 + r, r < grid.z, run ahead of the bulk on the second stream or
-// inside a step's panel.  Row band A0 + r takes every column band outside
-// [X0, X1 + r) and other than Y (< 0: none; Y >= X1 + r).  The callers put
-// the atoms' own bands (whose rows are final) in that set, and X1 = A0
-// where grid.z > 1: then row band A0 + r leaves out the row bands before it
-// (block (A0+r, A0+r') is block (A0+r', A0+r) of an earlier row band).
-// grid.x = the first row band's column bands, grid.y = molecules.  Block (A, J) is read and
-// written in its fresh orientation (dense) or as its U and L slots (packed);
-// with `both` (dense) its other orientation is written too, so that the
-// rows of band A can serve as a panel afterwards.  Thread (ty, tx) owns a
+// bands A0 + r, r < grid.z, other than the atoms' own, run ahead of the bulk
+// on the second stream or inside a step's panel.  Row band A0 + r takes
+// every column band outside [X0, X1 + r) and other than Y (< 0: none).  The
+// callers put the atoms' own bands (whose rows are final) in that set, and
+// X1 = A0 where grid.z > 1: then row band A0 + r leaves out the row bands
+// before it (block (A0+r, A0+r') is block (A0+r', A0+r) of an earlier row
+// band).  grid.x = the first row band's column bands, grid.y = molecules.
+// Block (A, J) is read and written in its fresh orientation (dense) or as
+// its U and L slots (packed); with `both` (dense), row bands before K write
+// the other orientation too, so that their rows can serve as a panel
+// afterwards.  Thread (ty, tx) owns a
 // 4x4 cell tile.  The panel rows of the atoms are staged through LDS in
 // chunks of KC atoms; the global loads of chunk c+1 are issued before chunk
 // c is computed.  Per atom and cell the VALU does one add and one min for U,
@@ -510,7 +511,8 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
   const int64_t xe = X1 + blockIdx.z < TB ? X1 + blockIdx.z : TB;
   const int64_t y = Y >= xe && Y < TB ? Y : -1;
   int64_t B = blockIdx.x;
-  if (B >= TB - (xe - X0) - (y >= 0)) return;  // uniform, before any barrier
+  // uniform over the workgroup, before any barrier
+  if (B >= TB - (xe - X0) - (y >= 0) || (A >= K && A < K + nk)) return;
   if (B >= X0) B += xe - X0;
   if (y >= 0 && B >= y) ++B;
   const bool rowor = fresh(A, B);  // stored as (A, B), else as its transpose (B, A)
@@ -645,7 +647,7 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
       store_transposed<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, u, tr);
       store_transposed<VEC>(Lb, n, a0, j0, bA, bJ, wy, wx, l, tr);
     }
-    if (!PK && both && A != B) {
+    if (!PK && both && A < K && A != B) {
       // the other orientation too (uniform over the workgroup)
       if (rowor) {
         store_transposed<VEC>(Ub, n, a0, j0, bA, bJ, wy, wx, u, tr);
@@ -1218,16 +1220,16 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
                   dim3(kThreads), st, U, L, n, batch, K, nk, A0, X0, X1, Y, (int)both);
   };
   // The rows of step t's bands final for all of its rounds, in both
-  // orientations.  Band b+j in turn takes the step's earlier blocks (one
-  // strip), runs phases 1-2 of its own block, and that block then goes over
-  // the earlier bands (one strip, both orientations).
+  // orientations: per block b+j in turn, its phases 1-2, then the block on
+  // the step's other bands (one strip; the bands before b+j, whose rows are
+  // panel rows already, in both orientations).  This is the one-block
+  // schedule restricted to the step's bands.
   auto step_panel = [&](int64_t t, hipStream_t st) -> hipError_t {
     const int64_t b = lo(t), w = hi(t) - b;
     hipError_t r = hipSuccess;
     for (int64_t j = 0; j < w && r == hipSuccess; ++j) {
-      if (j > 0 && (r = strip(b, j, b + j, 1, b, b + j, -1, false, st)) != hipSuccess) break;
       if ((r = phase12(b + j, st)) != hipSuccess) break;
-      if (j > 0) r = strip(b + j, 1, b, j, b, b, b + j, true, st);
+      if (w > 1) r = strip(b + j, 1, b, w, b, b, b + j, true, st);
     }
     return r;
   };

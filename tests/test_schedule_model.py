@@ -4,13 +4,13 @@ The GPU pass (csrc/blocked.hip) runs in steps of W k-blocks of BK = 64
 atoms (W = 1 one step ahead, 2 to 4 two steps ahead, any of 1..4 when forced),
 per step
   panel    the rows of the step's bands made final for all of its rounds:
-           for each band b+j of the step in turn, the step's earlier blocks
-           on it (a strip), phases 1+2 of block b+j (the rounds of band b+j
-           over the diagonal tile and, in the same loop, over each panel
-           tile of the band, one workgroup per panel tile, panel tiles read
-           from their fresh orientation (upper TILE x TILE region) and
-           written in both orientations), and block b+j on the step's
-           earlier bands (a strip that writes both orientations);
+           for each block b+j of the step in turn, phases 1+2 of it (the
+           rounds of band b+j over the diagonal tile and, in the same loop,
+           over each panel tile of the band, one workgroup per panel tile,
+           panel tiles read from their fresh orientation (upper TILE x TILE
+           region) and written in both orientations), then block b+j on the
+           step's other bands (one strip; the bands before b+j, which are
+           panel rows already, in both orientations);
   phase 3  the bands of the next steps first (strips, on a second stream,
            followed there by the next step's panel), and every other live
            cell of the upper TILE x TILE tiles (the bulk, on the caller's
@@ -159,16 +159,16 @@ class Model:
 
     def step_panel(self, Ks):
         """The rows of the step's bands Ks final for all of its rounds, as
-        (kind, reads, writes) launches.  On the GPU the rows of the last
-        strip of each band are one launch (row band Ks[r] leaves out the
-        columns of the bands before it, whose blocks those rows hold)."""
+        (kind, reads, writes) launches.  On the GPU each block's strip over
+        the other bands is one launch (row band Ks[r] leaves out the columns
+        of the bands before it, whose blocks those rows hold)."""
         out = []
-        for j, K in enumerate(Ks):
-            if j > 0:
-                out.append(("panel-strip", *self.strip(Ks[:j], K, set(Ks[:j]))))
+        for K in Ks:
             out.append(("phase12", *self.phase12(K)))
-            for r, A in enumerate(Ks[:j]):
-                out.append(("panel-strip", *self.strip([K], A, set(Ks[:r]) | {K}, both=True)))
+            for r, A in enumerate(Ks):
+                if A != K:
+                    out.append(("panel-strip",
+                                *self.strip([K], A, set(Ks[:r]) | {K}, both=A < K)))
         return out
 
     def run(self):
