@@ -51,6 +51,8 @@ OPS_PER_TRIPLE = 6              # 1 add + 1 min (upper), 2 sub + 2 max (lower)
 TILE, BK = 128, 64              # blocked-path geometry (csrc/blocked.hip)
 COUNTERS = os.path.join(ROOT, "profiles", "k_quads_n12288_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "distance_geometry_bound_amd", "csrc", "blocked.hip")
+ROUND_COUNTERS = os.path.join(ROOT, "profiles", "k_round_vec_n12288_counters.json")
+ROUND_SRC = os.path.join(ROOT, "distance_geometry_bound_amd", "csrc", "round.hip")
 
 
 def parse():
@@ -121,14 +123,15 @@ def source_digest(path):
     return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()
 
 
-def counters_traffic(n, batch):
-    """HBM bytes per phase-3 launch from the committed counter run, if the
-    kernel source (comments aside) is unchanged since it was taken; else None."""
+def counters_traffic(n, batch, record=COUNTERS, source=KERNEL_SRC):
+    """HBM bytes per launch of a kernel from its committed counter run (the
+    phase-3 bulk by default), if the kernel source (comments aside) is
+    unchanged since it was taken; else None."""
     try:
-        rec = json.load(open(COUNTERS))
+        rec = json.load(open(record))
     except (OSError, ValueError):
         return None
-    sha = source_digest(KERNEL_SRC)
+    sha = source_digest(source)
     if rec.get("source_sha256") != sha or rec.get("n") != n or rec.get("batch") != batch:
         return None
     return rec.get("traffic_bytes_per_launch")
@@ -397,7 +400,8 @@ def main():
             out["perk"] = {"kernel": "k_round_vec" if n % 4 == 0 else "k_round_scalar",
                            "rounds": R, "ms_per_round": ms, "GBps": gbps,
                            "frac_hbm": gbps * 1e9 / HBM_PEAK,
-                           "bytes_per_round": 16 * n * n * batch}
+                           "bytes_per_round": 16 * n * n * batch,
+                           "traffic": counters_traffic(n, batch, ROUND_COUNTERS, ROUND_SRC)}
 
     if args.steps_extra:
         out.update(extra_steps(W, U, L, U0, L0, dev))
