@@ -261,6 +261,30 @@ def test_n12288_invariants():
     assert torch.equal(L2.view(torch.int32), L.view(torch.int32))
 
 
+def test_n12288_schedule_independent():
+    # every schedule of the pass reaches the same bits (exact arithmetic on
+    # the grid): the benchmark's schedule (two steps ahead, steps of four
+    # k-blocks) against one stream with one-block steps, over the whole
+    # matrix, and the packed pass against the packed form of that result
+    W, U, L = big()
+    assert dgb.lookahead_bands(W.n) == 2 and dgb.step_blocks(W.n) == 4
+    try:
+        dgb.set_lookahead(0)
+        dgb.set_step_blocks(1)
+        U1, L1 = dev(W.U[0]), dev(W.L[0])
+        dgb.smooth(U1, L1, algo="blocked")
+        torch.cuda.synchronize(DEV)
+    finally:
+        dgb.set_lookahead(-1)
+        dgb.set_step_blocks(-1)
+    assert torch.equal(U1.view(torch.int32), U.view(torch.int32))
+    assert torch.equal(L1.view(torch.int32), L.view(torch.int32))
+    del U1, L1
+    P = dgb.pack(dev(W.U[0]), dev(W.L[0]))
+    dgb.smooth_packed(P)
+    assert torch.equal(P.view(torch.int32), dgb.pack(U, L).view(torch.int32))
+
+
 # -------------------------------------------------------------- contract
 def test_deterministic_and_side_stream():
     U0, L0 = sound_input(1000, 1, seed=77)
