@@ -14,8 +14,10 @@
 //            k_diag_panel, one workgroup per panel tile);
 //   phase 3  every remaining cell: all bK rounds at once from the finished
 //            panel (k_quads / k_quads_packed: the bulk on 64x64 quadrants;
-//            k_strip: one band alone when running ahead).  This is where
-//            1 - O(BK/n) of the work is.
+//            k_strip: given row bands alone, when running ahead or inside
+//            a step's panel).  This is where 1 - O(BK/n) of the work is.
+// A step of w k-blocks (launch_blocked) is the same with 64w atoms in
+// phase 3; its panel is built from the phase 1-2 kernel and strips.
 //
 // Symmetric schedule.  U and L stay exactly symmetric, so only the cells of
 // TILE x TILE tiles (I,J) with I <= J are kept current ("fresh"); tiles below
@@ -60,8 +62,8 @@ constexpr int64_t kAheadTiles = 256;
 constexpr int64_t kPanelFill = 256;
 constexpr int kThreads = 256;
 
-// The side-stream kernels (band K+1 strip, then phases 1-2 of block K+1) are
-// the critical path of a k-block whenever they share compute units with the
+// The side-stream kernels (strips, and phases 1-2 of the next blocks) are
+// on the critical path of a step whenever they share compute units with the
 // bulk kernel: their waves take instruction-issue priority over its waves on
 // the same SIMD (wave priority only; the streams keep the default priority).
 __device__ __forceinline__ void critical_path_priority() { __builtin_amdgcn_s_setprio(2); }
@@ -349,8 +351,8 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
 // L[k][x] = P[max(k,x)][min(k,x)].  Right of the band (x > k) U is a row
 // segment of P and L a column segment; left of it the other way round.  A
 // column segment is read as rows of P, four consecutive k per float4.  Each
-// of the 256 threads loads one float4 of each kind.  `dead` (band K, band
-// K+1 or beyond n: values no live cell uses) gives the neutral values.
+// of the 256 threads loads one float4 of each kind.  `dead` (values no live
+// cell uses) gives the neutral values.
 struct HalfLoad {
   float4 direct, across;
 };
@@ -1165,9 +1167,9 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
              : (ru ? (vec ? k_strip<true, false, true> : k_strip<false, false, true>)
                    : (vec ? k_strip<true, false, false> : k_strip<false, false, false>));
   // With many phase-3 tiles the bulk runs long enough to hide phases 1-2 of
-  // the next blocks: they run two bands ahead, on 256-thread workgroups that
+  // the next blocks: they run two steps ahead, on 256-thread workgroups that
   // fit where phase-3 workgroups finish.  With fewer tiles they are the
-  // critical path: one band ahead or none, on 1024-thread workgroups that
+  // critical path: one step ahead or none, on 1024-thread workgroups that
   // hide the latency of their rounds best.
   const int64_t pairs = T * (T + 1) / 2;
   const int ahead = lookahead_bands(n, batch, packed);
