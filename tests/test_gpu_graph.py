@@ -1,0 +1,62 @@
+"""The blocked pass under HIP graph capture (needs an MI355X).
+
+A caller may capture dbs_smooth into a graph: the library's second stream
+joins the capture through its ordering events, so the graph holds both
+streams' launches and their dependencies.  Each case captures one pass, then
+replays the graph three times with eager work in between, and checks every
+replay against the oracle bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import distance_geometry_bound_amd as dgb
+import oracle
+from distance_geometry_bound_amd import gen
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("n,batch,bands,blocks", [(700, 1, 2, 2), (700, 1, 2, 4), (385, 2, 1, 1),
+                                                  (385, 2, 0, 2)])
+def test_captured_pass_replays_match_oracle(n, batch, bands, blocks):
+    U0, L0, _ = gen.random_sound_bounds(n, seed=500 + n + bands, batch=batch, box=6.0 + n / 8)
+    Ue, Le = oracle.smooth(U0, L0)
+    Ui = torch.from_numpy(U0).to(DEV)
+    Li = torch.from_numpy(L0).to(DEV)
+    U, L = torch.empty_like(Ui), torch.empty_like(Li)
+    dgb.set_lookahead(bands)
+    dgb.set_step_blocks(blocks)
+    try:
+        s = torch.cuda.Stream(DEV)
+        s.wait_stream(torch.cuda.current_stream(DEV))
+        with torch.cuda.stream(s):               # warm-up on the capture stream
+            U.copy_(Ui)
+            L.copy_(Li)
+            dgb.smooth(U, L, algo="blocked")
+        torch.cuda.current_stream(DEV).wait_stream(s)
+        torch.cuda.synchronize(DEV)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            U.copy_(Ui)
+            L.copy_(Li)
+            dgb.smooth(U, L, algo="blocked")
+        torch.cuda.synchronize(DEV)
+        for rep in range(3):
+            U.fill_(-1.0)
+            L.fill_(-1.0)
+            g.replay()
+            torch.cuda.synchronize(DEV)
+            tag = f"n={n} batch={batch} bands={bands} blocks={blocks} replay {rep}"
+            assert np.array_equal(U.cpu().numpy().view(np.uint32), Ue.view(np.uint32)), tag
+            assert np.array_equal(L.cpu().numpy().view(np.uint32), Le.view(np.uint32)), tag
+            # eager work between replays, on the same buffers
+            U.copy_(Ui)
+            L.copy_(Li)
+            dgb.smooth(U, L, algo="blocked")
+            torch.cuda.synchronize(DEV)
+        del g
+    finally:
+        dgb.set_lookahead(-1)
+        dgb.set_step_blocks(-1)
