@@ -155,6 +155,30 @@ def test_directed_blocked_within_rounding_bound(n, batch):
     assert bits_equal(host(P), steps.pack(Ug, Lg))
 
 
+@pytest.mark.parametrize("n,batch,bands,blocks", [(700, 1, 2, 2), (700, 1, 2, 4), (700, 1, 1, 3),
+                                                  (385, 2, 2, 4)])
+def test_directed_steps_within_rounding_bound(n, batch, bands, blocks):
+    # steps of several k-blocks group the roundings differently again; every
+    # path sum still takes at most n - 2 roundings, so the same bound holds
+    U0, L0 = unquantised(n, batch, seed=3 * n + blocks)
+    Ue, Le = oracle.smooth_directed(U0, L0)
+    dgb.set_lookahead(bands)
+    dgb.set_step_blocks(blocks)
+    try:
+        U, L = dev(U0), dev(L0)
+        dgb.smooth_directed(U, L, algo="blocked")
+        Ug, Lg = host(U), host(L)
+        P = dgb.pack(dev(U0), dev(L0))
+        dgb.smooth_packed_directed(P)
+        Pg = host(P)
+    finally:
+        dgb.set_lookahead(-1)
+        dgb.set_step_blocks(-1)
+    assert within_bound(Ug, Lg, Ue, Le, L0)
+    assert np.all(Lg <= Ug)
+    assert bits_equal(Pg, steps.pack(Ug, Lg))
+
+
 @pytest.mark.parametrize("n", [300, 700])
 def test_directed_blocked_sound_on_line(n):
     U0, L0, X = gen.unquantised_line(n, seed=n)
