@@ -44,6 +44,11 @@ def fresh(a, b):
 
 
 class Model:
+    """Footprints are boolean n x n masks of the cells a launch reads or
+    writes.  Within a launch the relaxations are evaluated per block with
+    numpy; the values are exact int64 units, so a min or max over a block's
+    candidates does not depend on their order."""
+
     def __init__(self, U0, L0, depth=2, skip_second=True, W=None):
         self.depth = depth                # steps run ahead on the side stream
         self.W = W if W else (2 if depth == 2 else 1)   # k-blocks per step
@@ -55,14 +60,10 @@ class Model:
         self.T = -(-self.n // TILE)
 
     def band(self, K):
-        return list(range(K * BK, min(self.n, K * BK + BK)))
+        return np.arange(K * BK, min(self.n, K * BK + BK))
 
-    def relax(self, i, j, k, U, L):
-        """One round k on cell (i, j), reading row k for both operands
-        (U[i,k] = U[k,i] by symmetry)."""
-        u = min(U[i, j], U[k, i] + U[k, j])
-        l = max(L[i, j], L[k, i] - U[k, j], L[k, j] - U[k, i])
-        return u, l
+    def mask(self):
+        return np.zeros((self.n, self.n), dtype=bool)
 
     def phase12(self, K):
         """Phases 1 and 2 in one launch (k_diag_panel): every panel workgroup
@@ -71,61 +72,80 @@ class Model:
         the round (D's column m is its row m by symmetry).  Panel tiles are
         read from their fresh orientation and written in both; D is written
         as a full square."""
-        reads, writes = set(), set()
+        reads, writes = self.mask(), self.mask()
         kb = self.band(K)
         U, L = self.U, self.L
-        D = {(a, b): (U[a, b], L[a, b]) for a in kb for b in kb}
-        reads |= set(D)
-        R = {}
+        ix = np.ix_(kb, kb)
+        Du, Dl = U[ix].copy(), L[ix].copy()
+        reads[ix] = True
+        cols, Ru, Rl = [], [], []
         for J in range(self.TB):
             if J == K:
                 continue
-            for a in kb:
-                for c in self.band(J):
-                    src = (a, c) if fresh(K, J) else (c, a)
-                    R[(a, c)] = (U[src], L[src])
-                    reads.add(src)
-        for m in kb:
-            def rel(cell, row):
-                (u, l), (cu, cl), (ru, rl) = cell, D[(m, row[0])], row[1]
-                return min(u, cu + ru), max(l, cl - ru, rl - cu)
-            newD = {(a, b): rel(D[(a, b)], (a, D[(m, b)])) for (a, b) in D}
-            newR = {(a, c): rel(R[(a, c)], (a, R[(m, c)])) for (a, c) in R}
-            D, R = newD, newR
-        for (a, b), (u, l) in D.items():
-            U[a, b], L[a, b] = u, l
-            writes.add((a, b))
-        for (a, c), (u, l) in R.items():
-            U[a, c] = U[c, a] = u
-            L[a, c] = L[c, a] = l
-            writes |= {(a, c), (c, a)}
+            jb = self.band(J)
+            if fresh(K, J):
+                Ru.append(U[np.ix_(kb, jb)]), Rl.append(L[np.ix_(kb, jb)])
+                reads[np.ix_(kb, jb)] = True
+            else:
+                Ru.append(U[np.ix_(jb, kb)].T), Rl.append(L[np.ix_(jb, kb)].T)
+                reads[np.ix_(jb, kb)] = True
+            cols.append(jb)
+        cols = np.concatenate(cols)
+        Ru, Rl = np.concatenate(Ru, axis=1), np.concatenate(Rl, axis=1)
+        for m in range(len(kb)):
+            du, dl = Du[m].copy(), Dl[m].copy()      # D[m][*] = D[*][m]
+            ru, rl = Ru[m].copy(), Rl[m].copy()      # R[m][*]
+            Du = np.minimum(Du, du[:, None] + du[None, :])
+            Dl = np.maximum(Dl, np.maximum(dl[:, None] - du[None, :], dl[None, :] - du[:, None]))
+            Ru = np.minimum(Ru, du[:, None] + ru[None, :])
+            Rl = np.maximum(Rl, np.maximum(dl[:, None] - ru[None, :], rl[None, :] - du[:, None]))
+        U[ix], L[ix] = Du, Dl
+        writes[ix] = True
+        U[np.ix_(kb, cols)], L[np.ix_(kb, cols)] = Ru, Rl
+        U[np.ix_(cols, kb)], L[np.ix_(cols, kb)] = Ru.T, Rl.T
+        writes[np.ix_(kb, cols)] = True
+        writes[np.ix_(cols, kb)] = True
         return reads, writes
+
+    def _phase3(self, kb, rows, cols):
+        """Candidates of the atoms kb for the cells rows x cols, from the
+        atom rows (U[i,k] = U[k,i]): (best U, best L) blocks."""
+        Ur, Uc = self.U[np.ix_(kb, rows)], self.U[np.ix_(kb, cols)]
+        Lr, Lc = self.L[np.ix_(kb, rows)], self.L[np.ix_(kb, cols)]
+        bu = (Ur[:, :, None] + Uc[:, None, :]).min(0)
+        bl = np.maximum((Lr[:, :, None] - Uc[:, None, :]).max(0),
+                        (Lc[:, None, :] - Ur[:, :, None]).max(0))
+        return bu, bl
 
     def strip(self, Ks, A, excl, both=False):
         """Phase 3 of the blocks Ks (their atoms in order) on row band A only:
         blocks (A, J) for every column band J outside `excl`, each in its
         fresh orientation, and with `both` in the other one too."""
-        reads, writes = set(), set()
-        kb = [k for K in Ks for k in self.band(K)]
+        reads, writes = self.mask(), self.mask()
+        kb = np.concatenate([self.band(K) for K in Ks])
         ab = self.band(A)
         for J in range(self.TB):
             if J in excl:
                 continue
             jb = self.band(J)
-            reads |= {(k, x) for k in kb for x in ab + jb}
-            for a in ab:
-                for c in jb:
-                    dst = (a, c) if fresh(A, J) else (c, a)
-                    u, l = self.U[dst], self.L[dst]
-                    reads.add(dst)
-                    for k in kb:
-                        u = min(u, self.U[k, a] + self.U[k, c])
-                        l = max(l, self.L[k, a] - self.U[k, c], self.L[k, c] - self.U[k, a])
-                    self.U[dst], self.L[dst] = u, l
-                    writes.add(dst)
-                    if both:
-                        self.U[dst[::-1]], self.L[dst[::-1]] = u, l
-                        writes.add(dst[::-1])
+            reads[np.ix_(kb, np.concatenate([ab, jb]))] = True
+            bu, bl = self._phase3(kb, ab, jb)
+            dst = np.ix_(ab, jb) if fresh(A, J) else np.ix_(jb, ab)
+            cur_u, cur_l = (self.U[dst], self.L[dst]) if fresh(A, J) else (self.U[dst].T, self.L[dst].T)
+            reads[dst] = True
+            nu, nl = np.minimum(cur_u, bu), np.maximum(cur_l, bl)
+            if fresh(A, J):
+                self.U[dst], self.L[dst] = nu, nl
+            else:
+                self.U[dst], self.L[dst] = nu.T, nl.T
+            writes[dst] = True
+            if both:
+                other = np.ix_(jb, ab) if fresh(A, J) else np.ix_(ab, jb)
+                if fresh(A, J):
+                    self.U[other], self.L[other] = nu.T, nl.T
+                else:
+                    self.U[other], self.L[other] = nu, nl
+                writes[other] = True
         return reads, writes
 
     def bulk(self, Ks, skip_bands):
@@ -133,28 +153,27 @@ class Model:
         TILE x TILE tiles, a quadrant in a band of Ks or in a skipped band
         left whole."""
         n = self.n
-        reads, writes = set(), set()
-        dead = set()
+        reads, writes = self.mask(), self.mask()
+        live = np.ones(n, dtype=bool)
         for b in list(Ks) + list(skip_bands):
-            dead |= set(self.band(b))
-        kb = [k for K in Ks for k in self.band(K)]
-        new = {}
+            live[self.band(b)] = False
+        kb = np.concatenate([self.band(K) for K in Ks])
+        new = []
         for J in range(self.T):
             for I in range(J + 1):
-                rows = [i for i in range(I * TILE, min(n, I * TILE + TILE)) if i not in dead]
-                cols = [j for j in range(J * TILE, min(n, J * TILE + TILE)) if j not in dead]
-                reads |= {(k, x) for k in kb for x in rows + cols}
-                for i in rows:
-                    for j in cols:
-                        u, l = self.U[i, j], self.L[i, j]
-                        reads.add((i, j))
-                        for k in kb:
-                            u = min(u, self.U[k, i] + self.U[k, j])
-                            l = max(l, self.L[k, i] - self.U[k, j], self.L[k, j] - self.U[k, i])
-                        new[(i, j)] = (u, l)
-                        writes.add((i, j))
-        for (i, j), (u, l) in new.items():
-            self.U[i, j], self.L[i, j] = u, l
+                ti = np.arange(I * TILE, min(n, I * TILE + TILE))
+                tj = np.arange(J * TILE, min(n, J * TILE + TILE))
+                rows, cols = ti[live[ti]], tj[live[tj]]
+                if len(rows) == 0 or len(cols) == 0:
+                    continue
+                reads[np.ix_(kb, np.concatenate([rows, cols]))] = True
+                cell = np.ix_(rows, cols)
+                reads[cell] = True
+                bu, bl = self._phase3(kb, rows, cols)
+                new.append((cell, np.minimum(self.U[cell], bu), np.maximum(self.L[cell], bl)))
+                writes[cell] = True
+        for cell, nu, nl in new:
+            self.U[cell], self.L[cell] = nu, nl
         return reads, writes
 
     def step_panel(self, Ks):
@@ -216,30 +235,29 @@ class Model:
                 ready_at[t + 1] = len(side)
             ahead = steps[t + 1:t + 3] if deep and self.skip_second else steps[t + 1:t + 2]
             bulks[t] = self.bulk(steps[t], [b for s_ in ahead for b in s_])
-        sym = lambda cells: cells | {(j, i) for (i, j) in cells}
+        sym = lambda m: m | m.T
         for t, (br, bw) in bulks.items():
             lo = ready_at.get(t, 0)
             hi = wait_at.get(t, len(side))
             for it, kind, sr, sw in side[lo:hi]:
                 tag = f"bulk({t}) vs {kind}({it})"
-                assert not (sw & (br | bw)), tag + ": side writes what the bulk touches"
-                assert not (bw & sr), tag + ": bulk writes what the side reads"
+                assert not np.any(sw & (br | bw)), tag + ": side writes what the bulk touches"
+                assert not np.any(bw & sr), tag + ": bulk writes what the side reads"
                 # packed storage: a logical cell (i,j) lives in P[min][max] (U)
                 # and P[max][min] (L), so a footprint becomes its symmetric closure
-                assert not (sym(sw) & sym(br | bw)), tag + ": packed overlap (writes)"
-                assert not (sym(bw) & sym(sr)), tag + ": packed overlap (reads)"
-        n = self.n
-        for i in range(n):
-            for j in range(n):
-                if (i // BK) // RATIO > (j // BK) // RATIO:
-                    self.U[i, j], self.L[i, j] = self.U[j, i], self.L[j, i]
+                assert not np.any(sym(sw) & sym(br | bw)), tag + ": packed overlap (writes)"
+                assert not np.any(sym(bw) & sym(sr)), tag + ": packed overlap (reads)"
+        tile = (np.arange(self.n) // BK) // RATIO
+        stale = tile[:, None] > tile[None, :]
+        self.U[stale], self.L[stale] = self.U.T[stale], self.L.T[stale]
         return self.U, self.L
 
 
 @pytest.mark.parametrize("n,depth,W", [(65, 2, None), (130, 2, None), (200, 2, None),
                                        (257, 2, None), (330, 2, None), (130, 1, None),
                                        (257, 1, None), (330, 2, 3), (330, 2, 4), (257, 1, 3),
-                                       (200, 1, 2)])
+                                       (200, 1, 2), (520, 2, 3), (520, 2, 4), (700, 2, 4),
+                                       (520, 1, 4)])
 def test_schedule_model_matches_oracle_and_streams_are_disjoint(n, depth, W):
     U0, L0, _ = gen.random_sound_bounds(n, seed=n, box=6.0 + n / 8)
     Ue, Le = oracle.smooth(U0, L0)
@@ -255,3 +273,24 @@ def test_schedule_model_detects_a_planted_overlap():
     U0, L0, _ = gen.random_sound_bounds(260, seed=1, box=36.0)
     with pytest.raises(AssertionError, match="side writes what the bulk touches"):
         Model(U0, L0, skip_second=False).run()
+
+
+def test_schedule_model_detects_a_missing_panel_orientation():
+    # a step panel whose strips write only the fresh orientation leaves the
+    # stale copy of the earlier bands' rows behind; the bulk reads those rows
+    # as panel rows, so the pass must miss the oracle
+    class Broken(Model):
+        def step_panel(self, Ks):
+            out = []
+            for K in Ks:
+                out.append(("phase12", *self.phase12(K)))
+                for r, A in enumerate(Ks):
+                    if A != K:
+                        out.append(("panel-strip",
+                                    *self.strip([K], A, set(Ks[:r]) | {K}, both=False)))
+            return out
+
+    U0, L0, _ = gen.random_sound_bounds(520, seed=520, box=6.0 + 520 / 8)
+    Ue, Le = oracle.smooth(U0, L0)
+    Um, Lm = Broken(U0, L0, depth=2, W=4).run()
+    assert not (np.array_equal(Um, pins.units(Ue)) and np.array_equal(Lm, pins.units(Le)))
