@@ -377,6 +377,26 @@ __device__ __forceinline__ HalfLoad packed_half_load(const float *P, int64_t n, 
   return h;
 }
 
+// packed_half_load for a whole chunk of an interior block (no masks): the
+// thread's offsets od (direct: its atom row within the chunk and column) and
+// oa (across: its column's row and atom quad) are the same in every chunk,
+// 32-bit (n is below 2^27); only the wave-uniform bases move.
+__device__ __forceinline__ HalfLoad packed_half_load_whole(const float *P, int64_t n,
+                                                           int64_t k, int64_t xh, uint32_t od,
+                                                           uint32_t oa) {
+  HalfLoad h;
+  h.direct = *reinterpret_cast<const float4 *>(P + k * n + xh + od);
+  h.across = *reinterpret_cast<const float4 *>(P + xh * n + k + oa);
+  return h;
+}
+
+__device__ __forceinline__ uint32_t half_direct_offset(int64_t n, int tid) {
+  return (uint32_t)((tid / (BK / 4)) * n + (tid % (BK / 4)) * 4);
+}
+__device__ __forceinline__ uint32_t half_across_offset(int64_t n, int tid) {
+  return (uint32_t)((tid / (KC / 4)) * n + (tid % (KC / 4)) * 4);
+}
+
 // Store a HalfLoad into LDS arrays su, sl ([KC][stride] floats) at column col.
 __device__ __forceinline__ void packed_half_store(const HalfLoad &h, bool right, float *su,
                                                   float *sl, int stride, int col, int tid) {
@@ -557,8 +577,23 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
 
     // staged operands of one chunk: panel rows k0+kc.., columns of band A
     // (U/L[i,k] = U/L[k,i]) and of band B
+    // a whole chunk of an interior block loads without masks, from offsets
+    // that are the same in every chunk (see k_quads)
+    const uint32_t od = half_direct_offset(n, tid), oa = half_across_offset(n, tid);
+    const bool whole_rows = bA == BK && bJ == BK;
     auto fetch = [&](int kc, float4 (&st)[4], HalfLoad (&hl)[2]) {
-      if (PK) {
+      if (VEC && whole_rows && kc + KC <= bK) {
+        if (PK) {
+          hl[0] = packed_half_load_whole(Ub, n, k0 + kc, a0, od, oa);
+          hl[1] = packed_half_load_whole(Ub, n, k0 + kc, j0, od, oa);
+        } else {
+          const float *cu = Ub + (k0 + kc) * n, *cl = Lb + (k0 + kc) * n;
+          st[0] = *reinterpret_cast<const float4 *>(cu + a0 + od);
+          st[1] = *reinterpret_cast<const float4 *>(cl + a0 + od);
+          st[2] = *reinterpret_cast<const float4 *>(cu + j0 + od);
+          st[3] = *reinterpret_cast<const float4 *>(cl + j0 + od);
+        }
+      } else if (PK) {
         // band A and band B each lie right or left of band K; the addresses
         // are re-derived per chunk (laundered thread index), not kept live
         int tf = tid;
@@ -737,19 +772,40 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
           }
     }
 
+    // Staging: this thread's float4 of each panel array sits at the same
+    // offset from the chunk's first atom row in every chunk (32-bit: n is
+    // below 2^27), so only the wave-uniform chunk base moves.  A whole chunk
+    // of an interior block loads without masks.
     float4 st[ITER][4];
-    auto fetch = [&](int kc) {
+    uint32_t so[ITER];
 #pragma unroll
-      for (int it = 0; it < ITER; ++it) {
-        const int e = tid + it * NT, kk = e / (BK / 4), x4 = e % (BK / 4);
-        const int64_t k = k0 + kc + kk;
-        const bool kin = kc + kk < bK;
-        const int ni = kin ? clamp4(bA - x4 * 4) : 0;
-        const int nj = kin ? clamp4(bJ - x4 * 4) : 0;
-        st[it][0] = load4<VEC>(Ub + k * n + a0 + x4 * 4, ni, kInf, Ub);
-        st[it][1] = load4<VEC>(Lb + k * n + a0 + x4 * 4, ni, 0.0f, Lb);
-        st[it][2] = load4<VEC>(Ub + k * n + j0 + x4 * 4, nj, kInf, Ub);
-        st[it][3] = load4<VEC>(Lb + k * n + j0 + x4 * 4, nj, 0.0f, Lb);
+    for (int it = 0; it < ITER; ++it) {
+      const int e = tid + it * NT;
+      so[it] = (uint32_t)((e / (BK / 4)) * n + (e % (BK / 4)) * 4);
+    }
+    const bool interior = bA == BK && bJ == BK;
+    auto fetch = [&](int kc) {
+      const float *cu = Ub + (k0 + kc) * n, *cl = Lb + (k0 + kc) * n;
+      if (VEC && interior && kc + KCH <= bK) {
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+          st[it][0] = *reinterpret_cast<const float4 *>(cu + a0 + so[it]);
+          st[it][1] = *reinterpret_cast<const float4 *>(cl + a0 + so[it]);
+          st[it][2] = *reinterpret_cast<const float4 *>(cu + j0 + so[it]);
+          st[it][3] = *reinterpret_cast<const float4 *>(cl + j0 + so[it]);
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+          const int e = tid + it * NT, kk = e / (BK / 4), x4 = e % (BK / 4);
+          const bool kin = kc + kk < bK;
+          const int ni = kin ? clamp4(bA - x4 * 4) : 0;
+          const int nj = kin ? clamp4(bJ - x4 * 4) : 0;
+          st[it][0] = load4<VEC>(cu + a0 + so[it], ni, kInf, Ub);
+          st[it][1] = load4<VEC>(cl + a0 + so[it], ni, 0.0f, Lb);
+          st[it][2] = load4<VEC>(cu + j0 + so[it], nj, kInf, Ub);
+          st[it][3] = load4<VEC>(cl + j0 + so[it], nj, 0.0f, Lb);
+        }
       }
     };
     fetch(0);
@@ -926,6 +982,8 @@ __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P
 
     // the staging addresses are re-derived per chunk (laundered thread
     // index) rather than kept live through the k loop
+    // (the unmasked whole-chunk loads of k_quads and k_strip made this
+    // kernel slower: 74.3 -> 78.8 ms per packed pass at n12288)
     HalfLoad hl[2];
     auto fetch = [&](int kc) {
       int tf = tid;
