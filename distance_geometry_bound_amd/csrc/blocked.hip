@@ -1205,6 +1205,9 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   const int64_t TB = ceil_div(n, BK);    // k-blocks
   if (K1 > TB) K1 = TB;
   if (n <= 1 || K0 >= K1) return hipSuccess;
+  // the kernels' staging offsets are 32-bit (64 rows of n floats); such an
+  // n would need more than 2^54 bytes per matrix
+  if (n >= ((int64_t)1 << 26)) return hipErrorInvalidValue;
   const int64_t T = ceil_div(n, TILE);   // phase-3 tiles per side
   const bool packed = flags & kPacked, ru = flags & kDirected;
   const bool vec = (n % 4 == 0) && aligned16(U) && aligned16(L);
