@@ -52,6 +52,7 @@ TILE, BK = 128, 64              # blocked-path geometry (csrc/blocked.hip)
 COUNTERS = os.path.join(ROOT, "profiles", "k_quads_n12288_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "distance_geometry_bound_amd", "csrc", "blocked.hip")
 ROUND_COUNTERS = os.path.join(ROOT, "profiles", "k_round_vec_n12288_counters.json")
+VALU_COUNTERS = os.path.join(ROOT, "profiles", "k_quads_n12288_valu.json")
 ROUND_SRC = os.path.join(ROOT, "distance_geometry_bound_amd", "csrc", "round.hip")
 
 
@@ -135,6 +136,23 @@ def counters_traffic(n, batch, record=COUNTERS, source=KERNEL_SRC):
     if rec.get("source_sha256") != sha or rec.get("n") != n or rec.get("batch") != batch:
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def valu_counters(n, batch):
+    """Per-clock VALU issue and the clock of the bulk launch, from the
+    committed SQ/GRBM counter run, if the source is unchanged since; else None."""
+    try:
+        rec = json.load(open(VALU_COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest(KERNEL_SRC) or rec.get("n") != n or \
+            rec.get("batch") != batch:
+        return None
+    return {"valu_lanes_per_clk_per_simd": rec["valu_lanes_per_clk_per_simd"],
+            "clock_ghz": rec["clock_ghz"],
+            "mix_lanes_per_clk_4_waves": rec["mix_lanes_per_clk_4_waves"],
+            "sq_insts_valu_per_launch": rec["sq_insts_valu_per_launch"],
+            "modelled_insts_per_launch": rec["modelled_insts_per_launch"]}
 
 
 def extra_steps(W, U, L, U0, L0, dev, reps=3):
@@ -378,6 +396,7 @@ def main():
             "launch_ms": launch_ms, "launches": tot["tiles"][0], "lookahead_bands": ahead,
             "step_blocks": width,
             "ops_per_launch": ops,
+            "issue_counters": valu_counters(n, batch),
             "frac_effective": OPS_PER_TRIPLE * dense / launches / (launch_ms * 1e-3)
                               / FP32_VALU_PEAK,
         }
