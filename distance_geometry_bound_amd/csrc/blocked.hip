@@ -1159,32 +1159,32 @@ bool set_step_blocks(int blocks) {
   return true;
 }
 
-int step_blocks(int64_t n, int64_t batch, bool packed) {
+int step_blocks(int64_t n, int64_t batch) {
   const int forced = forced_step.load();
   if (forced > 0) return forced;
-  if (lookahead_bands(n, batch, packed) != 2) return 1;
+  if (lookahead_bands(n, batch) != 2) return 1;
   const int64_t T = ceil_div(n, TILE), tiles = T * (T + 1) / 2 * batch;
   return tiles >= kStep4Tiles ? 4 : tiles >= kStep3Tiles ? 3 : 2;
 }
 
-int lookahead_bands(int64_t n, int64_t batch, bool packed) {
+int lookahead_bands(int64_t n, int64_t batch) {
   const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
   if (TB <= 1 || T <= 1) return 0;
   const int forced = forced_lookahead.load();
   if (forced >= 0) return forced;
   const int64_t tiles = T * (T + 1) / 2 * batch;
   if (tiles >= kDeepTiles) return 2;
-  // the packed layout's phase 1-2 kernel is slower (packed loads and
-  // stores), and gains from running beside the bulk even where its launch
-  // fills the chip
-  if (tiles < kAheadTiles || (!packed && (TB - 1) * batch > kPanelFill)) return 0;
+  // where one phase 1-2 launch fills the chip the batch splits over the two
+  // streams instead (launch_blocked_on), in both layouts
+  if (tiles < kAheadTiles || (TB - 1) * batch > kPanelFill) return 0;
   return 1;
 }
 
 // Enqueue one pass.  With more than one k-block the pass may run ahead on a
 // second stream (lookahead_bands: by two steps when there are many phase-3
 // tiles, one for a mid-sized bulk, none when the bulk is too short to hide a
-// band strip or the phase 1-2 launch fills the chip).  A step is one
+// band strip or the phase 1-2 launch fills the chip; a batch then splits over
+// the two streams).  A step is one
 // k-block, or two when running two steps ahead: blocked Floyd-Warshall with
 // 128 atoms per phase 3, whose panel (the rows of both bands, final for all
 // 128 rounds) is built from the 64-wide phase 1-2 kernel and strips.  Per
@@ -1199,8 +1199,20 @@ int lookahead_bands(int64_t n, int64_t batch, bool packed) {
 // overlap touches only bands it leaves alone and reads only panel rows it
 // does not write; the CPU model of this schedule in the tests checks that
 // cell by cell, for both depths.
+namespace {
+hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
+                             hipStream_t s, Prof *prof, unsigned flags, bool half);
+}  // namespace
+
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
                           hipStream_t s, Prof *prof, unsigned flags) {
+  return launch_blocked_on(U, L, n, batch, K0, K1, s, prof, flags, false);
+}
+
+namespace {
+// `half`: one half of a split batch, run on one stream without look-ahead.
+hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
+                             hipStream_t s, Prof *prof, unsigned flags, bool half) {
   static_assert(BK == kBlockRounds, "k-block size");
   const int64_t TB = ceil_div(n, BK);    // k-blocks
   if (K1 > TB) K1 = TB;
@@ -1233,7 +1245,28 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   // critical path: one step ahead or none, on 1024-thread workgroups that
   // hide the latency of their rounds best.
   const int64_t pairs = T * (T + 1) / 2;
-  const int ahead = lookahead_bands(n, batch, packed);
+  const int ahead = half ? 0 : lookahead_bands(n, batch);
+  // A batch whose phase 1-2 launch fills the chip by itself splits into two
+  // halves, one per stream: the molecules share nothing, so the phase 1-2
+  // launches of one half run beside the bulk of the other.  With fewer
+  // workgroups per launch the two halves only contend, and one stream in
+  // order is faster.
+  if (ahead == 0 && !half && batch >= 2 && TB > 1 && T > 1 && (TB - 1) * batch > kPanelFill) {
+    hipStream_t side = side_stream();
+    Events *ev = side ? thread_events() : nullptr;
+    if (side && ev) {
+      const int64_t b1 = batch / 2;
+      hipError_t e = hipEventRecord(ev->start(), s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side, ev->start(), 0);
+      if (e == hipSuccess) e = launch_blocked_on(U, L, n, b1, K0, K1, s, prof, flags, true);
+      if (e == hipSuccess)
+        e = launch_blocked_on(U + b1 * nn, L + b1 * nn, n, batch - b1, K0, K1, side, prof, flags,
+                              true);
+      if (e == hipSuccess) e = hipEventRecord(ev->bulk(0), side);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, ev->bulk(0), 0);
+      return e;
+    }
+  }
   const bool deep = ahead == 2;
   if (ahead == 0 && 4 * pairs * batch <= kSmallGrid) {
     quads_kernel = DBS_QUADS(kSmallRT, kSmallCT, kSmallKC);
@@ -1261,7 +1294,7 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
   // [lo(t), hi(t)).  Two steps ahead the bulk takes several blocks per
   // launch, which spreads its fixed costs (the loads and stores of the
   // matrix, the launch's ramp and tail) over more atoms.
-  const int64_t W = step_blocks(n, batch, packed), NS = ceil_div(K1 - K0, W);
+  const int64_t W = step_blocks(n, batch), NS = ceil_div(K1 - K0, W);
   auto lo = [&](int64_t t) { return K0 + t * W; };
   auto hi = [&](int64_t t) { return K0 + (t + 1) * W < K1 ? K0 + (t + 1) * W : K1; };
 
@@ -1340,5 +1373,6 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
                L, n, batch, TB);
   return e;
 }
+}  // namespace
 
 }  // namespace dbs

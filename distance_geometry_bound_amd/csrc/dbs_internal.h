@@ -191,14 +191,14 @@ hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t 
 constexpr int kBlockRounds = 64;
 // Look-ahead depth of the blocked pass: steps it updates ahead on its second
 // stream (0, 1 or 2; at 2 a step is two k-blocks).
-int lookahead_bands(int64_t n, int64_t batch, bool packed = false);
+int lookahead_bands(int64_t n, int64_t batch);
 // Force the look-ahead depth (0..2) or restore the automatic choice (-1);
 // false (and no change) for any other value.
 bool set_lookahead(int bands);
 // k-blocks per step of the blocked pass (1 .. kMaxStepBlocks), and the
 // override of that choice (-1: automatic).
 constexpr int kMaxStepBlocks = 4;
-int step_blocks(int64_t n, int64_t batch, bool packed = false);
+int step_blocks(int64_t n, int64_t batch);
 bool set_step_blocks(int blocks);
 hipError_t launch_restraints(float *U, float *L, int64_t n, int64_t batch, float unknown_L,
                              float unknown_U, const int32_t *mol, const int32_t *ia,

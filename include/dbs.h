@@ -287,14 +287,15 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags
  *   0  no second stream: a single k-block or phase-3 tile; fewer than 256
  *      phase-3 tiles x molecules (the bulk launch is shorter than the band
  *      strip it would hide); or more than 256 phase 1-2 workgroups (the
- *      panel launch fills the chip by itself);
+ *      panel launch fills the chip by itself: a batch of two or more
+ *      molecules then splits into two halves, one per stream, so that one
+ *      half's phase 1-2 launches run beside the other half's phase 3);
  *   1  otherwise, below 960 tiles x molecules: steps of one k-block;
  *   2  from 960 tiles x molecules: steps of two to four k-blocks
  *      (dbs_step_blocks), so that each phase-3 launch runs 128 to 256 atoms
  *      (fewer loads and stores of the matrix per atom), and the panel of
  *      the next step has a whole phase-3 launch to hide under.
- * The packed passes (dbs_smooth_packed*) leave out the panel-fill test:
- * their slower phase 1-2 kernel still gains from running beside the bulk.
+ * The packed passes (dbs_smooth_packed*) follow the same choice.
  * A depth set by dbs_set_lookahead replaces the automatic choice (still 0
  * for a single k-block or tile).  Phase 3's bulk launches leave the bands of
  * the steps run ahead to the second stream.  For measurement and tests;

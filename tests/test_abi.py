@@ -117,6 +117,8 @@ def test_lookahead_bands_query():
     assert lib.dbs_lookahead_bands(200, 1) == 0       # 3 tiles: bulk shorter than a strip
     assert lib.dbs_lookahead_bands(1024, 1) == 0      # 36 tiles
     assert lib.dbs_lookahead_bands(500, 64) == 0      # 448 panel workgroups fill the chip
+    assert lib.dbs_lookahead_bands(130, 129) == 0     # 258 panel workgroups: split batch
+    assert lib.dbs_lookahead_bands(130, 128) == 1     # 384 tiles, 256 panel workgroups
     assert lib.dbs_lookahead_bands(2944, 1) == 1      # 276 tiles, 45 panel workgroups
     assert lib.dbs_lookahead_bands(4096, 1) == 1
     assert lib.dbs_lookahead_bands(5120, 1) == 1      # 820 tiles

@@ -18,8 +18,9 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
+# (130, 129) at the automatic choice: a batch split over the two streams
 @pytest.mark.parametrize("n,batch,bands,blocks", [(700, 1, 2, 2), (700, 1, 2, 4), (385, 2, 1, 1),
-                                                  (385, 2, 0, 2)])
+                                                  (385, 2, 0, 2), (130, 129, -1, -1)])
 def test_captured_pass_replays_match_oracle(n, batch, bands, blocks):
     U0, L0, _ = gen.random_sound_bounds(n, seed=500 + n + bands, batch=batch, box=6.0 + n / 8)
     Ue, Le = oracle.smooth(U0, L0)

@@ -177,6 +177,32 @@ def test_every_step_width(n, batch, bands, blocks, restore_lookahead):
     assert_bits(host(U), host(L), Ue, Le, "ranges 0,192,n " + tag)
 
 
+@pytest.mark.parametrize("n,batch", [(130, 129), (200, 87), (257, 86)])
+def test_split_batch(n, batch):
+    # more than 256 phase 1-2 workgroups: the batch splits into two unequal
+    # halves (batch // 2 and the rest), one per stream; dense, directed and
+    # packed passes, and ranges that cut the pass at k-block boundaries
+    from oracle import steps
+    assert (-(-n // 64) - 1) * batch > 256 and dgb.lookahead_bands(n, batch) == 0
+    U0, L0 = sound_input(n, batch, seed=11 * n + batch)
+    Ue, Le = oracle.smooth(U0, L0)
+    tag = f"split n={n} batch={batch}"
+    Ug, Lg = gpu_pass(U0, L0, "blocked")
+    assert_bits(Ug, Lg, Ue, Le, "blocked " + tag)
+    U, L = dev(U0), dev(L0)
+    dgb.smooth_directed(U, L, algo="blocked")
+    assert_bits(host(U), host(L), Ue, Le, "directed " + tag)
+    P = dgb.pack(dev(U0), dev(L0))
+    dgb.smooth_packed(P)
+    assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
+    U, L = dev(U0), dev(L0)
+    Ur, Lr = oracle.rounds(U0, L0, 0, 64)
+    dgb.smooth_range(U, L, 0, 64, algo="blocked")
+    assert_bits(host(U), host(L), Ur, Lr, "range 0..64 " + tag)
+    dgb.smooth_range(U, L, 64, n, algo="blocked")
+    assert_bits(host(U), host(L), Ue, Le, "range 64..n " + tag)
+
+
 def test_walk_molecules_batched():
     W = gen.make_workload("b64n500", batch=5)
     Ue, Le = oracle.smooth(W.U, W.L)
