@@ -321,8 +321,25 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
       }
     // R in both orientations (packed: the one slot of U and of L); D, which
     // lies in a fresh tile, as a full square
+    // With 1024 threads (S = 2) the transposed copy of R (packed: the slots
+    // below the diagonal of its cells) goes through an LDS tile, so that its
+    // global writes are row segments instead of one float per lane down a
+    // column.  The 256-thread variant runs beside the bulk of phase 3 and
+    // keeps its LDS footprint small.
+    constexpr bool kStageT = S == 2;
+    const bool up = k0 < j0;  // R lies right of the diagonal
     if (PK) {
-      packed_block_store<S>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
+      if (kStageT) {
+#pragma unroll
+        for (int r = 0; r < S; ++r)
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            const int a = ty * S + r, c = tx * S + q;
+            if (a < bK && c < bJ) Ub[(k0 + a) * n + j0 + c] = up ? u[r][q] : l[r][q];
+          }
+      } else {
+        packed_block_store<S>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
+      }
       if (writes_d) packed_block_store<S>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
     }
 #pragma unroll
@@ -333,14 +350,42 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
         if (!PK && a < bK && c < bJ) {
           Ub[(k0 + a) * n + j0 + c] = u[r][q];
           Lb[(k0 + a) * n + j0 + c] = l[r][q];
-          Ub[(j0 + c) * n + k0 + a] = u[r][q];
-          Lb[(j0 + c) * n + k0 + a] = l[r][q];
+          if (!kStageT) {
+            Ub[(j0 + c) * n + k0 + a] = u[r][q];
+            Lb[(j0 + c) * n + k0 + a] = l[r][q];
+          }
         }
         if (!PK && writes_d && a < bK && c < bK) {
           Ub[(k0 + a) * n + k0 + c] = du[r][q];
           Lb[(k0 + a) * n + k0 + c] = dl[r][q];
         }
       }
+    if constexpr (kStageT) {
+      // tt[.][c][a] = R[a][c]: U and L, or (packed) the slot at row j0 + c
+      __shared__ float tt[PK ? 1 : 2][BK][BK + 1];
+#pragma unroll
+      for (int r = 0; r < S; ++r)
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          if (PK) {
+            tt[0][tx * S + q][ty * S + r] = up ? l[r][q] : u[r][q];
+          } else {
+            tt[0][tx * S + q][ty * S + r] = u[r][q];
+            tt[PK ? 0 : 1][tx * S + q][ty * S + r] = l[r][q];
+          }
+        }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < S; ++r)
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          const int c = ty * S + r, a = tx * S + q;
+          if (c < bJ && a < bK) {
+            Ub[(j0 + c) * n + k0 + a] = tt[0][c][a];
+            if (!PK) Lb[(j0 + c) * n + k0 + a] = tt[PK ? 0 : 1][c][a];
+          }
+        }
+    }
     __syncthreads();  // LDS reuse by the next molecule
   }
 }
