@@ -221,6 +221,13 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
   constexpr int NT = BK / S;  // threads per side
   __shared__ __align__(16) float dvu[2][BK], dvl[2][BK];  // row m of D
   __shared__ __align__(16) float rvu[2][BK], rvl[2][BK];  // row m of R
+  // With 1024 threads (S = 2) the panel tile's copy in the other orientation
+  // is read and written through an LDS tile, as row segments instead of one
+  // or two floats per lane down a column: tt[.][c][a] = R[a][c] (U and L;
+  // packed, the one slot written there).  The 256-thread variant runs beside
+  // the bulk of phase 3 and keeps its LDS footprint small.
+  constexpr bool kStageT = S == 2;
+  __shared__ float tt[kStageT ? (PK ? 1 : 2) : 1][kStageT ? BK : 1][kStageT ? BK + 1 : 1];
 
   rounding_prologue<RU>();
   critical_path_priority();
@@ -255,13 +262,22 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
         xl[r] = load_seg<VEC, S>(Lb + g, left, 0.0f, Lb);
       }
       // the panel tile from its fresh orientation: R[a][c] = M[k0+a][j0+c]
-      // (row segments), else M[j0+c][k0+a] (column segments)
+      // (row segments), else M[j0+c][k0+a] (column segments, or with S = 2
+      // the rows of that copy, exchanged through LDS below)
+      const bool swap = kStageT && !rowor;
 #pragma unroll
       for (int r = 0; r < S; ++r) {
-        const int64_t left = rowor ? (ty * S + r < bK ? bJ - tx * S : 0)
-                                   : (tx * S + r < bJ ? bK - ty * S : 0);
-        const int64_t g = rowor ? (k0 + ty * S + r) * n + j0 + tx * S
-                                : (j0 + tx * S + r) * n + k0 + ty * S;
+        int64_t left, g;
+        if (rowor) {
+          left = ty * S + r < bK ? bJ - tx * S : 0;
+          g = (k0 + ty * S + r) * n + j0 + tx * S;
+        } else if (swap) {
+          left = ty * S + r < bJ ? bK - tx * S : 0;
+          g = (j0 + ty * S + r) * n + k0 + tx * S;
+        } else {
+          left = tx * S + r < bJ ? bK - ty * S : 0;
+          g = (j0 + tx * S + r) * n + k0 + ty * S;
+        }
         yu[r] = load_seg<VEC, S>(Ub + g, left, kInf, Ub);
         yl[r] = load_seg<VEC, S>(Lb + g, left, 0.0f, Lb);
       }
@@ -271,9 +287,28 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
         for (int q = 0; q < S; ++q) {
           du[r][q] = xu[r].v[q];
           dl[r][q] = xl[r].v[q];
-          u[r][q] = rowor ? yu[r].v[q] : yu[q].v[r];
-          l[r][q] = rowor ? yl[r].v[q] : yl[q].v[r];
+          u[r][q] = rowor || swap ? yu[r].v[q] : yu[q].v[r];
+          l[r][q] = rowor || swap ? yl[r].v[q] : yl[q].v[r];
         }
+      if constexpr (kStageT) {
+        if (swap) {  // uniform: u[r][q] holds M[j0 + ty*S + r][k0 + tx*S + q]
+#pragma unroll
+          for (int r = 0; r < S; ++r)
+#pragma unroll
+            for (int q = 0; q < S; ++q) {
+              tt[0][ty * S + r][tx * S + q] = u[r][q];
+              tt[PK ? 0 : 1][ty * S + r][tx * S + q] = l[r][q];
+            }
+          __syncthreads();
+#pragma unroll
+          for (int r = 0; r < S; ++r)
+#pragma unroll
+            for (int q = 0; q < S; ++q) {
+              u[r][q] = tt[0][tx * S + q][ty * S + r];
+              l[r][q] = tt[PK ? 0 : 1][tx * S + q][ty * S + r];
+            }
+        }
+      }
     }
 
     for (int mb = 0; mb < NT; ++mb) {
@@ -321,12 +356,6 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
       }
     // R in both orientations (packed: the one slot of U and of L); D, which
     // lies in a fresh tile, as a full square
-    // With 1024 threads (S = 2) the transposed copy of R (packed: the slots
-    // below the diagonal of its cells) goes through an LDS tile, so that its
-    // global writes are row segments instead of one float per lane down a
-    // column.  The 256-thread variant runs beside the bulk of phase 3 and
-    // keeps its LDS footprint small.
-    constexpr bool kStageT = S == 2;
     const bool up = k0 < j0;  // R lies right of the diagonal
     if (PK) {
       if (kStageT) {
@@ -360,9 +389,7 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
           Lb[(k0 + a) * n + k0 + c] = dl[r][q];
         }
       }
-    if constexpr (kStageT) {
-      // tt[.][c][a] = R[a][c]: U and L, or (packed) the slot at row j0 + c
-      __shared__ float tt[PK ? 1 : 2][BK][BK + 1];
+    if constexpr (kStageT) {  // the copy in the other orientation, through tt
 #pragma unroll
       for (int r = 0; r < S; ++r)
 #pragma unroll
