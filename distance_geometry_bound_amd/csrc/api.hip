@@ -28,9 +28,13 @@ int device_status() {
   return g_dev_ok[dev] == 1 ? DBS_OK : DBS_EDEVICE;
 }
 
+// The largest n + 1 accepted.  No such matrix fits in device memory (2^52
+// floats); the blocked kernels address a 64-row band with 32-bit offsets.
+constexpr int64_t kLimitN = (int64_t)1 << 26;
+
 // Size checks of one [batch][n][n] float buffer; 0 when fine.
 int check_buffer(const void *p, int64_t n, int64_t batch, uint64_t *bytes) {
-  if (!p || n < 1 || batch < 1 || n >= ((int64_t)1 << 31)) return DBS_EINVAL;
+  if (!p || n < 1 || batch < 1 || n >= kLimitN) return DBS_EINVAL;
   const int64_t nn = n * n;
   if (batch > INT64_MAX / 4 / nn) return DBS_EINVAL;
   *bytes = (uint64_t)(nn * batch) * 4u;
@@ -47,8 +51,8 @@ bool overlap(const void *a, const void *b, uint64_t bytes) {
 // Host-side argument checks shared by every entry point.
 int validate(const void *U, const void *L, int64_t n, int64_t batch) {
   if (!U || !L || n < 1 || batch < 1) return DBS_EINVAL;
-  if (n >= ((int64_t)1 << 31)) return DBS_EINVAL;
-  const int64_t nn = n * n;  // < 2^62
+  if (n >= kLimitN) return DBS_EINVAL;
+  const int64_t nn = n * n;  // < 2^52
   if (batch > INT64_MAX / 4 / nn) return DBS_EINVAL;
   const uint64_t bytes = (uint64_t)(nn * batch) * 4u;
   const uintptr_t u = reinterpret_cast<uintptr_t>(U), l = reinterpret_cast<uintptr_t>(L);
@@ -225,7 +229,7 @@ int dbs_block_rounds(void) { return dbs::kBlockRounds; }
 int dbs_tightened(const float *U0, const float *L0, const float *U1, const float *L1,
                   int64_t n, int64_t batch, uint8_t *mask, void *stream) {
   // the four inputs may alias one another; none may overlap the mask
-  if (!U0 || !L0 || !U1 || !L1 || !mask || n < 1 || batch < 1 || n >= ((int64_t)1 << 31))
+  if (!U0 || !L0 || !U1 || !L1 || !mask || n < 1 || batch < 1 || n >= kLimitN)
     return DBS_EINVAL;
   if (batch > INT64_MAX / 4 / (n * n)) return DBS_EINVAL;
   const uint64_t fbytes = (uint64_t)(n * n * batch) * 4u, mbytes = fbytes / 4u;

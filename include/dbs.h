@@ -79,8 +79,8 @@ extern "C" {
  *   batch  number of molecules, >= 1.
  *   stream hipStream_t to enqueue on (NULL = null stream).
  * Returns DBS_OK, DBS_EINVAL (null pointer, n < 1, batch < 1, a size that
- * overflows 64-bit byte counts, n >= 2^31, or overlapping U/L),
- * DBS_EDEVICE or DBS_ELAUNCH.
+ * overflows 64-bit byte counts, n >= 2^26 (no such matrix fits in device
+ * memory), or overlapping U/L), DBS_EDEVICE or DBS_ELAUNCH.
  */
 int dbs_smooth(float *U, float *L, int64_t n, int64_t batch, void *stream);
 
@@ -284,12 +284,15 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags
  * dbs_lookahead_bands -- the look-ahead depth of the blocked pass (DBS_ALGO_
  * BLOCKED) on the dense layout for this shape: how many steps it updates
  * ahead on its second stream.
- *   0  no second stream: a single k-block or phase-3 tile; fewer than 256
+ *   0  no look-ahead: a single k-block or phase-3 tile; fewer than 256
  *      phase-3 tiles x molecules (the bulk launch is shorter than the band
  *      strip it would hide); or more than 256 phase 1-2 workgroups (the
- *      panel launch fills the chip by itself: a batch of two or more
- *      molecules then splits into two halves, one per stream, so that one
- *      half's phase 1-2 launches run beside the other half's phase 3);
+ *      panel launch fills the chip by itself).  Without look-ahead, a batch
+ *      of two or more molecules with more than 256 phase 1-2 workgroups
+ *      ((k-blocks - 1) x molecules) splits into two halves, one on the
+ *      caller's stream and one on the second stream, so that one half's
+ *      phase 1-2 launches run beside the other half's phase 3; otherwise
+ *      the pass uses the caller's stream alone;
  *   1  otherwise, below 960 tiles x molecules: steps of one k-block;
  *   2  from 960 tiles x molecules: steps of two to four k-blocks
  *      (dbs_step_blocks), so that each phase-3 launch runs 128 to 256 atoms

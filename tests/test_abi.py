@@ -60,7 +60,8 @@ A, B = 0x10000000, 0x20000000
 
 @pytest.mark.parametrize("args", [
     (0, B, 4, 1), (A, 0, 4, 1), (A, B, 0, 1), (A, B, -3, 1), (A, B, 4, 0),
-    (A, B, 1 << 31, 1), (A, B, 1 << 20, 1 << 40), (A, A + 32, 4, 1), (A + 2, B, 4, 1),
+    (A, B, 1 << 31, 1), (A, A + (1 << 55), 1 << 26, 1),  # 2^26: the size limit alone
+    (A, B, 1 << 20, 1 << 40), (A, A + 32, 4, 1), (A + 2, B, 4, 1),
 ])
 def test_smooth_rejects_bad_arguments(args):
     L = dgb.lib()
