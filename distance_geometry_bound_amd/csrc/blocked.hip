@@ -1053,15 +1053,22 @@ __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P
     }
 
     // the staging addresses are re-derived per chunk (laundered thread
-    // index) rather than kept live through the k loop
-    // (the unmasked whole-chunk loads of k_quads and k_strip made this
-    // kernel slower: 74.3 -> 78.8 ms per packed pass at n12288)
+    // index) rather than kept live through the k loop.  A whole interior
+    // chunk loads from two 32-bit offsets without masks (73.1-73.8 ms per
+    // packed pass at n12288, against 74.6-74.9 masked; with the offsets kept
+    // live through the loop, as k_quads does, it was slower: 78.8 ms)
     HalfLoad hl[2];
     auto fetch = [&](int kc) {
       int tf = tid;
       asm volatile("" : "+v"(tf));
-      hl[0] = packed_half_load<VEC>(Pb, n, k0, kc, bK, a0, A > K, false, tf);
-      hl[1] = packed_half_load<VEC>(Pb, n, k0, kc, bK, j0, B > K, false, tf);
+      if (VEC && kc + KC <= bK && a0 + BK <= n && j0 + BK <= n) {  // uniform
+        const uint32_t od = half_direct_offset(n, tf), oa = half_across_offset(n, tf);
+        hl[0] = packed_half_load_whole(Pb, n, k0 + kc, a0, od, oa);
+        hl[1] = packed_half_load_whole(Pb, n, k0 + kc, j0, od, oa);
+      } else {
+        hl[0] = packed_half_load<VEC>(Pb, n, k0, kc, bK, a0, A > K, false, tf);
+        hl[1] = packed_half_load<VEC>(Pb, n, k0, kc, bK, j0, B > K, false, tf);
+      }
     };
     fetch(0);
     for (int kc = 0; kc < bK; kc += KC) {
