@@ -44,9 +44,10 @@ constexpr int TILE = 128;       // freshness granularity: tiles I <= J are kept 
 constexpr int RATIO = TILE / BK;
 constexpr int KC = 16;          // atoms per LDS chunk in phase 3
 // Phase-3 tiles (times molecules) from which the pass runs two steps ahead,
-// in steps of two k-blocks (measured crossover: n5120, 820 tiles, one step
-// ahead 8.40 ms, two 8.76 ms; n5632, 990 tiles, 10.56 against 10.41 ms).
-constexpr int64_t kDeepTiles = 960;
+// in steps of two or more k-blocks (measured crossover, one step ahead
+// against two: n5632, 990 tiles, 9.78-9.80 against 10.14-10.17 ms; n6144,
+// 1176 tiles, 12.15 against 11.59 ms).
+constexpr int64_t kDeepTiles = 1024;
 // k-blocks per step when running two steps ahead: 4 from kStep4Tiles phase-3
 // tiles (times molecules), 3 from kStep3Tiles, else 2.  Wider steps spread a
 // bulk launch's fixed costs over more atoms but leave more bands to the

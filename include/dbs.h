@@ -293,8 +293,8 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags
  *      caller's stream and one on the second stream, so that one half's
  *      phase 1-2 launches run beside the other half's phase 3; otherwise
  *      the pass uses the caller's stream alone;
- *   1  otherwise, below 960 tiles x molecules: steps of one k-block;
- *   2  from 960 tiles x molecules: steps of two to four k-blocks
+ *   1  otherwise, below 1024 tiles x molecules: steps of one k-block;
+ *   2  from 1024 tiles x molecules: steps of two to four k-blocks
  *      (dbs_step_blocks), so that each phase-3 launch runs 128 to 256 atoms
  *      (fewer loads and stores of the matrix per atom), and the panel of
  *      the next step has a whole phase-3 launch to hide under.

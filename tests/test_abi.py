@@ -123,7 +123,8 @@ def test_lookahead_bands_query():
     assert lib.dbs_lookahead_bands(2944, 1) == 1      # 276 tiles, 45 panel workgroups
     assert lib.dbs_lookahead_bands(4096, 1) == 1
     assert lib.dbs_lookahead_bands(5120, 1) == 1      # 820 tiles
-    assert lib.dbs_lookahead_bands(5632, 1) == 2      # 990 tiles
+    assert lib.dbs_lookahead_bands(5632, 1) == 1      # 990 tiles
+    assert lib.dbs_lookahead_bands(6144, 1) == 2      # 1176 tiles
     assert lib.dbs_lookahead_bands(4096, 2) == 2      # 1056 tiles x molecules
     assert lib.dbs_lookahead_bands(12288, 1) == 2
     assert lib.dbs_lookahead_bands(0, 1) == -1 and lib.dbs_lookahead_bands(5, 0) == -1
@@ -153,7 +154,7 @@ def test_step_blocks_query_and_override():
     lib = dgb.lib()
     assert dgb.step_blocks(12288) == 4 and dgb.step_blocks(10240) == 4   # 4656, 3240 tiles
     assert dgb.step_blocks(8192) == 3 and dgb.step_blocks(6144, 2) == 3  # 2080, 2352
-    assert dgb.step_blocks(5632) == 2 and dgb.step_blocks(6144) == 2     # 990, 1176
+    assert dgb.step_blocks(5632) == 1 and dgb.step_blocks(6144) == 2     # 990, 1176
     assert dgb.step_blocks(4096) == 1 and dgb.step_blocks(200) == 1
     assert lib.dbs_step_blocks(0, 1) == -1 and lib.dbs_step_blocks(5, 0) == -1
     try:
