@@ -9,8 +9,8 @@ __version__ = "0.1.0"
 
 _API = ("smooth", "smooth_round", "smooth_rounds", "check", "lib", "DbsError", "auto_algo", "smooth_profiled", "PROF_KINDS", "smooth_range", "tightened",
         "bounds_from_restraints", "RESTRAINT_FLAGS", "pack", "unpack", "smooth_packed", "check_packed",
-        "smooth_directed", "smooth_directed_range", "smooth_packed_directed", "lookahead_bands", "set_lookahead",
-        "step_blocks", "set_step_blocks",
+        "smooth_directed", "smooth_directed_range", "smooth_packed_directed", "lookahead_bands",
+        "step_blocks", "schedule", "options", "Options", "AUTO",
         "ALGO_AUTO", "ALGO_PERK", "ALGO_LDS", "ALGO_BLOCKED", "CHECK_FLAGS")
 
 

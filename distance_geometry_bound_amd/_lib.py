@@ -24,12 +24,22 @@ CHECK_FLAGS = {
 
 DBS_OK, DBS_EINVAL, DBS_EDEVICE, DBS_ELAUNCH, DBS_EUNSUPPORTED = 0, -1, -2, -3, -4
 
-EXPORTS = ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_round",
+EXPORTS = ("dbs_options_init", "dbs_smooth_opts", "dbs_smooth_packed_opts", "dbs_schedule",
+           "dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_round",
            "dbs_check", "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened", "dbs_bounds_from_restraints",
            "dbs_pack", "dbs_unpack", "dbs_smooth_packed", "dbs_smooth_packed_range",
            "dbs_check_packed", "dbs_smooth_directed", "dbs_smooth_directed_range",
-           "dbs_smooth_packed_directed_range", "dbs_lookahead_bands", "dbs_set_lookahead",
-           "dbs_step_blocks", "dbs_set_step_blocks", "dbs_lds_max_n", "dbs_auto_algo", "dbs_strerror", "dbs_version")
+           "dbs_smooth_packed_directed_range", "dbs_lookahead_bands", "dbs_step_blocks",
+           "dbs_lds_max_n", "dbs_auto_algo", "dbs_strerror", "dbs_version")
+
+AUTO = -1
+
+
+class Options(ctypes.Structure):
+    """struct dbs_options (include/dbs.h): per-call options of a pass."""
+    _fields_ = [("algo", ctypes.c_int32), ("directed", ctypes.c_int32),
+                ("lookahead", ctypes.c_int32), ("step_blocks", ctypes.c_int32)]
+
 
 RESTRAINT_FLAGS = {"index": 1, "value": 2}
 
@@ -56,7 +66,14 @@ def lib():
         vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.dbs_smooth.argtypes = [vp, vp, i64, i64, vp]
         L.dbs_smooth_algo.argtypes = [vp, vp, i64, i64, vp, c_int]
-        L.dbs_smooth_profiled.argtypes = [vp, vp, i64, i64, vp, c_int,
+        opp = ctypes.POINTER(Options)
+        L.dbs_options_init.argtypes = [opp]
+        L.dbs_options_init.restype = None
+        L.dbs_smooth_opts.argtypes = [vp, vp, i64, i64, i64, i64, vp, opp]
+        L.dbs_smooth_packed_opts.argtypes = [vp, i64, i64, i64, i64, vp, opp]
+        L.dbs_schedule.argtypes = [i64, i64, opp, ctypes.POINTER(ctypes.c_int32),
+                                   ctypes.POINTER(ctypes.c_int32)]
+        L.dbs_smooth_profiled.argtypes = [vp, vp, i64, i64, vp, opp,
                                           ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
         L.dbs_rounds.argtypes = [vp, vp, i64, i64, i64, i64, vp]
         L.dbs_round.argtypes = [vp, vp, i64, i64, i64, vp]
@@ -68,16 +85,14 @@ def lib():
         L.dbs_smooth_packed_range.argtypes = [vp, i64, i64, i64, i64, vp]
         L.dbs_bounds_from_restraints.argtypes = [vp, vp, i64, i64, ctypes.c_float,
                                                  ctypes.c_float, vp, vp, vp, vp, vp, i64, vp, vp]
-        L.dbs_check.argtypes = [vp, vp, i64, i64, vp, vp]
-        L.dbs_check_packed.argtypes = [vp, i64, i64, vp, vp]
+        L.dbs_check.argtypes = [vp, vp, i64, i64, vp, vp]          # ..., stream, d_flags
+        L.dbs_check_packed.argtypes = [vp, i64, i64, vp, vp]      # ..., stream, d_flags
         L.dbs_smooth_directed.argtypes = [vp, vp, i64, i64, vp]
         L.dbs_smooth_directed_range.argtypes = [vp, vp, i64, i64, i64, i64, vp, c_int]
         L.dbs_smooth_packed_directed_range.argtypes = [vp, i64, i64, i64, i64, vp]
         L.dbs_auto_algo.argtypes = [i64, i64]
         L.dbs_lookahead_bands.argtypes = [i64, i64]
-        L.dbs_set_lookahead.argtypes = [ctypes.c_int]
         L.dbs_step_blocks.argtypes = [i64, i64]
-        L.dbs_set_step_blocks.argtypes = [ctypes.c_int]
         L.dbs_strerror.argtypes = [c_int]
         L.dbs_strerror.restype = ctypes.c_char_p
         for f in ("dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_round",
@@ -86,8 +101,8 @@ def lib():
                   "dbs_bounds_from_restraints", "dbs_pack", "dbs_unpack", "dbs_smooth_packed",
                   "dbs_smooth_packed_range", "dbs_check_packed", "dbs_smooth_directed",
                   "dbs_smooth_directed_range", "dbs_smooth_packed_directed_range",
-                  "dbs_lds_max_n", "dbs_auto_algo", "dbs_lookahead_bands", "dbs_set_lookahead",
-                  "dbs_step_blocks", "dbs_set_step_blocks", "dbs_version"):
+                  "dbs_lds_max_n", "dbs_auto_algo", "dbs_lookahead_bands", "dbs_step_blocks",
+                  "dbs_version", "dbs_smooth_opts", "dbs_smooth_packed_opts", "dbs_schedule"):
             getattr(L, f).restype = c_int
         _lib = L
     return _lib
@@ -137,14 +152,35 @@ def _call(T, fn, *args):
         _raise(fn(*args))
 
 
-def smooth(U, L, algo: str = "auto", check: bool = False) -> None:
+def options(algo: str = "auto", directed: bool = False, lookahead=None, step_blocks=None):
+    """struct dbs_options for a pass: `lookahead` (0, 1, 2) and `step_blocks`
+    (1 .. 4) force the blocked schedule, None keeps the automatic choice."""
+    if algo not in _ALGOS:
+        raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
+    return Options(_ALGOS[algo], 1 if directed else 0,
+                   AUTO if lookahead is None else int(lookahead),
+                   AUTO if step_blocks is None else int(step_blocks))
+
+
+def _pass(U, L, k_begin, k_end, **kw):
+    n, batch = _shape(U, L)
+    o = options(**kw)
+    if n == 0 or batch == 0:
+        return
+    k_end = n if k_end is None else int(k_end)
+    _call(U, lib().dbs_smooth_opts, U.data_ptr(), L.data_ptr(), n, batch, int(k_begin), k_end,
+          _stream(U), ctypes.byref(o))
+
+
+def smooth(U, L, algo: str = "auto", check: bool = False, lookahead=None,
+           step_blocks=None) -> None:
     """One full smoothing pass on U, L in place (enqueued on the current stream).
 
     check=True first tests the preconditions on the device (dbs_check; this
-    synchronises) and raises ValueError naming the violated ones."""
+    synchronises) and raises ValueError naming the violated ones.  lookahead
+    and step_blocks force the blocked schedule (see options())."""
     n, batch = _shape(U, L)
-    if algo not in _ALGOS:
-        raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
+    options(algo, False, lookahead, step_blocks)
     if n == 0 or batch == 0:
         return
     if check:
@@ -152,21 +188,20 @@ def smooth(U, L, algo: str = "auto", check: bool = False) -> None:
         if bad:
             names = [k for k, v in CHECK_FLAGS.items() if bad & v]
             raise ValueError(f"bounds violate the preconditions: {', '.join(names)}")
-    _call(U, lib().dbs_smooth_algo, U.data_ptr(), L.data_ptr(), n, batch, _stream(U),
-          _ALGOS[algo])
+    _pass(U, L, 0, None, algo=algo, lookahead=lookahead, step_blocks=step_blocks)
 
 
-def smooth_profiled(U, L, algo: str = "auto") -> dict:
+def smooth_profiled(U, L, algo: str = "auto", directed: bool = False, lookahead=None,
+                    step_blocks=None) -> dict:
     """smooth() with HIP events around every kernel launch; synchronises and
     returns {kind: (launches, total_ms)} for the kernel kinds in PROF_KINDS."""
     n, batch = _shape(U, L)
-    if algo not in _ALGOS:
-        raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
+    o = options(algo, directed, lookahead, step_blocks)
     counts = (ctypes.c_int64 * len(PROF_KINDS))()
     ms = (ctypes.c_double * len(PROF_KINDS))()
     if n > 0 and batch > 0:
         _call(U, lib().dbs_smooth_profiled, U.data_ptr(), L.data_ptr(), n, batch, _stream(U),
-              _ALGOS[algo], counts, ms)
+              ctypes.byref(o), counts, ms)
     return {k: (int(counts[i]), float(ms[i])) for i, k in enumerate(PROF_KINDS)}
 
 
@@ -187,33 +222,23 @@ def smooth_round(U, L, k: int) -> None:
     _call(U, lib().dbs_round, U.data_ptr(), L.data_ptr(), n, batch, int(k), _stream(U))
 
 
-def smooth_range(U, L, k_begin: int, k_end: int, algo: str = "auto") -> None:
+def smooth_range(U, L, k_begin: int, k_end: int, algo: str = "auto", lookahead=None,
+                 step_blocks=None) -> None:
     """Rounds k_begin..k_end-1 of a pass, in place (see dbs_smooth_range)."""
-    n, batch = _shape(U, L)
-    if algo not in _ALGOS:
-        raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
-    if n == 0 or batch == 0:
-        return
-    _call(U, lib().dbs_smooth_range, U.data_ptr(), L.data_ptr(), n, batch, int(k_begin),
-          int(k_end), _stream(U), _ALGOS[algo])
+    _pass(U, L, k_begin, k_end, algo=algo, lookahead=lookahead, step_blocks=step_blocks)
 
 
-def smooth_directed_range(U, L, k_begin: int, k_end: int, algo: str = "auto") -> None:
+def smooth_directed_range(U, L, k_begin: int, k_end: int, algo: str = "auto", lookahead=None,
+                          step_blocks=None) -> None:
     """smooth_range with directed rounding: sums of upper bounds rounded up,
     differences of lower bounds rounded down (see dbs_smooth_directed_range)."""
-    n, batch = _shape(U, L)
-    if algo not in _ALGOS:
-        raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
-    if n == 0 or batch == 0:
-        return
-    _call(U, lib().dbs_smooth_directed_range, U.data_ptr(), L.data_ptr(), n, batch,
-          int(k_begin), int(k_end), _stream(U), _ALGOS[algo])
+    _pass(U, L, k_begin, k_end, algo=algo, directed=True, lookahead=lookahead,
+          step_blocks=step_blocks)
 
 
-def smooth_directed(U, L, algo: str = "auto") -> None:
+def smooth_directed(U, L, algo: str = "auto", lookahead=None, step_blocks=None) -> None:
     """A full pass with directed rounding, in place."""
-    n, _ = _shape(U, L)
-    smooth_directed_range(U, L, 0, n, algo)
+    _pass(U, L, 0, None, algo=algo, directed=True, lookahead=lookahead, step_blocks=step_blocks)
 
 
 def tightened(U0, L0, U1, L1):
@@ -303,24 +328,27 @@ def unpack(P):
     return U, L
 
 
-def smooth_packed(P, k_begin: int = 0, k_end=None) -> None:
+def _packed_pass(P, k_begin, k_end, **kw):
+    n, batch = _shape1(P)
+    o = options(**kw)
+    if n == 0 or batch == 0:
+        return
+    k_end = n if k_end is None else int(k_end)
+    _call(P, lib().dbs_smooth_packed_opts, P.data_ptr(), n, batch, int(k_begin), k_end,
+          _stream(P), ctypes.byref(o))
+
+
+def smooth_packed(P, k_begin: int = 0, k_end=None, algo: str = "auto", lookahead=None,
+                  step_blocks=None) -> None:
     """Rounds k_begin..k_end-1 (default: a full pass) on the packed form, in place."""
-    n, batch = _shape1(P)
-    if n == 0 or batch == 0:
-        return
-    k_end = n if k_end is None else int(k_end)
-    _call(P, lib().dbs_smooth_packed_range, P.data_ptr(), n, batch, int(k_begin), k_end,
-          _stream(P))
+    _packed_pass(P, k_begin, k_end, algo=algo, lookahead=lookahead, step_blocks=step_blocks)
 
 
-def smooth_packed_directed(P, k_begin: int = 0, k_end=None) -> None:
+def smooth_packed_directed(P, k_begin: int = 0, k_end=None, algo: str = "auto", lookahead=None,
+                           step_blocks=None) -> None:
     """smooth_packed with directed rounding, in place."""
-    n, batch = _shape1(P)
-    if n == 0 or batch == 0:
-        return
-    k_end = n if k_end is None else int(k_end)
-    _call(P, lib().dbs_smooth_packed_directed_range, P.data_ptr(), n, batch, int(k_begin), k_end,
-          _stream(P))
+    _packed_pass(P, k_begin, k_end, algo=algo, directed=True, lookahead=lookahead,
+                 step_blocks=step_blocks)
 
 
 def _check_flags(U, L) -> int:
@@ -331,8 +359,8 @@ def _check_flags(U, L) -> int:
     flags = torch.zeros(1, dtype=torch.int32, device=U.device)
     if n == 0 or batch == 0:
         return 0
-    _call(U, lib().dbs_check, U.data_ptr(), L.data_ptr(), n, batch, flags.data_ptr(),
-          _stream(U))
+    _call(U, lib().dbs_check, U.data_ptr(), L.data_ptr(), n, batch, _stream(U),
+          flags.data_ptr())
     return int(flags.item()) & 0xFFFFFFFF
 
 
@@ -349,8 +377,18 @@ def check_packed(P) -> int:
     flags = torch.zeros(1, dtype=torch.int32, device=P.device)
     if n == 0 or batch == 0:
         return 0
-    _call(P, lib().dbs_check_packed, P.data_ptr(), n, batch, flags.data_ptr(), _stream(P))
+    _call(P, lib().dbs_check_packed, P.data_ptr(), n, batch, _stream(P), flags.data_ptr())
     return int(flags.item()) & 0xFFFFFFFF
+
+
+def schedule(n: int, batch: int = 1, lookahead=None, step_blocks=None):
+    """(look-ahead depth, k-blocks per step) of a blocked pass of this shape,
+    with the given forced values (None: automatic); see dbs_schedule."""
+    o = options("auto", False, lookahead, step_blocks)
+    la, sb = ctypes.c_int32(), ctypes.c_int32()
+    _raise(lib().dbs_schedule(int(n), int(batch), ctypes.byref(o), ctypes.byref(la),
+                              ctypes.byref(sb)))
+    return int(la.value), int(sb.value)
 
 
 def lookahead_bands(n: int, batch: int = 1) -> int:
@@ -361,18 +399,6 @@ def lookahead_bands(n: int, batch: int = 1) -> int:
 def step_blocks(n: int, batch: int = 1) -> int:
     """k-blocks per step of the blocked pass (1 .. 4)."""
     return int(lib().dbs_step_blocks(int(n), int(batch)))
-
-
-def set_step_blocks(blocks: int) -> None:
-    """Force the k-blocks per step of later blocked passes (1 .. 4), or -1
-    for the automatic choice (process-wide)."""
-    _raise(lib().dbs_set_step_blocks(int(blocks)))
-
-
-def set_lookahead(bands: int) -> None:
-    """Force the look-ahead depth of later blocked passes (0, 1, 2), or -1
-    for the automatic choice (process-wide)."""
-    _raise(lib().dbs_set_lookahead(int(bands)))
 
 
 def auto_algo(n: int, batch: int = 1) -> str:

@@ -64,114 +64,124 @@ int validate(const void *U, const void *L, int64_t n, int64_t batch) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? DBS_OK : DBS_ELAUNCH; }
 
-int run(float *U, float *L, int64_t n, int64_t batch, void *stream, int algo,
-        dbs::Prof *prof = nullptr) {
-  int st = validate(U, L, n, batch);
-  if (st != DBS_OK) return st;
-  if (algo < DBS_ALGO_AUTO || algo > DBS_ALGO_BLOCKED) return DBS_EINVAL;
-  if (algo == DBS_ALGO_AUTO) algo = dbs_auto_algo(n, batch);
-  if (algo == DBS_ALGO_LDS && n > dbs::kSmallMaxN) return DBS_EUNSUPPORTED;
-  st = device_status();
-  if (st != DBS_OK) return st;
-  if (n == 1) return DBS_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (algo) {
-    case DBS_ALGO_PERK: {
-      hipError_t e = hipSuccess;
-      for (int64_t k = 0; k < n && e == hipSuccess; ++k)
-        e = dbs::launch_round(U, L, n, batch, k, s, prof);
-      return status_of(e);
-    }
-    case DBS_ALGO_LDS:
-      return status_of(dbs::launch_small(U, L, n, batch, 0, (int)n, s, prof));
-    default:
-      return status_of(dbs::launch_blocked(U, L, n, batch, 0, dbs::ceil_div(n, dbs::kBlockRounds),
-                                           s, prof));
-  }
+// Options of a pass with the defaults filled in; false for an invalid value.
+bool read_options(const dbs_options *o, dbs_options *out) {
+  dbs_options_init(out);
+  if (!o) return true;
+  if (o->algo < DBS_ALGO_AUTO || o->algo > DBS_ALGO_BLOCKED) return false;
+  if (o->directed != 0 && o->directed != 1) return false;
+  if (o->lookahead < DBS_AUTO || o->lookahead > 2) return false;
+  if (o->step_blocks != DBS_AUTO && (o->step_blocks < 1 || o->step_blocks > dbs::kMaxStepBlocks))
+    return false;
+  *out = *o;
+  return true;
 }
 
-// Rounds k_begin..k_end-1 with algorithm `algo` (AUTO: the single workgroup
-// for small n, blocked when both ends are on k-block boundaries, else one
-// launch per round); flags: dbs::kDirected or 0.
-int range_impl(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,
-               void *stream, int algo, unsigned flags) {
-  int st = validate(U, L, n, batch);
-  if (st != DBS_OK) return st;
+dbs::Sched sched_of(const dbs_options &o) {
+  dbs::Sched sc;
+  sc.lookahead = o.lookahead;
+  sc.step_blocks = o.step_blocks;
+  return sc;
+}
+
+// Rounds k_begin..k_end-1 of a pass on U, L (dense) or on P = U (packed,
+// L ignored), with the given options.  AUTO takes the single workgroup for
+// small n, blocked when both ends are on k-block boundaries, else one launch
+// per round.
+int pass_impl(float *U, float *L, bool packed, int64_t n, int64_t batch, int64_t k_begin,
+              int64_t k_end, void *stream, const dbs_options *opts, dbs::Prof *prof) {
+  if (packed) {
+    uint64_t bytes = 0;
+    if (check_buffer(U, n, batch, &bytes) != DBS_OK) return DBS_EINVAL;
+    L = U;
+  } else {
+    const int st = validate(U, L, n, batch);
+    if (st != DBS_OK) return st;
+  }
+  dbs_options o;
+  if (!read_options(opts, &o)) return DBS_EINVAL;
   if (k_begin < 0 || k_end > n || k_begin > k_end) return DBS_EINVAL;
-  if (algo < DBS_ALGO_AUTO || algo > DBS_ALGO_BLOCKED) return DBS_EINVAL;
   const int64_t B = dbs::kBlockRounds;
   const bool aligned = k_begin % B == 0 && (k_end % B == 0 || k_end == n);
+  int algo = o.algo;
   if (algo == DBS_ALGO_AUTO)
     algo = n <= dbs::kSmallMaxN ? DBS_ALGO_LDS : aligned ? DBS_ALGO_BLOCKED : DBS_ALGO_PERK;
   if (algo == DBS_ALGO_LDS && n > dbs::kSmallMaxN) return DBS_EUNSUPPORTED;
   if (algo == DBS_ALGO_BLOCKED && !aligned) return DBS_EUNSUPPORTED;
-  st = device_status();
-  if (st != DBS_OK) return st;
-  if (k_begin == k_end || n == 1) return DBS_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (algo) {
-    case DBS_ALGO_PERK: {
-      hipError_t e = hipSuccess;
-      for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
-        e = dbs::launch_round(U, L, n, batch, k, s, nullptr, flags);
-      return status_of(e);
-    }
-    case DBS_ALGO_LDS:
-      return status_of(
-          dbs::launch_small(U, L, n, batch, (int)k_begin, (int)k_end, s, nullptr, flags));
-    default:
-      return status_of(dbs::launch_blocked(U, L, n, batch, k_begin / B, dbs::ceil_div(k_end, B),
-                                           s, nullptr, flags));
-  }
-}
-
-// The packed counterpart (P in the one-buffer layout), same algorithm choice.
-int packed_range_impl(float *P, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,
-                      void *stream, unsigned flags) {
-  uint64_t bytes = 0;
-  if (check_buffer(P, n, batch, &bytes) != DBS_OK) return DBS_EINVAL;
-  if (k_begin < 0 || k_end > n || k_begin > k_end) return DBS_EINVAL;
   const int st = device_status();
   if (st != DBS_OK) return st;
   if (k_begin == k_end || n == 1) return DBS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t B = dbs::kBlockRounds;
-  flags |= dbs::kPacked;
-  if (n <= dbs::kSmallMaxN)
-    return status_of(
-        dbs::launch_small(P, P, n, batch, (int)k_begin, (int)k_end, s, nullptr, flags));
-  if (k_begin % B == 0 && (k_end % B == 0 || k_end == n))
-    return status_of(dbs::launch_blocked(P, P, n, batch, k_begin / B, dbs::ceil_div(k_end, B), s,
-                                         nullptr, flags));
-  hipError_t e = hipSuccess;
-  for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
-    e = dbs::launch_round_packed(P, n, batch, k, s, nullptr, flags);
-  return status_of(e);
+  const unsigned flags = (packed ? dbs::kPacked : 0u) | (o.directed ? dbs::kDirected : 0u);
+  switch (algo) {
+    case DBS_ALGO_PERK: {
+      hipError_t e = hipSuccess;
+      for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
+        e = packed ? dbs::launch_round_packed(U, n, batch, k, s, prof, flags)
+                   : dbs::launch_round(U, L, n, batch, k, s, prof, flags);
+      return status_of(e);
+    }
+    case DBS_ALGO_LDS:
+      return status_of(
+          dbs::launch_small(U, L, n, batch, (int)k_begin, (int)k_end, s, prof, flags));
+    default:
+      return status_of(dbs::launch_blocked(U, L, n, batch, k_begin / B, dbs::ceil_div(k_end, B),
+                                           s, prof, flags, sched_of(o)));
+  }
+}
+
+int pass_with(float *U, float *L, bool packed, int64_t n, int64_t batch, int64_t k_begin,
+              int64_t k_end, void *stream, int algo, int directed) {
+  dbs_options o;
+  dbs_options_init(&o);
+  o.algo = algo;
+  o.directed = directed;
+  return pass_impl(U, L, packed, n, batch, k_begin, k_end, stream, &o, nullptr);
 }
 
 }  // namespace
 
 extern "C" {
 
+void dbs_options_init(dbs_options *opts) {
+  if (!opts) return;
+  opts->algo = DBS_ALGO_AUTO;
+  opts->directed = 0;
+  opts->lookahead = DBS_AUTO;
+  opts->step_blocks = DBS_AUTO;
+}
+
+int dbs_smooth_opts(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
+                    int64_t k_end, void *stream, const dbs_options *opts) {
+  return pass_impl(U, L, false, n, batch, k_begin, k_end, stream, opts, nullptr);
+}
+
+int dbs_smooth_packed_opts(float *P, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,
+                           void *stream, const dbs_options *opts) {
+  return pass_impl(P, nullptr, true, n, batch, k_begin, k_end, stream, opts, nullptr);
+}
+
 int dbs_smooth(float *U, float *L, int64_t n, int64_t batch, void *stream) {
-  return run(U, L, n, batch, stream, DBS_ALGO_AUTO);
+  return pass_with(U, L, false, n, batch, 0, n, stream, DBS_ALGO_AUTO, 0);
 }
 
 int dbs_smooth_algo(float *U, float *L, int64_t n, int64_t batch, void *stream, int algo) {
-  return run(U, L, n, batch, stream, algo);
+  return pass_with(U, L, false, n, batch, 0, n, stream, algo, 0);
 }
 
-int dbs_smooth_profiled(float *U, float *L, int64_t n, int64_t batch, void *stream, int algo,
-                        int64_t *counts, double *ms) {
+int dbs_smooth_profiled(float *U, float *L, int64_t n, int64_t batch, void *stream,
+                        const dbs_options *opts, int64_t *counts, double *ms) {
   if (!counts || !ms) return DBS_EINVAL;
   for (int i = 0; i < DBS_PROF_KINDS; ++i) {
     counts[i] = 0;
     ms[i] = 0.0;
   }
   dbs::Prof prof;
-  int st = run(U, L, n, batch, stream, algo, &prof);
+  int st = pass_impl(U, L, false, n, batch, 0, n, stream, opts, &prof);
   if (st != DBS_OK) return st;
-  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return DBS_ELAUNCH;
+  // the launches may be spread over two streams: wait for every stop event
+  for (const auto &m : prof.marks)
+    if (hipEventSynchronize(m.stop) != hipSuccess) return DBS_ELAUNCH;
   for (const auto &m : prof.marks) {
     float t = 0.0f;
     if (hipEventElapsedTime(&t, m.start, m.stop) != hipSuccess) return DBS_ELAUNCH;
@@ -200,8 +210,8 @@ int dbs_round(float *U, float *L, int64_t n, int64_t batch, int64_t k, void *str
   return dbs_rounds(U, L, n, batch, k, k + 1, stream);
 }
 
-int dbs_check(const float *U, const float *L, int64_t n, int64_t batch, uint32_t *d_flags,
-              void *stream) {
+int dbs_check(const float *U, const float *L, int64_t n, int64_t batch, void *stream,
+              uint32_t *d_flags) {
   int st = validate(U, L, n, batch);
   if (st != DBS_OK) return st;
   if (!d_flags) return DBS_EINVAL;
@@ -212,16 +222,16 @@ int dbs_check(const float *U, const float *L, int64_t n, int64_t batch, uint32_t
 
 int dbs_smooth_range(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
                      int64_t k_end, void *stream, int algo) {
-  return range_impl(U, L, n, batch, k_begin, k_end, stream, algo, 0);
+  return pass_with(U, L, false, n, batch, k_begin, k_end, stream, algo, 0);
 }
 
 int dbs_smooth_directed_range(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
                               int64_t k_end, void *stream, int algo) {
-  return range_impl(U, L, n, batch, k_begin, k_end, stream, algo, dbs::kDirected);
+  return pass_with(U, L, false, n, batch, k_begin, k_end, stream, algo, 1);
 }
 
 int dbs_smooth_directed(float *U, float *L, int64_t n, int64_t batch, void *stream) {
-  return range_impl(U, L, n, batch, 0, n, stream, DBS_ALGO_AUTO, dbs::kDirected);
+  return pass_with(U, L, false, n, batch, 0, n, stream, DBS_ALGO_AUTO, 1);
 }
 
 int dbs_block_rounds(void) { return dbs::kBlockRounds; }
@@ -286,15 +296,15 @@ int dbs_unpack(const float *P, float *U, float *L, int64_t n, int64_t batch, voi
 
 int dbs_smooth_packed_range(float *P, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,
                             void *stream) {
-  return packed_range_impl(P, n, batch, k_begin, k_end, stream, 0);
+  return pass_with(P, nullptr, true, n, batch, k_begin, k_end, stream, DBS_ALGO_AUTO, 0);
 }
 
 int dbs_smooth_packed_directed_range(float *P, int64_t n, int64_t batch, int64_t k_begin,
                                      int64_t k_end, void *stream) {
-  return packed_range_impl(P, n, batch, k_begin, k_end, stream, dbs::kDirected);
+  return pass_with(P, nullptr, true, n, batch, k_begin, k_end, stream, DBS_ALGO_AUTO, 1);
 }
 
-int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags, void *stream) {
+int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uint32_t *d_flags) {
   uint64_t bytes = 0;
   if (check_buffer(P, n, batch, &bytes) != DBS_OK || !d_flags) return DBS_EINVAL;
   const int st = device_status();
@@ -308,22 +318,24 @@ int dbs_smooth_packed(float *P, int64_t n, int64_t batch, void *stream) {
 
 int dbs_lds_max_n(void) { return dbs::kSmallMaxN; }
 
+int dbs_schedule(int64_t n, int64_t batch, const dbs_options *opts, int32_t *lookahead,
+                 int32_t *step_blocks) {
+  dbs_options o;
+  if (n < 1 || batch < 1 || !read_options(opts, &o)) return DBS_EINVAL;
+  const dbs::Sched sc = sched_of(o);
+  if (lookahead) *lookahead = dbs::lookahead_bands(n, batch, sc);
+  if (step_blocks) *step_blocks = dbs::step_blocks(n, batch, sc);
+  return DBS_OK;
+}
+
 int dbs_lookahead_bands(int64_t n, int64_t batch) {
   if (n < 1 || batch < 1) return DBS_EINVAL;
   return dbs::lookahead_bands(n, batch);
 }
 
-int dbs_set_lookahead(int bands) {
-  return dbs::set_lookahead(bands) ? DBS_OK : DBS_EINVAL;
-}
-
 int dbs_step_blocks(int64_t n, int64_t batch) {
   if (n < 1 || batch < 1) return DBS_EINVAL;
   return dbs::step_blocks(n, batch);
-}
-
-int dbs_set_step_blocks(int blocks) {
-  return dbs::set_step_blocks(blocks) ? DBS_OK : DBS_EINVAL;
 }
 
 int dbs_auto_algo(int64_t n, int64_t batch) {

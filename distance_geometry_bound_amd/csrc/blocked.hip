@@ -31,8 +31,10 @@
 // register tile (512 threads with 4x2 tiles when a launch has fewer blocks
 // than CUs); the panel rows of the k-block are staged through LDS.  No
 // matrix cores: min-plus is not a multiply-add contraction.
-#include <atomic>
+#include <map>
+#include <memory>
 #include <mutex>
+#include <utility>
 
 #include "dbs_internal.h"
 
@@ -1167,91 +1169,101 @@ __global__ __launch_bounds__(kThreads) void k_mirror(float *__restrict__ U, floa
   }
 }
 
-// Side stream for the lookahead (one per device, default priority, created
-// on first use and kept for the life of the process).
-hipStream_t side_stream() {
-  static std::mutex mu;
-  static hipStream_t streams[64];
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!streams[dev]) {
-    hipStream_t st = nullptr;
-    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess) streams[dev] = st;
-  }
-  return streams[dev];
-}
-
-// Ordering events of the lookahead: one set per host thread and device,
-// created on first use and re-recorded by every pass (a stream wait captures
-// the event's state when it is enqueued, so re-recording is safe).
-// The events only order the two streams of one device: the kernels they
+// The ordering events of a pass that runs part of its work on a second
+// stream.  They only order the two streams of one device: the kernels they
 // follow end with a device-scope release and the kernels that wait on them
-// start with an acquire, so the event needs no timing and no system-scope
-// fence of its own (which writes back the caches and costs about 11 us per
+// start with an acquire, so the events need no timing and no system-scope
+// fence of their own (which writes back the caches and costs about 11 us per
 // hop between the streams).
 constexpr unsigned kOrderingEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
 
-struct Events {
-  // start: the first step's panel; bulk[t & 1]: bulk(t) done;
-  // ready[t & 1]: the side stream's work that bulk(t) needs is done
+// A lane: the library's second stream for one caller stream on one device
+// (default priority, non-blocking), and the events that order the two.  A
+// lane is created on the first pass enqueued on that caller stream that needs
+// it and kept for the life of the process; its mutex is held while a pass
+// is enqueued through it, so that passes enqueued from several host threads
+// on one caller stream do not interleave their event records.  Passes on
+// different caller streams use different lanes and share nothing.
+struct Lane {
+  std::mutex mu;
+  hipStream_t side = nullptr;
+  // start: the fork from the caller's stream; bulk[t & 1]: bulk(t) done;
+  // ready[t & 1]: the side stream's work that bulk(t) needs is done.  A
+  // stream wait captures the event's state when it is enqueued, so the
+  // events are re-recorded by every pass.
   hipEvent_t e[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
   hipEvent_t &start() { return e[0]; }
   hipEvent_t &bulk(int64_t t) { return e[1 + (t & 1)]; }
   hipEvent_t &ready(int64_t t) { return e[3 + (t & 1)]; }
-  bool created = false;
   bool init() {
-    if (created) return true;
+    if (hipStreamCreateWithFlags(&side, hipStreamNonBlocking) != hipSuccess) {
+      side = nullptr;
+      return false;
+    }
     for (auto &x : e)
-      if (!x && hipEventCreateWithFlags(&x, kOrderingEventFlags) != hipSuccess) return false;
-    created = true;
+      if (hipEventCreateWithFlags(&x, kOrderingEventFlags) != hipSuccess) return false;
     return true;
-  }
-  ~Events() {
-    for (auto &x : e)
-      if (x) (void)hipEventDestroy(x);
   }
 };
 
-Events *thread_events() {
-  thread_local Events per_device[64];
+// Lanes per device; passes on further caller streams run on one stream.
+constexpr int kMaxLanes = 64;
+constexpr int kMaxDevices = 64;
+
+// The lane of caller stream `s` on the current device, locked; none (an
+// unlocked guard) when no lane can be had.  A lane whose second stream is
+// part of a graph capture that this pass does not belong to (a capture of
+// another stream sharing the handle, still open) is not used either.
+std::unique_lock<std::mutex> lock_lane(hipStream_t s, Lane **out) {
+  *out = nullptr;
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  return per_device[dev].init() ? &per_device[dev] : nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return {};
+  static std::mutex registry_mu;
+  static std::map<std::pair<int, uintptr_t>, std::unique_ptr<Lane>> lanes;
+  static int per_device[kMaxDevices];
+  Lane *lane = nullptr;
+  {
+    std::lock_guard<std::mutex> g(registry_mu);
+    const auto key = std::make_pair(dev, reinterpret_cast<uintptr_t>(s));
+    auto it = lanes.find(key);
+    if (it != lanes.end()) {
+      lane = it->second.get();
+    } else if (per_device[dev] < kMaxLanes) {
+      auto fresh_lane = std::make_unique<Lane>();
+      if (!fresh_lane->init()) return {};  // a half-made lane is dropped (its handles leak)
+      lane = fresh_lane.get();
+      lanes.emplace(key, std::move(fresh_lane));
+      ++per_device[dev];
+    }
+  }
+  if (!lane) return {};
+  std::unique_lock<std::mutex> lk(lane->mu);
+  hipStreamCaptureStatus cs_side = hipStreamCaptureStatusNone, cs_own = hipStreamCaptureStatusNone;
+  unsigned long long id_side = 0, id_own = 0;
+  if (hipStreamGetCaptureInfo(lane->side, &cs_side, &id_side) != hipSuccess ||
+      hipStreamGetCaptureInfo(s, &cs_own, &id_own) != hipSuccess)
+    return {};
+  if (cs_side != hipStreamCaptureStatusNone &&
+      (cs_own != hipStreamCaptureStatusActive || cs_side != hipStreamCaptureStatusActive ||
+       id_own != id_side))
+    return {};
+  *out = lane;
+  return lk;
 }
 
 }  // namespace
 
-namespace {
-std::atomic<int> forced_lookahead{-1};  // -1: automatic
-std::atomic<int> forced_step{-1};       // -1: automatic
-}  // namespace
-
-bool set_lookahead(int bands) {
-  if (bands < -1 || bands > 2) return false;
-  forced_lookahead.store(bands);
-  return true;
-}
-
-bool set_step_blocks(int blocks) {
-  if (blocks != -1 && (blocks < 1 || blocks > kMaxStepBlocks)) return false;
-  forced_step.store(blocks);
-  return true;
-}
-
-int step_blocks(int64_t n, int64_t batch) {
-  const int forced = forced_step.load();
-  if (forced > 0) return forced;
-  if (lookahead_bands(n, batch) != 2) return 1;
+int step_blocks(int64_t n, int64_t batch, const Sched &sched) {
+  if (sched.step_blocks > 0) return sched.step_blocks;
+  if (lookahead_bands(n, batch, sched) != 2) return 1;
   const int64_t T = ceil_div(n, TILE), tiles = T * (T + 1) / 2 * batch;
   return tiles >= kStep4Tiles ? 4 : tiles >= kStep3Tiles ? 3 : 2;
 }
 
-int lookahead_bands(int64_t n, int64_t batch) {
+int lookahead_bands(int64_t n, int64_t batch, const Sched &sched) {
   const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
   if (TB <= 1 || T <= 1) return 0;
-  const int forced = forced_lookahead.load();
-  if (forced >= 0) return forced;
+  if (sched.lookahead >= 0) return sched.lookahead;
   const int64_t tiles = T * (T + 1) / 2 * batch;
   if (tiles >= kDeepTiles) return 2;
   // where one phase 1-2 launch fills the chip the batch splits over the two
@@ -1281,18 +1293,20 @@ int lookahead_bands(int64_t n, int64_t batch) {
 // cell by cell, for both depths.
 namespace {
 hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
-                             hipStream_t s, Prof *prof, unsigned flags, bool half);
+                             hipStream_t s, Prof *prof, unsigned flags, const Sched &sched,
+                             bool half);
 }  // namespace
 
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
-                          hipStream_t s, Prof *prof, unsigned flags) {
-  return launch_blocked_on(U, L, n, batch, K0, K1, s, prof, flags, false);
+                          hipStream_t s, Prof *prof, unsigned flags, const Sched &sched) {
+  return launch_blocked_on(U, L, n, batch, K0, K1, s, prof, flags, sched, false);
 }
 
 namespace {
 // `half`: one half of a split batch, run on one stream without look-ahead.
 hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
-                             hipStream_t s, Prof *prof, unsigned flags, bool half) {
+                             hipStream_t s, Prof *prof, unsigned flags, const Sched &sched,
+                             bool half) {
   static_assert(BK == kBlockRounds, "k-block size");
   const int64_t TB = ceil_div(n, BK);    // k-blocks
   if (K1 > TB) K1 = TB;
@@ -1325,27 +1339,30 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   // critical path: one step ahead or none, on 1024-thread workgroups that
   // hide the latency of their rounds best.
   const int64_t pairs = T * (T + 1) / 2;
-  const int ahead = half ? 0 : lookahead_bands(n, batch);
+  const int ahead = half ? 0 : lookahead_bands(n, batch, sched);
   // A batch whose phase 1-2 launch fills the chip by itself splits into two
   // halves, one per stream: the molecules share nothing, so the phase 1-2
   // launches of one half run beside the bulk of the other.  With fewer
   // workgroups per launch the two halves only contend, and one stream in
   // order is faster.
-  if (ahead == 0 && !half && batch >= 2 && TB > 1 && T > 1 && (TB - 1) * batch > kPanelFill) {
-    hipStream_t side = side_stream();
-    Events *ev = side ? thread_events() : nullptr;
-    if (side && ev) {
-      const int64_t b1 = batch / 2;
-      hipError_t e = hipEventRecord(ev->start(), s);
-      if (e == hipSuccess) e = hipStreamWaitEvent(side, ev->start(), 0);
-      if (e == hipSuccess) e = launch_blocked_on(U, L, n, b1, K0, K1, s, prof, flags, true);
-      if (e == hipSuccess)
-        e = launch_blocked_on(U + b1 * nn, L + b1 * nn, n, batch - b1, K0, K1, side, prof, flags,
-                              true);
-      if (e == hipSuccess) e = hipEventRecord(ev->bulk(0), side);
-      if (e == hipSuccess) e = hipStreamWaitEvent(s, ev->bulk(0), 0);
-      return e;
-    }
+  const bool split =
+      ahead == 0 && !half && batch >= 2 && TB > 1 && T > 1 && (TB - 1) * batch > kPanelFill;
+  // the second stream of this caller stream, held (locked) until the whole
+  // pass is enqueued
+  Lane *lane = nullptr;
+  std::unique_lock<std::mutex> lane_lock;
+  if (split || (ahead > 0 && TB > 1)) lane_lock = lock_lane(s, &lane);
+  if (split && lane) {
+    const int64_t b1 = batch / 2;
+    hipError_t e = hipEventRecord(lane->start(), s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(lane->side, lane->start(), 0);
+    if (e == hipSuccess) e = launch_blocked_on(U, L, n, b1, K0, K1, s, prof, flags, sched, true);
+    if (e == hipSuccess)
+      e = launch_blocked_on(U + b1 * nn, L + b1 * nn, n, batch - b1, K0, K1, lane->side, prof,
+                            flags, sched, true);
+    if (e == hipSuccess) e = hipEventRecord(lane->bulk(0), lane->side);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, lane->bulk(0), 0);
+    return e;
   }
   const bool deep = ahead == 2;
   if (ahead == 0 && 4 * pairs * batch <= kSmallGrid) {
@@ -1374,7 +1391,7 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   // [lo(t), hi(t)).  Two steps ahead the bulk takes several blocks per
   // launch, which spreads its fixed costs (the loads and stores of the
   // matrix, the launch's ramp and tail) over more atoms.
-  const int64_t W = step_blocks(n, batch), NS = ceil_div(K1 - K0, W);
+  const int64_t W = step_blocks(n, batch, sched), NS = ceil_div(K1 - K0, W);
   auto lo = [&](int64_t t) { return K0 + t * W; };
   auto hi = [&](int64_t t) { return K0 + (t + 1) * W < K1 ? K0 + (t + 1) * W : K1; };
 
@@ -1413,9 +1430,9 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   hipError_t e = step_panel(0, s);
   if (e != hipSuccess || TB == 1) return e;
 
-  hipStream_t side = ahead > 0 ? side_stream() : nullptr;
-  Events *ev = side ? thread_events() : nullptr;
-  if (side == nullptr || ev == nullptr) {
+  hipStream_t side = ahead > 0 && lane ? lane->side : nullptr;
+  Lane *ev = lane;
+  if (side == nullptr) {
     for (int64_t t = 0; t < NS && e == hipSuccess; ++t) {
       e = phase3(lo(t), hi(t) - lo(t), hi(t), s);
       if (e == hipSuccess && t + 1 < NS) e = step_panel(t + 1, s);

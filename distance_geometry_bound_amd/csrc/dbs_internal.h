@@ -185,21 +185,24 @@ hipError_t launch_round(float *U, float *L, int64_t n, int64_t batch, int64_t k,
 // rounds k_lo..k_hi-1 of a whole small molecule in one workgroup
 hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, int k_lo, int k_hi,
                         hipStream_t s, Prof *prof = nullptr, unsigned flags = 0);
+// Schedule of a blocked pass chosen by the caller: a forced look-ahead depth
+// (0..2) and k-blocks per step (1..kMaxStepBlocks), or -1 for the automatic
+// choice.  Every schedule gives the same results.
+struct Sched {
+  int lookahead = -1;
+  int step_blocks = -1;
+};
 // k-blocks K0..K1-1 of the blocked pass (rounds 64*K0 .. min(64*K1, n)-1)
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
-                          hipStream_t s, Prof *prof = nullptr, unsigned flags = 0);
+                          hipStream_t s, Prof *prof = nullptr, unsigned flags = 0,
+                          const Sched &sched = Sched());
 constexpr int kBlockRounds = 64;
 // Look-ahead depth of the blocked pass: steps it updates ahead on its second
-// stream (0, 1 or 2; at 2 a step is two k-blocks).
-int lookahead_bands(int64_t n, int64_t batch);
-// Force the look-ahead depth (0..2) or restore the automatic choice (-1);
-// false (and no change) for any other value.
-bool set_lookahead(int bands);
-// k-blocks per step of the blocked pass (1 .. kMaxStepBlocks), and the
-// override of that choice (-1: automatic).
+// stream (0, 1 or 2; at 2 a step is several k-blocks).
+int lookahead_bands(int64_t n, int64_t batch, const Sched &sched = Sched());
+// k-blocks per step of the blocked pass (1 .. kMaxStepBlocks).
 constexpr int kMaxStepBlocks = 4;
-int step_blocks(int64_t n, int64_t batch);
-bool set_step_blocks(int blocks);
+int step_blocks(int64_t n, int64_t batch, const Sched &sched = Sched());
 hipError_t launch_restraints(float *U, float *L, int64_t n, int64_t batch, float unknown_L,
                              float unknown_U, const int32_t *mol, const int32_t *ia,
                              const int32_t *ja, const float *lo, const float *hi, int64_t count,

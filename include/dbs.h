@@ -41,9 +41,21 @@
  * Execution: every call validates its arguments on the host, then enqueues
  * kernels on `stream` (a hipStream_t; NULL means the null stream) and
  * returns without synchronising.  Faults of enqueued kernels surface at the
- * caller's next synchronisation, as usual in HIP.  Calls on different
- * streams are independent; calls that touch the same matrices must be
- * ordered by the caller.  The library is thread-safe.
+ * caller's next synchronisation, as usual in HIP.  Calls that touch the same
+ * matrices must be ordered by the caller.  The library is thread-safe and
+ * keeps no settings between calls: every choice a pass makes comes from its
+ * arguments (dbs_options below).
+ *
+ * A blocked pass may also run part of its work on a second stream that the
+ * library owns (see dbs_schedule): one such stream per device and caller
+ * stream, created on the first pass enqueued on that caller stream and kept
+ * for the life of the process, forked from and joined back into the caller's
+ * stream with events.  Passes on different caller streams therefore share
+ * no library stream and run independently.  (Past 64 caller streams on one
+ * device, further streams get no second stream of their own and their
+ * passes run on the caller's stream alone, with the same results.)  A pass
+ * enqueued on a stream that is being captured into a HIP graph brings the
+ * second stream into that capture and joins it back before returning.
  *
  * Status codes (every int-returning entry point):
  */
@@ -70,6 +82,49 @@ extern "C" {
                               n <= dbs_lds_max_n()                            */
 #define DBS_ALGO_BLOCKED 3 /* three-phase blocked pass (diagonal tile, panel,
                               remaining tiles), symmetric tile schedule       */
+
+/*
+ * Per-call options of a pass (dbs_smooth_opts, dbs_smooth_packed_opts,
+ * dbs_smooth_profiled, dbs_schedule).  A NULL pointer means the defaults,
+ * which dbs_options_init also writes:
+ *   algo         DBS_ALGO_* (default DBS_ALGO_AUTO);
+ *   directed     0: round to nearest (default); 1: directed rounding, see
+ *                dbs_smooth_directed_range;
+ *   lookahead    DBS_AUTO (default), or 0, 1, 2: force that look-ahead depth
+ *                of a blocked pass (dbs_schedule);
+ *   step_blocks  DBS_AUTO (default), or 1 .. 4: force that many k-blocks per
+ *                step of a blocked pass.
+ * The schedule fields only reorder independent cell updates: every value
+ * gives the same results.  They exist for tests and tuning.  Any other value
+ * of a field makes the call return DBS_EINVAL.  The options are read during
+ * the call; the library keeps no pointer to them.
+ */
+#define DBS_AUTO (-1)
+typedef struct dbs_options {
+  int32_t algo;
+  int32_t directed;
+  int32_t lookahead;
+  int32_t step_blocks;
+} dbs_options;
+
+void dbs_options_init(dbs_options *opts);
+
+/*
+ * dbs_smooth_opts -- rounds k_begin..k_end-1 of a pass on U, L in place with
+ * the given options: the general form of dbs_smooth, dbs_smooth_algo,
+ * dbs_smooth_range, dbs_smooth_directed and dbs_smooth_directed_range
+ * (which are this call with the matching options).  Arguments, algorithm
+ * rules and errors as dbs_smooth_range; DBS_EINVAL for invalid options.
+ *
+ * dbs_smooth_packed_opts -- the same on the packed one-buffer layout P (see
+ * dbs_smooth_packed_range): DBS_ALGO_PERK, DBS_ALGO_LDS and DBS_ALGO_BLOCKED
+ * follow the rules of dbs_smooth_range; DBS_ALGO_AUTO takes LDS when it
+ * fits, else BLOCKED when both ends are on k-block boundaries, else PERK.
+ */
+int dbs_smooth_opts(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
+                    int64_t k_end, void *stream, const dbs_options *opts);
+int dbs_smooth_packed_opts(float *P, int64_t n, int64_t batch, int64_t k_begin,
+                           int64_t k_end, void *stream, const dbs_options *opts);
 
 /*
  * dbs_smooth -- one full smoothing pass (rounds k = 0..n-1) on every molecule,
@@ -115,8 +170,8 @@ int dbs_round(float *U, float *L, int64_t n, int64_t batch, int64_t k, void *str
  * the output of a pass to detect inconsistent bounds (DBS_CHECK_L_GT_U).
  * Same argument errors as dbs_smooth (d_flags must be non-null).
  */
-int dbs_check(const float *U, const float *L, int64_t n, int64_t batch,
-              uint32_t *d_flags, void *stream);
+int dbs_check(const float *U, const float *L, int64_t n, int64_t batch, void *stream,
+              uint32_t *d_flags);
 
 #define DBS_CHECK_ASYM 1u        /* U or L not bit-for-bit symmetric          */
 #define DBS_CHECK_DIAG 2u        /* a diagonal entry is not +0.0              */
@@ -128,16 +183,17 @@ int dbs_check(const float *U, const float *L, int64_t n, int64_t batch,
 #define DBS_CHECK_NEGZERO 128u   /* -0.0                                      */
 
 /*
- * dbs_smooth_profiled -- dbs_smooth_algo with every kernel launch bracketed by
- * a HIP event pair on `stream`; waits for the pass to finish (synchronises
- * `stream`) and fills, per kernel kind DBS_PROF_*, the number of launches
- * (counts[kind]) and their summed device time in milliseconds (ms[kind]).
+ * dbs_smooth_profiled -- one full pass as dbs_smooth_opts(U, L, n, batch, 0,
+ * n, stream, opts), with every kernel launch bracketed by a HIP event pair
+ * on the stream it is launched on; waits for the pass to finish and fills,
+ * per kernel kind DBS_PROF_*, the number of launches (counts[kind]) and their
+ * summed device time in milliseconds (ms[kind]).
  *   counts, ms  host arrays of DBS_PROF_KINDS elements, written by the call.
- * Same argument errors as dbs_smooth_algo; DBS_EINVAL if counts or ms is
+ * Same argument errors as dbs_smooth_opts; DBS_EINVAL if counts or ms is
  * null.  The events add a few microseconds per launch; for measurement only.
  */
 int dbs_smooth_profiled(float *U, float *L, int64_t n, int64_t batch, void *stream,
-                        int algo, int64_t *counts, double *ms);
+                        const struct dbs_options *opts, int64_t *counts, double *ms);
 
 #define DBS_PROF_ROUND 0   /* per-round kernel                                 */
 #define DBS_PROF_SMALL 1   /* single-workgroup pass (whole molecule or diagonal tile) */
@@ -278,61 +334,40 @@ int dbs_unpack(const float *P, float *U, float *L, int64_t n, int64_t batch, voi
 int dbs_smooth_packed(float *P, int64_t n, int64_t batch, void *stream);
 int dbs_smooth_packed_range(float *P, int64_t n, int64_t batch, int64_t k_begin, int64_t k_end,
                             void *stream);
-int dbs_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *d_flags, void *stream);
+int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uint32_t *d_flags);
 
 /*
- * dbs_lookahead_bands -- the look-ahead depth of the blocked pass (DBS_ALGO_
- * BLOCKED) on the dense layout for this shape: how many steps it updates
- * ahead on its second stream.
- *   0  no look-ahead: a single k-block or phase-3 tile; fewer than 256
- *      phase-3 tiles x molecules (the bulk launch is shorter than the band
- *      strip it would hide); or more than 256 phase 1-2 workgroups (the
- *      panel launch fills the chip by itself).  Without look-ahead, a batch
- *      of two or more molecules with more than 256 phase 1-2 workgroups
- *      ((k-blocks - 1) x molecules) splits into two halves, one on the
- *      caller's stream and one on the second stream, so that one half's
- *      phase 1-2 launches run beside the other half's phase 3; otherwise
- *      the pass uses the caller's stream alone;
- *   1  otherwise, below 1024 tiles x molecules: steps of one k-block;
- *   2  from 1024 tiles x molecules: steps of two to four k-blocks
- *      (dbs_step_blocks), so that each phase-3 launch runs 128 to 256 atoms
- *      (fewer loads and stores of the matrix per atom), and the panel of
- *      the next step has a whole phase-3 launch to hide under.
- * The packed passes (dbs_smooth_packed*) follow the same choice.
- * A depth set by dbs_set_lookahead replaces the automatic choice (still 0
- * for a single k-block or tile).  Phase 3's bulk launches leave the bands of
- * the steps run ahead to the second stream.  For measurement and tests;
- * DBS_EINVAL for n < 1 or batch < 1.
+ * dbs_schedule -- the schedule a blocked pass (DBS_ALGO_BLOCKED, dense or
+ * packed layout) takes for this shape under `opts` (NULL: the defaults):
+ *   *lookahead    how many steps it updates ahead on its second stream:
+ *     0  no look-ahead: a single k-block or phase-3 tile; fewer than 256
+ *        phase-3 tiles x molecules (the bulk launch is shorter than the band
+ *        strip it would hide); or more than 256 phase 1-2 workgroups (the
+ *        panel launch fills the chip by itself).  Without look-ahead, a
+ *        batch of two or more molecules with more than 256 phase 1-2
+ *        workgroups ((k-blocks - 1) x molecules) splits into two halves, one
+ *        on the caller's stream and one on the second stream, so that one
+ *        half's phase 1-2 launches run beside the other half's phase 3;
+ *        otherwise the pass uses the caller's stream alone;
+ *     1  otherwise, below 1024 tiles x molecules: steps of one k-block;
+ *     2  from 1024 tiles x molecules: steps of several k-blocks.
+ *   *step_blocks  k-blocks per step: where it runs two steps ahead, 4 from
+ *     3000 phase-3 tiles x molecules, 3 from 1800, else 2; otherwise 1.  A
+ *     step of w blocks is blocked Floyd-Warshall with 64w atoms per phase-3
+ *     launch; its panel (the rows of the step's bands, final for all of its
+ *     rounds) is built from the 64-wide phase 1-2 kernel and phase-3 strips.
+ * opts->lookahead and opts->step_blocks, when not DBS_AUTO, replace these
+ * choices (the depth stays 0 for a single k-block or tile).  Every schedule
+ * gives the same results.  Either output pointer may be NULL.  Returns
+ * DBS_OK, or DBS_EINVAL for n < 1, batch < 1 or invalid options.
  */
+int dbs_schedule(int64_t n, int64_t batch, const struct dbs_options *opts, int32_t *lookahead,
+                 int32_t *step_blocks);
+
+/* dbs_schedule's automatic look-ahead depth and step width for this shape
+   (DBS_EINVAL for n < 1 or batch < 1). */
 int dbs_lookahead_bands(int64_t n, int64_t batch);
-
-/*
- * dbs_set_lookahead -- process-wide override of the look-ahead depth of the
- * blocked passes enqueued after the call: bands = 0, 1 or 2 forces that
- * depth, -1 restores the automatic choice.  Every depth gives the same
- * results (the schedule only reorders independent cell updates); this is
- * for tests and tuning.  Returns DBS_OK, or DBS_EINVAL for any other value
- * (the setting is then unchanged).
- */
-int dbs_set_lookahead(int bands);
-
-/*
- * dbs_step_blocks -- k-blocks per step of the blocked pass on the dense
- * layout for this shape, unless dbs_set_step_blocks set a width: where it
- * runs two steps ahead (dbs_lookahead_bands), 4 from 3000 phase-3 tiles x
- * molecules, 3 from 1800, else 2; 1 where it runs one step ahead or none.
- * A step of w blocks is blocked Floyd-Warshall with 64w atoms per phase-3
- * launch; its panel (the rows of the step's bands, final for all of its
- * rounds) is built from the 64-wide phase 1-2 kernel and strips of phase 3.
- * For measurement and tests; DBS_EINVAL for n < 1 or batch < 1.
- *
- * dbs_set_step_blocks -- process-wide override for the blocked passes
- * enqueued after the call: blocks = 1 .. 4 forces that width, -1 restores
- * the automatic choice.  Every width gives the same results.  Returns
- * DBS_OK, or DBS_EINVAL for any other value (the setting is then unchanged).
- */
 int dbs_step_blocks(int64_t n, int64_t batch);
-int dbs_set_step_blocks(int blocks);
 
 /* Largest n the LDS algorithm accepts. */
 int dbs_lds_max_n(void);

@@ -54,8 +54,18 @@ def test_static_queries():
     assert L.dbs_strerror(12345) == b"unknown status"
 
 
-# host-side argument validation: fake, never dereferenced addresses
+# host-side argument validation: fake, never dereferenced addresses.  These
+# cases run only where no GPU is visible: with a GPU, a regression in the
+# order of the checks could launch a kernel on them.
 A, B = 0x10000000, 0x20000000
+
+
+@pytest.fixture
+def no_gpu():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("fake device addresses are only passed where no GPU is visible")
 
 
 @pytest.mark.parametrize("args", [
@@ -63,30 +73,59 @@ A, B = 0x10000000, 0x20000000
     (A, B, 1 << 31, 1), (A, A + (1 << 55), 1 << 26, 1),  # 2^26: the size limit alone
     (A, B, 1 << 20, 1 << 40), (A, A + 32, 4, 1), (A + 2, B, 4, 1),
 ])
-def test_smooth_rejects_bad_arguments(args):
+def test_smooth_rejects_bad_arguments(args, no_gpu):
     L = dgb.lib()
     assert L.dbs_smooth(*args, None) == _lib.DBS_EINVAL
     assert L.dbs_smooth_algo(*args, None, 0) == _lib.DBS_EINVAL
 
 
-def test_rounds_and_algo_range_checks():
+def test_rounds_and_algo_range_checks(no_gpu):
     L = dgb.lib()
     assert L.dbs_rounds(A, B, 8, 1, 5, 4, None) == _lib.DBS_EINVAL
     assert L.dbs_rounds(A, B, 8, 1, -1, 4, None) == _lib.DBS_EINVAL
     assert L.dbs_rounds(A, B, 8, 1, 0, 9, None) == _lib.DBS_EINVAL
     assert L.dbs_smooth_algo(A, B, 8, 1, None, 7) == _lib.DBS_EINVAL
     assert L.dbs_smooth_algo(A, B, 1000, 1, None, _lib.ALGO_LDS) == _lib.DBS_EUNSUPPORTED
-    assert L.dbs_check(A, B, 8, 1, None, None) == _lib.DBS_EINVAL
+    assert L.dbs_check(A, B, 8, 1, None, None) == _lib.DBS_EINVAL     # null d_flags
+    assert L.dbs_check(A, B, 0, 1, None, A + 64) == _lib.DBS_EINVAL
+    assert L.dbs_check_packed(A, 8, 1, None, None) == _lib.DBS_EINVAL
 
 
-def test_no_device_is_reported():
-    import torch
+def test_options_are_validated_on_the_host(no_gpu):
+    L = dgb.lib()
+    byref = ctypes.byref
+    good = _lib.Options(0, 0, -1, -1)
+    d = _lib.Options(9, 9, 9, 9)
+    L.dbs_options_init(byref(d))
+    assert (d.algo, d.directed, d.lookahead, d.step_blocks) == (0, 0, -1, -1)
+    for bad in (_lib.Options(4, 0, -1, -1), _lib.Options(-1, 0, -1, -1),
+                _lib.Options(0, 2, -1, -1), _lib.Options(0, 0, 3, -1),
+                _lib.Options(0, 0, -2, -1), _lib.Options(0, 0, -1, 0),
+                _lib.Options(0, 0, -1, 5)):
+        assert L.dbs_smooth_opts(A, B, 8, 1, 0, 8, None, byref(bad)) == _lib.DBS_EINVAL
+        assert L.dbs_smooth_packed_opts(A, 8, 1, 0, 8, None, byref(bad)) == _lib.DBS_EINVAL
+        assert L.dbs_schedule(8, 1, byref(bad), None, None) == _lib.DBS_EINVAL
+    # blocked ranges must start and end on k-block boundaries
+    blk = _lib.Options(_lib.ALGO_BLOCKED, 0, -1, -1)
+    assert L.dbs_smooth_opts(A, B, 300, 1, 0, 100, None, byref(blk)) == _lib.DBS_EUNSUPPORTED
+    assert L.dbs_smooth_packed_opts(A, 300, 1, 64, 100, None, byref(blk)) == \
+        _lib.DBS_EUNSUPPORTED
+    lds = _lib.Options(_lib.ALGO_LDS, 0, -1, -1)
+    assert L.dbs_smooth_packed_opts(A, 300, 1, 0, 300, None, byref(lds)) == \
+        _lib.DBS_EUNSUPPORTED
+    assert L.dbs_smooth_opts(A, B, 8, 1, 5, 4, None, byref(good)) == _lib.DBS_EINVAL
+    assert L.dbs_smooth_opts(A, A + 16, 8, 1, 0, 8, None, byref(good)) == _lib.DBS_EINVAL
+    counts = (ctypes.c_int64 * len(_lib.PROF_KINDS))()
+    ms = (ctypes.c_double * len(_lib.PROF_KINDS))()
+    assert L.dbs_smooth_profiled(A, B, 8, 1, None, byref(good), None, ms) == _lib.DBS_EINVAL
+    assert L.dbs_smooth_profiled(A, B, 8, 1, None, byref(d), counts, None) == _lib.DBS_EINVAL
 
-    if torch.cuda.is_available():
-        pytest.skip("a GPU is present")
+
+def test_no_device_is_reported(no_gpu):
     L = dgb.lib()
     assert L.dbs_smooth(A, B, 8, 1, None) == _lib.DBS_EDEVICE
     assert L.dbs_rounds(A, B, 8, 1, 0, 1, None) == _lib.DBS_EDEVICE
+    assert L.dbs_smooth_opts(A, B, 8, 1, 0, 8, None, None) == _lib.DBS_EDEVICE
 
 
 def test_python_wrapper_rejects_cpu_tensors():
@@ -131,40 +170,33 @@ def test_lookahead_bands_query():
     assert dgb.lookahead_bands(12288) == 2
 
 
-def test_set_lookahead_overrides_the_choice():
-    lib = dgb.lib()
-    dgb.set_lookahead(2)
-    try:
-        assert dgb.lookahead_bands(200) == 2 and dgb.lookahead_bands(4096) == 2
-        assert dgb.lookahead_bands(64) == 0 and dgb.lookahead_bands(128, 3) == 0  # nothing to run ahead
-        dgb.set_lookahead(0)
-        assert dgb.lookahead_bands(12288) == 0
-        assert lib.dbs_set_lookahead(3) == -1 and lib.dbs_set_lookahead(-2) == -1  # DBS_EINVAL
-        assert dgb.lookahead_bands(12288) == 0                                     # unchanged
+def test_schedule_query_with_forced_values():
+    # a forced depth or width applies to that call's options only; the
+    # library keeps no setting between calls
+    assert dgb.schedule(200, lookahead=2) == (2, 2)
+    assert dgb.schedule(4096, lookahead=2)[0] == 2
+    assert dgb.schedule(64, lookahead=2)[0] == 0 and dgb.schedule(128, 3, lookahead=2)[0] == 0
+    assert dgb.schedule(12288, lookahead=0) == (0, 1)
+    assert dgb.schedule(12288) == (2, 4) and dgb.schedule(200) == (0, 1)
+    assert dgb.schedule(200, step_blocks=4) == (0, 4)
+    assert dgb.schedule(12288, lookahead=1, step_blocks=3) == (1, 3)
+    for la, sb in ((3, None), (-2, None), (None, 0), (None, 5)):
         with pytest.raises(ValueError):
-            dgb.set_lookahead(7)
-    finally:
-        dgb.set_lookahead(-1)
-    assert dgb.lookahead_bands(12288) == 2 and dgb.lookahead_bands(200) == 0
+            dgb.schedule(12288, lookahead=la, step_blocks=sb)
+    lib = dgb.lib()
+    la, sb = ctypes.c_int32(7), ctypes.c_int32(7)
+    assert lib.dbs_schedule(12288, 1, None, ctypes.byref(la), ctypes.byref(sb)) == 0
+    assert (la.value, sb.value) == (2, 4)
+    assert lib.dbs_schedule(0, 1, None, None, None) == -1
+    assert lib.dbs_schedule(5, 0, None, None, None) == -1
+    assert lib.dbs_schedule(5, 1, None, None, None) == 0
 
 
-def test_step_blocks_query_and_override():
-    # steps of two k-blocks where the pass runs two steps ahead, else one;
-    # the override forces a width for every shape, -1 restores the choice
+def test_step_blocks_query():
+    # steps of several k-blocks where the pass runs two steps ahead, else one
     lib = dgb.lib()
     assert dgb.step_blocks(12288) == 4 and dgb.step_blocks(10240) == 4   # 4656, 3240 tiles
     assert dgb.step_blocks(8192) == 3 and dgb.step_blocks(6144, 2) == 3  # 2080, 2352
     assert dgb.step_blocks(5632) == 1 and dgb.step_blocks(6144) == 2     # 990, 1176
     assert dgb.step_blocks(4096) == 1 and dgb.step_blocks(200) == 1
     assert lib.dbs_step_blocks(0, 1) == -1 and lib.dbs_step_blocks(5, 0) == -1
-    try:
-        dgb.set_step_blocks(4)
-        assert dgb.step_blocks(200) == 4 and dgb.step_blocks(12288) == 4
-        assert lib.dbs_set_step_blocks(0) == -1 and lib.dbs_set_step_blocks(5) == -1
-        assert lib.dbs_set_step_blocks(-2) == -1
-        assert dgb.step_blocks(12288) == 4                                         # unchanged
-        with pytest.raises(ValueError):
-            dgb.set_step_blocks(9)
-    finally:
-        dgb.set_step_blocks(-1)
-    assert dgb.step_blocks(12288) == 4 and dgb.step_blocks(4096) == 1

@@ -162,18 +162,12 @@ def test_directed_steps_within_rounding_bound(n, batch, bands, blocks):
     # path sum still takes at most n - 2 roundings, so the same bound holds
     U0, L0 = unquantised(n, batch, seed=3 * n + blocks)
     Ue, Le = oracle.smooth_directed(U0, L0)
-    dgb.set_lookahead(bands)
-    dgb.set_step_blocks(blocks)
-    try:
-        U, L = dev(U0), dev(L0)
-        dgb.smooth_directed(U, L, algo="blocked")
-        Ug, Lg = host(U), host(L)
-        P = dgb.pack(dev(U0), dev(L0))
-        dgb.smooth_packed_directed(P)
-        Pg = host(P)
-    finally:
-        dgb.set_lookahead(-1)
-        dgb.set_step_blocks(-1)
+    U, L = dev(U0), dev(L0)
+    dgb.smooth_directed(U, L, algo="blocked", lookahead=bands, step_blocks=blocks)
+    Ug, Lg = host(U), host(L)
+    P = dgb.pack(dev(U0), dev(L0))
+    dgb.smooth_packed_directed(P, lookahead=bands, step_blocks=blocks)
+    Pg = host(P)
     assert within_bound(Ug, Lg, Ue, Le, L0)
     assert np.all(Lg <= Ug)
     assert bits_equal(Pg, steps.pack(Ug, Lg))

@@ -27,37 +27,39 @@ def test_captured_pass_replays_match_oracle(n, batch, bands, blocks):
     Ui = torch.from_numpy(U0).to(DEV)
     Li = torch.from_numpy(L0).to(DEV)
     U, L = torch.empty_like(Ui), torch.empty_like(Li)
-    dgb.set_lookahead(bands)
-    dgb.set_step_blocks(blocks)
-    try:
-        s = torch.cuda.Stream(DEV)
-        s.wait_stream(torch.cuda.current_stream(DEV))
-        with torch.cuda.stream(s):               # warm-up on the capture stream
-            U.copy_(Ui)
-            L.copy_(Li)
-            dgb.smooth(U, L, algo="blocked")
-        torch.cuda.current_stream(DEV).wait_stream(s)
+    kw = dict(algo="blocked", lookahead=None if bands < 0 else bands,
+              step_blocks=None if blocks < 0 else blocks)
+    s = torch.cuda.Stream(DEV)
+    s.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(s):               # warm-up on the capture stream
+        U.copy_(Ui)
+        L.copy_(Li)
+        dgb.smooth(U, L, **kw)
+    torch.cuda.current_stream(DEV).wait_stream(s)
+    torch.cuda.synchronize(DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        U.copy_(Ui)
+        L.copy_(Li)
+        dgb.smooth(U, L, **kw)
+    torch.cuda.synchronize(DEV)
+    for rep in range(3):
+        U.fill_(-1.0)
+        L.fill_(-1.0)
+        g.replay()
         torch.cuda.synchronize(DEV)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            U.copy_(Ui)
-            L.copy_(Li)
-            dgb.smooth(U, L, algo="blocked")
+        tag = f"n={n} batch={batch} bands={bands} blocks={blocks} replay {rep}"
+        assert np.array_equal(U.cpu().numpy().view(np.uint32), Ue.view(np.uint32)), tag
+        assert np.array_equal(L.cpu().numpy().view(np.uint32), Le.view(np.uint32)), tag
+        # eager work between replays, on the same buffers and on the
+        # capture stream, whose library stream is part of the graph
+        U.copy_(Ui)
+        L.copy_(Li)
+        dgb.smooth(U, L, **kw)
+        with torch.cuda.stream(s):
+            U2, L2 = Ui.clone(), Li.clone()
+            dgb.smooth(U2, L2, **kw)
         torch.cuda.synchronize(DEV)
-        for rep in range(3):
-            U.fill_(-1.0)
-            L.fill_(-1.0)
-            g.replay()
-            torch.cuda.synchronize(DEV)
-            tag = f"n={n} batch={batch} bands={bands} blocks={blocks} replay {rep}"
-            assert np.array_equal(U.cpu().numpy().view(np.uint32), Ue.view(np.uint32)), tag
-            assert np.array_equal(L.cpu().numpy().view(np.uint32), Le.view(np.uint32)), tag
-            # eager work between replays, on the same buffers
-            U.copy_(Ui)
-            L.copy_(Li)
-            dgb.smooth(U, L, algo="blocked")
-            torch.cuda.synchronize(DEV)
-        del g
-    finally:
-        dgb.set_lookahead(-1)
-        dgb.set_step_blocks(-1)
+        assert np.array_equal(U2.cpu().numpy().view(np.uint32), Ue.view(np.uint32)), tag
+        assert np.array_equal(L2.cpu().numpy().view(np.uint32), Le.view(np.uint32)), tag
+    del g

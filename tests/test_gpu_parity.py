@@ -45,9 +45,9 @@ def assert_bits(Ug, Lg, Ue, Le, tag):
                              f"L {Le.ravel()[first]})")
 
 
-def gpu_pass(U0, L0, algo):
+def gpu_pass(U0, L0, algo, **kw):
     U, L = dev(U0), dev(L0)
-    dgb.smooth(U, L, algo=algo)
+    dgb.smooth(U, L, algo=algo, **kw)
     return host(U), host(L)
 
 
@@ -107,16 +107,9 @@ def test_full_pass_multi_tile(n):
         assert_bits(Ug, Lg, Ue, Le, f"{algo} n={n}")
 
 
-@pytest.fixture
-def restore_lookahead():
-    yield
-    dgb.set_lookahead(-1)
-    dgb.set_step_blocks(-1)
-
-
 @pytest.mark.parametrize("bands", [0, 1, 2])
 @pytest.mark.parametrize("n,batch", [(129, 2), (300, 1), (385, 2), (700, 1)])
-def test_every_lookahead_depth(n, batch, bands, restore_lookahead):
+def test_every_lookahead_depth(n, batch, bands):
     # the automatic choice runs these sizes without a second stream; forcing
     # each depth covers the one- and two-step schedules (steps of one and of
     # two k-blocks) at small sizes, on the dense, directed and packed passes
@@ -124,56 +117,55 @@ def test_every_lookahead_depth(n, batch, bands, restore_lookahead):
     from oracle import steps
     U0, L0 = sound_input(n, batch, seed=31 * n + bands)
     Ue, Le = oracle.smooth(U0, L0)
-    dgb.set_lookahead(bands)
-    assert dgb.lookahead_bands(n, batch) == bands
-    Ug, Lg = gpu_pass(U0, L0, "blocked")
+    assert dgb.schedule(n, batch, lookahead=bands)[0] == bands
+    kw = dict(algo="blocked", lookahead=bands)
+    Ug, Lg = gpu_pass(U0, L0, **kw)
     assert_bits(Ug, Lg, Ue, Le, f"blocked n={n} batch={batch} bands={bands}")
     U, L = dev(U0), dev(L0)
-    dgb.smooth_directed(U, L, algo="blocked")
+    dgb.smooth_directed(U, L, **kw)
     assert_bits(host(U), host(L), Ue, Le, f"directed n={n} bands={bands}")
     P = dgb.pack(dev(U0), dev(L0))
-    dgb.smooth_packed(P)
+    dgb.smooth_packed(P, **kw)
     assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32))
     U, L = dev(U0), dev(L0)
     Ur, Lr = oracle.rounds(U0, L0, 0, 128)
-    dgb.smooth_range(U, L, 0, 128, algo="blocked")
+    dgb.smooth_range(U, L, 0, 128, **kw)
     assert_bits(host(U), host(L), Ur, Lr, f"range 0..128 n={n} bands={bands}")
-    dgb.smooth_range(U, L, 128, n, algo="blocked")
+    dgb.smooth_range(U, L, 128, n, **kw)
     assert_bits(host(U), host(L), Ue, Le, f"range 128..n n={n} bands={bands}")
     # ranges that start at an odd k-block (two steps ahead pairs the blocks
     # from the range's first one, so the pairs fall differently)
     U, L = dev(U0), dev(L0)
     cuts = sorted({0, 64, min(n, 320), n})
     for a, b in zip(cuts[:-1], cuts[1:]):
-        dgb.smooth_range(U, L, a, b, algo="blocked")
+        dgb.smooth_range(U, L, a, b, **kw)
     assert_bits(host(U), host(L), Ue, Le, f"ranges 0,64,320,n n={n} bands={bands}")
 
 
 @pytest.mark.parametrize("blocks", [1, 2, 3, 4])
 @pytest.mark.parametrize("bands", [0, 1, 2])
 @pytest.mark.parametrize("n,batch", [(385, 2), (700, 1)])
-def test_every_step_width(n, batch, bands, blocks, restore_lookahead):
+def test_every_step_width(n, batch, bands, blocks):
     # steps of 1..4 k-blocks (the pass picks 1 or 2) at every look-ahead
     # depth, on the dense, directed and packed passes and on ranges that
     # start inside a step
     from oracle import steps
     U0, L0 = sound_input(n, batch, seed=97 * n + 7 * bands + blocks)
     Ue, Le = oracle.smooth(U0, L0)
-    dgb.set_lookahead(bands)
-    dgb.set_step_blocks(blocks)
-    assert dgb.step_blocks(n, batch) == blocks
+    assert dgb.schedule(n, batch, lookahead=bands, step_blocks=blocks)[1] == blocks
+    kw = dict(algo="blocked", lookahead=bands, step_blocks=blocks)
     tag = f"n={n} batch={batch} bands={bands} blocks={blocks}"
-    Ug, Lg = gpu_pass(U0, L0, "blocked")
+    Ug, Lg = gpu_pass(U0, L0, **kw)
     assert_bits(Ug, Lg, Ue, Le, "blocked " + tag)
     U, L = dev(U0), dev(L0)
-    dgb.smooth_directed(U, L, algo="blocked")
+    dgb.smooth_directed(U, L, **kw)
     assert_bits(host(U), host(L), Ue, Le, "directed " + tag)
     P = dgb.pack(dev(U0), dev(L0))
-    dgb.smooth_packed(P)
+    dgb.smooth_packed(P, **kw)
     assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
     U, L = dev(U0), dev(L0)
     for a, b in ((0, 192), (192, n)):
-        dgb.smooth_range(U, L, a, b, algo="blocked")
+        dgb.smooth_range(U, L, a, b, **kw)
     assert_bits(host(U), host(L), Ue, Le, "ranges 0,192,n " + tag)
 
 
@@ -294,15 +286,9 @@ def test_n12288_schedule_independent():
     # matrix, and the packed pass against the packed form of that result
     W, U, L = big()
     assert dgb.lookahead_bands(W.n) == 2 and dgb.step_blocks(W.n) == 4
-    try:
-        dgb.set_lookahead(0)
-        dgb.set_step_blocks(1)
-        U1, L1 = dev(W.U[0]), dev(W.L[0])
-        dgb.smooth(U1, L1, algo="blocked")
-        torch.cuda.synchronize(DEV)
-    finally:
-        dgb.set_lookahead(-1)
-        dgb.set_step_blocks(-1)
+    U1, L1 = dev(W.U[0]), dev(W.L[0])
+    dgb.smooth(U1, L1, algo="blocked", lookahead=0, step_blocks=1)
+    torch.cuda.synchronize(DEV)
     assert torch.equal(U1.view(torch.int32), U.view(torch.int32))
     assert torch.equal(L1.view(torch.int32), L.view(torch.int32))
     del U1, L1
@@ -408,3 +394,64 @@ def test_single_round_entry_and_smooth_check_option():
     Ub[0, 1, 2] = Ub[0, 2, 1] = Ub[0, 1, 2] + 0.001   # off the grid
     with pytest.raises(ValueError, match="unquant"):
         dgb.smooth(dev(Ub), dev(L0), check=True)
+
+
+# -------------------------------------------------------------- caller streams
+def _expected_pair(n, batch, seed):
+    U0, L0 = sound_input(n, batch, seed=seed)
+    return U0, L0, *oracle.smooth(U0, L0)
+
+
+@pytest.mark.parametrize("kw", [dict(lookahead=2, step_blocks=2), dict(lookahead=1),
+                                dict()])
+def test_passes_on_two_caller_streams(kw):
+    # two passes in flight at once on two caller streams, each with the
+    # library's second stream of its own (forced look-ahead at these sizes;
+    # the last case is (130, 129), a batch split over the two streams)
+    cases = [(700, 1, 71), (385, 2, 72)] if kw else [(130, 129, 73), (200, 87, 74)]
+    data = [_expected_pair(*c) for c in cases]
+    streams = [torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)]
+    out = []
+    for (U0, L0, _, _), s in zip(data, streams):
+        s.wait_stream(torch.cuda.current_stream(DEV))
+        with torch.cuda.stream(s):
+            U, L = dev(U0), dev(L0)
+            for _ in range(2):                 # the second pass changes nothing
+                dgb.smooth(U, L, algo="blocked", **kw)
+        out.append((U, L))
+    for (U, L), (_, _, Ue, Le), c in zip(out, data, cases):
+        assert_bits(host(U), host(L), Ue, Le, f"stream pass {c} {kw}")
+
+
+def test_passes_from_two_host_threads():
+    # host threads enqueue passes concurrently, each on its own stream, and
+    # also both on one shared stream (the library serialises the enqueue of
+    # the passes that share its second stream)
+    import threading
+    cases = [(700, 1, 81), (640, 1, 82), (385, 2, 83), (520, 1, 84)]
+    data = [_expected_pair(*c) for c in cases]
+    shared = torch.cuda.Stream(DEV)
+    own = [torch.cuda.Stream(DEV) for _ in cases]
+    results, errors = [None] * len(cases), []
+
+    def work(i):
+        try:
+            U0, L0, _, _ = data[i]
+            s = shared if i % 2 else own[i]
+            with torch.cuda.stream(s):
+                U, L = dev(U0), dev(L0)
+                for _ in range(3):
+                    dgb.smooth(U, L, algo="blocked", lookahead=2, step_blocks=1 + i % 3)
+                s.synchronize()
+                results[i] = (U.cpu().numpy(), L.cpu().numpy())
+        except Exception as e:  # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for (Ug, Lg), (_, _, Ue, Le), c in zip(results, data, cases):
+        assert_bits(Ug, Lg, Ue, Le, f"thread pass {c}")

@@ -1,7 +1,7 @@
 """Seeded random sweep of shapes and options against the CPU oracle (needs an MI355X).
 
-Each case draws n (including k-block and tile tails), a batch, an algorithm, the layout (dense
-or packed), the rounding entry point (plain or directed; on grid inputs both must give the plain
+Each case draws n (including k-block and tile tails), a batch, an algorithm (on either layout),
+the layout (dense or packed), the rounding entry point (plain or directed; on grid inputs both must give the plain
 pass's bits), a look-ahead depth (automatic or forced 0, 1, 2) and a step width (automatic or
 forced 1..4 k-blocks). It runs one full pass, or a
 pass split at a k-block boundary, and compares every entry with the oracle bit for bit. The draws
@@ -35,28 +35,24 @@ def _case(seed):
 
 
 def _run(U0, L0, n, algo, packed, directed, depth, split, blocks):
-    dgb.set_lookahead(depth)
-    dgb.set_step_blocks(blocks)
-    try:
-        cuts = [0, 128, n] if split else [0, n]
-        if packed:
-            P = dgb.pack(torch.from_numpy(U0).to(DEV), torch.from_numpy(L0).to(DEV))
-            for a, b in zip(cuts[:-1], cuts[1:]):
-                (dgb.smooth_packed_directed if directed else dgb.smooth_packed)(P, a, b)
-            torch.cuda.synchronize(DEV)
-            return P.cpu().numpy(), None
-        U = torch.from_numpy(U0).to(DEV)
-        L = torch.from_numpy(L0).to(DEV)
+    kw = dict(algo=algo, lookahead=None if depth < 0 else depth,
+              step_blocks=None if blocks < 0 else blocks)
+    cuts = [0, 128, n] if split else [0, n]
+    if packed:
+        P = dgb.pack(torch.from_numpy(U0).to(DEV), torch.from_numpy(L0).to(DEV))
         for a, b in zip(cuts[:-1], cuts[1:]):
-            if directed:
-                dgb.smooth_directed_range(U, L, a, b, algo=algo)
-            else:
-                dgb.smooth_range(U, L, a, b, algo=algo)
+            (dgb.smooth_packed_directed if directed else dgb.smooth_packed)(P, a, b, **kw)
         torch.cuda.synchronize(DEV)
-        return U.cpu().numpy(), L.cpu().numpy()
-    finally:
-        dgb.set_lookahead(-1)
-        dgb.set_step_blocks(-1)
+        return P.cpu().numpy(), None
+    U = torch.from_numpy(U0).to(DEV)
+    L = torch.from_numpy(L0).to(DEV)
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        if directed:
+            dgb.smooth_directed_range(U, L, a, b, **kw)
+        else:
+            dgb.smooth_range(U, L, a, b, **kw)
+    torch.cuda.synchronize(DEV)
+    return U.cpu().numpy(), L.cpu().numpy()
 
 
 @pytest.mark.parametrize("seed", range(64))
