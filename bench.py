@@ -8,13 +8,18 @@ dbs_smooth.  The default workload is n = 12288: 48 self-avoiding chains of
 
 Printed: one JSON line with
   value        bound-updates/s = 2 n^3 batch / (seconds per step)
-  pct_fp32_valu_peak  = 6 n^3 batch / t / 157.3e12 (3 ops per bound-update)
+  executed_frac_of_fp32_peak  the operations the symmetric schedule
+               executes (6 per (i,j,k) triple of the cells it keeps current)
+               / t / 157.3e12, the MI355X fp32 vector peak
+  dense_equivalent_frac_of_fp32_peak  = 6 n^3 batch / t / 157.3e12: the
+               metric's dense count, about twice the executed work, so it can
+               exceed 1
   roofline     the bulk phase-3 kernel (k_quads on 64x64 quadrants):
-               algorithmic ops of the cells a launch stores / mean launch
-               time from HIP events (dbs_smooth_profiled on the launch stream),
-               against the issue ceiling of its fp32 add/sub/min/max mix
-               (92 T op/s on gfx950; the 157.3 T fp32 vector peak counts
-               FMAs, which this path has none of)
+               executed ops of the cells a launch stores / mean launch time
+               from HIP events (dbs_smooth_profiled on the launch stream),
+               against the 157.3 T fp32 vector peak
+  all_configs  the four smaller workloads: median GPU pass time, executed
+               fraction of peak, and the oracle's full pass on this host
   perk         the per-round kernel: HBM bytes of the round formulation
                (16 B per cell per round) / mean round time
   restraints   the workload's restraint list to dense bounds (fill + scatter)
@@ -41,11 +46,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "bound-updates/s (2·n³ per pass) + % fp32 VALU peak; HBM GB/s per-k kernel"
 FP32_VALU_PEAK = 157.3e12       # MI355X fp32 vector, ops/s (an FMA counted as 2)
-# Issue ceiling of phase 3's own instruction mix (add/sub at 32 lanes/clk per
-# SIMD, min/max at 16, partly overlapped): 256 CUs x 4 SIMDs x 37.4 op-lanes/clk
-# x 2.4 GHz, measured register-only by probe/valu_rates
-# (profiles/valu_issue_rates_gfx950.md).
-MIX_PEAK = 92.0e12
 HBM_PEAK = 8.0e12               # MI355X HBM3E, bytes/s
 OPS_PER_TRIPLE = 6              # 1 add + 1 min (upper), 2 sub + 2 max (lower)
 TILE, BK = 128, 64              # blocked-path geometry (csrc/blocked.hip)
@@ -73,6 +73,8 @@ def parse():
                     help="skip timing the restraint-to-bounds and tightened-mask steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy 5 times (counter scale)")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the sweep over the smaller workloads")
     return ap.parse_args()
 
 
@@ -116,6 +118,16 @@ def tiles_units_per_pass(n, batch, ahead, W):
     return stored * batch, dense * batch
 
 
+def executed_triples(n, batch):
+    """(i,j,k) triples the symmetric schedule executes in one pass: every
+    cell of the TILE x TILE tiles with I <= J, for every atom k (phases 1-2
+    repeat the diagonal tile's rounds per panel workgroup; those repeats are
+    not counted)."""
+    T = -(-n // TILE)
+    rows = [min(n, (I + 1) * TILE) - I * TILE for I in range(T)]
+    return (n * n + sum(r * r for r in rows)) // 2 * n * batch
+
+
 def source_digest(path):
     """sha256 of a C++ source with its // comments and all whitespace removed,
     so that the counter record stays valid across edits of comments only."""
@@ -150,7 +162,6 @@ def valu_counters(n, batch):
         return None
     return {"valu_lanes_per_clk_per_simd": rec["valu_lanes_per_clk_per_simd"],
             "clock_ghz": rec["clock_ghz"],
-            "mix_lanes_per_clk_4_waves": rec["mix_lanes_per_clk_4_waves"],
             "sq_insts_valu_per_launch": rec["sq_insts_valu_per_launch"],
             "modelled_insts_per_launch": rec["modelled_insts_per_launch"]}
 
@@ -233,7 +244,10 @@ def packed_pass(U0, L0, dev, reps=2):
     triples = float(n) ** 3 * batch
     cells = n * n * batch
     return {"pass_ms": ms[1], "value": 2.0 * triples / (ms[1] * 1e-3),
-            "pct_fp32_valu_peak": OPS_PER_TRIPLE * triples / (ms[1] * 1e-3) / FP32_VALU_PEAK,
+            "executed_frac_of_fp32_peak": OPS_PER_TRIPLE * executed_triples(n, batch)
+            / (ms[1] * 1e-3) / FP32_VALU_PEAK,
+            "dense_equivalent_frac_of_fp32_peak": OPS_PER_TRIPLE * triples / (ms[1] * 1e-3)
+            / FP32_VALU_PEAK,
             "pack_ms": ms[0], "pack_GBps": 12.0 * cells / (ms[0] * 1e-3) / 1e9,
             "unpack_ms": ms[2], "unpack_GBps": 16.0 * cells / (ms[2] * 1e-3) / 1e9,
             "bytes": 4 * cells}
@@ -263,7 +277,10 @@ def directed_pass(U, L, U0, L0, dev, reps=2):
     n, batch = U0.shape[-1], U0.numel() // (U0.shape[-1] ** 2)
     triples = float(n) ** 3 * batch
     return {"pass_ms": ms, "value": 2.0 * triples / (ms * 1e-3),
-            "pct_fp32_valu_peak": OPS_PER_TRIPLE * triples / (ms * 1e-3) / FP32_VALU_PEAK}
+            "executed_frac_of_fp32_peak": OPS_PER_TRIPLE * executed_triples(n, batch)
+            / (ms * 1e-3) / FP32_VALU_PEAK,
+            "dense_equivalent_frac_of_fp32_peak": OPS_PER_TRIPLE * triples / (ms * 1e-3)
+            / FP32_VALU_PEAK}
 
 
 def cpu_baseline(W, target_s):
@@ -301,6 +318,59 @@ def cpu_baseline(W, target_s):
             "sample": f"rounds 0..{rounds - 1} of the {W.name} pass on molecule 0 "
                       f"({rounds} of {W.n} rounds, {t:.1f} s)",
             "seconds": t}
+
+
+def config_sweep(names, dev, reps=15, oracle_on=True):
+    """Each workload in `names`: the median device time of one full pass
+    (HIP events on the launch stream, the input restored outside them), its
+    executed fraction of the fp32 peak, and the oracle's full pass on this
+    host's cores (wall time, one run)."""
+    import numpy as np
+    import torch
+
+    import distance_geometry_bound_amd as dgb
+    from distance_geometry_bound_amd import gen
+
+    res = {}
+    s = torch.cuda.current_stream(dev)
+    for name in names:
+        W = gen.make_workload(name)
+        n, batch = W.n, W.batch
+        U0 = torch.from_numpy(W.U).to(dev)
+        L0 = torch.from_numpy(W.L).to(dev)
+        U, L = torch.empty_like(U0), torch.empty_like(L0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        times = []
+        for r in range(reps + 2):
+            U.copy_(U0)
+            L.copy_(L0)
+            ev[0].record(s)
+            dgb.smooth(U, L)
+            ev[1].record(s)
+            torch.cuda.synchronize(dev)
+            if r >= 2:
+                times.append(ev[0].elapsed_time(ev[1]))
+        ms = float(np.median(times))
+        triples = float(n) ** 3 * batch
+        entry = {"n": n, "batch": batch, "algo": dgb.auto_algo(n, batch),
+                 "lookahead_bands": dgb.lookahead_bands(n, batch),
+                 "pass_ms_median": ms, "pass_ms_min": float(min(times)), "reps": reps,
+                 "value": 2.0 * triples / (ms * 1e-3),
+                 "executed_frac_of_fp32_peak": OPS_PER_TRIPLE * executed_triples(n, batch)
+                 / (ms * 1e-3) / FP32_VALU_PEAK}
+        if oracle_on:
+            import oracle
+            t0 = time.perf_counter()
+            oracle.smooth(W.U, W.L)
+            t = time.perf_counter() - t0
+            entry["oracle_full_pass_s"] = t
+            entry["oracle_value"] = 2.0 * triples / t
+            entry["oracle_cores"] = oracle.max_threads()
+            entry["gpu_over_oracle"] = t / (ms * 1e-3)
+        res[name] = entry
+        print(f"[bench] {name}: {ms:.3f} ms per pass", file=sys.stderr, flush=True)
+        del U0, L0, U, L
+    return res
 
 
 def main():
@@ -361,7 +431,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": W.name, "n": n, "batch": batch, "algo": algo,
                    "step": "restore U,L (device copy) + one full pass"},
-        "pct_fp32_valu_peak": OPS_PER_TRIPLE * triples / dt / FP32_VALU_PEAK,
+        "executed_frac_of_fp32_peak": OPS_PER_TRIPLE * executed_triples(n, batch) / dt
+        / FP32_VALU_PEAK,
+        "dense_equivalent_frac_of_fp32_peak": OPS_PER_TRIPLE * triples / dt / FP32_VALU_PEAK,
     }
 
     # per-kernel device times from HIP events around every launch of a pass
@@ -385,20 +457,24 @@ def main():
         ops = OPS_PER_TRIPLE * stored / launches          # per launch, averaged over the pass
         achieved = ops / (launch_ms * 1e-3)
         traffic = counters_traffic(n, batch)
+        # algorithmic HBM bytes of a launch: read and write U and L of every
+        # stored cell once (16 B), and read the step's panel rows once
+        atoms = min(n, width * BK)
+        alg_bytes = 16.0 * stored / launches / atoms + 8.0 * atoms * n * batch
         out["roofline"] = {
             "bound": "alu", "kernel": "k_quads (dense bulk of phase 3)",
-            "achieved": achieved / 1e12, "peak": MIX_PEAK / 1e12, "unit": "TFLOP/s",
-            "frac": achieved / MIX_PEAK,
-            "peak_basis": "issue ceiling of the kernel's fp32 add/sub/min/max mix on gfx950 "
-                          "(256 CUs x 4 SIMDs x 37.4 op-lanes/clk x 2.4 GHz)",
-            "frac_of_fp32_vector_peak": achieved / FP32_VALU_PEAK,
+            "achieved": achieved / 1e12, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
+            "frac": achieved / FP32_VALU_PEAK,
+            "peak_basis": "MI355X fp32 vector peak; achieved counts the 6 fp32 add/sub/min/max "
+                          "operations per (i,j,k) triple of the cells a launch stores",
             "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes,
             "launch_ms": launch_ms, "launches": tot["tiles"][0], "lookahead_bands": ahead,
             "step_blocks": width,
             "ops_per_launch": ops,
             "issue_counters": valu_counters(n, batch),
-            "frac_effective": OPS_PER_TRIPLE * dense / launches / (launch_ms * 1e-3)
-                              / FP32_VALU_PEAK,
+            "dense_equivalent_frac": OPS_PER_TRIPLE * dense / launches / (launch_ms * 1e-3)
+                                     / FP32_VALU_PEAK,
         }
 
     if args.perk_rounds > 0:
@@ -430,6 +506,11 @@ def main():
     if not args.no_cpu and args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
+
+    if args.configs and W.name == "n12288":
+        del U0, L0, U, L
+        out["all_configs"] = config_sweep(("n128", "n1024", "b64n500", "n4096"), dev,
+                                          oracle_on=not args.no_cpu)
     print(json.dumps(out), flush=True)
 
 

@@ -17,7 +17,6 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 SO = os.path.join(HERE, "libdbs.so")
-PROBE = os.path.join(HERE, "probe")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -50,17 +49,7 @@ def build(verbose: bool = False) -> str:
     tmp = SO + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, SO)
-    build_probe(verbose)
     return SO
-
-
-def build_probe(verbose: bool = False) -> str:
-    """The VALU issue-rate probe (a stand-alone program, not part of the library)."""
-    src = os.path.join(PROBE, "valu_rates.hip")
-    exe = os.path.join(PROBE, "valu_rates")
-    _run([HIPCC, f"--offload-arch={ARCH}", "-O3", src, "-o", exe + ".tmp"], verbose)
-    os.replace(exe + ".tmp", exe)
-    return exe
 
 
 if __name__ == "__main__":
