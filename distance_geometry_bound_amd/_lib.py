@@ -38,7 +38,8 @@ AUTO = -1
 class Options(ctypes.Structure):
     """struct dbs_options (include/dbs.h): per-call options of a pass."""
     _fields_ = [("algo", ctypes.c_int32), ("directed", ctypes.c_int32),
-                ("lookahead", ctypes.c_int32), ("step_blocks", ctypes.c_int32)]
+                ("lookahead", ctypes.c_int32), ("step_blocks", ctypes.c_int32),
+                ("lead", ctypes.c_int32)]
 
 
 RESTRAINT_FLAGS = {"index": 1, "value": 2}
@@ -71,8 +72,8 @@ def lib():
         L.dbs_options_init.restype = None
         L.dbs_smooth_opts.argtypes = [vp, vp, i64, i64, i64, i64, vp, opp]
         L.dbs_smooth_packed_opts.argtypes = [vp, i64, i64, i64, i64, vp, opp]
-        L.dbs_schedule.argtypes = [i64, i64, opp, ctypes.POINTER(ctypes.c_int32),
-                                   ctypes.POINTER(ctypes.c_int32)]
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        L.dbs_schedule.argtypes = [i64, i64, opp, i32p, i32p, i32p]
         L.dbs_smooth_profiled.argtypes = [vp, vp, i64, i64, vp, opp,
                                           ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
         L.dbs_rounds.argtypes = [vp, vp, i64, i64, i64, i64, vp]
@@ -152,14 +153,17 @@ def _call(T, fn, *args):
         _raise(fn(*args))
 
 
-def options(algo: str = "auto", directed: bool = False, lookahead=None, step_blocks=None):
-    """struct dbs_options for a pass: `lookahead` (0, 1, 2) and `step_blocks`
-    (1 .. 4) force the blocked schedule, None keeps the automatic choice."""
+def options(algo: str = "auto", directed: bool = False, lookahead=None, step_blocks=None,
+            lead=None):
+    """struct dbs_options for a pass: `lookahead` (0, 1, 2), `step_blocks`
+    (1 .. 4) and `lead` (False, True) force the blocked schedule, None keeps
+    the automatic choice."""
     if algo not in _ALGOS:
         raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
     return Options(_ALGOS[algo], 1 if directed else 0,
                    AUTO if lookahead is None else int(lookahead),
-                   AUTO if step_blocks is None else int(step_blocks))
+                   AUTO if step_blocks is None else int(step_blocks),
+                   AUTO if lead is None else int(lead))
 
 
 def _pass(U, L, k_begin, k_end, **kw):
@@ -173,14 +177,14 @@ def _pass(U, L, k_begin, k_end, **kw):
 
 
 def smooth(U, L, algo: str = "auto", check: bool = False, lookahead=None,
-           step_blocks=None) -> None:
+           step_blocks=None, lead=None) -> None:
     """One full smoothing pass on U, L in place (enqueued on the current stream).
 
     check=True first tests the preconditions on the device (dbs_check; this
     synchronises) and raises ValueError naming the violated ones.  lookahead
     and step_blocks force the blocked schedule (see options())."""
     n, batch = _shape(U, L)
-    options(algo, False, lookahead, step_blocks)
+    options(algo, False, lookahead, step_blocks, lead)
     if n == 0 or batch == 0:
         return
     if check:
@@ -188,15 +192,15 @@ def smooth(U, L, algo: str = "auto", check: bool = False, lookahead=None,
         if bad:
             names = [k for k, v in CHECK_FLAGS.items() if bad & v]
             raise ValueError(f"bounds violate the preconditions: {', '.join(names)}")
-    _pass(U, L, 0, None, algo=algo, lookahead=lookahead, step_blocks=step_blocks)
+    _pass(U, L, 0, None, algo=algo, lookahead=lookahead, step_blocks=step_blocks, lead=lead)
 
 
 def smooth_profiled(U, L, algo: str = "auto", directed: bool = False, lookahead=None,
-                    step_blocks=None) -> dict:
+                    step_blocks=None, lead=None) -> dict:
     """smooth() with HIP events around every kernel launch; synchronises and
     returns {kind: (launches, total_ms)} for the kernel kinds in PROF_KINDS."""
     n, batch = _shape(U, L)
-    o = options(algo, directed, lookahead, step_blocks)
+    o = options(algo, directed, lookahead, step_blocks, lead)
     counts = (ctypes.c_int64 * len(PROF_KINDS))()
     ms = (ctypes.c_double * len(PROF_KINDS))()
     if n > 0 and batch > 0:
@@ -223,22 +227,25 @@ def smooth_round(U, L, k: int) -> None:
 
 
 def smooth_range(U, L, k_begin: int, k_end: int, algo: str = "auto", lookahead=None,
-                 step_blocks=None) -> None:
+                 step_blocks=None, lead=None) -> None:
     """Rounds k_begin..k_end-1 of a pass, in place (see dbs_smooth_range)."""
-    _pass(U, L, k_begin, k_end, algo=algo, lookahead=lookahead, step_blocks=step_blocks)
+    _pass(U, L, k_begin, k_end, algo=algo, lookahead=lookahead, step_blocks=step_blocks,
+          lead=lead)
 
 
 def smooth_directed_range(U, L, k_begin: int, k_end: int, algo: str = "auto", lookahead=None,
-                          step_blocks=None) -> None:
+                          step_blocks=None, lead=None) -> None:
     """smooth_range with directed rounding: sums of upper bounds rounded up,
     differences of lower bounds rounded down (see dbs_smooth_directed_range)."""
     _pass(U, L, k_begin, k_end, algo=algo, directed=True, lookahead=lookahead,
-          step_blocks=step_blocks)
+          step_blocks=step_blocks, lead=lead)
 
 
-def smooth_directed(U, L, algo: str = "auto", lookahead=None, step_blocks=None) -> None:
+def smooth_directed(U, L, algo: str = "auto", lookahead=None, step_blocks=None,
+                    lead=None) -> None:
     """A full pass with directed rounding, in place."""
-    _pass(U, L, 0, None, algo=algo, directed=True, lookahead=lookahead, step_blocks=step_blocks)
+    _pass(U, L, 0, None, algo=algo, directed=True, lookahead=lookahead, step_blocks=step_blocks,
+          lead=lead)
 
 
 def tightened(U0, L0, U1, L1):
@@ -339,16 +346,17 @@ def _packed_pass(P, k_begin, k_end, **kw):
 
 
 def smooth_packed(P, k_begin: int = 0, k_end=None, algo: str = "auto", lookahead=None,
-                  step_blocks=None) -> None:
+                  step_blocks=None, lead=None) -> None:
     """Rounds k_begin..k_end-1 (default: a full pass) on the packed form, in place."""
-    _packed_pass(P, k_begin, k_end, algo=algo, lookahead=lookahead, step_blocks=step_blocks)
+    _packed_pass(P, k_begin, k_end, algo=algo, lookahead=lookahead, step_blocks=step_blocks,
+                 lead=lead)
 
 
 def smooth_packed_directed(P, k_begin: int = 0, k_end=None, algo: str = "auto", lookahead=None,
-                           step_blocks=None) -> None:
+                           step_blocks=None, lead=None) -> None:
     """smooth_packed with directed rounding, in place."""
     _packed_pass(P, k_begin, k_end, algo=algo, directed=True, lookahead=lookahead,
-                 step_blocks=step_blocks)
+                 step_blocks=step_blocks, lead=lead)
 
 
 def _check_flags(U, L) -> int:
@@ -381,14 +389,15 @@ def check_packed(P) -> int:
     return int(flags.item()) & 0xFFFFFFFF
 
 
-def schedule(n: int, batch: int = 1, lookahead=None, step_blocks=None):
-    """(look-ahead depth, k-blocks per step) of a blocked pass of this shape,
-    with the given forced values (None: automatic); see dbs_schedule."""
-    o = options("auto", False, lookahead, step_blocks)
-    la, sb = ctypes.c_int32(), ctypes.c_int32()
+def schedule(n: int, batch: int = 1, lookahead=None, step_blocks=None, lead=None):
+    """(look-ahead depth, k-blocks per step, lead schedule 0/1) of a blocked
+    pass of this shape, with the given forced values (None: automatic); see
+    dbs_schedule."""
+    o = options("auto", False, lookahead, step_blocks, lead)
+    la, sb, ld = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _raise(lib().dbs_schedule(int(n), int(batch), ctypes.byref(o), ctypes.byref(la),
-                              ctypes.byref(sb)))
-    return int(la.value), int(sb.value)
+                              ctypes.byref(sb), ctypes.byref(ld)))
+    return int(la.value), int(sb.value), int(ld.value)
 
 
 def lookahead_bands(n: int, batch: int = 1) -> int:

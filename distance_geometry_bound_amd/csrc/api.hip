@@ -73,6 +73,7 @@ bool read_options(const dbs_options *o, dbs_options *out) {
   if (o->lookahead < DBS_AUTO || o->lookahead > 2) return false;
   if (o->step_blocks != DBS_AUTO && (o->step_blocks < 1 || o->step_blocks > dbs::kMaxStepBlocks))
     return false;
+  if (o->lead < DBS_AUTO || o->lead > 1) return false;
   *out = *o;
   return true;
 }
@@ -81,6 +82,7 @@ dbs::Sched sched_of(const dbs_options &o) {
   dbs::Sched sc;
   sc.lookahead = o.lookahead;
   sc.step_blocks = o.step_blocks;
+  sc.lead = o.lead;
   return sc;
 }
 
@@ -149,6 +151,7 @@ void dbs_options_init(dbs_options *opts) {
   opts->directed = 0;
   opts->lookahead = DBS_AUTO;
   opts->step_blocks = DBS_AUTO;
+  opts->lead = DBS_AUTO;
 }
 
 int dbs_smooth_opts(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
@@ -319,12 +322,13 @@ int dbs_smooth_packed(float *P, int64_t n, int64_t batch, void *stream) {
 int dbs_lds_max_n(void) { return dbs::kSmallMaxN; }
 
 int dbs_schedule(int64_t n, int64_t batch, const dbs_options *opts, int32_t *lookahead,
-                 int32_t *step_blocks) {
+                 int32_t *step_blocks, int32_t *lead) {
   dbs_options o;
   if (n < 1 || batch < 1 || !read_options(opts, &o)) return DBS_EINVAL;
   const dbs::Sched sc = sched_of(o);
   if (lookahead) *lookahead = dbs::lookahead_bands(n, batch, sc);
   if (step_blocks) *step_blocks = dbs::step_blocks(n, batch, sc);
+  if (lead) *lead = dbs::lead_schedule(n, batch, sc) ? 1 : 0;
   return DBS_OK;
 }
 

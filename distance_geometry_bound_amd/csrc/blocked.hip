@@ -773,80 +773,60 @@ __global__ __launch_bounds__(kThreads) void k_strip(float *__restrict__ U, float
   }
 }
 
-// Bulk of phase 3 for the dense layout: the atoms of k-blocks K .. K+nk-1 in
-// order on every fresh cell outside the bands [X0, X1), as the four BK x BK
-// quadrants of each upper TILE x TILE tile (grid.x = 4 T(T+1)/2, grid.y =
-// molecules).  [X0, X1) starts with the atoms' own bands, whose rows are
-// final, and goes on over the bands updated ahead on the other stream.  A
-// quadrant in any of them is skipped whole (quadrants and bands are both BK
-// wide): it is neither read nor written, and the panel columns of the bands
-// run ahead are not read, since the other stream may be updating exactly
-// those cells while this launch runs.  Thread (ty, tx) owns RT x CT cells (rows a0 + RT*ty + r, columns
-// j0 + CT*tx + q).  The panel rows of band K are staged through LDS, KCH
-// atoms per chunk with the next chunk's loads in flight; the quadrant is
-// written back as row segments.  Larger tiles read fewer staged operand
-// floats per cell but lose occupancy; 4x4 is the fastest measured (kBulkRT
-// below).
+// One BK x BK block of the dense layout as phase 3 handles it: thread
+// (ty, tx) owns RT x CT cells (rows a0 + RT*ty + r, columns j0 + CT*tx + q),
+// and the panel rows of the atoms are staged through LDS, KCH atoms per
+// chunk with the next chunk's loads in flight.  Used by the bulk (k_quads)
+// and by the lead launch (k_lead).  Larger register tiles read fewer staged
+// operand floats per cell but lose occupancy; 4x4 is the fastest measured
+// for the bulk (kBulkRT below).
 template <bool VEC, bool RU, int RT, int CT, int KCH>
-__global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restrict__ U,
-                                                                 float *__restrict__ L,
-                                                                 int64_t n, int64_t batch,
-                                                                 int64_t K, int64_t nk,
-                                                                 int64_t X0, int64_t X1) {
-  constexpr int NTX = BK / CT, NT = (BK / RT) * NTX;
+struct Quad {
+  static constexpr int NTX = BK / CT, NT = (BK / RT) * NTX;
   // operands and cells move as vectors of RW rows / CW columns (4, or 2 for
   // 2-wide tiles)
-  constexpr int RW = RT < 4 ? RT : 4, CW = CT < 4 ? CT : 4;
-  constexpr int RQ = RT / RW, CQ = CT / CW;
+  static constexpr int RW = RT < 4 ? RT : 4, CW = CT < 4 ? CT : 4;
+  static constexpr int RQ = RT / RW, CQ = CT / CW;
   static_assert(RW % 2 == 0 && CW % 2 == 0 && RT % RW == 0 && CT % CW == 0, "tile shape");
-  constexpr int ITER = KCH * (BK / 4) / NT;          // staged float4 per thread and array
+  static constexpr int ITER = KCH * (BK / 4) / NT;  // staged float4 per thread and array
   static_assert(ITER >= 1 && KCH * (BK / 4) % NT == 0, "staging split");
-  __shared__ float4 scu[KCH][BK / 4];
-  __shared__ float4 scl[KCH][BK / 4];
-  __shared__ float4 sru[KCH][BK / 4];
-  __shared__ float4 srl[KCH][BK / 4];
+  struct Stage {
+    float4 cu[KCH][BK / 4], cl[KCH][BK / 4], ru[KCH][BK / 4], rl[KCH][BK / 4];
+  };
 
-  rounding_prologue<RU>();
-  const int tid = threadIdx.x, ty = tid / NTX, tx = tid % NTX;
-  const int64_t p = blockIdx.x >> 2, qd = blockIdx.x & 3;
-  const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
-  const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
-  if (A * BK >= n || B * BK >= n || (A >= X0 && A < X1) || (B >= X0 && B < X1))
-    return;  // uniform over the workgroup, before any barrier
-  const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
-  const int bK = (int)(n - k0 < nk * BK ? n - k0 : nk * BK);
-  const int bA = (int)(n - a0 < BK ? n - a0 : BK);
-  const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
-  const int64_t nn = n * n;
-
-  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
-    float *Ub = U + b * nn;
-    float *Lb = L + b * nn;
-
-    float u[RT][CT], l[RT][CT];
-    {
-      Seg<CW> x[RT][CQ], y[RT][CQ];
+  // the block's cells of one molecule (neutral outside the matrix)
+  static __device__ __forceinline__ void load(const float *Ub, const float *Lb, int64_t n,
+                                              int64_t a0, int64_t j0, int bA, int bJ, int ty,
+                                              int tx, float (&u)[RT][CT], float (&l)[RT][CT]) {
+    Seg<CW> x[RT][CQ], y[RT][CQ];
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int h = 0; h < CQ; ++h) {
-          const int a = ty * RT + r, c = tx * CT + CW * h;
-          const int64_t left = a < bA ? bJ - c : 0;
-          const int64_t g = (a0 + a) * n + j0 + c;
-          x[r][h] = load_seg<VEC, CW>(Ub + g, left, kInf, Ub);
-          y[r][h] = load_seg<VEC, CW>(Lb + g, left, 0.0f, Lb);
+      for (int h = 0; h < CQ; ++h) {
+        const int a = ty * RT + r, c = tx * CT + CW * h;
+        const int64_t left = a < bA ? bJ - c : 0;
+        const int64_t g = (a0 + a) * n + j0 + c;
+        x[r][h] = load_seg<VEC, CW>(Ub + g, left, kInf, Ub);
+        y[r][h] = load_seg<VEC, CW>(Lb + g, left, 0.0f, Lb);
+      }
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int h = 0; h < CQ; ++h)
+#pragma unroll
+        for (int i = 0; i < CW; ++i) {
+          u[r][CW * h + i] = x[r][h].v[i];
+          l[r][CW * h + i] = y[r][h].v[i];
         }
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int h = 0; h < CQ; ++h)
-#pragma unroll
-          for (int i = 0; i < CW; ++i) {
-            u[r][CW * h + i] = x[r][h].v[i];
-            l[r][CW * h + i] = y[r][h].v[i];
-          }
-    }
+  }
 
+  // The atoms k0 .. k0+bK-1 applied to the cells: the panel rows of the atoms
+  // at the columns of band A (U/L[i,k] = U/L[k,i]) and of band B, staged
+  // through sm.  Contains barriers: every thread of the workgroup calls it.
+  static __device__ __forceinline__ void relax(Stage &sm, const float *Ub, const float *Lb,
+                                               int64_t n, int64_t k0, int bK, int64_t a0,
+                                               int64_t j0, int bA, int bJ, int tid, int ty,
+                                               int tx, float (&u)[RT][CT], float (&l)[RT][CT]) {
     // Staging: this thread's float4 of each panel array sits at the same
     // offset from the chunk's first atom row in every chunk (32-bit: n is
     // below 2^27), so only the wave-uniform chunk base moves.  A whole chunk
@@ -888,10 +868,10 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
 #pragma unroll
       for (int it = 0; it < ITER; ++it) {
         const int e = tid + it * NT, kk = e / (BK / 4), x4 = e % (BK / 4);
-        scu[kk][x4] = st[it][0];
-        scl[kk][x4] = st[it][1];
-        sru[kk][x4] = st[it][2];
-        srl[kk][x4] = st[it][3];
+        sm.cu[kk][x4] = st[it][0];
+        sm.cl[kk][x4] = st[it][1];
+        sm.ru[kk][x4] = st[it][2];
+        sm.rl[kk][x4] = st[it][3];
       }
       __syncthreads();
       if (kc + KCH < bK) fetch(kc + KCH);  // in flight during this chunk
@@ -911,18 +891,18 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
 #pragma unroll
         for (int h = 0; h < RQ; ++h) {
           const int i0 = RT * ty + RW * h;
-          vec(scu, kk, i0, RW, cu0 + RW * h);
-          vec(scl, kk, i0, RW, cl0 + RW * h);
-          vec(scu, kk + 1, i0, RW, cu1 + RW * h);
-          vec(scl, kk + 1, i0, RW, cl1 + RW * h);
+          vec(sm.cu, kk, i0, RW, cu0 + RW * h);
+          vec(sm.cl, kk, i0, RW, cl0 + RW * h);
+          vec(sm.cu, kk + 1, i0, RW, cu1 + RW * h);
+          vec(sm.cl, kk + 1, i0, RW, cl1 + RW * h);
         }
 #pragma unroll
         for (int h = 0; h < CQ; ++h) {
           const int i0 = CT * tx + CW * h;
-          vec(sru, kk, i0, CW, ru0 + CW * h);
-          vec(srl, kk, i0, CW, rl0 + CW * h);
-          vec(sru, kk + 1, i0, CW, ru1 + CW * h);
-          vec(srl, kk + 1, i0, CW, rl1 + CW * h);
+          vec(sm.ru, kk, i0, CW, ru0 + CW * h);
+          vec(sm.rl, kk, i0, CW, rl0 + CW * h);
+          vec(sm.ru, kk + 1, i0, CW, ru1 + CW * h);
+          vec(sm.rl, kk + 1, i0, CW, rl1 + CW * h);
         }
 #pragma unroll
         for (int r = 0; r < RT; ++r)
@@ -933,8 +913,15 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
       }
       __syncthreads();
     }
+  }
 
-    // write-back, one CW-float vector per row group
+  // write-back of the cells, one CW-float vector per row group.  The thread
+  // index is re-derived here so that the write addresses are computed after
+  // the k loop instead of being kept live through it.
+  static __device__ __forceinline__ void store(float *Ub, float *Lb, int64_t n, int64_t a0,
+                                               int64_t j0, int bA, int bJ, int tid,
+                                               const float (&u)[RT][CT],
+                                               const float (&l)[RT][CT]) {
     int tw = tid;
     asm volatile("" : "+v"(tw));
     const int wy = tw / NTX, wx = tw % NTX;
@@ -970,30 +957,451 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
         }
       }
     }
+  }
+};
+
+// Bulk of phase 3 for the dense layout: the atoms of k-blocks K .. K+nk-1 in
+// order on every fresh cell outside the bands [X0, X1), as the four BK x BK
+// quadrants of each upper TILE x TILE tile (grid.x = 4 T(T+1)/2, grid.y =
+// molecules).  [X0, X1) starts with the atoms' own bands, whose rows are
+// final, and goes on over the bands updated ahead on the other stream.  A
+// quadrant in any of them is skipped whole (quadrants and bands are both BK
+// wide): it is neither read nor written, and the panel columns of the bands
+// run ahead are not read, since the other stream may be updating exactly
+// those cells while this launch runs.  Each quadrant is a Quad block.
+template <bool VEC, bool RU, int RT, int CT, int KCH>
+__global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restrict__ U,
+                                                                 float *__restrict__ L,
+                                                                 int64_t n, int64_t batch,
+                                                                 int64_t K, int64_t nk,
+                                                                 int64_t X0, int64_t X1) {
+  using Q = Quad<VEC, RU, RT, CT, KCH>;
+  __shared__ typename Q::Stage sm;
+
+  rounding_prologue<RU>();
+  const int tid = threadIdx.x, ty = tid / Q::NTX, tx = tid % Q::NTX;
+  const int64_t p = blockIdx.x >> 2, qd = blockIdx.x & 3;
+  const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
+  const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
+  if (A * BK >= n || B * BK >= n || (A >= X0 && A < X1) || (B >= X0 && B < X1))
+    return;  // uniform over the workgroup, before any barrier
+  const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
+  const int bK = (int)(n - k0 < nk * BK ? n - k0 : nk * BK);
+  const int bA = (int)(n - a0 < BK ? n - a0 : BK);
+  const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
+  const int64_t nn = n * n;
+
+  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    float *Ub = U + b * nn;
+    float *Lb = L + b * nn;
+    float u[RT][CT], l[RT][CT];
+    Q::load(Ub, Lb, n, a0, j0, bA, bJ, ty, tx, u, l);
+    Q::relax(sm, Ub, Lb, n, k0, bK, a0, j0, bA, bJ, tid, ty, tx, u, l);
+    Q::store(Ub, Lb, n, a0, j0, bA, bJ, tid, u, l);
     __syncthreads();
   }
 }
 
-// Bulk of phase 3 for the packed layout (one buffer P: U above the diagonal,
-// L below), 4x4 cells per thread on the same quadrants as k_quads; the
-// lower-left quadrant of a diagonal tile is left out, since its slots are the
-// upper-right one's.  An off-diagonal quadrant (a0 < j0) reads its U as row
-// segments P[a0+a][j0..] and its L as column segments P[j0+c][a0..] (float4
-// along a, turned around in registers), and writes them back the same way,
-// the L half through an LDS tile so that the global writes are row segments.
-// A diagonal quadrant loads the same segments, swaps U and L of its cells
-// left of the diagonal, and writes its rows only (they cover both halves).
-// The panel rows of band K lie right or left of the diagonal, so each staged
-// half is a row segment of P and a column segment read four atoms per float4
-// (packed_half_load).
+// Phase 1 of k-block Z on a Quad block's cells: the closure of the diagonal
+// tile (Z, Z) over its own atoms, in order, by the plain rounds of the
+// notes' §3 restricted to the tile.  Row m is published through LDS (dv,
+// double-buffered, one barrier per round); column m equals row m by
+// symmetry.  Cells outside the matrix are neutral and stay so.  Contains
+// barriers: every thread of the workgroup calls it.
+template <bool RU, int RT, int CT>
+__device__ __forceinline__ void close_tile(float (*dv)[2][BK], int bZ, int ty, int tx,
+                                           float (&u)[RT][CT], float (&l)[RT][CT]) {
+  for (int mb = 0; mb * RT < bZ; ++mb) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int m = mb * RT + r;
+      if (m >= bZ) break;  // uniform
+      const int buf = m & 1;
+      if (ty == mb) {
+#pragma unroll
+        for (int q = 0; q < CT; ++q) {
+          dv[buf][0][tx * CT + q] = u[r][q];
+          dv[buf][1][tx * CT + q] = l[r][q];
+        }
+      }
+      __syncthreads();
+      float cu[RT], cl[RT], eu[CT], el[CT];
+#pragma unroll
+      for (int a = 0; a < RT; ++a) {
+        cu[a] = dv[buf][0][ty * RT + a];  // D[a][m] = D[m][a]
+        cl[a] = dv[buf][1][ty * RT + a];
+      }
+#pragma unroll
+      for (int q = 0; q < CT; ++q) {
+        eu[q] = dv[buf][0][tx * CT + q];  // D[m][b]
+        el[q] = dv[buf][1][tx * CT + q];
+      }
+#pragma unroll
+      for (int a = 0; a < RT; ++a)
+#pragma unroll
+        for (int q = 0; q < CT; ++q) relax1<RU>(u[a][q], l[a][q], cu[a], cl[a], eu[q], el[q]);
+    }
+  }
+}
+
+// The lead launch of the one-stream schedule for k-block K: phase 3 of K on
+// every cell outside band K and outside the diagonal tile (Z, Z) of the next
+// k-block Z = K + 1 (the dense bulk, grid.y = 1 + 4 T(T+1)/2 quadrants), and,
+// in workgroup y = 0 of each molecule, that diagonal tile: phase 3 of K on it
+// (the atoms of K from their finished panel rows), then phase 1 of Z (its
+// closure).  The two parts touch disjoint cells and read only band K, which
+// neither writes, so phase 1 of the next k-block runs beside this one's bulk
+// instead of after it.  With K < 0 the launch is the closure of tile Z alone
+// (the first k-block); with Z < 0 it is the bulk alone (the last).  The
+// closure is on the critical path: grid.x = molecules, so that workgroups
+// dispatch x-fastest and every molecule's closure starts first, and its
+// waves raise their issue priority.
+template <bool VEC, bool RU, int RT, int CT, int KCH>
+__global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_lead(float *__restrict__ U,
+                                                                float *__restrict__ L,
+                                                                int64_t n, int64_t batch,
+                                                                int64_t K, int64_t Z) {
+  using Q = Quad<VEC, RU, RT, CT, KCH>;
+  __shared__ typename Q::Stage sm;
+  __shared__ __align__(16) float dv[2][2][BK];
+
+  rounding_prologue<RU>();
+  const int tid = threadIdx.x, ty = tid / Q::NTX, tx = tid % Q::NTX;
+  const int64_t nn = n * n;
+  if (blockIdx.y == 0) {
+    if (Z < 0) return;  // uniform
+    critical_path_priority();
+    const int64_t z0 = Z * BK, k0 = K * BK;
+    const int bZ = (int)(n - z0 < BK ? n - z0 : BK);
+    const int bK = K < 0 ? 0 : (int)(n - k0 < BK ? n - k0 : BK);
+    for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {
+      float *Ub = U + b * nn;
+      float *Lb = L + b * nn;
+      float u[RT][CT], l[RT][CT];
+      Q::load(Ub, Lb, n, z0, z0, bZ, bZ, ty, tx, u, l);
+      if (K >= 0) Q::relax(sm, Ub, Lb, n, k0, bK, z0, z0, bZ, bZ, tid, ty, tx, u, l);
+      close_tile<RU>(dv, bZ, ty, tx, u, l);
+      Q::store(Ub, Lb, n, z0, z0, bZ, bZ, tid, u, l);
+      __syncthreads();
+    }
+    return;
+  }
+  if (K < 0) return;
+  const int64_t p = (blockIdx.y - 1) >> 2, qd = (blockIdx.y - 1) & 3;
+  const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
+  const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
+  if (A * BK >= n || B * BK >= n || A == K || B == K || (A == Z && B == Z))
+    return;  // uniform over the workgroup, before any barrier
+  const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
+  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int bA = (int)(n - a0 < BK ? n - a0 : BK);
+  const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
+  for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {
+    float *Ub = U + b * nn;
+    float *Lb = L + b * nn;
+    float u[RT][CT], l[RT][CT];
+    Q::load(Ub, Lb, n, a0, j0, bA, bJ, ty, tx, u, l);
+    Q::relax(sm, Ub, Lb, n, k0, bK, a0, j0, bA, bJ, tid, ty, tx, u, l);
+    Q::store(Ub, Lb, n, a0, j0, bA, bJ, tid, u, l);
+    __syncthreads();
+  }
+}
+
+// Phase 2 of k-block K with its diagonal tile D* = (K, K) already closed: the
+// panel tile R = (K, J) (grid.x = the k-blocks J other than K, grid.y =
+// molecules) becomes
+//   R*[a][c] = min(R[a][c], min_m D*[a][m] + R[m][c])              (upper)
+//   L*[a][c] = max(L[a][c], max_m L_D*[a][m] - U_R[m][c], L_R[m][c] - U_D*[a][m])
+// over the atoms m of band K, with R as it was before this phase on the
+// right-hand side.  In the graph view (the 2n-vertex digraph whose shortest
+// paths the fused rounds compute) these are the paths from band K's vertices
+// through band K to J's, split at the last atom of band K they visit, so on
+// the 2^-6 grid this equals running the rounds of band K in order over the
+// panel tile, which the phase 1-2 kernel does.  Unlike those rounds the
+// products need no barrier per atom: D* and R are staged in LDS whole, and
+// every thread relaxes its 4x4 cells over the atoms as the bulk does.  R is
+// read from its fresh orientation and written in both (dense), or as its U
+// and L slots (packed).
+template <bool VEC, bool PK, bool RU>
+__global__ __launch_bounds__(kThreads) void k_product(float *__restrict__ U,
+                                                      float *__restrict__ L, int64_t n,
+                                                      int64_t batch, int64_t K) {
+  __shared__ __align__(16) float su[2][BK][BK];  // D* rows: su[.][m][a] = U/L D*[m][a]
+  __shared__ __align__(16) float sr[2][BK][BK];  // R rows:  sr[.][m][c] = U/L R[m][c]
+  float(*tr)[BK + 1] = reinterpret_cast<float(*)[BK + 1]>(&su[0][0][0]);  // write-back
+
+  rounding_prologue<RU>();
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  int64_t J = blockIdx.x;
+  if (J >= K) ++J;
+  const int64_t k0 = K * BK, j0 = J * BK;
+  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
+  const bool rowor = fresh(K, J);
+  const int64_t nn = n * n;
+
+  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    float *Ub = U + b * nn;
+    float *Lb = PK ? Ub : L + b * nn;
+
+    // D* straight into LDS, one row segment of four at a time (rows of the
+    // dense diagonal tile; the packed one through its logical cells)
+    if (PK) {
+      float du[4][4], dl[4][4];
+      packed_block_load<VEC>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<float4 *>(&su[0][ty * 4 + r][tx * 4]) =
+            make_float4(du[r][0], du[r][1], du[r][2], du[r][3]);
+        *reinterpret_cast<float4 *>(&su[1][ty * 4 + r][tx * 4]) =
+            make_float4(dl[r][0], dl[r][1], dl[r][2], dl[r][3]);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < BK * BK / 4 / kThreads; ++it) {
+        const int e = tid + it * kThreads, a = e / (BK / 4), c = (e % (BK / 4)) * 4;
+        const int64_t g = (k0 + a) * n + k0 + c;
+        const int cnt = a < bK ? clamp4(bK - c) : 0;
+        *reinterpret_cast<float4 *>(&su[0][a][c]) = load4<VEC>(Ub + g, cnt, kInf, Ub);
+        *reinterpret_cast<float4 *>(&su[1][a][c]) = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+      }
+    }
+    // this thread's 4x4 cells of R, the logical cells (k0 + 4ty + r, j0 + 4tx + q)
+    float u[4][4], l[4][4];
+    if (PK) {
+      packed_block_load<VEC>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
+    } else {
+      float4 yu[4], yl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int cnt = rowor ? (ty * 4 + r < bK ? clamp4(bJ - tx * 4) : 0)
+                              : (tx * 4 + r < bJ ? clamp4(bK - ty * 4) : 0);
+        const int64_t g = rowor ? (k0 + ty * 4 + r) * n + j0 + tx * 4
+                                : (j0 + tx * 4 + r) * n + k0 + ty * 4;
+        yu[r] = load4<VEC>(Ub + g, cnt, kInf, Ub);
+        yl[r] = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float bu[4] = {yu[r].x, yu[r].y, yu[r].z, yu[r].w};
+        const float bl[4] = {yl[r].x, yl[r].y, yl[r].z, yl[r].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          (rowor ? u[r][q] : u[q][r]) = bu[q];
+          (rowor ? l[r][q] : l[q][r]) = bl[q];
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<float4 *>(&sr[0][ty * 4 + r][tx * 4]) =
+          make_float4(u[r][0], u[r][1], u[r][2], u[r][3]);
+      *reinterpret_cast<float4 *>(&sr[1][ty * 4 + r][tx * 4]) =
+          make_float4(l[r][0], l[r][1], l[r][2], l[r][3]);
+    }
+    __syncthreads();
+
+    // atoms past bK carry the neutral values (+inf above, 0 below), so the
+    // loop may run over whole pairs
+#pragma unroll 2
+    for (int m = 0; m < bK; m += 2) {
+      const float4 a0v = *reinterpret_cast<const float4 *>(&su[0][m][ty * 4]);
+      const float4 b0v = *reinterpret_cast<const float4 *>(&su[1][m][ty * 4]);
+      const float4 c0v = *reinterpret_cast<const float4 *>(&sr[0][m][tx * 4]);
+      const float4 d0v = *reinterpret_cast<const float4 *>(&sr[1][m][tx * 4]);
+      const float4 a1v = *reinterpret_cast<const float4 *>(&su[0][m + 1][ty * 4]);
+      const float4 b1v = *reinterpret_cast<const float4 *>(&su[1][m + 1][ty * 4]);
+      const float4 c1v = *reinterpret_cast<const float4 *>(&sr[0][m + 1][tx * 4]);
+      const float4 d1v = *reinterpret_cast<const float4 *>(&sr[1][m + 1][tx * 4]);
+      const float cu0[4] = {a0v.x, a0v.y, a0v.z, a0v.w}, cl0[4] = {b0v.x, b0v.y, b0v.z, b0v.w};
+      const float ru0[4] = {c0v.x, c0v.y, c0v.z, c0v.w}, rl0[4] = {d0v.x, d0v.y, d0v.z, d0v.w};
+      const float cu1[4] = {a1v.x, a1v.y, a1v.z, a1v.w}, cl1[4] = {b1v.x, b1v.y, b1v.z, b1v.w};
+      const float ru1[4] = {c1v.x, c1v.y, c1v.z, c1v.w}, rl1[4] = {d1v.x, d1v.y, d1v.z, d1v.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          relax2<RU>(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
+                     rl1[q]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) l[r][q] = lower_out<RU>(l[r][q]);
+
+    // write-back (tr aliases su, free once every thread has left the loop,
+    // which store_transposed's first barrier ensures)
+    int tw = tid;
+    asm volatile("" : "+v"(tw));
+    const int wy = tw >> 4, wx = tw & 15;
+    if (PK) {
+      // R lies on one side of the diagonal: its row slots hold U right of
+      // it, L left of it
+      if (k0 < j0) {
+        store_rows<VEC>(Ub, n, k0, j0, bK, bJ, wy, wx, u);
+        store_transposed<VEC>(Ub, n, k0, j0, bK, bJ, wy, wx, l, tr);
+      } else {
+        store_rows<VEC>(Ub, n, k0, j0, bK, bJ, wy, wx, l);
+        store_transposed<VEC>(Ub, n, k0, j0, bK, bJ, wy, wx, u, tr);
+      }
+    } else {
+      store_rows<VEC>(Ub, n, k0, j0, bK, bJ, wy, wx, u);
+      store_rows<VEC>(Lb, n, k0, j0, bK, bJ, wy, wx, l);
+      store_transposed<VEC>(Ub, n, k0, j0, bK, bJ, wy, wx, u, tr);
+      store_transposed<VEC>(Lb, n, k0, j0, bK, bJ, wy, wx, l, tr);
+    }
+    __syncthreads();  // LDS reuse by the next molecule
+  }
+}
+
+// One BK x BK block of the packed layout (one buffer P: U above the
+// diagonal, L below) as phase 3 handles it, 4x4 cells per thread on 256
+// threads.  An off-diagonal block (a0 < j0) reads its U as row segments
+// P[a0+a][j0..] and its L as column segments P[j0+c][a0..] (float4 along a,
+// turned around in registers), and writes them back the same way, the L half
+// through an LDS tile so that the global writes are row segments.  A
+// diagonal block (a0 == j0) loads the same segments, swaps U and L of its
+// cells left of the diagonal, and writes its rows only (they cover both
+// halves).  The panel rows of the atoms lie right or left of the diagonal,
+// so each staged half is a row segment of P and a column segment read four
+// atoms per float4 (packed_half_load).  Used by the packed bulk
+// (k_quads_packed) and the packed lead launch (k_lead_packed).
+template <bool VEC, bool RU>
+struct PQuad {
+  struct Stage {
+    float4 cu[KC][BK / 4], cl[KC][BK / 4], ru[KC][BK / 4], rl[KC][BK / 4];
+  };
+
+  static __device__ __forceinline__ void load(const float *Pb, int64_t n, int64_t a0, int64_t j0,
+                                              int bA, int bJ, int ty, int tx, bool diag,
+                                              float (&u)[4][4], float (&l)[4][4]) {
+    float4 x[4], y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a = ty * 4 + r;
+      x[r] = load4<VEC>(Pb + (a0 + a) * n + j0 + tx * 4, a < bA ? clamp4(bJ - tx * 4) : 0,
+                        kInf, Pb);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = tx * 4 + q;
+      y[q] = load4<VEC>(Pb + (j0 + c) * n + a0 + ty * 4, c < bJ ? clamp4(bA - ty * 4) : 0,
+                        0.0f, Pb);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float xr[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u[r][q] = xr[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float yq[4] = {y[q].x, y[q].y, y[q].z, y[q].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) l[r][q] = yq[r];
+    }
+    if (diag) {
+      // left of the diagonal the row segment holds L and the column one U
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (ty * 4 + r > tx * 4 + q) {
+            const float t = u[r][q];
+            u[r][q] = l[r][q];
+            l[r][q] = t;
+          }
+    }
+  }
+
+  // The atoms k0 .. k0+bK-1 (band K's, or a step's from K on) applied to the
+  // cells of block (A, B); A and B are outside the atoms' bands.  Contains
+  // barriers: every thread of the workgroup calls it.
+  static __device__ __forceinline__ void relax(Stage &sm, const float *Pb, int64_t n,
+                                               int64_t k0, int bK, int64_t K, int64_t A,
+                                               int64_t B, int64_t a0, int64_t j0, int tid,
+                                               int ty, int tx, float (&u)[4][4],
+                                               float (&l)[4][4]) {
+    // the staging addresses are re-derived per chunk (laundered thread
+    // index) rather than kept live through the k loop.  A whole interior
+    // chunk loads from two 32-bit offsets without masks (73.1-73.8 ms per
+    // packed pass at n12288, against 74.6-74.9 masked; with the offsets kept
+    // live through the loop, as the dense bulk does, it was slower: 78.8 ms)
+    HalfLoad hl[2];
+    auto fetch = [&](int kc) {
+      int tf = tid;
+      asm volatile("" : "+v"(tf));
+      if (VEC && kc + KC <= bK && a0 + BK <= n && j0 + BK <= n) {  // uniform
+        const uint32_t od = half_direct_offset(n, tf), oa = half_across_offset(n, tf);
+        hl[0] = packed_half_load_whole(Pb, n, k0 + kc, a0, od, oa);
+        hl[1] = packed_half_load_whole(Pb, n, k0 + kc, j0, od, oa);
+      } else {
+        hl[0] = packed_half_load<VEC>(Pb, n, k0, kc, bK, a0, A > K, false, tf);
+        hl[1] = packed_half_load<VEC>(Pb, n, k0, kc, bK, j0, B > K, false, tf);
+      }
+    };
+    fetch(0);
+    for (int kc = 0; kc < bK; kc += KC) {
+      int ts = tid;
+      asm volatile("" : "+v"(ts));
+      packed_half_store(hl[0], A > K, reinterpret_cast<float *>(&sm.cu[0][0]),
+                        reinterpret_cast<float *>(&sm.cl[0][0]), BK, 0, ts);
+      packed_half_store(hl[1], B > K, reinterpret_cast<float *>(&sm.ru[0][0]),
+                        reinterpret_cast<float *>(&sm.rl[0][0]), BK, 0, ts);
+      __syncthreads();
+      if (kc + KC < bK) fetch(kc + KC);  // in flight during this chunk
+#pragma unroll 2
+      for (int kk = 0; kk < KC; kk += 2) {
+        const float4 a0v = sm.cu[kk][ty], b0 = sm.cl[kk][ty], c0 = sm.ru[kk][tx],
+                     d0 = sm.rl[kk][tx];
+        const float4 a1 = sm.cu[kk + 1][ty], b1 = sm.cl[kk + 1][ty], c1 = sm.ru[kk + 1][tx],
+                     d1 = sm.rl[kk + 1][tx];
+        const float cu0[4] = {a0v.x, a0v.y, a0v.z, a0v.w}, cl0[4] = {b0.x, b0.y, b0.z, b0.w};
+        const float ru0[4] = {c0.x, c0.y, c0.z, c0.w}, rl0[4] = {d0.x, d0.y, d0.z, d0.w};
+        const float cu1[4] = {a1.x, a1.y, a1.z, a1.w}, cl1[4] = {b1.x, b1.y, b1.z, b1.w};
+        const float ru1[4] = {c1.x, c1.y, c1.z, c1.w}, rl1[4] = {d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            relax2<RU>(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
+                       rl1[q]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // write-back: the addresses are computed after the k loop, not kept live
+  // in it.  Contains barriers: every thread of the workgroup calls it.
+  static __device__ __forceinline__ void store(float *Pb, int64_t n, int64_t a0, int64_t j0,
+                                               int bA, int bJ, int tid, bool diag,
+                                               float (&u)[4][4], float (&l)[4][4],
+                                               float (*tr)[BK + 1]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) l[r][q] = lower_out<RU>(l[r][q]);
+    int tw = tid;
+    asm volatile("" : "+v"(tw));
+    const int wy = tw >> 4, wx = tw & 15;
+    if (diag) {
+      store_packed_diagonal<VEC>(Pb, n, a0, bA, wy, wx, u, l);
+    } else {
+      store_rows<VEC>(Pb, n, a0, j0, bA, bJ, wy, wx, u);
+      store_transposed<VEC>(Pb, n, a0, j0, bA, bJ, wy, wx, l, tr);
+    }
+  }
+};
+
+// Bulk of phase 3 for the packed layout on the same quadrants as k_quads,
+// each a PQuad block; the lower-left quadrant of a diagonal tile is left
+// out, since its slots are the upper-right one's.
 template <bool VEC, bool RU>
 __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P, int64_t n,
                                                            int64_t batch, int64_t K, int64_t nk,
                                                            int64_t X0, int64_t X1) {
-  __shared__ float4 scu[KC][BK / 4];
-  __shared__ float4 scl[KC][BK / 4];
-  __shared__ float4 sru[KC][BK / 4];
-  __shared__ float4 srl[KC][BK / 4];
+  using Q = PQuad<VEC, RU>;
+  __shared__ typename Q::Stage sm;
   __shared__ float tr[BK][BK + 1];  // write-back of the L half
 
   rounding_prologue<RU>();
@@ -1013,110 +1421,64 @@ __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
     float *Pb = P + b * nn;
-
     float u[4][4], l[4][4];
-    {
-      float4 x[4], y[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int a = ty * 4 + r;
-        x[r] = load4<VEC>(Pb + (a0 + a) * n + j0 + tx * 4, a < bA ? clamp4(bJ - tx * 4) : 0,
-                          kInf, Pb);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = tx * 4 + q;
-        y[q] = load4<VEC>(Pb + (j0 + c) * n + a0 + ty * 4, c < bJ ? clamp4(bA - ty * 4) : 0,
-                          0.0f, Pb);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float xr[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) u[r][q] = xr[q];
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float yq[4] = {y[q].x, y[q].y, y[q].z, y[q].w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) l[r][q] = yq[r];
-      }
-    }
-    if (diag) {
-      // left of the diagonal the row segment holds L and the column one U
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (ty * 4 + r > tx * 4 + q) {
-            const float t = u[r][q];
-            u[r][q] = l[r][q];
-            l[r][q] = t;
-          }
-    }
-
-    // the staging addresses are re-derived per chunk (laundered thread
-    // index) rather than kept live through the k loop.  A whole interior
-    // chunk loads from two 32-bit offsets without masks (73.1-73.8 ms per
-    // packed pass at n12288, against 74.6-74.9 masked; with the offsets kept
-    // live through the loop, as k_quads does, it was slower: 78.8 ms)
-    HalfLoad hl[2];
-    auto fetch = [&](int kc) {
-      int tf = tid;
-      asm volatile("" : "+v"(tf));
-      if (VEC && kc + KC <= bK && a0 + BK <= n && j0 + BK <= n) {  // uniform
-        const uint32_t od = half_direct_offset(n, tf), oa = half_across_offset(n, tf);
-        hl[0] = packed_half_load_whole(Pb, n, k0 + kc, a0, od, oa);
-        hl[1] = packed_half_load_whole(Pb, n, k0 + kc, j0, od, oa);
-      } else {
-        hl[0] = packed_half_load<VEC>(Pb, n, k0, kc, bK, a0, A > K, false, tf);
-        hl[1] = packed_half_load<VEC>(Pb, n, k0, kc, bK, j0, B > K, false, tf);
-      }
-    };
-    fetch(0);
-    for (int kc = 0; kc < bK; kc += KC) {
-      int ts = tid;
-      asm volatile("" : "+v"(ts));
-      packed_half_store(hl[0], A > K, reinterpret_cast<float *>(&scu[0][0]),
-                        reinterpret_cast<float *>(&scl[0][0]), BK, 0, ts);
-      packed_half_store(hl[1], B > K, reinterpret_cast<float *>(&sru[0][0]),
-                        reinterpret_cast<float *>(&srl[0][0]), BK, 0, ts);
-      __syncthreads();
-      if (kc + KC < bK) fetch(kc + KC);  // in flight during this chunk
-#pragma unroll 2
-      for (int kk = 0; kk < KC; kk += 2) {
-        const float4 a0v = scu[kk][ty], b0 = scl[kk][ty], c0 = sru[kk][tx], d0 = srl[kk][tx];
-        const float4 a1 = scu[kk + 1][ty], b1 = scl[kk + 1][ty], c1 = sru[kk + 1][tx],
-                     d1 = srl[kk + 1][tx];
-        const float cu0[4] = {a0v.x, a0v.y, a0v.z, a0v.w}, cl0[4] = {b0.x, b0.y, b0.z, b0.w};
-        const float ru0[4] = {c0.x, c0.y, c0.z, c0.w}, rl0[4] = {d0.x, d0.y, d0.z, d0.w};
-        const float cu1[4] = {a1.x, a1.y, a1.z, a1.w}, cl1[4] = {b1.x, b1.y, b1.z, b1.w};
-        const float ru1[4] = {c1.x, c1.y, c1.z, c1.w}, rl1[4] = {d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            relax2<RU>(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
-                       rl1[q]);
-      }
-      __syncthreads();
-    }
-
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) l[r][q] = lower_out<RU>(l[r][q]);
-    // the write addresses are computed after the k loop, not kept live in it
-    int tw = tid;
-    asm volatile("" : "+v"(tw));
-    const int wy = tw >> 4, wx = tw & 15;
-    if (diag) {
-      store_packed_diagonal<VEC>(Pb, n, a0, bA, wy, wx, u, l);
-    } else {
-      store_rows<VEC>(Pb, n, a0, j0, bA, bJ, wy, wx, u);
-      store_transposed<VEC>(Pb, n, a0, j0, bA, bJ, wy, wx, l, tr);
-    }
+    Q::load(Pb, n, a0, j0, bA, bJ, ty, tx, diag, u, l);
+    Q::relax(sm, Pb, n, k0, bK, K, A, B, a0, j0, tid, ty, tx, u, l);
+    Q::store(Pb, n, a0, j0, bA, bJ, tid, diag, u, l, tr);
     __syncthreads();  // tr and the staging arrays are reused by the next molecule
+  }
+}
+
+// The lead launch of the one-stream schedule on the packed layout: k_lead
+// with PQuad blocks (quadrants of the upper tiles, less the lower-left one
+// of each diagonal tile; the closure workgroup's tile is a diagonal block).
+template <bool VEC, bool RU>
+__global__ __launch_bounds__(kThreads) void k_lead_packed(float *__restrict__ P, int64_t n,
+                                                          int64_t batch, int64_t K, int64_t Z) {
+  using Q = PQuad<VEC, RU>;
+  __shared__ typename Q::Stage sm;
+  __shared__ float tr[BK][BK + 1];
+  __shared__ __align__(16) float dv[2][2][BK];
+
+  rounding_prologue<RU>();
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int64_t nn = n * n;
+  if (blockIdx.y == 0) {
+    if (Z < 0) return;  // uniform
+    critical_path_priority();
+    const int64_t z0 = Z * BK, k0 = K * BK;
+    const int bZ = (int)(n - z0 < BK ? n - z0 : BK);
+    const int bK = K < 0 ? 0 : (int)(n - k0 < BK ? n - k0 : BK);
+    for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {
+      float *Pb = P + b * nn;
+      float u[4][4], l[4][4];
+      Q::load(Pb, n, z0, z0, bZ, bZ, ty, tx, true, u, l);
+      if (K >= 0) Q::relax(sm, Pb, n, k0, bK, K, Z, Z, z0, z0, tid, ty, tx, u, l);
+      close_tile<RU>(dv, bZ, ty, tx, u, l);
+      Q::store(Pb, n, z0, z0, bZ, bZ, tid, true, u, l, tr);
+      __syncthreads();
+    }
+    return;
+  }
+  if (K < 0) return;
+  const int64_t p = (blockIdx.y - 1) >> 2, qd = (blockIdx.y - 1) & 3;
+  const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
+  const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
+  if (A * BK >= n || B * BK >= n || A == K || B == K || (A == Z && B == Z) ||
+      (I2 == J2 && qd == 2))
+    return;  // uniform over the workgroup, before any barrier
+  const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
+  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int bA = (int)(n - a0 < BK ? n - a0 : BK);
+  const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
+  const bool diag = A == B;
+  for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {
+    float *Pb = P + b * nn;
+    float u[4][4], l[4][4];
+    Q::load(Pb, n, a0, j0, bA, bJ, ty, tx, diag, u, l);
+    Q::relax(sm, Pb, n, k0, bK, K, A, B, a0, j0, tid, ty, tx, u, l);
+    Q::store(Pb, n, a0, j0, bA, bJ, tid, diag, u, l, tr);
+    __syncthreads();
   }
 }
 
@@ -1260,6 +1622,16 @@ int step_blocks(int64_t n, int64_t batch, const Sched &sched) {
   return tiles >= kStep4Tiles ? 4 : tiles >= kStep3Tiles ? 3 : 2;
 }
 
+bool lead_schedule(int64_t n, int64_t batch, const Sched &sched) {
+  const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
+  // a lead launch's quadrants (and its closure) are one grid dimension
+  if (TB <= 1 || 1 + 2 * T * (T + 1) > kMaxGridYZ || lookahead_bands(n, batch, sched) != 0 ||
+      step_blocks(n, batch, sched) != 1)
+    return false;
+  if (sched.lead >= 0) return sched.lead == 1;
+  return batch >= 2 && (TB - 1) * batch > kPanelFill;
+}
+
 int lookahead_bands(int64_t n, int64_t batch, const Sched &sched) {
   const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
   if (TB <= 1 || T <= 1) return 0;
@@ -1345,8 +1717,16 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   // launches of one half run beside the bulk of the other.  With fewer
   // workgroups per launch the two halves only contend, and one stream in
   // order is faster.
-  const bool split =
-      ahead == 0 && !half && batch >= 2 && TB > 1 && T > 1 && (TB - 1) * batch > kPanelFill;
+  const int64_t W = step_blocks(n, batch, sched), NS = ceil_div(K1 - K0, W);
+  // One stream, one k-block per step, dense layout: the lead schedule.  Per
+  // k-block K, phase 2 of K (k_product, its diagonal tile closed the launch
+  // before), then one launch holding phase 3 of K and, beside it, phase 1 of
+  // K + 1 (k_lead).  The chain per k-block is the longer of the two parts of
+  // a lead launch plus a product launch, instead of a phase 1-2 launch (64
+  // rounds over the diagonal tile and a panel tile) plus a bulk launch.
+  const bool lead_sched = !half && lead_schedule(n, batch, sched);
+  const bool split = ahead == 0 && !half && !lead_sched && batch >= 2 && TB > 1 && T > 1 &&
+                     (TB - 1) * batch > kPanelFill;
   // the second stream of this caller stream, held (locked) until the whole
   // pass is enqueued
   Lane *lane = nullptr;
@@ -1365,6 +1745,47 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
     return e;
   }
   const bool deep = ahead == 2;
+  if (lead_sched) {
+#define DBS_LEAD(R, C, KC)                                                                   \
+  (ru ? (vec ? k_lead<true, true, R, C, KC> : k_lead<false, true, R, C, KC>)                  \
+      : (vec ? k_lead<true, false, R, C, KC> : k_lead<false, false, R, C, KC>))
+    const bool small = !packed && 4 * pairs * batch <= kSmallGrid;
+    auto lead_kernel = small ? DBS_LEAD(kSmallRT, kSmallCT, kSmallKC)
+                             : DBS_LEAD(kBulkRT, kBulkCT, kBulkKC);
+    const unsigned lead_block = small ? (BK / kSmallRT) * (BK / kSmallCT)
+                                      : (BK / kBulkRT) * (BK / kBulkCT);
+#undef DBS_LEAD
+    auto lead_packed = ru ? (vec ? k_lead_packed<true, true> : k_lead_packed<false, true>)
+                          : (vec ? k_lead_packed<true, false> : k_lead_packed<false, false>);
+    auto product_kernel =
+        packed ? (ru ? (vec ? k_product<true, true, true> : k_product<false, true, true>)
+                     : (vec ? k_product<true, true, false> : k_product<false, true, false>))
+               : (ru ? (vec ? k_product<true, false, true> : k_product<false, false, true>)
+                     : (vec ? k_product<true, false, false> : k_product<false, false, false>));
+    // phase 3 of K (none for K < 0) beside phase 1 of Z (none for Z < 0)
+    // grid.x = molecules, grid.y = the closure and then the quadrants
+    const unsigned mx = (unsigned)(batch < kMaxGridX ? batch : kMaxGridX);
+    auto lead = [&](int64_t K, int64_t Z) -> hipError_t {
+      const unsigned gq = (unsigned)(1 + (K >= 0 ? 4 * pairs : 0));
+      const int kind = K >= 0 ? kProfTiles : kProfSmall;
+      if (packed)
+        return launch(prof, kind, lead_packed, dim3(mx, gq), dim3(kThreads), s, U, n, batch, K,
+                      Z);
+      return launch(prof, kind, lead_kernel, dim3(mx, gq), dim3(lead_block), s, U, L, n, batch,
+                    K, Z);
+    };
+    hipError_t e = lead(-1, K0);
+    for (int64_t K = K0; K < K1 && e == hipSuccess; ++K) {
+      e = launch(prof, kProfPanel, product_kernel, dim3((unsigned)(TB - 1), gy), dim3(kThreads),
+                 s, U, L, n, batch, K);
+      if (e == hipSuccess) e = lead(K, K + 1 < K1 ? K + 1 : -1);
+    }
+    // packed storage keeps one slot per value: nothing goes stale
+    if (e == hipSuccess && T > 1 && !packed)
+      e = launch(prof, kProfMirror, k_mirror, dim3((unsigned)(TB * TB), gy), dim3(kThreads), s,
+                 U, L, n, batch, TB);
+    return e;
+  }
   if (ahead == 0 && 4 * pairs * batch <= kSmallGrid) {
     quads_kernel = DBS_QUADS(kSmallRT, kSmallCT, kSmallKC);
     quads_block = (BK / kSmallRT) * (BK / kSmallCT);
@@ -1391,7 +1812,6 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   // [lo(t), hi(t)).  Two steps ahead the bulk takes several blocks per
   // launch, which spreads its fixed costs (the loads and stores of the
   // matrix, the launch's ramp and tail) over more atoms.
-  const int64_t W = step_blocks(n, batch, sched), NS = ceil_div(K1 - K0, W);
   auto lo = [&](int64_t t) { return K0 + t * W; };
   auto hi = [&](int64_t t) { return K0 + (t + 1) * W < K1 ? K0 + (t + 1) * W : K1; };
 

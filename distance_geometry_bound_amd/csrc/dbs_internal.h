@@ -66,13 +66,23 @@ __device__ __forceinline__ float lower_out(float l) {
   return RU ? l + 0.0f : l;
 }
 
+// The smaller of two upper bounds.  Upper bounds are never negative and never
+// NaN (+0, positive values and +inf, under either rounding), and on those the
+// IEEE order is the unsigned order of the bit patterns, so an integer minimum
+// gives the bits fminf gives.  A loop-carried fminf pays one extra VALU
+// instruction to quiet a possible signalling NaN in its operand; the integer
+// minimum needs none.
+__device__ __forceinline__ float upper_min(float a, float b) {
+  return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+}
+
 // One intermediate atom applied to one cell:
 //   (u, l) <- (min(u, cu + ru), max(l, cl - ru, rl - cu))
 // where cu/cl = U/L[i,k] and ru/rl = U/L[k,j].
 template <bool RU = false>
 __device__ __forceinline__ void relax1(float &u, float &l, float cu, float cl, float ru,
                                        float rl) {
-  u = fminf(u, cu + ru);
+  u = upper_min(u, cu + ru);
   if (RU)
     l = fmaxf(fmaxf(l, -(ru - cl)), -(cu - rl));
   else
@@ -191,6 +201,7 @@ hipError_t launch_small(float *U, float *L, int64_t n, int64_t batch, int k_lo, 
 struct Sched {
   int lookahead = -1;
   int step_blocks = -1;
+  int lead = -1;
 };
 // k-blocks K0..K1-1 of the blocked pass (rounds 64*K0 .. min(64*K1, n)-1)
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
@@ -203,6 +214,9 @@ int lookahead_bands(int64_t n, int64_t batch, const Sched &sched = Sched());
 // k-blocks per step of the blocked pass (1 .. kMaxStepBlocks).
 constexpr int kMaxStepBlocks = 4;
 int step_blocks(int64_t n, int64_t batch, const Sched &sched = Sched());
+// Whether the blocked pass takes the lead schedule (one stream, one-block
+// steps: phase 1 of the next k-block beside phase 3, phase 2 as a product).
+bool lead_schedule(int64_t n, int64_t batch, const Sched &sched = Sched());
 hipError_t launch_restraints(float *U, float *L, int64_t n, int64_t batch, float unknown_L,
                              float unknown_U, const int32_t *mol, const int32_t *ia,
                              const int32_t *ja, const float *lo, const float *hi, int64_t count,
@@ -239,7 +253,8 @@ __device__ __forceinline__ int64_t tri_col(int64_t p) {
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Grid dimensions above this are folded into in-kernel loops.
+// Grid dimensions above these are folded into in-kernel loops.
 constexpr int64_t kMaxGridYZ = 65535;
+constexpr int64_t kMaxGridX = 0x7fffffff;
 
 }  // namespace dbs

@@ -94,6 +94,9 @@ extern "C" {
  *                of a blocked pass (dbs_schedule);
  *   step_blocks  DBS_AUTO (default), or 1 .. 4: force that many k-blocks per
  *                step of a blocked pass.
+ *   lead         DBS_AUTO (default), 0 or 1: where a blocked pass runs on the
+ *                caller's stream alone in steps of one k-block, 1 takes the
+ *                lead schedule and 0 the plain one (see dbs_schedule).
  * The schedule fields only reorder independent cell updates: every value
  * gives the same results.  They exist for tests and tuning.  Any other value
  * of a field makes the call return DBS_EINVAL.  The options are read during
@@ -105,6 +108,7 @@ typedef struct dbs_options {
   int32_t directed;
   int32_t lookahead;
   int32_t step_blocks;
+  int32_t lead;
 } dbs_options;
 
 void dbs_options_init(dbs_options *opts);
@@ -356,13 +360,24 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uin
  *     step of w blocks is blocked Floyd-Warshall with 64w atoms per phase-3
  *     launch; its panel (the rows of the step's bands, final for all of its
  *     rounds) is built from the 64-wide phase 1-2 kernel and phase-3 strips.
- * opts->lookahead and opts->step_blocks, when not DBS_AUTO, replace these
- * choices (the depth stays 0 for a single k-block or tile).  Every schedule
- * gives the same results.  Either output pointer may be NULL.  Returns
- * DBS_OK, or DBS_EINVAL for n < 1, batch < 1 or invalid options.
+ *   *lead  1 where the pass takes the lead schedule, else 0.  It applies to
+ *     a pass without look-ahead in steps of one k-block and n below 23 040
+ *     (the phase-3 quadrants of a launch fit one grid dimension), and is
+ *     chosen where
+ *     a batch has more than 256 phase 1-2 workgroups ((k-blocks - 1) x
+ *     molecules).  Per k-block K it runs two launches on the caller's stream:
+ *     phase 2 of K as a product with K's diagonal tile, closed the launch
+ *     before, and one launch that holds phase 3 of K and, beside it, phase 1
+ *     of K + 1 (phase 3 of K on the diagonal tile of K + 1, then its
+ *     closure).  A batch on the lead schedule does not split over two
+ *     streams.
+ * opts->lookahead, opts->step_blocks and opts->lead, when not DBS_AUTO,
+ * replace these choices (the depth stays 0 for a single k-block or tile).
+ * Every schedule gives the same results.  Any output pointer may be NULL.
+ * Returns DBS_OK, or DBS_EINVAL for n < 1, batch < 1 or invalid options.
  */
 int dbs_schedule(int64_t n, int64_t batch, const struct dbs_options *opts, int32_t *lookahead,
-                 int32_t *step_blocks);
+                 int32_t *step_blocks, int32_t *lead);
 
 /* dbs_schedule's automatic look-ahead depth and step width for this shape
    (DBS_EINVAL for n < 1 or batch < 1). */

@@ -94,23 +94,24 @@ def test_rounds_and_algo_range_checks(no_gpu):
 def test_options_are_validated_on_the_host(no_gpu):
     L = dgb.lib()
     byref = ctypes.byref
-    good = _lib.Options(0, 0, -1, -1)
-    d = _lib.Options(9, 9, 9, 9)
+    good = _lib.Options(0, 0, -1, -1, -1)
+    d = _lib.Options(9, 9, 9, 9, 9)
     L.dbs_options_init(byref(d))
-    assert (d.algo, d.directed, d.lookahead, d.step_blocks) == (0, 0, -1, -1)
-    for bad in (_lib.Options(4, 0, -1, -1), _lib.Options(-1, 0, -1, -1),
-                _lib.Options(0, 2, -1, -1), _lib.Options(0, 0, 3, -1),
-                _lib.Options(0, 0, -2, -1), _lib.Options(0, 0, -1, 0),
-                _lib.Options(0, 0, -1, 5)):
+    assert (d.algo, d.directed, d.lookahead, d.step_blocks, d.lead) == (0, 0, -1, -1, -1)
+    for bad in (_lib.Options(4, 0, -1, -1, -1), _lib.Options(-1, 0, -1, -1, -1),
+                _lib.Options(0, 2, -1, -1, -1), _lib.Options(0, 0, 3, -1, -1),
+                _lib.Options(0, 0, -2, -1, -1), _lib.Options(0, 0, -1, 0, -1),
+                _lib.Options(0, 0, -1, 5, -1), _lib.Options(0, 0, -1, -1, 2),
+                _lib.Options(0, 0, -1, -1, -2)):
         assert L.dbs_smooth_opts(A, B, 8, 1, 0, 8, None, byref(bad)) == _lib.DBS_EINVAL
         assert L.dbs_smooth_packed_opts(A, 8, 1, 0, 8, None, byref(bad)) == _lib.DBS_EINVAL
-        assert L.dbs_schedule(8, 1, byref(bad), None, None) == _lib.DBS_EINVAL
+        assert L.dbs_schedule(8, 1, byref(bad), None, None, None) == _lib.DBS_EINVAL
     # blocked ranges must start and end on k-block boundaries
-    blk = _lib.Options(_lib.ALGO_BLOCKED, 0, -1, -1)
+    blk = _lib.Options(_lib.ALGO_BLOCKED, 0, -1, -1, -1)
     assert L.dbs_smooth_opts(A, B, 300, 1, 0, 100, None, byref(blk)) == _lib.DBS_EUNSUPPORTED
     assert L.dbs_smooth_packed_opts(A, 300, 1, 64, 100, None, byref(blk)) == \
         _lib.DBS_EUNSUPPORTED
-    lds = _lib.Options(_lib.ALGO_LDS, 0, -1, -1)
+    lds = _lib.Options(_lib.ALGO_LDS, 0, -1, -1, -1)
     assert L.dbs_smooth_packed_opts(A, 300, 1, 0, 300, None, byref(lds)) == \
         _lib.DBS_EUNSUPPORTED
     assert L.dbs_smooth_opts(A, B, 8, 1, 5, 4, None, byref(good)) == _lib.DBS_EINVAL
@@ -173,23 +174,34 @@ def test_lookahead_bands_query():
 def test_schedule_query_with_forced_values():
     # a forced depth or width applies to that call's options only; the
     # library keeps no setting between calls
-    assert dgb.schedule(200, lookahead=2) == (2, 2)
+    assert dgb.schedule(200, lookahead=2) == (2, 2, 0)
     assert dgb.schedule(4096, lookahead=2)[0] == 2
     assert dgb.schedule(64, lookahead=2)[0] == 0 and dgb.schedule(128, 3, lookahead=2)[0] == 0
-    assert dgb.schedule(12288, lookahead=0) == (0, 1)
-    assert dgb.schedule(12288) == (2, 4) and dgb.schedule(200) == (0, 1)
-    assert dgb.schedule(200, step_blocks=4) == (0, 4)
-    assert dgb.schedule(12288, lookahead=1, step_blocks=3) == (1, 3)
-    for la, sb in ((3, None), (-2, None), (None, 0), (None, 5)):
+    assert dgb.schedule(12288, lookahead=0) == (0, 1, 0)
+    assert dgb.schedule(12288) == (2, 4, 0) and dgb.schedule(200) == (0, 1, 0)
+    assert dgb.schedule(200, step_blocks=4) == (0, 4, 0)
+    assert dgb.schedule(12288, lookahead=1, step_blocks=3) == (1, 3, 0)
+    # the lead schedule: automatic where a batch's phase 1-2 launch would
+    # fill the chip; forced on any one-stream pass with one-block steps
+    assert dgb.schedule(500, 64) == (0, 1, 1) and dgb.schedule(130, 129) == (0, 1, 1)
+    assert dgb.schedule(130, 128)[2] == 0 and dgb.schedule(1024)[2] == 0
+    assert dgb.schedule(500, 64, lead=False) == (0, 1, 0)
+    assert dgb.schedule(1024, lead=True) == (0, 1, 1)
+    assert dgb.schedule(12288, lead=True) == (2, 4, 0)        # runs ahead: no lead
+    assert dgb.schedule(1024, lead=True, step_blocks=2) == (0, 2, 0)
+    assert dgb.schedule(64, lead=True)[2] == 0                 # one k-block
+    for la, sb, ld in ((3, None, None), (-2, None, None), (None, 0, None), (None, 5, None),
+                       (None, None, 2)):
         with pytest.raises(ValueError):
-            dgb.schedule(12288, lookahead=la, step_blocks=sb)
+            dgb.schedule(12288, lookahead=la, step_blocks=sb, lead=ld)
     lib = dgb.lib()
-    la, sb = ctypes.c_int32(7), ctypes.c_int32(7)
-    assert lib.dbs_schedule(12288, 1, None, ctypes.byref(la), ctypes.byref(sb)) == 0
-    assert (la.value, sb.value) == (2, 4)
-    assert lib.dbs_schedule(0, 1, None, None, None) == -1
-    assert lib.dbs_schedule(5, 0, None, None, None) == -1
-    assert lib.dbs_schedule(5, 1, None, None, None) == 0
+    la, sb, ld = ctypes.c_int32(7), ctypes.c_int32(7), ctypes.c_int32(7)
+    assert lib.dbs_schedule(12288, 1, None, ctypes.byref(la), ctypes.byref(sb),
+                            ctypes.byref(ld)) == 0
+    assert (la.value, sb.value, ld.value) == (2, 4, 0)
+    assert lib.dbs_schedule(0, 1, None, None, None, None) == -1
+    assert lib.dbs_schedule(5, 0, None, None, None, None) == -1
+    assert lib.dbs_schedule(5, 1, None, None, None, None) == 0
 
 
 def test_step_blocks_query():

@@ -155,31 +155,35 @@ def test_directed_blocked_within_rounding_bound(n, batch):
     assert bits_equal(host(P), steps.pack(Ug, Lg))
 
 
-@pytest.mark.parametrize("n,batch,bands,blocks", [(700, 1, 2, 2), (700, 1, 2, 4), (700, 1, 1, 3),
-                                                  (385, 2, 2, 4)])
-def test_directed_steps_within_rounding_bound(n, batch, bands, blocks):
-    # steps of several k-blocks group the roundings differently again; every
-    # path sum still takes at most n - 2 roundings, so the same bound holds
+@pytest.mark.parametrize("n,batch,bands,blocks,lead", [
+    (700, 1, 2, 2, None), (700, 1, 2, 4, None), (700, 1, 1, 3, None), (385, 2, 2, 4, None),
+    (700, 1, 0, 1, True), (385, 3, 0, 1, True)])
+def test_directed_steps_within_rounding_bound(n, batch, bands, blocks, lead):
+    # steps of several k-blocks, and the lead schedule's products, group the
+    # roundings differently again; every path sum still takes at most n - 2
+    # roundings, so the same bound holds
     U0, L0 = unquantised(n, batch, seed=3 * n + blocks)
     Ue, Le = oracle.smooth_directed(U0, L0)
+    kw = dict(lookahead=bands, step_blocks=blocks, lead=lead)
     U, L = dev(U0), dev(L0)
-    dgb.smooth_directed(U, L, algo="blocked", lookahead=bands, step_blocks=blocks)
+    dgb.smooth_directed(U, L, algo="blocked", **kw)
     Ug, Lg = host(U), host(L)
     P = dgb.pack(dev(U0), dev(L0))
-    dgb.smooth_packed_directed(P, lookahead=bands, step_blocks=blocks)
+    dgb.smooth_packed_directed(P, **kw)
     Pg = host(P)
     assert within_bound(Ug, Lg, Ue, Le, L0)
     assert np.all(Lg <= Ug)
     assert bits_equal(Pg, steps.pack(Ug, Lg))
 
 
+@pytest.mark.parametrize("lead", [None, True])
 @pytest.mark.parametrize("n", [300, 700])
-def test_directed_blocked_sound_on_line(n):
+def test_directed_blocked_sound_on_line(n, lead):
     U0, L0, X = gen.unquantised_line(n, seed=n)
     d = gen.true_distances(X)
     Ue, Le = oracle.smooth_directed(U0, L0)
     U, L = dev(U0), dev(L0)
-    dgb.smooth_directed(U, L, algo="blocked")
+    dgb.smooth_directed(U, L, algo="blocked", lead=lead)
     Ug, Lg = host(U), host(L)
     assert np.all(Ug.astype(np.float64) >= d) and np.all(Lg.astype(np.float64) <= d)
     assert np.all(Lg <= Ug)

@@ -18,17 +18,19 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-# (130, 129) at the automatic choice: a batch split over the two streams
-@pytest.mark.parametrize("n,batch,bands,blocks", [(700, 1, 2, 2), (700, 1, 2, 4), (385, 2, 1, 1),
-                                                  (385, 2, 0, 2), (130, 129, -1, -1)])
-def test_captured_pass_replays_match_oracle(n, batch, bands, blocks):
+# (130, 129): at the automatic choice the lead schedule on one stream; with
+# lead=False a batch split over the two streams
+@pytest.mark.parametrize("n,batch,bands,blocks,lead", [
+    (700, 1, 2, 2, None), (700, 1, 2, 4, None), (385, 2, 1, 1, None), (385, 2, 0, 2, None),
+    (130, 129, -1, -1, None), (130, 129, -1, -1, False), (385, 2, 0, 1, True)])
+def test_captured_pass_replays_match_oracle(n, batch, bands, blocks, lead):
     U0, L0, _ = gen.random_sound_bounds(n, seed=500 + n + bands, batch=batch, box=6.0 + n / 8)
     Ue, Le = oracle.smooth(U0, L0)
     Ui = torch.from_numpy(U0).to(DEV)
     Li = torch.from_numpy(L0).to(DEV)
     U, L = torch.empty_like(Ui), torch.empty_like(Li)
     kw = dict(algo="blocked", lookahead=None if bands < 0 else bands,
-              step_blocks=None if blocks < 0 else blocks)
+              step_blocks=None if blocks < 0 else blocks, lead=lead)
     s = torch.cuda.Stream(DEV)
     s.wait_stream(torch.cuda.current_stream(DEV))
     with torch.cuda.stream(s):               # warm-up on the capture stream

@@ -169,30 +169,67 @@ def test_every_step_width(n, batch, bands, blocks):
     assert_bits(host(U), host(L), Ue, Le, "ranges 0,192,n " + tag)
 
 
+@pytest.mark.parametrize("lead", [None, False])
 @pytest.mark.parametrize("n,batch", [(130, 129), (200, 87), (257, 86)])
-def test_split_batch(n, batch):
-    # more than 256 phase 1-2 workgroups: the batch splits into two unequal
-    # halves (batch // 2 and the rest), one per stream; dense, directed and
+def test_split_batch(n, batch, lead):
+    # more than 256 phase 1-2 workgroups: automatically the lead schedule on
+    # one stream; without it (lead=False) the batch splits into two unequal
+    # halves (batch // 2 and the rest), one per stream.  Dense, directed and
     # packed passes, and ranges that cut the pass at k-block boundaries
     from oracle import steps
     assert (-(-n // 64) - 1) * batch > 256 and dgb.lookahead_bands(n, batch) == 0
+    assert dgb.schedule(n, batch, lead=lead)[2] == (0 if lead is False else 1)
     U0, L0 = sound_input(n, batch, seed=11 * n + batch)
     Ue, Le = oracle.smooth(U0, L0)
-    tag = f"split n={n} batch={batch}"
-    Ug, Lg = gpu_pass(U0, L0, "blocked")
+    tag = f"n={n} batch={batch} lead={lead}"
+    kw = dict(algo="blocked", lead=lead)
+    Ug, Lg = gpu_pass(U0, L0, **kw)
     assert_bits(Ug, Lg, Ue, Le, "blocked " + tag)
     U, L = dev(U0), dev(L0)
-    dgb.smooth_directed(U, L, algo="blocked")
+    dgb.smooth_directed(U, L, **kw)
     assert_bits(host(U), host(L), Ue, Le, "directed " + tag)
     P = dgb.pack(dev(U0), dev(L0))
-    dgb.smooth_packed(P)
+    dgb.smooth_packed(P, **kw)
     assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
     U, L = dev(U0), dev(L0)
     Ur, Lr = oracle.rounds(U0, L0, 0, 64)
-    dgb.smooth_range(U, L, 0, 64, algo="blocked")
+    dgb.smooth_range(U, L, 0, 64, **kw)
     assert_bits(host(U), host(L), Ur, Lr, "range 0..64 " + tag)
-    dgb.smooth_range(U, L, 64, n, algo="blocked")
+    dgb.smooth_range(U, L, 64, n, **kw)
     assert_bits(host(U), host(L), Ue, Le, "range 64..n " + tag)
+
+
+@pytest.mark.parametrize("n", [65, 127, 128, 129, 191, 192, 257, 300, 385, 503, 700])
+@pytest.mark.parametrize("batch", [1, 3])
+def test_lead_schedule(n, batch):
+    # the lead schedule forced on (phase 2 as a product with the closed
+    # diagonal tile; phase 3 of each k-block beside phase 1 of the next, in
+    # one launch) at sizes with ragged last k-blocks and tiles: dense,
+    # directed and packed passes, and ranges that start inside the pass
+    from oracle import steps
+    assert dgb.schedule(n, batch, lead=True) == (0, 1, 1)
+    U0, L0 = sound_input(n, batch, seed=17 * n + batch)
+    Ue, Le = oracle.smooth(U0, L0)
+    kw = dict(algo="blocked", lead=True)
+    tag = f"lead n={n} batch={batch}"
+    Ug, Lg = gpu_pass(U0, L0, **kw)
+    assert_bits(Ug, Lg, Ue, Le, "blocked " + tag)
+    U, L = dev(U0), dev(L0)
+    dgb.smooth_directed(U, L, **kw)
+    assert_bits(host(U), host(L), Ue, Le, "directed " + tag)
+    P = dgb.pack(dev(U0), dev(L0))
+    dgb.smooth_packed(P, **kw)
+    assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
+    U, L = dev(U0), dev(L0)
+    cuts = sorted({0, 64, min(n, 192), n})
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        dgb.smooth_range(U, L, a, b, **kw)
+        Ur, Lr = oracle.rounds(U0, L0, 0, b)
+        assert_bits(host(U), host(L), Ur, Lr, f"range 0..{b} " + tag)
+    P = dgb.pack(dev(U0), dev(L0))
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        dgb.smooth_packed(P, a, b, **kw)
+    assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
 
 
 def test_walk_molecules_batched():

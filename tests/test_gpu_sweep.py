@@ -2,8 +2,8 @@
 
 Each case draws n (including k-block and tile tails), a batch, an algorithm (on either layout),
 the layout (dense or packed), the rounding entry point (plain or directed; on grid inputs both must give the plain
-pass's bits), a look-ahead depth (automatic or forced 0, 1, 2) and a step width (automatic or
-forced 1..4 k-blocks). It runs one full pass, or a
+pass's bits), a look-ahead depth (automatic or forced 0, 1, 2), a step width (automatic or
+forced 1..4 k-blocks) and the lead schedule (automatic, off or on). It runs one full pass, or a
 pass split at a k-block boundary, and compares every entry with the oracle bit for bit. The draws
 are fixed by the seed, so a failure names a reproducible case.
 """
@@ -31,12 +31,13 @@ def _case(seed):
     depth = int(rng.choice([-1, 0, 1, 2]))
     split = bool(rng.integers(0, 2)) and n > 128
     blocks = int(rng.choice([-1, 1, 2, 3, 4]))
-    return n, batch, algo, packed, directed, depth, split, blocks
+    lead = [None, False, True][int(rng.integers(0, 3))]
+    return n, batch, algo, packed, directed, depth, split, blocks, lead
 
 
-def _run(U0, L0, n, algo, packed, directed, depth, split, blocks):
+def _run(U0, L0, n, algo, packed, directed, depth, split, blocks, lead):
     kw = dict(algo=algo, lookahead=None if depth < 0 else depth,
-              step_blocks=None if blocks < 0 else blocks)
+              step_blocks=None if blocks < 0 else blocks, lead=lead)
     cuts = [0, 128, n] if split else [0, n]
     if packed:
         P = dgb.pack(torch.from_numpy(U0).to(DEV), torch.from_numpy(L0).to(DEV))
@@ -57,12 +58,12 @@ def _run(U0, L0, n, algo, packed, directed, depth, split, blocks):
 
 @pytest.mark.parametrize("seed", range(64))
 def test_random_case_matches_oracle(seed):
-    n, batch, algo, packed, directed, depth, split, blocks = _case(seed)
+    n, batch, algo, packed, directed, depth, split, blocks, lead = _case(seed)
     tag = (f"seed={seed} n={n} batch={batch} algo={algo} packed={packed} "
-           f"directed={directed} depth={depth} split={split} blocks={blocks}")
+           f"directed={directed} depth={depth} split={split} blocks={blocks} lead={lead}")
     U0, L0, _ = gen.random_sound_bounds(n, seed=seed, batch=batch, box=6.0 + n / 8)
     Ue, Le = oracle.smooth(U0, L0)
-    A, B = _run(U0, L0, n, algo, packed, directed, depth, split, blocks)
+    A, B = _run(U0, L0, n, algo, packed, directed, depth, split, blocks, lead)
     if packed:
         assert np.array_equal(A.view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
     else:

@@ -294,3 +294,161 @@ def test_schedule_model_detects_a_missing_panel_orientation():
     Ue, Le = oracle.smooth(U0, L0)
     Um, Lm = Broken(U0, L0, depth=2, W=4).run()
     assert not (np.array_equal(Um, pins.units(Ue)) and np.array_equal(Lm, pins.units(Le)))
+
+
+class LeadModel(Model):
+    """The one-stream lead schedule (one k-block per step), per k-block K:
+      product(K)  phase 2 of K with the diagonal tile (K,K) already closed:
+                  every panel tile (K,J), J != K, read from its fresh
+                  orientation, becomes the min/max over the atoms m of band K
+                  of D*[a][m] (+/-) R[m][c] with R as read (one workgroup per
+                  tile), written in both orientations;
+      lead(K, Z)  in one launch: phase 3 of K on every quadrant outside band
+                  K and outside the diagonal tile (Z,Z), Z = K + 1 (the bulk
+                  workgroups), and phase 3 of K on (Z,Z) followed by the
+                  rounds of band Z over it (the closure workgroup);
+    after a first launch that closes (K0,K0) alone.  Checked: the oracle's
+    result, and that within a launch no workgroup writes what another one
+    reads or writes (the two parts of a lead launch, and the panel tiles of a
+    product launch), in the dense layout and under the packed layout's
+    symmetric closure of the footprints."""
+
+    def __init__(self, U0, L0, skip_diag=True, fresh_read=True):
+        super().__init__(U0, L0, depth=0, W=1)
+        self.skip_diag = skip_diag      # False plants an overlap (self-test)
+        self.fresh_read = fresh_read    # False plants a stale read (self-test)
+
+    def close(self, Z):
+        zb = self.band(Z)
+        ix = np.ix_(zb, zb)
+        Du, Dl = self.U[ix].copy(), self.L[ix].copy()
+        for m in range(len(zb)):
+            du, dl = Du[m].copy(), Dl[m].copy()
+            Du = np.minimum(Du, du[:, None] + du[None, :])
+            Dl = np.maximum(Dl, np.maximum(dl[:, None] - du[None, :], dl[None, :] - du[:, None]))
+        self.U[ix], self.L[ix] = Du, Dl
+
+    def closure_part(self, K, Z):
+        reads, writes = self.mask(), self.mask()
+        zb = self.band(Z)
+        ix = np.ix_(zb, zb)
+        reads[ix] = True
+        if K >= 0:
+            kb = self.band(K)
+            reads[np.ix_(kb, zb)] = True
+            bu, bl = self._phase3(kb, zb, zb)
+            self.U[ix], self.L[ix] = np.minimum(self.U[ix], bu), np.maximum(self.L[ix], bl)
+        self.close(Z)
+        writes[ix] = True
+        return reads, writes
+
+    def bulk_part(self, K, Z):
+        """Phase 3 of K on the quadrants of the upper tiles outside band K and
+        outside (Z,Z), as separate quadrant workgroups."""
+        reads, writes = self.mask(), self.mask()
+        kb = self.band(K)
+        new = []
+        for A in range(self.TB):
+            for B in range(self.TB):
+                if not fresh(A, B) or A == K or B == K:
+                    continue
+                if self.skip_diag and A == Z and B == Z:
+                    continue
+                ab, jb = self.band(A), self.band(B)
+                reads[np.ix_(kb, np.concatenate([ab, jb]))] = True
+                cell = np.ix_(ab, jb)
+                reads[cell] = True
+                bu, bl = self._phase3(kb, ab, jb)
+                new.append((cell, np.minimum(self.U[cell], bu), np.maximum(self.L[cell], bl)))
+                writes[cell] = True
+        for cell, nu, nl in new:
+            self.U[cell], self.L[cell] = nu, nl
+        return reads, writes
+
+    def product(self, K):
+        """Phase 2 of K from the closed diagonal tile: (reads, writes) per
+        panel workgroup."""
+        kb = self.band(K)
+        dix = np.ix_(kb, kb)
+        Du, Dl = self.U[dix].copy(), self.L[dix].copy()
+        parts, new = [], []
+        for J in range(self.TB):
+            if J == K:
+                continue
+            reads, writes = self.mask(), self.mask()
+            reads[dix] = True
+            jb = self.band(J)
+            if fresh(K, J) or not self.fresh_read:
+                Ru, Rl = self.U[np.ix_(kb, jb)].copy(), self.L[np.ix_(kb, jb)].copy()
+                reads[np.ix_(kb, jb)] = True
+            else:
+                Ru, Rl = self.U[np.ix_(jb, kb)].T.copy(), self.L[np.ix_(jb, kb)].T.copy()
+                reads[np.ix_(jb, kb)] = True
+            # min / max over the atoms m: D*[a][m] with R[m][c] as read
+            bu = (Du[:, :, None] + Ru[None, :, :]).min(1)
+            bl = np.maximum((Dl[:, :, None] - Ru[None, :, :]).max(1),
+                            (Rl[None, :, :] - Du[:, :, None]).max(1))
+            nu, nl = np.minimum(Ru, bu), np.maximum(Rl, bl)
+            new.append((kb, jb, nu, nl))
+            writes[np.ix_(kb, jb)] = True
+            writes[np.ix_(jb, kb)] = True
+            parts.append((f"product({K}) tile {J}", reads, writes))
+        for kb_, jb, nu, nl in new:
+            self.U[np.ix_(kb_, jb)], self.L[np.ix_(kb_, jb)] = nu, nl
+            self.U[np.ix_(jb, kb_)], self.L[np.ix_(jb, kb_)] = nu.T, nl.T
+        return parts
+
+    @staticmethod
+    def disjoint(parts):
+        sym = lambda m: m | m.T
+        for i, (ta, ra, wa) in enumerate(parts):
+            for tb, rb, wb in parts[i + 1:]:
+                tag = f"{ta} vs {tb}"
+                assert not np.any(wa & (rb | wb)), tag + ": overlap"
+                assert not np.any(wb & ra), tag + ": overlap"
+                assert not np.any(sym(wa) & sym(rb | wb)), tag + ": packed overlap"
+                assert not np.any(sym(wb) & sym(ra)), tag + ": packed overlap"
+
+    def run(self):
+        TB = self.TB
+        self.closure_part(-1, 0)
+        for K in range(TB):
+            self.disjoint(self.product(K))
+            Z = K + 1 if K + 1 < TB else -1
+            parts = [(f"bulk({K})", *self.bulk_part(K, Z))]
+            if Z >= 0:
+                # the closure workgroup computes from the state before the
+                # launch, as the bulk part does; the model runs it after the
+                # bulk part, which is equivalent when the two are disjoint
+                parts.append((f"closure({Z})", *self.closure_part(K, Z)))
+            self.disjoint(parts)
+        tile = (np.arange(self.n) // BK) // RATIO
+        stale = tile[:, None] > tile[None, :]
+        self.U[stale], self.L[stale] = self.U.T[stale], self.L.T[stale]
+        return self.U, self.L
+
+
+@pytest.mark.parametrize("n", [65, 127, 128, 129, 200, 257, 330, 450])
+def test_lead_schedule_matches_oracle_and_launches_are_disjoint(n):
+    U0, L0, _ = gen.random_sound_bounds(n, seed=3 * n, box=6.0 + n / 8)
+    Ue, Le = oracle.smooth(U0, L0)
+    Um, Lm = LeadModel(U0, L0).run()
+    assert np.array_equal(Um, pins.units(Ue))
+    assert np.array_equal(Lm, pins.units(Le))
+
+
+def test_lead_model_detects_a_planted_overlap():
+    # a lead launch whose bulk part also takes the next diagonal tile writes
+    # what the closure workgroup reads and writes
+    U0, L0, _ = gen.random_sound_bounds(200, seed=2, box=31.0)
+    with pytest.raises(AssertionError, match="overlap"):
+        LeadModel(U0, L0, skip_diag=False).run()
+
+
+def test_lead_model_detects_a_stale_panel_read():
+    # a product that reads panel tiles in the row orientation even where the
+    # symmetric schedule left that copy stale misses the oracle
+    U0, L0, _ = gen.random_sound_bounds(330, seed=4, box=47.0)
+    Ue, Le = oracle.smooth(U0, L0)
+    Um, Lm = LeadModel(U0, L0, fresh_read=False).run()
+    assert not (np.array_equal(Um, pins.units(Ue)) and np.array_equal(Lm, pins.units(Le)))
