@@ -562,13 +562,66 @@ __device__ __forceinline__ void store_transposed(float *P, int64_t n, int64_t r0
 
 // ---------------------------------------------------------------- phase 3
 
-// TILE x TILE tiles are numbered column-major over the upper triangle, and
-// each is split into its four BK x BK quadrants (consecutive workgroups).
-// The hardware deals consecutive workgroups to the 8 XCDs in turn, so at any
-// moment an XCD works on a few tile columns and on every 8th tile row of
-// them: the panel slices it needs fit its L2.  (Giving each XCD a contiguous
-// run of tiles instead makes it sweep every row slice of the panel, and is
-// slower.)
+// Quadrant order of a bulk launch.  The upper TILE x TILE tiles are split
+// into their four BK x BK quadrants (consecutive workgroups), and the
+// hardware deals consecutive workgroups to the 8 XCDs in turn.
+//  * Plain order: tiles column-major over the upper triangle, so at any
+//    moment an XCD works on a few tile columns and on every 8th tile row of
+//    them.
+//  * XCD order: the tiles are grouped into super-blocks of SB x SB tiles,
+//    numbered column-major over the upper triangle (a diagonal super-block
+//    keeps its lower tiles, which exit at once); workgroup w takes
+//    super-block 8 * (w / 8 / (4 SB^2)) + w % 8, so each XCD works through
+//    every 8th super-block, four quadrants of a tile after another.  The
+//    quadrants an XCD runs at once then share few panel row slices, which
+//    stay in its L2: at n = 12288 with 256-atom steps a launch reads 1.26 GB
+//    instead of 2.39 GB, at the same launch time.  It deals the work less
+//    evenly among the XCDs, since the bands a launch leaves out empty some
+//    super-blocks: that costs nothing where a launch runs many rounds of
+//    workgroups, but 2 % at n = 4096 (about two rounds per launch).  Larger
+//    super-blocks cut the reads a little further (SB = 4: 1.18 GB) and are
+//    less even again (n = 12288 pass 69.4 against 68.6 ms); one contiguous
+//    run per XCD is worse still (74 ms).
+constexpr int64_t kSuperBlock = 2;
+// Tiles per side from which a pass that runs two steps ahead takes the XCD
+// order.
+constexpr int64_t kXcdTiles = 64;
+
+// Workgroups of a bulk launch over T x T tiles (the quadrants' grid.x).
+inline int64_t bulk_workgroups(int64_t T, bool xcd) {
+  if (!xcd) return 4 * (T * (T + 1) / 2);
+  const int64_t NSB = ceil_div(T, kSuperBlock), nsp = NSB * (NSB + 1) / 2;
+  return 8 * ceil_div(nsp, 8) * kSuperBlock * kSuperBlock * 4;
+}
+
+// The quadrant (row band A, column band B) of bulk workgroup w in the plain
+// or XCD order, and whether it is the lower-left quadrant of a diagonal
+// tile; false if the workgroup has no quadrant.
+__device__ __forceinline__ bool bulk_quadrant(int64_t w, int64_t n, bool xcd, int64_t &A,
+                                              int64_t &B, bool &lower_left) {
+  int64_t I2, J2, qd;
+  if (!xcd) {
+    const int64_t p = w >> 2;
+    qd = w & 3;
+    J2 = tri_col(p);
+    I2 = p - J2 * (J2 + 1) / 2;
+  } else {
+    constexpr int64_t SB = kSuperBlock, PER = SB * SB * 4;
+    const int64_t T = (n + TILE - 1) / TILE, NSB = (T + SB - 1) / SB;
+    const int64_t loc = w >> 3, sp = (loc / PER) * 8 + (w & 7);
+    if (sp >= NSB * (NSB + 1) / 2) return false;
+    const int64_t r = loc % PER, t = r >> 2;
+    qd = r & 3;
+    const int64_t SJ = tri_col(sp), SI = sp - SJ * (SJ + 1) / 2;
+    I2 = SI * SB + t % SB;
+    J2 = SJ * SB + t / SB;
+    if (I2 > J2 || J2 >= T) return false;
+  }
+  A = RATIO * I2 + (qd >> 1);
+  B = RATIO * J2 + (qd & 1);
+  lower_left = I2 == J2 && qd == 2;
+  return true;
+}
 
 // Phase 3 of the k-blocks K .. K+nk-1 (their atoms in order) on the row
 // bands A0 + r, r < grid.z, other than the atoms' own, run ahead of the bulk
@@ -962,8 +1015,8 @@ struct Quad {
 
 // Bulk of phase 3 for the dense layout: the atoms of k-blocks K .. K+nk-1 in
 // order on every fresh cell outside the bands [X0, X1), as the four BK x BK
-// quadrants of each upper TILE x TILE tile (grid.x = 4 T(T+1)/2, grid.y =
-// molecules).  [X0, X1) starts with the atoms' own bands, whose rows are
+// quadrants of each upper TILE x TILE tile (grid.x = bulk_workgroups(T), in
+// the order of bulk_quadrant; grid.y = molecules).  [X0, X1) starts with the atoms' own bands, whose rows are
 // final, and goes on over the bands updated ahead on the other stream.  A
 // quadrant in any of them is skipped whole (quadrants and bands are both BK
 // wide): it is neither read nor written, and the panel columns of the bands
@@ -974,16 +1027,17 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
                                                                  float *__restrict__ L,
                                                                  int64_t n, int64_t batch,
                                                                  int64_t K, int64_t nk,
-                                                                 int64_t X0, int64_t X1) {
+                                                                 int64_t X0, int64_t X1,
+                                                                 int xcd) {
   using Q = Quad<VEC, RU, RT, CT, KCH>;
   __shared__ typename Q::Stage sm;
 
   rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid / Q::NTX, tx = tid % Q::NTX;
-  const int64_t p = blockIdx.x >> 2, qd = blockIdx.x & 3;
-  const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
-  const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
-  if (A * BK >= n || B * BK >= n || (A >= X0 && A < X1) || (B >= X0 && B < X1))
+  int64_t A, B;
+  bool lower_left;
+  if (!bulk_quadrant(blockIdx.x, n, xcd, A, B, lower_left) || A * BK >= n || B * BK >= n ||
+      (A >= X0 && A < X1) || (B >= X0 && B < X1))
     return;  // uniform over the workgroup, before any barrier
   const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
   const int bK = (int)(n - k0 < nk * BK ? n - k0 : nk * BK);
@@ -1399,18 +1453,17 @@ struct PQuad {
 template <bool VEC, bool RU>
 __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P, int64_t n,
                                                            int64_t batch, int64_t K, int64_t nk,
-                                                           int64_t X0, int64_t X1) {
+                                                           int64_t X0, int64_t X1, int xcd) {
   using Q = PQuad<VEC, RU>;
   __shared__ typename Q::Stage sm;
   __shared__ float tr[BK][BK + 1];  // write-back of the L half
 
   rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int64_t p = blockIdx.x >> 2, qd = blockIdx.x & 3;
-  const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
-  const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
-  if (A * BK >= n || B * BK >= n || (A >= X0 && A < X1) || (B >= X0 && B < X1) ||
-      (I2 == J2 && qd == 2))
+  int64_t A, B;
+  bool lower_left;
+  if (!bulk_quadrant(blockIdx.x, n, xcd, A, B, lower_left) || A * BK >= n || B * BK >= n ||
+      (A >= X0 && A < X1) || (B >= X0 && B < X1) || lower_left)
     return;  // uniform over the workgroup, before any barrier
   const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
   const int bK = (int)(n - k0 < nk * BK ? n - k0 : nk * BK);
@@ -1816,12 +1869,17 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   auto hi = [&](int64_t t) { return K0 + (t + 1) * W < K1 ? K0 + (t + 1) * W : K1; };
 
   // phase 3 of the blocks [K, K + nk) on the cells outside the bands [K, X1)
+  // the XCD order where a bulk launch runs many rounds of workgroups
+  // (measured pass ms, plain / XCD order: n6144 11.29-11.43 / 11.54, n8192
+  // 24.09-24.10 / 24.02-24.13, n12288 68.63-68.84 / 68.41-68.76)
+  const int xcd = deep && T >= kXcdTiles ? 1 : 0;
+  const unsigned bulk_grid = (unsigned)bulk_workgroups(T, xcd);
   auto phase3 = [&](int64_t K, int64_t nk, int64_t X1, hipStream_t st) -> hipError_t {
     if (!packed)
-      return launch(prof, kProfTiles, quads_kernel, dim3((unsigned)(4 * pairs), gy),
-                    dim3(quads_block), st, U, L, n, batch, K, nk, K, X1);
-    return launch(prof, kProfTiles, packed_kernel, dim3((unsigned)(4 * pairs), gy),
-                  dim3(kThreads), st, U, n, batch, K, nk, K, X1);
+      return launch(prof, kProfTiles, quads_kernel, dim3(bulk_grid, gy),
+                    dim3(quads_block), st, U, L, n, batch, K, nk, K, X1, xcd);
+    return launch(prof, kProfTiles, packed_kernel, dim3(bulk_grid, gy),
+                  dim3(kThreads), st, U, n, batch, K, nk, K, X1, xcd);
   };
   // phase 3 of the blocks [K, K + nk) on the nr row bands from A0: row band
   // A0 + r on every column band outside [X0, X1 + r) and other than Y
