@@ -11,7 +11,9 @@
 //   phase 1  the diagonal tile (K,K): a full pass over it, rounds in order;
 //   phase 2  every other tile of band K ("panel"): rounds in order, over
 //            the diagonal tile's rows (phases 1 and 2 run together in
-//            k_diag_panel, one workgroup per panel tile);
+//            k_diag_panel, one workgroup per panel tile; or phase 1 as the
+//            closure of the diagonal tile alone and phase 2 as a product
+//            from it, k_lead and k_product);
 //   phase 3  every remaining cell: all bK rounds at once from the finished
 //            panel (k_quads / k_quads_packed: the bulk on 64x64 quadrants;
 //            k_strip: given row bands alone, when running ahead or inside
@@ -212,7 +214,8 @@ __device__ __forceinline__ void packed_block_store(float *P, int64_t n, int64_t 
 // S*tx..), so the workgroup has (BK/S)^2 threads.  S = 2 (1024 threads, four
 // waves per SIMD) hides the latency of the rounds best when the kernel has
 // the chip to itself; S = 4 (256 threads, a footprint like a phase-3
-// workgroup) gets compute units while the bulk of phase 3 runs.
+// workgroup) gets compute units while the bulk of phase 3 runs (the packed
+// layout's two-step look-ahead).
 template <int S>
 constexpr int panel_threads() { return (BK / S) * (BK / S); }
 
@@ -1185,6 +1188,9 @@ __global__ __launch_bounds__(kThreads) void k_product(float *__restrict__ U,
   float(*tr)[BK + 1] = reinterpret_cast<float(*)[BK + 1]>(&su[0][0][0]);  // write-back
 
   rounding_prologue<RU>();
+  // beside the bulk (two steps ahead) its waves take issue priority, as the
+  // phase 1-2 kernel's do (n12288 pass 67.15-67.17 ms against 67.6-67.7)
+  critical_path_priority();
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   int64_t J = blockIdx.x;
   if (J >= K) ++J;
@@ -1771,7 +1777,7 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   // workgroups per launch the two halves only contend, and one stream in
   // order is faster.
   const int64_t W = step_blocks(n, batch, sched), NS = ceil_div(K1 - K0, W);
-  // One stream, one k-block per step, dense layout: the lead schedule.  Per
+  // One stream, one k-block per step: the lead schedule.  Per
   // k-block K, phase 2 of K (k_product, its diagonal tile closed the launch
   // before), then one launch holding phase 3 of K and, beside it, phase 1 of
   // K + 1 (k_lead).  The chain per k-block is the longer of the two parts of
@@ -1798,40 +1804,45 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
     return e;
   }
   const bool deep = ahead == 2;
-  if (lead_sched) {
+  // Phase 1 of a k-block as the closure of its diagonal tile alone (a lead
+  // launch with no bulk part), and phase 2 as a product from it: the lead
+  // schedule's parts, also the panels of the two-step look-ahead.
 #define DBS_LEAD(R, C, KC)                                                                   \
   (ru ? (vec ? k_lead<true, true, R, C, KC> : k_lead<false, true, R, C, KC>)                  \
       : (vec ? k_lead<true, false, R, C, KC> : k_lead<false, false, R, C, KC>))
-    const bool small = !packed && 4 * pairs * batch <= kSmallGrid;
-    auto lead_kernel = small ? DBS_LEAD(kSmallRT, kSmallCT, kSmallKC)
-                             : DBS_LEAD(kBulkRT, kBulkCT, kBulkKC);
-    const unsigned lead_block = small ? (BK / kSmallRT) * (BK / kSmallCT)
-                                      : (BK / kBulkRT) * (BK / kBulkCT);
+  const bool small_lead = !packed && 4 * pairs * batch <= kSmallGrid;
+  auto lead_kernel = small_lead ? DBS_LEAD(kSmallRT, kSmallCT, kSmallKC)
+                                : DBS_LEAD(kBulkRT, kBulkCT, kBulkKC);
+  const unsigned lead_block = small_lead ? (BK / kSmallRT) * (BK / kSmallCT)
+                                         : (BK / kBulkRT) * (BK / kBulkCT);
 #undef DBS_LEAD
-    auto lead_packed = ru ? (vec ? k_lead_packed<true, true> : k_lead_packed<false, true>)
-                          : (vec ? k_lead_packed<true, false> : k_lead_packed<false, false>);
-    auto product_kernel =
-        packed ? (ru ? (vec ? k_product<true, true, true> : k_product<false, true, true>)
-                     : (vec ? k_product<true, true, false> : k_product<false, true, false>))
-               : (ru ? (vec ? k_product<true, false, true> : k_product<false, false, true>)
-                     : (vec ? k_product<true, false, false> : k_product<false, false, false>));
-    // phase 3 of K (none for K < 0) beside phase 1 of Z (none for Z < 0)
-    // grid.x = molecules, grid.y = the closure and then the quadrants
-    const unsigned mx = (unsigned)(batch < kMaxGridX ? batch : kMaxGridX);
-    auto lead = [&](int64_t K, int64_t Z) -> hipError_t {
-      const unsigned gq = (unsigned)(1 + (K >= 0 ? 4 * pairs : 0));
-      const int kind = K >= 0 ? kProfTiles : kProfSmall;
-      if (packed)
-        return launch(prof, kind, lead_packed, dim3(mx, gq), dim3(kThreads), s, U, n, batch, K,
-                      Z);
-      return launch(prof, kind, lead_kernel, dim3(mx, gq), dim3(lead_block), s, U, L, n, batch,
-                    K, Z);
-    };
-    hipError_t e = lead(-1, K0);
+  auto lead_packed = ru ? (vec ? k_lead_packed<true, true> : k_lead_packed<false, true>)
+                        : (vec ? k_lead_packed<true, false> : k_lead_packed<false, false>);
+  auto product_kernel =
+      packed ? (ru ? (vec ? k_product<true, true, true> : k_product<false, true, true>)
+                   : (vec ? k_product<true, true, false> : k_product<false, true, false>))
+             : (ru ? (vec ? k_product<true, false, true> : k_product<false, false, true>)
+                   : (vec ? k_product<true, false, false> : k_product<false, false, false>));
+  // phase 3 of K (none for K < 0) beside phase 1 of Z (none for Z < 0);
+  // grid.x = molecules, grid.y = the closure and then the quadrants
+  const unsigned mx = (unsigned)(batch < kMaxGridX ? batch : kMaxGridX);
+  auto lead = [&](int64_t K, int64_t Z, hipStream_t st) -> hipError_t {
+    const unsigned gq = (unsigned)(1 + (K >= 0 ? 4 * pairs : 0));
+    const int kind = K >= 0 ? kProfTiles : kProfSmall;
+    if (packed)
+      return launch(prof, kind, lead_packed, dim3(mx, gq), dim3(kThreads), st, U, n, batch, K, Z);
+    return launch(prof, kind, lead_kernel, dim3(mx, gq), dim3(lead_block), st, U, L, n, batch, K,
+                  Z);
+  };
+  auto product = [&](int64_t K, hipStream_t st) -> hipError_t {
+    return launch(prof, kProfPanel, product_kernel, dim3((unsigned)(TB - 1), gy), dim3(kThreads),
+                  st, U, L, n, batch, K);
+  };
+  if (lead_sched) {
+    hipError_t e = lead(-1, K0, s);
     for (int64_t K = K0; K < K1 && e == hipSuccess; ++K) {
-      e = launch(prof, kProfPanel, product_kernel, dim3((unsigned)(TB - 1), gy), dim3(kThreads),
-                 s, U, L, n, batch, K);
-      if (e == hipSuccess) e = lead(K, K + 1 < K1 ? K + 1 : -1);
+      e = product(K, s);
+      if (e == hipSuccess) e = lead(K, K + 1 < K1 ? K + 1 : -1, s);
     }
     // packed storage keeps one slot per value: nothing goes stale
     if (e == hipSuccess && T > 1 && !packed)
@@ -1849,15 +1860,31 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
                 : (vec ? k_diag_panel<true, true, false, S> : k_diag_panel<false, true, false, S>)) \
           : (ru ? (vec ? k_diag_panel<true, false, true, S> : k_diag_panel<false, false, true, S>)  \
                 : (vec ? k_diag_panel<true, false, false, S> : k_diag_panel<false, false, false, S>)))
-  auto panel = deep ? DBS_PICK_PANEL(4) : DBS_PICK_PANEL(2);
-  const unsigned panel_block = deep ? panel_threads<4>() : panel_threads<2>();
+  // the packed layout's two-step look-ahead keeps the 64-round launch, on
+  // 256-thread workgroups that fit where bulk workgroups retire
+  const bool packed_deep = deep && packed;
+  auto panel = packed_deep ? DBS_PICK_PANEL(4) : DBS_PICK_PANEL(2);
+  const unsigned panel_block = packed_deep ? panel_threads<4>() : panel_threads<2>();
 #undef DBS_PICK_PANEL
 
-  // phases 1 and 2 of block K: one launch (the diagonal tile alone when it is
-  // the only block)
+  // Phases 1 and 2 of block K (the diagonal tile alone when it is the only
+  // block).  On the critical path (no look-ahead, or one step) as one launch
+  // of 64 rounds over the diagonal tile and each panel tile, whose
+  // 1024-thread workgroups hide the rounds' latency best.  Two steps ahead
+  // they run beside the bulk, off the critical path, and take its compute
+  // units: there, in the dense layout, as the closure of the diagonal tile
+  // (one workgroup per molecule) and the product, which does not repeat the
+  // diagonal tile's rounds in every panel workgroup (measured n12288 pass,
+  // dense: 68.59 ms with the 64-round launch, 67.71-67.73 ms closure and
+  // product; packed: 72.3 against 80.6 ms the other way round; at n4096,
+  // one step ahead, 4.24 against 4.65-4.78 ms).
   auto phase12 = [&](int64_t K, hipStream_t st) -> hipError_t {
     if (TB == 1)
       return launch_small_block(U, L, n, nn, 0, (int)n, 0, (int)n, batch, st, prof, flags);
+    if (deep && !packed) {
+      const hipError_t r = lead(-1, K, st);
+      return r == hipSuccess ? product(K, st) : r;
+    }
     return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(panel_block), st, U,
                   L, n, batch, K);
   };

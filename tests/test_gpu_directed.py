@@ -173,7 +173,16 @@ def test_directed_steps_within_rounding_bound(n, batch, bands, blocks, lead):
     Pg = host(P)
     assert within_bound(Ug, Lg, Ue, Le, L0)
     assert np.all(Lg <= Ug)
-    assert bits_equal(Pg, steps.pack(Ug, Lg))
+    if bands == 2:
+        # two steps ahead the dense layout builds its panels as the closure of
+        # the diagonal tile and a product, the packed one by the 64-round
+        # phase 1-2 launch: another grouping of the roundings, in the bound
+        Up, Lp = steps.unpack(Pg)
+        assert within_bound(Up, Lp, Ue, Le, L0)
+        assert np.all(Lp <= Up)
+    else:
+        # the packed layout runs the same kernels in the same order
+        assert bits_equal(Pg, steps.pack(Ug, Lg))
 
 
 @pytest.mark.parametrize("lead", [None, True])

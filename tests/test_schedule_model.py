@@ -49,10 +49,16 @@ class Model:
     numpy; the values are exact int64 units, so a min or max over a block's
     candidates does not depend on their order."""
 
-    def __init__(self, U0, L0, depth=2, skip_second=True, W=None):
+    def __init__(self, U0, L0, depth=2, skip_second=True, W=None, fresh_read=True,
+                 product_panels=None):
         self.depth = depth                # steps run ahead on the side stream
         self.W = W if W else (2 if depth == 2 else 1)   # k-blocks per step
         self.skip_second = skip_second    # False plants an overlap (self-test)
+        self.fresh_read = fresh_read      # False plants a stale read (self-test)
+        # two steps ahead (dense layout), phases 1-2 of a block are the
+        # closure of its diagonal tile and a product launch; else one
+        # k_diag_panel launch
+        self.product_panels = depth == 2 if product_panels is None else product_panels
         self.n = U0.shape[0]
         self.U = pins.units(U0).copy()
         self.L = pins.units(L0).copy()
@@ -106,6 +112,66 @@ class Model:
         writes[np.ix_(kb, cols)] = True
         writes[np.ix_(cols, kb)] = True
         return reads, writes
+
+    def close(self, Z):
+        """The rounds of band Z over the diagonal tile (Z,Z) alone, in order
+        (phase 1; one workgroup per molecule): (reads, writes)."""
+        reads, writes = self.mask(), self.mask()
+        zb = self.band(Z)
+        ix = np.ix_(zb, zb)
+        reads[ix] = True
+        Du, Dl = self.U[ix].copy(), self.L[ix].copy()
+        for m in range(len(zb)):
+            du, dl = Du[m].copy(), Dl[m].copy()
+            Du = np.minimum(Du, du[:, None] + du[None, :])
+            Dl = np.maximum(Dl, np.maximum(dl[:, None] - du[None, :], dl[None, :] - du[:, None]))
+        self.U[ix], self.L[ix] = Du, Dl
+        writes[ix] = True
+        return reads, writes
+
+    def product(self, K):
+        """Phase 2 of K from the closed diagonal tile: (reads, writes) per
+        panel workgroup."""
+        kb = self.band(K)
+        dix = np.ix_(kb, kb)
+        Du, Dl = self.U[dix].copy(), self.L[dix].copy()
+        parts, new = [], []
+        for J in range(self.TB):
+            if J == K:
+                continue
+            reads, writes = self.mask(), self.mask()
+            reads[dix] = True
+            jb = self.band(J)
+            if fresh(K, J) or not self.fresh_read:
+                Ru, Rl = self.U[np.ix_(kb, jb)].copy(), self.L[np.ix_(kb, jb)].copy()
+                reads[np.ix_(kb, jb)] = True
+            else:
+                Ru, Rl = self.U[np.ix_(jb, kb)].T.copy(), self.L[np.ix_(jb, kb)].T.copy()
+                reads[np.ix_(jb, kb)] = True
+            # min / max over the atoms m: D*[a][m] with R[m][c] as read
+            bu = (Du[:, :, None] + Ru[None, :, :]).min(1)
+            bl = np.maximum((Dl[:, :, None] - Ru[None, :, :]).max(1),
+                            (Rl[None, :, :] - Du[:, :, None]).max(1))
+            nu, nl = np.minimum(Ru, bu), np.maximum(Rl, bl)
+            new.append((kb, jb, nu, nl))
+            writes[np.ix_(kb, jb)] = True
+            writes[np.ix_(jb, kb)] = True
+            parts.append((f"product({K}) tile {J}", reads, writes))
+        for kb_, jb, nu, nl in new:
+            self.U[np.ix_(kb_, jb)], self.L[np.ix_(kb_, jb)] = nu, nl
+            self.U[np.ix_(jb, kb_)], self.L[np.ix_(jb, kb_)] = nu.T, nl.T
+        return parts
+
+    @staticmethod
+    def disjoint(parts):
+        sym = lambda m: m | m.T
+        for i, (ta, ra, wa) in enumerate(parts):
+            for tb, rb, wb in parts[i + 1:]:
+                tag = f"{ta} vs {tb}"
+                assert not np.any(wa & (rb | wb)), tag + ": overlap"
+                assert not np.any(wb & ra), tag + ": overlap"
+                assert not np.any(sym(wa) & sym(rb | wb)), tag + ": packed overlap"
+                assert not np.any(sym(wb) & sym(ra)), tag + ": packed overlap"
 
     def _phase3(self, kb, rows, cols):
         """Candidates of the atoms kb for the cells rows x cols, from the
@@ -176,6 +242,22 @@ class Model:
             self.U[cell], self.L[cell] = nu, nl
         return reads, writes
 
+    def block_panel(self, K):
+        """Phases 1-2 of block K as (kind, reads, writes) launches: the
+        closure of the diagonal tile, then the product launch (whose panel
+        workgroups must be disjoint), or one k_diag_panel launch."""
+        if not self.product_panels:
+            return [("phase12", *self.phase12(K))]
+        out = [("close", *self.close(K))]
+        parts = self.product(K)
+        self.disjoint(parts)
+        reads, writes = self.mask(), self.mask()
+        for _, r, w in parts:
+            reads |= r
+            writes |= w
+        out.append(("product", reads, writes))
+        return out
+
     def step_panel(self, Ks):
         """The rows of the step's bands Ks final for all of its rounds, as
         (kind, reads, writes) launches.  On the GPU each block's strip over
@@ -183,7 +265,7 @@ class Model:
         of the bands before it, whose blocks those rows hold)."""
         out = []
         for K in Ks:
-            out.append(("phase12", *self.phase12(K)))
+            out.extend(self.block_panel(K))
             for r, A in enumerate(Ks):
                 if A != K:
                     out.append(("panel-strip",
@@ -266,6 +348,17 @@ def test_schedule_model_matches_oracle_and_streams_are_disjoint(n, depth, W):
     assert np.array_equal(Lm, pins.units(Le))
 
 
+@pytest.mark.parametrize("n,W", [(200, None), (330, 3), (520, 4)])
+def test_schedule_model_two_ahead_with_round_panels(n, W):
+    # the packed layout's two-step look-ahead keeps the 64-round phase 1-2
+    # launch; the footprint checks are the same
+    U0, L0, _ = gen.random_sound_bounds(n, seed=n + 1, box=6.0 + n / 8)
+    Ue, Le = oracle.smooth(U0, L0)
+    Um, Lm = Model(U0, L0, depth=2, W=W, product_panels=False).run()
+    assert np.array_equal(Um, pins.units(Ue))
+    assert np.array_equal(Lm, pins.units(Le))
+
+
 def test_schedule_model_detects_a_planted_overlap():
     # a bulk that forgets to leave the bands of step t+2 alone overlaps the
     # side stream's second strip: the footprint check must say so
@@ -283,7 +376,7 @@ def test_schedule_model_detects_a_missing_panel_orientation():
         def step_panel(self, Ks):
             out = []
             for K in Ks:
-                out.append(("phase12", *self.phase12(K)))
+                out.extend(self.block_panel(K))
                 for r, A in enumerate(Ks):
                     if A != K:
                         out.append(("panel-strip",
@@ -293,6 +386,20 @@ def test_schedule_model_detects_a_missing_panel_orientation():
     U0, L0, _ = gen.random_sound_bounds(520, seed=520, box=6.0 + 520 / 8)
     Ue, Le = oracle.smooth(U0, L0)
     Um, Lm = Broken(U0, L0, depth=2, W=4).run()
+    assert not (np.array_equal(Um, pins.units(Ue)) and np.array_equal(Lm, pins.units(Le)))
+
+
+def test_schedule_model_detects_a_product_before_its_closure():
+    # two steps ahead the panel of a block is the product from its closed
+    # diagonal tile; a product from the tile as it stood misses the oracle
+    class Broken(Model):
+        def block_panel(self, K):
+            self.product(K)
+            return [("product", self.mask(), self.mask()), ("close", *self.close(K))]
+
+    U0, L0, _ = gen.random_sound_bounds(330, seed=330, box=6.0 + 330 / 8)
+    Ue, Le = oracle.smooth(U0, L0)
+    Um, Lm = Broken(U0, L0, depth=2).run()
     assert not (np.array_equal(Um, pins.units(Ue)) and np.array_equal(Lm, pins.units(Le)))
 
 
@@ -314,19 +421,8 @@ class LeadModel(Model):
     symmetric closure of the footprints."""
 
     def __init__(self, U0, L0, skip_diag=True, fresh_read=True):
-        super().__init__(U0, L0, depth=0, W=1)
+        super().__init__(U0, L0, depth=0, W=1, fresh_read=fresh_read)
         self.skip_diag = skip_diag      # False plants an overlap (self-test)
-        self.fresh_read = fresh_read    # False plants a stale read (self-test)
-
-    def close(self, Z):
-        zb = self.band(Z)
-        ix = np.ix_(zb, zb)
-        Du, Dl = self.U[ix].copy(), self.L[ix].copy()
-        for m in range(len(zb)):
-            du, dl = Du[m].copy(), Dl[m].copy()
-            Du = np.minimum(Du, du[:, None] + du[None, :])
-            Dl = np.maximum(Dl, np.maximum(dl[:, None] - du[None, :], dl[None, :] - du[:, None]))
-        self.U[ix], self.L[ix] = Du, Dl
 
     def closure_part(self, K, Z):
         reads, writes = self.mask(), self.mask()
@@ -364,50 +460,6 @@ class LeadModel(Model):
         for cell, nu, nl in new:
             self.U[cell], self.L[cell] = nu, nl
         return reads, writes
-
-    def product(self, K):
-        """Phase 2 of K from the closed diagonal tile: (reads, writes) per
-        panel workgroup."""
-        kb = self.band(K)
-        dix = np.ix_(kb, kb)
-        Du, Dl = self.U[dix].copy(), self.L[dix].copy()
-        parts, new = [], []
-        for J in range(self.TB):
-            if J == K:
-                continue
-            reads, writes = self.mask(), self.mask()
-            reads[dix] = True
-            jb = self.band(J)
-            if fresh(K, J) or not self.fresh_read:
-                Ru, Rl = self.U[np.ix_(kb, jb)].copy(), self.L[np.ix_(kb, jb)].copy()
-                reads[np.ix_(kb, jb)] = True
-            else:
-                Ru, Rl = self.U[np.ix_(jb, kb)].T.copy(), self.L[np.ix_(jb, kb)].T.copy()
-                reads[np.ix_(jb, kb)] = True
-            # min / max over the atoms m: D*[a][m] with R[m][c] as read
-            bu = (Du[:, :, None] + Ru[None, :, :]).min(1)
-            bl = np.maximum((Dl[:, :, None] - Ru[None, :, :]).max(1),
-                            (Rl[None, :, :] - Du[:, :, None]).max(1))
-            nu, nl = np.minimum(Ru, bu), np.maximum(Rl, bl)
-            new.append((kb, jb, nu, nl))
-            writes[np.ix_(kb, jb)] = True
-            writes[np.ix_(jb, kb)] = True
-            parts.append((f"product({K}) tile {J}", reads, writes))
-        for kb_, jb, nu, nl in new:
-            self.U[np.ix_(kb_, jb)], self.L[np.ix_(kb_, jb)] = nu, nl
-            self.U[np.ix_(jb, kb_)], self.L[np.ix_(jb, kb_)] = nu.T, nl.T
-        return parts
-
-    @staticmethod
-    def disjoint(parts):
-        sym = lambda m: m | m.T
-        for i, (ta, ra, wa) in enumerate(parts):
-            for tb, rb, wb in parts[i + 1:]:
-                tag = f"{ta} vs {tb}"
-                assert not np.any(wa & (rb | wb)), tag + ": overlap"
-                assert not np.any(wb & ra), tag + ": overlap"
-                assert not np.any(sym(wa) & sym(rb | wb)), tag + ": packed overlap"
-                assert not np.any(sym(wb) & sym(ra)), tag + ": packed overlap"
 
     def run(self):
         TB = self.TB
