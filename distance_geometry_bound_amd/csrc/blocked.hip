@@ -23,8 +23,11 @@
 //
 // Symmetric schedule.  U and L stay exactly symmetric, so only the cells of
 // TILE x TILE tiles (I,J) with I <= J are kept current ("fresh"); tiles below
-// the diagonal go stale and are rebuilt by one transposed copy at the end
-// (k_mirror).  Phase 3 therefore does half the work of a dense schedule.  It
+// the diagonal go stale and get their final values from the last launch that
+// writes their transposes (the last bulk launch of a pass writes each
+// off-diagonal quadrant at both positions; the panels are written in both
+// orientations anyway).  Phase 3 therefore does half the work of a dense
+// schedule.  It
 // reads its operands U/L[i,k] and U/L[k,j] from row k only (U[i,k] = U[k,i]),
 // so phase 2 must leave all of row band K fresh: it updates each panel tile
 // from whichever orientation is fresh and writes both orientations.
@@ -1014,6 +1017,47 @@ struct Quad {
       }
     }
   }
+
+  // The cells also at their transposed positions (j0 + c, a0 + a), for the
+  // stale copy of an off-diagonal tile when this is the last launch of the
+  // pass to write it.  Each matrix is turned around in the LDS tile `tr`
+  // (stride BK + 1) so that the global writes are row segments.  Contains
+  // barriers: every thread of the workgroup calls it.
+  static __device__ __forceinline__ void store_transposed(float *Ub, float *Lb, int64_t n,
+                                                          int64_t a0, int64_t j0, int bA, int bJ,
+                                                          int tid, const float (&u)[RT][CT],
+                                                          const float (&l)[RT][CT],
+                                                          float (*tr)[BK + 1]) {
+    int tw = tid;
+    asm volatile("" : "+v"(tw));
+    const int wy = tw / NTX, wx = tw % NTX;
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat) {
+      __syncthreads();  // tr free (the staging, or the previous matrix)
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int q = 0; q < CT; ++q)
+          tr[wx * CT + q][wy * RT + r] = mat ? lower_out<RU>(l[r][q]) : u[r][q];
+      __syncthreads();
+      float *M = mat ? Lb : Ub;
+      // row c of the transposed block: BK / 4 float4 per row, NT threads
+#pragma unroll
+      for (int it = 0; it < BK * BK / 4 / NT; ++it) {
+        const int e = tw + it * NT, c = e / (BK / 4), a = (e % (BK / 4)) * 4;
+        if (c >= bJ) continue;
+        float *p = M + (j0 + c) * n + a0 + a;
+        if (VEC && a + 3 < bA) {
+          *reinterpret_cast<float4 *>(p) =
+              make_float4(tr[c][a], tr[c][a + 1], tr[c][a + 2], tr[c][a + 3]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (a + i < bA) p[i] = tr[c][a + i];
+        }
+      }
+    }
+  }
 };
 
 // Bulk of phase 3 for the dense layout: the atoms of k-blocks K .. K+nk-1 in
@@ -1024,8 +1068,12 @@ struct Quad {
 // quadrant in any of them is skipped whole (quadrants and bands are both BK
 // wide): it is neither read nor written, and the panel columns of the bands
 // run ahead are not read, since the other stream may be updating exactly
-// those cells while this launch runs.  Each quadrant is a Quad block.
-template <bool VEC, bool RU, int RT, int CT, int KCH>
+// those cells while this launch runs.  Each quadrant is a Quad block.  With
+// MIR (the last launch of a pass) a quadrant of an off-diagonal tile is
+// also written at its transposed position, which leaves the stale tiles
+// final (measured, b64n500 / n1024 / n12288 pass: a separate transposed-copy
+// kernel after the pass took 37 / 15 / 330 us).
+template <bool VEC, bool RU, int RT, int CT, int KCH, bool MIR>
 __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restrict__ U,
                                                                  float *__restrict__ L,
                                                                  int64_t n, int64_t batch,
@@ -1033,7 +1081,11 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
                                                                  int64_t X0, int64_t X1,
                                                                  int xcd) {
   using Q = Quad<VEC, RU, RT, CT, KCH>;
-  __shared__ typename Q::Stage sm;
+  __shared__ union {
+    typename Q::Stage sm;
+    float tr[MIR ? BK : 1][BK + 1];  // the transposed write-back (MIR only)
+  } lds;
+  auto &sm = lds.sm;
 
   rounding_prologue<RU>();
   const int tid = threadIdx.x, ty = tid / Q::NTX, tx = tid % Q::NTX;
@@ -1055,6 +1107,10 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
     Q::load(Ub, Lb, n, a0, j0, bA, bJ, ty, tx, u, l);
     Q::relax(sm, Ub, Lb, n, k0, bK, a0, j0, bA, bJ, tid, ty, tx, u, l);
     Q::store(Ub, Lb, n, a0, j0, bA, bJ, tid, u, l);
+    if constexpr (MIR) {
+      if (A / RATIO < B / RATIO)  // uniform: the quadrant's tile is off the diagonal
+        Q::store_transposed(Ub, Lb, n, a0, j0, bA, bJ, tid, u, l, lds.tr);
+    }
     __syncthreads();
   }
 }
@@ -1109,17 +1165,22 @@ __device__ __forceinline__ void close_tile(float (*dv)[2][BK], int bZ, int ty, i
 // closure).  The two parts touch disjoint cells and read only band K, which
 // neither writes, so phase 1 of the next k-block runs beside this one's bulk
 // instead of after it.  With K < 0 the launch is the closure of tile Z alone
-// (the first k-block); with Z < 0 it is the bulk alone (the last).  The
+// (the first k-block); with Z < 0 it is the bulk alone (the last, which with
+// MIR also writes the transposed copies, as k_quads does).  The
 // closure is on the critical path: grid.x = molecules, so that workgroups
 // dispatch x-fastest and every molecule's closure starts first, and its
 // waves raise their issue priority.
-template <bool VEC, bool RU, int RT, int CT, int KCH>
+template <bool VEC, bool RU, int RT, int CT, int KCH, bool MIR>
 __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_lead(float *__restrict__ U,
                                                                 float *__restrict__ L,
                                                                 int64_t n, int64_t batch,
                                                                 int64_t K, int64_t Z) {
   using Q = Quad<VEC, RU, RT, CT, KCH>;
-  __shared__ typename Q::Stage sm;
+  __shared__ union {
+    typename Q::Stage sm;
+    float tr[MIR ? BK : 1][BK + 1];  // the transposed write-back (MIR only)
+  } lds;
+  auto &sm = lds.sm;
   __shared__ __align__(16) float dv[2][2][BK];
 
   rounding_prologue<RU>();
@@ -1160,6 +1221,10 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_lead(float *__restric
     Q::load(Ub, Lb, n, a0, j0, bA, bJ, ty, tx, u, l);
     Q::relax(sm, Ub, Lb, n, k0, bK, a0, j0, bA, bJ, tid, ty, tx, u, l);
     Q::store(Ub, Lb, n, a0, j0, bA, bJ, tid, u, l);
+    if constexpr (MIR) {
+      if (A / RATIO < B / RATIO)  // uniform: the quadrant's tile is off the diagonal
+        Q::store_transposed(Ub, Lb, n, a0, j0, bA, bJ, tid, u, l, lds.tr);
+    }
     __syncthreads();
   }
 }
@@ -1553,43 +1618,6 @@ constexpr int kBulkRT = 4, kBulkCT = 4, kBulkKC = 16;
 constexpr int kSmallRT = 4, kSmallCT = 2, kSmallKC = 32;
 constexpr int64_t kSmallGrid = 256;
 
-// ---------------------------------------------------------------- mirror
-// grid.x = TB*TB k-block tiles (a = x / TB, b = x % TB), grid.y = molecules.
-// Stale tiles (a,b) (a/RATIO > b/RATIO) are overwritten with the transpose
-// of the fresh tile (b,a).
-__global__ __launch_bounds__(kThreads) void k_mirror(float *__restrict__ U, float *__restrict__ L,
-                                                     int64_t n, int64_t batch, int64_t TB) {
-  __shared__ float su[BK][BK + 1];
-  __shared__ float sl[BK][BK + 1];
-  const int64_t a = blockIdx.x / TB, bt = blockIdx.x % TB;
-  if (fresh(a, bt)) return;  // uniform: whole workgroup leaves
-  const int tid = threadIdx.x;
-  const int64_t nn = n * n;
-  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
-    float *Ub = U + b * nn;
-    float *Lb = L + b * nn;
-    // read fresh tile (bt, a): rows bt*BK + r, columns a*BK + c
-    for (int e = tid; e < BK * BK; e += kThreads) {
-      const int r = e / BK, c = e % BK;
-      const int64_t i = bt * BK + r, j = a * BK + c;
-      if (i < n && j < n) {
-        su[r][c] = Ub[i * n + j];
-        sl[r][c] = Lb[i * n + j];
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < BK * BK; e += kThreads) {
-      const int r = e / BK, c = e % BK;
-      const int64_t i = a * BK + r, j = bt * BK + c;
-      if (i < n && j < n) {
-        Ub[i * n + j] = su[c][r];
-        Lb[i * n + j] = sl[c][r];
-      }
-    }
-    __syncthreads();
-  }
-}
-
 // The ordering events of a pass that runs part of its work on a second
 // stream.  They only order the two streams of one device: the kernels they
 // follow end with a device-scope release and the kernels that wait on them
@@ -1754,10 +1782,11 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   auto packed_kernel = ru ? (vec ? k_quads_packed<true, true> : k_quads_packed<false, true>)
                           : (vec ? k_quads_packed<true, false> : k_quads_packed<false, false>);
   // the dense bulk runs with larger register tiles
-#define DBS_QUADS(R, C, KC)                                                                  \
-  (ru ? (vec ? k_quads<true, true, R, C, KC> : k_quads<false, true, R, C, KC>)                \
-      : (vec ? k_quads<true, false, R, C, KC> : k_quads<false, false, R, C, KC>))
-  auto quads_kernel = DBS_QUADS(kBulkRT, kBulkCT, kBulkKC);
+#define DBS_QUADS(R, C, KC, M)                                                               \
+  (ru ? (vec ? k_quads<true, true, R, C, KC, M> : k_quads<false, true, R, C, KC, M>)          \
+      : (vec ? k_quads<true, false, R, C, KC, M> : k_quads<false, false, R, C, KC, M>))
+  auto quads_kernel = DBS_QUADS(kBulkRT, kBulkCT, kBulkKC, false);
+  auto quads_last = DBS_QUADS(kBulkRT, kBulkCT, kBulkKC, true);
   unsigned quads_block = (BK / kBulkRT) * (BK / kBulkCT);
   auto strip_kernel =
       packed ? (ru ? (vec ? k_strip<true, true, true> : k_strip<false, true, true>)
@@ -1807,12 +1836,14 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   // Phase 1 of a k-block as the closure of its diagonal tile alone (a lead
   // launch with no bulk part), and phase 2 as a product from it: the lead
   // schedule's parts, also the panels of the two-step look-ahead.
-#define DBS_LEAD(R, C, KC)                                                                   \
-  (ru ? (vec ? k_lead<true, true, R, C, KC> : k_lead<false, true, R, C, KC>)                  \
-      : (vec ? k_lead<true, false, R, C, KC> : k_lead<false, false, R, C, KC>))
+#define DBS_LEAD(R, C, KC, M)                                                                \
+  (ru ? (vec ? k_lead<true, true, R, C, KC, M> : k_lead<false, true, R, C, KC, M>)            \
+      : (vec ? k_lead<true, false, R, C, KC, M> : k_lead<false, false, R, C, KC, M>))
   const bool small_lead = !packed && 4 * pairs * batch <= kSmallGrid;
-  auto lead_kernel = small_lead ? DBS_LEAD(kSmallRT, kSmallCT, kSmallKC)
-                                : DBS_LEAD(kBulkRT, kBulkCT, kBulkKC);
+  auto lead_kernel = small_lead ? DBS_LEAD(kSmallRT, kSmallCT, kSmallKC, false)
+                                : DBS_LEAD(kBulkRT, kBulkCT, kBulkKC, false);
+  auto lead_last = small_lead ? DBS_LEAD(kSmallRT, kSmallCT, kSmallKC, true)
+                              : DBS_LEAD(kBulkRT, kBulkCT, kBulkKC, true);
   const unsigned lead_block = small_lead ? (BK / kSmallRT) * (BK / kSmallCT)
                                          : (BK / kBulkRT) * (BK / kBulkCT);
 #undef DBS_LEAD
@@ -1826,32 +1857,31 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   // phase 3 of K (none for K < 0) beside phase 1 of Z (none for Z < 0);
   // grid.x = molecules, grid.y = the closure and then the quadrants
   const unsigned mx = (unsigned)(batch < kMaxGridX ? batch : kMaxGridX);
-  auto lead = [&](int64_t K, int64_t Z, hipStream_t st) -> hipError_t {
+  // (last: the last launch of the pass, which also writes the stale tiles'
+  // copies; packed storage keeps one slot per value, so nothing goes stale)
+  auto lead = [&](int64_t K, int64_t Z, hipStream_t st, bool last) -> hipError_t {
     const unsigned gq = (unsigned)(1 + (K >= 0 ? 4 * pairs : 0));
     const int kind = K >= 0 ? kProfTiles : kProfSmall;
     if (packed)
       return launch(prof, kind, lead_packed, dim3(mx, gq), dim3(kThreads), st, U, n, batch, K, Z);
-    return launch(prof, kind, lead_kernel, dim3(mx, gq), dim3(lead_block), st, U, L, n, batch, K,
-                  Z);
+    return launch(prof, kind, last ? lead_last : lead_kernel, dim3(mx, gq), dim3(lead_block), st,
+                  U, L, n, batch, K, Z);
   };
   auto product = [&](int64_t K, hipStream_t st) -> hipError_t {
     return launch(prof, kProfPanel, product_kernel, dim3((unsigned)(TB - 1), gy), dim3(kThreads),
                   st, U, L, n, batch, K);
   };
   if (lead_sched) {
-    hipError_t e = lead(-1, K0, s);
+    hipError_t e = lead(-1, K0, s, false);
     for (int64_t K = K0; K < K1 && e == hipSuccess; ++K) {
       e = product(K, s);
-      if (e == hipSuccess) e = lead(K, K + 1 < K1 ? K + 1 : -1, s);
+      if (e == hipSuccess) e = lead(K, K + 1 < K1 ? K + 1 : -1, s, K + 1 == K1);
     }
-    // packed storage keeps one slot per value: nothing goes stale
-    if (e == hipSuccess && T > 1 && !packed)
-      e = launch(prof, kProfMirror, k_mirror, dim3((unsigned)(TB * TB), gy), dim3(kThreads), s,
-                 U, L, n, batch, TB);
     return e;
   }
   if (ahead == 0 && 4 * pairs * batch <= kSmallGrid) {
-    quads_kernel = DBS_QUADS(kSmallRT, kSmallCT, kSmallKC);
+    quads_kernel = DBS_QUADS(kSmallRT, kSmallCT, kSmallKC, false);
+    quads_last = DBS_QUADS(kSmallRT, kSmallCT, kSmallKC, true);
     quads_block = (BK / kSmallRT) * (BK / kSmallCT);
   }
 #undef DBS_QUADS
@@ -1882,7 +1912,7 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
     if (TB == 1)
       return launch_small_block(U, L, n, nn, 0, (int)n, 0, (int)n, batch, st, prof, flags);
     if (deep && !packed) {
-      const hipError_t r = lead(-1, K, st);
+      const hipError_t r = lead(-1, K, st, false);
       return r == hipSuccess ? product(K, st) : r;
     }
     return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(panel_block), st, U,
@@ -1901,9 +1931,11 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   // 24.09-24.10 / 24.02-24.13, n12288 68.63-68.84 / 68.41-68.76)
   const int xcd = deep && T >= kXcdTiles ? 1 : 0;
   const unsigned bulk_grid = (unsigned)bulk_workgroups(T, xcd);
-  auto phase3 = [&](int64_t K, int64_t nk, int64_t X1, hipStream_t st) -> hipError_t {
+  // (last: the last one of the pass, which also writes the stale tiles'
+  // copies; packed storage keeps one slot per value, so nothing goes stale)
+  auto phase3 = [&](int64_t K, int64_t nk, int64_t X1, hipStream_t st, bool last) -> hipError_t {
     if (!packed)
-      return launch(prof, kProfTiles, quads_kernel, dim3(bulk_grid, gy),
+      return launch(prof, kProfTiles, last ? quads_last : quads_kernel, dim3(bulk_grid, gy),
                     dim3(quads_block), st, U, L, n, batch, K, nk, K, X1, xcd);
     return launch(prof, kProfTiles, packed_kernel, dim3(bulk_grid, gy),
                   dim3(kThreads), st, U, n, batch, K, nk, K, X1, xcd);
@@ -1939,7 +1971,7 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   Lane *ev = lane;
   if (side == nullptr) {
     for (int64_t t = 0; t < NS && e == hipSuccess; ++t) {
-      e = phase3(lo(t), hi(t) - lo(t), hi(t), s);
+      e = phase3(lo(t), hi(t) - lo(t), hi(t), s, t + 1 == NS);
       if (e == hipSuccess && t + 1 < NS) e = step_panel(t + 1, s);
     }
   } else {
@@ -1949,7 +1981,9 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
       const bool n1 = t + 1 < NS, n2 = deep && t + 2 < NS;
       const int64_t b = lo(t), w = hi(t) - b;
       if (t > 0 && (e = hipStreamWaitEvent(s, ev->ready(t), 0)) != hipSuccess) break;
-      if ((e = phase3(b, w, n2 ? hi(t + 2) : n1 ? hi(t + 1) : hi(t), s)) != hipSuccess) break;
+      if ((e = phase3(b, w, n2 ? hi(t + 2) : n1 ? hi(t + 1) : hi(t), s, t + 1 == NS)) !=
+          hipSuccess)
+        break;
       if ((e = hipEventRecord(ev->bulk(t), s)) != hipSuccess) break;
       if (n1) {
         // one step ahead, step t+1's bands after step t-1 come from bulk(t-1)
@@ -1969,10 +2003,6 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
       if (n1 && (e = hipEventRecord(ev->ready(t + 1), side)) != hipSuccess) break;
     }
   }
-  // packed storage keeps one slot per value: nothing goes stale
-  if (e == hipSuccess && T > 1 && !packed)
-    e = launch(prof, kProfMirror, k_mirror, dim3((unsigned)(TB * TB), gy), dim3(kThreads), s, U,
-               L, n, batch, TB);
   return e;
 }
 }  // namespace

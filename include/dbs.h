@@ -204,7 +204,8 @@ int dbs_smooth_profiled(float *U, float *L, int64_t n, int64_t batch, void *stre
 #define DBS_PROF_PANEL 2   /* blocked phase 2: panel tiles                     */
 #define DBS_PROF_TILES 3   /* blocked phase 3: the bulk (every upper tile, less
                               the current and the next k-block's bands)       */
-#define DBS_PROF_MIRROR 4  /* blocked: final transposed copy                   */
+#define DBS_PROF_MIRROR 4  /* reserved, always 0: the last phase-3 launch of a
+                              blocked pass writes the stale transposed copies */
 #define DBS_PROF_STRIP 5   /* blocked phase 3 on the next k-block's band, run
                               ahead on a second stream                        */
 #define DBS_PROF_FILL 6    /* restraints: placeholder fill                     */
