@@ -210,7 +210,7 @@ __device__ __forceinline__ void packed_block_store(float *P, int64_t n, int64_t 
 // K, so they reach the values of finishing D first and the panel from it
 // (exactly, on the 2^-6 grid).  Every workgroup repeats D's rounds: that
 // costs less than a launch of its own on the critical path of the pass.
-// Workgroup 0 writes D back.  Cells outside the matrix start neutral and stay
+// The last workgroup writes D back.  Cells outside the matrix start neutral and stay
 // neutral (every candidate through them is +inf for U and <= 0 for L).
 //
 // Thread (ty, tx) owns an S x S cell block of D and of R (rows S*ty.., columns
@@ -247,7 +247,10 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
   const int bK = (int)(n - k0 < BK ? n - k0 : BK);
   const int bJ = (int)(n - j0 < BK ? n - j0 : BK);
   const bool rowor = fresh(K, J);
-  const bool writes_d = blockIdx.x == 0;
+  // the last workgroup of the molecule writes D back: every other one was
+  // dispatched before it and reads D at its start, long before that
+  // workgroup's 64 rounds are done
+  const bool writes_d = blockIdx.x == gridDim.x - 1;
   const int64_t nn = n * n;
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
