@@ -86,10 +86,28 @@ dbs::Sched sched_of(const dbs_options &o) {
   return sc;
 }
 
+// The algorithm DBS_ALGO_AUTO takes: the single workgroup per molecule where
+// the pass fits it, except for a round-to-nearest pass in the dense layout
+// from n = 128 with at most kAutoBlockedBatch molecules, where the blocked
+// pass is faster; else the blocked pass on k-block boundaries, else one
+// launch per round.  A directed pass keeps the single workgroup where it
+// fits: it applies the roundings in the plain round order (the blocked pass
+// groups them differently, within the bound of the directed rounding).  (Measured
+// dense pass ms, single workgroup / blocked: n120 0.076 / 0.078, n128 0.088
+// / 0.080, n176 0.137 / 0.114; 16 molecules of n128 0.089 / 0.085, of n176
+// 0.139 / 0.119; 64 of n128 0.088 / 0.092.  The packed single workgroup is
+// faster than the packed blocked pass at every n up to 176 and batch: n128
+// 0.079 / 0.089, n176 0.127 / 0.128.)
+constexpr int64_t kAutoBlockedMinN = 128, kAutoBlockedBatch = 16;
+int auto_algo(int64_t n, int64_t batch, bool packed, bool directed, bool aligned) {
+  if (n <= dbs::kSmallMaxN && (packed || directed || n < kAutoBlockedMinN ||
+                               batch > kAutoBlockedBatch || !aligned))
+    return DBS_ALGO_LDS;
+  return aligned ? DBS_ALGO_BLOCKED : DBS_ALGO_PERK;
+}
+
 // Rounds k_begin..k_end-1 of a pass on U, L (dense) or on P = U (packed,
-// L ignored), with the given options.  AUTO takes the single workgroup for
-// small n, blocked when both ends are on k-block boundaries, else one launch
-// per round.
+// L ignored), with the given options (AUTO: auto_algo).
 int pass_impl(float *U, float *L, bool packed, int64_t n, int64_t batch, int64_t k_begin,
               int64_t k_end, void *stream, const dbs_options *opts, dbs::Prof *prof) {
   if (packed) {
@@ -106,8 +124,7 @@ int pass_impl(float *U, float *L, bool packed, int64_t n, int64_t batch, int64_t
   const int64_t B = dbs::kBlockRounds;
   const bool aligned = k_begin % B == 0 && (k_end % B == 0 || k_end == n);
   int algo = o.algo;
-  if (algo == DBS_ALGO_AUTO)
-    algo = n <= dbs::kSmallMaxN ? DBS_ALGO_LDS : aligned ? DBS_ALGO_BLOCKED : DBS_ALGO_PERK;
+  if (algo == DBS_ALGO_AUTO) algo = auto_algo(n, batch, packed, o.directed != 0, aligned);
   if (algo == DBS_ALGO_LDS && n > dbs::kSmallMaxN) return DBS_EUNSUPPORTED;
   if (algo == DBS_ALGO_BLOCKED && !aligned) return DBS_EUNSUPPORTED;
   const int st = device_status();
@@ -342,10 +359,7 @@ int dbs_step_blocks(int64_t n, int64_t batch) {
   return dbs::step_blocks(n, batch);
 }
 
-int dbs_auto_algo(int64_t n, int64_t batch) {
-  (void)batch;
-  return n <= dbs::kSmallMaxN ? DBS_ALGO_LDS : DBS_ALGO_BLOCKED;
-}
+int dbs_auto_algo(int64_t n, int64_t batch) { return auto_algo(n, batch, false, false, true); }
 
 const char *dbs_strerror(int status) {
   switch (status) {

@@ -75,7 +75,8 @@ extern "C" {
 #define DBS_EUNSUPPORTED (-4) /* the requested algorithm cannot run this shape */
 
 /* Algorithms for dbs_smooth_algo.  All of them produce the same bits. */
-#define DBS_ALGO_AUTO 0    /* LDS when it fits, else BLOCKED                  */
+#define DBS_ALGO_AUTO 0    /* dbs_auto_algo: mostly LDS when it fits, else
+                              BLOCKED                                         */
 #define DBS_ALGO_PERK 1    /* one launch per round k (the notes' §3-§4 round
                               structure, in place instead of front/back buffers) */
 #define DBS_ALGO_LDS 2     /* one workgroup per molecule runs the whole pass;
@@ -122,8 +123,10 @@ void dbs_options_init(dbs_options *opts);
  *
  * dbs_smooth_packed_opts -- the same on the packed one-buffer layout P (see
  * dbs_smooth_packed_range): DBS_ALGO_PERK, DBS_ALGO_LDS and DBS_ALGO_BLOCKED
- * follow the rules of dbs_smooth_range; DBS_ALGO_AUTO takes LDS when it
- * fits, else BLOCKED when both ends are on k-block boundaries, else PERK.
+ * follow the rules of dbs_smooth_range; DBS_ALGO_AUTO takes the choice of
+ * dbs_auto_algo (the packed layout and directed rounding: LDS whenever it
+ * fits) when both ends are on k-block boundaries, else LDS when it fits,
+ * else PERK.
  */
 int dbs_smooth_opts(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,
                     int64_t k_end, void *stream, const dbs_options *opts);
@@ -299,7 +302,8 @@ int dbs_bounds_from_restraints(float *U, float *L, int64_t n, int64_t batch,
  *   rounding error (relative 2^-23 per addition along a path); it is sound
  *   in the same sense.  On grid inputs (every operation exact) all
  *   algorithms give the bits of dbs_smooth_range.
- * dbs_smooth_directed -- a full pass, algorithm as dbs_smooth.
+ * dbs_smooth_directed -- a full pass, algorithm as dbs_smooth except that
+ *   DBS_ALGO_AUTO keeps DBS_ALGO_LDS wherever it fits.
  * dbs_smooth_packed_directed_range -- dbs_smooth_packed_range with directed
  *   rounding (same algorithm choice, same remarks).
  * Preconditions and argument errors as dbs_smooth, except that values need
@@ -390,7 +394,10 @@ int dbs_step_blocks(int64_t n, int64_t batch);
 /* Largest n the LDS algorithm accepts. */
 int dbs_lds_max_n(void);
 
-/* The algorithm DBS_ALGO_AUTO picks for this shape (n, batch >= 1). */
+/* The algorithm DBS_ALGO_AUTO picks for a whole round-to-nearest pass in the
+ * dense layout of this shape (n, batch >= 1): BLOCKED from n = 128 with at
+ * most 16 molecules and above dbs_lds_max_n(), else LDS (the packed layout
+ * and directed rounding take LDS whenever it fits). */
 int dbs_auto_algo(int64_t n, int64_t batch);
 
 /* Static description of a status code (never NULL). */

@@ -48,7 +48,12 @@ def test_static_queries():
     L = dgb.lib()
     assert L.dbs_version() == 0x000100
     assert L.dbs_lds_max_n() >= 128
-    assert L.dbs_auto_algo(128, 1) == _lib.ALGO_LDS
+    assert L.dbs_auto_algo(127, 1) == _lib.ALGO_LDS
+    assert L.dbs_auto_algo(128, 1) == _lib.ALGO_BLOCKED
+    assert L.dbs_auto_algo(176, 16) == _lib.ALGO_BLOCKED
+    assert L.dbs_auto_algo(128, 17) == _lib.ALGO_LDS
+    assert L.dbs_auto_algo(176, 64) == _lib.ALGO_LDS
+    assert L.dbs_auto_algo(177, 64) == _lib.ALGO_BLOCKED
     assert L.dbs_auto_algo(12288, 1) == _lib.ALGO_BLOCKED
     assert L.dbs_strerror(-1) == b"invalid argument"
     assert L.dbs_strerror(12345) == b"unknown status"
