@@ -11,7 +11,8 @@ _API = ("smooth", "smooth_round", "smooth_rounds", "check", "lib", "DbsError", "
         "bounds_from_restraints", "RESTRAINT_FLAGS", "pack", "unpack", "smooth_packed", "check_packed",
         "smooth_directed", "smooth_directed_range", "smooth_packed_directed", "lookahead_bands",
         "step_blocks", "schedule", "options", "Options", "AUTO",
-        "ALGO_AUTO", "ALGO_PERK", "ALGO_LDS", "ALGO_BLOCKED", "CHECK_FLAGS")
+        "ALGO_AUTO", "ALGO_PERK", "ALGO_LDS", "ALGO_BLOCKED", "CHECK_FLAGS",
+        "INFEASIBLE_EARLY", "INFEASIBLE_END")
 
 
 def __getattr__(name):

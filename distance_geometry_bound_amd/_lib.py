@@ -39,7 +39,12 @@ class Options(ctypes.Structure):
     """struct dbs_options (include/dbs.h): per-call options of a pass."""
     _fields_ = [("algo", ctypes.c_int32), ("directed", ctypes.c_int32),
                 ("lookahead", ctypes.c_int32), ("step_blocks", ctypes.c_int32),
-                ("lead", ctypes.c_int32)]
+                ("lead", ctypes.c_int32), ("infeasible", ctypes.c_void_p)]
+
+
+# bits of the infeasibility words (include/dbs.h)
+INFEASIBLE_EARLY = 1
+INFEASIBLE_END = 2
 
 
 RESTRAINT_FLAGS = {"index": 1, "value": 2}
@@ -154,20 +159,36 @@ def _call(T, fn, *args):
 
 
 def options(algo: str = "auto", directed: bool = False, lookahead=None, step_blocks=None,
-            lead=None):
+            lead=None, infeasible=None):
     """struct dbs_options for a pass: `lookahead` (0, 1, 2), `step_blocks`
     (1 .. 4) and `lead` (False, True) force the blocked schedule, None keeps
-    the automatic choice."""
+    the automatic choice.  `infeasible`: None, or an int32 device tensor of
+    one word per molecule that the pass ORs INFEASIBLE_* bits into."""
     if algo not in _ALGOS:
         raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
     return Options(_ALGOS[algo], 1 if directed else 0,
                    AUTO if lookahead is None else int(lookahead),
                    AUTO if step_blocks is None else int(step_blocks),
-                   AUTO if lead is None else int(lead))
+                   AUTO if lead is None else int(lead),
+                   None if infeasible is None else infeasible.data_ptr())
+
+
+def _check_words(W, batch, device):
+    """The infeasibility words of a pass: None, or a contiguous int32 tensor of
+    at least `batch` elements on the pass's device."""
+    import torch
+
+    if W is None:
+        return
+    if not isinstance(W, torch.Tensor) or W.dtype != torch.int32 or not W.is_contiguous():
+        raise ValueError("infeasible must be a contiguous int32 tensor")
+    if W.device != device or W.numel() < batch:
+        raise ValueError(f"infeasible must hold {batch} words on {device}")
 
 
 def _pass(U, L, k_begin, k_end, **kw):
     n, batch = _shape(U, L)
+    _check_words(kw.get("infeasible"), batch, U.device)
     o = options(**kw)
     if n == 0 or batch == 0:
         return
@@ -177,12 +198,13 @@ def _pass(U, L, k_begin, k_end, **kw):
 
 
 def smooth(U, L, algo: str = "auto", check: bool = False, lookahead=None,
-           step_blocks=None, lead=None) -> None:
+           step_blocks=None, lead=None, infeasible=None) -> None:
     """One full smoothing pass on U, L in place (enqueued on the current stream).
 
     check=True first tests the preconditions on the device (dbs_check; this
     synchronises) and raises ValueError naming the violated ones.  lookahead
-    and step_blocks force the blocked schedule (see options())."""
+    and step_blocks force the blocked schedule; infeasible takes the
+    per-molecule words of the infeasibility test (see options())."""
     n, batch = _shape(U, L)
     options(algo, False, lookahead, step_blocks, lead)
     if n == 0 or batch == 0:
@@ -192,7 +214,8 @@ def smooth(U, L, algo: str = "auto", check: bool = False, lookahead=None,
         if bad:
             names = [k for k, v in CHECK_FLAGS.items() if bad & v]
             raise ValueError(f"bounds violate the preconditions: {', '.join(names)}")
-    _pass(U, L, 0, None, algo=algo, lookahead=lookahead, step_blocks=step_blocks, lead=lead)
+    _pass(U, L, 0, None, algo=algo, lookahead=lookahead, step_blocks=step_blocks, lead=lead,
+          infeasible=infeasible)
 
 
 def smooth_profiled(U, L, algo: str = "auto", directed: bool = False, lookahead=None,
@@ -227,25 +250,25 @@ def smooth_round(U, L, k: int) -> None:
 
 
 def smooth_range(U, L, k_begin: int, k_end: int, algo: str = "auto", lookahead=None,
-                 step_blocks=None, lead=None) -> None:
+                 step_blocks=None, lead=None, infeasible=None) -> None:
     """Rounds k_begin..k_end-1 of a pass, in place (see dbs_smooth_range)."""
     _pass(U, L, k_begin, k_end, algo=algo, lookahead=lookahead, step_blocks=step_blocks,
-          lead=lead)
+          lead=lead, infeasible=infeasible)
 
 
 def smooth_directed_range(U, L, k_begin: int, k_end: int, algo: str = "auto", lookahead=None,
-                          step_blocks=None, lead=None) -> None:
+                          step_blocks=None, lead=None, infeasible=None) -> None:
     """smooth_range with directed rounding: sums of upper bounds rounded up,
     differences of lower bounds rounded down (see dbs_smooth_directed_range)."""
     _pass(U, L, k_begin, k_end, algo=algo, directed=True, lookahead=lookahead,
-          step_blocks=step_blocks, lead=lead)
+          step_blocks=step_blocks, lead=lead, infeasible=infeasible)
 
 
 def smooth_directed(U, L, algo: str = "auto", lookahead=None, step_blocks=None,
-                    lead=None) -> None:
+                    lead=None, infeasible=None) -> None:
     """A full pass with directed rounding, in place."""
     _pass(U, L, 0, None, algo=algo, directed=True, lookahead=lookahead, step_blocks=step_blocks,
-          lead=lead)
+          lead=lead, infeasible=infeasible)
 
 
 def tightened(U0, L0, U1, L1):
@@ -337,6 +360,7 @@ def unpack(P):
 
 def _packed_pass(P, k_begin, k_end, **kw):
     n, batch = _shape1(P)
+    _check_words(kw.get("infeasible"), batch, P.device)
     o = options(**kw)
     if n == 0 or batch == 0:
         return
@@ -346,17 +370,17 @@ def _packed_pass(P, k_begin, k_end, **kw):
 
 
 def smooth_packed(P, k_begin: int = 0, k_end=None, algo: str = "auto", lookahead=None,
-                  step_blocks=None, lead=None) -> None:
+                  step_blocks=None, lead=None, infeasible=None) -> None:
     """Rounds k_begin..k_end-1 (default: a full pass) on the packed form, in place."""
     _packed_pass(P, k_begin, k_end, algo=algo, lookahead=lookahead, step_blocks=step_blocks,
-                 lead=lead)
+                 lead=lead, infeasible=infeasible)
 
 
 def smooth_packed_directed(P, k_begin: int = 0, k_end=None, algo: str = "auto", lookahead=None,
-                           step_blocks=None, lead=None) -> None:
+                           step_blocks=None, lead=None, infeasible=None) -> None:
     """smooth_packed with directed rounding, in place."""
     _packed_pass(P, k_begin, k_end, algo=algo, directed=True, lookahead=lookahead,
-                 step_blocks=step_blocks, lead=lead)
+                 step_blocks=step_blocks, lead=lead, infeasible=infeasible)
 
 
 def _check_flags(U, L) -> int:

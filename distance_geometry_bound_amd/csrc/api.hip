@@ -74,6 +74,7 @@ bool read_options(const dbs_options *o, dbs_options *out) {
   if (o->step_blocks != DBS_AUTO && (o->step_blocks < 1 || o->step_blocks > dbs::kMaxStepBlocks))
     return false;
   if (o->lead < DBS_AUTO || o->lead > 1) return false;
+  if (reinterpret_cast<uintptr_t>(o->infeasible) % alignof(uint32_t) != 0) return false;
   *out = *o;
   return true;
 }
@@ -106,6 +107,30 @@ int auto_algo(int64_t n, int64_t batch, bool packed, bool directed, bool aligned
   return aligned ? DBS_ALGO_BLOCKED : DBS_ALGO_PERK;
 }
 
+// The kernels of a pass (arguments already checked).
+int pass_dispatch(float *U, float *L, bool packed, int64_t n, int64_t batch, int64_t k_begin,
+                  int64_t k_end, hipStream_t s, dbs::Prof *prof, const dbs_options &o,
+                  int algo) {
+  if (k_begin == k_end || n == 1) return DBS_OK;
+  const int64_t B = dbs::kBlockRounds;
+  const unsigned flags = (packed ? dbs::kPacked : 0u) | (o.directed ? dbs::kDirected : 0u);
+  switch (algo) {
+    case DBS_ALGO_PERK: {
+      hipError_t e = hipSuccess;
+      for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
+        e = packed ? dbs::launch_round_packed(U, n, batch, k, s, prof, flags)
+                   : dbs::launch_round(U, L, n, batch, k, s, prof, flags);
+      return status_of(e);
+    }
+    case DBS_ALGO_LDS:
+      return status_of(
+          dbs::launch_small(U, L, n, batch, (int)k_begin, (int)k_end, s, prof, flags));
+    default:
+      return status_of(dbs::launch_blocked(U, L, n, batch, k_begin / B, dbs::ceil_div(k_end, B),
+                                           s, prof, flags, sched_of(o), o.infeasible));
+  }
+}
+
 // Rounds k_begin..k_end-1 of a pass on U, L (dense) or on P = U (packed,
 // L ignored), with the given options (AUTO: auto_algo).
 int pass_impl(float *U, float *L, bool packed, int64_t n, int64_t batch, int64_t k_begin,
@@ -129,24 +154,12 @@ int pass_impl(float *U, float *L, bool packed, int64_t n, int64_t batch, int64_t
   if (algo == DBS_ALGO_BLOCKED && !aligned) return DBS_EUNSUPPORTED;
   const int st = device_status();
   if (st != DBS_OK) return st;
-  if (k_begin == k_end || n == 1) return DBS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const unsigned flags = (packed ? dbs::kPacked : 0u) | (o.directed ? dbs::kDirected : 0u);
-  switch (algo) {
-    case DBS_ALGO_PERK: {
-      hipError_t e = hipSuccess;
-      for (int64_t k = k_begin; k < k_end && e == hipSuccess; ++k)
-        e = packed ? dbs::launch_round_packed(U, n, batch, k, s, prof, flags)
-                   : dbs::launch_round(U, L, n, batch, k, s, prof, flags);
-      return status_of(e);
-    }
-    case DBS_ALGO_LDS:
-      return status_of(
-          dbs::launch_small(U, L, n, batch, (int)k_begin, (int)k_end, s, prof, flags));
-    default:
-      return status_of(dbs::launch_blocked(U, L, n, batch, k_begin / B, dbs::ceil_div(k_end, B),
-                                           s, prof, flags, sched_of(o)));
-  }
+  const int ps = pass_dispatch(U, L, packed, n, batch, k_begin, k_end, s, prof, o, algo);
+  if (ps != DBS_OK || !o.infeasible) return ps;
+  // the infeasibility option's test of the output (DBS_INFEASIBLE_END)
+  return status_of(packed ? dbs::launch_infeasible_packed(U, n, batch, o.infeasible, s)
+                          : dbs::launch_infeasible(U, L, n, batch, o.infeasible, s));
 }
 
 int pass_with(float *U, float *L, bool packed, int64_t n, int64_t batch, int64_t k_begin,
@@ -169,6 +182,7 @@ void dbs_options_init(dbs_options *opts) {
   opts->lookahead = DBS_AUTO;
   opts->step_blocks = DBS_AUTO;
   opts->lead = DBS_AUTO;
+  opts->infeasible = nullptr;
 }
 
 int dbs_smooth_opts(float *U, float *L, int64_t n, int64_t batch, int64_t k_begin,

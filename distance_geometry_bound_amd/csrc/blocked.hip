@@ -41,6 +41,7 @@
 #include <mutex>
 #include <utility>
 
+#include "dbs.h"
 #include "dbs_internal.h"
 
 namespace dbs {
@@ -78,6 +79,24 @@ __device__ __forceinline__ void critical_path_priority() { __builtin_amdgcn_s_se
 
 // (k-block tile a, k-block tile b) is fresh under the symmetric schedule
 __device__ __forceinline__ bool fresh(int64_t a, int64_t b) { return a / RATIO <= b / RATIO; }
+
+// The early test of the infeasibility option, where phase 1 has closed a
+// diagonal tile (bZ atoms; thread (ty, tx) holds RT x CT of its cells): a
+// cell with L > U marks the molecule's word with DBS_INFEASIBLE_EARLY.  On
+// consistent bounds L <= U holds at every step (L only rises and U only
+// falls towards the closure), so the mark is never wrong.
+template <int RT, int CT>
+__device__ __forceinline__ void flag_infeasible(uint32_t *word, int bZ, int ty, int tx,
+                                                const float (&u)[RT][CT],
+                                                const float (&l)[RT][CT]) {
+  bool bad = false;
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int q = 0; q < CT; ++q)
+      bad |= ty * RT + r < bZ && tx * CT + q < bZ && l[r][q] > u[r][q];
+  if (bad) atomicOr(word, DBS_INFEASIBLE_EARLY);
+}
 
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ float4 inf4() { return make_float4(kInf, kInf, kInf, kInf); }
@@ -226,7 +245,8 @@ template <bool VEC, bool PK, bool RU, int S>
 __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__restrict__ U,
                                                                    float *__restrict__ L,
                                                                    int64_t n, int64_t batch,
-                                                                   int64_t K) {
+                                                                   int64_t K,
+                                                                   uint32_t *infeasible) {
   constexpr int NT = BK / S;  // threads per side
   __shared__ __align__(16) float dvu[2][BK], dvl[2][BK];  // row m of D
   __shared__ __align__(16) float rvu[2][BK], rvl[2][BK];  // row m of R
@@ -359,6 +379,7 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
       }
     }
 
+    if (infeasible && writes_d) flag_infeasible<S, S>(infeasible + b, bK, ty, tx, du, dl);
 #pragma unroll
     for (int r = 0; r < S; ++r)
 #pragma unroll
@@ -1177,7 +1198,8 @@ template <bool VEC, bool RU, int RT, int CT, int KCH, bool MIR>
 __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_lead(float *__restrict__ U,
                                                                 float *__restrict__ L,
                                                                 int64_t n, int64_t batch,
-                                                                int64_t K, int64_t Z) {
+                                                                int64_t K, int64_t Z,
+                                                                uint32_t *infeasible) {
   using Q = Quad<VEC, RU, RT, CT, KCH>;
   __shared__ union {
     typename Q::Stage sm;
@@ -1202,6 +1224,7 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_lead(float *__restric
       Q::load(Ub, Lb, n, z0, z0, bZ, bZ, ty, tx, u, l);
       if (K >= 0) Q::relax(sm, Ub, Lb, n, k0, bK, z0, z0, bZ, bZ, tid, ty, tx, u, l);
       close_tile<RU>(dv, bZ, ty, tx, u, l);
+      if (infeasible) flag_infeasible<RT, CT>(infeasible + b, bZ, ty, tx, u, l);
       Q::store(Ub, Lb, n, z0, z0, bZ, bZ, tid, u, l);
       __syncthreads();
     }
@@ -1561,7 +1584,8 @@ __global__ __launch_bounds__(kThreads) void k_quads_packed(float *__restrict__ P
 // of each diagonal tile; the closure workgroup's tile is a diagonal block).
 template <bool VEC, bool RU>
 __global__ __launch_bounds__(kThreads) void k_lead_packed(float *__restrict__ P, int64_t n,
-                                                          int64_t batch, int64_t K, int64_t Z) {
+                                                          int64_t batch, int64_t K, int64_t Z,
+                                                          uint32_t *infeasible) {
   using Q = PQuad<VEC, RU>;
   __shared__ typename Q::Stage sm;
   __shared__ float tr[BK][BK + 1];
@@ -1582,6 +1606,7 @@ __global__ __launch_bounds__(kThreads) void k_lead_packed(float *__restrict__ P,
       Q::load(Pb, n, z0, z0, bZ, bZ, ty, tx, true, u, l);
       if (K >= 0) Q::relax(sm, Pb, n, k0, bK, K, Z, Z, z0, z0, tid, ty, tx, u, l);
       close_tile<RU>(dv, bZ, ty, tx, u, l);
+      if (infeasible) flag_infeasible<4, 4>(infeasible + b, bZ, ty, tx, u, l);
       Q::store(Pb, n, z0, z0, bZ, bZ, tid, true, u, l, tr);
       __syncthreads();
     }
@@ -1756,19 +1781,20 @@ int lookahead_bands(int64_t n, int64_t batch, const Sched &sched) {
 namespace {
 hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
                              hipStream_t s, Prof *prof, unsigned flags, const Sched &sched,
-                             bool half);
+                             bool half, uint32_t *infeasible);
 }  // namespace
 
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
-                          hipStream_t s, Prof *prof, unsigned flags, const Sched &sched) {
-  return launch_blocked_on(U, L, n, batch, K0, K1, s, prof, flags, sched, false);
+                          hipStream_t s, Prof *prof, unsigned flags, const Sched &sched,
+                          uint32_t *infeasible) {
+  return launch_blocked_on(U, L, n, batch, K0, K1, s, prof, flags, sched, false, infeasible);
 }
 
 namespace {
 // `half`: one half of a split batch, run on one stream without look-ahead.
 hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
                              hipStream_t s, Prof *prof, unsigned flags, const Sched &sched,
-                             bool half) {
+                             bool half, uint32_t *infeasible) {
   static_assert(BK == kBlockRounds, "k-block size");
   const int64_t TB = ceil_div(n, BK);    // k-blocks
   if (K1 > TB) K1 = TB;
@@ -1827,10 +1853,11 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
     const int64_t b1 = batch / 2;
     hipError_t e = hipEventRecord(lane->start(), s);
     if (e == hipSuccess) e = hipStreamWaitEvent(lane->side, lane->start(), 0);
-    if (e == hipSuccess) e = launch_blocked_on(U, L, n, b1, K0, K1, s, prof, flags, sched, true);
+    if (e == hipSuccess)
+      e = launch_blocked_on(U, L, n, b1, K0, K1, s, prof, flags, sched, true, infeasible);
     if (e == hipSuccess)
       e = launch_blocked_on(U + b1 * nn, L + b1 * nn, n, batch - b1, K0, K1, lane->side, prof,
-                            flags, sched, true);
+                            flags, sched, true, infeasible ? infeasible + b1 : nullptr);
     if (e == hipSuccess) e = hipEventRecord(lane->bulk(0), lane->side);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, lane->bulk(0), 0);
     return e;
@@ -1866,9 +1893,10 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
     const unsigned gq = (unsigned)(1 + (K >= 0 ? 4 * pairs : 0));
     const int kind = K >= 0 ? kProfTiles : kProfSmall;
     if (packed)
-      return launch(prof, kind, lead_packed, dim3(mx, gq), dim3(kThreads), st, U, n, batch, K, Z);
+      return launch(prof, kind, lead_packed, dim3(mx, gq), dim3(kThreads), st, U, n, batch, K, Z,
+                    infeasible);
     return launch(prof, kind, last ? lead_last : lead_kernel, dim3(mx, gq), dim3(lead_block), st,
-                  U, L, n, batch, K, Z);
+                  U, L, n, batch, K, Z, infeasible);
   };
   auto product = [&](int64_t K, hipStream_t st) -> hipError_t {
     return launch(prof, kProfPanel, product_kernel, dim3((unsigned)(TB - 1), gy), dim3(kThreads),
@@ -1919,7 +1947,7 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
       return r == hipSuccess ? product(K, st) : r;
     }
     return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(panel_block), st, U,
-                  L, n, batch, K);
+                  L, n, batch, K, infeasible);
   };
   // The pass advances by steps of W k-blocks: step t holds the blocks
   // [lo(t), hi(t)).  Two steps ahead the bulk takes several blocks per

@@ -93,7 +93,74 @@ __global__ __launch_bounds__(kThreads) void k_check_packed(const float *__restri
   if (f) atomicOr(flags, f);
 }
 
+// The infeasibility option's test of a pass's output (dense): words[b] gets
+// DBS_INFEASIBLE_END when a cell of molecule b has L > U.  grid.y =
+// molecules; each workgroup ORs the result of its cells once.
+__global__ __launch_bounds__(kThreads) void k_infeasible(const float *__restrict__ U,
+                                                         const float *__restrict__ L, int64_t n,
+                                                         int64_t batch,
+                                                         uint32_t *__restrict__ words) {
+  const int64_t nn = n * n;
+  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    const float *Ub = U + b * nn, *Lb = L + b * nn;
+    int bad = 0;
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < nn;
+         e += (int64_t)gridDim.x * kThreads)
+      bad |= Lb[e] > Ub[e];
+    if (__syncthreads_or(bad) && threadIdx.x == 0) atomicOr(&words[b], DBS_INFEASIBLE_END);
+  }
+}
+
+// The same on the packed buffer: for i < j, L = P[j][i] against U = P[i][j].
+// The tile pairs (I <= J) of PT x PT tiles are dealt to the workgroups of
+// grid.x; a workgroup reads tile (J, I) transposed through LDS, so that both
+// reads are row-contiguous.
+__global__ __launch_bounds__(kThreads) void k_infeasible_packed(const float *__restrict__ P,
+                                                                int64_t n, int64_t batch,
+                                                                uint32_t *__restrict__ words) {
+  __shared__ float t[PT][PT + 1];
+  const int tid = threadIdx.x;
+  const int64_t T = ceil_div(n, PT), pairs = T * (T + 1) / 2, nn = n * n;
+  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    const float *Pb = P + b * nn;
+    int bad = 0;
+    for (int64_t p = blockIdx.x; p < pairs; p += gridDim.x) {
+      const int64_t J = tri_col(p), I = p - J * (J + 1) / 2;
+      const int64_t i0 = I * PT, j0 = J * PT;
+      for (int e = tid; e < PT * PT; e += kThreads) {
+        const int r = e / PT, c = e % PT;
+        const int64_t gi = j0 + r, gj = i0 + c;  // P[j0 + r][i0 + c]
+        if (gi < n && gj < n) t[r][c] = Pb[gi * n + gj];
+      }
+      __syncthreads();
+      for (int e = tid; e < PT * PT; e += kThreads) {
+        const int r = e / PT, c = e % PT;
+        const int64_t i = i0 + r, j = j0 + c;
+        if (i < j && j < n) bad |= t[c][r] > Pb[i * n + j];  // L(i,j) > U(i,j)
+      }
+      __syncthreads();
+    }
+    if (__syncthreads_or(bad) && tid == 0) atomicOr(&words[b], DBS_INFEASIBLE_END);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_infeasible(const float *U, const float *L, int64_t n, int64_t batch,
+                             uint32_t *words, hipStream_t s) {
+  int64_t blocks = ceil_div(n * n, kThreads);
+  if (blocks > 1024) blocks = 1024;
+  const dim3 g((unsigned)blocks, (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ));
+  return launch(nullptr, 0, k_infeasible, g, dim3(kThreads), s, U, L, n, batch, words);
+}
+
+hipError_t launch_infeasible_packed(const float *P, int64_t n, int64_t batch, uint32_t *words,
+                                    hipStream_t s) {
+  const int64_t T = ceil_div(n, PT), pairs = T * (T + 1) / 2;
+  const dim3 g((unsigned)(pairs < 1024 ? pairs : 1024),
+               (unsigned)(batch < kMaxGridYZ ? batch : kMaxGridYZ));
+  return launch(nullptr, 0, k_infeasible_packed, g, dim3(kThreads), s, P, n, batch, words);
+}
 
 hipError_t launch_check_packed(const float *P, int64_t n, int64_t batch, uint32_t *flags,
                                hipStream_t s) {

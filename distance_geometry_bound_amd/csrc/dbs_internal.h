@@ -204,9 +204,19 @@ struct Sched {
   int lead = -1;
 };
 // k-blocks K0..K1-1 of the blocked pass (rounds 64*K0 .. min(64*K1, n)-1)
+// `infeasible` (may be null): per-molecule words for the early test of the
+// infeasibility option (DBS_INFEASIBLE_EARLY, where phase 1 closes a
+// diagonal tile).
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
                           hipStream_t s, Prof *prof = nullptr, unsigned flags = 0,
-                          const Sched &sched = Sched());
+                          const Sched &sched = Sched(), uint32_t *infeasible = nullptr);
+// The infeasibility option's test of a pass's output: words[b] |=
+// DBS_INFEASIBLE_END where molecule b has a cell with L > U (dense U, L, or
+// the packed buffer P).
+hipError_t launch_infeasible(const float *U, const float *L, int64_t n, int64_t batch,
+                             uint32_t *words, hipStream_t s);
+hipError_t launch_infeasible_packed(const float *P, int64_t n, int64_t batch, uint32_t *words,
+                                    hipStream_t s);
 constexpr int kBlockRounds = 64;
 // Look-ahead depth of the blocked pass: steps it updates ahead on its second
 // stream (0, 1 or 2; at 2 a step is several k-blocks).

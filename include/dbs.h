@@ -98,18 +98,36 @@ extern "C" {
  *   lead         DBS_AUTO (default), 0 or 1: where a blocked pass runs on the
  *                caller's stream alone in steps of one k-block, 1 takes the
  *                lead schedule and 0 the plain one (see dbs_schedule).
+ *   infeasible   NULL (default), or a device pointer to `batch` uint32 words,
+ *                one per molecule, owned by the caller (who clears them):
+ *                the pass ORs DBS_INFEASIBLE_* bits into the word of a
+ *                molecule whose bounds it finds inconsistent, that is, with
+ *                L[i,j] > U[i,j] for some pair (the notes' §2: L and U only
+ *                approach each other, so on consistent bounds L <= U holds
+ *                at every step, and on inconsistent ones the output of a
+ *                whole pass has L > U somewhere):
+ *     DBS_INFEASIBLE_EARLY  seen during a blocked pass, where the diagonal
+ *                tile of a k-block is closed (phase 1): some cell of that
+ *                tile has L > U after the rounds of its k-block;
+ *     DBS_INFEASIBLE_END    seen in the output of the call: some cell has
+ *                L > U (a test of every cell, enqueued after the pass).
+ *                For a whole pass it is set exactly for the inconsistent
+ *                molecules; EARLY is never set without END.
  * The schedule fields only reorder independent cell updates: every value
  * gives the same results.  They exist for tests and tuning.  Any other value
  * of a field makes the call return DBS_EINVAL.  The options are read during
  * the call; the library keeps no pointer to them.
  */
 #define DBS_AUTO (-1)
+#define DBS_INFEASIBLE_EARLY 1u
+#define DBS_INFEASIBLE_END 2u
 typedef struct dbs_options {
   int32_t algo;
   int32_t directed;
   int32_t lookahead;
   int32_t step_blocks;
   int32_t lead;
+  uint32_t *infeasible;
 } dbs_options;
 
 void dbs_options_init(dbs_options *opts);

@@ -3,6 +3,7 @@ arguments on the host before touching a device (CPU only)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -100,14 +101,15 @@ def test_options_are_validated_on_the_host(no_gpu):
     L = dgb.lib()
     byref = ctypes.byref
     good = _lib.Options(0, 0, -1, -1, -1)
-    d = _lib.Options(9, 9, 9, 9, 9)
+    d = _lib.Options(9, 9, 9, 9, 9, A)
     L.dbs_options_init(byref(d))
     assert (d.algo, d.directed, d.lookahead, d.step_blocks, d.lead) == (0, 0, -1, -1, -1)
+    assert d.infeasible is None
     for bad in (_lib.Options(4, 0, -1, -1, -1), _lib.Options(-1, 0, -1, -1, -1),
                 _lib.Options(0, 2, -1, -1, -1), _lib.Options(0, 0, 3, -1, -1),
                 _lib.Options(0, 0, -2, -1, -1), _lib.Options(0, 0, -1, 0, -1),
                 _lib.Options(0, 0, -1, 5, -1), _lib.Options(0, 0, -1, -1, 2),
-                _lib.Options(0, 0, -1, -1, -2)):
+                _lib.Options(0, 0, -1, -1, -2), _lib.Options(0, 0, -1, -1, -1, A + 2)):
         assert L.dbs_smooth_opts(A, B, 8, 1, 0, 8, None, byref(bad)) == _lib.DBS_EINVAL
         assert L.dbs_smooth_packed_opts(A, 8, 1, 0, 8, None, byref(bad)) == _lib.DBS_EINVAL
         assert L.dbs_schedule(8, 1, byref(bad), None, None, None) == _lib.DBS_EINVAL
@@ -125,6 +127,22 @@ def test_options_are_validated_on_the_host(no_gpu):
     ms = (ctypes.c_double * len(_lib.PROF_KINDS))()
     assert L.dbs_smooth_profiled(A, B, 8, 1, None, byref(good), None, ms) == _lib.DBS_EINVAL
     assert L.dbs_smooth_profiled(A, B, 8, 1, None, byref(d), counts, None) == _lib.DBS_EINVAL
+
+
+def test_options_layout_matches_the_header(tmp_path):
+    # the binding's struct dbs_options against the C compiler's
+    src = tmp_path / "layout.c"
+    src.write_text('#include "dbs.h"\n#include <stddef.h>\n#include <stdio.h>\n'
+                   'int main(void) { printf("%zu %zu %zu\\n", sizeof(dbs_options), '
+                   'offsetof(dbs_options, lead), offsetof(dbs_options, infeasible)); '
+                   'return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-o", str(exe)], check=True)
+    got = tuple(int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                               text=True).stdout.split())
+    assert got == (ctypes.sizeof(_lib.Options), _lib.Options.lead.offset,
+                   _lib.Options.infeasible.offset)
 
 
 def test_no_device_is_reported(no_gpu):
