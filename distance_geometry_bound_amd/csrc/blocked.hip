@@ -199,17 +199,20 @@ __device__ __forceinline__ void packed_block_load(const float *P, int64_t n, int
 // The inverse of packed_block_load (the diagonal of a diagonal block is not
 // written: its single slot holds U[i][i]).  On a diagonal block cells (a, c)
 // and (c, a) write the same two slots with equal values.
+// `bad` (may be null) accumulates whether a stored cell has L > U.
 template <int S = 4>
 __device__ __forceinline__ void packed_block_store(float *P, int64_t n, int64_t r0, int64_t c0,
                                                    int rows, int cols, int ty, int tx,
                                                    const float (&u)[S][S],
-                                                   const float (&l)[S][S]) {
+                                                   const float (&l)[S][S],
+                                                   bool *bad = nullptr) {
 #pragma unroll
   for (int r = 0; r < S; ++r)
 #pragma unroll
     for (int q = 0; q < S; ++q) {
       const int a = ty * S + r, c = tx * S + q;
       if (a >= rows || c >= cols || (r0 == c0 && a == c)) continue;
+      if (bad) *bad |= l[r][q] > u[r][q];
       const bool upper = r0 < c0 || (r0 == c0 && a < c);
       P[(r0 + a) * n + c0 + c] = upper ? u[r][q] : l[r][q];
       P[(c0 + c) * n + r0 + a] = upper ? l[r][q] : u[r][q];
@@ -379,7 +382,6 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
       }
     }
 
-    if (infeasible && writes_d) flag_infeasible<S, S>(infeasible + b, bK, ty, tx, du, dl);
 #pragma unroll
     for (int r = 0; r < S; ++r)
 #pragma unroll
@@ -402,8 +404,12 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
       } else {
         packed_block_store<S>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
       }
-      if (writes_d) packed_block_store<S>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
     }
+    // the early infeasibility test (as in flag_infeasible), on the cells of D
+    // as they are stored, which keeps the test within the store's registers
+    bool bad = false;
+    if (PK && writes_d)
+      packed_block_store<S>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl, infeasible ? &bad : nullptr);
 #pragma unroll
     for (int r = 0; r < S; ++r)
 #pragma unroll
@@ -418,6 +424,7 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
           }
         }
         if (!PK && writes_d && a < bK && c < bK) {
+          bad |= infeasible && dl[r][q] > du[r][q];
           Ub[(k0 + a) * n + k0 + c] = du[r][q];
           Lb[(k0 + a) * n + k0 + c] = dl[r][q];
         }
@@ -446,6 +453,7 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
           }
         }
     }
+    if (bad) atomicOr(infeasible + b, DBS_INFEASIBLE_EARLY);
     __syncthreads();  // LDS reuse by the next molecule
   }
 }
