@@ -69,6 +69,16 @@ constexpr int64_t kAheadTiles = 256;
 // Above this many phase 1-2 workgroups the panel launch fills the chip by
 // itself, and running it beside the bulk gains nothing (one per CU).
 constexpr int64_t kPanelFill = 256;
+// Between these many phase-3 tiles (times molecules) a one-stream pass takes
+// the lead schedule even where its phase 1-2 launch would not fill the chip:
+// there a bulk launch is long enough to hide the closure of the next
+// diagonal tile, and the product is shorter than a phase 1-2 launch.
+// Measured (median of 10 passes, lead against the plain or one-step
+// schedule): n1792 (105 tiles) 1.10x, n2048 (136) 0.93x, n3072 (300) 0.81x,
+// n4096 (528) 1.02x; 8 x n500 (80) 1.05x, 16 x n500 (160) 0.94x,
+// 32 x n500 (320) 0.76x; 2 x n1024 (72) 1.11x, 8 x n1024 (288) 0.83x;
+// 32 x n256 (96) 1.06x, 64 x n256 (192) 0.95x.
+constexpr int64_t kLeadTilesMin = 128, kLeadTilesMax = 512;
 constexpr int kThreads = 256;
 
 // The side-stream kernels (strips, and phases 1-2 of the next blocks) are
@@ -99,9 +109,6 @@ __device__ __forceinline__ void flag_infeasible(uint32_t *word, int bZ, int ty, 
 }
 
 // ---------------------------------------------------------------- helpers
-__device__ __forceinline__ float4 inf4() { return make_float4(kInf, kInf, kInf, kInf); }
-__device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-
 // Four consecutive entries p[0..3]; entry q is used only if q < cnt, else the
 // neutral value `fill`.  VEC: p is 16-byte aligned and cnt is 0 or >= 4.
 // Branch-free: an entry that is not used is read from `safe` (any valid,
@@ -528,22 +535,26 @@ __device__ __forceinline__ void packed_half_store(const HalfLoad &h, bool right,
 }
 
 // ---------------------------------------------------------------- block write-back
-// v[r][q] of thread (ty, tx) (a 4x4 cell tile of a BK x BK block) to
-// P[r0 + 4ty + r][c0 + 4tx + q], rows < rows and columns < cols: one float4
-// per row where the row segment is whole (VEC: 16-byte aligned).
-template <bool VEC>
+// v[r][q] of thread (ty, tx) (a 4 x CT cell tile of a BK x BK block) to
+// P[r0 + 4ty + r][c0 + CT*tx + q], rows < rows and columns < cols: one
+// CT-float vector per row where the row segment is whole (VEC: aligned).
+template <bool VEC, int CT = 4>
 __device__ __forceinline__ void store_rows(float *P, int64_t n, int64_t r0, int64_t c0, int rows,
-                                           int cols, int ty, int tx, const float (&v)[4][4]) {
+                                           int cols, int ty, int tx, const float (&v)[4][CT]) {
+  static_assert(CT == 4 || CT == 2, "4 or 2 columns");
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int a = ty * 4 + r, c = tx * 4;
+    const int a = ty * 4 + r, c = tx * CT;
     if (a >= rows) continue;
     float *p = P + (r0 + a) * n + c0 + c;
-    if (VEC && c + 3 < cols) {
-      *reinterpret_cast<float4 *>(p) = make_float4(v[r][0], v[r][1], v[r][2], v[r][3]);
+    if (VEC && c + CT - 1 < cols) {
+      if constexpr (CT == 4)
+        *reinterpret_cast<float4 *>(p) = make_float4(v[r][0], v[r][1], v[r][2], v[r][3]);
+      else
+        *reinterpret_cast<float2 *>(p) = make_float2(v[r][0], v[r][1]);
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < CT; ++q)
         if (c + q < cols) p[q] = v[r][q];
     }
   }
@@ -565,26 +576,28 @@ __device__ __forceinline__ void store_packed_diagonal(float *P, int64_t n, int64
   store_rows<VEC>(P, n, r0, r0, rows, rows, ty, tx, v);
 }
 
-// The same cells to their transposed position P[c0 + 4tx + q][r0 + 4ty + r].
-// The block is turned around in the LDS tile `tr` first (stride BK + 1: the
-// writes meet at most 8 threads on a bank, the reads 2), so that the global
-// writes are row segments, 16 threads to a 256-byte row.  Contains barriers:
-// every thread of the workgroup must call it.
-template <bool VEC>
+// The same cells to their transposed position P[c0 + CT*tx + q][r0 + 4ty + r]
+// (the workgroup: (BK / 4) x (BK / CT) threads).  The block is turned around
+// in the LDS tile `tr` first (stride BK + 1: the writes meet at most 8
+// threads on a bank, the reads 2), so that the global writes are row
+// segments, 16 threads to a 256-byte row.  Contains barriers: every thread of
+// the workgroup must call it.
+template <bool VEC, int CT = 4>
 __device__ __forceinline__ void store_transposed(float *P, int64_t n, int64_t r0, int64_t c0,
                                                  int rows, int cols, int ty, int tx,
-                                                 const float (&v)[4][4],
+                                                 const float (&v)[4][CT],
                                                  float (*tr)[BK + 1]) {
+  constexpr int NTH = (BK / 4) * (BK / CT);
   __syncthreads();  // tr free (a previous call may still be reading it)
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) tr[tx * 4 + q][ty * 4 + r] = v[r][q];
+    for (int q = 0; q < CT; ++q) tr[tx * CT + q][ty * 4 + r] = v[r][q];
   __syncthreads();
-  const int tid = ty * (BK / 4) + tx;
+  const int tid = ty * (BK / CT) + tx;
 #pragma unroll
-  for (int it = 0; it < BK * BK / 4 / kThreads; ++it) {
-    const int e = tid + it * kThreads, c = e / (BK / 4), a = (e % (BK / 4)) * 4;
+  for (int it = 0; it < BK * BK / 4 / NTH; ++it) {
+    const int e = tid + it * NTH, c = e / (BK / 4), a = (e % (BK / 4)) * 4;
     if (c >= cols) continue;
     float *p = P + (c0 + c) * n + r0 + a;
     if (VEC && a + 3 < rows) {
@@ -1278,10 +1291,21 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_lead(float *__restric
 // every thread relaxes its 4x4 cells over the atoms as the bulk does.  R is
 // read from its fresh orientation and written in both (dense), or as its U
 // and L slots (packed).
-template <bool VEC, bool PK, bool RU>
-__global__ __launch_bounds__(kThreads) void k_product(float *__restrict__ U,
-                                                      float *__restrict__ L, int64_t n,
-                                                      int64_t batch, int64_t K) {
+// Thread (ty, tx) owns 4 x CT cells of R.  CT = 4 (256 threads) runs beside
+// the bulk (the two-step look-ahead); CT = 2 (512 threads, dense layout)
+// where the launch has the chip to itself: D* and R take 64 KB of LDS, so a
+// compute unit holds two workgroups, and 4x2 cells give its SIMDs four waves
+// each instead of two to issue from.
+template <int CT>
+constexpr int product_threads() { return (BK / 4) * (BK / CT); }
+
+template <bool VEC, bool PK, bool RU, int CT>
+__global__ __launch_bounds__(product_threads<CT>()) void k_product(float *__restrict__ U,
+                                                                   float *__restrict__ L,
+                                                                   int64_t n, int64_t batch,
+                                                                   int64_t K) {
+  static_assert(CT == 4 || (CT == 2 && !PK), "4x4 cells, or 4x2 on the dense layout");
+  constexpr int NTX = BK / CT, NTH = product_threads<CT>();
   __shared__ __align__(16) float su[2][BK][BK];  // D* rows: su[.][m][a] = U/L D*[m][a]
   __shared__ __align__(16) float sr[2][BK][BK];  // R rows:  sr[.][m][c] = U/L R[m][c]
   float(*tr)[BK + 1] = reinterpret_cast<float(*)[BK + 1]>(&su[0][0][0]);  // write-back
@@ -1290,7 +1314,7 @@ __global__ __launch_bounds__(kThreads) void k_product(float *__restrict__ U,
   // beside the bulk (two steps ahead) its waves take issue priority, as the
   // phase 1-2 kernel's do (n12288 pass 67.15-67.17 ms against 67.6-67.7)
   critical_path_priority();
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int tid = threadIdx.x, ty = tid / NTX, tx = tid % NTX;
   int64_t J = blockIdx.x;
   if (J >= K) ++J;
   const int64_t k0 = K * BK, j0 = J * BK;
@@ -1305,7 +1329,7 @@ __global__ __launch_bounds__(kThreads) void k_product(float *__restrict__ U,
 
     // D* straight into LDS, one row segment of four at a time (rows of the
     // dense diagonal tile; the packed one through its logical cells)
-    if (PK) {
+    if constexpr (PK) {
       float du[4][4], dl[4][4];
       packed_block_load<VEC>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
 #pragma unroll
@@ -1317,46 +1341,75 @@ __global__ __launch_bounds__(kThreads) void k_product(float *__restrict__ U,
       }
     } else {
 #pragma unroll
-      for (int it = 0; it < BK * BK / 4 / kThreads; ++it) {
-        const int e = tid + it * kThreads, a = e / (BK / 4), c = (e % (BK / 4)) * 4;
+      for (int it = 0; it < BK * BK / 4 / NTH; ++it) {
+        const int e = tid + it * NTH, a = e / (BK / 4), c = (e % (BK / 4)) * 4;
         const int64_t g = (k0 + a) * n + k0 + c;
         const int cnt = a < bK ? clamp4(bK - c) : 0;
         *reinterpret_cast<float4 *>(&su[0][a][c]) = load4<VEC>(Ub + g, cnt, kInf, Ub);
         *reinterpret_cast<float4 *>(&su[1][a][c]) = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
       }
     }
-    // this thread's 4x4 cells of R, the logical cells (k0 + 4ty + r, j0 + 4tx + q)
-    float u[4][4], l[4][4];
-    if (PK) {
+    // this thread's 4 x CT cells of R, the logical cells (k0 + 4ty + r, j0 + CT*tx + q)
+    float u[4][CT], l[4][CT];
+    if constexpr (PK) {
       packed_block_load<VEC>(Ub, n, k0, j0, bK, bJ, ty, tx, u, l);
-    } else {
-      float4 yu[4], yl[4];
+    } else if (rowor) {  // row segments M[k0 + a][j0 + c ..]
+      Seg<CT> yu[4], yl[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int cnt = rowor ? (ty * 4 + r < bK ? clamp4(bJ - tx * 4) : 0)
-                              : (tx * 4 + r < bJ ? clamp4(bK - ty * 4) : 0);
-        const int64_t g = rowor ? (k0 + ty * 4 + r) * n + j0 + tx * 4
-                                : (j0 + tx * 4 + r) * n + k0 + ty * 4;
-        yu[r] = load4<VEC>(Ub + g, cnt, kInf, Ub);
-        yl[r] = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+        const int64_t left = ty * 4 + r < bK ? bJ - tx * CT : 0;
+        const int64_t g = (k0 + ty * 4 + r) * n + j0 + tx * CT;
+        yu[r] = load_seg<VEC, CT>(Ub + g, left, kInf, Ub);
+        yl[r] = load_seg<VEC, CT>(Lb + g, left, 0.0f, Lb);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float bu[4] = {yu[r].x, yu[r].y, yu[r].z, yu[r].w};
-        const float bl[4] = {yl[r].x, yl[r].y, yl[r].z, yl[r].w};
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          (rowor ? u[r][q] : u[q][r]) = bu[q];
-          (rowor ? l[r][q] : l[q][r]) = bl[q];
+        for (int q = 0; q < CT; ++q) {
+          u[r][q] = yu[r].v[q];
+          l[r][q] = yl[r].v[q];
+        }
+    } else {  // column segments M[j0 + c][k0 + a ..] of the other orientation
+      float4 yu[CT], yl[CT];
+#pragma unroll
+      for (int q = 0; q < CT; ++q) {
+        const int c = tx * CT + q;
+        const int cnt = c < bJ ? clamp4(bK - ty * 4) : 0;
+        const int64_t g = (j0 + c) * n + k0 + ty * 4;
+        yu[q] = load4<VEC>(Ub + g, cnt, kInf, Ub);
+        yl[q] = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+      }
+#pragma unroll
+      for (int q = 0; q < CT; ++q) {
+        const float bu[4] = {yu[q].x, yu[q].y, yu[q].z, yu[q].w};
+        const float bl[4] = {yl[q].x, yl[q].y, yl[q].z, yl[q].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u[r][q] = bu[r];
+          l[r][q] = bl[r];
         }
       }
     }
+    // CT consecutive floats of an LDS row, as one vector
+    auto put = [](float *p, const float *v) {
+      if constexpr (CT == 4)
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+      else
+        *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
+    };
+    auto get = [](const float *p, float *v) {
+      if constexpr (CT == 4) {
+        const float4 x = *reinterpret_cast<const float4 *>(p);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      } else {
+        const float2 x = *reinterpret_cast<const float2 *>(p);
+        v[0] = x.x; v[1] = x.y;
+      }
+    };
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<float4 *>(&sr[0][ty * 4 + r][tx * 4]) =
-          make_float4(u[r][0], u[r][1], u[r][2], u[r][3]);
-      *reinterpret_cast<float4 *>(&sr[1][ty * 4 + r][tx * 4]) =
-          make_float4(l[r][0], l[r][1], l[r][2], l[r][3]);
+      put(&sr[0][ty * 4 + r][tx * CT], u[r]);
+      put(&sr[1][ty * 4 + r][tx * CT], l[r]);
     }
     __syncthreads();
 
@@ -1366,34 +1419,33 @@ __global__ __launch_bounds__(kThreads) void k_product(float *__restrict__ U,
     for (int m = 0; m < bK; m += 2) {
       const float4 a0v = *reinterpret_cast<const float4 *>(&su[0][m][ty * 4]);
       const float4 b0v = *reinterpret_cast<const float4 *>(&su[1][m][ty * 4]);
-      const float4 c0v = *reinterpret_cast<const float4 *>(&sr[0][m][tx * 4]);
-      const float4 d0v = *reinterpret_cast<const float4 *>(&sr[1][m][tx * 4]);
       const float4 a1v = *reinterpret_cast<const float4 *>(&su[0][m + 1][ty * 4]);
       const float4 b1v = *reinterpret_cast<const float4 *>(&su[1][m + 1][ty * 4]);
-      const float4 c1v = *reinterpret_cast<const float4 *>(&sr[0][m + 1][tx * 4]);
-      const float4 d1v = *reinterpret_cast<const float4 *>(&sr[1][m + 1][tx * 4]);
+      float ru0[CT], rl0[CT], ru1[CT], rl1[CT];
+      get(&sr[0][m][tx * CT], ru0);
+      get(&sr[1][m][tx * CT], rl0);
+      get(&sr[0][m + 1][tx * CT], ru1);
+      get(&sr[1][m + 1][tx * CT], rl1);
       const float cu0[4] = {a0v.x, a0v.y, a0v.z, a0v.w}, cl0[4] = {b0v.x, b0v.y, b0v.z, b0v.w};
-      const float ru0[4] = {c0v.x, c0v.y, c0v.z, c0v.w}, rl0[4] = {d0v.x, d0v.y, d0v.z, d0v.w};
       const float cu1[4] = {a1v.x, a1v.y, a1v.z, a1v.w}, cl1[4] = {b1v.x, b1v.y, b1v.z, b1v.w};
-      const float ru1[4] = {c1v.x, c1v.y, c1v.z, c1v.w}, rl1[4] = {d1v.x, d1v.y, d1v.z, d1v.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < CT; ++q)
           relax2<RU>(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
                      rl1[q]);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) l[r][q] = lower_out<RU>(l[r][q]);
+      for (int q = 0; q < CT; ++q) l[r][q] = lower_out<RU>(l[r][q]);
 
     // write-back (tr aliases su, free once every thread has left the loop,
     // which store_transposed's first barrier ensures)
     int tw = tid;
     asm volatile("" : "+v"(tw));
-    const int wy = tw >> 4, wx = tw & 15;
-    if (PK) {
+    const int wy = tw / NTX, wx = tw % NTX;
+    if constexpr (PK) {
       // R lies on one side of the diagonal: its row slots hold U right of
       // it, L left of it
       if (k0 < j0) {
@@ -1404,10 +1456,10 @@ __global__ __launch_bounds__(kThreads) void k_product(float *__restrict__ U,
         store_transposed<VEC>(Ub, n, k0, j0, bK, bJ, wy, wx, u, tr);
       }
     } else {
-      store_rows<VEC>(Ub, n, k0, j0, bK, bJ, wy, wx, u);
-      store_rows<VEC>(Lb, n, k0, j0, bK, bJ, wy, wx, l);
-      store_transposed<VEC>(Ub, n, k0, j0, bK, bJ, wy, wx, u, tr);
-      store_transposed<VEC>(Lb, n, k0, j0, bK, bJ, wy, wx, l, tr);
+      store_rows<VEC, CT>(Ub, n, k0, j0, bK, bJ, wy, wx, u);
+      store_rows<VEC, CT>(Lb, n, k0, j0, bK, bJ, wy, wx, l);
+      store_transposed<VEC, CT>(Ub, n, k0, j0, bK, bJ, wy, wx, u, tr);
+      store_transposed<VEC, CT>(Lb, n, k0, j0, bK, bJ, wy, wx, l, tr);
     }
     __syncthreads();  // LDS reuse by the next molecule
   }
@@ -1745,6 +1797,15 @@ int step_blocks(int64_t n, int64_t batch, const Sched &sched) {
   return tiles >= kStep4Tiles ? 4 : tiles >= kStep3Tiles ? 3 : 2;
 }
 
+// The automatic choice of the lead schedule (for a one-stream pass of one
+// k-block per step).
+bool auto_lead(int64_t n, int64_t batch) {
+  const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
+  const int64_t tiles = T * (T + 1) / 2 * batch;
+  return (batch >= 2 && (TB - 1) * batch > kPanelFill) ||
+         (tiles >= kLeadTilesMin && tiles < kLeadTilesMax);
+}
+
 bool lead_schedule(int64_t n, int64_t batch, const Sched &sched) {
   const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
   // a lead launch's quadrants (and its closure) are one grid dimension
@@ -1752,7 +1813,7 @@ bool lead_schedule(int64_t n, int64_t batch, const Sched &sched) {
       step_blocks(n, batch, sched) != 1)
     return false;
   if (sched.lead >= 0) return sched.lead == 1;
-  return batch >= 2 && (TB - 1) * batch > kPanelFill;
+  return auto_lead(n, batch);
 }
 
 int lookahead_bands(int64_t n, int64_t batch, const Sched &sched) {
@@ -1761,6 +1822,9 @@ int lookahead_bands(int64_t n, int64_t batch, const Sched &sched) {
   if (sched.lookahead >= 0) return sched.lookahead;
   const int64_t tiles = T * (T + 1) / 2 * batch;
   if (tiles >= kDeepTiles) return 2;
+  // the lead schedule runs on one stream
+  if (sched.step_blocks <= 1 && (sched.lead == 1 || (sched.lead < 0 && auto_lead(n, batch))))
+    return 0;
   // where one phase 1-2 launch fills the chip the batch splits over the two
   // streams instead (launch_blocked_on), in both layouts
   if (tiles < kAheadTiles || (TB - 1) * batch > kPanelFill) return 0;
@@ -1887,11 +1951,17 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
 #undef DBS_LEAD
   auto lead_packed = ru ? (vec ? k_lead_packed<true, true> : k_lead_packed<false, true>)
                         : (vec ? k_lead_packed<true, false> : k_lead_packed<false, false>);
-  auto product_kernel =
-      packed ? (ru ? (vec ? k_product<true, true, true> : k_product<false, true, true>)
-                   : (vec ? k_product<true, true, false> : k_product<false, true, false>))
-             : (ru ? (vec ? k_product<true, false, true> : k_product<false, false, true>)
-                   : (vec ? k_product<true, false, false> : k_product<false, false, false>));
+  // (4x2 cells where the product launch runs alone: the lead schedule of
+  // the dense layout)
+  const bool wide_product = !packed && lead_sched;
+#define DBS_PRODUCT(P, C)                                                                    \
+  (ru ? (vec ? k_product<true, P, true, C> : k_product<false, P, true, C>)                    \
+      : (vec ? k_product<true, P, false, C> : k_product<false, P, false, C>))
+  auto product_kernel = packed ? DBS_PRODUCT(true, 4)
+                               : (wide_product ? DBS_PRODUCT(false, 2) : DBS_PRODUCT(false, 4));
+#undef DBS_PRODUCT
+  const unsigned product_block =
+      (unsigned)(wide_product ? product_threads<2>() : product_threads<4>());
   // phase 3 of K (none for K < 0) beside phase 1 of Z (none for Z < 0);
   // grid.x = molecules, grid.y = the closure and then the quadrants
   const unsigned mx = (unsigned)(batch < kMaxGridX ? batch : kMaxGridX);
@@ -1907,8 +1977,8 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
                   U, L, n, batch, K, Z, infeasible);
   };
   auto product = [&](int64_t K, hipStream_t st) -> hipError_t {
-    return launch(prof, kProfPanel, product_kernel, dim3((unsigned)(TB - 1), gy), dim3(kThreads),
-                  st, U, L, n, batch, K);
+    return launch(prof, kProfPanel, product_kernel, dim3((unsigned)(TB - 1), gy),
+                  dim3(product_block), st, U, L, n, batch, K);
   };
   if (lead_sched) {
     hipError_t e = lead(-1, K0, s, false);

@@ -369,8 +369,9 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uin
  *   *lookahead    how many steps it updates ahead on its second stream:
  *     0  no look-ahead: a single k-block or phase-3 tile; fewer than 256
  *        phase-3 tiles x molecules (the bulk launch is shorter than the band
- *        strip it would hide); or more than 256 phase 1-2 workgroups (the
- *        panel launch fills the chip by itself).  Without look-ahead, a
+ *        strip it would hide); more than 256 phase 1-2 workgroups (the
+ *        panel launch fills the chip by itself); or, below 1024 tiles x
+ *        molecules, where the pass takes the lead schedule (below).  Without look-ahead, a
  *        batch of two or more molecules with more than 256 phase 1-2
  *        workgroups ((k-blocks - 1) x molecules) splits into two halves, one
  *        on the caller's stream and one on the second stream, so that one
@@ -390,7 +391,8 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uin
  *     a pass without look-ahead in steps of one k-block and n below 23 040
  *     (the phase-3 quadrants of a launch fit one grid dimension), and is
  *     chosen where a batch has more than 256 phase 1-2 workgroups
- *     ((k-blocks - 1) x molecules).  Per k-block K it runs two launches on the caller's stream:
+ *     ((k-blocks - 1) x molecules), and from 128 to 511 phase-3 tiles x
+ *     molecules.  Per k-block K it runs two launches on the caller's stream:
  *     phase 2 of K as a product with K's diagonal tile, closed the launch
  *     before, and one launch that holds phase 3 of K and, beside it, phase 1
  *     of K + 1 (phase 3 of K on the diagonal tile of K + 1, then its

@@ -182,8 +182,8 @@ def test_lookahead_bands_query():
     assert lib.dbs_lookahead_bands(1024, 1) == 0      # 36 tiles
     assert lib.dbs_lookahead_bands(500, 64) == 0      # 448 panel workgroups fill the chip
     assert lib.dbs_lookahead_bands(130, 129) == 0     # 258 panel workgroups: split batch
-    assert lib.dbs_lookahead_bands(130, 128) == 1     # 384 tiles, 256 panel workgroups
-    assert lib.dbs_lookahead_bands(2944, 1) == 1      # 276 tiles, 45 panel workgroups
+    assert lib.dbs_lookahead_bands(130, 128) == 0     # 384 tiles: the lead schedule
+    assert lib.dbs_lookahead_bands(2944, 1) == 0      # 276 tiles: the lead schedule
     assert lib.dbs_lookahead_bands(4096, 1) == 1
     assert lib.dbs_lookahead_bands(5120, 1) == 1      # 820 tiles
     assert lib.dbs_lookahead_bands(5632, 1) == 1      # 990 tiles
@@ -205,9 +205,18 @@ def test_schedule_query_with_forced_values():
     assert dgb.schedule(200, step_blocks=4) == (0, 4, 0)
     assert dgb.schedule(12288, lookahead=1, step_blocks=3) == (1, 3, 0)
     # the lead schedule: automatic where a batch's phase 1-2 launch would
-    # fill the chip; forced on any one-stream pass with one-block steps
+    # fill the chip, and between 128 and 512 phase-3 tiles (128-atom tiles
+    # I <= J, times molecules); forced on any one-stream pass with one-block
+    # steps
     assert dgb.schedule(500, 64) == (0, 1, 1) and dgb.schedule(130, 129) == (0, 1, 1)
-    assert dgb.schedule(130, 128)[2] == 0 and dgb.schedule(1024)[2] == 0
+    assert dgb.schedule(300, 100) == (0, 1, 1)               # 600 tiles, 400 panel tiles
+    assert dgb.schedule(300, 100, lead=False) == (0, 1, 0)   # the split batch instead
+    assert dgb.schedule(1024)[2] == 0 and dgb.schedule(1792) == (0, 1, 0)   # 36, 105 tiles
+    assert dgb.schedule(500, 8) == (0, 1, 0)                 # 80 tiles
+    assert dgb.schedule(2048) == (0, 1, 1) and dgb.schedule(3072) == (0, 1, 1)  # 136, 300
+    assert dgb.schedule(500, 16) == (0, 1, 1) and dgb.schedule(130, 128) == (0, 1, 1)
+    assert dgb.schedule(4096) == (1, 1, 0)                   # 528 tiles: one step ahead
+    assert dgb.schedule(3072, lead=False) == (1, 1, 0)
     assert dgb.schedule(500, 64, lead=False) == (0, 1, 0)
     assert dgb.schedule(1024, lead=True) == (0, 1, 1)
     assert dgb.schedule(12288, lead=True) == (2, 4, 0)        # runs ahead: no lead

@@ -232,6 +232,27 @@ def test_lead_schedule(n, batch):
     assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
 
 
+@pytest.mark.parametrize("n,batch", [(2048, 1), (700, 12), (1500, 2), (130, 128)])
+def test_automatic_lead_window(n, batch):
+    # between 128 and 512 phase-3 tiles (times molecules) the automatic
+    # schedule of a blocked pass is the lead one, whether or not the phase 1-2
+    # launch would fill the chip (4x2-cell products on the dense layout): dense, directed
+    # and packed blocked passes against the oracle
+    from oracle import steps
+    assert dgb.schedule(n, batch) == (0, 1, 1)
+    U0, L0 = sound_input(n, batch, seed=5 * n + batch)
+    Ue, Le = oracle.smooth(U0, L0)
+    tag = f"automatic n={n} batch={batch}"
+    Ug, Lg = gpu_pass(U0, L0, "blocked")
+    assert_bits(Ug, Lg, Ue, Le, "dense " + tag)
+    U, L = dev(U0), dev(L0)
+    dgb.smooth_directed(U, L, algo="blocked")
+    assert_bits(host(U), host(L), Ue, Le, "directed " + tag)
+    P = dgb.pack(dev(U0), dev(L0))
+    dgb.smooth_packed(P, algo="blocked")
+    assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
+
+
 def test_walk_molecules_batched():
     W = gen.make_workload("b64n500", batch=5)
     Ue, Le = oracle.smooth(W.U, W.L)
