@@ -74,11 +74,11 @@ constexpr int64_t kPanelFill = 256;
 // there a bulk launch is long enough to hide the closure of the next
 // diagonal tile, and the product is shorter than a phase 1-2 launch.
 // Measured (median of 10 passes, lead against the plain or one-step
-// schedule): n1792 (105 tiles) 1.10x, n2048 (136) 0.93x, n3072 (300) 0.81x,
-// n4096 (528) 1.02x; 8 x n500 (80) 1.05x, 16 x n500 (160) 0.94x,
-// 32 x n500 (320) 0.76x; 2 x n1024 (72) 1.11x, 8 x n1024 (288) 0.83x;
-// 32 x n256 (96) 1.06x, 64 x n256 (192) 0.95x.
-constexpr int64_t kLeadTilesMin = 128, kLeadTilesMax = 512;
+// schedule): n1024 (36 tiles) 1.09x, n1280 (55) 1.08x, 4 x n500 (40)
+// 1.07x; 2 x n1024 (72) 0.95x, n1536 (78) 0.94x, 8 x n500 (80) 0.89x,
+// 16 x n300 (96) 0.92x, n1792 (105) 0.95x, n2048 (136) 0.88x, n3072 (300)
+// 0.81x, 32 x n500 (320) 0.76x; n4096 (528) 1.02x.
+constexpr int64_t kLeadTilesMin = 64, kLeadTilesMax = 512;
 constexpr int kThreads = 256;
 
 // The side-stream kernels (strips, and phases 1-2 of the next blocks) are
@@ -1699,12 +1699,19 @@ __global__ __launch_bounds__(kThreads) void k_lead_packed(float *__restrict__ P,
 // and 8x4 with 8-atom chunks 422-428 us at 3; 4x8, 8x4 with 16-atom chunks
 // 484-494 us at 2; 8x8 needs more than 256 VGPRs)
 constexpr int kBulkRT = 4, kBulkCT = 4, kBulkKC = 16;
-// A bulk launch with fewer quadrant workgroups than CUs (small n, one
-// stream) is latency-bound: there each quadrant takes 512 threads with 4x2
-// cells (measured at n1024, bulk launch: 4x4 17.3 us, 2x2 15.6 us with the
-// whole k-block staged at once, 2x4 13.3 us, 4x2 13.2 us).
+// A bulk launch on one stream with few quadrant workgroups leaves its SIMDs
+// one or two waves each: there each quadrant takes 512 threads with 4x2
+// cells instead of 256 with 4x4.  Plain bulk launches, up to kSmallGrid
+// quadrants (measured at n1024, 144 quadrants, bulk launch: 4x4 17.3 us,
+// 2x2 15.6 us with the whole k-block staged at once, 2x4 13.3 us, 4x2
+// 13.2 us; passes at 312 and 420 quadrants, n1536 and n1792, 2 % faster
+// with 4x4).  Lead launches, up to kSmallLeadGrid quadrants, the 4x4
+// workgroups the chip holds at once (passes, 4x2 against 4x4: n2048, 544
+// quadrants, 1.26 against 1.44 ms; 64 x n256, 768, 0.199 against 0.225 ms;
+// 24 x n500, 960, 0.427 against 0.435 ms; from 1088 quadrants 4x4 is
+// faster: 2 x n2048 1.58 against 1.67 ms, n3072 2.35 against 2.48 ms).
 constexpr int kSmallRT = 4, kSmallCT = 2, kSmallKC = 32;
-constexpr int64_t kSmallGrid = 256;
+constexpr int64_t kSmallGrid = 256, kSmallLeadGrid = 1024;
 
 // The ordering events of a pass that runs part of its work on a second
 // stream.  They only order the two streams of one device: the kernels they
@@ -1941,7 +1948,7 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
 #define DBS_LEAD(R, C, KC, M)                                                                \
   (ru ? (vec ? k_lead<true, true, R, C, KC, M> : k_lead<false, true, R, C, KC, M>)            \
       : (vec ? k_lead<true, false, R, C, KC, M> : k_lead<false, false, R, C, KC, M>))
-  const bool small_lead = !packed && 4 * pairs * batch <= kSmallGrid;
+  const bool small_lead = !packed && 4 * pairs * batch <= kSmallLeadGrid;
   auto lead_kernel = small_lead ? DBS_LEAD(kSmallRT, kSmallCT, kSmallKC, false)
                                 : DBS_LEAD(kBulkRT, kBulkCT, kBulkKC, false);
   auto lead_last = small_lead ? DBS_LEAD(kSmallRT, kSmallCT, kSmallKC, true)

@@ -391,7 +391,7 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uin
  *     a pass without look-ahead in steps of one k-block and n below 23 040
  *     (the phase-3 quadrants of a launch fit one grid dimension), and is
  *     chosen where a batch has more than 256 phase 1-2 workgroups
- *     ((k-blocks - 1) x molecules), and from 128 to 511 phase-3 tiles x
+ *     ((k-blocks - 1) x molecules), and from 64 to 511 phase-3 tiles x
  *     molecules.  Per k-block K it runs two launches on the caller's stream:
  *     phase 2 of K as a product with K's diagonal tile, closed the launch
  *     before, and one launch that holds phase 3 of K and, beside it, phase 1

@@ -205,14 +205,15 @@ def test_schedule_query_with_forced_values():
     assert dgb.schedule(200, step_blocks=4) == (0, 4, 0)
     assert dgb.schedule(12288, lookahead=1, step_blocks=3) == (1, 3, 0)
     # the lead schedule: automatic where a batch's phase 1-2 launch would
-    # fill the chip, and between 128 and 512 phase-3 tiles (128-atom tiles
+    # fill the chip, and between 64 and 512 phase-3 tiles (128-atom tiles
     # I <= J, times molecules); forced on any one-stream pass with one-block
     # steps
     assert dgb.schedule(500, 64) == (0, 1, 1) and dgb.schedule(130, 129) == (0, 1, 1)
     assert dgb.schedule(300, 100) == (0, 1, 1)               # 600 tiles, 400 panel tiles
     assert dgb.schedule(300, 100, lead=False) == (0, 1, 0)   # the split batch instead
-    assert dgb.schedule(1024)[2] == 0 and dgb.schedule(1792) == (0, 1, 0)   # 36, 105 tiles
-    assert dgb.schedule(500, 8) == (0, 1, 0)                 # 80 tiles
+    assert dgb.schedule(1024)[2] == 0 and dgb.schedule(1280) == (0, 1, 0)   # 36, 55 tiles
+    assert dgb.schedule(500, 4) == (0, 1, 0)                 # 40 tiles
+    assert dgb.schedule(500, 8) == (0, 1, 1) and dgb.schedule(1792) == (0, 1, 1)  # 80, 105
     assert dgb.schedule(2048) == (0, 1, 1) and dgb.schedule(3072) == (0, 1, 1)  # 136, 300
     assert dgb.schedule(500, 16) == (0, 1, 1) and dgb.schedule(130, 128) == (0, 1, 1)
     assert dgb.schedule(4096) == (1, 1, 0)                   # 528 tiles: one step ahead

@@ -232,9 +232,10 @@ def test_lead_schedule(n, batch):
     assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
 
 
-@pytest.mark.parametrize("n,batch", [(2048, 1), (700, 12), (1500, 2), (130, 128)])
+@pytest.mark.parametrize("n,batch", [(2048, 1), (700, 12), (1500, 2), (130, 128), (1536, 1),
+                                     (500, 8), (300, 16)])
 def test_automatic_lead_window(n, batch):
-    # between 128 and 512 phase-3 tiles (times molecules) the automatic
+    # between 64 and 512 phase-3 tiles (times molecules) the automatic
     # schedule of a blocked pass is the lead one, whether or not the phase 1-2
     # launch would fill the chip (4x2-cell products on the dense layout): dense, directed
     # and packed blocked passes against the oracle
