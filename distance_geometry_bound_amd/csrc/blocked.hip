@@ -1288,7 +1288,7 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_lead(float *__restric
 // the 2^-6 grid this equals running the rounds of band K in order over the
 // panel tile, which the phase 1-2 kernel does.  Unlike those rounds the
 // products need no barrier per atom: D* and R are staged in LDS whole, and
-// every thread relaxes its 4x4 cells over the atoms as the bulk does.  R is
+// every thread relaxes its cells over the atoms as the bulk does.  R is
 // read from its fresh orientation and written in both (dense), or as its U
 // and L slots (packed).
 // Thread (ty, tx) owns 4 x CT cells of R.  CT = 4 (256 threads) runs beside
