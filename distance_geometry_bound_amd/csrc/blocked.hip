@@ -69,6 +69,9 @@ constexpr int64_t kAheadTiles = 256;
 // Above this many phase 1-2 workgroups the panel launch fills the chip by
 // itself, and running it beside the bulk gains nothing (one per CU).
 constexpr int64_t kPanelFill = 256;
+// Phase 1-2 workgroups (times molecules) up to which the dense phase 1-2
+// launch splits each panel tile's columns over several workgroups.
+constexpr int64_t kSplitPanelFill = 256;
 // Between these many phase-3 tiles (times molecules) a one-stream pass takes
 // the lead schedule even where its phase 1-2 launch would not fill the chip:
 // there a bulk launch is long enough to hide the closure of the next
@@ -457,6 +460,172 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
           if (c < bJ && a < bK) {
             Ub[(j0 + c) * n + k0 + a] = tt[0][c][a];
             if (!PK) Lb[(j0 + c) * n + k0 + a] = tt[PK ? 0 : 1][c][a];
+          }
+        }
+    }
+    if (bad) atomicOr(infeasible + b, DBS_INFEASIBLE_EARLY);
+    __syncthreads();  // LDS reuse by the next molecule
+  }
+}
+
+// Phases 1 and 2 of k-block K with each panel tile's columns split over P
+// workgroups (dense layout, where the launch is on the critical path):
+// workgroup (J, h) (grid.x = P per k-block tile other than K, grid.y =
+// molecules) holds the diagonal tile D, 2x2 cells per thread as
+// k_diag_panel with S = 2 does, and the W = BK / P columns h*W .. of the
+// panel tile R = (K, J), W / 16 cells per thread, and runs the rounds of
+// band K in order over both.  Every workgroup repeats D's rounds; a round's
+// arithmetic on one compute unit falls from D and R (8192 cells) to D and a
+// P-th of R.  The slice is staged through an LDS tile for its loads and its
+// stores in both orientations, so that the global accesses are row
+// segments.  The last workgroup of the molecule writes D back, as in
+// k_diag_panel.
+template <bool VEC, bool RU, int P>
+__global__ __launch_bounds__(1024) void k_diag_panel_split(float *__restrict__ U,
+                                                          float *__restrict__ L, int64_t n,
+                                                          int64_t batch, int64_t K,
+                                                          uint32_t *infeasible) {
+  static_assert(P == 2 || P == 4, "two or four column slices");
+  constexpr int W = BK / P;   // columns of R per workgroup
+  constexpr int NR = W / 16;  // R cells per thread: 2 (P = 2) or 1 (P = 4)
+  __shared__ __align__(16) float dvu[2][BK], dvl[2][BK];  // row m of D
+  __shared__ __align__(16) float rvu[2][W], rvl[2][W];    // row m of the slice
+  __shared__ float sr[2][BK][W + 1];                      // the slice (U, L)
+
+  rounding_prologue<RU>();
+  critical_path_priority();
+  const int tid = threadIdx.x, ty = tid >> 5, tx = tid & 31;
+  // this thread's cells of the slice: column rc, rows 2ty + rr + i (i < NR)
+  const int rc = P == 2 ? tx : (tx & 15);
+  const int rr = P == 2 ? 0 : (tx >> 4);
+  int64_t J = blockIdx.x / P;
+  if (J >= K) ++J;
+  const int64_t k0 = K * BK, c0 = J * BK + (blockIdx.x % P) * W;  // the slice's first column
+  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int bW = (int)(n - c0 < W ? (n - c0 > 0 ? n - c0 : 0) : W);  // its columns inside
+  const bool rowor = fresh(K, J);
+  const bool writes_d = blockIdx.x == gridDim.x - 1;
+  const int64_t nn = n * n;
+
+  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    float *Ub = U + b * nn;
+    float *Lb = L + b * nn;
+    Seg<2> xu[2], xl[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int a = ty * 2 + r;
+      const int64_t g = (k0 + a) * n + k0 + tx * 2;
+      const int64_t left = a < bK ? bK - tx * 2 : 0;
+      xu[r] = load_seg<VEC, 2>(Ub + g, left, kInf, Ub);
+      xl[r] = load_seg<VEC, 2>(Lb + g, left, 0.0f, Lb);
+    }
+    // the slice from its fresh orientation: R[a][c] = M[k0+a][c0+c] (lanes
+    // along c), else M[c0+c][k0+a] (lanes along a)
+#pragma unroll
+    for (int it = 0; it < BK * W / 1024; ++it) {
+      const int e = tid + it * 1024;
+      const int a = rowor ? e / W : e % BK, c = rowor ? e % W : e / BK;
+      const bool in = a < bK && c < bW;
+      const int64_t g = in ? (rowor ? (k0 + a) * n + c0 + c : (c0 + c) * n + k0 + a) : 0;
+      const float xu = Ub[g], xl = Lb[g];
+      sr[0][a][c] = in ? xu : kInf;
+      sr[1][a][c] = in ? xl : 0.0f;
+    }
+    float du[2][2], dl[2][2];  // D[2ty + r][2tx + q]
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        du[r][q] = xu[r].v[q];
+        dl[r][q] = xl[r].v[q];
+      }
+    __syncthreads();
+    float ur[NR], lr[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      ur[i] = sr[0][2 * ty + rr + i][rc];
+      lr[i] = sr[1][2 * ty + rr + i][rc];
+    }
+
+    for (int mb = 0; mb < BK / 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int m = mb * 2 + r;
+        if (m >= bK) break;  // uniform
+        const int buf = m & 1;
+        if (ty == mb) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            dvu[buf][tx * 2 + q] = du[r][q];
+            dvl[buf][tx * 2 + q] = dl[r][q];
+          }
+          if constexpr (P == 2) {
+            rvu[buf][rc] = ur[r];
+            rvl[buf][rc] = lr[r];
+          } else if (rr == r) {
+            rvu[buf][rc] = ur[0];
+            rvl[buf][rc] = lr[0];
+          }
+        }
+        __syncthreads();
+        float cu[2], cl[2], eu[2], el[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          cu[q] = dvu[buf][ty * 2 + q];  // D[a][m] = D[m][a]
+          cl[q] = dvl[buf][ty * 2 + q];
+          eu[q] = dvu[buf][tx * 2 + q];  // D[m][b]
+          el[q] = dvl[buf][tx * 2 + q];
+        }
+        const float ru = rvu[buf][rc], rl = rvl[buf][rc];  // R[m][c]
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) relax1<RU>(du[a][q], dl[a][q], cu[a], cl[a], eu[q], el[q]);
+        if constexpr (P == 2) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) relax1<RU>(ur[i], lr[i], cu[i], cl[i], ru, rl);
+        } else {
+          relax1<RU>(ur[0], lr[0], rr ? cu[1] : cu[0], rr ? cl[1] : cl[0], ru, rl);
+        }
+      }
+    }
+
+    // the slice in both orientations, through sr (each thread rewrites the
+    // entries it read; no other thread reads sr during the rounds)
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      sr[0][2 * ty + rr + i][rc] = ur[i];
+      sr[1][2 * ty + rr + i][rc] = lower_out<RU>(lr[i]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < BK * W / 1024; ++it) {
+      const int e = tid + it * 1024;
+      const int a = e / W, c = e % W;  // rows of band K, lanes along c
+      if (a < bK && c < bW) {
+        Ub[(k0 + a) * n + c0 + c] = sr[0][a][c];
+        Lb[(k0 + a) * n + c0 + c] = sr[1][a][c];
+      }
+      const int at = e % BK, ct = e / BK;  // the other orientation, lanes along a
+      if (at < bK && ct < bW) {
+        Ub[(c0 + ct) * n + k0 + at] = sr[0][at][ct];
+        Lb[(c0 + ct) * n + k0 + at] = sr[1][at][ct];
+      }
+    }
+    // D (a fresh tile, as a full square) from the last workgroup, with the
+    // early test of the infeasibility option on its cells as they are stored
+    bool bad = false;
+    if (writes_d) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int a = ty * 2 + r, c = tx * 2 + q;
+          const float lo = lower_out<RU>(dl[r][q]);
+          if (a < bK && c < bK) {
+            bad |= infeasible && lo > du[r][q];
+            Ub[(k0 + a) * n + k0 + c] = du[r][q];
+            Lb[(k0 + a) * n + k0 + c] = lo;
           }
         }
     }
@@ -2012,6 +2181,22 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   auto panel = packed_deep ? DBS_PICK_PANEL(4) : DBS_PICK_PANEL(2);
   const unsigned panel_block = packed_deep ? panel_threads<4>() : panel_threads<2>();
 #undef DBS_PICK_PANEL
+  // The dense phase 1-2 launch splits each panel tile's columns over P
+  // workgroups where P times its workgroups still get a compute unit each:
+  // four on the critical path of a one-stream pass, two beside the bulk one
+  // step ahead (measured passes, P = 1 / 2 / 4: n1024 0.576 / 0.520 / 0.515
+  // ms, n128 0.087 / 0.079 / 0.075 ms, 4 x n500 0.310 / 0.285 / 0.284 ms;
+  // n4096, one step ahead, 4.24 / 4.12 / 4.56 ms).
+  const int64_t panel_wgs = (TB - 1) * batch;
+  const int split_p = packed || deep ? 1
+                      : ahead == 0 && 4 * panel_wgs <= kSplitPanelFill ? 4
+                      : 2 * panel_wgs <= kSplitPanelFill ? 2
+                                                          : 1;
+#define DBS_PICK_SPLIT(P)                                                                    \
+  (ru ? (vec ? k_diag_panel_split<true, true, P> : k_diag_panel_split<false, true, P>)        \
+      : (vec ? k_diag_panel_split<true, false, P> : k_diag_panel_split<false, false, P>))
+  auto panel_split = split_p == 4 ? DBS_PICK_SPLIT(4) : DBS_PICK_SPLIT(2);
+#undef DBS_PICK_SPLIT
 
   // Phases 1 and 2 of block K (the diagonal tile alone when it is the only
   // block).  On the critical path (no look-ahead, or one step) as one launch
@@ -2031,6 +2216,9 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
       const hipError_t r = lead(-1, K, st, false);
       return r == hipSuccess ? product(K, st) : r;
     }
+    if (split_p > 1)
+      return launch(prof, kProfPanel, panel_split, dim3((unsigned)((TB - 1) * split_p), gy),
+                    dim3(1024), st, U, L, n, batch, K, infeasible);
     return launch(prof, kProfPanel, panel, dim3((unsigned)(TB - 1), gy), dim3(panel_block), st, U,
                   L, n, batch, K, infeasible);
   };
