@@ -469,7 +469,7 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
 }
 
 // Phases 1 and 2 of k-block K with each panel tile's columns split over P
-// workgroups (dense layout, where the launch is on the critical path):
+// workgroups (where the launch is on the critical path):
 // workgroup (J, h) (grid.x = P per k-block tile other than K, grid.y =
 // molecules) holds the diagonal tile D, 2x2 cells per thread as
 // k_diag_panel with S = 2 does, and the W = BK / P columns h*W .. of the
@@ -478,9 +478,10 @@ __global__ __launch_bounds__(panel_threads<S>()) void k_diag_panel(float *__rest
 // arithmetic on one compute unit falls from D and R (8192 cells) to D and a
 // P-th of R.  The slice is staged through an LDS tile for its loads and its
 // stores in both orientations, so that the global accesses are row
-// segments.  The last workgroup of the molecule writes D back, as in
-// k_diag_panel.
-template <bool VEC, bool RU, int P>
+// segments (packed: the row slots of R's cells hold U right of the diagonal
+// and L left of it, the transposed slots the other).  The last workgroup of
+// the molecule writes D back, as in k_diag_panel.
+template <bool VEC, bool PK, bool RU, int P>
 __global__ __launch_bounds__(1024) void k_diag_panel_split(float *__restrict__ U,
                                                           float *__restrict__ L, int64_t n,
                                                           int64_t batch, int64_t K,
@@ -501,6 +502,7 @@ __global__ __launch_bounds__(1024) void k_diag_panel_split(float *__restrict__ U
   int64_t J = blockIdx.x / P;
   if (J >= K) ++J;
   const int64_t k0 = K * BK, c0 = J * BK + (blockIdx.x % P) * W;  // the slice's first column
+  const bool up = K < J;  // R lies right of the diagonal
   const int bK = (int)(n - k0 < BK ? n - k0 : BK);
   const int bW = (int)(n - c0 < W ? (n - c0 > 0 ? n - c0 : 0) : W);  // its columns inside
   const bool rowor = fresh(K, J);
@@ -509,36 +511,52 @@ __global__ __launch_bounds__(1024) void k_diag_panel_split(float *__restrict__ U
 
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
     float *Ub = U + b * nn;
-    float *Lb = L + b * nn;
-    Seg<2> xu[2], xl[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int a = ty * 2 + r;
-      const int64_t g = (k0 + a) * n + k0 + tx * 2;
-      const int64_t left = a < bK ? bK - tx * 2 : 0;
-      xu[r] = load_seg<VEC, 2>(Ub + g, left, kInf, Ub);
-      xl[r] = load_seg<VEC, 2>(Lb + g, left, 0.0f, Lb);
-    }
-    // the slice from its fresh orientation: R[a][c] = M[k0+a][c0+c] (lanes
-    // along c), else M[c0+c][k0+a] (lanes along a)
-#pragma unroll
-    for (int it = 0; it < BK * W / 1024; ++it) {
-      const int e = tid + it * 1024;
-      const int a = rowor ? e / W : e % BK, c = rowor ? e % W : e / BK;
-      const bool in = a < bK && c < bW;
-      const int64_t g = in ? (rowor ? (k0 + a) * n + c0 + c : (c0 + c) * n + k0 + a) : 0;
-      const float xu = Ub[g], xl = Lb[g];
-      sr[0][a][c] = in ? xu : kInf;
-      sr[1][a][c] = in ? xl : 0.0f;
-    }
+    float *Lb = PK ? Ub : L + b * nn;
     float du[2][2], dl[2][2];  // D[2ty + r][2tx + q]
+    if constexpr (PK) {
+      packed_block_load<VEC, 2>(Ub, n, k0, k0, bK, bK, ty, tx, du, dl);
+      // the slice's row slots P[k0+a][c0+c] (lanes along c) and transposed
+      // slots P[c0+c][k0+a] (lanes along a)
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        du[r][q] = xu[r].v[q];
-        dl[r][q] = xl[r].v[q];
+      for (int it = 0; it < BK * W / 1024; ++it) {
+        const int e = tid + it * 1024;
+        const int a = e / W, c = e % W, at = e % BK, ct = e / BK;
+        const bool in = a < bK && c < bW, inT = at < bK && ct < bW;
+        const float x = Ub[in ? (k0 + a) * n + c0 + c : 0];
+        const float y = Ub[inT ? (c0 + ct) * n + k0 + at : 0];
+        sr[up ? 0 : 1][a][c] = in ? x : (up ? kInf : 0.0f);
+        sr[up ? 1 : 0][at][ct] = inT ? y : (up ? 0.0f : kInf);
       }
+    } else {
+      Seg<2> xu[2], xl[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int a = ty * 2 + r;
+        const int64_t g = (k0 + a) * n + k0 + tx * 2;
+        const int64_t left = a < bK ? bK - tx * 2 : 0;
+        xu[r] = load_seg<VEC, 2>(Ub + g, left, kInf, Ub);
+        xl[r] = load_seg<VEC, 2>(Lb + g, left, 0.0f, Lb);
+      }
+      // the slice from its fresh orientation: R[a][c] = M[k0+a][c0+c] (lanes
+      // along c), else M[c0+c][k0+a] (lanes along a)
+#pragma unroll
+      for (int it = 0; it < BK * W / 1024; ++it) {
+        const int e = tid + it * 1024;
+        const int a = rowor ? e / W : e % BK, c = rowor ? e % W : e / BK;
+        const bool in = a < bK && c < bW;
+        const int64_t g = in ? (rowor ? (k0 + a) * n + c0 + c : (c0 + c) * n + k0 + a) : 0;
+        const float xu = Ub[g], xl = Lb[g];
+        sr[0][a][c] = in ? xu : kInf;
+        sr[1][a][c] = in ? xl : 0.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          du[r][q] = xu[r].v[q];
+          dl[r][q] = xl[r].v[q];
+        }
+    }
     __syncthreads();
     float ur[NR], lr[NR];
 #pragma unroll
@@ -603,19 +621,35 @@ __global__ __launch_bounds__(1024) void k_diag_panel_split(float *__restrict__ U
       const int e = tid + it * 1024;
       const int a = e / W, c = e % W;  // rows of band K, lanes along c
       if (a < bK && c < bW) {
-        Ub[(k0 + a) * n + c0 + c] = sr[0][a][c];
-        Lb[(k0 + a) * n + c0 + c] = sr[1][a][c];
+        if (PK) {
+          Ub[(k0 + a) * n + c0 + c] = sr[up ? 0 : 1][a][c];
+        } else {
+          Ub[(k0 + a) * n + c0 + c] = sr[0][a][c];
+          Lb[(k0 + a) * n + c0 + c] = sr[1][a][c];
+        }
       }
       const int at = e % BK, ct = e / BK;  // the other orientation, lanes along a
       if (at < bK && ct < bW) {
-        Ub[(c0 + ct) * n + k0 + at] = sr[0][at][ct];
-        Lb[(c0 + ct) * n + k0 + at] = sr[1][at][ct];
+        if (PK) {
+          Ub[(c0 + ct) * n + k0 + at] = sr[up ? 1 : 0][at][ct];
+        } else {
+          Ub[(c0 + ct) * n + k0 + at] = sr[0][at][ct];
+          Lb[(c0 + ct) * n + k0 + at] = sr[1][at][ct];
+        }
       }
     }
     // D (a fresh tile, as a full square) from the last workgroup, with the
     // early test of the infeasibility option on its cells as they are stored
     bool bad = false;
-    if (writes_d) {
+    if (PK && writes_d) {
+      float dlo[2][2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) dlo[r][q] = lower_out<RU>(dl[r][q]);
+      packed_block_store<2>(Ub, n, k0, k0, bK, bK, ty, tx, du, dlo, infeasible ? &bad : nullptr);
+    }
+    if (!PK && writes_d) {
 #pragma unroll
       for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -2181,21 +2215,24 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   auto panel = packed_deep ? DBS_PICK_PANEL(4) : DBS_PICK_PANEL(2);
   const unsigned panel_block = packed_deep ? panel_threads<4>() : panel_threads<2>();
 #undef DBS_PICK_PANEL
-  // The dense phase 1-2 launch splits each panel tile's columns over P
+  // The phase 1-2 launch splits each panel tile's columns over P
   // workgroups where P times its workgroups still get a compute unit each:
-  // four on the critical path of a one-stream pass, two beside the bulk one
-  // step ahead (measured passes, P = 1 / 2 / 4: n1024 0.576 / 0.520 / 0.515
-  // ms, n128 0.087 / 0.079 / 0.075 ms, 4 x n500 0.310 / 0.285 / 0.284 ms;
-  // n4096, one step ahead, 4.24 / 4.12 / 4.56 ms).
+  // four on the critical path of a one-stream pass, and in the dense layout
+  // two beside the bulk one step ahead (measured passes, P = 1 / 2 / 4:
+  // n1024 0.576 / 0.520 / 0.515 ms, n128 0.087 / 0.079 / 0.075 ms, 4 x n500
+  // 0.310 / 0.285 / 0.284 ms; n4096, one step ahead, 4.24 / 4.12 / 4.56 ms;
+  // packed, P = 1 / 4: n1024 0.688 / 0.627 ms, 4 x n500 0.364 / 0.337 ms,
+  // and n4096 one step ahead 4.60 against 4.71 ms with P = 2).
   const int64_t panel_wgs = (TB - 1) * batch;
-  const int split_p = packed || deep ? 1
+  const int split_p = deep || (packed && ahead > 0) ? 1
                       : ahead == 0 && 4 * panel_wgs <= kSplitPanelFill ? 4
                       : 2 * panel_wgs <= kSplitPanelFill ? 2
                                                           : 1;
-#define DBS_PICK_SPLIT(P)                                                                    \
-  (ru ? (vec ? k_diag_panel_split<true, true, P> : k_diag_panel_split<false, true, P>)        \
-      : (vec ? k_diag_panel_split<true, false, P> : k_diag_panel_split<false, false, P>))
-  auto panel_split = split_p == 4 ? DBS_PICK_SPLIT(4) : DBS_PICK_SPLIT(2);
+#define DBS_PICK_SPLIT(K, P)                                                                 \
+  (ru ? (vec ? k_diag_panel_split<true, K, true, P> : k_diag_panel_split<false, K, true, P>)  \
+      : (vec ? k_diag_panel_split<true, K, false, P> : k_diag_panel_split<false, K, false, P>))
+  auto panel_split = packed ? (split_p == 4 ? DBS_PICK_SPLIT(true, 4) : DBS_PICK_SPLIT(true, 2))
+                            : (split_p == 4 ? DBS_PICK_SPLIT(false, 4) : DBS_PICK_SPLIT(false, 2));
 #undef DBS_PICK_SPLIT
 
   // Phases 1 and 2 of block K (the diagonal tile alone when it is the only
