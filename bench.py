@@ -214,9 +214,10 @@ def extra_steps(W, U, L, U0, L0, dev, reps=3):
 
 
 def packed_pass(U0, L0, dev, reps=2):
-    """Time the one-buffer layout on the same workload: pack (reads 8, writes
-    4 bytes per cell), one full pass in place on the packed buffer, unpack
-    (reads 8, writes 8 bytes per cell)."""
+    """Time the one-buffer layout on the same workload: pack (reads the one
+    bound a cell keeps and writes it: 8 bytes per cell), one full pass in
+    place on the packed buffer, unpack (reads P once and writes U and L: 12
+    bytes per cell)."""
     import torch
 
     import distance_geometry_bound_amd as dgb
@@ -248,8 +249,8 @@ def packed_pass(U0, L0, dev, reps=2):
             / (ms[1] * 1e-3) / FP32_VALU_PEAK,
             "dense_equivalent_frac_of_fp32_peak": OPS_PER_TRIPLE * triples / (ms[1] * 1e-3)
             / FP32_VALU_PEAK,
-            "pack_ms": ms[0], "pack_GBps": 12.0 * cells / (ms[0] * 1e-3) / 1e9,
-            "unpack_ms": ms[2], "unpack_GBps": 16.0 * cells / (ms[2] * 1e-3) / 1e9,
+            "pack_ms": ms[0], "pack_GBps": 8.0 * cells / (ms[0] * 1e-3) / 1e9,
+            "unpack_ms": ms[2], "unpack_GBps": 12.0 * cells / (ms[2] * 1e-3) / 1e9,
             "bytes": 4 * cells}
 
 
