@@ -32,7 +32,7 @@ Printed: one JSON line with
                L below), with the pack and unpack steps timed apart
   cpu_baseline the CPU reference (oracle) on a bounded prefix of rounds of
                the same workload, on this host's cores
-Run with --gpus N > 1 and it exits: this build runs on one GPU.
+Run with --gpus N > 1 and it exits: the library has no multi-GPU path.
 """
 from __future__ import annotations
 
@@ -381,7 +381,7 @@ def config_sweep(names, dev, reps=15, oracle_on=True):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
