@@ -25,6 +25,7 @@ CHECK_FLAGS = {
 DBS_OK, DBS_EINVAL, DBS_EDEVICE, DBS_ELAUNCH, DBS_EUNSUPPORTED = 0, -1, -2, -3, -4
 
 EXPORTS = ("dbs_options_init", "dbs_smooth_opts", "dbs_smooth_packed_opts", "dbs_schedule",
+           "dbs_schedule_packed",
            "dbs_smooth", "dbs_smooth_algo", "dbs_smooth_profiled", "dbs_rounds", "dbs_round",
            "dbs_check", "dbs_smooth_range", "dbs_block_rounds", "dbs_tightened", "dbs_bounds_from_restraints",
            "dbs_pack", "dbs_unpack", "dbs_smooth_packed", "dbs_smooth_packed_range",
@@ -79,6 +80,7 @@ def lib():
         L.dbs_smooth_packed_opts.argtypes = [vp, i64, i64, i64, i64, vp, opp]
         i32p = ctypes.POINTER(ctypes.c_int32)
         L.dbs_schedule.argtypes = [i64, i64, opp, i32p, i32p, i32p]
+        L.dbs_schedule_packed.argtypes = [i64, i64, opp, i32p, i32p, i32p]
         L.dbs_smooth_profiled.argtypes = [vp, vp, i64, i64, vp, opp,
                                           ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
         L.dbs_rounds.argtypes = [vp, vp, i64, i64, i64, i64, vp]
@@ -108,7 +110,8 @@ def lib():
                   "dbs_smooth_packed_range", "dbs_check_packed", "dbs_smooth_directed",
                   "dbs_smooth_directed_range", "dbs_smooth_packed_directed_range",
                   "dbs_lds_max_n", "dbs_auto_algo", "dbs_lookahead_bands", "dbs_step_blocks",
-                  "dbs_version", "dbs_smooth_opts", "dbs_smooth_packed_opts", "dbs_schedule"):
+                  "dbs_version", "dbs_smooth_opts", "dbs_smooth_packed_opts", "dbs_schedule",
+                  "dbs_schedule_packed"):
             getattr(L, f).restype = c_int
         _lib = L
     return _lib
@@ -413,14 +416,16 @@ def check_packed(P) -> int:
     return int(flags.item()) & 0xFFFFFFFF
 
 
-def schedule(n: int, batch: int = 1, lookahead=None, step_blocks=None, lead=None):
+def schedule(n: int, batch: int = 1, lookahead=None, step_blocks=None, lead=None,
+             packed: bool = False):
     """(look-ahead depth, k-blocks per step, lead schedule 0/1) of a blocked
-    pass of this shape, with the given forced values (None: automatic); see
-    dbs_schedule."""
+    pass of this shape on the dense (or packed) layout, with the given forced
+    values (None: automatic); see dbs_schedule and dbs_schedule_packed."""
     o = options("auto", False, lookahead, step_blocks, lead)
     la, sb, ld = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    _raise(lib().dbs_schedule(int(n), int(batch), ctypes.byref(o), ctypes.byref(la),
-                              ctypes.byref(sb), ctypes.byref(ld)))
+    f = lib().dbs_schedule_packed if packed else lib().dbs_schedule
+    _raise(f(int(n), int(batch), ctypes.byref(o), ctypes.byref(la), ctypes.byref(sb),
+             ctypes.byref(ld)))
     return int(la.value), int(sb.value), int(ld.value)
 
 

@@ -352,15 +352,28 @@ int dbs_smooth_packed(float *P, int64_t n, int64_t batch, void *stream) {
 
 int dbs_lds_max_n(void) { return dbs::kSmallMaxN; }
 
-int dbs_schedule(int64_t n, int64_t batch, const dbs_options *opts, int32_t *lookahead,
-                 int32_t *step_blocks, int32_t *lead) {
+namespace {
+int schedule_query(int64_t n, int64_t batch, const dbs_options *opts, bool packed,
+                   int32_t *lookahead, int32_t *step_blocks, int32_t *lead) {
   dbs_options o;
   if (n < 1 || batch < 1 || !read_options(opts, &o)) return DBS_EINVAL;
-  const dbs::Sched sc = sched_of(o);
+  dbs::Sched sc = sched_of(o);
+  sc.packed = packed;
   if (lookahead) *lookahead = dbs::lookahead_bands(n, batch, sc);
   if (step_blocks) *step_blocks = dbs::step_blocks(n, batch, sc);
   if (lead) *lead = dbs::lead_schedule(n, batch, sc) ? 1 : 0;
   return DBS_OK;
+}
+}  // namespace
+
+int dbs_schedule(int64_t n, int64_t batch, const dbs_options *opts, int32_t *lookahead,
+                 int32_t *step_blocks, int32_t *lead) {
+  return schedule_query(n, batch, opts, false, lookahead, step_blocks, lead);
+}
+
+int dbs_schedule_packed(int64_t n, int64_t batch, const dbs_options *opts, int32_t *lookahead,
+                        int32_t *step_blocks, int32_t *lead) {
+  return schedule_query(n, batch, opts, true, lookahead, step_blocks, lead);
 }
 
 int dbs_lookahead_bands(int64_t n, int64_t batch) {

@@ -80,8 +80,12 @@ constexpr int64_t kSplitPanelFill = 256;
 // schedule): n1024 (36 tiles) 1.09x, n1280 (55) 1.08x, 4 x n500 (40)
 // 1.07x; 2 x n1024 (72) 0.95x, n1536 (78) 0.94x, 8 x n500 (80) 0.89x,
 // 16 x n300 (96) 0.92x, n1792 (105) 0.95x, n2048 (136) 0.88x, n3072 (300)
-// 0.81x, 32 x n500 (320) 0.76x; n4096 (528) 1.02x.
-constexpr int64_t kLeadTilesMin = 64, kLeadTilesMax = 512;
+// 0.81x, 32 x n500 (320) 0.76x; n4096 (528) 1.02x.  The packed layout, whose
+// product keeps 4x4 cells, from kLeadTilesMinPacked (packed passes, lead
+// against plain: n1536 (78) 1.26x, 32 x n256 (96) 1.21x, n2048 (136) 1.07x,
+// 4 x n1024 (144) 1.08x, n2560 (210) 0.99x, n3072 (300) 0.94x, 8 x n1024
+// (288) 0.90x).
+constexpr int64_t kLeadTilesMin = 64, kLeadTilesMinPacked = 256, kLeadTilesMax = 512;
 constexpr int kThreads = 256;
 
 // The side-stream kernels (strips, and phases 1-2 of the next blocks) are
@@ -2009,11 +2013,11 @@ int step_blocks(int64_t n, int64_t batch, const Sched &sched) {
 
 // The automatic choice of the lead schedule (for a one-stream pass of one
 // k-block per step).
-bool auto_lead(int64_t n, int64_t batch) {
+bool auto_lead(int64_t n, int64_t batch, bool packed) {
   const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
   const int64_t tiles = T * (T + 1) / 2 * batch;
   return (batch >= 2 && (TB - 1) * batch > kPanelFill) ||
-         (tiles >= kLeadTilesMin && tiles < kLeadTilesMax);
+         (tiles >= (packed ? kLeadTilesMinPacked : kLeadTilesMin) && tiles < kLeadTilesMax);
 }
 
 bool lead_schedule(int64_t n, int64_t batch, const Sched &sched) {
@@ -2023,7 +2027,7 @@ bool lead_schedule(int64_t n, int64_t batch, const Sched &sched) {
       step_blocks(n, batch, sched) != 1)
     return false;
   if (sched.lead >= 0) return sched.lead == 1;
-  return auto_lead(n, batch);
+  return auto_lead(n, batch, sched.packed);
 }
 
 int lookahead_bands(int64_t n, int64_t batch, const Sched &sched) {
@@ -2033,7 +2037,8 @@ int lookahead_bands(int64_t n, int64_t batch, const Sched &sched) {
   const int64_t tiles = T * (T + 1) / 2 * batch;
   if (tiles >= kDeepTiles) return 2;
   // the lead schedule runs on one stream
-  if (sched.step_blocks <= 1 && (sched.lead == 1 || (sched.lead < 0 && auto_lead(n, batch))))
+  if (sched.step_blocks <= 1 &&
+      (sched.lead == 1 || (sched.lead < 0 && auto_lead(n, batch, sched.packed))))
     return 0;
   // where one phase 1-2 launch fills the chip the batch splits over the two
   // streams instead (launch_blocked_on), in both layouts
@@ -2069,7 +2074,9 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
 hipError_t launch_blocked(float *U, float *L, int64_t n, int64_t batch, int64_t K0, int64_t K1,
                           hipStream_t s, Prof *prof, unsigned flags, const Sched &sched,
                           uint32_t *infeasible) {
-  return launch_blocked_on(U, L, n, batch, K0, K1, s, prof, flags, sched, false, infeasible);
+  Sched sc = sched;
+  sc.packed = (flags & kPacked) != 0;
+  return launch_blocked_on(U, L, n, batch, K0, K1, s, prof, flags, sc, false, infeasible);
 }
 
 namespace {

@@ -202,6 +202,7 @@ struct Sched {
   int lookahead = -1;
   int step_blocks = -1;
   int lead = -1;
+  bool packed = false;  // the layout (the automatic lead schedule differs)
 };
 // k-blocks K0..K1-1 of the blocked pass (rounds 64*K0 .. min(64*K1, n)-1)
 // `infeasible` (may be null): per-molecule words for the early test of the

@@ -364,8 +364,10 @@ int dbs_smooth_packed_range(float *P, int64_t n, int64_t batch, int64_t k_begin,
 int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uint32_t *d_flags);
 
 /*
- * dbs_schedule -- the schedule a blocked pass (DBS_ALGO_BLOCKED, dense or
- * packed layout) takes for this shape under `opts` (NULL: the defaults):
+ * dbs_schedule -- the schedule a blocked pass (DBS_ALGO_BLOCKED) on the dense
+ * layout takes for this shape under `opts` (NULL: the defaults);
+ * dbs_schedule_packed the same for the packed layout (dbs_smooth_packed and
+ * its variants), which differs only in the lead schedule's automatic choice:
  *   *lookahead    how many steps it updates ahead on its second stream:
  *     0  no look-ahead: a single k-block or phase-3 tile; fewer than 256
  *        phase-3 tiles x molecules (the bulk launch is shorter than the band
@@ -391,8 +393,8 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uin
  *     a pass without look-ahead in steps of one k-block and n below 23 040
  *     (the phase-3 quadrants of a launch fit one grid dimension), and is
  *     chosen where a batch has more than 256 phase 1-2 workgroups
- *     ((k-blocks - 1) x molecules), and from 64 to 511 phase-3 tiles x
- *     molecules.  Per k-block K it runs two launches on the caller's stream:
+ *     ((k-blocks - 1) x molecules), and from 64 (packed layout: 256) to
+ *     511 phase-3 tiles x molecules.  Per k-block K it runs two launches on the caller's stream:
  *     phase 2 of K as a product with K's diagonal tile, closed the launch
  *     before, and one launch that holds phase 3 of K and, beside it, phase 1
  *     of K + 1 (phase 3 of K on the diagonal tile of K + 1, then its
@@ -405,6 +407,8 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uin
  */
 int dbs_schedule(int64_t n, int64_t batch, const struct dbs_options *opts, int32_t *lookahead,
                  int32_t *step_blocks, int32_t *lead);
+int dbs_schedule_packed(int64_t n, int64_t batch, const struct dbs_options *opts,
+                        int32_t *lookahead, int32_t *step_blocks, int32_t *lead);
 
 /* dbs_schedule's automatic look-ahead depth and step width for this shape
    (DBS_EINVAL for n < 1 or batch < 1). */

@@ -218,6 +218,15 @@ def test_schedule_query_with_forced_values():
     assert dgb.schedule(500, 16) == (0, 1, 1) and dgb.schedule(130, 128) == (0, 1, 1)
     assert dgb.schedule(4096) == (1, 1, 0)                   # 528 tiles: one step ahead
     assert dgb.schedule(3072, lead=False) == (1, 1, 0)
+    # the packed layout takes the lead window from 256 tiles
+    assert dgb.schedule(1536, packed=True) == (0, 1, 0)      # 78 tiles
+    assert dgb.schedule(2048, packed=True) == (0, 1, 0)      # 136 tiles
+    assert dgb.schedule(2560, packed=True) == (0, 1, 0)      # 210 tiles
+    assert dgb.schedule(3072, packed=True) == (0, 1, 1)      # 300 tiles
+    assert dgb.schedule(500, 64, packed=True) == (0, 1, 1)   # the panel launch fills the chip
+    assert dgb.schedule(4096, packed=True) == (1, 1, 0)
+    assert dgb.schedule(12288, packed=True) == (2, 4, 0)
+    assert dgb.schedule(1536, packed=True, lead=True) == (0, 1, 1)
     assert dgb.schedule(500, 64, lead=False) == (0, 1, 0)
     assert dgb.schedule(1024, lead=True) == (0, 1, 1)
     assert dgb.schedule(12288, lead=True) == (2, 4, 0)        # runs ahead: no lead

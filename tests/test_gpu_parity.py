@@ -236,11 +236,15 @@ def test_lead_schedule(n, batch):
                                      (500, 8), (300, 16)])
 def test_automatic_lead_window(n, batch):
     # between 64 and 512 phase-3 tiles (times molecules) the automatic
-    # schedule of a blocked pass is the lead one, whether or not the phase 1-2
-    # launch would fill the chip (4x2-cell products on the dense layout): dense, directed
-    # and packed blocked passes against the oracle
+    # schedule of a dense blocked pass is the lead one, whether or not the
+    # phase 1-2 launch would fill the chip (4x2-cell products); the packed
+    # layout takes it from 256 tiles: dense, directed and packed blocked
+    # passes against the oracle
     from oracle import steps
     assert dgb.schedule(n, batch) == (0, 1, 1)
+    T = -(-n // 128)
+    assert dgb.schedule(n, batch, packed=True)[2] == (1 if T * (T + 1) // 2 * batch >= 256 or
+                                                      (-(-n // 64) - 1) * batch > 256 else 0)
     U0, L0 = sound_input(n, batch, seed=5 * n + batch)
     Ue, Le = oracle.smooth(U0, L0)
     tag = f"automatic n={n} batch={batch}"
