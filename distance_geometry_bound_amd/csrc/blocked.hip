@@ -1672,6 +1672,131 @@ __global__ __launch_bounds__(product_threads<CT>()) void k_product(float *__rest
   }
 }
 
+// Phase 2 of k-block K as k_product computes it (dense layout), with each
+// panel tile's columns split over P workgroups: workgroup (J, h) stages D*
+// whole and the W = BK / P columns h*W .. of R, and relaxes 4 x (W / 16)
+// cells per thread on 256 threads.  Where a product launch has fewer
+// workgroups than the chip has CUs, this spreads each tile over P of them.
+// R's slice is staged through LDS from its fresh orientation (lanes along
+// the slice's rows or columns, so both reads are row segments) and written
+// back the same way in both orientations.
+template <bool VEC, bool RU, int P>
+__global__ __launch_bounds__(256) void k_product_slice(float *__restrict__ U,
+                                                      float *__restrict__ L, int64_t n,
+                                                      int64_t batch, int64_t K) {
+  static_assert(P == 2 || P == 4, "two or four column slices");
+  constexpr int W = BK / P, CT = W / 16;  // slice columns, cells per thread along them
+  __shared__ __align__(16) float su[2][BK][BK];  // D* rows: su[.][m][a] = U/L D*[m][a]
+  __shared__ __align__(16) float sr[2][BK][W];   // the slice's rows: sr[.][m][c] = R[m][c]
+  __shared__ float tt[2][W][BK + 1];             // the slice turned around for its copy
+
+  rounding_prologue<RU>();
+  critical_path_priority();
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  int64_t J = blockIdx.x / P;
+  if (J >= K) ++J;
+  const int64_t k0 = K * BK, c0 = J * BK + (blockIdx.x % P) * W;
+  if (c0 >= n) return;  // uniform: a slice past the matrix
+  const int bK = (int)(n - k0 < BK ? n - k0 : BK);
+  const int bW = (int)(n - c0 < W ? n - c0 : W);
+  const bool rowor = fresh(K, J);
+  const int64_t nn = n * n;
+
+  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    float *Ub = U + b * nn;
+    float *Lb = L + b * nn;
+    // D* straight into LDS, one row segment of four at a time
+#pragma unroll
+    for (int it = 0; it < BK * BK / 4 / 256; ++it) {
+      const int e = tid + it * 256, a = e / (BK / 4), c = (e % (BK / 4)) * 4;
+      const int64_t g = (k0 + a) * n + k0 + c;
+      const int cnt = a < bK ? clamp4(bK - c) : 0;
+      *reinterpret_cast<float4 *>(&su[0][a][c]) = load4<VEC>(Ub + g, cnt, kInf, Ub);
+      *reinterpret_cast<float4 *>(&su[1][a][c]) = load4<VEC>(Lb + g, cnt, 0.0f, Lb);
+    }
+    // the slice from its fresh orientation: R[a][c] = M[k0+a][c0+c] (lanes
+    // along c), else M[c0+c][k0+a] (lanes along a)
+#pragma unroll
+    for (int it = 0; it < BK * W / 256; ++it) {
+      const int e = tid + it * 256;
+      const int a = rowor ? e / W : e % BK, c = rowor ? e % W : e / BK;
+      const bool in = a < bK && c < bW;
+      const int64_t g = in ? (rowor ? (k0 + a) * n + c0 + c : (c0 + c) * n + k0 + a) : 0;
+      const float xu = Ub[g], xl = Lb[g];
+      sr[0][a][c] = in ? xu : kInf;
+      sr[1][a][c] = in ? xl : 0.0f;
+    }
+    __syncthreads();
+    // this thread's cells: rows 4ty + r, columns CT*tx + q of the slice
+    float u[4][CT], l[4][CT];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < CT; ++q) {
+        u[r][q] = sr[0][ty * 4 + r][tx * CT + q];
+        l[r][q] = sr[1][ty * 4 + r][tx * CT + q];
+      }
+    // atoms past bK carry the neutral values (+inf above, 0 below)
+#pragma unroll 2
+    for (int m = 0; m < bK; m += 2) {
+      const float4 a0v = *reinterpret_cast<const float4 *>(&su[0][m][ty * 4]);
+      const float4 b0v = *reinterpret_cast<const float4 *>(&su[1][m][ty * 4]);
+      const float4 a1v = *reinterpret_cast<const float4 *>(&su[0][m + 1][ty * 4]);
+      const float4 b1v = *reinterpret_cast<const float4 *>(&su[1][m + 1][ty * 4]);
+      float ru0[CT], rl0[CT], ru1[CT], rl1[CT];
+#pragma unroll
+      for (int q = 0; q < CT; ++q) {
+        ru0[q] = sr[0][m][tx * CT + q];
+        rl0[q] = sr[1][m][tx * CT + q];
+        ru1[q] = sr[0][m + 1][tx * CT + q];
+        rl1[q] = sr[1][m + 1][tx * CT + q];
+      }
+      const float cu0[4] = {a0v.x, a0v.y, a0v.z, a0v.w}, cl0[4] = {b0v.x, b0v.y, b0v.z, b0v.w};
+      const float cu1[4] = {a1v.x, a1v.y, a1v.z, a1v.w}, cl1[4] = {b1v.x, b1v.y, b1v.z, b1v.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < CT; ++q)
+          relax2<RU>(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
+                     rl1[q]);
+    }
+    // the slice in both orientations: rows through sr, the copy through tt
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < CT; ++q) {
+        const float lo = lower_out<RU>(l[r][q]);
+        tt[0][tx * CT + q][ty * 4 + r] = u[r][q];
+        tt[1][tx * CT + q][ty * 4 + r] = lo;
+        l[r][q] = lo;
+      }
+    __syncthreads();  // every thread has left the loop: sr may be rewritten
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < CT; ++q) {
+        sr[0][ty * 4 + r][tx * CT + q] = u[r][q];
+        sr[1][ty * 4 + r][tx * CT + q] = l[r][q];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < BK * W / 256; ++it) {
+      const int e = tid + it * 256;
+      const int a = e / W, c = e % W;  // rows of band K, lanes along c
+      if (a < bK && c < bW) {
+        Ub[(k0 + a) * n + c0 + c] = sr[0][a][c];
+        Lb[(k0 + a) * n + c0 + c] = sr[1][a][c];
+      }
+      const int at = e % BK, ct = e / BK;  // the other orientation, lanes along a
+      if (at < bK && ct < bW) {
+        Ub[(c0 + ct) * n + k0 + at] = tt[0][ct][at];
+        Lb[(c0 + ct) * n + k0 + at] = tt[1][ct][at];
+      }
+    }
+    __syncthreads();  // LDS reuse by the next molecule
+  }
+}
+
 // One BK x BK block of the packed layout (one buffer P: U above the
 // diagonal, L below) as phase 3 handles it, 4x4 cells per thread on 256
 // threads.  An off-diagonal block (a0 < j0) reads its U as row segments
@@ -2179,6 +2304,14 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
 #undef DBS_PRODUCT
   const unsigned product_block =
       (unsigned)(wide_product ? product_threads<2>() : product_threads<4>());
+  // ... and its columns split over four workgroups where four times its
+  // workgroups still get a compute unit each (measured passes, against the
+  // 4x2-cell product: n1536 0.860 / 0.930 ms, n2048 1.168 / 1.259, n3072
+  // 2.239 / 2.359, 4 x n1024 0.639 / 0.682, 8 x n500 0.321 / 0.335; two
+  // slices lost 1-2 %: 16 x n500 0.382 / 0.373, 32 x n256 0.186 / 0.184)
+  const int product_p = wide_product && 4 * (TB - 1) * batch <= kSplitPanelFill ? 4 : 1;
+  auto product_slice = ru ? (vec ? k_product_slice<true, true, 4> : k_product_slice<false, true, 4>)
+                          : (vec ? k_product_slice<true, false, 4> : k_product_slice<false, false, 4>);
   // phase 3 of K (none for K < 0) beside phase 1 of Z (none for Z < 0);
   // grid.x = molecules, grid.y = the closure and then the quadrants
   const unsigned mx = (unsigned)(batch < kMaxGridX ? batch : kMaxGridX);
@@ -2194,6 +2327,9 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
                   U, L, n, batch, K, Z, infeasible);
   };
   auto product = [&](int64_t K, hipStream_t st) -> hipError_t {
+    if (product_p > 1)
+      return launch(prof, kProfPanel, product_slice, dim3((unsigned)((TB - 1) * product_p), gy),
+                    dim3(256), st, U, L, n, batch, K);
     return launch(prof, kProfPanel, product_kernel, dim3((unsigned)(TB - 1), gy),
                   dim3(product_block), st, U, L, n, batch, K);
   };
