@@ -98,23 +98,20 @@ def copy_calibration():
 def tiles_units_per_pass(n, batch, ahead, W):
     """(stored, dense) (i,j,k) triples of the bulk phase-3 launches over one pass.
 
-    The pass steps over W k-blocks at a time (dbs_step_blocks).  The launch of the step starting at block K runs the
-    step's atoms over the 64x64 quadrants of every TILE x TILE tile with
-    I <= J and stores every cell outside the step's bands (final after its
-    panel) and the bands of the `ahead` steps after it (updated ahead on the
-    second stream; fewer near the end).  `stored` counts those cells x the
-    launch's atoms; `dense` counts the full square of live rows x live
-    columns (the cells below the diagonal follow by symmetry)."""
-    T = -(-n // TILE)
+    The pass steps over W k-blocks at a time (dbs_step_blocks).  The launch of
+    the step starting at block K runs the step's atoms over the 64x64
+    quadrants (A, B) of the TILE x TILE tiles with A <= B (the upper tiles'
+    quadrants and the upper and diagonal ones of the diagonal tiles) and
+    stores every cell outside the step's bands (final after its panel) and
+    the bands of the `ahead` steps after it (updated ahead on the second
+    stream; fewer near the end).  `stored` counts those cells x the launch's
+    atoms; `dense` counts the full square of live rows x live columns (the
+    cells below the diagonal follow by symmetry)."""
     TB = -(-n // BK)
     stored = dense = 0
     for K in range(0, TB, W):
         end = min(TB, K + W * (1 + ahead))
-        bands = [(B * BK, min(n, B * BK + BK)) for B in range(K, end)]
-        r = []
-        for I in range(T):
-            lo, hi = I * TILE, min(n, I * TILE + TILE)
-            r.append(hi - lo - sum(max(0, min(hi, b1) - max(lo, b0)) for b0, b1 in bands))
+        r = [0 if K <= B < end else min(n, B * BK + BK) - B * BK for B in range(TB)]
         S, Q = sum(r), sum(x * x for x in r)
         atoms = min(n, (K + W) * BK) - K * BK
         stored += (S * S + Q) // 2 * atoms
@@ -124,11 +121,11 @@ def tiles_units_per_pass(n, batch, ahead, W):
 
 def executed_triples(n, batch):
     """(i,j,k) triples the symmetric schedule executes in one pass: every
-    cell of the TILE x TILE tiles with I <= J, for every atom k (phases 1-2
-    repeat the diagonal tile's rounds per panel workgroup; those repeats are
-    not counted)."""
-    T = -(-n // TILE)
-    rows = [min(n, (I + 1) * TILE) - I * TILE for I in range(T)]
+    cell of the 64x64 quadrants (A, B) with A <= B, for every atom k (phases
+    1-2 repeat the diagonal tile's rounds per panel workgroup; those repeats
+    are not counted)."""
+    TB = -(-n // BK)
+    rows = [min(n, (B + 1) * BK) - B * BK for B in range(TB)]
     return (n * n + sum(r * r for r in rows)) // 2 * n * batch
 
 

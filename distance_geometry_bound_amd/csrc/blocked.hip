@@ -22,10 +22,11 @@
 // phase 3; its panel is built from the phase 1-2 kernel and strips.
 //
 // Symmetric schedule.  U and L stay exactly symmetric, so only the cells of
-// TILE x TILE tiles (I,J) with I <= J are kept current ("fresh"); tiles below
-// the diagonal go stale and get their final values from the last launch that
-// writes their transposes (the last bulk launch of a pass writes each
-// off-diagonal quadrant at both positions; the panels are written in both
+// TILE x TILE tiles (I,J) with I < J, and of the upper and diagonal BK x BK
+// quadrants of the tiles (I,I), are kept current ("fresh"); the rest goes
+// stale and gets its final values from the last launch that writes its
+// transposes (the last bulk launch of a pass writes each quadrant whose
+// mirror is stale at both positions; the panels are written in both
 // orientations anyway).  Phase 3 therefore does half the work of a dense
 // schedule.  It
 // reads its operands U/L[i,k] and U/L[k,j] from row k only (U[i,k] = U[k,i]),
@@ -94,8 +95,10 @@ constexpr int kThreads = 256;
 // the same SIMD (wave priority only; the streams keep the default priority).
 __device__ __forceinline__ void critical_path_priority() { __builtin_amdgcn_s_setprio(2); }
 
-// (k-block tile a, k-block tile b) is fresh under the symmetric schedule
-__device__ __forceinline__ bool fresh(int64_t a, int64_t b) { return a / RATIO <= b / RATIO; }
+// Quadrant (band a, band b) is fresh under the symmetric schedule: it lies in
+// an upper TILE x TILE tile, or is an upper or diagonal quadrant of a diagonal
+// tile; with tiles RATIO whole bands wide, that is a <= b
+__device__ __forceinline__ bool fresh(int64_t a, int64_t b) { return a <= b; }
 
 // The early test of the infeasibility option, where phase 1 has closed a
 // diagonal tile (bZ atoms; thread (ty, tx) holds RT x CT of its cells): a
@@ -1344,7 +1347,7 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
   int64_t A, B;
   bool lower_left;
   if (!bulk_quadrant(blockIdx.x, n, xcd, A, B, lower_left) || A * BK >= n || B * BK >= n ||
-      (A >= X0 && A < X1) || (B >= X0 && B < X1))
+      (A >= X0 && A < X1) || (B >= X0 && B < X1) || lower_left)
     return;  // uniform over the workgroup, before any barrier
   const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
   const int bK = (int)(n - k0 < nk * BK ? n - k0 : nk * BK);
@@ -1360,7 +1363,7 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_quads(float *__restri
     Q::relax(sm, Ub, Lb, n, k0, bK, a0, j0, bA, bJ, tid, ty, tx, u, l);
     Q::store(Ub, Lb, n, a0, j0, bA, bJ, tid, u, l);
     if constexpr (MIR) {
-      if (A / RATIO < B / RATIO)  // uniform: the quadrant's tile is off the diagonal
+      if (!fresh(B, A))  // uniform: the quadrant's mirror is stale
         Q::store_transposed(Ub, Lb, n, a0, j0, bA, bJ, tid, u, l, lds.tr);
     }
     __syncthreads();
@@ -1462,7 +1465,8 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_lead(float *__restric
   const int64_t p = (blockIdx.y - 1) >> 2, qd = (blockIdx.y - 1) & 3;
   const int64_t J2 = tri_col(p), I2 = p - J2 * (J2 + 1) / 2;
   const int64_t A = RATIO * I2 + (qd >> 1), B = RATIO * J2 + (qd & 1);
-  if (A * BK >= n || B * BK >= n || A == K || B == K || (A == Z && B == Z))
+  if (A * BK >= n || B * BK >= n || A == K || B == K || (A == Z && B == Z) ||
+      (I2 == J2 && qd == 2))
     return;  // uniform over the workgroup, before any barrier
   const int64_t k0 = K * BK, a0 = A * BK, j0 = B * BK;
   const int bK = (int)(n - k0 < BK ? n - k0 : BK);
@@ -1476,7 +1480,7 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_lead(float *__restric
     Q::relax(sm, Ub, Lb, n, k0, bK, a0, j0, bA, bJ, tid, ty, tx, u, l);
     Q::store(Ub, Lb, n, a0, j0, bA, bJ, tid, u, l);
     if constexpr (MIR) {
-      if (A / RATIO < B / RATIO)  // uniform: the quadrant's tile is off the diagonal
+      if (!fresh(B, A))  // uniform: the quadrant's mirror is stale
         Q::store_transposed(Ub, Lb, n, a0, j0, bA, bJ, tid, u, l, lds.tr);
     }
     __syncthreads();

@@ -40,7 +40,28 @@ RATIO = TILE // BK
 
 
 def fresh(a, b):
-    return a // RATIO <= b // RATIO
+    """Band pair (a, b) is kept current: a quadrant of an upper TILE x TILE
+    tile, or an upper or diagonal quadrant of a diagonal tile (tiles are
+    RATIO whole bands wide, so these are the pairs a <= b)."""
+    return a // RATIO < b // RATIO or (a // RATIO == b // RATIO and a <= b)
+
+
+def stale_cells(n):
+    """Cells whose band pair is not kept current (mirrored at the end)."""
+    band = np.arange(n) // BK
+    return band[:, None] > band[None, :]
+
+
+def test_fresh_quadrants_are_the_upper_band_pairs():
+    # the kernels test freshness as a <= b on band indices; the tile form
+    # above and the stale set of the final mirror say the same
+    for a in range(4 * RATIO + 1):
+        for b in range(4 * RATIO + 1):
+            assert fresh(a, b) == (a <= b), (a, b)
+    n = 5 * BK + 7
+    band = np.arange(n) // BK
+    fr = np.array([[fresh(a, b) for b in band] for a in band])
+    assert np.array_equal(stale_cells(n), ~fr)
 
 
 class Model:
@@ -162,6 +183,12 @@ class Model:
             self.U[np.ix_(jb, kb_)], self.L[np.ix_(jb, kb_)] = nu.T, nl.T
         return parts
 
+    def mirror(self):
+        """The final mirror: every cell not kept current takes its transpose."""
+        stale = stale_cells(self.n)
+        self.U[stale], self.L[stale] = self.U.T[stale], self.L.T[stale]
+        return self.U, self.L
+
     @staticmethod
     def disjoint(parts):
         sym = lambda m: m | m.T
@@ -215,9 +242,9 @@ class Model:
         return reads, writes
 
     def bulk(self, Ks, skip_bands):
-        """Phase 3 of the blocks Ks on the BK x BK quadrants of the upper
-        TILE x TILE tiles, a quadrant in a band of Ks or in a skipped band
-        left whole."""
+        """Phase 3 of the blocks Ks on the BK x BK quadrants kept current (of
+        the upper TILE x TILE tiles, less the lower-left one of each diagonal
+        tile), a quadrant in a band of Ks or in a skipped band left whole."""
         n = self.n
         reads, writes = self.mask(), self.mask()
         live = np.ones(n, dtype=bool)
@@ -225,11 +252,12 @@ class Model:
             live[self.band(b)] = False
         kb = np.concatenate([self.band(K) for K in Ks])
         new = []
-        for J in range(self.T):
-            for I in range(J + 1):
-                ti = np.arange(I * TILE, min(n, I * TILE + TILE))
-                tj = np.arange(J * TILE, min(n, J * TILE + TILE))
-                rows, cols = ti[live[ti]], tj[live[tj]]
+        for B in range(self.TB):
+            for A in range(self.TB):
+                if not fresh(A, B):
+                    continue
+                ta, tb = self.band(A), self.band(B)
+                rows, cols = ta[live[ta]], tb[live[tb]]
                 if len(rows) == 0 or len(cols) == 0:
                     continue
                 reads[np.ix_(kb, np.concatenate([rows, cols]))] = True
@@ -329,10 +357,7 @@ class Model:
                 # and P[max][min] (L), so a footprint becomes its symmetric closure
                 assert not np.any(sym(sw) & sym(br | bw)), tag + ": packed overlap (writes)"
                 assert not np.any(sym(bw) & sym(sr)), tag + ": packed overlap (reads)"
-        tile = (np.arange(self.n) // BK) // RATIO
-        stale = tile[:, None] > tile[None, :]
-        self.U[stale], self.L[stale] = self.U.T[stale], self.L.T[stale]
-        return self.U, self.L
+        return self.mirror()
 
 
 @pytest.mark.parametrize("n,depth,W", [(65, 2, None), (130, 2, None), (200, 2, None),
@@ -369,23 +394,43 @@ def test_schedule_model_detects_a_planted_overlap():
 
 
 def test_schedule_model_detects_a_missing_panel_orientation():
-    # a step panel whose strips write only the fresh orientation leaves the
-    # stale copy of the earlier bands' rows behind; the bulk reads those rows
-    # as panel rows, so the pass must miss the oracle
+    # the panel of a block must leave its tiles current in both orientations:
+    # the bulk and the strips read the block's atom rows, and a product that
+    # writes only the fresh orientation leaves the other one stale
     class Broken(Model):
-        def step_panel(self, Ks):
-            out = []
-            for K in Ks:
-                out.extend(self.block_panel(K))
-                for r, A in enumerate(Ks):
-                    if A != K:
-                        out.append(("panel-strip",
-                                    *self.strip([K], A, set(Ks[:r]) | {K}, both=False)))
-            return out
+        def product(self, K):
+            U, L = self.U.copy(), self.L.copy()
+            parts = super().product(K)
+            kb = self.band(K)
+            for J in range(self.TB):
+                if J != K:
+                    jb = self.band(J)
+                    old = np.ix_(jb, kb) if fresh(K, J) else np.ix_(kb, jb)
+                    self.U[old], self.L[old] = U[old], L[old]
+            return parts
 
     U0, L0, _ = gen.random_sound_bounds(520, seed=520, box=6.0 + 520 / 8)
     Ue, Le = oracle.smooth(U0, L0)
     Um, Lm = Broken(U0, L0, depth=2, W=4).run()
+    assert not (np.array_equal(Um, pins.units(Ue)) and np.array_equal(Lm, pins.units(Le)))
+
+
+@pytest.mark.parametrize("lead", [False, True])
+def test_schedule_model_detects_a_tile_level_mirror(lead):
+    # the bulk leaves the lower-left quadrant of each diagonal tile to the
+    # final mirror; a mirror of whole tiles only keeps those quadrants as
+    # their own bands' panels left them, which misses the oracle
+    def tile_mirror(self):
+        tile = (np.arange(self.n) // BK) // RATIO
+        stale = tile[:, None] > tile[None, :]
+        self.U[stale], self.L[stale] = self.U.T[stale], self.L.T[stale]
+        return self.U, self.L
+
+    base = LeadModel if lead else Model
+    Broken = type("Broken", (base,), {"mirror": tile_mirror})
+    U0, L0, _ = gen.random_sound_bounds(330, seed=331, box=6.0 + 330 / 8)
+    Ue, Le = oracle.smooth(U0, L0)
+    Um, Lm = Broken(U0, L0).run()
     assert not (np.array_equal(Um, pins.units(Ue)) and np.array_equal(Lm, pins.units(Le)))
 
 
@@ -474,10 +519,7 @@ class LeadModel(Model):
                 # bulk part, which is equivalent when the two are disjoint
                 parts.append((f"closure({Z})", *self.closure_part(K, Z)))
             self.disjoint(parts)
-        tile = (np.arange(self.n) // BK) // RATIO
-        stale = tile[:, None] > tile[None, :]
-        self.U[stale], self.L[stale] = self.U.T[stale], self.L.T[stale]
-        return self.U, self.L
+        return self.mirror()
 
 
 @pytest.mark.parametrize("n", [65, 127, 128, 129, 200, 257, 330, 450])
