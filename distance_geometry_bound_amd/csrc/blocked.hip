@@ -57,6 +57,12 @@ constexpr int KC = 16;          // atoms per LDS chunk in phase 3
 // against two: n5632, 990 tiles, 9.78-9.80 against 10.14-10.17 ms; n6144,
 // 1176 tiles, 12.15 against 11.59 ms).
 constexpr int64_t kDeepTiles = 1024;
+// A single molecule in the dense layout runs two steps ahead, in steps of
+// one k-block, from this many tiles (measured, two steps of one block
+// against one step: n5120, 820 tiles, 7.51-7.54 against 7.58-7.70 ms;
+// n5376, 903 tiles, 8.07 against 8.36; n5632, 990 tiles, 9.06-9.14 against
+// 9.54-9.58; n4864, 741 tiles, 7.07 against 6.54).
+constexpr int64_t kDeepTilesSingle = 800;
 // k-blocks per step when running two steps ahead: 4 from kStep4Tiles phase-3
 // tiles (times molecules), 3 from kStep3Tiles, else 2.  Wider steps spread a
 // bulk launch's fixed costs over more atoms but leave more bands to the
@@ -64,6 +70,13 @@ constexpr int64_t kDeepTiles = 1024;
 // 2/3/4: n6144 11.8/13.2/14.0; n8192 25.5/24.9/25.8; n10240 49.5/47.8/47.0;
 // n12288 73.9/72.6/71.1).
 constexpr int64_t kStep4Tiles = 3000, kStep3Tiles = 1800;
+// A batch in the dense layout takes narrower steps: one k-block below
+// kStep2TilesBatch tiles, two below kStep4Tiles (measured, widths 1/2/3:
+// 128 x n500, 1280 tiles, 1.50/1.59/-; 32 x n1024, 1152, 2.31/2.38/-;
+// 8 x n2048, 1088, 3.78/4.02/-; 64 x n700, 1344, 1.82/1.97/-; 64 x n1024,
+// 2304, 4.13/4.04/4.27; 16 x n2048, 2176, 7.24/6.72/7.20; 128 x n700, 2688,
+// 3.37/3.26/3.38; 256 x n500, 2560, 2.85/2.79/2.76 ms).
+constexpr int64_t kStep2TilesBatch = 1600;
 // Below this many phase-3 tiles (times molecules) a bulk launch is too short
 // to hide the band strip that running ahead puts on the critical path.
 constexpr int64_t kAheadTiles = 256;
@@ -73,7 +86,12 @@ constexpr int64_t kPanelFill = 256;
 // Phase 1-2 workgroups (times molecules) up to which the dense phase 1-2
 // launch splits each panel tile's columns over several workgroups.
 constexpr int64_t kSplitPanelFill = 256;
-// Between these many phase-3 tiles (times molecules) a one-stream pass takes
+// A batch in the dense layout takes the lead schedule from kLeadTilesMin up
+// to kDeepTiles tiles (measured, lead against one step ahead: 4 x n2048, 544
+// tiles, 2.32 against 2.50-2.52 ms; 8 x n1536, 624, 1.93 against 2.06; 16 x
+// n1024, 576, 1.23 against 1.41-1.42; 2 x n3072, 600, 3.62 against 3.71-3.72;
+// 6 x n2048, 816, 3.00 against 3.23).  Otherwise,
+// between these many phase-3 tiles (times molecules) a one-stream pass takes
 // the lead schedule even where its phase 1-2 launch would not fill the chip:
 // there a bulk launch is long enough to hide the closure of the next
 // diagonal tile, and the product is shorter than a phase 1-2 launch.
@@ -2137,6 +2155,9 @@ int step_blocks(int64_t n, int64_t batch, const Sched &sched) {
   if (sched.step_blocks > 0) return sched.step_blocks;
   if (lookahead_bands(n, batch, sched) != 2) return 1;
   const int64_t T = ceil_div(n, TILE), tiles = T * (T + 1) / 2 * batch;
+  if (!sched.packed && batch > 1 && tiles >= kDeepTiles)
+    return tiles >= kStep4Tiles ? 4 : tiles >= kStep2TilesBatch ? 2 : 1;
+  if (!sched.packed && batch == 1 && tiles >= kDeepTilesSingle && tiles < kDeepTiles) return 1;
   return tiles >= kStep4Tiles ? 4 : tiles >= kStep3Tiles ? 3 : 2;
 }
 
@@ -2145,6 +2166,7 @@ int step_blocks(int64_t n, int64_t batch, const Sched &sched) {
 bool auto_lead(int64_t n, int64_t batch, bool packed) {
   const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
   const int64_t tiles = T * (T + 1) / 2 * batch;
+  if (!packed && batch >= 2) return tiles >= kLeadTilesMin && tiles < kDeepTiles;
   return (batch >= 2 && (TB - 1) * batch > kPanelFill) ||
          (tiles >= (packed ? kLeadTilesMinPacked : kLeadTilesMin) && tiles < kLeadTilesMax);
 }
@@ -2164,7 +2186,7 @@ int lookahead_bands(int64_t n, int64_t batch, const Sched &sched) {
   if (TB <= 1 || T <= 1) return 0;
   if (sched.lookahead >= 0) return sched.lookahead;
   const int64_t tiles = T * (T + 1) / 2 * batch;
-  if (tiles >= kDeepTiles) return 2;
+  if (tiles >= kDeepTiles || (!sched.packed && batch == 1 && tiles >= kDeepTilesSingle)) return 2;
   // the lead schedule runs on one stream
   if (sched.step_blocks <= 1 &&
       (sched.lead == 1 || (sched.lead < 0 && auto_lead(n, batch, sched.packed))))

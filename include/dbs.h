@@ -367,7 +367,8 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uin
  * dbs_schedule -- the schedule a blocked pass (DBS_ALGO_BLOCKED) on the dense
  * layout takes for this shape under `opts` (NULL: the defaults);
  * dbs_schedule_packed the same for the packed layout (dbs_smooth_packed and
- * its variants), which differs only in the lead schedule's automatic choice:
+ * its variants).  The rules below are the packed layout's; the dense layout
+ * differs where noted [dense]:
  *   *lookahead    how many steps it updates ahead on its second stream:
  *     0  no look-ahead: a single k-block or phase-3 tile; fewer than 256
  *        phase-3 tiles x molecules (the bulk launch is shorter than the band
@@ -380,12 +381,14 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uin
  *        half's phase 1-2 launches run beside the other half's phase 3;
  *        otherwise the pass uses the caller's stream alone;
  *     1  otherwise, below 1024 tiles x molecules: steps of one k-block;
- *     2  from 1024 tiles x molecules: steps of several k-blocks.  In the
- *        dense layout phase 1 of a block is then the closure of its diagonal
- *        tile alone (one workgroup per molecule) and phase 2 a product from
- *        it, both on the second stream.
+ *     2  from 1024 tiles x molecules [dense: and for a single molecule from
+ *        800 tiles].  In the dense layout phase 1 of a block is then the
+ *        closure of its diagonal tile alone (one workgroup per molecule)
+ *        and phase 2 a product from it, both on the second stream.
  *   *step_blocks  k-blocks per step: where it runs two steps ahead, 4 from
- *     3000 phase-3 tiles x molecules, 3 from 1800, else 2; otherwise 1.  A
+ *     3000 phase-3 tiles x molecules, 3 from 1800, else 2 [dense: a single
+ *     molecule below 1024 tiles 1; a batch 1 below 1600 tiles, 2 below
+ *     3000, else 4]; otherwise 1.  A
  *     step of w blocks is blocked Floyd-Warshall with 64w atoms per phase-3
  *     launch; its panel (the rows of the step's bands, final for all of its
  *     rounds) is built from the 64-wide phases 1-2 and phase-3 strips.
@@ -393,8 +396,9 @@ int dbs_check_packed(const float *P, int64_t n, int64_t batch, void *stream, uin
  *     a pass without look-ahead in steps of one k-block and n below 23 040
  *     (the phase-3 quadrants of a launch fit one grid dimension), and is
  *     chosen where a batch has more than 256 phase 1-2 workgroups
- *     ((k-blocks - 1) x molecules), and from 64 (packed layout: 256) to
- *     511 phase-3 tiles x molecules.  Per k-block K it runs two launches on the caller's stream:
+ *     ((k-blocks - 1) x molecules), and from 256 to 511 phase-3 tiles x
+ *     molecules [dense: for a batch from 64 to 1023 tiles x molecules, for
+ *     a single molecule from 64 to 511].  Per k-block K it runs two launches on the caller's stream:
  *     phase 2 of K as a product with K's diagonal tile, closed the launch
  *     before, and one launch that holds phase 3 of K and, beside it, phase 1
  *     of K + 1 (phase 3 of K on the diagonal tile of K + 1, then its

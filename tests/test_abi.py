@@ -181,12 +181,15 @@ def test_lookahead_bands_query():
     assert lib.dbs_lookahead_bands(200, 1) == 0       # 3 tiles: bulk shorter than a strip
     assert lib.dbs_lookahead_bands(1024, 1) == 0      # 36 tiles
     assert lib.dbs_lookahead_bands(500, 64) == 0      # 448 panel workgroups fill the chip
-    assert lib.dbs_lookahead_bands(130, 129) == 0     # 258 panel workgroups: split batch
+    assert lib.dbs_lookahead_bands(130, 129) == 0     # 387 tiles, a batch: the lead schedule
     assert lib.dbs_lookahead_bands(130, 128) == 0     # 384 tiles: the lead schedule
     assert lib.dbs_lookahead_bands(2944, 1) == 0      # 276 tiles: the lead schedule
     assert lib.dbs_lookahead_bands(4096, 1) == 1
-    assert lib.dbs_lookahead_bands(5120, 1) == 1      # 820 tiles
-    assert lib.dbs_lookahead_bands(5632, 1) == 1      # 990 tiles
+    assert lib.dbs_lookahead_bands(4864, 1) == 1      # 741 tiles
+    assert lib.dbs_lookahead_bands(5120, 1) == 2      # 820 tiles, one molecule
+    assert lib.dbs_lookahead_bands(5632, 1) == 2      # 990 tiles
+    assert lib.dbs_lookahead_bands(2048, 4) == 0      # 544 tiles, a batch: the lead schedule
+    assert lib.dbs_lookahead_bands(1024, 28) == 0     # 1008 tiles, a batch
     assert lib.dbs_lookahead_bands(6144, 1) == 2      # 1176 tiles
     assert lib.dbs_lookahead_bands(4096, 2) == 2      # 1056 tiles x molecules
     assert lib.dbs_lookahead_bands(12288, 1) == 2
@@ -204,10 +207,9 @@ def test_schedule_query_with_forced_values():
     assert dgb.schedule(12288) == (2, 4, 0) and dgb.schedule(200) == (0, 1, 0)
     assert dgb.schedule(200, step_blocks=4) == (0, 4, 0)
     assert dgb.schedule(12288, lookahead=1, step_blocks=3) == (1, 3, 0)
-    # the lead schedule: automatic where a batch's phase 1-2 launch would
-    # fill the chip, and between 64 and 512 phase-3 tiles (128-atom tiles
-    # I <= J, times molecules); forced on any one-stream pass with one-block
-    # steps
+    # the lead schedule: automatic for a batch from 64 to 1023 phase-3 tiles
+    # (128-atom tiles I <= J, times molecules), for one molecule from 64 to
+    # 511; forced on any one-stream pass with one-block steps
     assert dgb.schedule(500, 64) == (0, 1, 1) and dgb.schedule(130, 129) == (0, 1, 1)
     assert dgb.schedule(300, 100) == (0, 1, 1)               # 600 tiles, 400 panel tiles
     assert dgb.schedule(300, 100, lead=False) == (0, 1, 0)   # the split batch instead
@@ -217,6 +219,14 @@ def test_schedule_query_with_forced_values():
     assert dgb.schedule(2048) == (0, 1, 1) and dgb.schedule(3072) == (0, 1, 1)  # 136, 300
     assert dgb.schedule(500, 16) == (0, 1, 1) and dgb.schedule(130, 128) == (0, 1, 1)
     assert dgb.schedule(4096) == (1, 1, 0)                   # 528 tiles: one step ahead
+    assert dgb.schedule(4864) == (1, 1, 0)                   # 741 tiles
+    assert dgb.schedule(5120) == (2, 1, 0)                   # 820: two ahead, one-block steps
+    assert dgb.schedule(6144) == (2, 2, 0)                   # 1176 tiles
+    assert dgb.schedule(1024, 16) == (0, 1, 1) and dgb.schedule(2048, 4) == (0, 1, 1)
+    assert dgb.schedule(3072, 2) == (0, 1, 1) and dgb.schedule(2048, 6) == (0, 1, 1)
+    assert dgb.schedule(500, 128) == (2, 1, 0)               # a batch, 1280 tiles
+    assert dgb.schedule(1024, 64) == (2, 2, 0)               # 2304 tiles
+    assert dgb.schedule(500, 512) == (2, 4, 0)               # 5120 tiles
     assert dgb.schedule(3072, lead=False) == (1, 1, 0)
     # the packed layout takes the lead window from 256 tiles
     assert dgb.schedule(1536, packed=True) == (0, 1, 0)      # 78 tiles
@@ -225,6 +235,9 @@ def test_schedule_query_with_forced_values():
     assert dgb.schedule(3072, packed=True) == (0, 1, 1)      # 300 tiles
     assert dgb.schedule(500, 64, packed=True) == (0, 1, 1)   # the panel launch fills the chip
     assert dgb.schedule(4096, packed=True) == (1, 1, 0)
+    assert dgb.schedule(5120, packed=True) == (1, 1, 0)      # the dense rules above only
+    assert dgb.schedule(2048, 4, packed=True) == (1, 1, 0)
+    assert dgb.schedule(500, 128, packed=True) == (2, 2, 0)
     assert dgb.schedule(12288, packed=True) == (2, 4, 0)
     assert dgb.schedule(1536, packed=True, lead=True) == (0, 1, 1)
     assert dgb.schedule(500, 64, lead=False) == (0, 1, 0)
@@ -250,7 +263,8 @@ def test_step_blocks_query():
     # steps of several k-blocks where the pass runs two steps ahead, else one
     lib = dgb.lib()
     assert dgb.step_blocks(12288) == 4 and dgb.step_blocks(10240) == 4   # 4656, 3240 tiles
-    assert dgb.step_blocks(8192) == 3 and dgb.step_blocks(6144, 2) == 3  # 2080, 2352
+    assert dgb.step_blocks(8192) == 3 and dgb.step_blocks(6144, 2) == 2  # 2080, 2352
+    assert dgb.step_blocks(500, 128) == 1 and dgb.step_blocks(1024, 64) == 2  # 1280, 2304
     assert dgb.step_blocks(5632) == 1 and dgb.step_blocks(6144) == 2     # 990, 1176
     assert dgb.step_blocks(4096) == 1 and dgb.step_blocks(200) == 1
     assert lib.dbs_step_blocks(0, 1) == -1 and lib.dbs_step_blocks(5, 0) == -1

@@ -233,21 +233,44 @@ def test_lead_schedule(n, batch):
 
 
 @pytest.mark.parametrize("n,batch", [(2048, 1), (700, 12), (1500, 2), (130, 128), (1536, 1),
-                                     (500, 8), (300, 16)])
+                                     (500, 8), (300, 16), (300, 100), (700, 40)])
 def test_automatic_lead_window(n, batch):
-    # between 64 and 512 phase-3 tiles (times molecules) the automatic
-    # schedule of a dense blocked pass is the lead one, whether or not the
-    # phase 1-2 launch would fill the chip (4x2-cell products); the packed
-    # layout takes it from 256 tiles: dense, directed and packed blocked
-    # passes against the oracle
+    # from 64 phase-3 tiles (times molecules) the automatic schedule of a
+    # dense blocked pass is the lead one, up to 512 tiles for one molecule
+    # and 1024 for a batch, whether or not the phase 1-2 launch would fill
+    # the chip; the packed layout takes it from 256 to 512 tiles, or where
+    # that launch fills the chip: dense, directed and packed blocked passes
+    # against the oracle
     from oracle import steps
     assert dgb.schedule(n, batch) == (0, 1, 1)
     T = -(-n // 128)
-    assert dgb.schedule(n, batch, packed=True)[2] == (1 if T * (T + 1) // 2 * batch >= 256 or
+    tiles = T * (T + 1) // 2 * batch
+    assert dgb.schedule(n, batch, packed=True)[2] == (1 if 256 <= tiles < 512 or
                                                       (-(-n // 64) - 1) * batch > 256 else 0)
     U0, L0 = sound_input(n, batch, seed=5 * n + batch)
     Ue, Le = oracle.smooth(U0, L0)
     tag = f"automatic n={n} batch={batch}"
+    Ug, Lg = gpu_pass(U0, L0, "blocked")
+    assert_bits(Ug, Lg, Ue, Le, "dense " + tag)
+    U, L = dev(U0), dev(L0)
+    dgb.smooth_directed(U, L, algo="blocked")
+    assert_bits(host(U), host(L), Ue, Le, "directed " + tag)
+    P = dgb.pack(dev(U0), dev(L0))
+    dgb.smooth_packed(P, algo="blocked")
+    assert np.array_equal(host(P).view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
+
+
+@pytest.mark.parametrize("n,batch,width", [(300, 171, 1), (500, 103, 1), (300, 300, 2)])
+def test_automatic_two_ahead_for_batches(n, batch, width):
+    # a dense batch from 1024 phase-3 tiles runs two steps ahead in steps of
+    # one k-block, from 1600 tiles of two: dense, directed and packed passes
+    # (the packed layout keeps its own widths) against the oracle
+    from oracle import steps
+    assert dgb.schedule(n, batch) == (2, width, 0)
+    assert dgb.schedule(n, batch, packed=True)[0] == 2
+    U0, L0 = sound_input(n, batch, seed=13 * n + batch)
+    Ue, Le = oracle.smooth(U0, L0)
+    tag = f"two ahead n={n} batch={batch}"
     Ug, Lg = gpu_pass(U0, L0, "blocked")
     assert_bits(Ug, Lg, Ue, Le, "dense " + tag)
     U, L = dev(U0), dev(L0)
