@@ -52,10 +52,11 @@ constexpr int BK = 64;          // atoms per k-block (phases 1 and 2 tile size)
 constexpr int TILE = 128;       // freshness granularity: tiles I <= J are kept current
 constexpr int RATIO = TILE / BK;
 constexpr int KC = 16;          // atoms per LDS chunk in phase 3
-// Phase-3 tiles (times molecules) from which the pass runs two steps ahead,
-// in steps of two or more k-blocks (measured crossover, one step ahead
-// against two: n5632, 990 tiles, 9.78-9.80 against 10.14-10.17 ms; n6144,
-// 1176 tiles, 12.15 against 11.59 ms).
+// Phase-3 tiles (times molecules) from which the pass runs two steps ahead
+// (the packed layout's crossover, and the dense one's for a batch, below
+// which a dense batch takes the lead schedule; measured, one step ahead
+// against two in two-block steps: n5632, 990 tiles, 9.78-9.80 against
+// 10.14-10.17 ms; n6144, 1176 tiles, 12.15 against 11.59 ms).
 constexpr int64_t kDeepTiles = 1024;
 // A single molecule in the dense layout runs two steps ahead, in steps of
 // one k-block, from this many tiles (measured, two steps of one block
