@@ -364,7 +364,7 @@ class Model:
                                        (257, 2, None), (330, 2, None), (130, 1, None),
                                        (257, 1, None), (330, 2, 3), (330, 2, 4), (257, 1, 3),
                                        (200, 1, 2), (520, 2, 3), (520, 2, 4), (700, 2, 4),
-                                       (520, 1, 4)])
+                                       (520, 1, 4), (257, 2, 1), (330, 2, 1), (520, 2, 1)])
 def test_schedule_model_matches_oracle_and_streams_are_disjoint(n, depth, W):
     U0, L0, _ = gen.random_sound_bounds(n, seed=n, box=6.0 + n / 8)
     Ue, Le = oracle.smooth(U0, L0)
