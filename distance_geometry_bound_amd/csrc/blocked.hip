@@ -2167,7 +2167,8 @@ int step_blocks(int64_t n, int64_t batch, const Sched &sched) {
 bool auto_lead(int64_t n, int64_t batch, bool packed) {
   const int64_t TB = ceil_div(n, BK), T = ceil_div(n, TILE);
   const int64_t tiles = T * (T + 1) / 2 * batch;
-  if (!packed && batch >= 2) return tiles >= kLeadTilesMin && tiles < kDeepTiles;
+  if (!packed && batch >= 2 && tiles >= kLeadTilesMin && tiles < kDeepTiles) return true;
+  // (molecules of one tile never run ahead: from kDeepTiles they keep this rule)
   return (batch >= 2 && (TB - 1) * batch > kPanelFill) ||
          (tiles >= (packed ? kLeadTilesMinPacked : kLeadTilesMin) && tiles < kLeadTilesMax);
 }

@@ -227,6 +227,7 @@ def test_schedule_query_with_forced_values():
     assert dgb.schedule(500, 128) == (2, 1, 0)               # a batch, 1280 tiles
     assert dgb.schedule(1024, 64) == (2, 2, 0)               # 2304 tiles
     assert dgb.schedule(500, 512) == (2, 4, 0)               # 5120 tiles
+    assert dgb.schedule(128, 1200) == (0, 1, 1)              # one tile each: never ahead
     assert dgb.schedule(3072, lead=False) == (1, 1, 0)
     # the packed layout takes the lead window from 256 tiles
     assert dgb.schedule(1536, packed=True) == (0, 1, 0)      # 78 tiles

@@ -69,3 +69,45 @@ def test_random_case_matches_oracle(seed):
     else:
         assert np.array_equal(A.view(np.uint32), Ue.view(np.uint32)), tag
         assert np.array_equal(B.view(np.uint32), Le.view(np.uint32)), tag
+
+
+def _batch_case(seed):
+    # many small molecules: 100 to 4000 phase-3 tiles x molecules, across the
+    # automatic choices for batches (lead below 1024 tiles, then two steps
+    # ahead in steps of one, two or four k-blocks)
+    rng = np.random.default_rng(7000 + seed)
+    n = int(rng.integers(65, 330))
+    T = -(-n // 128)
+    tiles = T * (T + 1) // 2
+    batch = int(rng.integers(max(2, 100 // tiles), 4000 // tiles + 1))
+    batch = min(batch, 1200)
+    packed = bool(rng.integers(0, 2))
+    directed = bool(rng.integers(0, 2))
+    return n, batch, packed, directed
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_batch_matches_oracle(seed):
+    n, batch, packed, directed = _batch_case(seed)
+    sched = dgb.schedule(n, batch, packed=packed)
+    tag = f"seed={seed} n={n} batch={batch} packed={packed} directed={directed} schedule={sched}"
+    U0, L0, _ = gen.random_sound_bounds(n, seed=seed, batch=batch, box=6.0 + n / 8)
+    Ue, Le = oracle.smooth(U0, L0)
+    A, B = _run(U0, L0, n, "auto", packed, directed, -1, False, -1, None)
+    if packed:
+        assert np.array_equal(A.view(np.uint32), steps.pack(Ue, Le).view(np.uint32)), tag
+    else:
+        assert np.array_equal(A.view(np.uint32), Ue.view(np.uint32)), tag
+        assert np.array_equal(B.view(np.uint32), Le.view(np.uint32)), tag
+
+
+def test_single_molecule_two_ahead_in_one_block_steps():
+    # n = 5120 (820 phase-3 tiles): a single dense molecule runs two steps
+    # ahead in steps of one k-block; every entry against the oracle
+    n = 5120
+    assert dgb.schedule(n, 1) == (2, 1, 0)
+    U0, L0, _ = gen.random_sound_bounds(n, seed=n, batch=1, box=6.0 + n / 8)
+    Ue, Le = oracle.smooth(U0, L0)
+    A, B = _run(U0, L0, n, "auto", False, False, -1, False, -1, None)
+    assert np.array_equal(A.view(np.uint32), Ue.view(np.uint32))
+    assert np.array_equal(B.view(np.uint32), Le.view(np.uint32))
