@@ -30,8 +30,10 @@
 // orientations anyway).  Phase 3 therefore does half the work of a dense
 // schedule.  It
 // reads its operands U/L[i,k] and U/L[k,j] from row k only (U[i,k] = U[k,i]),
-// so phase 2 must leave all of row band K fresh: it updates each panel tile
-// from whichever orientation is fresh and writes both orientations.
+// so phase 2 must leave all of row band K current: it updates each panel
+// tile from whichever orientation is fresh and writes its row orientation
+// and its fresh one (the products leave a stale copy right of the diagonal,
+// which nothing reads before the panel of that band rewrites it).
 //
 // Phase 3: a 256-thread workgroup owns a 64x64 block, each thread a 4x4
 // register tile (512 threads with 4x2 tiles when a launch has fewer blocks
@@ -1519,8 +1521,11 @@ __global__ __launch_bounds__((BK / RT) * (BK / CT)) void k_lead(float *__restric
 // panel tile, which the phase 1-2 kernel does.  Unlike those rounds the
 // products need no barrier per atom: D* and R are staged in LDS whole, and
 // every thread relaxes its cells over the atoms as the bulk does.  R is
-// read from its fresh orientation and written in both (dense), or as its U
-// and L slots (packed).
+// read from its fresh orientation and written in its row orientation, which
+// the bulk of K reads, and in the other one where that is fresh (J < K) or
+// where block J is past the end Kend of the pass or range (dense).  For
+// K < J < Kend the other copy stays stale: no launch reads it before the
+// phase 2 of J rewrites tile (J, K).  Packed: as its U and L slots.
 // Thread (ty, tx) owns 4 x CT cells of R.  CT = 4 (256 threads) runs beside
 // the bulk (the two-step look-ahead); CT = 2 (512 threads, dense layout)
 // where the launch has the chip to itself: D* and R take 64 KB of LDS, so a
@@ -1533,7 +1538,7 @@ template <bool VEC, bool PK, bool RU, int CT>
 __global__ __launch_bounds__(product_threads<CT>()) void k_product(float *__restrict__ U,
                                                                    float *__restrict__ L,
                                                                    int64_t n, int64_t batch,
-                                                                   int64_t K) {
+                                                                   int64_t K, int64_t Kend) {
   static_assert(CT == 4 || (CT == 2 && !PK), "4x4 cells, or 4x2 on the dense layout");
   constexpr int NTX = BK / CT, NTH = product_threads<CT>();
   __shared__ __align__(16) float su[2][BK][BK];  // D* rows: su[.][m][a] = U/L D*[m][a]
@@ -1688,8 +1693,10 @@ __global__ __launch_bounds__(product_threads<CT>()) void k_product(float *__rest
     } else {
       store_rows<VEC, CT>(Ub, n, k0, j0, bK, bJ, wy, wx, u);
       store_rows<VEC, CT>(Lb, n, k0, j0, bK, bJ, wy, wx, l);
-      store_transposed<VEC, CT>(Ub, n, k0, j0, bK, bJ, wy, wx, u, tr);
-      store_transposed<VEC, CT>(Lb, n, k0, j0, bK, bJ, wy, wx, l, tr);
+      if (J < K || J >= Kend) {  // uniform: the other orientation is read
+        store_transposed<VEC, CT>(Ub, n, k0, j0, bK, bJ, wy, wx, u, tr);
+        store_transposed<VEC, CT>(Lb, n, k0, j0, bK, bJ, wy, wx, l, tr);
+      }
     }
     __syncthreads();  // LDS reuse by the next molecule
   }
@@ -1702,11 +1709,12 @@ __global__ __launch_bounds__(product_threads<CT>()) void k_product(float *__rest
 // workgroups than the chip has CUs, this spreads each tile over P of them.
 // R's slice is staged through LDS from its fresh orientation (lanes along
 // the slice's rows or columns, so both reads are row segments) and written
-// back the same way in both orientations.
+// back the same way, in its row orientation and, left of the diagonal, in
+// the other one (as k_product).
 template <bool VEC, bool RU, int P>
 __global__ __launch_bounds__(256) void k_product_slice(float *__restrict__ U,
                                                       float *__restrict__ L, int64_t n,
-                                                      int64_t batch, int64_t K) {
+                                                      int64_t batch, int64_t K, int64_t Kend) {
   static_assert(P == 2 || P == 4, "two or four column slices");
   constexpr int W = BK / P, CT = W / 16;  // slice columns, cells per thread along them
   __shared__ __align__(16) float su[2][BK][BK];  // D* rows: su[.][m][a] = U/L D*[m][a]
@@ -1783,7 +1791,7 @@ __global__ __launch_bounds__(256) void k_product_slice(float *__restrict__ U,
           relax2<RU>(u[r][q], l[r][q], cu0[r], cl0[r], ru0[q], rl0[q], cu1[r], cl1[r], ru1[q],
                      rl1[q]);
     }
-    // the slice in both orientations: rows through sr, the copy through tt
+    // the slice's rows through sr, its other orientation through tt
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -1811,7 +1819,7 @@ __global__ __launch_bounds__(256) void k_product_slice(float *__restrict__ U,
         Lb[(k0 + a) * n + c0 + c] = sr[1][a][c];
       }
       const int at = e % BK, ct = e / BK;  // the other orientation, lanes along a
-      if (at < bK && ct < bW) {
+      if ((J < K || J >= Kend) && at < bK && ct < bW) {  // (as k_product)
         Ub[(c0 + ct) * n + k0 + at] = tt[0][ct][at];
         Lb[(c0 + ct) * n + k0 + at] = tt[1][ct][at];
       }
@@ -2357,9 +2365,9 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   auto product = [&](int64_t K, hipStream_t st) -> hipError_t {
     if (product_p > 1)
       return launch(prof, kProfPanel, product_slice, dim3((unsigned)((TB - 1) * product_p), gy),
-                    dim3(256), st, U, L, n, batch, K);
+                    dim3(256), st, U, L, n, batch, K, K1);
     return launch(prof, kProfPanel, product_kernel, dim3((unsigned)(TB - 1), gy),
-                  dim3(product_block), st, U, L, n, batch, K);
+                  dim3(product_block), st, U, L, n, batch, K, K1);
   };
   if (lead_sched) {
     hipError_t e = lead(-1, K0, s, false);

@@ -180,7 +180,10 @@ class Model:
             parts.append((f"product({K}) tile {J}", reads, writes))
         for kb_, jb, nu, nl in new:
             self.U[np.ix_(kb_, jb)], self.L[np.ix_(kb_, jb)] = nu, nl
-            self.U[np.ix_(jb, kb_)], self.L[np.ix_(jb, kb_)] = nu.T, nl.T
+            # right of the diagonal the other copy stays stale until the
+            # panel of J rewrites it (a range ending before J writes it here)
+            if jb[0] < kb_[0]:
+                self.U[np.ix_(jb, kb_)], self.L[np.ix_(jb, kb_)] = nu.T, nl.T
         return parts
 
     def mirror(self):
@@ -394,9 +397,9 @@ def test_schedule_model_detects_a_planted_overlap():
 
 
 def test_schedule_model_detects_a_missing_panel_orientation():
-    # the panel of a block must leave its tiles current in both orientations:
-    # the bulk and the strips read the block's atom rows, and a product that
-    # writes only the fresh orientation leaves the other one stale
+    # the panel of a block must leave its atom rows current: the bulk and the
+    # strips read them, and a product that writes only the fresh orientation
+    # leaves the row orientation of the tiles left of the diagonal stale
     class Broken(Model):
         def product(self, K):
             U, L = self.U.copy(), self.L.copy()
@@ -454,7 +457,8 @@ class LeadModel(Model):
                   every panel tile (K,J), J != K, read from its fresh
                   orientation, becomes the min/max over the atoms m of band K
                   of D*[a][m] (+/-) R[m][c] with R as read (one workgroup per
-                  tile), written in both orientations;
+                  tile), written in its row orientation and, for J < K, in
+                  the other (its fresh one) too;
       lead(K, Z)  in one launch: phase 3 of K on every quadrant outside band
                   K and outside the diagonal tile (Z,Z), Z = K + 1 (the bulk
                   workgroups), and phase 3 of K on (Z,Z) followed by the
