@@ -150,9 +150,10 @@ class Model:
         writes[ix] = True
         return reads, writes
 
-    def product(self, K):
+    def product(self, K, Kend=None):
         """Phase 2 of K from the closed diagonal tile: (reads, writes) per
-        panel workgroup."""
+        panel workgroup (Kend: the end of the pass or range)."""
+        Kend = self.TB if Kend is None else Kend
         kb = self.band(K)
         dix = np.ix_(kb, kb)
         Du, Dl = self.U[dix].copy(), self.L[dix].copy()
@@ -174,21 +175,27 @@ class Model:
             bl = np.maximum((Dl[:, :, None] - Ru[None, :, :]).max(1),
                             (Rl[None, :, :] - Du[:, :, None]).max(1))
             nu, nl = np.minimum(Ru, bu), np.maximum(Rl, bl)
-            new.append((kb, jb, nu, nl))
+            new.append((kb, jb, nu, nl, J))
             writes[np.ix_(kb, jb)] = True
             writes[np.ix_(jb, kb)] = True
             parts.append((f"product({K}) tile {J}", reads, writes))
-        for kb_, jb, nu, nl in new:
+        for kb_, jb, nu, nl, J in new:
             self.U[np.ix_(kb_, jb)], self.L[np.ix_(kb_, jb)] = nu, nl
             # right of the diagonal the other copy stays stale until the
             # panel of J rewrites it (a range ending before J writes it here)
-            if jb[0] < kb_[0]:
+            if J < K or J >= Kend:
                 self.U[np.ix_(jb, kb_)], self.L[np.ix_(jb, kb_)] = nu.T, nl.T
         return parts
 
-    def mirror(self):
-        """The final mirror: every cell not kept current takes its transpose."""
+    def mirror(self, excl=()):
+        """The last launch's mirror: the stale cells of the quadrants that
+        launch computes (every band but `excl`, the bands of its own step)
+        take their transposes.  The stale cells of the `excl` bands keep what
+        the panels wrote: they must be current already."""
         stale = stale_cells(self.n)
+        band = np.arange(self.n) // BK
+        inx = np.isin(band, list(excl))
+        stale &= ~(inx[:, None] | inx[None, :])
         self.U[stale], self.L[stale] = self.U.T[stale], self.L.T[stale]
         return self.U, self.L
 
@@ -360,7 +367,7 @@ class Model:
                 # and P[max][min] (L), so a footprint becomes its symmetric closure
                 assert not np.any(sym(sw) & sym(br | bw)), tag + ": packed overlap (writes)"
                 assert not np.any(sym(bw) & sym(sr)), tag + ": packed overlap (reads)"
-        return self.mirror()
+        return self.mirror(steps[-1])
 
 
 @pytest.mark.parametrize("n,depth,W", [(65, 2, None), (130, 2, None), (200, 2, None),
@@ -423,9 +430,11 @@ def test_schedule_model_detects_a_tile_level_mirror(lead):
     # the bulk leaves the lower-left quadrant of each diagonal tile to the
     # final mirror; a mirror of whole tiles only keeps those quadrants as
     # their own bands' panels left them, which misses the oracle
-    def tile_mirror(self):
-        tile = (np.arange(self.n) // BK) // RATIO
-        stale = tile[:, None] > tile[None, :]
+    def tile_mirror(self, excl=()):
+        band = np.arange(self.n) // BK
+        tile = band // RATIO
+        inx = np.isin(band, list(excl))
+        stale = (tile[:, None] > tile[None, :]) & ~(inx[:, None] | inx[None, :])
         self.U[stale], self.L[stale] = self.U.T[stale], self.L.T[stale]
         return self.U, self.L
 
@@ -510,12 +519,13 @@ class LeadModel(Model):
             self.U[cell], self.L[cell] = nu, nl
         return reads, writes
 
-    def run(self):
-        TB = self.TB
-        self.closure_part(-1, 0)
-        for K in range(TB):
-            self.disjoint(self.product(K))
-            Z = K + 1 if K + 1 < TB else -1
+    def run(self, K0=0, K1=None):
+        """The k-blocks K0 .. K1-1 (a whole pass by default)."""
+        K1 = self.TB if K1 is None else K1
+        self.closure_part(-1, K0)
+        for K in range(K0, K1):
+            self.disjoint(self.product(K, K1))
+            Z = K + 1 if K + 1 < K1 else -1
             parts = [(f"bulk({K})", *self.bulk_part(K, Z))]
             if Z >= 0:
                 # the closure workgroup computes from the state before the
@@ -523,7 +533,7 @@ class LeadModel(Model):
                 # bulk part, which is equivalent when the two are disjoint
                 parts.append((f"closure({Z})", *self.closure_part(K, Z)))
             self.disjoint(parts)
-        return self.mirror()
+        return self.mirror({K1 - 1})
 
 
 @pytest.mark.parametrize("n", [65, 127, 128, 129, 200, 257, 330, 450])
@@ -533,6 +543,35 @@ def test_lead_schedule_matches_oracle_and_launches_are_disjoint(n):
     Um, Lm = LeadModel(U0, L0).run()
     assert np.array_equal(Um, pins.units(Ue))
     assert np.array_equal(Lm, pins.units(Le))
+
+
+@pytest.mark.parametrize("n,K0,K1", [(200, 0, 1), (200, 0, 2), (200, 1, 3), (330, 0, 2),
+                                      (330, 2, 4), (330, 1, 6), (450, 3, 5)])
+def test_lead_ranges_match_oracle(n, K0, K1):
+    # a range of k-blocks K0 .. K1-1 from the state after the rounds before
+    # it: the result, both copies of every cell, equals the oracle's rounds
+    # (a product leaves the stale copy of (K, J), K < J, only where J is
+    # inside the range)
+    U0, L0, _ = gen.random_sound_bounds(n, seed=5 * n + K0, box=6.0 + n / 8)
+    Us, Ls = oracle.rounds(U0, L0, 0, K0 * BK)
+    Ue, Le = oracle.rounds(U0, L0, 0, min(n, K1 * BK))
+    Um, Lm = LeadModel(Us, Ls).run(K0, K1)
+    assert np.array_equal(Um, pins.units(Ue)) and np.array_equal(Lm, pins.units(Le))
+
+
+def test_lead_model_detects_a_range_that_leaves_a_copy_stale():
+    # a product that skips the other copy of every tile right of the
+    # diagonal, also where the range ends before that tile's band is a
+    # panel, leaves a stale copy in the range's result
+    class Broken(LeadModel):
+        def product(self, K, Kend=None):
+            return super().product(K, self.TB)
+
+    n = 330
+    U0, L0, _ = gen.random_sound_bounds(n, seed=9, box=6.0 + n / 8)
+    Ue, Le = oracle.rounds(U0, L0, 0, 2 * BK)
+    Um, Lm = Broken(U0, L0).run(0, 2)
+    assert not (np.array_equal(Um, pins.units(Ue)) and np.array_equal(Lm, pins.units(Le)))
 
 
 def test_lead_model_detects_a_planted_overlap():
