@@ -21,7 +21,8 @@ Printed: one JSON line with
                from HIP events (dbs_smooth_profiled on the launch stream),
                against the 157.3 T fp32 vector peak
   all_configs  the four smaller workloads: median GPU pass time, executed
-               fraction of peak, and the oracle's full pass on this host
+               fraction of peak, the same pass replayed from a captured HIP
+               graph, and the oracle's full pass on this host
   perk         the per-round kernel: HBM bytes of the round formulation
                (16 B per cell per round) / mean round time
   restraints   the workload's restraint list to dense bounds (fill + scatter)
@@ -325,8 +326,10 @@ def cpu_baseline(W, target_s):
 def config_sweep(names, dev, reps=15, oracle_on=True):
     """Each workload in `names`: the median device time of one full pass
     (HIP events on the launch stream, the input restored outside them), its
-    executed fraction of the fp32 peak, and the oracle's full pass on this
-    host's cores (wall time, one run)."""
+    executed fraction of the fp32 peak, the median time of the same pass
+    replayed from a captured HIP graph (and whether its bits equal the eager
+    pass's), and the oracle's full pass on this host's cores (wall time, one
+    run)."""
     import numpy as np
     import torch
 
@@ -353,13 +356,40 @@ def config_sweep(names, dev, reps=15, oracle_on=True):
             if r >= 2:
                 times.append(ev[0].elapsed_time(ev[1]))
         ms = float(np.median(times))
+        ref_u, ref_l = U.clone(), L.clone()
+        # the same pass captured once into a HIP graph and replayed (its own
+        # stream; the input restored outside the events), which removes the
+        # host's launch gaps between the pass's kernels
+        gs = torch.cuda.Stream(dev)
+        graph = torch.cuda.CUDAGraph()
+        gtimes = []
+        with torch.cuda.stream(gs):
+            U.copy_(U0)
+            L.copy_(L0)
+            gs.synchronize()
+            with torch.cuda.graph(graph, stream=gs):
+                dgb.smooth(U, L)
+            for r in range(reps + 2):
+                U.copy_(U0)
+                L.copy_(L0)
+                ev[0].record(gs)
+                graph.replay()
+                ev[1].record(gs)
+                gs.synchronize()
+                if r >= 2:
+                    gtimes.append(ev[0].elapsed_time(ev[1]))
+        same = bool(torch.equal(U.view(torch.int32), ref_u.view(torch.int32)) and
+                    torch.equal(L.view(torch.int32), ref_l.view(torch.int32)))
+        del graph
         triples = float(n) ** 3 * batch
         entry = {"n": n, "batch": batch, "algo": dgb.auto_algo(n, batch),
                  "lookahead_bands": dgb.lookahead_bands(n, batch),
                  "pass_ms_median": ms, "pass_ms_min": float(min(times)), "reps": reps,
                  "value": 2.0 * triples / (ms * 1e-3),
                  "executed_frac_of_fp32_peak": OPS_PER_TRIPLE * executed_triples(n, batch)
-                 / (ms * 1e-3) / FP32_VALU_PEAK}
+                 / (ms * 1e-3) / FP32_VALU_PEAK,
+                 "graph_replay_ms_median": float(np.median(gtimes)),
+                 "graph_replay_same_bits": same}
         if oracle_on:
             import oracle
             t0 = time.perf_counter()
@@ -370,8 +400,9 @@ def config_sweep(names, dev, reps=15, oracle_on=True):
             entry["oracle_cores"] = oracle.max_threads()
             entry["gpu_over_oracle"] = t / (ms * 1e-3)
         res[name] = entry
-        print(f"[bench] {name}: {ms:.3f} ms per pass", file=sys.stderr, flush=True)
-        del U0, L0, U, L
+        print(f"[bench] {name}: {ms:.3f} ms per pass, {entry['graph_replay_ms_median']:.3f} ms "
+              f"replayed from a graph", file=sys.stderr, flush=True)
+        del U0, L0, U, L, ref_u, ref_l
     return res
 
 
