@@ -593,26 +593,33 @@ __global__ __launch_bounds__(1024) void k_diag_panel_split(float *__restrict__ U
       lr[i] = sr[1][2 * ty + rr + i][rc];
     }
 
+    // Row m of D and of the slice is published into dv/rv[m & 1] by its
+    // owners during round m - 1, right after they relax it and before their
+    // other cells, so that the LDS write overlaps that work instead of
+    // preceding the barrier (buffer m & 1 was last read in round m - 2,
+    // which every thread finished before round m - 1 began).
+    auto publish = [&](int m, int buf, int a) {
+      // this thread's cells of row m = 2ty + a (D) and of slice row m
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        dvu[buf][tx * 2 + q] = du[a][q];
+        dvl[buf][tx * 2 + q] = dl[a][q];
+      }
+      if constexpr (P == 2) {
+        rvu[buf][rc] = ur[a];
+        rvl[buf][rc] = lr[a];
+      } else if (rr == a) {
+        rvu[buf][rc] = ur[0];
+        rvl[buf][rc] = lr[0];
+      }
+    };
+    if (ty == 0) publish(0, 0, 0);
     for (int mb = 0; mb < BK / 2; ++mb) {
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int m = mb * 2 + r;
         if (m >= bK) break;  // uniform
         const int buf = m & 1;
-        if (ty == mb) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            dvu[buf][tx * 2 + q] = du[r][q];
-            dvl[buf][tx * 2 + q] = dl[r][q];
-          }
-          if constexpr (P == 2) {
-            rvu[buf][rc] = ur[r];
-            rvl[buf][rc] = lr[r];
-          } else if (rr == r) {
-            rvu[buf][rc] = ur[0];
-            rvl[buf][rc] = lr[0];
-          }
-        }
         __syncthreads();
         float cu[2], cl[2], eu[2], el[2];
 #pragma unroll
@@ -623,16 +630,19 @@ __global__ __launch_bounds__(1024) void k_diag_panel_split(float *__restrict__ U
           el[q] = dvl[buf][tx * 2 + q];
         }
         const float ru = rvu[buf][rc], rl = rvl[buf][rc];  // R[m][c]
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) relax1<RU>(du[a][q], dl[a][q], cu[a], cl[a], eu[q], el[q]);
+        // row m + 1 (parity 1 - r) first: its owners publish it next
+        const int r1 = 1 - r;  // the loop is unrolled: a constant per copy
         if constexpr (P == 2) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) relax1<RU>(ur[i], lr[i], cu[i], cl[i], ru, rl);
+          relax1<RU>(ur[r1], lr[r1], cu[r1], cl[r1], ru, rl);
         } else {
           relax1<RU>(ur[0], lr[0], rr ? cu[1] : cu[0], rr ? cl[1] : cl[0], ru, rl);
         }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) relax1<RU>(du[r1][q], dl[r1][q], cu[r1], cl[r1], eu[q], el[q]);
+        if (m + 1 < bK && ty == (r == 0 ? mb : mb + 1)) publish(m + 1, buf ^ 1, r1);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) relax1<RU>(du[r][q], dl[r][q], cu[r], cl[r], eu[q], el[q]);
+        if constexpr (P == 2) relax1<RU>(ur[r], lr[r], cu[r], cl[r], ru, rl);
       }
     }
 
