@@ -2354,7 +2354,10 @@ hipError_t launch_blocked_on(float *U, float *L, int64_t n, int64_t batch, int64
   // workgroups still get a compute unit each (measured passes, against the
   // 4x2-cell product: n1536 0.860 / 0.930 ms, n2048 1.168 / 1.259, n3072
   // 2.239 / 2.359, 4 x n1024 0.639 / 0.682, 8 x n500 0.321 / 0.335; two
-  // slices lost 1-2 %: 16 x n500 0.382 / 0.373, 32 x n256 0.186 / 0.184)
+  // slices lost 1-2 %: 16 x n500 0.382 / 0.373, 32 x n256 0.186 / 0.184;
+  // four slices where the launch has more workgroups than CUs lost 5-7 %:
+  // 64 x n500 0.729 / 0.681, 16 x n1024 1.293 / 1.233, 40 x n700 1.128 /
+  // 1.077)
   const int product_p = wide_product && 4 * (TB - 1) * batch <= kSplitPanelFill ? 4 : 1;
   auto product_slice = ru ? (vec ? k_product_slice<true, true, 4> : k_product_slice<false, true, 4>)
                           : (vec ? k_product_slice<true, false, 4> : k_product_slice<false, false, 4>);
